@@ -1,0 +1,244 @@
+"""Benchmark of the GDN hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Headline: prefill tokens/s on the native-context workload (B=1, T=262,144,
+16 heads, d_k = d_v = 128, bf16 q/k/v/out, fp32 gates, zero initial state,
+final state returned).  One step = one gdn_prefill call over that sequence
+with inputs already resident in HBM.  The decode leg (256 sequences x 16
+heads, fp32 state 256 MiB updated in place, 64 consecutive steps with fresh
+tokens) is reported in the same JSON line as state GB/s.
+
+Timing uses HIP events on the stream the library launches on (torch's
+current stream, handed to the C ABI).  `roofline` uses algorithmic bytes and
+flops per call (see the design doc for the formulas); `cpu_baseline` times the
+fp64 oracle on a bounded sample of the same prefill workload on host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 matrix peak, TFLOP/s
+CHUNK = 64
+
+
+def prefill_bytes(T, N, hqk, hv, dk, dv, elem=2, init=False, final=True):
+    """Compulsory HBM bytes of one prefill call: q, k, v read, out written,
+    g and beta read, initial state read (if given) and final state written."""
+    b = T * (2 * hqk * dk + 2 * hv * dv) * elem + T * hv * 8
+    st = N * hv * dv * dk * 4
+    return b + (st if init else 0) + (st if final else 0)
+
+
+def prefill_flops_per_token(hqk, hv, dk, dv, C=CHUNK):
+    """Algorithmic flops per token of the chunk-C WY/UT form (dense C x C tiles):
+    per value head the state products 6 dk dv (K S^T, Q S^T, state update),
+    2 C dk for A's scaling-free half, 4 C dv for T~R and P U, C^2/3 for the
+    triangular inverse; per q/k head 4 C dk for K K^T and Q K^T."""
+    return hv * (6 * dk * dv + 2 * C * dk + 4 * C * dv + C * C / 3) + hqk * (4 * C * dk)
+
+
+def decode_bytes(N, hqk, hv, dk, dv, elem=2):
+    return 2 * N * hv * dv * dk * 4 + N * (2 * hqk * dk + 2 * hv * dv) * elem + N * hv * 8
+
+
+def _sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+PREFILL_SOURCES = ["gated_deltanet_linear_rule_amd/csrc/gdn_prefill.hip",
+                   "gated_deltanet_linear_rule_amd/csrc/gdn_device.h"]
+DECODE_SOURCES = ["gated_deltanet_linear_rule_amd/csrc/gdn_decode.hip",
+                  "gated_deltanet_linear_rule_amd/csrc/gdn_device.h"]
+
+
+def measured_traffic(name, sources):
+    """HBM bytes per call from the committed rocprofv3 counter summary, or None
+    if absent or taken on a different version of the kernel source."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)[name]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha") != _sha(sources):
+        return None
+    return rec.get("bytes_per_call")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-runs", type=int, default=3, help="timed 64-step decode runs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=131072)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the GDN path here is single-GPU); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_deltanet_linear_rule_amd import binding as B
+    from gated_deltanet_linear_rule_amd import inputs as gi
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    B.lib()
+
+    def dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ------------------------------------------------------------ prefill leg
+    t_gen = time.time()
+    inp = gi.make_inputs("prefill_256k", seed=0)
+    wl = inp.wl
+    T, hqk, hv, dk, dv = wl.total_tokens, wl.num_qk_heads, wl.num_v_heads, wl.head_dim_k, wl.head_dim_v
+    q, k, v, g, beta = dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta)
+    out = torch.empty((T, hv, dv), dtype=torch.bfloat16, device="cuda")
+    fin = torch.empty((1, hv, dv, dk), dtype=torch.float32, device="cuda")
+    log(f"prefill inputs generated and uploaded in {time.time() - t_gen:.1f}s")
+
+    def step():
+        B.gdn_prefill(q, k, v, g, beta, None, None, out=out, final_state=fin)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call_ms = [a.elapsed_time(b) for a, b in ev]
+    ms = float(np.mean(per_call_ms))
+    assert torch.isfinite(out.float()).all().item(), "non-finite prefill output"
+    log(f"prefill: mean {ms:.3f} ms/call, median {np.median(per_call_ms):.3f}, wall {1e3 * wall / args.steps:.3f} ms/step")
+
+    bytes_call = prefill_bytes(T, 1, hqk, hv, dk, dv)
+    flops_call = prefill_flops_per_token(hqk, hv, dk, dv) * T
+    gbs = bytes_call / (ms * 1e-3) / 1e9
+    tflops = flops_call / (ms * 1e-3) / 1e12
+    tok_s = T / (ms * 1e-3)
+    traffic = measured_traffic("gdn_prefill", PREFILL_SOURCES)
+    del q, k, v, g, beta, out
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------- decode leg
+    decode = None
+    if not args.no_decode:
+        t_gen = time.time()
+        d = gi.make_inputs("decode_256x64", seed=0)
+        N, dhqk, dhv, ddk, ddv = d.wl.num_seqs, d.wl.num_qk_heads, d.wl.num_v_heads, d.wl.head_dim_k, d.wl.head_dim_v
+        state = dev(d.init_state)
+        steps = [tuple(dev(s[n]) for n in ("q", "k", "v", "g", "beta")) for s in d.steps]
+        dout = torch.empty((N, dhv, ddv), dtype=torch.bfloat16, device="cuda")
+        log(f"decode inputs generated and uploaded in {time.time() - t_gen:.1f}s")
+
+        def run64():
+            for s in steps:
+                B.gdn_decode_step(*s, state, out=dout)
+
+        run64()
+        torch.cuda.synchronize()
+        dev_ms = []
+        for _ in range(args.decode_runs):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            run64()
+            b.record(stream)
+            torch.cuda.synchronize()
+            dev_ms.append(a.elapsed_time(b) / len(steps))
+        dms = float(np.mean(dev_ms))
+        dbytes = decode_bytes(N, dhqk, dhv, ddk, ddv)
+        dgbs = dbytes / (dms * 1e-3) / 1e9
+        assert torch.isfinite(state).all().item()
+        dtraffic = measured_traffic("gdn_decode", DECODE_SOURCES)
+        decode = {
+            "workload": "decode_256x64: 256 seqs x 16 heads, d=128, bf16 q/k/v, fp32 state [256,16,128,128] in place, 64 steps",
+            "value": round(dgbs, 1), "unit": "GB/s", "ms_per_step": round(dms, 5),
+            "tokens_per_s": round(N / (dms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(dgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(dgbs / HBM_PEAK_GBS, 4),
+                         "traffic": None if dtraffic is None else round(dtraffic / (dms * 1e-3) / 1e9, 1),
+                         "bytes_per_step": dbytes},
+        }
+        log(f"decode: {dms * 1e3:.1f} us/step, {dgbs:.0f} GB/s")
+        del state, steps, d
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import c_oracle
+        Ts = min(args.cpu_sample_tokens, T)
+        sub = inp
+        threads = min(16, os.cpu_count() or 1, hv)
+        t1 = time.perf_counter()
+        c_oracle.prefill(sub.q[:Ts], sub.k[:Ts], sub.v[:Ts], sub.g[:Ts], sub.beta[:Ts], None, None,
+                         nthreads=threads)
+        cw = time.perf_counter() - t1
+        cpu = {"value": round(Ts / cw, 1), "unit": "tokens/s", "cores": c_oracle.threads(threads),
+               "kind": "oracle",
+               "sample": f"first {Ts} tokens of the T=262144, H=16, d=128 prefill (all 16 heads), "
+                         f"fp64 sequential oracle, {cw:.1f}s wall"}
+        log(f"cpu oracle: {Ts} tokens in {cw:.1f}s on {cpu['cores']} threads")
+
+    rec = {
+        "metric": "GDN prefill tokens/sec (T=262144, H=16, d=128); decode state GB/s",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded: q,k ~ N(0,1) L2-normalised, v ~ N(0,1), beta = sigmoid(N(0,1)), g = -softplus(N(0,1)))",
+        "config": {"workload": "prefill_256k: B=1, T=262144, H_qk=H_v=16, d_k=d_v=128, bf16 I/O, fp32 gates and state, zero initial state, chunk 64",
+                   "global_batch": 1, "seq_len": T, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic / (ms * 1e-3) / 1e9, 1),
+                     "kernel": "gdn_prefill call (prep + scan kernels)",
+                     "bytes_per_call": bytes_call,
+                     "mfma_tflops": round(tflops, 1),
+                     "mfma_frac_of_bf16_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "cpu_baseline": cpu,
+        "decode": decode,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

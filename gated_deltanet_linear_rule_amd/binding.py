@@ -1,0 +1,173 @@
+"""Thin Python binding of libgdn.so (argument marshalling only).
+
+The functions here take torch tensors that live on the GPU, check that their
+dtypes/shapes/contiguity match the C ABI (include/gdn.h), and pass raw device
+pointers and the current HIP stream to the library.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback: if the
+library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+_lib = None
+
+GDN_SUCCESS = 0
+GDN_ERROR_INVALID_VALUE = 1
+GDN_ERROR_NOT_SUPPORTED = 2
+GDN_ERROR_LAUNCH = 3
+GDN_ERROR_OUT_OF_MEMORY = 4
+GDN_DTYPE_F32 = 0
+GDN_DTYPE_BF16 = 1
+
+
+class GdnShape(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_tokens", ctypes.c_int64),
+                ("num_qk_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
+                ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+                ("dtype", ctypes.c_int)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status} ({status_string(status)}): {detail}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m gated_deltanet_linear_rule_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        L.gdn_prefill.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, P]
+        L.gdn_prefill.restype = ctypes.c_int
+        L.gdn_decode_step.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P]
+        L.gdn_decode_step.restype = ctypes.c_int
+        L.gdn_status_string.argtypes = [ctypes.c_int]
+        L.gdn_status_string.restype = ctypes.c_char_p
+        L.gdn_last_error.argtypes = []
+        L.gdn_last_error.restype = ctypes.c_char_p
+        L.gdn_abi_version.argtypes = []
+        L.gdn_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def gdn_abi_version() -> int:
+    return lib().gdn_abi_version()
+
+
+def status_string(status: int) -> str:
+    return lib().gdn_status_string(status).decode()
+
+
+gdn_status_string = status_string
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _io_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDN_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return GDN_DTYPE_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(t, name, dtype=None, shape=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _raise(rc, where):
+    if rc != GDN_SUCCESS:
+        raise GdnError(rc, where, lib().gdn_last_error().decode())
+
+
+def gdn_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, out=None, final_state=None,
+                stream=None, num_seqs=None, return_final_state=True):
+    """Chunked GDN prefill over packed sequences.
+
+    q, k [T, Hqk, dk]; v [T, Hv, dv] (bf16 or fp32, same dtype); g, beta [T, Hv]
+    fp32; init_state [N, Hv, dv, dk] fp32 or None; cu_seqlens int32 [N+1] on
+    the GPU or None (then ``num_seqs`` equal-length sequences, default 1).
+    Returns (out, final_state); final_state is None if not requested.
+    """
+    T, hqk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    io = _io_dtype(q)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", torch.int32)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = 1 if num_seqs is None else int(num_seqs)
+    _check(q, "q", q.dtype, (T, hqk, dk))
+    _check(k, "k", q.dtype, (T, hqk, dk))
+    _check(v, "v", q.dtype, (T, hv, dv))
+    _check(g, "g", torch.float32, (T, hv))
+    _check(beta, "beta", torch.float32, (T, hv))
+    _check(init_state, "init_state", torch.float32, (N, hv, dv, dk))
+    if out is None:
+        out = torch.empty((T, hv, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", q.dtype, (T, hv, dv))
+    if final_state is None and return_final_state:
+        final_state = torch.empty((N, hv, dv, dk), dtype=torch.float32, device=q.device)
+    _check(final_state, "final_state", torch.float32, (N, hv, dv, dk))
+    shape = GdnShape(N, T, hqk, hv, dk, dv, io)
+    rc = lib().gdn_prefill(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                           _ptr(init_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state),
+                           _stream(stream))
+    _raise(rc, "gdn_prefill")
+    return out, final_state
+
+
+def gdn_decode_step(q, k, v, g, beta, state, out=None, stream=None):
+    """One decode token per sequence; ``state`` [N, Hv, dv, dk] is updated in place.
+
+    q, k [N, Hqk, dk]; v [N, Hv, dv]; g, beta [N, Hv].  Returns out [N, Hv, dv].
+    """
+    N, hqk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    io = _io_dtype(q)
+    _check(q, "q", q.dtype, (N, hqk, dk))
+    _check(k, "k", q.dtype, (N, hqk, dk))
+    _check(v, "v", q.dtype, (N, hv, dv))
+    _check(g, "g", torch.float32, (N, hv))
+    _check(beta, "beta", torch.float32, (N, hv))
+    _check(state, "state", torch.float32, (N, hv, dv, dk))
+    if out is None:
+        out = torch.empty((N, hv, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", q.dtype, (N, hv, dv))
+    shape = GdnShape(N, N, hqk, hv, dk, dv, io)
+    rc = lib().gdn_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               _ptr(state), _ptr(out), _stream(stream))
+    _raise(rc, "gdn_decode_step")
+    return out

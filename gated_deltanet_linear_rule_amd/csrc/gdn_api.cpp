@@ -1,0 +1,195 @@
+// gdn_api.cpp -- the C ABI of libgdn.so (declared in include/gdn.h).
+//
+// Validates every host-checkable argument before touching HIP, picks the
+// kernel variant, takes the prefill workspace from HIP's stream-ordered pool
+// and enqueues the kernels on the caller's stream.  No exception or abort
+// crosses the ABI; the text of the last failure is kept per thread.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <mutex>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+gdn_status fail(gdn_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Optional debugging aid: GDN_DEBUG_SYNC=1 synchronises the stream after each
+// call and reports asynchronous kernel errors as GDN_ERROR_LAUNCH.
+bool debug_sync() {
+    static const bool on = [] {
+        const char* s = std::getenv("GDN_DEBUG_SYNC");
+        return s && s[0] && s[0] != '0';
+    }();
+    return on;
+}
+
+gdn_status check_shape(const gdn_shape* s, bool decode) {
+    if (!s) return fail(GDN_ERROR_INVALID_VALUE, "shape is NULL");
+    if (s->num_seqs < 0 || s->num_tokens < 0)
+        return fail(GDN_ERROR_INVALID_VALUE, "negative size (num_seqs=%d, num_tokens=%lld)", s->num_seqs,
+                    (long long)s->num_tokens);
+    if (s->num_qk_heads <= 0 || s->num_v_heads <= 0 || s->head_dim_k <= 0 || s->head_dim_v <= 0)
+        return fail(GDN_ERROR_INVALID_VALUE, "head counts and head dims must be positive");
+    if (s->num_v_heads % s->num_qk_heads != 0)
+        return fail(GDN_ERROR_INVALID_VALUE, "num_v_heads (%d) is not a multiple of num_qk_heads (%d)",
+                    s->num_v_heads, s->num_qk_heads);
+    if (s->dtype != GDN_DTYPE_F32 && s->dtype != GDN_DTYPE_BF16)
+        return fail(GDN_ERROR_INVALID_VALUE, "unknown dtype %d", (int)s->dtype);
+    if (decode && s->num_tokens != s->num_seqs)
+        return fail(GDN_ERROR_INVALID_VALUE, "decode needs num_tokens == num_seqs (got %lld, %d)",
+                    (long long)s->num_tokens, s->num_seqs);
+    if (s->num_seqs == 0 && s->num_tokens != 0)
+        return fail(GDN_ERROR_INVALID_VALUE, "tokens without sequences");
+    if ((s->head_dim_k != 64 && s->head_dim_k != 128) || (s->head_dim_v != 64 && s->head_dim_v != 128))
+        return fail(GDN_ERROR_NOT_SUPPORTED, "head dims (%d, %d) not in {64, 128}", s->head_dim_k,
+                    s->head_dim_v);
+    const int64_t units = (int64_t)s->num_seqs * s->num_v_heads;
+    if (units > INT32_MAX) return fail(GDN_ERROR_NOT_SUPPORTED, "too many (sequence, head) pairs");
+    return GDN_SUCCESS;
+}
+
+gdn_status check_ptr(const void* p, const char* name, uintptr_t align, bool required) {
+    if (!p) return required ? fail(GDN_ERROR_INVALID_VALUE, "%s is NULL", name) : GDN_SUCCESS;
+    if (!aligned(p, align)) return fail(GDN_ERROR_INVALID_VALUE, "%s is not %u-byte aligned", name, (unsigned)align);
+    return GDN_SUCCESS;
+}
+
+#define GDN_TRY(expr)                         \
+    do {                                      \
+        gdn_status st_ = (expr);              \
+        if (st_ != GDN_SUCCESS) return st_;   \
+    } while (0)
+
+// Keep freed workspace in HIP's default pool instead of returning it to the
+// driver at every synchronisation (set once per device).
+void keep_pool_memory(int dev) {
+    static std::mutex mu;
+    static bool done[64] = {};
+    if (dev < 0 || dev >= 64) return;
+    std::lock_guard<std::mutex> lk(mu);
+    if (done[dev]) return;
+    hipMemPool_t pool;
+    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+        uint64_t thr = UINT64_MAX;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+    }
+    done[dev] = true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_last_error(void) { return g_last_error; }
+
+const char* gdn_status_string(gdn_status status) {
+    switch (status) {
+        case GDN_SUCCESS: return "success";
+        case GDN_ERROR_INVALID_VALUE: return "invalid argument";
+        case GDN_ERROR_NOT_SUPPORTED: return "shape or type not supported";
+        case GDN_ERROR_LAUNCH: return "kernel launch failed";
+        case GDN_ERROR_OUT_OF_MEMORY: return "workspace allocation failed";
+    }
+    return "unknown status";
+}
+
+gdn_status gdn_decode_step(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                           const float* g, const float* beta, float* state, void* out, void* stream) {
+    g_last_error[0] = '\0';
+    GDN_TRY(check_shape(shape, true));
+    const bool any = shape->num_seqs > 0;
+    GDN_TRY(check_ptr(q, "q", 16, any));
+    GDN_TRY(check_ptr(k, "k", 16, any));
+    GDN_TRY(check_ptr(v, "v", 16, any));
+    GDN_TRY(check_ptr(g, "g", 4, any));
+    GDN_TRY(check_ptr(beta, "beta", 4, any));
+    GDN_TRY(check_ptr(state, "state", 16, any));
+    GDN_TRY(check_ptr(out, "out", 16, any));
+    if (!any) return GDN_SUCCESS;
+    gdn::DecodeArgs a{q, k, v, g, beta, state, out, shape->num_seqs, shape->num_qk_heads, shape->num_v_heads};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = gdn::launch_decode(a, shape->dtype == GDN_DTYPE_BF16, shape->head_dim_k, shape->head_dim_v, st);
+    if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(GDN_ERROR_LAUNCH, "decode: %s", hipGetErrorString(e));
+    return GDN_SUCCESS;
+}
+
+gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, const float* init_state, const int32_t* cu_seqlens, void* out,
+                       float* final_state, void* stream) {
+    g_last_error[0] = '\0';
+    GDN_TRY(check_shape(shape, false));
+    const bool tok = shape->num_tokens > 0;
+    GDN_TRY(check_ptr(q, "q", 16, tok));
+    GDN_TRY(check_ptr(k, "k", 16, tok));
+    GDN_TRY(check_ptr(v, "v", 16, tok));
+    GDN_TRY(check_ptr(g, "g", 4, tok));
+    GDN_TRY(check_ptr(beta, "beta", 4, tok));
+    GDN_TRY(check_ptr(out, "out", 16, tok));
+    GDN_TRY(check_ptr(init_state, "init_state", 16, false));
+    GDN_TRY(check_ptr(final_state, "final_state", 16, false));
+    GDN_TRY(check_ptr(cu_seqlens, "cu_seqlens", 4, false));
+    if (!cu_seqlens && shape->num_seqs > 0 && shape->num_tokens % shape->num_seqs != 0)
+        return fail(GDN_ERROR_INVALID_VALUE, "num_tokens (%lld) is not a multiple of num_seqs (%d) and no cu_seqlens",
+                    (long long)shape->num_tokens, shape->num_seqs);
+    if (init_state && final_state && init_state != final_state) {
+        const size_t bytes = (size_t)shape->num_seqs * shape->num_v_heads * shape->head_dim_v * shape->head_dim_k * 4;
+        const char* a0 = reinterpret_cast<const char*>(init_state);
+        const char* b0 = reinterpret_cast<const char*>(final_state);
+        if (a0 < b0 + bytes && b0 < a0 + bytes)
+            return fail(GDN_ERROR_INVALID_VALUE, "init_state and final_state overlap partially");
+    }
+    if (shape->num_seqs == 0) return GDN_SUCCESS;
+
+    const bool bf16 = shape->dtype == GDN_DTYPE_BF16;
+    gdn::PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.init_state = init_state; a.cu = cu_seqlens; a.out = out; a.final_state = final_state;
+    a.num_tokens = shape->num_tokens;
+    a.seqlen = shape->num_tokens / shape->num_seqs;
+    a.num_seqs = shape->num_seqs;
+    a.hqk = shape->num_qk_heads;
+    a.hv = shape->num_v_heads;
+    a.dv = shape->head_dim_v;
+    a.num_slots = (shape->num_tokens + 63) / 64 + shape->num_seqs;
+    if (a.num_slots > INT32_MAX) return fail(GDN_ERROR_NOT_SUPPORTED, "too many chunks");
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t half = gdn::prefill_workspace_bytes(a.num_slots, a.hv, bf16 ? 2 : 4) / 2;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(GDN_ERROR_LAUNCH, "hipGetDevice failed");
+    keep_pool_memory(dev);
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, (size_t)(2 * half), st) != hipSuccess || !ws) {
+        (void)hipGetLastError();
+        return fail(GDN_ERROR_OUT_OF_MEMORY, "prefill workspace of %lld bytes", (long long)(2 * half));
+    }
+    a.ws_t = ws;
+    a.ws_p = static_cast<char*>(ws) + half;
+    hipError_t e = gdn::launch_prefill(a, bf16, shape->head_dim_k, st);
+    hipError_t ef = hipFreeAsync(ws, st);
+    if (e == hipSuccess) e = ef;
+    if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(GDN_ERROR_LAUNCH, "prefill: %s", hipGetErrorString(e));
+    return GDN_SUCCESS;
+}
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+/*
+ * gdn.h -- C ABI of libgdn.so, the MI355X (gfx950) Gated DeltaNet library.
+ *
+ * A Gated DeltaNet (GDN) layer mixes tokens through a fixed-size recurrent
+ * state per head instead of a per-token key/value cache (flozi.net,
+ * "Qwen3.8-Flash-Next architecture": the stack table, 48 token-mixing layers
+ * of which 36 are GDN, and "Der Weg eines Tokens durch das Modell", item 1).
+ * The pages give no formula; the recurrence computed here, per value head with
+ * an fp32 state S of shape d_v x d_k, is the gated delta rule
+ *
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t,                 alpha_t = exp(g_t),
+ *
+ * with the output read after the token's own write, no query scaling and no
+ * normalisation of q or k inside the library.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor arguments are DEVICE pointers owned by the caller; the library
+ *   keeps no pointer after the call returns.  Work is enqueued on `stream`
+ *   (a hipStream_t; NULL = the null stream) and the call returns without
+ *   waiting: the caller synchronises before reading results.
+ * - Layouts are dense row-major, token-major:
+ *     q, k         [tokens, num_qk_heads, head_dim_k]   element type `dtype`
+ *     v, out       [tokens, num_v_heads,  head_dim_v]   element type `dtype`
+ *     g, beta      [tokens, num_v_heads]                fp32 (g = log alpha <= 0, beta in [0, 1])
+ *     state        [num_seqs, num_v_heads, head_dim_v, head_dim_k]  fp32
+ *   Value head h reads q/k head floor(h * num_qk_heads / num_v_heads)
+ *   (grouped value heads: contiguous groups share one q/k head).
+ * - Alignment: q, k, v, out and states 16-byte aligned; g, beta 4-byte.
+ * - Supported: head_dim_k, head_dim_v in {64, 128}; num_v_heads a multiple of
+ *   num_qk_heads; dtype fp32 or bf16.  Other well-formed shapes return
+ *   GDN_ERROR_NOT_SUPPORTED.
+ * - Every host-checkable argument is validated before any HIP call; on an
+ *   error nothing is enqueued.  No call throws or aborts.  The text of the
+ *   last error on the calling thread is available from gdn_last_error().
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_status {
+    GDN_SUCCESS = 0,
+    GDN_ERROR_INVALID_VALUE = 1,  /* malformed argument (NULL, negative size, misaligned ...) */
+    GDN_ERROR_NOT_SUPPORTED = 2,  /* well-formed shape this build has no kernel for */
+    GDN_ERROR_LAUNCH = 3,         /* a HIP launch or enqueue failed */
+    GDN_ERROR_OUT_OF_MEMORY = 4   /* the stream-ordered workspace could not be allocated */
+} gdn_status;
+
+typedef enum gdn_dtype {
+    GDN_DTYPE_F32 = 0,            /* q, k, v, out are fp32 */
+    GDN_DTYPE_BF16 = 1            /* q, k, v, out are bf16 (out rounded to nearest even) */
+} gdn_dtype;
+
+/* Problem shape.
+ * num_seqs   N >= 0 sequences.
+ * num_tokens total tokens in q/k/v/out (prefill: sum of the lengths;
+ *            decode: must equal num_seqs, one token per sequence).
+ * Without cu_seqlens the N sequences have equal length num_tokens / N
+ * (num_tokens must be a multiple of N), stored one after another. */
+typedef struct gdn_shape {
+    int32_t num_seqs;
+    int64_t num_tokens;
+    int32_t num_qk_heads;
+    int32_t num_v_heads;
+    int32_t head_dim_k;
+    int32_t head_dim_v;
+    gdn_dtype dtype;
+} gdn_shape;
+
+/*
+ * gdn_prefill -- run the recurrence over whole sequences (packed varlen).
+ *
+ * Computes o_t for every token of every sequence and, if final_state is not
+ * NULL, the state after each sequence's last token.  The chunk-wise WY / UT
+ * form (chunks of 64 tokens, restarting at every sequence start) is used on
+ * the GPU; the result equals the token-by-token recurrence up to rounding.
+ *
+ * init_state  [N, Hv, dv, dk] fp32 or NULL (zero initial state).  It may be
+ *             the same buffer as final_state (each sequence's slice is read
+ *             before it is written); partial overlap is not allowed.
+ * cu_seqlens  DEVICE int32 [N + 1] token offsets or NULL (equal lengths).
+ *             Precondition (not checked, it lives on the device):
+ *             cu[0] = 0, non-decreasing, cu[N] = num_tokens.  Empty sequences
+ *             are allowed: their final state equals their initial state.
+ * out         [num_tokens, Hv, dv] in `dtype`.
+ * final_state [N, Hv, dv, dk] fp32 or NULL.
+ *
+ * Memory: a stream-ordered workspace of about
+ * (num_tokens / 64 + N) * Hv * 2 * 64 * 64 * sizeof(element) bytes is taken
+ * from HIP's default memory pool on `stream` and returned to it before the
+ * call's work completes (GDN_ERROR_OUT_OF_MEMORY if that fails).
+ */
+gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, const float* init_state,
+                       const int32_t* cu_seqlens, void* out, float* final_state,
+                       void* stream);
+
+/*
+ * gdn_decode_step -- advance N sequences by one token each.
+ *
+ * Tokens = sequences: q, k [N, Hqk, dk]; v, out [N, Hv, dv]; g, beta [N, Hv].
+ * state [N, Hv, dv, dk] fp32 is read and updated in place (one pass over it).
+ * Needs no workspace and allocates nothing.
+ */
+gdn_status gdn_decode_step(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                           const float* g, const float* beta, float* state, void* out,
+                           void* stream);
+
+/* Static English text for a status code (never NULL). */
+const char* gdn_status_string(gdn_status status);
+
+/* Details of the last non-success status returned on this thread ("" if none). */
+const char* gdn_last_error(void);
+
+/* GDN_ABI_VERSION of the loaded library. */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,143 @@
+"""C-ABI host checks that need no GPU: the library loads, exports every entry
+point declared in include/gdn.h, and rejects malformed arguments before any
+HIP call (so these calls are safe without a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_deltanet_linear_rule_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def _lib():
+    if not os.path.exists(B.lib_path()):
+        pytest.fail("libgdn.so is not built (run python -m gated_deltanet_linear_rule_amd.build)")
+    return B.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert _declared_functions() == ["gdn_abi_version", "gdn_decode_step", "gdn_last_error",
+                                     "gdn_prefill", "gdn_status_string"]
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_library_exports_only_the_abi():
+    """No stray C symbols: the dynamic table holds the declared gdn_* functions."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", B.lib_path()], capture_output=True, text=True).stdout
+    exported = sorted({ln.split()[-1] for ln in out.splitlines() if " T gdn_" in ln})
+    assert exported == _declared_functions()
+
+
+def test_abi_version_and_status_strings():
+    assert B.gdn_abi_version() == 1
+    seen = set()
+    for st in range(5):
+        s = B.status_string(st)
+        assert s and s not in seen
+        seen.add(s)
+    assert B.status_string(99) == "unknown status"
+
+
+def _shape(**kw):
+    d = dict(num_seqs=1, num_tokens=64, num_qk_heads=2, num_v_heads=2, head_dim_k=64, head_dim_v=64,
+             dtype=B.GDN_DTYPE_BF16)
+    d.update(kw)
+    return B.GdnShape(d["num_seqs"], d["num_tokens"], d["num_qk_heads"], d["num_v_heads"],
+                      d["head_dim_k"], d["head_dim_v"], d["dtype"])
+
+
+FAKE = 1 << 20   # non-NULL, 16-byte aligned host-side stand-in (never dereferenced)
+
+
+def _prefill(shape, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, init=None, cu=None, out=FAKE, fin=None)
+    p.update(ptrs)
+    c = ctypes.c_void_p
+    L = _lib()
+    rc = L.gdn_prefill(ctypes.byref(shape) if shape is not None else None, c(p["q"]), c(p["k"]), c(p["v"]),
+                       c(p["g"]), c(p["beta"]), c(p["init"]), c(p["cu"]), c(p["out"]), c(p["fin"]), None)
+    return rc, L.gdn_last_error().decode()
+
+
+def _decode(shape, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state=FAKE, out=FAKE)
+    p.update(ptrs)
+    c = ctypes.c_void_p
+    L = _lib()
+    rc = L.gdn_decode_step(ctypes.byref(shape), c(p["q"]), c(p["k"]), c(p["v"]), c(p["g"]), c(p["beta"]),
+                           c(p["state"]), c(p["out"]), None)
+    return rc, L.gdn_last_error().decode()
+
+
+@pytest.mark.parametrize("shape_kw,ptrs,status,msg", [
+    (None, {}, B.GDN_ERROR_INVALID_VALUE, "shape is NULL"),
+    (dict(num_seqs=-1), {}, B.GDN_ERROR_INVALID_VALUE, "negative"),
+    (dict(num_tokens=-5), {}, B.GDN_ERROR_INVALID_VALUE, "negative"),
+    (dict(num_qk_heads=0), {}, B.GDN_ERROR_INVALID_VALUE, "positive"),
+    (dict(num_qk_heads=3, num_v_heads=4), {}, B.GDN_ERROR_INVALID_VALUE, "multiple"),
+    (dict(dtype=7), {}, B.GDN_ERROR_INVALID_VALUE, "dtype"),
+    (dict(head_dim_k=96), {}, B.GDN_ERROR_NOT_SUPPORTED, "head dims"),
+    (dict(head_dim_v=256), {}, B.GDN_ERROR_NOT_SUPPORTED, "head dims"),
+    (dict(num_seqs=0, num_tokens=3), {}, B.GDN_ERROR_INVALID_VALUE, "without sequences"),
+    (dict(num_seqs=3, num_tokens=64), {}, B.GDN_ERROR_INVALID_VALUE, "multiple of num_seqs"),
+    ({}, dict(q=None), B.GDN_ERROR_INVALID_VALUE, "q is NULL"),
+    ({}, dict(out=None), B.GDN_ERROR_INVALID_VALUE, "out is NULL"),
+    ({}, dict(beta=None), B.GDN_ERROR_INVALID_VALUE, "beta is NULL"),
+    ({}, dict(k=FAKE + 2), B.GDN_ERROR_INVALID_VALUE, "aligned"),
+    ({}, dict(g=FAKE + 2), B.GDN_ERROR_INVALID_VALUE, "aligned"),
+    ({}, dict(init=FAKE + 8), B.GDN_ERROR_INVALID_VALUE, "aligned"),
+    ({}, dict(cu=FAKE + 1), B.GDN_ERROR_INVALID_VALUE, "aligned"),
+    ({}, dict(init=FAKE, fin=FAKE + 4096), B.GDN_ERROR_INVALID_VALUE, "overlap"),
+])
+def test_prefill_rejects_bad_arguments_before_any_hip_call(shape_kw, ptrs, status, msg):
+    rc, err = _prefill(None if shape_kw is None else _shape(**shape_kw), **ptrs)
+    assert rc == status and msg in err, (rc, err)
+
+
+def test_prefill_with_nothing_to_do_succeeds_without_a_device():
+    rc, err = _prefill(_shape(num_seqs=0, num_tokens=0), q=None, k=None, v=None, g=None, beta=None, out=None)
+    assert rc == B.GDN_SUCCESS and err == ""
+
+
+@pytest.mark.parametrize("shape_kw,ptrs,status,msg", [
+    (dict(num_seqs=4, num_tokens=5), {}, B.GDN_ERROR_INVALID_VALUE, "num_tokens == num_seqs"),
+    (dict(num_seqs=4, num_tokens=4), dict(state=None), B.GDN_ERROR_INVALID_VALUE, "state is NULL"),
+    (dict(num_seqs=4, num_tokens=4), dict(state=FAKE + 4), B.GDN_ERROR_INVALID_VALUE, "aligned"),
+    (dict(num_seqs=4, num_tokens=4, head_dim_k=32), {}, B.GDN_ERROR_NOT_SUPPORTED, "head dims"),
+])
+def test_decode_rejects_bad_arguments(shape_kw, ptrs, status, msg):
+    rc, err = _decode(_shape(**shape_kw), **ptrs)
+    assert rc == status and msg in err, (rc, err)
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "_LIB_PATH", "/nonexistent/libgdn.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        B.lib()
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """No file of the library imports, links or loads the oracle."""
+    pkg = os.path.join(ROOT, "gated_deltanet_linear_rule_amd")
+    pat = re.compile(r"\b(from|import)\s+oracle\b|c_oracle|gdn_oracle|libgdn_oracle")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                assert not pat.search(open(os.path.join(dirpath, f)).read()), f

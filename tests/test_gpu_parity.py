@@ -1,0 +1,185 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Tolerances: max|gpu - ref| / max|ref| <= 1e-5 on the fp32 path and <= 1e-2
+on the bf16 path, for outputs and final states separately.  Inputs are the
+seeded synthetic workloads (gated_deltanet_linear_rule_amd.inputs); the
+oracle sees exactly the stored values the GPU reads.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_linear_rule_amd import binding as B
+from gated_deltanet_linear_rule_amd import inputs as gi
+from oracle import c_oracle
+from tests.gpu_util import TOL, check_prefill, dev, host64, rel_err, run_prefill, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()   # fails loudly if the HIP library is missing
+
+
+# ---------------------------------------------------------------- small shapes
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
+def test_single_chunk_shapes(dtype, dk, dv):
+    inp = gi.make_inputs(gi.custom(dtype=dtype, Hqk=2, Hv=2, dk=dk, dv=dv, seqlens=(64,)), seed=1)
+    check_prefill(inp, label=f"one chunk {dtype} dk={dk} dv={dv}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("lens", [(1,), (63,), (65,), (200,), (64, 1, 127, 0, 5), (0, 0), (300, 64)])
+def test_ragged_packed_lengths(dtype, lens):
+    inp = gi.make_inputs(gi.custom(dtype=dtype, Hqk=2, Hv=4, dk=64, dv=64, seqlens=lens,
+                                   init_state="normal"), seed=2)
+    check_prefill(inp, label=f"ragged {dtype} {lens}")
+
+
+@pytest.mark.parametrize("ratio", [1, 2, 4])
+def test_grouped_value_heads(ratio):
+    inp = gi.make_inputs(gi.custom(dtype="bf16", Hqk=2, Hv=2 * ratio, dk=128, dv=128, seqlens=(150, 77),
+                                   init_state="normal"), seed=3)
+    check_prefill(inp, label=f"GVA 1:{ratio}")
+
+
+def test_equal_length_batch_without_offsets():
+    inp = gi.make_inputs(gi.custom(dtype="bf16", Hqk=2, Hv=2, dk=128, dv=128, seqlens=(96, 96, 96),
+                                   init_state="normal"), seed=4)
+    cu = inp.cu_seqlens
+    inp.cu_seqlens = None            # equal lengths: the library derives the offsets
+    out, fin = run_prefill(inp, num_seqs=3)
+    inp.cu_seqlens = cu
+    ro, rf = c_oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.init_state, cu)
+    assert rel_err(out, ro) <= 1e-2 and rel_err(fin, rf) <= 1e-2
+
+
+def test_zero_initial_state_null_equals_zeros():
+    inp = gi.make_inputs(gi.custom(dtype="bf16", Hqk=2, Hv=2, dk=128, dv=128, seqlens=(130,)), seed=5)
+    a = run_prefill(inp, init_mode="null")
+    b = run_prefill(inp, init_mode="zeros")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    check_prefill(inp, init_mode="null", label="NULL init")
+
+
+def test_init_state_may_alias_final_state():
+    inp = gi.make_inputs(gi.custom(dtype="bf16", Hqk=2, Hv=4, dk=128, dv=128, seqlens=(100, 40),
+                                   init_state="normal"), seed=6)
+    a = run_prefill(inp)
+    b = run_prefill(inp, out_alias=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_split_with_state_handoff_matches_unsplit():
+    inp = gi.make_inputs(gi.custom(dtype="f32", Hqk=2, Hv=2, dk=64, dv=64, seqlens=(300,),
+                                   init_state="normal"), seed=7)
+    full_o, full_s = run_prefill(inp)
+    for cut in (1, 64, 100):
+        a = gi.Inputs(gi.custom(dtype="f32", Hqk=2, Hv=2, dk=64, dv=64, seqlens=(cut,)))
+        a.q, a.k, a.v, a.g, a.beta, a.init_state = inp.q[:cut], inp.k[:cut], inp.v[:cut], inp.g[:cut], inp.beta[:cut], inp.init_state
+        oa, sa = run_prefill(a)
+        b = gi.Inputs(gi.custom(dtype="f32", Hqk=2, Hv=2, dk=64, dv=64, seqlens=(300 - cut,)))
+        b.q, b.k, b.v, b.g, b.beta = inp.q[cut:], inp.k[cut:], inp.v[cut:], inp.g[cut:], inp.beta[cut:]
+        b.init_state = sa.astype(np.float32)
+        ob, sb = run_prefill(b)
+        assert rel_err(np.concatenate([oa, ob]), full_o) < 1e-5 and rel_err(sb, full_s) < 1e-5
+
+
+def test_results_are_bitwise_deterministic():
+    inp = gi.make_inputs(gi.custom(dtype="bf16", Hqk=4, Hv=8, dk=128, dv=128, seqlens=(500, 300),
+                                   init_state="normal"), seed=8)
+    a = run_prefill(inp)
+    b = run_prefill(inp)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_long_decay_free_stretch_stays_accurate():
+    """g = 0 and small beta: no decay hides accumulated error across many chunks."""
+    inp = gi.make_inputs(gi.custom(dtype="bf16", Hqk=1, Hv=1, dk=128, dv=128, seqlens=(2048,)), seed=9)
+    inp.g = np.zeros_like(inp.g)
+    inp.beta = (inp.beta * 0.1).astype(np.float32)
+    check_prefill(inp, label="g=0, beta/10")
+
+
+# ------------------------------------------------------------- the workloads
+def test_tiny_f32_workload():
+    """T=256, H=2, d=64, fp32 throughout, zero initial state, seed 0."""
+    check_prefill(gi.make_inputs("tiny_f32", seed=0))
+
+
+def test_prefill_4k_workload():
+    """T=4096, H=16, d=128, bf16, zero initial state."""
+    check_prefill(gi.make_inputs("prefill_4k", seed=0))
+
+
+def test_varlen_packed_workload():
+    """8 packed sequences (lengths U[1024,16384] from the seed), 32 v-heads on 16 q/k heads."""
+    inp = gi.make_inputs("varlen_8x", seed=0)
+    say(f"[parity] varlen lengths {inp.wl.seqlens}")
+    check_prefill(inp)
+
+
+def test_prefill_256k_workload_sampled_heads():
+    """T=262144, H=16, d=128: the full call, checked on 4 of the 16 heads (full length)."""
+    inp = gi.make_inputs("prefill_256k", seed=0)
+    out, fin = run_prefill(inp)
+    heads = [0, 5, 10, 15]
+    ro, rf = c_oracle.prefill(inp.q[:, heads], inp.k[:, heads], inp.v[:, heads], inp.g[:, heads],
+                              inp.beta[:, heads], None, None)
+    eo, ef = rel_err(out[:, heads], ro), rel_err(fin[:, heads], rf)
+    say(f"[parity] prefill_256k heads {heads}: out {eo:.3e} final {ef:.3e}")
+    assert np.all(np.isfinite(out))
+    assert eo <= 1e-2 and ef <= 1e-2
+
+
+# ------------------------------------------------------------------- decode
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (128, 64)])
+def test_decode_small(dtype, dk, dv):
+    wl = gi.custom(dtype=dtype, Hqk=2, Hv=4, dk=dk, dv=dv, seqlens=(1,) * 5, init_state="normal",
+                   decode_steps=6)
+    inp = gi.make_inputs(wl, seed=10)
+    state = dev(inp.init_state)
+    ref = inp.init_state.astype(np.float64)
+    worst = 0.0
+    for st in inp.steps:
+        out = B.gdn_decode_step(dev(st["q"]), dev(st["k"]), dev(st["v"]), dev(st["g"]), dev(st["beta"]), state)
+        ro = c_oracle.decode_step(st["q"], st["k"], st["v"], st["g"], st["beta"], ref)
+        worst = max(worst, rel_err(host64(out), ro))
+    es = rel_err(host64(state), ref)
+    say(f"[parity] decode {dtype} dk={dk} dv={dv}: out {worst:.3e} state {es:.3e}")
+    assert worst <= TOL[dtype] and es <= TOL[dtype]
+
+
+def test_decode_equals_prefill_token_by_token():
+    inp = gi.make_inputs(gi.custom(dtype="f32", Hqk=2, Hv=2, dk=64, dv=64, seqlens=(20,),
+                                   init_state="normal"), seed=11)
+    po, ps = run_prefill(inp)
+    state = dev(inp.init_state)
+    for t in range(20):
+        out = B.gdn_decode_step(dev(inp.q[t:t + 1]), dev(inp.k[t:t + 1]), dev(inp.v[t:t + 1]),
+                                dev(inp.g[t:t + 1]), dev(inp.beta[t:t + 1]), state)
+        assert rel_err(host64(out), po[t:t + 1]) < 1e-5
+    assert rel_err(host64(state), ps) < 1e-5
+
+
+def test_decode_256x64_workload():
+    """256 sequences x 16 heads, d=128, bf16, fp32 state in place, 64 steps."""
+    inp = gi.make_inputs("decode_256x64", seed=0)
+    state = dev(inp.init_state)
+    ref = inp.init_state.astype(np.float64)
+    worst_num, worst_den = 0.0, 0.0
+    for st in inp.steps:
+        out = B.gdn_decode_step(dev(st["q"]), dev(st["k"]), dev(st["v"]), dev(st["g"]), dev(st["beta"]), state)
+        ro = c_oracle.decode_step(st["q"], st["k"], st["v"], st["g"], st["beta"], ref)
+        o = host64(out)
+        worst_num = max(worst_num, float(np.max(np.abs(o - ro))))
+        worst_den = max(worst_den, float(np.max(np.abs(ro))))
+    eo = worst_num / worst_den
+    es = rel_err(host64(state), ref)
+    say(f"[parity] decode_256x64: out {eo:.3e} state {es:.3e}")
+    assert eo <= 1e-2 and es <= 1e-2

@@ -31,7 +31,8 @@ constexpr int kChunk = 64;   // tokens per chunk
 constexpr int kWave = 64;    // lanes per wavefront
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// Wave index, marked wave-uniform so that branches on it stay scalar.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // ---------------------------------------------------------------------------
 // operand traits

@@ -97,15 +97,34 @@ __device__ __forceinline__ float wave_cumsum(float x) {
     return x;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave, in fp64.
+// Lane shuffle of a double by a DPP control (two 32-bit halves); lanes whose
+// source is outside the pattern (or whose row is masked off) read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double x) {
+    const long long b = __builtin_bit_cast(long long, x);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xffffffff), CTRL, ROW_MASK, 0xF, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, ROW_MASK, 0xF, true);
+    return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned)lo);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, in fp64, on DPP lane
+// moves only: shifts by 1, 2, 4, 8 inside each row of 16 lanes, then lane 15
+// of a row into the next row (rows 1, 3) and lane 31 into rows 2, 3.
 __device__ __forceinline__ double wave_cumsum_f64(double x) {
-    const int l = lane_id();
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        double y = __shfl_up(x, off, kWave);
-        if (l >= off) x += y;
-    }
+    x += dpp_f64<0x111, 0xF>(x);   // row_shr:1
+    x += dpp_f64<0x112, 0xF>(x);   // row_shr:2
+    x += dpp_f64<0x114, 0xF>(x);   // row_shr:4
+    x += dpp_f64<0x118, 0xF>(x);   // row_shr:8
+    x += dpp_f64<0x142, 0xA>(x);   // row_bcast:15
+    x += dpp_f64<0x143, 0xC>(x);   // row_bcast:31
     return x;
+}
+
+__device__ __forceinline__ double lane63_f64(double x) {
+    const long long b = __builtin_bit_cast(long long, x);
+    const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffff), 63);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), 63);
+    return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned)lo);
 }
 
 // Gates of one chunk, computed by one wave: lane l holds g_l (0 past the end
@@ -115,7 +134,7 @@ __device__ __forceinline__ double wave_cumsum_f64(double x) {
 __device__ __forceinline__ void chunk_gates(float g, float* gam, float* dec) {
     const int l = lane_id();
     const double G = wave_cumsum_f64((double)g * 1.4426950408889634);
-    const double Gl = __shfl(G, kWave - 1, kWave);
+    const double Gl = lane63_f64(G);
     gam[l] = fast_exp2((float)G);
     dec[l] = fast_exp2((float)(Gl - G));
     if (l == 0) gam[kChunk] = fast_exp2((float)Gl);
@@ -665,13 +684,13 @@ struct SplitStage {
 template <typename OP, int DK>
 struct SplitSmem {
     static constexpr int NWS = DK / 32;
-    static constexpr int RLD = kChunk + 2 * pad_elems<OP>();   // 16-byte aligned rows
+    static constexpr int RLD = kChunk + (sizeof(OP) == 2 ? 8 : 4);   // 16-byte rows, staggered banks
     f32x4 part[NWS][8][kWave];          // E1: X^T partials (0..3) and Y^T partials (4..7)
     alignas(16) OP Rt[16 * RLD];        // E2: R as [column][token]
     alignas(16) OP Ut[16 * RLD];        // E3: U as [column][token]
     alignas(16) OP Dt[16 * RLD];        // E3: D o U as [column][token]
-    alignas(16) float gam[NWS][kChunk + 4];   // per-wave gates: e^{G_t}, [64] = e^{G_last}
-    alignas(16) float dec[NWS][kChunk];       // e^{G_last - G_t}
+    alignas(16) float gam[2][kChunk + 4];   // gates by chunk parity: e^{G_t}, [64] = e^{G_last}
+    alignas(16) float dec[2][kChunk];       // e^{G_last - G_t}
 };
 
 template <typename OP, int DK>
@@ -733,24 +752,27 @@ struct SplitCtx {
     // loads in flight.
     __device__ __forceinline__ void load(St& s, int64_t j, bool valid) const {
         const int64_t jc = valid ? j : 0;
-        const int64_t nt = valid ? seq_tokens - jc * kChunk : 0;   // g past the sequence reads 0
-        const auto rg = make_rsrc(gb + jc * g_step, nt > 0 ? ((nt - 1) * hv + 1) * 4 : 0);
+        const int64_t kqo = jc * kq_step, vo = jc * v_step, go = jc * g_step, wo = jc * w_step;
+        const int64_t nt = seq_tokens - jc * kChunk;              // g past the sequence reads 0
+        const auto rg = make_rsrc(gb + go, (valid && nt > 0) ? ((nt - 1) * hv + 1) * 4 : 0);
         s.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, goff, 0, 0));
-        const auto rk = make_rsrc(kb + jc * kq_step, valid ? kqn - jc * kq_step : 0);
-        const auto rq = make_rsrc(qb + jc * kq_step, valid ? kqn - jc * kq_step : 0);
+        const int64_t kqb = valid ? kqn - kqo : 0;
+        const auto rk = make_rsrc(kb + kqo, kqb);
+        const auto rq = make_rsrc(qb + kqo, kqb);
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm) s.kf[tm] = B::frag(rk, koff[tm]);
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm) s.qf[tm] = B::frag(rq, koff[tm]);
-        const auto rv = make_rsrc(vb + jc * v_step, valid ? vn - jc * v_step : 0);
+        const auto rv = make_rsrc(vb + vo, valid ? vn - vo : 0);
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt) s.v[jt] = B::quad(rv, voff[jt]);
-        const auto rt = make_rsrc(tb + jc * w_step, valid ? kChunk * kChunk * E : 0);
+        const int64_t wb = valid ? kChunk * kChunk * E : 0;
+        const auto rt = make_rsrc(tb + wo, wb);
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt)
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) s.tf[jt][kk] = B::frag(rt, toff[jt] + 32 * kk * E);
-        const auto rp = make_rsrc(pb + jc * w_step, valid ? kChunk * kChunk * E : 0);
+        const auto rp = make_rsrc(pb + wo, wb);
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt)
 #pragma unroll
@@ -816,12 +838,12 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_split_kernel(Prefill
     }
 
     const int64_t nchunks = (s1 - s0 + kChunk - 1) / kChunk;
-    auto chunk = [&](St& cur, int64_t j) {
+    // One chunk; `nxt` holds the next chunk's operands (its gates are
+    // prepared here, by wave 0, into the other parity buffer).
+    auto chunk = [&](St& cur, const St& nxt, int64_t j, int par) {
         const int64_t t0 = s0 + j * kChunk;
         const int nt = (int)((s1 - t0) < kChunk ? (s1 - t0) : kChunk);
-        // ---- gates, per wave: lane l has g_l
-        chunk_gates(cur.g, sm.gam[w], sm.dec[w]);
-        // ---- partial products over the d_k slice; K^T via identity
+        // ---- partial products over the d_k slice
         const frag Sb = Ops::pack(S[0], S[1]);
         f32x4 Xp[4], Yp[4];
 #pragma unroll
@@ -829,6 +851,13 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_split_kernel(Prefill
             Xp[tm] = Ops::mma(Sb, cur.kf[tm], zero4());
             Yp[tm] = Ops::mma(Sb, cur.qf[tm], zero4());
         }
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) {
+            sm.part[w][tm][l] = Xp[tm];
+            sm.part[w][4 + tm][l] = Yp[tm];
+        }
+        __syncthreads();                                                        // E1
+        // K^T in operand layout (exact identity product), off the critical path
         frag Ktf[2][2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
@@ -836,12 +865,6 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_split_kernel(Prefill
             for (int sub = 0; sub < 2; ++sub)
                 Ktf[sub][kk] = Ops::pack(Ops::mma(cur.kf[2 * kk], Iden[sub], zero4()),
                                          Ops::mma(cur.kf[2 * kk + 1], Iden[sub], zero4()));
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm) {
-            sm.part[w][tm][l] = Xp[tm];
-            sm.part[w][4 + tm][l] = Yp[tm];
-        }
-        __syncthreads();                                                        // E1
         f32x4 Y[TPW];
         float gt[TPW];
 #pragma unroll
@@ -854,19 +877,19 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_split_kernel(Prefill
                 X += sm.part[v2][tw][l];
                 Y[jt] += sm.part[v2][4 + tw][l];
             }
-            gt[jt] = sm.gam[w][16 * tw + r];
+            gt[jt] = sm.gam[par][16 * tw + r];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 sm.Rt[(4 * gq + i) * RLD + 16 * tw + r] = from_f32<OP>(to_f32(cur.v[jt][i]) - gt[jt] * X[i]);
         }
-        const float gn = sm.gam[w][kChunk];
+        const float gn = sm.gam[par][kChunk];
         __syncthreads();                                                        // E2
         const frag Rb0 = frag_nat(sm.Rt, RLD, r, 0), Rb1 = frag_nat(sm.Rt, RLD, r, 32);
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt) {
             const int tw = w + NWS * jt;
             const f32x4 U = Ops::mma(cur.tf[jt][1], Rb1, Ops::mma(cur.tf[jt][0], Rb0, zero4()));
-            const f32x4 dc = *reinterpret_cast<const f32x4*>(&sm.dec[w][16 * tw + 4 * gq]);
+            const f32x4 dc = *reinterpret_cast<const f32x4*>(&sm.dec[par][16 * tw + 4 * gq]);
             quad uq, dq;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -877,16 +900,22 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_split_kernel(Prefill
             *reinterpret_cast<quad*>(&sm.Dt[r * RLD + 16 * tw + 4 * gq]) = dq;
         }
         __syncthreads();                                                        // E3
-        const frag Ub0 = frag_nat(sm.Ut, RLD, r, 0), Ub1 = frag_nat(sm.Ut, RLD, r, 32);
+        // ---- S_w^T <- gamma_n S_w^T + K_w^T (D o U)   (the serial chain first)
         const frag Db0 = frag_rows(sm.Dt, RLD, r, 0), Db1 = frag_rows(sm.Dt, RLD, r, 32);
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+            S[sub] = Ops::mma(Ktf[sub][1], Db1, Ops::mma(Ktf[sub][0], Db0, gn * S[sub]));
+        // ---- O^T tiles: rows = columns 16 blk + 4 gq + i, column = token 16 tw + r
+        const frag Ub0 = frag_nat(sm.Ut, RLD, r, 0), Ub1 = frag_nat(sm.Ut, RLD, r, 32);
         f32x4 Ot[TPW];
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt)
             Ot[jt] = Ops::mma(Ub1, cur.pf[jt][1], Ops::mma(Ub0, cur.pf[jt][0], gt[jt] * Y[jt]));
+        // gates of the next chunk (read after the next E1 barrier)
+        if (w == 0) chunk_gates(nxt.g, sm.gam[par ^ 1], sm.dec[par ^ 1]);
         // this stage is free: fetch the chunk two steps ahead
         ctx.load(cur, j + 2, j + 2 < nchunks);
         {
-            // O^T: rows = columns 16 blk + 4 gq + i, column = token 16 tw + r;
             // rows past the end of the sequence fall outside the resource
             const auto ro = make_rsrc(static_cast<OP*>(a.out) + ((size_t)t0 * a.hv + h) * a.dv + blk * 16,
                                       ((int64_t)(nt - 1) * a.hv * a.dv + 16) * (int64_t)sizeof(OP));
@@ -898,10 +927,6 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_split_kernel(Prefill
                 B::store4(oq, ro, ctx.voff[jt]);
             }
         }
-        // ---- S_w^T <- gamma_n S_w^T + K_w^T (D o U)
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-            S[sub] = Ops::mma(Ktf[sub][1], Db1, Ops::mma(Ktf[sub][0], Db0, gn * S[sub]));
     };
 
     // Chunks are processed in pairs (stages A, B).  An odd count gets one
@@ -912,9 +937,10 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_split_kernel(Prefill
     St A, Bs;
     ctx.load(A, 0, nchunks > 0);
     ctx.load(Bs, 1, nchunks > 1);
+    if (w == 0) chunk_gates(A.g, sm.gam[0], sm.dec[0]);
     for (int64_t j = 0; j < nchunks; j += 2) {
-        chunk(A, j);
-        chunk(Bs, j + 1);
+        chunk(A, Bs, j, 0);
+        chunk(Bs, A, j + 1, 1);
     }
     if (a.final_state) {
         *reinterpret_cast<f32x4*>(a.final_state + srow) = S[0];

@@ -81,6 +81,62 @@ def measured_traffic(name, sources):
     return rec.get("bytes_per_call")
 
 
+CALIB_BYTES = 1 << 30      # bytes read and bytes written by the calibration kernel
+KERNELS = {"gdn_prefill": ("gdn_prep_kernel", "gdn_scan_split_kernel"), "gdn_decode": ("gdn_decode_kernel",)}
+
+
+def _pmc_per_dispatch(path, counter):
+    """{dispatch id: (kernel name, value in KiB)} for one counter of a rocprofv3 csv."""
+    import csv
+    out = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            d = int(row["Dispatch_Id"])
+            name, val = out.get(d, (row["Kernel_Name"], 0.0))
+            out[d] = (name, val + float(row["Counter_Value"]))
+    return out
+
+
+def write_traffic_summary(fetch_csv, write_csv):
+    """HBM bytes per call from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled
+    by what the same counter reads for the calibration kernel (1 GiB in, 1 GiB out)."""
+    fetch = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _pmc_per_dispatch(write_csv, "WRITE_SIZE")
+
+    def mean_of(table, pred):
+        v = [val for name, val in table.values() if pred(name)]
+        return (sum(v) / len(v) if v else None), len(v)
+
+    is_calib = lambda n: "neg_kernel" in n
+    cf, _ = mean_of(fetch, is_calib)
+    cw, _ = mean_of(write, is_calib)
+    if not cf or not cw:
+        raise SystemExit("calibration kernel (torch.neg) not found in the counter files")
+    sf, sw = CALIB_BYTES / (cf * 1024), CALIB_BYTES / (cw * 1024)
+    rec = {"calibration": {"kernel": "torch.neg fp32, 1 GiB read + 1 GiB written",
+                           "fetch_kib": cf, "write_kib": cw, "fetch_scale": sf, "write_scale": sw}}
+    for call, kernels in KERNELS.items():
+        per = {}
+        total = 0.0
+        for kn in kernels:
+            f, nf = mean_of(fetch, lambda n, kn=kn: kn in n)
+            w, nw = mean_of(write, lambda n, kn=kn: kn in n)
+            if f is None or w is None:
+                break
+            rb, wb = f * 1024 * sf, w * 1024 * sw
+            per[kn] = {"read_bytes": rb, "write_bytes": wb, "dispatches": min(nf, nw)}
+            total += rb + wb
+        else:
+            srcs = PREFILL_SOURCES if call == "gdn_prefill" else DECODE_SOURCES
+            rec[call] = {"bytes_per_call": total, "kernels": per, "source_sha": _sha(srcs)}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -90,7 +146,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=131072)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB -> 1 GiB elementwise kernel (torch.neg, fp32), the "
+                         "known-size reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) of a --calib-copy run into profiles/hbm_traffic.json")
     args = ap.parse_args()
+    if args.traffic_summary:
+        write_traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the GDN path here is single-GPU); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -211,6 +276,14 @@ def main():
                "sample": f"first {Ts} tokens of the T=262144, H=16, d=128 prefill (all 16 heads), "
                          f"fp64 sequential oracle, {cw:.1f}s wall"}
         log(f"cpu oracle: {Ts} tokens in {cw:.1f}s on {cpu['cores']} threads")
+
+    if args.calib_copy:
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     rec = {
         "metric": "GDN prefill tokens/sec (T=262144, H=16, d=128); decode state GB/s",

@@ -173,17 +173,19 @@ gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, con
     if (a.num_slots > INT32_MAX) return fail(GDN_ERROR_NOT_SUPPORTED, "too many chunks");
 
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int64_t half = gdn::prefill_workspace_bytes(a.num_slots, a.hv, bf16 ? 2 : 4) / 2;
+    const int64_t wbytes = gdn::prefill_workspace_bytes(a.num_slots, a.hv, bf16 ? 2 : 4);
+    const int64_t mbytes = a.num_slots * a.hv * gdn::prefill_matrix_bytes(bf16 ? 2 : 4);
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(GDN_ERROR_LAUNCH, "hipGetDevice failed");
     keep_pool_memory(dev);
     void* ws = nullptr;
-    if (hipMallocAsync(&ws, (size_t)(2 * half), st) != hipSuccess || !ws) {
+    if (hipMallocAsync(&ws, (size_t)wbytes, st) != hipSuccess || !ws) {
         (void)hipGetLastError();
-        return fail(GDN_ERROR_OUT_OF_MEMORY, "prefill workspace of %lld bytes", (long long)(2 * half));
+        return fail(GDN_ERROR_OUT_OF_MEMORY, "prefill workspace of %lld bytes", (long long)wbytes);
     }
     a.ws_t = ws;
-    a.ws_p = static_cast<char*>(ws) + half;
+    a.ws_p = static_cast<char*>(ws) + mbytes;
+    a.ws_g = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * mbytes);
     hipError_t e = gdn::launch_prefill(a, bf16, shape->head_dim_k, st);
     hipError_t ef = hipFreeAsync(ws, st);
     if (e == hipSuccess) e = ef;

@@ -37,13 +37,18 @@ struct PrefillArgs {
     int32_t hv;
     int32_t dv;
     int64_t num_slots;         // ceil(num_tokens / 64) + num_seqs
-    void* ws_t;                // [num_slots, hv, 64, 64] T~ = (I + A)^-1 diag(beta)
-    void* ws_p;                // [num_slots, hv, 64, 64] P = lower_incl(Gamma o Q K^T)
+    // Workspace written by the prep kernel and read by the scan, per (slot, value head):
+    void* ws_t;                // 64 x 64 T~ = (I + A)^-1 diag(beta), fragment-major order
+    void* ws_p;                // 64 x 64 P = lower_incl(Gamma o Q K^T), fragment-major order
+    float* ws_g;               // 64 pairs (G2_t, G2_last - G2_t): log2-scaled cumulative gates
 };
 
-// Workspace bytes for one prefill call (element size 2 for bf16, 4 for fp32).
+// Workspace bytes per (slot, value head) of each part (element size 2 for bf16, 4 for fp32).
+inline int64_t prefill_matrix_bytes(int elem_size) { return (int64_t)64 * 64 * elem_size; }
+inline int64_t prefill_gate_bytes() { return (int64_t)64 * 2 * 4; }
+// Workspace bytes for one prefill call: T~, P and the gates of every (slot, value head).
 inline int64_t prefill_workspace_bytes(int64_t num_slots, int hv, int elem_size) {
-    return num_slots * (int64_t)hv * 2 * 64 * 64 * elem_size;
+    return num_slots * (int64_t)hv * (2 * prefill_matrix_bytes(elem_size) + prefill_gate_bytes());
 }
 
 // Launchers: return hipSuccess or the launch error.  `bf16` selects the

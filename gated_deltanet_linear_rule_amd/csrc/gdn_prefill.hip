@@ -16,29 +16,24 @@
 //
 // Two kernels:
 //  * gdn_prep_kernel  -- one workgroup per (chunk, value head), all chunks in
-//    parallel: stages K and Q in LDS, the gate cumsum, Gamma-weighted K K^T and
-//    Q K^T on bf16 (or fp32) matrix cores, the unit-lower-triangular inverse
-//    in LDS (16x16 diagonal blocks by forward substitution, off-diagonal
-//    blocks by fp32 MFMA block products), and writes T~ and P to a workspace.
+//    parallel: stages K and Q in LDS, the gate cumsum (fp64), Gamma-weighted
+//    K K^T and Q K^T on bf16 (or fp32) matrix cores, the unit-lower-triangular
+//    inverse in LDS (16x16 diagonal blocks by forward substitution,
+//    off-diagonal blocks by fp32 MFMA block products), and writes T~, P (in
+//    the order the scan's operand fragments use) and the chunk's gates to a
+//    workspace.
 //  * gdn_scan_kernel  -- sequential over the chunks of one sequence, parallel
-//    over (sequence, value head, 16-column block of d_v): rows of S are
-//    independent, so each wave owns 16 rows of S (as S^T tiles in fp32
-//    accumulators: d_k x 16) for the whole sequence and never exchanges them.
-//    Per chunk a wave runs X = K S^T, Y = Q S^T, U = T~ R, O = gamma Y + P U
-//    and the state update on the matrix cores, with every intermediate kept in
-//    registers (accumulator tiles double as operand fragments, see
-//    gdn_device.h).  The workgroup's waves share one LDS copy of the chunk's
-//    K (row-major and transposed), Q, V columns, T~ and P; the global loads
-//    of chunk j+1 are issued before chunk j is computed so that their latency
-//    overlaps the matrix work, and outputs leave through LDS as 16-byte rows.
+//    over (sequence, value head, 16-column block of d_v); the d_k rows of the
+//    state block are split over the workgroup's waves and stay in fp32
+//    matrix-core accumulators for the whole sequence (details above the
+//    kernel).
 //
 // Exponentials use exp2 of log2-scaled cumulative gates (G2 = G log2 e).
-// Padding: a final partial chunk is padded with k = q = v = 0, g = 0,
-// beta = 0; padded rows then carry u = 0 and leave S and the real rows
-// untouched, and gamma_n = e^{G_63} equals the decay up to the last real token.
-// All global loads are unconditional with the row index clamped into the
-// sequence (the padding value is selected afterwards), so no load sits behind
-// a branch.
+// Padding: a final partial chunk is padded with k = q = 0, g = 0, beta = 0 in
+// the prep kernel; padded rows then carry u = 0 (their rows and columns of
+// T~ vanish), so they leave S and the real rows untouched whatever the scan
+// reads for them, and gamma_n = e^{G2_63} equals the decay up to the last
+// real token.
 #include <cstdlib>
 
 #include "gdn_device.h"
@@ -86,17 +81,6 @@ __device__ __forceinline__ bool locate_slot(const SeqIndex& si, int nseq, int64_
     return t0 < s1;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ float wave_cumsum(float x) {
-    const int l = lane_id();
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        float y = __shfl_up(x, off, kWave);
-        if (l >= off) x += y;
-    }
-    return x;
-}
-
 // Lane shuffle of a double by a DPP control (two 32-bit halves); lanes whose
 // source is outside the pattern (or whose row is masked off) read 0.
 template <int CTRL, int ROW_MASK>
@@ -127,18 +111,30 @@ __device__ __forceinline__ double lane63_f64(double x) {
     return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned)lo);
 }
 
-// Gates of one chunk, computed by one wave: lane l holds g_l (0 past the end
-// of the sequence).  With G_t = g_1 + ... + g_t accumulated in fp64 (so that
-// differences of nearby prefix sums keep full fp32 accuracy), writes
-// gam[t] = e^{G_t}, dec[t] = e^{G_last - G_t} and gam[64] = e^{G_last}.
-__device__ __forceinline__ void chunk_gates(float g, float* gam, float* dec) {
-    const int l = lane_id();
-    const double G = wave_cumsum_f64((double)g * 1.4426950408889634);
-    const double Gl = lane63_f64(G);
-    gam[l] = fast_exp2((float)G);
-    dec[l] = fast_exp2((float)(Gl - G));
-    if (l == 0) gam[kChunk] = fast_exp2((float)Gl);
-}
+// ===========================================================================
+// workspace layout shared by the two kernels
+// ===========================================================================
+// T~ and P of one (chunk, value head) are stored fragment-major: 16-byte unit
+//     e = ((tw * 2 + kk) * FU + u) * 64 + lane
+// holds row 16 tw + (lane & 15), columns 32 kk + 8 (lane >> 4) + VE u .. + VE
+// of the 64 x 64 matrix, i.e. unit u of the scan's operand fragment (tw, kk)
+// for that lane, so a wave reads a fragment as one contiguous 1 KB block.
+// The gates of a chunk are 64 float pairs (G2_t, G2_last - G2_t), the
+// difference taken in fp64; zeros (what a read past the end returns) stand
+// for a chunk without decay.
+template <typename OP> struct FragMajor {
+    static constexpr int VE = 16 / (int)sizeof(OP);      // elements per 16-byte unit
+    static constexpr int FU = 8 / VE;                    // units per operand fragment
+    static constexpr int UNITS = kChunk * kChunk / VE;
+    __device__ __forceinline__ static int row(int e) {
+        return 16 * (((e >> 6) / FU) >> 1) + (e & 15);
+    }
+    __device__ __forceinline__ static int col(int e) {
+        const int rest = e >> 6;
+        return 32 * ((rest / FU) & 1) + 8 * ((e >> 4) & 3) + VE * (rest % FU);
+    }
+};
+constexpr int kGateFloats = 2 * kChunk;   // floats per (chunk, value head)
 
 // ===========================================================================
 // prep: T~ and P for one (chunk, value head)
@@ -163,7 +159,6 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
     constexpr int LD = Sm::LD, LDP = Sm::LDP;
     constexpr int VE = 16 / (int)sizeof(OP);      // elements per 16-byte vector
     constexpr int NV = DK / VE;                    // vectors per K/Q row
-    constexpr int MV = kChunk / VE;                // vectors per T~/P row
     __shared__ Sm sm;
 
     const int64_t slot = blockIdx.x;
@@ -193,8 +188,12 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
         float gv = a.g[(size_t)(t0 + lc) * a.hv + h];
         float bv = a.beta[(size_t)(t0 + lc) * a.hv + h];
         if (l >= nt) { gv = 0.f; bv = 0.f; }
-        sm.G[l] = wave_cumsum_f64((double)gv * 1.4426950408889634);
+        const double G = wave_cumsum_f64((double)gv * 1.4426950408889634);
+        sm.G[l] = G;
         sm.B[l] = bv;
+        const double Gl = lane63_f64(G);
+        reinterpret_cast<f32x2*>(a.ws_g + ((size_t)slot * a.hv + h) * kGateFloats)[l] =
+            f32x2{(float)G, (float)(Gl - G)};
     }
     __syncthreads();
 
@@ -279,386 +278,100 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
     }
     __syncthreads();
 
-    // ---- coalesced 16-byte stores of T~ and P
+    // ---- T~ and P to the workspace, fragment-major, consecutive lanes on
+    // consecutive 16-byte units
+    using FM = FragMajor<OP>;
     OP* Pw = static_cast<OP*>(a.ws_p) + ((size_t)slot * a.hv + h) * (kChunk * kChunk);
     OP* Tw = static_cast<OP*>(a.ws_t) + ((size_t)slot * a.hv + h) * (kChunk * kChunk);
-    for (int e = tid; e < kChunk * MV; e += kPrepThreads) {
-        const int row = e / MV, cv = e - row * MV;
-        *reinterpret_cast<u32x4*>(Tw + row * kChunk + cv * VE) = ld16(Tl + row * LDP + cv * VE);
-        *reinterpret_cast<u32x4*>(Pw + row * kChunk + cv * VE) = ld16(Pl + row * LDP + cv * VE);
+    for (int e = tid; e < FM::UNITS; e += kPrepThreads) {
+        const int row = FM::row(e), col = FM::col(e);
+        *reinterpret_cast<u32x4*>(Tw + e * VE) = ld16(Tl + row * LDP + col);
+        *reinterpret_cast<u32x4*>(Pw + e * VE) = ld16(Pl + row * LDP + col);
     }
 }
 
 // ===========================================================================
-// scan: sequential over chunks, 16 state rows per wave
+// scan: sequential over the chunks of one sequence
 // ===========================================================================
-template <typename OP, int DK, int NW>
-struct ScanSmem {
-    static constexpr int PAD = pad_elems<OP>();
-    static constexpr int LD = DK + PAD;          // K, Q rows (token-major)
-    static constexpr int LDT = kChunk + PAD;     // K^T rows (d_k-major), T~ and P rows
-    static constexpr int LDV = 16 * NW + PAD;    // V and O rows (this workgroup's columns)
-    alignas(16) OP K[kChunk * LD];
-    alignas(16) OP Q[kChunk * LD];
-    alignas(16) OP Kt[DK * LDT];
-    alignas(16) OP T[kChunk * LDT];
-    alignas(16) OP P[kChunk * LDT];
-    alignas(16) OP V[kChunk * LDV];
-    alignas(16) OP O[kChunk * LDV];
-    alignas(16) float gam[kChunk + 4];           // e^{G_t}; [64] = e^{G_last}
-    alignas(16) float dec[kChunk];               // e^{G_last - G_t}
-};
-
-// Per-thread register staging of one chunk's inputs (16-byte vectors).
-template <typename OP, int DK, int NW>
-struct ScanStage {
-    static constexpr int NT = NW * kWave;
-    static constexpr int VE = 16 / (int)sizeof(OP);
-    static constexpr int NV = DK / VE;                       // vectors per K/Q row
-    static constexpr int KTASKS = (kChunk / 4) * NV;         // 4 tokens x 1 vector
-    static constexpr int KT = (KTASKS + NT - 1) / NT;
-    static constexpr int QTASKS = kChunk * NV;
-    static constexpr int QT = (QTASKS + NT - 1) / NT;
-    static constexpr int VV = 16 * NW / VE;                  // vectors per V/O row
-    static constexpr int VTASKS = kChunk * VV;
-    static constexpr int VT = (VTASKS + NT - 1) / NT;
-    static constexpr int MV = kChunk / VE;                   // vectors per T~/P row
-    static constexpr int MTASKS = kChunk * MV;
-    static constexpr int MT = (MTASKS + NT - 1) / NT;
-    u32x4 k[KT][4];
-    u32x4 q[QT];
-    u32x4 v[VT];
-    u32x4 t[MT];
-    u32x4 p[MT];
-    float g;
-    int nt;   // valid rows; padding is applied when the stage is committed
-};
-
-template <typename OP, int DK, int NW>
-struct ScanCtx {
-    using St = ScanStage<OP, DK, NW>;
-    const OP* kg;
-    const OP* qg;
-    const OP* vg;
-    const float* gg;
-    const OP* tws;
-    const OP* pws;
-    int hqk, hv, dv, hq, h, col0;
-
-    // Issue the global loads of the chunk starting at t0 (nt >= 1 tokens).
-    __device__ __forceinline__ void load(St& s, int64_t t0, int nt, int64_t slot) const {
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < St::KT; ++i) {
-            const int e = tid + i * St::NT;
-            if (St::KTASKS % St::NT == 0 || e < St::KTASKS) {
-                const int rq = e % (kChunk / 4), cv = e / (kChunk / 4);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int row = 4 * rq + j;
-                    const int rc = row < nt ? row : nt - 1;
-                    s.k[i][j] = ld16(kg + ((size_t)(t0 + rc) * hqk + hq) * DK + (size_t)cv * St::VE);
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < St::QT; ++i) {
-            const int e = tid + i * St::NT;
-            if (St::QTASKS % St::NT == 0 || e < St::QTASKS) {
-                const int row = e / St::NV, cv = e - row * St::NV;
-                const int rc = row < nt ? row : nt - 1;
-                s.q[i] = ld16(qg + ((size_t)(t0 + rc) * hqk + hq) * DK + (size_t)cv * St::VE);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < St::VT; ++i) {
-            const int e = tid + i * St::NT;
-            if (St::VTASKS % St::NT == 0 || e < St::VTASKS) {
-                const int row = e / St::VV, cv = e - row * St::VV;
-                const int rc = row < nt ? row : nt - 1;
-                s.v[i] = ld16(vg + ((size_t)(t0 + rc) * hv + h) * dv + col0 + cv * St::VE);
-            }
-        }
-        const OP* tw = tws + ((size_t)slot * hv + h) * (kChunk * kChunk);
-        const OP* pw = pws + ((size_t)slot * hv + h) * (kChunk * kChunk);
-#pragma unroll
-        for (int i = 0; i < St::MT; ++i) {
-            const int e = tid + i * St::NT;
-            if (St::MTASKS % St::NT == 0 || e < St::MTASKS) {
-                s.t[i] = ld16(tw + (size_t)e * St::VE);
-                s.p[i] = ld16(pw + (size_t)e * St::VE);
-            }
-        }
-        if (wave_id() == 0) {
-            const int l = lane_id();
-            const int lc = l < nt ? l : nt - 1;
-            s.g = gg[(size_t)(t0 + lc) * hv + h];
-        }
-        s.nt = nt;
-    }
-
-    // Write a staged chunk into LDS (K row-major and transposed, Q, V, T~, P, G).
-    __device__ __forceinline__ void commit(const St& s, ScanSmem<OP, DK, NW>& sm) const {
-        using SS = ScanSmem<OP, DK, NW>;
-        using vecE = typename VecE<OP>::type;
-        using quad = typename Op<OP>::quad;
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < St::KT; ++i) {
-            const int e = tid + i * St::NT;
-            if (St::KTASKS % St::NT == 0 || e < St::KTASKS) {
-                const int rq = e % (kChunk / 4), cv = e / (kChunk / 4);
-                u32x4 kv[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    kv[j] = (4 * rq + j) < s.nt ? s.k[i][j] : zero_u4();
-                    *reinterpret_cast<u32x4*>(&sm.K[(4 * rq + j) * SS::LD + cv * St::VE]) = kv[j];
-                }
-#pragma unroll
-                for (int e2 = 0; e2 < St::VE; ++e2) {
-                    quad col;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) col[j] = __builtin_bit_cast(vecE, kv[j])[e2];
-                    *reinterpret_cast<quad*>(&sm.Kt[(cv * St::VE + e2) * SS::LDT + 4 * rq]) = col;
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < St::QT; ++i) {
-            const int e = tid + i * St::NT;
-            if (St::QTASKS % St::NT == 0 || e < St::QTASKS) {
-                const int row = e / St::NV, cv = e - row * St::NV;
-                *reinterpret_cast<u32x4*>(&sm.Q[row * SS::LD + cv * St::VE]) = row < s.nt ? s.q[i] : zero_u4();
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < St::VT; ++i) {
-            const int e = tid + i * St::NT;
-            if (St::VTASKS % St::NT == 0 || e < St::VTASKS) {
-                const int row = e / St::VV, cv = e - row * St::VV;
-                *reinterpret_cast<u32x4*>(&sm.V[row * SS::LDV + cv * St::VE]) = row < s.nt ? s.v[i] : zero_u4();
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < St::MT; ++i) {
-            const int e = tid + i * St::NT;
-            if (St::MTASKS % St::NT == 0 || e < St::MTASKS) {
-                const int row = e / St::MV, cv = e - row * St::MV;
-                *reinterpret_cast<u32x4*>(&sm.T[row * SS::LDT + cv * St::VE]) = s.t[i];
-                *reinterpret_cast<u32x4*>(&sm.P[row * SS::LDT + cv * St::VE]) = s.p[i];
-            }
-        }
-        if (wave_id() == 0) chunk_gates(lane_id() < s.nt ? s.g : 0.f, sm.gam, sm.dec);
-    }
-
-    // 16-byte stores of the O rows of a finished chunk (rows < nt).
-    __device__ __forceinline__ void store_out(const ScanSmem<OP, DK, NW>& sm, OP* og, int64_t t0, int nt) const {
-        using SS = ScanSmem<OP, DK, NW>;
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < St::VT; ++i) {
-            const int e = tid + i * St::NT;
-            if (St::VTASKS % St::NT == 0 || e < St::VTASKS) {
-                const int row = e / St::VV, cv = e - row * St::VV;
-                if (row < nt)
-                    *reinterpret_cast<u32x4*>(og + ((size_t)(t0 + row) * hv + h) * dv + col0 + cv * St::VE) =
-                        ld16(&sm.O[row * SS::LDV + cv * St::VE]);
-            }
-        }
-    }
-};
-
-template <typename OP, int DK, int NW, bool PREFETCH>
-__global__ __launch_bounds__(NW * kWave) void gdn_scan_kernel(PrefillArgs a) {
-    using Ops = Op<OP>;
-    using frag = typename Ops::frag;
-    using SS = ScanSmem<OP, DK, NW>;
-    using St = ScanStage<OP, DK, NW>;
-    constexpr int LD = SS::LD, LDT = SS::LDT, LDV = SS::LDV;
-    constexpr int NTI = DK / 16;   // S^T tiles along d_k
-    __shared__ SS sm;
-
-    const int chain = blockIdx.x;
-    const int n = chain / a.hv;
-    const int h = chain - n * a.hv;
-    const int l = lane_id(), w = wave_id(), r = l & 15, gq = l >> 4;
-    const int col0 = blockIdx.y * NW * 16;                  // workgroup's first d_v column
-    const int cl = w * 16 + r;                               // this lane's column within the workgroup
-    const int c = col0 + cl;                                 // this lane's d_v column
-
-    ScanCtx<OP, DK, NW> ctx{static_cast<const OP*>(a.k), static_cast<const OP*>(a.q),
-                            static_cast<const OP*>(a.v), a.g,
-                            static_cast<const OP*>(a.ws_t), static_cast<const OP*>(a.ws_p),
-                            a.hqk, a.hv, a.dv, (h * a.hqk) / a.hv, h, col0};
-    OP* og = static_cast<OP*>(a.out);
-
-    const SeqIndex si{a.cu, a.seqlen};
-    const int64_t s0 = si.start(n), s1 = si.start(n + 1);
-    const int64_t base = slot_base(s0, n);
-
-    // S^T tiles: St[ti] holds S[c][16 ti + 4 gq + i], i = 0..3
-    f32x4 S[NTI];
-    const size_t srow = ((size_t)chain * a.dv + c) * DK;
-    if (a.init_state) {
-#pragma unroll
-        for (int ti = 0; ti < NTI; ++ti) S[ti] = *reinterpret_cast<const f32x4*>(a.init_state + srow + 16 * ti + 4 * gq);
-    } else {
-#pragma unroll
-        for (int ti = 0; ti < NTI; ++ti) S[ti] = zero4();
-    }
-
-    St stage;
-    if (PREFETCH && s0 < s1) ctx.load(stage, s0, (int)((s1 - s0) < kChunk ? (s1 - s0) : kChunk), base);
-
-    int64_t prev_t0 = 0;
-    int prev_nt = 0;
-    int64_t slot = base;
-    for (int64_t t0 = s0; t0 < s1; t0 += kChunk, ++slot) {
-        const int nt = (int)((s1 - t0) < kChunk ? (s1 - t0) : kChunk);
-        __syncthreads();                       // LDS of the previous chunk is free, its O rows complete
-        if (prev_nt > 0) ctx.store_out(sm, og, prev_t0, prev_nt);
-        if (!PREFETCH) ctx.load(stage, t0, nt, slot);
-        ctx.commit(stage, sm);
-        __syncthreads();
-        if (PREFETCH && t0 + kChunk < s1) {
-            const int64_t rem = s1 - t0 - kChunk;
-            ctx.load(stage, t0 + kChunk, (int)(rem < kChunk ? rem : kChunk), slot + 1);
-        }
-
-        // ---- X = K S^T, Y = Q S^T (64 tokens x 16 columns)
-        frag Sb[DK / 32];
-#pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) Sb[kk] = Ops::pack(S[2 * kk], S[2 * kk + 1]);
-        f32x4 X[4], Y[4];
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm) { X[tm] = zero4(); Y[tm] = zero4(); }
-#pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) {
-            frag kf[4], qf[4];
-#pragma unroll
-            for (int tm = 0; tm < 4; ++tm) {
-                kf[tm] = frag_rows(sm.K, LD, 16 * tm + r, 32 * kk);
-                qf[tm] = frag_rows(sm.Q, LD, 16 * tm + r, 32 * kk);
-            }
-#pragma unroll
-            for (int tm = 0; tm < 4; ++tm) {
-                X[tm] = Ops::mma(kf[tm], Sb[kk], X[tm]);
-                Y[tm] = Ops::mma(qf[tm], Sb[kk], Y[tm]);
-            }
-        }
-        // ---- gates for this lane's rows
-        f32x4 gam[4], dec[4];
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm) {
-            gam[tm] = *reinterpret_cast<const f32x4*>(&sm.gam[16 * tm + 4 * gq]);
-            dec[tm] = *reinterpret_cast<const f32x4*>(&sm.dec[16 * tm + 4 * gq]);
-        }
-        // ---- R = V - diag(gamma) X
-        f32x4 R[4];
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                R[tm][i] = to_f32(sm.V[(16 * tm + 4 * gq + i) * LDV + cl]) - gam[tm][i] * X[tm][i];
-        // ---- U = T~ R (T~ lower triangular: skip zero K steps)
-        const frag Rb0 = Ops::pack(R[0], R[1]), Rb1 = Ops::pack(R[2], R[3]);
-        f32x4 U[4];
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm) {
-            U[tm] = Ops::mma(frag_rows(sm.T, LDT, 16 * tm + r, 0), Rb0, zero4());
-            if (tm >= 2) U[tm] = Ops::mma(frag_rows(sm.T, LDT, 16 * tm + r, 32), Rb1, U[tm]);
-        }
-        // ---- O = diag(gamma) Y + P U  (staged in LDS for 16-byte stores)
-        const frag Ub0 = Ops::pack(U[0], U[1]), Ub1 = Ops::pack(U[2], U[3]);
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm) {
-            f32x4 O = gam[tm] * Y[tm];
-            O = Ops::mma(frag_rows(sm.P, LDT, 16 * tm + r, 0), Ub0, O);
-            if (tm >= 2) O = Ops::mma(frag_rows(sm.P, LDT, 16 * tm + r, 32), Ub1, O);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm.O[(16 * tm + 4 * gq + i) * LDV + cl] = from_f32<OP>(O[i]);
-        }
-        // ---- S^T <- gamma_n S^T + K^T diag(e^{G_n - G}) U
-        f32x4 UD[4];
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm) UD[tm] = U[tm] * dec[tm];
-        const frag Db0 = Ops::pack(UD[0], UD[1]), Db1 = Ops::pack(UD[2], UD[3]);
-        const float gl = sm.gam[kChunk];
-#pragma unroll
-        for (int ti = 0; ti < NTI; ++ti) {
-            f32x4 acc = gl * S[ti];
-            acc = Ops::mma(frag_rows(sm.Kt, LDT, 16 * ti + r, 0), Db0, acc);
-            S[ti] = Ops::mma(frag_rows(sm.Kt, LDT, 16 * ti + r, 32), Db1, acc);
-        }
-        prev_t0 = t0;
-        prev_nt = nt;
-    }
-    __syncthreads();
-    if (prev_nt > 0) ctx.store_out(sm, og, prev_t0, prev_nt);
-    if (a.final_state) {
-#pragma unroll
-        for (int ti = 0; ti < NTI; ++ti)
-            *reinterpret_cast<f32x4*>(a.final_state + srow + 16 * ti + 4 * gq) = S[ti];
-    }
-}
-
-
-// ===========================================================================
-// split scan: one workgroup per (sequence, value head, 16-column block of d_v);
-// its NWS = DK/32 waves split d_k, wave w owning state rows S[:, 32w .. 32w+32)
-// as two fp32 accumulator tiles (d_k x 16).  Inside the slice the d_k order
-// of the tiles is permuted (tile `sub`, row 4 gq + i  <->  d_k 8 gq + 4 sub + i)
-// so that an operand fragment of K or Q is one contiguous 16-byte load.
-// Wave w also owns token tiles tw = w + NWS j (j < TPW = 4 / NWS).  Per chunk:
-//   wave w:  Xp^T = S_w K_w^T,  Yp^T = S_w Q_w^T          (partial over d_k)
+// One workgroup per (sequence, value head, 16-column block of d_v).  Its
+// NWS = DK / 32 waves split d_k: wave w owns state rows S[:, 32w .. 32w+32)
+// as two fp32 accumulator tiles (d_k x 16).  Inside the slice the d_k order of
+// the tiles is permuted (tile `sub`, row 4 gq + i  <->  d_k 8 gq + 4 sub + i)
+// so that an operand fragment of K or Q is one contiguous 16-byte piece.
+// Wave w also owns token tiles tw = w + NWS jt (jt < TPW = 4 / NWS).  Per chunk:
+//   wave w:  X_w^T = S_w K_w^T,  Y_w^T = S_w Q_w^T          (partial over d_k)
+//   E1 (LDS): X partials -> the owner of token tile tw sums X^T there
+//   owner:   R^T = V^T - X^T diag(gamma)
 //            K_w^T in operand layout via an exact identity product
-//   E1 (LDS): partial sums -> owner of token tile tw holds X^T and Y^T there
-//   owner:   R^T = V^T - X^T diag(gamma)        (one 8-byte V load per lane)
-//   E2 (LDS): R for all tokens to every wave
-//   owner:   U = T~_tw R,  D o U
+//   E2 (LDS): R for all tokens to every wave, Y partials to the owners
+//   owner:   U = T~_tw R,  D o U  (D = e^{G_last - G_t} per token)
 //   E3 (LDS): U and D o U for all tokens to every wave
-//   owner:   O^T = Y^T diag(gamma) + U^T P_tw^T  (one 8-byte store per lane)
 //   wave w:  S_w^T <- gamma_n S_w^T + K_w^T (D o U)
-// Loads come from buffer resources two chunks ahead of use (two register
-// stages), with no load, store or use of a loaded value behind a branch, so
-// the compiler's memory-counter waits stay exact.  Padded rows of a partial
-// last chunk need no zeroing: the prep kernel padded K with zero rows and beta
-// with zeros, so those rows carry u = 0 exactly.
-// ===========================================================================
+//   owner:   O^T = Y^T diag(gamma) + U^T P_tw^T
+//
+// Global memory.  The vector memory path serves a wave request four lanes at
+// a time, and four lanes on four different rows cost four times as much as
+// four lanes on one 64-byte piece, so every access here keeps consecutive
+// lanes on consecutive bytes:
+//  * K and Q of the wave's d_k slice are read row by row (four lanes per
+//    row) and turned into operand fragments through a wave-private LDS area;
+//  * V and O take the same route through a small wave-private area;
+//  * T~ and P arrive fragment-major from the prep kernel, one 1 KB block per
+//    fragment;
+//  * the gates arrive as one 512-byte record per chunk.
+// K, Q and the gates are fetched two chunks before their chunk and moved into
+// LDS one chunk before it; V, T~ and P are fetched about two chunks ahead
+// into registers.  All loads go through buffer resources (reads past the end
+// of a resource return 0, writes past it are dropped), and no load, store or
+// use of a loaded value sits behind a branch, so the compiler's memory-counter
+// waits stay exact.
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-// Buffer resource over [base, base + bytes): loads past the end read 0 and
-// stores past the end are dropped by the hardware.
+// Buffer resource over [base, base + bytes).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
     const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 
+__device__ __forceinline__ u32x4 buf_b128(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 template <typename OP> struct Buf;
 template <> struct Buf<__bf16> {
-    __device__ __forceinline__ static bf16x8 frag(__amdgpu_buffer_rsrc_t r, unsigned off) {
-        return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    // operand fragment: one 16-byte unit
+    __device__ __forceinline__ static bf16x8 frag(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+        return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
     }
-    __device__ __forceinline__ static bf16x4 quad(__amdgpu_buffer_rsrc_t r, unsigned off) {
-        return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    __device__ __forceinline__ static bf16x4 quad(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+        return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
     }
-    __device__ __forceinline__ static void store4(bf16x4 x, __amdgpu_buffer_rsrc_t r, unsigned off) {
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, x), r, off, 0, 0);
+    __device__ __forceinline__ static void store4(bf16x4 x, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, x), r, voff, soff, 0);
+    }
+    // operand fragment from LDS (16-byte unit offsets of its two halves)
+    __device__ __forceinline__ static bf16x8 lds_frag(const char* base, unsigned off0, unsigned) {
+        return *reinterpret_cast<const bf16x8*>(base + off0);
     }
 };
 template <> struct Buf<float> {
-    __device__ __forceinline__ static f32x8 frag(__amdgpu_buffer_rsrc_t r, unsigned off) {
-        const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-        const i32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
-        return __builtin_bit_cast(f32x8, i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    // operand fragment: two units, the second 1 KB after the first
+    __device__ __forceinline__ static f32x8 frag(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+        const f32x4 lo = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+        const f32x4 hi = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 1024, 0));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
-    __device__ __forceinline__ static f32x4 quad(__amdgpu_buffer_rsrc_t r, unsigned off) {
-        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    __device__ __forceinline__ static f32x4 quad(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
     }
-    __device__ __forceinline__ static void store4(f32x4 x, __amdgpu_buffer_rsrc_t r, unsigned off) {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, off, 0, 0);
+    __device__ __forceinline__ static void store4(f32x4 x, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, voff, soff, 0);
+    }
+    __device__ __forceinline__ static f32x8 lds_frag(const char* base, unsigned off0, unsigned off1) {
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(base + off0);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(base + off1);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
 };
 
@@ -669,57 +382,94 @@ __device__ __forceinline__ typename Op<T>::frag frag_nat(const T* M, int ld, int
     return *reinterpret_cast<const frag*>(M + (size_t)row * ld + k0 + 8 * (lane_id() >> 4));
 }
 
-template <typename OP, int TPW>
-struct SplitStage {
+// XOR swizzles of the wave-private staging areas: the unit (16 bytes, or a
+// 4-element quad for V/O) index inside a row is XORed with a function of the
+// row, so that both the row-wise writes (consecutive lanes along a row) and
+// the fragment reads (consecutive lanes down a column) spread over the banks.
+__device__ __forceinline__ int swz_kq(int row, int units) {
+    return units == 4 ? (((row >> 1) ^ (row >> 3)) & 3) : ((row ^ (row >> 3)) & 7);
+}
+__device__ __forceinline__ int swz_vo(int row, int elem) {
+    return elem == 2 ? ((row >> 2) & 3) : (((row >> 1) ^ (row >> 3)) & 3);
+}
+
+// Orders this wave's LDS writes before its later LDS reads of the same area.
+// LDS executes one wave's operations in issue order; the fence only keeps the
+// compiler from moving them.
+__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
+template <typename OP, int DK>
+struct ScanGeom {
+    static constexpr int NWS = DK / 32;                 // waves per workgroup (d_k split)
+    static constexpr int TPW = 4 / NWS;                 // token tiles per wave
+    static constexpr int E = (int)sizeof(OP);
+    static constexpr int SEGS = 32 * E / 16;            // 16-byte units per row of a wave's K slice
+    static constexpr int RPI = kWave / SEGS;            // rows per row-wise load
+    static constexpr int KU = kChunk / RPI;             // row-wise loads per tensor and chunk
+    static constexpr int FU = 8 * E / 16;               // 16-byte units per operand fragment
+    static constexpr int ROWB = SEGS * 16;              // bytes per staged K/Q row
+    static constexpr int KQB = kChunk * ROWB;           // bytes of a wave's K (or Q) slice of a chunk
+    static constexpr int QE = 4 * E;                    // bytes per V/O quad
+    static constexpr int VROWB = 16 * E;                // bytes per V/O tile row
+    static constexpr int VB = 16 * VROWB;               // bytes per V/O tile
+    static constexpr int RLD = kChunk + (E == 2 ? 8 : 4);   // 16-byte rows, staggered banks
+};
+
+template <typename OP, int DK>
+struct ScanSmem {
+    using G = ScanGeom<OP, DK>;
+    f32x4 part[G::NWS][8][kWave];        // X^T partials (0..3) and Y^T partials (4..7)
+    alignas(16) OP Rt[16 * G::RLD];      // R as [column][token]
+    alignas(16) OP Ut[16 * G::RLD];      // U as [column][token]
+    alignas(16) OP Dt[16 * G::RLD];      // D o U as [column][token]
+    alignas(16) float gam[2][kChunk];    // by chunk parity: e^{G_t}
+    alignas(16) float dec[2][kChunk];    //                  e^{G_last - G_t}
+    alignas(16) char kst[G::NWS][G::KQB];          // wave-private: K slice of the next chunk
+    alignas(16) char qst[G::NWS][G::KQB];          //               Q slice
+    alignas(16) char vst[G::NWS][G::TPW][G::VB];   //               V / O tiles
+};
+
+template <typename OP, int DK>
+struct ScanCtx {
+    using G = ScanGeom<OP, DK>;
+    using B = Buf<OP>;
     using frag = typename Op<OP>::frag;
     using quad = typename Op<OP>::quad;
-    frag kf[4];          // K[16 tm + r][32 w + 8 gq + (0..7)]
-    frag qf[4];          // Q, same positions
-    frag tf[TPW][2];     // T~[16 tw + r][32 kk + 8 gq + (0..7)]
-    frag pf[TPW][2];     // P, same positions
-    quad v[TPW];         // V[16 tw + r][16 blk + 4 gq + (0..3)]
-    float g;             // g of token `lane` (0 past the end of the sequence)
-};
+    static constexpr int NWS = G::NWS, TPW = G::TPW, E = G::E, KU = G::KU, RPI = G::RPI, FU = G::FU;
+    // K and Q slices (row-wise) and gates of one chunk
+    struct KQG {
+        u32x4 k[KU];
+        u32x4 q[KU];
+        f32x2 gate;          // (G2_l, G2_last - G2_l) of token `lane`
+    };
+    // V tiles (row-wise) and T~ / P fragments of one chunk
+    struct VTP {
+        quad v[TPW];         // V[16 tw + (l >> 2)][16 blk + 4 (l & 3) + (0..3)]
+        frag t[TPW][2];      // T~[16 tw + r][32 kk + 8 gq + (0..7)]
+        frag p[TPW][2];      // P, same positions
+    };
 
-template <typename OP, int DK>
-struct SplitSmem {
-    static constexpr int NWS = DK / 32;
-    static constexpr int RLD = kChunk + (sizeof(OP) == 2 ? 8 : 4);   // 16-byte rows, staggered banks
-    f32x4 part[NWS][8][kWave];          // E1: X^T partials (0..3) and Y^T partials (4..7)
-    alignas(16) OP Rt[16 * RLD];        // E2: R as [column][token]
-    alignas(16) OP Ut[16 * RLD];        // E3: U as [column][token]
-    alignas(16) OP Dt[16 * RLD];        // E3: D o U as [column][token]
-    alignas(16) float gam[2][kChunk + 4];   // gates by chunk parity: e^{G_t}, [64] = e^{G_last}
-    alignas(16) float dec[2][kChunk];       // e^{G_last - G_t}
-};
-
-template <typename OP, int DK>
-struct SplitCtx {
-    static constexpr int NWS = DK / 32, TPW = 4 / NWS;
-    static constexpr int E = (int)sizeof(OP);
-    using St = SplitStage<OP, TPW>;
-    using B = Buf<OP>;
-    // per-sequence scalars: byte address of the sequence's first chunk in each
-    // tensor and the bytes from there to the end of the tensor
+    // per-sequence: byte address of the sequence's first chunk in each tensor
+    // and the bytes from there to the end of the tensor
     const char* kb; const char* qb; int64_t kqn;
     const char* vb; int64_t vn;
-    const char* gb;
-    const char* tb;
-    const char* pb;
-    int64_t kq_step, v_step, g_step, w_step;   // bytes per chunk step
-    int64_t seq_tokens;
-    int hv;
-    // loop-invariant per-lane byte offsets
-    unsigned koff[4];      // ((16 tm + r) * hqk * DK + 8 gq) * E
-    unsigned voff[TPW];    // ((16 tw + r) * hv * dv + 4 gq) * E
-    unsigned toff[TPW];    // ((16 tw + r) * 64 + 8 gq) * E
-    unsigned goff;         // lane * hv * 4
+    const char* tb; const char* pb; const char* gb;
+    int64_t kq_step, v_step, w_step, g_step;   // bytes per chunk step
+    int kq_row, v_row;                          // bytes per token row
+    int w;
+    // Loop-invariant per-lane byte offsets.  Row offsets that a bounds check
+    // must see stay in the per-lane offset (the scalar offset only ever
+    // carries fragment-block offsets inside a fully valid T~/P block).
+    unsigned kq_voff[KU];   // row-wise K/Q load i: row RPI i + l / SEGS, unit l % SEGS
+    unsigned v_voff[TPW];   // row-wise V/O of tile tw: row 16 tw + (l >> 2), quad l & 3
+    unsigned f_voff;        // fragment-major T~/P: unit `lane`
+    unsigned g_voff;        // gate pair of token `lane`
 
-    __device__ __forceinline__ void init(const PrefillArgs& a, int64_t s0, int64_t s1, int64_t base, int h,
-                                         int blk, int w) {
-        const int l = lane_id(), r = l & 15, gq = l >> 4;
+    __device__ __forceinline__ void init(const PrefillArgs& a, int64_t s0, int64_t base, int h, int blk,
+                                         int wave) {
+        const int l = lane_id();
         const int hq = (h * a.hqk) / a.hv;
-        hv = a.hv;
+        w = wave;
         const size_t kq0 = ((size_t)s0 * a.hqk + hq) * DK + 32 * w;
         kb = reinterpret_cast<const char*>(static_cast<const OP*>(a.k) + kq0);
         qb = reinterpret_cast<const char*>(static_cast<const OP*>(a.q) + kq0);
@@ -727,70 +477,76 @@ struct SplitCtx {
         const size_t v0 = ((size_t)s0 * a.hv + h) * a.dv + blk * 16;
         vb = reinterpret_cast<const char*>(static_cast<const OP*>(a.v) + v0);
         vn = ((int64_t)a.num_tokens * a.hv * a.dv - (int64_t)v0) * E;
-        gb = reinterpret_cast<const char*>(a.g + (size_t)s0 * a.hv + h);
         const size_t w0 = ((size_t)base * a.hv + h) * (kChunk * kChunk);
         tb = reinterpret_cast<const char*>(static_cast<const OP*>(a.ws_t) + w0);
         pb = reinterpret_cast<const char*>(static_cast<const OP*>(a.ws_p) + w0);
-        kq_step = (int64_t)kChunk * a.hqk * DK * E;
-        v_step = (int64_t)kChunk * a.hv * a.dv * E;
-        g_step = (int64_t)kChunk * a.hv * 4;
+        gb = reinterpret_cast<const char*>(a.ws_g + ((size_t)base * a.hv + h) * kGateFloats);
+        kq_row = a.hqk * DK * E;
+        v_row = a.hv * a.dv * E;
+        kq_step = (int64_t)kChunk * kq_row;
+        v_step = (int64_t)kChunk * v_row;
         w_step = (int64_t)a.hv * kChunk * kChunk * E;
-        seq_tokens = s1 - s0;
+        g_step = (int64_t)a.hv * kGateFloats * 4;
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) koff[tm] = (unsigned)(((16 * tm + r) * a.hqk * DK + 8 * gq) * E);
-#pragma unroll
-        for (int jt = 0; jt < TPW; ++jt) {
-            const int tw = w + NWS * jt;
-            voff[jt] = (unsigned)(((16 * tw + r) * a.hv * a.dv + 4 * gq) * E);
-            toff[jt] = (unsigned)(((16 * tw + r) * kChunk + 8 * gq) * E);
-        }
-        goff = (unsigned)(l * a.hv * 4);
-    }
-
-    // Fetch the operands of the sequence's chunk j (zeros when !valid), in the
-    // order the chunk consumes them, so that each wait covers only the oldest
-    // loads in flight.
-    __device__ __forceinline__ void load(St& s, int64_t j, bool valid) const {
-        const int64_t jc = valid ? j : 0;
-        const int64_t kqo = jc * kq_step, vo = jc * v_step, go = jc * g_step, wo = jc * w_step;
-        const int64_t nt = seq_tokens - jc * kChunk;              // g past the sequence reads 0
-        const auto rg = make_rsrc(gb + go, (valid && nt > 0) ? ((nt - 1) * hv + 1) * 4 : 0);
-        s.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, goff, 0, 0));
-        const int64_t kqb = valid ? kqn - kqo : 0;
-        const auto rk = make_rsrc(kb + kqo, kqb);
-        const auto rq = make_rsrc(qb + kqo, kqb);
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm) s.kf[tm] = B::frag(rk, koff[tm]);
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm) s.qf[tm] = B::frag(rq, koff[tm]);
-        const auto rv = make_rsrc(vb + vo, valid ? vn - vo : 0);
-#pragma unroll
-        for (int jt = 0; jt < TPW; ++jt) s.v[jt] = B::quad(rv, voff[jt]);
-        const int64_t wb = valid ? kChunk * kChunk * E : 0;
-        const auto rt = make_rsrc(tb + wo, wb);
+        for (int i = 0; i < KU; ++i)
+            kq_voff[i] = (unsigned)((RPI * i + l / G::SEGS) * kq_row + (l % G::SEGS) * 16);
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt)
+            v_voff[jt] = (unsigned)((16 * (w + NWS * jt) + (l >> 2)) * v_row + (l & 3) * G::QE);
+        f_voff = (unsigned)(l * 16);
+        g_voff = (unsigned)(l * 8);
+    }
+
+    __device__ __forceinline__ void load_kqg(KQG& s, int64_t j, bool valid) const {
+        const int64_t jc = valid ? j : 0;
+        const auto rg = make_rsrc(gb + jc * g_step, valid ? kGateFloats * 4 : 0);
+        s.gate = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, g_voff, 0, 0));
+        const int64_t o = jc * kq_step;
+        const int64_t nb = valid ? kqn - o : 0;
+        const auto rk = make_rsrc(kb + o, nb);
+        const auto rq = make_rsrc(qb + o, nb);
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) s.tf[jt][kk] = B::frag(rt, toff[jt] + 32 * kk * E);
+        for (int i = 0; i < KU; ++i) s.k[i] = buf_b128(rk, kq_voff[i], 0);
+#pragma unroll
+        for (int i = 0; i < KU; ++i) s.q[i] = buf_b128(rq, kq_voff[i], 0);
+    }
+
+    __device__ __forceinline__ void load_vtp(VTP& s, int64_t j, bool valid) const {
+        const int64_t jc = valid ? j : 0;
+        const int64_t vo = jc * v_step;
+        const auto rv = make_rsrc(vb + vo, valid ? vn - vo : 0);
+#pragma unroll
+        for (int jt = 0; jt < TPW; ++jt) s.v[jt] = B::quad(rv, v_voff[jt], 0);
+        const int64_t wo = jc * w_step;
+        const int64_t wb = valid ? kChunk * kChunk * E : 0;
+        const auto rt = make_rsrc(tb + wo, wb);
         const auto rp = make_rsrc(pb + wo, wb);
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt)
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) s.pf[jt][kk] = B::frag(rp, toff[jt] + 32 * kk * E);
+            for (int kk = 0; kk < 2; ++kk)
+                s.t[jt][kk] = B::frag(rt, f_voff, (unsigned)(((w + NWS * jt) * 2 + kk) * FU * 1024));
+#pragma unroll
+        for (int jt = 0; jt < TPW; ++jt)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                s.p[jt][kk] = B::frag(rp, f_voff, (unsigned)(((w + NWS * jt) * 2 + kk) * FU * 1024));
     }
 };
 
 template <typename OP, int DK>
-__global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_split_kernel(PrefillArgs a, int xcd_map) {
+__global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_kernel(PrefillArgs a, int xcd_map) {
     using Ops = Op<OP>;
     using frag = typename Ops::frag;
     using quad = typename Ops::quad;
-    using SS = SplitSmem<OP, DK>;
-    using Ctx = SplitCtx<OP, DK>;
-    using St = typename Ctx::St;
+    using G = ScanGeom<OP, DK>;
+    using Ctx = ScanCtx<OP, DK>;
+    using KQG = typename Ctx::KQG;
+    using VTP = typename Ctx::VTP;
     using B = Buf<OP>;
-    constexpr int NWS = SS::NWS, RLD = SS::RLD, TPW = Ctx::TPW;
-    __shared__ SS sm;
+    constexpr int NWS = G::NWS, TPW = G::TPW, RLD = G::RLD, KU = G::KU, RPI = G::RPI, SEGS = G::SEGS;
+    constexpr int ROWB = G::ROWB, FU = G::FU, E = G::E;
+    __shared__ ScanSmem<OP, DK> sm;
 
     // Work item (chain, 16-column block).  With xcd_map, the 8 column blocks of
     // a chain get workgroup ids that the dispatcher sends to one XCD, so they
@@ -815,7 +571,7 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_split_kernel(Prefill
     const int64_t s0 = si.start(n), s1 = si.start(n + 1);
     const int64_t base = slot_base(s0, n);
     Ctx ctx;
-    ctx.init(a, s0, s1, base, h, blk, w);
+    ctx.init(a, s0, base, h, blk, w);
 
     // identity fragments: K slot (gq, i) <-> d_k 8 gq + i, state tile `sub`
     // row n <-> d_k 8 (n/4) + 4 sub + n%4
@@ -837,58 +593,99 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_split_kernel(Prefill
         S[1] = zero4();
     }
 
+    // wave-private staging: byte offsets of the row-wise writes (load i) and
+    // of the fragment reads (unit u of tile 0; tile tm adds 16 tm rows)
+    char* const kst = sm.kst[w];
+    char* const qst = sm.qst[w];
+    unsigned kq_wr[KU];
+#pragma unroll
+    for (int i = 0; i < KU; ++i) {
+        const int row = RPI * i + l / SEGS;
+        kq_wr[i] = (unsigned)(row * ROWB + 16 * ((l % SEGS) ^ swz_kq(row & 15, SEGS)));
+    }
+    unsigned kq_rd[FU];
+#pragma unroll
+    for (int u = 0; u < FU; ++u) kq_rd[u] = (unsigned)(r * ROWB + 16 * ((FU * gq + u) ^ swz_kq(r, SEGS)));
+    const unsigned v_wr = (unsigned)((l >> 2) * G::VROWB + G::QE * ((l & 3) ^ swz_vo(l >> 2, E)));
+    const unsigned v_rd = (unsigned)(r * G::VROWB + G::QE * (gq ^ swz_vo(r, E)));
+
+    // K, Q slices and gates of a chunk into LDS (gates into parity buffer `par`)
+    auto stage = [&](const KQG& s, int par) {
+#pragma unroll
+        for (int i = 0; i < KU; ++i) {
+            *reinterpret_cast<u32x4*>(kst + kq_wr[i]) = s.k[i];
+            *reinterpret_cast<u32x4*>(qst + kq_wr[i]) = s.q[i];
+        }
+        sm.gam[par][l] = fast_exp2(s.gate[0]);
+        sm.dec[par][l] = fast_exp2(s.gate[1]);
+    };
+    // operand fragments of the staged chunk
+    auto fetch = [&](frag* kf, frag* qf) {
+        wave_lds_fence();
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) {
+            const int t = 16 * tm * ROWB;
+            kf[tm] = B::lds_frag(kst + t, kq_rd[0], kq_rd[FU - 1]);
+            qf[tm] = B::lds_frag(qst + t, kq_rd[0], kq_rd[FU - 1]);
+        }
+    };
+
     const int64_t nchunks = (s1 - s0 + kChunk - 1) / kChunk;
-    // One chunk; `nxt` holds the next chunk's operands (its gates are
-    // prepared here, by wave 0, into the other parity buffer).
-    auto chunk = [&](St& cur, const St& nxt, int64_t j, int par) {
+    frag kf[4], qf[4];
+    // One chunk j: `cur` holds its V, T~ and P; `nxt` holds chunk j+1's K, Q
+    // and gates (staged here, then refilled with chunk j+3's).
+    auto chunk = [&](VTP& cur, KQG& nxt, int64_t j, int par) {
         const int64_t t0 = s0 + j * kChunk;
-        const int nt = (int)((s1 - t0) < kChunk ? (s1 - t0) : kChunk);
+        // V tiles into lane layout (read back after E1)
+#pragma unroll
+        for (int jt = 0; jt < TPW; ++jt) *reinterpret_cast<quad*>(sm.vst[w][jt] + v_wr) = cur.v[jt];
         // ---- partial products over the d_k slice
         const frag Sb = Ops::pack(S[0], S[1]);
         f32x4 Xp[4], Yp[4];
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) {
-            Xp[tm] = Ops::mma(Sb, cur.kf[tm], zero4());
-            Yp[tm] = Ops::mma(Sb, cur.qf[tm], zero4());
-        }
+        for (int tm = 0; tm < 4; ++tm) Xp[tm] = Ops::mma(Sb, kf[tm], zero4());
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) {
-            sm.part[w][tm][l] = Xp[tm];
-            sm.part[w][4 + tm][l] = Yp[tm];
-        }
+        for (int tm = 0; tm < 4; ++tm) sm.part[w][tm][l] = Xp[tm];
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) Yp[tm] = Ops::mma(Sb, qf[tm], zero4());
         __syncthreads();                                                        // E1
-        // K^T in operand layout (exact identity product), off the critical path
-        frag Ktf[2][2];
+        // next chunk's K, Q and gates into LDS; fetch the chunk after next
+        stage(nxt, par ^ 1);
+        ctx.load_kqg(nxt, j + 3, j + 3 < nchunks);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int sub = 0; sub < 2; ++sub)
-                Ktf[sub][kk] = Ops::pack(Ops::mma(cur.kf[2 * kk], Iden[sub], zero4()),
-                                         Ops::mma(cur.kf[2 * kk + 1], Iden[sub], zero4()));
-        f32x4 Y[TPW];
+        for (int tm = 0; tm < 4; ++tm) sm.part[w][4 + tm][l] = Yp[tm];
+        // owner: R^T = V^T - X^T diag(gamma)
         float gt[TPW];
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt) {
             const int tw = w + NWS * jt;
             f32x4 X = sm.part[0][tw][l];
-            Y[jt] = sm.part[0][4 + tw][l];
 #pragma unroll
-            for (int v2 = 1; v2 < NWS; ++v2) {
-                X += sm.part[v2][tw][l];
-                Y[jt] += sm.part[v2][4 + tw][l];
-            }
+            for (int v2 = 1; v2 < NWS; ++v2) X += sm.part[v2][tw][l];
             gt[jt] = sm.gam[par][16 * tw + r];
+            const quad vq = *reinterpret_cast<const quad*>(sm.vst[w][jt] + v_rd);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                sm.Rt[(4 * gq + i) * RLD + 16 * tw + r] = from_f32<OP>(to_f32(cur.v[jt][i]) - gt[jt] * X[i]);
+                sm.Rt[(4 * gq + i) * RLD + 16 * tw + r] = from_f32<OP>(to_f32(vq[i]) - gt[jt] * X[i]);
         }
-        const float gn = sm.gam[par][kChunk];
+        const float gn = sm.gam[par][kChunk - 1];
+        // K^T in operand layout (exact identity product)
+        frag Ktf[2][2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub)
+                Ktf[sub][kk] = Ops::pack(Ops::mma(kf[2 * kk], Iden[sub], zero4()),
+                                         Ops::mma(kf[2 * kk + 1], Iden[sub], zero4()));
+        // operand fragments of the next chunk
+        frag kn[4], qn[4];
+        fetch(kn, qn);
         __syncthreads();                                                        // E2
         const frag Rb0 = frag_nat(sm.Rt, RLD, r, 0), Rb1 = frag_nat(sm.Rt, RLD, r, 32);
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt) {
             const int tw = w + NWS * jt;
-            const f32x4 U = Ops::mma(cur.tf[jt][1], Rb1, Ops::mma(cur.tf[jt][0], Rb0, zero4()));
+            const f32x4 U = Ops::mma(cur.t[jt][1], Rb1, Ops::mma(cur.t[jt][0], Rb0, zero4()));
             const f32x4 dc = *reinterpret_cast<const f32x4*>(&sm.dec[par][16 * tw + 4 * gq]);
             quad uq, dq;
 #pragma unroll
@@ -898,6 +695,14 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_split_kernel(Prefill
             }
             *reinterpret_cast<quad*>(&sm.Ut[r * RLD + 16 * tw + 4 * gq]) = uq;
             *reinterpret_cast<quad*>(&sm.Dt[r * RLD + 16 * tw + 4 * gq]) = dq;
+        }
+        f32x4 Y[TPW];
+#pragma unroll
+        for (int jt = 0; jt < TPW; ++jt) {
+            const int tw = w + NWS * jt;
+            Y[jt] = sm.part[0][4 + tw][l];
+#pragma unroll
+            for (int v2 = 1; v2 < NWS; ++v2) Y[jt] += sm.part[v2][4 + tw][l];
         }
         __syncthreads();                                                        // E3
         // ---- S_w^T <- gamma_n S_w^T + K_w^T (D o U)   (the serial chain first)
@@ -910,53 +715,57 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_split_kernel(Prefill
         f32x4 Ot[TPW];
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt)
-            Ot[jt] = Ops::mma(Ub1, cur.pf[jt][1], Ops::mma(Ub0, cur.pf[jt][0], gt[jt] * Y[jt]));
-        // gates of the next chunk (read after the next E1 barrier)
-        if (w == 0) chunk_gates(nxt.g, sm.gam[par ^ 1], sm.dec[par ^ 1]);
-        // this stage is free: fetch the chunk two steps ahead
-        ctx.load(cur, j + 2, j + 2 < nchunks);
+            Ot[jt] = Ops::mma(Ub1, cur.p[jt][1], Ops::mma(Ub0, cur.p[jt][0], gt[jt] * Y[jt]));
+        // this chunk's V, T~ and P are consumed: fetch those of chunk j+2
+        ctx.load_vtp(cur, j + 2, j + 2 < nchunks);
+        // O through the wave's V/O area to row-wise stores; rows past the end
+        // of the sequence fall outside the resource
         {
-            // rows past the end of the sequence fall outside the resource
+            const int64_t ntl = s1 - t0;
             const auto ro = make_rsrc(static_cast<OP*>(a.out) + ((size_t)t0 * a.hv + h) * a.dv + blk * 16,
-                                      ((int64_t)(nt - 1) * a.hv * a.dv + 16) * (int64_t)sizeof(OP));
+                                      ntl > 0 ? (ntl - 1) * ctx.v_row + 16 * E : 0);
 #pragma unroll
             for (int jt = 0; jt < TPW; ++jt) {
                 quad oq;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) oq[i] = from_f32<OP>(Ot[jt][i]);
-                B::store4(oq, ro, ctx.voff[jt]);
+                *reinterpret_cast<quad*>(sm.vst[w][jt] + v_rd) = oq;
             }
+            wave_lds_fence();
+#pragma unroll
+            for (int jt = 0; jt < TPW; ++jt)
+                B::store4(*reinterpret_cast<const quad*>(sm.vst[w][jt] + v_wr), ro, ctx.v_voff[jt], 0);
+        }
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) {
+            kf[tm] = kn[tm];
+            qf[tm] = qn[tm];
         }
     };
 
-    // Chunks are processed in pairs (stages A, B).  An odd count gets one
-    // trailing empty chunk, which is an exact no-op: its loads read zeros
-    // (g = 0, so gamma_n = 1 and S is unchanged) and its stores are dropped.
-    // Keeping the loop free of an early exit keeps the load order identical on
-    // every path into the loop, so the memory-counter waits stay exact.
-    St A, Bs;
-    ctx.load(A, 0, nchunks > 0);
-    ctx.load(Bs, 1, nchunks > 1);
-    if (w == 0) chunk_gates(A.g, sm.gam[0], sm.dec[0]);
+    // Chunks are processed in pairs.  An odd count gets one trailing empty
+    // chunk, which is an exact no-op: its loads read zeros (gates 0, so
+    // gamma_n = 1 and S is unchanged) and its stores are dropped.  Keeping
+    // the loop free of an early exit keeps the load order identical on every
+    // path into the loop, so the memory-counter waits stay exact.
+    KQG ka, kb;
+    VTP va, vb;
+    ctx.load_kqg(ka, 0, nchunks > 0);
+    ctx.load_vtp(va, 0, nchunks > 0);
+    ctx.load_kqg(kb, 1, nchunks > 1);
+    ctx.load_vtp(vb, 1, nchunks > 1);
+    stage(ka, 0);
+    ctx.load_kqg(ka, 2, nchunks > 2);
+    fetch(kf, qf);
+    __syncthreads();   // gates of chunk 0
     for (int64_t j = 0; j < nchunks; j += 2) {
-        chunk(A, Bs, j, 0);
-        chunk(Bs, A, j + 1, 1);
+        chunk(va, kb, j, 0);
+        chunk(vb, ka, j + 1, 1);
     }
     if (a.final_state) {
         *reinterpret_cast<f32x4*>(a.final_state + srow) = S[0];
         *reinterpret_cast<f32x4*>(a.final_state + srow + 4) = S[1];
     }
-}
-
-// Scan variant: 1 = split (default), 0 = wide.  GDN_SCAN=wide|split overrides
-// (both compute the same result; the choice only affects speed).
-int scan_variant() {
-    static const int v = [] {
-        const char* e = getenv("GDN_SCAN");
-        if (e && e[0] == 'w') return 0;
-        return 1;
-    }();
-    return v;
 }
 
 template <typename OP, int DK>
@@ -969,21 +778,9 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
     }
     const int64_t chains = (int64_t)a.num_seqs * a.hv;
     const int nblk = a.dv / 16;
-    if (scan_variant() == 1) {
-        // split scan: DK/32 waves per 16-column block
-        const int xcd = (nblk == 8 && chains % 8 == 0) ? 1 : 0;
-        dim3 grid((unsigned)(chains * nblk)), block(DK / 32 * kWave);
-        hipLaunchKernelGGL((gdn_scan_split_kernel<OP, DK>), grid, block, 0, st, a, xcd);
-        return hipGetLastError();
-    }
-    // wide scan.  bf16: 4 waves (64 columns) per workgroup with register
-    // prefetch of the next chunk; fp32: 2 waves (LDS budget), loads at the top
-    // of each chunk.
-    constexpr bool BF = sizeof(OP) == 2;
-    constexpr int NW = BF ? 4 : 2;
-    const int groups = a.dv / (16 * NW);
-    dim3 grid((unsigned)chains, (unsigned)groups), block(NW * kWave);
-    hipLaunchKernelGGL((gdn_scan_kernel<OP, DK, NW, BF>), grid, block, 0, st, a);
+    const int xcd = (nblk == 8 && chains % 8 == 0) ? 1 : 0;
+    dim3 grid((unsigned)(chains * nblk)), block(DK / 32 * kWave);
+    hipLaunchKernelGGL((gdn_scan_kernel<OP, DK>), grid, block, 0, st, a, xcd);
     return hipGetLastError();
 }
 

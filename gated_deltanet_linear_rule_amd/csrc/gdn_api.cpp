@@ -173,8 +173,8 @@ gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, con
     if (a.num_slots > INT32_MAX) return fail(GDN_ERROR_NOT_SUPPORTED, "too many chunks");
 
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int64_t wbytes = gdn::prefill_workspace_bytes(a.num_slots, a.hv, bf16 ? 2 : 4);
-    const int64_t mbytes = a.num_slots * a.hv * gdn::prefill_matrix_bytes(bf16 ? 2 : 4);
+    const gdn::PrefillWorkspace wl(a.num_slots, a.hqk, a.hv, shape->head_dim_k, bf16 ? 2 : 4);
+    const int64_t wbytes = wl.total;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(GDN_ERROR_LAUNCH, "hipGetDevice failed");
     keep_pool_memory(dev);
@@ -183,9 +183,12 @@ gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, con
         (void)hipGetLastError();
         return fail(GDN_ERROR_OUT_OF_MEMORY, "prefill workspace of %lld bytes", (long long)wbytes);
     }
-    a.ws_t = ws;
-    a.ws_p = static_cast<char*>(ws) + mbytes;
-    a.ws_g = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * mbytes);
+    char* wc = static_cast<char*>(ws);
+    a.ws_t = wc + wl.t;
+    a.ws_p = wc + wl.p;
+    a.ws_g = reinterpret_cast<float*>(wc + wl.g);
+    a.ws_k = wc + wl.k;
+    a.ws_q = wc + wl.q;
     hipError_t e = gdn::launch_prefill(a, bf16, shape->head_dim_k, st);
     hipError_t ef = hipFreeAsync(ws, st);
     if (e == hipSuccess) e = ef;

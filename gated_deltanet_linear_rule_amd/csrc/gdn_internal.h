@@ -37,19 +37,31 @@ struct PrefillArgs {
     int32_t hv;
     int32_t dv;
     int64_t num_slots;         // ceil(num_tokens / 64) + num_seqs
-    // Workspace written by the prep kernel and read by the scan, per (slot, value head):
-    void* ws_t;                // 64 x 64 T~ = (I + A)^-1 diag(beta), fragment-major order
-    void* ws_p;                // 64 x 64 P = lower_incl(Gamma o Q K^T), fragment-major order
-    float* ws_g;               // 64 pairs (G2_t, G2_last - G2_t): log2-scaled cumulative gates
+    // Workspace written by the prep kernel and read by the scan, in the order
+    // of the scan's operand fragments ("fragment-major"):
+    void* ws_t;                // per (slot, value head): 64 x 64 T~ = (I + A)^-1 diag(beta)
+    void* ws_p;                // per (slot, value head): 64 x 64 P = lower_incl(Gamma o Q K^T)
+    float* ws_g;               // per (slot, value head): 64 pairs (G2_t, G2_last - G2_t)
+    void* ws_k;                // per (slot, q/k head): the chunk's 64 x dk block of K
+    void* ws_q;                // per (slot, q/k head): the chunk's 64 x dk block of Q
 };
 
-// Workspace bytes per (slot, value head) of each part (element size 2 for bf16, 4 for fp32).
-inline int64_t prefill_matrix_bytes(int elem_size) { return (int64_t)64 * 64 * elem_size; }
-inline int64_t prefill_gate_bytes() { return (int64_t)64 * 2 * 4; }
-// Workspace bytes for one prefill call: T~, P and the gates of every (slot, value head).
-inline int64_t prefill_workspace_bytes(int64_t num_slots, int hv, int elem_size) {
-    return num_slots * (int64_t)hv * (2 * prefill_matrix_bytes(elem_size) + prefill_gate_bytes());
-}
+// Workspace layout of one prefill call (byte offsets of each part and total),
+// element size 2 for bf16, 4 for fp32.
+struct PrefillWorkspace {
+    int64_t t, p, g, k, q, total;
+    PrefillWorkspace(int64_t num_slots, int hqk, int hv, int dk, int elem_size) {
+        const int64_t mat = num_slots * hv * 64 * 64 * (int64_t)elem_size;
+        const int64_t gate = num_slots * hv * 64 * 2 * 4;
+        const int64_t kq = num_slots * hqk * 64 * (int64_t)dk * elem_size;
+        t = 0;
+        p = t + mat;
+        g = p + mat;
+        k = g + gate;
+        q = k + kq;
+        total = q + kq;
+    }
+};
 
 // Launchers: return hipSuccess or the launch error.  `bf16` selects the
 // element type of q/k/v/out; dk/dv are 64 or 128.

@@ -114,25 +114,31 @@ __device__ __forceinline__ double lane63_f64(double x) {
 // ===========================================================================
 // workspace layout shared by the two kernels
 // ===========================================================================
-// T~ and P of one (chunk, value head) are stored fragment-major: 16-byte unit
-//     e = ((tw * 2 + kk) * FU + u) * 64 + lane
-// holds row 16 tw + (lane & 15), columns 32 kk + 8 (lane >> 4) + VE u .. + VE
-// of the 64 x 64 matrix, i.e. unit u of the scan's operand fragment (tw, kk)
-// for that lane, so a wave reads a fragment as one contiguous 1 KB block.
+// Every matrix the scan reads as matrix-core operands is stored
+// fragment-major: 16-byte unit e = (f * FU + u) * 64 + lane holds unit u of
+// operand fragment f for that lane, so a wave reads a fragment as one
+// contiguous 1 KB block.  A fragment holds, for lane (r, gq) =
+// (lane & 15, lane >> 4), eight elements of row r of a 16-row tile, columns
+// c0 + 8 gq .. c0 + 8 gq + 7 (u = 0, 1 split them for fp32).
+//  * T~ and P of a (chunk, value head): f = tw * 2 + kk, rows 16 tw + r,
+//    c0 = 32 kk (64 x 64);
+//  * K and Q of a (chunk, q/k head): f = w * 4 + tm, rows 16 tm + r (tokens),
+//    c0 = 32 w (64 x d_k; the scan's wave w owns d_k columns 32 w .. 32 w + 31).
 // The gates of a chunk are 64 float pairs (G2_t, G2_last - G2_t), the
 // difference taken in fp64; zeros (what a read past the end returns) stand
 // for a chunk without decay.
 template <typename OP> struct FragMajor {
     static constexpr int VE = 16 / (int)sizeof(OP);      // elements per 16-byte unit
     static constexpr int FU = 8 / VE;                    // units per operand fragment
-    static constexpr int UNITS = kChunk * kChunk / VE;
-    __device__ __forceinline__ static int row(int e) {
-        return 16 * (((e >> 6) / FU) >> 1) + (e & 15);
-    }
-    __device__ __forceinline__ static int col(int e) {
-        const int rest = e >> 6;
-        return 32 * ((rest / FU) & 1) + 8 * ((e >> 4) & 3) + VE * (rest % FU);
-    }
+    static constexpr int UNITS = kChunk * kChunk / VE;   // of a 64 x 64 matrix
+    __device__ __forceinline__ static int frag_of(int e) { return (e >> 6) / FU; }
+    __device__ __forceinline__ static int col_in(int e) { return 8 * ((e >> 4) & 3) + VE * ((e >> 6) % FU); }
+    // 64 x 64 (T~, P)
+    __device__ __forceinline__ static int row(int e) { return 16 * (frag_of(e) >> 1) + (e & 15); }
+    __device__ __forceinline__ static int col(int e) { return 32 * (frag_of(e) & 1) + col_in(e); }
+    // 64 x d_k (K, Q)
+    __device__ __forceinline__ static int kq_row(int e) { return 16 * (frag_of(e) & 3) + (e & 15); }
+    __device__ __forceinline__ static int kq_col(int e) { return 32 * (frag_of(e) >> 2) + col_in(e); }
 };
 constexpr int kGateFloats = 2 * kChunk;   // floats per (chunk, value head)
 
@@ -196,6 +202,19 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
             f32x2{(float)G, (float)(Gl - G)};
     }
     __syncthreads();
+
+    // ---- fragment-major copies of K and Q for the scan (padded rows are
+    // zero); one writer per q/k head
+    if ((h * a.hqk) % a.hv == 0) {
+        using FM = FragMajor<OP>;
+        OP* Kw = static_cast<OP*>(a.ws_k) + ((size_t)slot * a.hqk + hq) * (kChunk * DK);
+        OP* Qw = static_cast<OP*>(a.ws_q) + ((size_t)slot * a.hqk + hq) * (kChunk * DK);
+        for (int e = tid; e < kChunk * DK / VE; e += kPrepThreads) {
+            const int row = FM::kq_row(e), col = FM::kq_col(e);
+            *reinterpret_cast<u32x4*>(Kw + e * VE) = ld16(sm.K + row * LD + col);
+            *reinterpret_cast<u32x4*>(Qw + e * VE) = ld16(sm.Q + row * LD + col);
+        }
+    }
 
     // ---- Gamma-weighted K K^T (-> A, fp32) and Q K^T (-> P, staged as OP)
     for (int job = w; job < 20; job += kPrepThreads / kWave) {
@@ -297,7 +316,7 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
 // NWS = DK / 32 waves split d_k: wave w owns state rows S[:, 32w .. 32w+32)
 // as two fp32 accumulator tiles (d_k x 16).  Inside the slice the d_k order of
 // the tiles is permuted (tile `sub`, row 4 gq + i  <->  d_k 8 gq + 4 sub + i)
-// so that an operand fragment of K or Q is one contiguous 16-byte piece.
+// so that an operand fragment of K or Q pairs with the state tiles directly.
 // Wave w also owns token tiles tw = w + NWS jt (jt < TPW = 4 / NWS).  Per chunk:
 //   wave w:  X_w^T = S_w K_w^T,  Y_w^T = S_w Q_w^T          (partial over d_k)
 //   E1 (LDS): X partials -> the owner of token tile tw sums X^T there
@@ -308,23 +327,20 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
 //   E3 (LDS): U and D o U for all tokens to every wave
 //   wave w:  S_w^T <- gamma_n S_w^T + K_w^T (D o U)
 //   owner:   O^T = Y^T diag(gamma) + U^T P_tw^T
+// A wave keeps its own partial tiles in registers and writes only the tiles
+// other waves own.
 //
 // Global memory.  The vector memory path serves a wave request four lanes at
 // a time, and four lanes on four different rows cost four times as much as
-// four lanes on one 64-byte piece, so every access here keeps consecutive
-// lanes on consecutive bytes:
-//  * K and Q of the wave's d_k slice are read row by row (four lanes per
-//    row) and turned into operand fragments through a wave-private LDS area;
-//  * V and O take the same route through a small wave-private area;
-//  * T~ and P arrive fragment-major from the prep kernel, one 1 KB block per
-//    fragment;
-//  * the gates arrive as one 512-byte record per chunk.
-// K, Q and the gates are fetched two chunks before their chunk and moved into
-// LDS one chunk before it; V, T~ and P are fetched about two chunks ahead
-// into registers.  All loads go through buffer resources (reads past the end
-// of a resource return 0, writes past it are dropped), and no load, store or
-// use of a loaded value sits behind a branch, so the compiler's memory-counter
-// waits stay exact.
+// four lanes on one 64-byte piece, so every access keeps consecutive lanes on
+// consecutive bytes: K, Q, T~ and P come fragment-major from the prep
+// kernel's workspace (one 1 KB block per fragment), the gates as one
+// 512-byte record per chunk, and V and O pass through a small wave-private
+// LDS area between their row-wise global form and the lanes' tile layout.
+// Operands are fetched two chunks ahead into registers.  All loads go
+// through buffer resources (reads past the end of a resource return 0, writes
+// past it are dropped), and no load, store or use of a loaded value sits
+// behind a branch, so the compiler's memory-counter waits stay exact.
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -334,25 +350,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 
-__device__ __forceinline__ u32x4 buf_b128(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-
 template <typename OP> struct Buf;
 template <> struct Buf<__bf16> {
     // operand fragment: one 16-byte unit
     __device__ __forceinline__ static bf16x8 frag(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
         return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
     }
-    __device__ __forceinline__ static bf16x4 quad(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
-        return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+    __device__ __forceinline__ static bf16x4 quad(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+        return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
     }
-    __device__ __forceinline__ static void store4(bf16x4 x, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, x), r, voff, soff, 0);
-    }
-    // operand fragment from LDS (16-byte unit offsets of its two halves)
-    __device__ __forceinline__ static bf16x8 lds_frag(const char* base, unsigned off0, unsigned) {
-        return *reinterpret_cast<const bf16x8*>(base + off0);
+    __device__ __forceinline__ static void store4(bf16x4 x, __amdgpu_buffer_rsrc_t r, unsigned voff) {
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, x), r, voff, 0, 0);
     }
 };
 template <> struct Buf<float> {
@@ -362,16 +370,11 @@ template <> struct Buf<float> {
         const f32x4 hi = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 1024, 0));
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
-    __device__ __forceinline__ static f32x4 quad(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
-        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    __device__ __forceinline__ static f32x4 quad(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
     }
-    __device__ __forceinline__ static void store4(f32x4 x, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, voff, soff, 0);
-    }
-    __device__ __forceinline__ static f32x8 lds_frag(const char* base, unsigned off0, unsigned off1) {
-        const f32x4 lo = *reinterpret_cast<const f32x4*>(base + off0);
-        const f32x4 hi = *reinterpret_cast<const f32x4*>(base + off1);
-        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    __device__ __forceinline__ static void store4(f32x4 x, __amdgpu_buffer_rsrc_t r, unsigned voff) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, voff, 0, 0);
     }
 };
 
@@ -382,13 +385,10 @@ __device__ __forceinline__ typename Op<T>::frag frag_nat(const T* M, int ld, int
     return *reinterpret_cast<const frag*>(M + (size_t)row * ld + k0 + 8 * (lane_id() >> 4));
 }
 
-// XOR swizzles of the wave-private staging areas: the unit (16 bytes, or a
-// 4-element quad for V/O) index inside a row is XORed with a function of the
-// row, so that both the row-wise writes (consecutive lanes along a row) and
-// the fragment reads (consecutive lanes down a column) spread over the banks.
-__device__ __forceinline__ int swz_kq(int row, int units) {
-    return units == 4 ? (((row >> 1) ^ (row >> 3)) & 3) : ((row ^ (row >> 3)) & 7);
-}
+// XOR swizzle of the V/O staging tiles (16 rows of four 4-element quads): the
+// quad index is XORed with a function of the row so that both the row-wise
+// side (four lanes per row) and the tile side (one row per lane) spread over
+// the LDS banks.
 __device__ __forceinline__ int swz_vo(int row, int elem) {
     return elem == 2 ? ((row >> 2) & 3) : (((row >> 1) ^ (row >> 3)) & 3);
 }
@@ -403,12 +403,7 @@ struct ScanGeom {
     static constexpr int NWS = DK / 32;                 // waves per workgroup (d_k split)
     static constexpr int TPW = 4 / NWS;                 // token tiles per wave
     static constexpr int E = (int)sizeof(OP);
-    static constexpr int SEGS = 32 * E / 16;            // 16-byte units per row of a wave's K slice
-    static constexpr int RPI = kWave / SEGS;            // rows per row-wise load
-    static constexpr int KU = kChunk / RPI;             // row-wise loads per tensor and chunk
     static constexpr int FU = 8 * E / 16;               // 16-byte units per operand fragment
-    static constexpr int ROWB = SEGS * 16;              // bytes per staged K/Q row
-    static constexpr int KQB = kChunk * ROWB;           // bytes of a wave's K (or Q) slice of a chunk
     static constexpr int QE = 4 * E;                    // bytes per V/O quad
     static constexpr int VROWB = 16 * E;                // bytes per V/O tile row
     static constexpr int VB = 16 * VROWB;               // bytes per V/O tile
@@ -424,9 +419,7 @@ struct ScanSmem {
     alignas(16) OP Dt[16 * G::RLD];      // D o U as [column][token]
     alignas(16) float gam[2][kChunk];    // by chunk parity: e^{G_t}
     alignas(16) float dec[2][kChunk];    //                  e^{G_last - G_t}
-    alignas(16) char kst[G::NWS][G::KQB];          // wave-private: K slice of the next chunk
-    alignas(16) char qst[G::NWS][G::KQB];          //               Q slice
-    alignas(16) char vst[G::NWS][G::TPW][G::VB];   //               V / O tiles
+    alignas(16) char vst[G::NWS][G::TPW][G::VB];   // wave-private V / O tiles
 };
 
 template <typename OP, int DK>
@@ -435,34 +428,29 @@ struct ScanCtx {
     using B = Buf<OP>;
     using frag = typename Op<OP>::frag;
     using quad = typename Op<OP>::quad;
-    static constexpr int NWS = G::NWS, TPW = G::TPW, E = G::E, KU = G::KU, RPI = G::RPI, FU = G::FU;
-    // K and Q slices (row-wise) and gates of one chunk
-    struct KQG {
-        u32x4 k[KU];
-        u32x4 q[KU];
+    static constexpr int NWS = G::NWS, TPW = G::TPW, E = G::E, FU = G::FU;
+    // One chunk's operands for one wave, in the order the chunk uses them.
+    struct Stage {
         f32x2 gate;          // (G2_l, G2_last - G2_l) of token `lane`
-    };
-    // V tiles (row-wise) and T~ / P fragments of one chunk
-    struct VTP {
+        frag kf[4];          // K[16 tm + r][32 w + 8 gq + (0..7)]
+        frag qf[4];          // Q, same positions
         quad v[TPW];         // V[16 tw + (l >> 2)][16 blk + 4 (l & 3) + (0..3)]
         frag t[TPW][2];      // T~[16 tw + r][32 kk + 8 gq + (0..7)]
         frag p[TPW][2];      // P, same positions
     };
 
     // per-sequence: byte address of the sequence's first chunk in each tensor
-    // and the bytes from there to the end of the tensor
-    const char* kb; const char* qb; int64_t kqn;
-    const char* vb; int64_t vn;
-    const char* tb; const char* pb; const char* gb;
-    int64_t kq_step, v_step, w_step, g_step;   // bytes per chunk step
-    int kq_row, v_row;                          // bytes per token row
+    const char* kb; const char* qb; const char* gb;
+    const char* tb; const char* pb;
+    const char* vb; int64_t vn;                 // V: and the bytes to its end
+    int64_t kq_step, g_step, w_step, v_step;    // bytes per chunk step
+    int v_row;                                  // bytes per token row of V and O
     int w;
     // Loop-invariant per-lane byte offsets.  Row offsets that a bounds check
-    // must see stay in the per-lane offset (the scalar offset only ever
-    // carries fragment-block offsets inside a fully valid T~/P block).
-    unsigned kq_voff[KU];   // row-wise K/Q load i: row RPI i + l / SEGS, unit l % SEGS
+    // must see stay in the per-lane offset; the scalar offset only carries
+    // fragment offsets inside a fully valid block.
     unsigned v_voff[TPW];   // row-wise V/O of tile tw: row 16 tw + (l >> 2), quad l & 3
-    unsigned f_voff;        // fragment-major T~/P: unit `lane`
+    unsigned f_voff;        // fragment-major blocks: unit `lane`
     unsigned g_voff;        // gate pair of token `lane`
 
     __device__ __forceinline__ void init(const PrefillArgs& a, int64_t s0, int64_t base, int h, int blk,
@@ -470,26 +458,21 @@ struct ScanCtx {
         const int l = lane_id();
         const int hq = (h * a.hqk) / a.hv;
         w = wave;
-        const size_t kq0 = ((size_t)s0 * a.hqk + hq) * DK + 32 * w;
-        kb = reinterpret_cast<const char*>(static_cast<const OP*>(a.k) + kq0);
-        qb = reinterpret_cast<const char*>(static_cast<const OP*>(a.q) + kq0);
-        kqn = ((int64_t)a.num_tokens * a.hqk * DK - (int64_t)kq0) * E;
-        const size_t v0 = ((size_t)s0 * a.hv + h) * a.dv + blk * 16;
-        vb = reinterpret_cast<const char*>(static_cast<const OP*>(a.v) + v0);
-        vn = ((int64_t)a.num_tokens * a.hv * a.dv - (int64_t)v0) * E;
+        const size_t kq0 = ((size_t)base * a.hqk + hq) * (kChunk * DK);
+        kb = reinterpret_cast<const char*>(static_cast<const OP*>(a.ws_k) + kq0);
+        qb = reinterpret_cast<const char*>(static_cast<const OP*>(a.ws_q) + kq0);
         const size_t w0 = ((size_t)base * a.hv + h) * (kChunk * kChunk);
         tb = reinterpret_cast<const char*>(static_cast<const OP*>(a.ws_t) + w0);
         pb = reinterpret_cast<const char*>(static_cast<const OP*>(a.ws_p) + w0);
         gb = reinterpret_cast<const char*>(a.ws_g + ((size_t)base * a.hv + h) * kGateFloats);
-        kq_row = a.hqk * DK * E;
+        const size_t v0 = ((size_t)s0 * a.hv + h) * a.dv + blk * 16;
+        vb = reinterpret_cast<const char*>(static_cast<const OP*>(a.v) + v0);
+        vn = ((int64_t)a.num_tokens * a.hv * a.dv - (int64_t)v0) * E;
         v_row = a.hv * a.dv * E;
-        kq_step = (int64_t)kChunk * kq_row;
-        v_step = (int64_t)kChunk * v_row;
-        w_step = (int64_t)a.hv * kChunk * kChunk * E;
+        kq_step = (int64_t)a.hqk * kChunk * DK * E;
         g_step = (int64_t)a.hv * kGateFloats * 4;
-#pragma unroll
-        for (int i = 0; i < KU; ++i)
-            kq_voff[i] = (unsigned)((RPI * i + l / G::SEGS) * kq_row + (l % G::SEGS) * 16);
+        w_step = (int64_t)a.hv * kChunk * kChunk * E;
+        v_step = (int64_t)kChunk * v_row;
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt)
             v_voff[jt] = (unsigned)((16 * (w + NWS * jt) + (l >> 2)) * v_row + (l & 3) * G::QE);
@@ -497,74 +480,69 @@ struct ScanCtx {
         g_voff = (unsigned)(l * 8);
     }
 
-    __device__ __forceinline__ void load_kqg(KQG& s, int64_t j, bool valid) const {
-        const int64_t jc = valid ? j : 0;
-        const auto rg = make_rsrc(gb + jc * g_step, valid ? kGateFloats * 4 : 0);
-        s.gate = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, g_voff, 0, 0));
-        const int64_t o = jc * kq_step;
-        const int64_t nb = valid ? kqn - o : 0;
-        const auto rk = make_rsrc(kb + o, nb);
-        const auto rq = make_rsrc(qb + o, nb);
+    // Fetch the operands of the sequence's chunk j (zeros when !valid), in
+    // four groups issued at different points of a chunk, each as soon as the
+    // registers it refills are free: Q and V, then K and the gates, then T~,
+    // then P.
+    __device__ __forceinline__ int64_t cj(int64_t j, bool valid) const { return valid ? j : 0; }
+    __device__ __forceinline__ void load_qv(Stage& s, int64_t j, bool valid) const {
+        const int64_t jc = cj(j, valid);
+        const auto rq = make_rsrc(qb + jc * kq_step, valid ? (int64_t)kChunk * DK * E : 0);
 #pragma unroll
-        for (int i = 0; i < KU; ++i) s.k[i] = buf_b128(rk, kq_voff[i], 0);
-#pragma unroll
-        for (int i = 0; i < KU; ++i) s.q[i] = buf_b128(rq, kq_voff[i], 0);
-    }
-
-    __device__ __forceinline__ void load_vtp(VTP& s, int64_t j, bool valid) const {
-        const int64_t jc = valid ? j : 0;
+        for (int tm = 0; tm < 4; ++tm) s.qf[tm] = B::frag(rq, f_voff, (unsigned)((w * 4 + tm) * FU * 1024));
         const int64_t vo = jc * v_step;
         const auto rv = make_rsrc(vb + vo, valid ? vn - vo : 0);
 #pragma unroll
-        for (int jt = 0; jt < TPW; ++jt) s.v[jt] = B::quad(rv, v_voff[jt], 0);
-        const int64_t wo = jc * w_step;
-        const int64_t wb = valid ? kChunk * kChunk * E : 0;
-        const auto rt = make_rsrc(tb + wo, wb);
-        const auto rp = make_rsrc(pb + wo, wb);
+        for (int jt = 0; jt < TPW; ++jt) s.v[jt] = B::quad(rv, v_voff[jt]);
+    }
+    __device__ __forceinline__ void load_kg(Stage& s, int64_t j, bool valid) const {
+        const int64_t jc = cj(j, valid);
+        const auto rk = make_rsrc(kb + jc * kq_step, valid ? (int64_t)kChunk * DK * E : 0);
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) s.kf[tm] = B::frag(rk, f_voff, (unsigned)((w * 4 + tm) * FU * 1024));
+        const auto rg = make_rsrc(gb + jc * g_step, valid ? kGateFloats * 4 : 0);
+        s.gate = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, g_voff, 0, 0));
+    }
+    __device__ __forceinline__ void load_t(Stage& s, int64_t j, bool valid) const {
+        const auto rt = make_rsrc(tb + cj(j, valid) * w_step, valid ? kChunk * kChunk * E : 0);
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt)
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
                 s.t[jt][kk] = B::frag(rt, f_voff, (unsigned)(((w + NWS * jt) * 2 + kk) * FU * 1024));
+    }
+    __device__ __forceinline__ void load_p(Stage& s, int64_t j, bool valid) const {
+        const auto rp = make_rsrc(pb + cj(j, valid) * w_step, valid ? kChunk * kChunk * E : 0);
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt)
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
                 s.p[jt][kk] = B::frag(rp, f_voff, (unsigned)(((w + NWS * jt) * 2 + kk) * FU * 1024));
     }
+    __device__ __forceinline__ void load(Stage& s, int64_t j, bool valid) const {
+        load_qv(s, j, valid);
+        load_kg(s, j, valid);
+        load_t(s, j, valid);
+        load_p(s, j, valid);
+    }
 };
 
-template <typename OP, int DK>
-__global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_kernel(PrefillArgs a, int xcd_map) {
+// The work of wave W of a scan workgroup (W is a compile-time constant, so
+// every tile index below is static).
+template <typename OP, int DK, int W>
+__device__ __forceinline__ void scan_wave(const PrefillArgs& a, ScanSmem<OP, DK>& sm, int chain, int blk) {
     using Ops = Op<OP>;
     using frag = typename Ops::frag;
     using quad = typename Ops::quad;
     using G = ScanGeom<OP, DK>;
     using Ctx = ScanCtx<OP, DK>;
-    using KQG = typename Ctx::KQG;
-    using VTP = typename Ctx::VTP;
+    using St = typename Ctx::Stage;
     using B = Buf<OP>;
-    constexpr int NWS = G::NWS, TPW = G::TPW, RLD = G::RLD, KU = G::KU, RPI = G::RPI, SEGS = G::SEGS;
-    constexpr int ROWB = G::ROWB, FU = G::FU, E = G::E;
-    __shared__ ScanSmem<OP, DK> sm;
-
-    // Work item (chain, 16-column block).  With xcd_map, the 8 column blocks of
-    // a chain get workgroup ids that the dispatcher sends to one XCD, so they
-    // share that XCD's L2 for K, Q, T~ and P.
-    int chain, blk;
-    {
-        const int L = blockIdx.x, nblk = a.dv / 16;
-        if (xcd_map) {
-            chain = (L & 7) + 8 * (L / 64);
-            blk = (L >> 3) & 7;
-        } else {
-            chain = L / nblk;
-            blk = L - chain * nblk;
-        }
-    }
+    constexpr int NWS = G::NWS, TPW = G::TPW, RLD = G::RLD, E = G::E;
+    constexpr int w = W;
     const int n = chain / a.hv;
     const int h = chain - n * a.hv;
-    const int l = lane_id(), w = wave_id(), r = l & 15, gq = l >> 4;
+    const int l = lane_id(), r = l & 15, gq = l >> 4;
     const int c = blk * 16 + r;
 
     const SeqIndex si{a.cu, a.seqlen};
@@ -593,75 +571,52 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_kernel(PrefillArgs a
         S[1] = zero4();
     }
 
-    // wave-private staging: byte offsets of the row-wise writes (load i) and
-    // of the fragment reads (unit u of tile 0; tile tm adds 16 tm rows)
-    char* const kst = sm.kst[w];
-    char* const qst = sm.qst[w];
-    unsigned kq_wr[KU];
-#pragma unroll
-    for (int i = 0; i < KU; ++i) {
-        const int row = RPI * i + l / SEGS;
-        kq_wr[i] = (unsigned)(row * ROWB + 16 * ((l % SEGS) ^ swz_kq(row & 15, SEGS)));
-    }
-    unsigned kq_rd[FU];
-#pragma unroll
-    for (int u = 0; u < FU; ++u) kq_rd[u] = (unsigned)(r * ROWB + 16 * ((FU * gq + u) ^ swz_kq(r, SEGS)));
+    // V/O staging: row-wise side (row l >> 2, quad l & 3) and tile side
+    // (row r, quad gq), byte offsets inside a tile
     const unsigned v_wr = (unsigned)((l >> 2) * G::VROWB + G::QE * ((l & 3) ^ swz_vo(l >> 2, E)));
     const unsigned v_rd = (unsigned)(r * G::VROWB + G::QE * (gq ^ swz_vo(r, E)));
-
-    // K, Q slices and gates of a chunk into LDS (gates into parity buffer `par`)
-    auto stage = [&](const KQG& s, int par) {
-#pragma unroll
-        for (int i = 0; i < KU; ++i) {
-            *reinterpret_cast<u32x4*>(kst + kq_wr[i]) = s.k[i];
-            *reinterpret_cast<u32x4*>(qst + kq_wr[i]) = s.q[i];
-        }
+    auto gates = [&](const St& s, int par) {
         sm.gam[par][l] = fast_exp2(s.gate[0]);
         sm.dec[par][l] = fast_exp2(s.gate[1]);
     };
-    // operand fragments of the staged chunk
-    auto fetch = [&](frag* kf, frag* qf) {
-        wave_lds_fence();
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm) {
-            const int t = 16 * tm * ROWB;
-            kf[tm] = B::lds_frag(kst + t, kq_rd[0], kq_rd[FU - 1]);
-            qf[tm] = B::lds_frag(qst + t, kq_rd[0], kq_rd[FU - 1]);
-        }
-    };
 
     const int64_t nchunks = (s1 - s0 + kChunk - 1) / kChunk;
-    frag kf[4], qf[4];
-    // One chunk j: `cur` holds its V, T~ and P; `nxt` holds chunk j+1's K, Q
-    // and gates (staged here, then refilled with chunk j+3's).
-    auto chunk = [&](VTP& cur, KQG& nxt, int64_t j, int par) {
+    // One chunk j: `cur` holds its operands, `nxt` those of chunk j+1, whose
+    // gates are moved into LDS here (read after the next chunk's first barrier).
+    auto chunk = [&](St& cur, const St& nxt, int64_t j, int par) {
         const int64_t t0 = s0 + j * kChunk;
         // V tiles into lane layout (read back after E1)
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt) *reinterpret_cast<quad*>(sm.vst[w][jt] + v_wr) = cur.v[jt];
-        // ---- partial products over the d_k slice
+        // ---- partial products over the d_k slice; other waves' X tiles to LDS
         const frag Sb = Ops::pack(S[0], S[1]);
         f32x4 Xp[4], Yp[4];
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) Xp[tm] = Ops::mma(Sb, kf[tm], zero4());
+        for (int tm = 0; tm < 4; ++tm) Xp[tm] = Ops::mma(Sb, cur.kf[tm], zero4());
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) sm.part[w][tm][l] = Xp[tm];
+        for (int tm = 0; tm < 4; ++tm)
+            if (tm % NWS != w) sm.part[w][tm][l] = Xp[tm];
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) Yp[tm] = Ops::mma(Sb, qf[tm], zero4());
+        for (int tm = 0; tm < 4; ++tm) Yp[tm] = Ops::mma(Sb, cur.qf[tm], zero4());
         __syncthreads();                                                        // E1
-        // next chunk's K, Q and gates into LDS; fetch the chunk after next
-        stage(nxt, par ^ 1);
-        ctx.load_kqg(nxt, j + 3, j + 3 < nchunks);
+        gates(nxt, par ^ 1);
+        // Q and V of this chunk are consumed: fetch those of chunk j+2
+        const bool pre = j + 2 < nchunks;
+        __builtin_amdgcn_sched_barrier(0);
+        ctx.load_qv(cur, j + 2, pre);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) sm.part[w][4 + tm][l] = Yp[tm];
+        for (int tm = 0; tm < 4; ++tm)
+            if (tm % NWS != w) sm.part[w][4 + tm][l] = Yp[tm];
         // owner: R^T = V^T - X^T diag(gamma)
         float gt[TPW];
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt) {
             const int tw = w + NWS * jt;
-            f32x4 X = sm.part[0][tw][l];
+            f32x4 X = Xp[tw];
 #pragma unroll
-            for (int v2 = 1; v2 < NWS; ++v2) X += sm.part[v2][tw][l];
+            for (int v2 = 0; v2 < NWS; ++v2)
+                if (v2 != w) X += sm.part[v2][tw][l];
             gt[jt] = sm.gam[par][16 * tw + r];
             const quad vq = *reinterpret_cast<const quad*>(sm.vst[w][jt] + v_rd);
 #pragma unroll
@@ -675,11 +630,11 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_kernel(PrefillArgs a
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub)
-                Ktf[sub][kk] = Ops::pack(Ops::mma(kf[2 * kk], Iden[sub], zero4()),
-                                         Ops::mma(kf[2 * kk + 1], Iden[sub], zero4()));
-        // operand fragments of the next chunk
-        frag kn[4], qn[4];
-        fetch(kn, qn);
+                Ktf[sub][kk] = Ops::pack(Ops::mma(cur.kf[2 * kk], Iden[sub], zero4()),
+                                         Ops::mma(cur.kf[2 * kk + 1], Iden[sub], zero4()));
+        __builtin_amdgcn_sched_barrier(0);
+        ctx.load_kg(cur, j + 2, pre);
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();                                                        // E2
         const frag Rb0 = frag_nat(sm.Rt, RLD, r, 0), Rb1 = frag_nat(sm.Rt, RLD, r, 32);
 #pragma unroll
@@ -696,13 +651,17 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_kernel(PrefillArgs a
             *reinterpret_cast<quad*>(&sm.Ut[r * RLD + 16 * tw + 4 * gq]) = uq;
             *reinterpret_cast<quad*>(&sm.Dt[r * RLD + 16 * tw + 4 * gq]) = dq;
         }
+        __builtin_amdgcn_sched_barrier(0);
+        ctx.load_t(cur, j + 2, pre);
+        __builtin_amdgcn_sched_barrier(0);
         f32x4 Y[TPW];
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt) {
             const int tw = w + NWS * jt;
-            Y[jt] = sm.part[0][4 + tw][l];
+            Y[jt] = Yp[tw];
 #pragma unroll
-            for (int v2 = 1; v2 < NWS; ++v2) Y[jt] += sm.part[v2][4 + tw][l];
+            for (int v2 = 0; v2 < NWS; ++v2)
+                if (v2 != w) Y[jt] += sm.part[v2][4 + tw][l];
         }
         __syncthreads();                                                        // E3
         // ---- S_w^T <- gamma_n S_w^T + K_w^T (D o U)   (the serial chain first)
@@ -716,8 +675,9 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_kernel(PrefillArgs a
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt)
             Ot[jt] = Ops::mma(Ub1, cur.p[jt][1], Ops::mma(Ub0, cur.p[jt][0], gt[jt] * Y[jt]));
-        // this chunk's V, T~ and P are consumed: fetch those of chunk j+2
-        ctx.load_vtp(cur, j + 2, j + 2 < nchunks);
+        __builtin_amdgcn_sched_barrier(0);
+        ctx.load_p(cur, j + 2, pre);
+        __builtin_amdgcn_sched_barrier(0);
         // O through the wave's V/O area to row-wise stores; rows past the end
         // of the sequence fall outside the resource
         {
@@ -734,37 +694,52 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_kernel(PrefillArgs a
             wave_lds_fence();
 #pragma unroll
             for (int jt = 0; jt < TPW; ++jt)
-                B::store4(*reinterpret_cast<const quad*>(sm.vst[w][jt] + v_wr), ro, ctx.v_voff[jt], 0);
-        }
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm) {
-            kf[tm] = kn[tm];
-            qf[tm] = qn[tm];
+                B::store4(*reinterpret_cast<const quad*>(sm.vst[w][jt] + v_wr), ro, ctx.v_voff[jt]);
         }
     };
 
-    // Chunks are processed in pairs.  An odd count gets one trailing empty
-    // chunk, which is an exact no-op: its loads read zeros (gates 0, so
-    // gamma_n = 1 and S is unchanged) and its stores are dropped.  Keeping
-    // the loop free of an early exit keeps the load order identical on every
-    // path into the loop, so the memory-counter waits stay exact.
-    KQG ka, kb;
-    VTP va, vb;
-    ctx.load_kqg(ka, 0, nchunks > 0);
-    ctx.load_vtp(va, 0, nchunks > 0);
-    ctx.load_kqg(kb, 1, nchunks > 1);
-    ctx.load_vtp(vb, 1, nchunks > 1);
-    stage(ka, 0);
-    ctx.load_kqg(ka, 2, nchunks > 2);
-    fetch(kf, qf);
+    // Chunks are processed in pairs (stages A, B).  An odd count gets one
+    // trailing empty chunk, which is an exact no-op: its loads read zeros
+    // (gates 0, so gamma_n = 1 and S is unchanged) and its stores are dropped.
+    // Keeping the loop free of an early exit keeps the load order identical on
+    // every path into the loop, so the memory-counter waits stay exact.
+    St A, Bs;
+    ctx.load(A, 0, nchunks > 0);
+    ctx.load(Bs, 1, nchunks > 1);
+    gates(A, 0);
     __syncthreads();   // gates of chunk 0
     for (int64_t j = 0; j < nchunks; j += 2) {
-        chunk(va, kb, j, 0);
-        chunk(vb, ka, j + 1, 1);
+        chunk(A, Bs, j, 0);
+        chunk(Bs, A, j + 1, 1);
     }
     if (a.final_state) {
         *reinterpret_cast<f32x4*>(a.final_state + srow) = S[0];
         *reinterpret_cast<f32x4*>(a.final_state + srow + 4) = S[1];
+    }
+}
+
+template <typename OP, int DK>
+__global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_kernel(PrefillArgs a, int xcd_map) {
+    __shared__ ScanSmem<OP, DK> sm;
+    // Work item (chain, 16-column block).  With xcd_map, the 8 column blocks of
+    // a chain get workgroup ids that the dispatcher sends to one XCD, so they
+    // share that XCD's L2 for K, Q, T~ and P.
+    int chain, blk;
+    {
+        const int L = blockIdx.x, nblk = a.dv / 16;
+        if (xcd_map) {
+            chain = (L & 7) + 8 * (L / 64);
+            blk = (L >> 3) & 7;
+        } else {
+            chain = L / nblk;
+            blk = L - chain * nblk;
+        }
+    }
+    switch (wave_id()) {
+        case 0: scan_wave<OP, DK, 0>(a, sm, chain, blk); break;
+        case 1: scan_wave<OP, DK, 1>(a, sm, chain, blk); break;
+        case 2: if constexpr (DK / 32 > 2) scan_wave<OP, DK, 2>(a, sm, chain, blk); break;
+        default: if constexpr (DK / 32 > 3) scan_wave<OP, DK, 3>(a, sm, chain, blk); break;
     }
 }
 

@@ -173,7 +173,7 @@ gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, con
     if (a.num_slots > INT32_MAX) return fail(GDN_ERROR_NOT_SUPPORTED, "too many chunks");
 
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const gdn::PrefillWorkspace wl(a.num_slots, a.hqk, a.hv, shape->head_dim_k, bf16 ? 2 : 4);
+    const gdn::PrefillWorkspace wl(a.num_slots, a.hv, shape->head_dim_k, shape->head_dim_v, bf16 ? 2 : 4);
     const int64_t wbytes = wl.total;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(GDN_ERROR_LAUNCH, "hipGetDevice failed");
@@ -184,12 +184,13 @@ gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, con
         return fail(GDN_ERROR_OUT_OF_MEMORY, "prefill workspace of %lld bytes", (long long)wbytes);
     }
     char* wc = static_cast<char*>(ws);
-    a.ws_t = wc + wl.t;
+    a.ws_w = wc + wl.w;
+    a.ws_q = wc + wl.q;
+    a.ws_k = wc + wl.k;
+    a.ws_u = wc + wl.u;
     a.ws_p = wc + wl.p;
     a.ws_g = reinterpret_cast<float*>(wc + wl.g);
-    a.ws_k = wc + wl.k;
-    a.ws_q = wc + wl.q;
-    hipError_t e = gdn::launch_prefill(a, bf16, shape->head_dim_k, st);
+    hipError_t e = gdn::launch_prefill(a, bf16, shape->head_dim_k, shape->head_dim_v, st);
     hipError_t ef = hipFreeAsync(ws, st);
     if (e == hipSuccess) e = ef;
     if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(st);

@@ -37,35 +37,36 @@ struct PrefillArgs {
     int32_t hv;
     int32_t dv;
     int64_t num_slots;         // ceil(num_tokens / 64) + num_seqs
-    // Workspace written by the prep kernel and read by the scan, in the order
-    // of the scan's operand fragments ("fragment-major"):
-    void* ws_t;                // per (slot, value head): 64 x 64 T~ = (I + A)^-1 diag(beta)
-    void* ws_p;                // per (slot, value head): 64 x 64 P = lower_incl(Gamma o Q K^T)
-    float* ws_g;               // per (slot, value head): 64 pairs (G2_t, G2_last - G2_t)
-    void* ws_k;                // per (slot, q/k head): the chunk's 64 x dk block of K
-    void* ws_q;                // per (slot, q/k head): the chunk's 64 x dk block of Q
+    // Workspace written by the prep kernel and read by the scan, per (slot,
+    // value head), in the order of the scan's matrix-core operands:
+    void* ws_w;                // 64 x dk  W  = T~ diag(gamma) K
+    void* ws_q;                // 64 x dk  Q~ = diag(gamma) Q
+    void* ws_k;                // dk x 64  K~^T = (diag(e^{G_last - G}) K)^T
+    void* ws_u;                // 64 x dv  u  = T~ V
+    void* ws_p;                // 64 x 64  P  = lower_incl(Gamma o Q K^T)
+    float* ws_g;               // G2_last: log2 of the chunk's total decay
 };
 
 // Workspace layout of one prefill call (byte offsets of each part and total),
 // element size 2 for bf16, 4 for fp32.
 struct PrefillWorkspace {
-    int64_t t, p, g, k, q, total;
-    PrefillWorkspace(int64_t num_slots, int hqk, int hv, int dk, int elem_size) {
-        const int64_t mat = num_slots * hv * 64 * 64 * (int64_t)elem_size;
-        const int64_t gate = num_slots * hv * 64 * 2 * 4;
-        const int64_t kq = num_slots * hqk * 64 * (int64_t)dk * elem_size;
-        t = 0;
-        p = t + mat;
-        g = p + mat;
-        k = g + gate;
-        q = k + kq;
-        total = q + kq;
+    int64_t w, q, k, u, p, g, total;
+    PrefillWorkspace(int64_t num_slots, int hv, int dk, int dv, int elem_size) {
+        const int64_t blocks = num_slots * hv;
+        const int64_t mk = blocks * 64 * (int64_t)dk * elem_size;
+        w = 0;
+        q = w + mk;
+        k = q + mk;
+        u = k + mk;
+        p = u + blocks * 64 * (int64_t)dv * elem_size;
+        g = p + blocks * 64 * 64 * (int64_t)elem_size;
+        total = g + ((blocks * 4 + 255) / 256) * 256;
     }
 };
 
 // Launchers: return hipSuccess or the launch error.  `bf16` selects the
 // element type of q/k/v/out; dk/dv are 64 or 128.
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, int dk, int dv, hipStream_t s);
-hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int dk, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int dk, int dv, hipStream_t s);
 
 }  // namespace gdn

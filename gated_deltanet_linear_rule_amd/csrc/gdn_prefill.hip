@@ -5,23 +5,28 @@
 // "Qwen3.8-Flash-Next architecture", "Der Weg eines Tokens durch das
 // Modell", item 1) is evaluated over chunks of C = 64 tokens.  Within a chunk
 // with start state S, cumulative log-decay G_t = g_1 + ... + g_t (so every
-// exponent below is <= 0), gamma_t = e^{G_t}, Gamma_ts = e^{G_t - G_s}:
+// exponent below is <= 0), gamma_t = e^{G_t}, Gamma_ts = e^{G_t - G_s},
+// D_t = e^{G_last - G_t}:
 //
 //   A  = strict_lower(diag(beta) (Gamma o K K^T)),   T = (I + A)^{-1}
-//   T~ = T diag(beta),   P = lower_incl(Gamma o Q K^T)         [state-free]
-//   R  = V - diag(gamma) K S^T
-//   U  = T~ R                       (the chunk's effective writes u_t)
-//   O  = diag(gamma) Q S^T + P U
-//   S' = gamma_n S + U^T diag(e^{G_n - G}) K
+//   T~ = T diag(beta)
+//   W  = T~ diag(gamma) K,   u = T~ V                            [state-free]
+//   K~ = diag(D) K,   Q~ = diag(gamma) Q,   P = lower_incl(Gamma o Q K^T)
+//   U  = u - W S^T            (the chunk's effective writes u_t)
+//   O  = Q~ S^T + P U
+//   S' = gamma_last S + U^T K~
+//
+// (U = T~ (V - diag(gamma) K S^T) is the WY / UT form of the chunk's
+// sequential delta-rule writes; the rest follows by expanding the product of
+// the per-token transitions over the chunk.)
 //
 // Two kernels:
 //  * gdn_prep_kernel  -- one workgroup per (chunk, value head), all chunks in
-//    parallel: stages K and Q in LDS, the gate cumsum (fp64), Gamma-weighted
-//    K K^T and Q K^T on bf16 (or fp32) matrix cores, the unit-lower-triangular
-//    inverse in LDS (16x16 diagonal blocks by forward substitution,
-//    off-diagonal blocks by fp32 MFMA block products), and writes T~, P (in
-//    the order the scan's operand fragments use) and the chunk's gates to a
-//    workspace.
+//    parallel: the gate cumsum (fp64), Gamma-weighted K K^T and Q K^T on the
+//    matrix cores, the unit-lower-triangular inverse (16x16 diagonal blocks by
+//    forward substitution, off-diagonal blocks by fp32 MFMA block products),
+//    then W, u, K~^T, Q~ and P, written to a workspace in exactly the
+//    register layout in which the scan feeds them to its matrix cores.
 //  * gdn_scan_kernel  -- sequential over the chunks of one sequence, parallel
 //    over (sequence, value head, 16-column block of d_v); the d_k rows of the
 //    state block are split over the workgroup's waves and stay in fp32
@@ -29,13 +34,10 @@
 //    kernel).
 //
 // Exponentials use exp2 of log2-scaled cumulative gates (G2 = G log2 e).
-// Padding: a final partial chunk is padded with k = q = 0, g = 0, beta = 0 in
-// the prep kernel; padded rows then carry u = 0 (their rows and columns of
-// T~ vanish), so they leave S and the real rows untouched whatever the scan
-// reads for them, and gamma_n = e^{G2_63} equals the decay up to the last
-// real token.
-#include <cstdlib>
-
+// Padding: a final partial chunk is padded with k = q = v = 0, g = 0,
+// beta = 0 in the prep kernel; padded rows then carry u = 0 and zero rows of
+// W and K~, so they leave S and the real rows untouched, and
+// gamma_last = e^{G2_63} equals the decay up to the last real token.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -43,13 +45,8 @@ namespace gdn {
 namespace {
 
 constexpr int kPrepThreads = 256;
-constexpr float kLog2e = 1.4426950408889634f;
 
 template <typename OP> constexpr int pad_elems() { return 16 / (int)sizeof(OP); }
-
-template <typename OP> struct VecE;                       // 16 bytes as elements
-template <> struct VecE<__bf16> { using type = bf16x8; };
-template <> struct VecE<float> { using type = f32x4; };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -111,60 +108,115 @@ __device__ __forceinline__ double lane63_f64(double x) {
     return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned)lo);
 }
 
+// A/B fragment of a row-major LDS matrix in natural K order: k0 + 8 gq + (0..7).
+template <typename T>
+__device__ __forceinline__ typename Op<T>::frag frag_nat(const T* M, int ld, int row, int k0) {
+    using frag = typename Op<T>::frag;
+    return *reinterpret_cast<const frag*>(M + (size_t)row * ld + k0 + 8 * (lane_id() >> 4));
+}
+
 // ===========================================================================
 // workspace layout shared by the two kernels
 // ===========================================================================
-// Every matrix the scan reads as matrix-core operands is stored
-// fragment-major: 16-byte unit e = (f * FU + u) * 64 + lane holds unit u of
-// operand fragment f for that lane, so a wave reads a fragment as one
-// contiguous 1 KB block.  A fragment holds, for lane (r, gq) =
-// (lane & 15, lane >> 4), eight elements of row r of a 16-row tile, columns
-// c0 + 8 gq .. c0 + 8 gq + 7 (u = 0, 1 split them for fp32).
-//  * T~ and P of a (chunk, value head): f = tw * 2 + kk, rows 16 tw + r,
-//    c0 = 32 kk (64 x 64);
-//  * K and Q of a (chunk, q/k head): f = w * 4 + tm, rows 16 tm + r (tokens),
-//    c0 = 32 w (64 x d_k; the scan's wave w owns d_k columns 32 w .. 32 w + 31).
-// The gates of a chunk are 64 float pairs (G2_t, G2_last - G2_t), the
-// difference taken in fp64; zeros (what a read past the end returns) stand
-// for a chunk without decay.
-template <typename OP> struct FragMajor {
+// Operand fragments are stored fragment-major: 16-byte unit
+//     e = (f * FU + u) * 64 + lane
+// holds unit u of fragment f for that lane (FU = 1 for bf16, 2 for fp32), so
+// a wave reads a fragment as one contiguous 1 KB block.  Lane (r, gq) =
+// (lane & 15, lane >> 4) of a fragment holds 8 elements of row r of a
+// 16-row tile.  Per (chunk, value head), with slice ws = d_k columns
+// 32 ws .. 32 ws + 31 (scan wave ws) and "paired" column order
+//     slot i < 4  <->  c0 + 4 gq + i,     slot 4 + i  <->  c0 + 16 + 4 gq + i:
+//  * W, Q~ : f = ws * 4 + tm, row = token 16 tm + r, paired columns from 32 ws;
+//  * K~^T  : f = (ws * 2 + sub) * 2 + kk, row = d_k 32 ws + 16 sub + r,
+//            paired columns (tokens) from 32 kk;
+//  * P     : f = tw * 2 + kk, row = token 16 tw + r, natural columns
+//            (tokens) 32 kk + 8 gq + (0..7);
+//  * u     : accumulator-major: per (token tile tw, 16-column block cb),
+//            lane (r, gq) holds u[16 tw + 4 gq + i][16 cb + r], i = 0..3;
+//  * G2_last of the chunk as one float (0, as read past the end, means no
+//    decay).
+template <typename OP> struct Frag {
     static constexpr int VE = 16 / (int)sizeof(OP);      // elements per 16-byte unit
     static constexpr int FU = 8 / VE;                    // units per operand fragment
-    static constexpr int UNITS = kChunk * kChunk / VE;   // of a 64 x 64 matrix
-    __device__ __forceinline__ static int frag_of(int e) { return (e >> 6) / FU; }
-    __device__ __forceinline__ static int col_in(int e) { return 8 * ((e >> 4) & 3) + VE * ((e >> 6) % FU); }
-    // 64 x 64 (T~, P)
-    __device__ __forceinline__ static int row(int e) { return 16 * (frag_of(e) >> 1) + (e & 15); }
-    __device__ __forceinline__ static int col(int e) { return 32 * (frag_of(e) & 1) + col_in(e); }
-    // 64 x d_k (K, Q)
-    __device__ __forceinline__ static int kq_row(int e) { return 16 * (frag_of(e) & 3) + (e & 15); }
-    __device__ __forceinline__ static int kq_col(int e) { return 32 * (frag_of(e) >> 2) + col_in(e); }
 };
-constexpr int kGateFloats = 2 * kChunk;   // floats per (chunk, value head)
+
+template <typename OP>
+__device__ __forceinline__ void store_frag(OP* base, int f, const typename Op<OP>::frag& x) {
+    constexpr int VE = Frag<OP>::VE, FU = Frag<OP>::FU;
+    const int l = lane_id();
+    if constexpr (FU == 1) {
+        *reinterpret_cast<typename Op<OP>::frag*>(base + ((size_t)f * 64 + l) * VE) = x;
+    } else {
+        *reinterpret_cast<f32x4*>(base + ((size_t)(f * 2) * 64 + l) * VE) =
+            __builtin_shufflevector(x, x, 0, 1, 2, 3);
+        *reinterpret_cast<f32x4*>(base + ((size_t)(f * 2 + 1) * 64 + l) * VE) =
+            __builtin_shufflevector(x, x, 4, 5, 6, 7);
+    }
+}
+
+// Identity fragment for exact transposes on the matrix cores: as the B
+// operand of a product whose K range is 32 consecutive columns c0 + (0..31)
+// (natural order), it selects column c0 + 16 sub + n into output column n.
+template <typename OP>
+__device__ __forceinline__ typename Op<OP>::frag iden_frag(int sub) {
+    typename Op<OP>::frag x;
+    const int l = lane_id(), n = l & 15, gq = l >> 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = from_f32<OP>((8 * gq + i == 16 * sub + n) ? 1.f : 0.f);
+    return x;
+}
+
+// Rows 32 kk + (0..31) of a row-major LDS matrix, columns c0 + 16 sub +
+// (0..15), transposed into an operand fragment whose K order is the paired
+// row order: lane (n, gq) gets M[32 kk + 4 gq + i][c0 + 16 sub + n] and
+// M[32 kk + 16 + 4 gq + i][c0 + 16 sub + n].  Exact (products with 0 and 1);
+// I = iden_frag(sub).
+template <typename OP>
+__device__ __forceinline__ typename Op<OP>::frag transpose_frag(const OP* M, int ld, int kk, int c0,
+                                                               const typename Op<OP>::frag& I) {
+    using Ops = Op<OP>;
+    const int r = lane_id() & 15;
+    const f32x4 lo = Ops::mma(frag_nat(M, ld, 32 * kk + r, c0), I, zero4());
+    const f32x4 hi = Ops::mma(frag_nat(M, ld, 32 * kk + 16 + r, c0), I, zero4());
+    return Ops::pack(lo, hi);
+}
 
 // ===========================================================================
-// prep: T~ and P for one (chunk, value head)
+// prep: W, u, K~^T, Q~, P and G2_last for one (chunk, value head)
 // ===========================================================================
-template <typename OP, int DK>
+template <typename OP, int DK, int DV>
 struct PrepSmem {
-    static constexpr int LD = DK + pad_elems<OP>();
-    static constexpr int LDP = kChunk + pad_elems<OP>();
-    alignas(16) OP K[kChunk * LD];     // later: T~ (LDP rows) for the store
-    alignas(16) OP Q[kChunk * LD];
-    alignas(16) OP P[kChunk * LDP];    // P staged for the store
-    alignas(16) float A[kChunk][kChunk + 4];
+    static constexpr int PAD = pad_elems<OP>();
+    static constexpr int LD = DK + PAD;                      // K rows
+    static constexpr int LDQV = (DK > DV ? DK : DV) + PAD;   // Q rows, later V rows
+    static constexpr int LDP = kChunk + PAD;                 // P, T~, T~ diag(gamma) rows
+    alignas(16) OP K[kChunk * LD];
+    alignas(16) OP QV[kChunk * LDQV];
+    alignas(16) OP P[kChunk * LDP];                          // P, later T~
+    alignas(16) float A[kChunk][kChunk + 4];                 // A, later T~ diag(gamma) (OP, LDP rows)
     alignas(16) float T[kChunk][kChunk + 4];
-    alignas(16) double G[kChunk];      // log2-scaled cumulative gates (fp64)
-    alignas(16) float B[kChunk];
+    alignas(16) double G[kChunk];                            // log2-scaled cumulative gates (fp64)
+    alignas(16) float B[kChunk];                             // beta
+    alignas(16) float gam[kChunk];                           // e^{G_t}
+    alignas(16) float dec[kChunk];                           // e^{G_last - G_t}
 };
 
-template <typename OP, int DK>
+template <typename OP, int DK, int DV>
 __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
     using Ops = Op<OP>;
-    using Sm = PrepSmem<OP, DK>;
-    constexpr int LD = Sm::LD, LDP = Sm::LDP;
-    constexpr int VE = 16 / (int)sizeof(OP);      // elements per 16-byte vector
-    constexpr int NV = DK / VE;                    // vectors per K/Q row
+    using frag = typename Ops::frag;
+    using quad = typename Ops::quad;
+    using Sm = PrepSmem<OP, DK, DV>;
+    constexpr int LD = Sm::LD, LDQV = Sm::LDQV, LDP = Sm::LDP;
+    constexpr int VE = Frag<OP>::VE;                       // elements per 16-byte vector
+    constexpr int FU = Frag<OP>::FU;
+    constexpr int NV = DK / VE;                            // vectors per K/Q row
+    constexpr int NVV = DV / VE;                           // vectors per V row
+    constexpr int VREG = kChunk * NVV / kPrepThreads;      // V vectors per thread
+    constexpr int NS = DK / 32;                            // scan slices of d_k
+    constexpr int NCP = DV / 32;                           // pairs of 16-column blocks of d_v
+    static_assert(VREG * kPrepThreads == kChunk * NVV, "V staging");
+    static_assert(sizeof(OP) * kChunk * LDP <= sizeof(float) * kChunk * (kChunk + 4), "T~ diag(gamma) in A");
     __shared__ Sm sm;
 
     const int64_t slot = blockIdx.x;
@@ -176,10 +228,17 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
     const int nt = (int)((t1 - t0) < kChunk ? (t1 - t0) : kChunk);
     const int hq = (h * a.hqk) / a.hv;
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), r = l & 15, gq = l >> 4;
+    const size_t blk = (size_t)slot * a.hv + h;
+    OP* const Ww = static_cast<OP*>(a.ws_w) + blk * (kChunk * DK);
+    OP* const Qw = static_cast<OP*>(a.ws_q) + blk * (kChunk * DK);
+    OP* const Kw = static_cast<OP*>(a.ws_k) + blk * (kChunk * DK);
+    OP* const Uw = static_cast<OP*>(a.ws_u) + blk * (kChunk * DV);
+    OP* const Pw = static_cast<OP*>(a.ws_p) + blk * (kChunk * kChunk);
 
-    // ---- stage K, Q (rows past the end are zero) and the gates
+    // ---- stage K, Q (rows past the end are zero), V into registers, gates
     const OP* kg = static_cast<const OP*>(a.k);
     const OP* qg = static_cast<const OP*>(a.q);
+    const OP* vg = static_cast<const OP*>(a.v);
     for (int e = tid; e < kChunk * NV; e += kPrepThreads) {
         const int row = e / NV, cv = e - row * NV;
         const int rc = row < nt ? row : nt - 1;
@@ -187,7 +246,16 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
         u32x4 kv = ld16(kg + off), qv = ld16(qg + off);
         if (row >= nt) { kv = zero_u4(); qv = zero_u4(); }
         *reinterpret_cast<u32x4*>(&sm.K[row * LD + cv * VE]) = kv;
-        *reinterpret_cast<u32x4*>(&sm.Q[row * LD + cv * VE]) = qv;
+        *reinterpret_cast<u32x4*>(&sm.QV[row * LDQV + cv * VE]) = qv;
+    }
+    u32x4 vreg[VREG];
+#pragma unroll
+    for (int i = 0; i < VREG; ++i) {
+        const int e = tid + i * kPrepThreads;
+        const int row = e / NVV, cv = e - row * NVV;
+        const int rc = row < nt ? row : nt - 1;
+        vreg[i] = ld16(vg + ((size_t)(t0 + rc) * a.hv + h) * DV + (size_t)cv * VE);
+        if (row >= nt) vreg[i] = zero_u4();
     }
     if (w == 0) {
         const int lc = l < nt ? l : nt - 1;
@@ -195,24 +263,44 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
         float bv = a.beta[(size_t)(t0 + lc) * a.hv + h];
         if (l >= nt) { gv = 0.f; bv = 0.f; }
         const double G = wave_cumsum_f64((double)gv * 1.4426950408889634);
+        const double Gl = lane63_f64(G);
         sm.G[l] = G;
         sm.B[l] = bv;
-        const double Gl = lane63_f64(G);
-        reinterpret_cast<f32x2*>(a.ws_g + ((size_t)slot * a.hv + h) * kGateFloats)[l] =
-            f32x2{(float)G, (float)(Gl - G)};
+        sm.gam[l] = fast_exp2((float)G);
+        sm.dec[l] = fast_exp2((float)(Gl - G));
+        if (l == 0) a.ws_g[blk] = (float)Gl;
     }
     __syncthreads();
 
-    // ---- fragment-major copies of K and Q for the scan (padded rows are
-    // zero); one writer per q/k head
-    if ((h * a.hqk) % a.hv == 0) {
-        using FM = FragMajor<OP>;
-        OP* Kw = static_cast<OP*>(a.ws_k) + ((size_t)slot * a.hqk + hq) * (kChunk * DK);
-        OP* Qw = static_cast<OP*>(a.ws_q) + ((size_t)slot * a.hqk + hq) * (kChunk * DK);
-        for (int e = tid; e < kChunk * DK / VE; e += kPrepThreads) {
-            const int row = FM::kq_row(e), col = FM::kq_col(e);
-            *reinterpret_cast<u32x4*>(Kw + e * VE) = ld16(sm.K + row * LD + col);
-            *reinterpret_cast<u32x4*>(Qw + e * VE) = ld16(sm.Q + row * LD + col);
+    // ---- per wave (scan slice ws = w): Q~ fragments, and K^T fragments by
+    // exact identity products -- kept for W, stored as K~^T = K^T diag(D)
+    frag Ktr[2][2];
+    if (w < NS) {
+        const int ws = w;
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) {
+            const int row = 16 * tm + r;
+            const frag q = frag_rows(sm.QV, LDQV, row, 32 * ws);
+            const float gm = sm.gam[row];
+            frag qs;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qs[i] = from_f32<OP>(to_f32(q[i]) * gm);
+            store_frag(Qw, ws * 4 + tm, qs);
+        }
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const frag I = iden_frag<OP>(sub);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                Ktr[sub][kk] = transpose_frag(sm.K, LD, kk, 32 * ws, I);
+                frag ks;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int s = 32 * kk + (i < 4 ? 4 * gq + i : 16 + 4 * gq + i - 4);
+                    ks[i] = from_f32<OP>(to_f32(Ktr[sub][kk][i]) * sm.dec[s]);
+                }
+                store_frag(Kw, (ws * 2 + sub) * 2 + kk, ks);
+            }
         }
     }
 
@@ -220,11 +308,12 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
     for (int job = w; job < 20; job += kPrepThreads / kWave) {
         const bool qk = job >= 10;
         const int tm = kLowerTiles[job % 10][0], tn = kLowerTiles[job % 10][1];
-        const OP* X = qk ? sm.Q : sm.K;
+        const OP* X = qk ? sm.QV : sm.K;
+        const int ldx = qk ? LDQV : LD;
         f32x4 acc = zero4();
 #pragma unroll
         for (int kk = 0; kk < DK / 32; ++kk)
-            acc = Ops::mma(frag_rows(X, LD, 16 * tm + r, 32 * kk), frag_rows(sm.K, LD, 16 * tn + r, 32 * kk), acc);
+            acc = Ops::mma(frag_rows(X, ldx, 16 * tm + r, 32 * kk), frag_rows(sm.K, LD, 16 * tn + r, 32 * kk), acc);
         const int s = 16 * tn + r;
         if (!qk) {
 #pragma unroll
@@ -240,17 +329,21 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
             }
         }
     }
-    __syncthreads();   // K no longer read: its space holds T~ from here on
+    __syncthreads();   // Q done: its space takes V; P is complete
 
-    OP* Pl = sm.P;
-    OP* Tl = sm.K;     // T~ staged as [64][LDP]
-    // strictly-upper 16x16 tiles of P and T~ are zero (read as padding by the scan)
-    for (int e = tid; e < kChunk * kChunk; e += kPrepThreads) {
-        const int t = e >> 6, s = e & 63;
-        if ((s >> 4) > (t >> 4)) {
-            Pl[t * LDP + s] = from_f32<OP>(0.f);
-            Tl[t * LDP + s] = from_f32<OP>(0.f);
-        }
+    // ---- P to the workspace (strictly-upper tiles are zero), V into LDS
+    for (int e = tid; e < kChunk * kChunk / VE; e += kPrepThreads) {
+        const int f = (e >> 6) / FU, ln = e & 63;
+        const int row = 16 * (f >> 1) + (ln & 15);
+        const int col = 32 * (f & 1) + 8 * (ln >> 4) + VE * ((e >> 6) % FU);
+        const u32x4 x = ((col >> 4) > (row >> 4)) ? zero_u4() : ld16(sm.P + row * LDP + col);
+        *reinterpret_cast<u32x4*>(Pw + (size_t)e * VE) = x;
+    }
+#pragma unroll
+    for (int i = 0; i < VREG; ++i) {
+        const int e = tid + i * kPrepThreads;
+        const int row = e / NVV, cv = e - row * NVV;
+        *reinterpret_cast<u32x4*>(&sm.QV[row * LDQV + cv * VE]) = vreg[i];
     }
     // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution
     // (lane c of wave b solves column c of block b), fp32.
@@ -290,22 +383,56 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
         __syncthreads();
     }
 
-    // ---- T~ = T diag(beta) on the lower blocks, staged as OP
+    // ---- T~ = T diag(beta) (into P's space) and T~ diag(gamma) (into A's)
+    OP* const Tb = sm.P;
+    OP* const Tg = reinterpret_cast<OP*>(&sm.A[0][0]);
     for (int e = tid; e < kChunk * kChunk; e += kPrepThreads) {
         const int t = e >> 6, s = e & 63;
-        if ((s >> 4) <= (t >> 4)) Tl[t * LDP + s] = from_f32<OP>((s <= t) ? sm.T[t][s] * sm.B[s] : 0.f);
+        const float x = (s <= t) ? sm.T[t][s] * sm.B[s] : 0.f;
+        Tb[t * LDP + s] = from_f32<OP>(x);
+        Tg[t * LDP + s] = from_f32<OP>(x * sm.gam[s]);
     }
     __syncthreads();
 
-    // ---- T~ and P to the workspace, fragment-major, consecutive lanes on
-    // consecutive 16-byte units
-    using FM = FragMajor<OP>;
-    OP* Pw = static_cast<OP*>(a.ws_p) + ((size_t)slot * a.hv + h) * (kChunk * kChunk);
-    OP* Tw = static_cast<OP*>(a.ws_t) + ((size_t)slot * a.hv + h) * (kChunk * kChunk);
-    for (int e = tid; e < FM::UNITS; e += kPrepThreads) {
-        const int row = FM::row(e), col = FM::col(e);
-        *reinterpret_cast<u32x4*>(Tw + e * VE) = ld16(Tl + row * LDP + col);
-        *reinterpret_cast<u32x4*>(Pw + e * VE) = ld16(Pl + row * LDP + col);
+    // ---- W^T = K^T (T~ diag(gamma))^T for scan slice ws = w; the two 16-row
+    // halves of the slice form the scan's paired-order W fragment
+    if (w < NS) {
+        const int ws = w;
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) {
+            f32x4 acc[2];
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub) {
+                acc[sub] = zero4();
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    acc[sub] = Ops::mma(Ktr[sub][kk], frag_rows(Tg, LDP, 16 * tm + r, 32 * kk), acc[sub]);
+            }
+            store_frag(Ww, ws * 4 + tm, Ops::pack(acc[0], acc[1]));
+        }
+    }
+    // ---- u = T~ V for the column-block pair cp = w, in the scan's
+    // accumulator layout
+    if (w < NCP) {
+        const int cp = w;
+        constexpr int NCB = DV / 16;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const frag I = iden_frag<OP>(sub);
+            frag Vtr[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) Vtr[kk] = transpose_frag(sm.QV, LDQV, kk, 32 * cp, I);
+#pragma unroll
+            for (int tw = 0; tw < 4; ++tw) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) acc = Ops::mma(frag_rows(Tb, LDP, 16 * tw + r, 32 * kk), Vtr[kk], acc);
+                quad uq;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) uq[i] = from_f32<OP>(acc[i]);
+                *reinterpret_cast<quad*>(Uw + ((size_t)(tw * NCB + 2 * cp + sub) * 64 + l) * 4) = uq;
+            }
+        }
     }
 }
 
@@ -314,30 +441,27 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
 // ===========================================================================
 // One workgroup per (sequence, value head, 16-column block of d_v).  Its
 // NWS = DK / 32 waves split d_k: wave w owns state rows S[:, 32w .. 32w+32)
-// as two fp32 accumulator tiles (d_k x 16).  Inside the slice the d_k order of
-// the tiles is permuted (tile `sub`, row 4 gq + i  <->  d_k 8 gq + 4 sub + i)
-// so that an operand fragment of K or Q pairs with the state tiles directly.
-// Wave w also owns token tiles tw = w + NWS jt (jt < TPW = 4 / NWS).  Per chunk:
-//   wave w:  X_w^T = S_w K_w^T,  Y_w^T = S_w Q_w^T          (partial over d_k)
-//   E1 (LDS): X partials -> the owner of token tile tw sums X^T there
-//   owner:   R^T = V^T - X^T diag(gamma)
-//            K_w^T in operand layout via an exact identity product
-//   E2 (LDS): R for all tokens to every wave, Y partials to the owners
-//   owner:   U = T~_tw R,  D o U  (D = e^{G_last - G_t} per token)
-//   E3 (LDS): U and D o U for all tokens to every wave
-//   wave w:  S_w^T <- gamma_n S_w^T + K_w^T (D o U)
-//   owner:   O^T = Y^T diag(gamma) + U^T P_tw^T
+// as two fp32 accumulator tiles S^T (16 d_k rows x 16 columns each, tile `sub`
+// holding d_k 32 w + 16 sub + (0..15)); packed together they are the state's
+// operand fragment in paired d_k order.  Wave w also owns token tiles
+// tw = w + NWS jt (jt < TPW = 4 / NWS).  Per chunk:
+//   wave w:  Z_w = W_w S_w^T,  Y_w^T = S_w Q~_w^T        (partial over d_k)
+//   E1 (LDS): Z partials -> the owner of token tile tw sums Z there
+//   owner:   U = u - Z for its tokens, to LDS
+//   E2 (LDS): U for all tokens to every wave, Y partials to the owners
+//   wave w:  S_w^T <- gamma_last S_w^T + K~_w^T U
+//   owner:   O^T = Y^T + U^T P_tw^T
 // A wave keeps its own partial tiles in registers and writes only the tiles
 // other waves own.
 //
 // Global memory.  The vector memory path serves a wave request four lanes at
 // a time, and four lanes on four different rows cost four times as much as
 // four lanes on one 64-byte piece, so every access keeps consecutive lanes on
-// consecutive bytes: K, Q, T~ and P come fragment-major from the prep
-// kernel's workspace (one 1 KB block per fragment), the gates as one
-// 512-byte record per chunk, and V and O pass through a small wave-private
-// LDS area between their row-wise global form and the lanes' tile layout.
-// Operands are fetched two chunks ahead into registers.  All loads go
+// consecutive bytes: all operands come fragment-major from the prep kernel's
+// workspace (one 1 KB block per fragment; u as 8-byte lane records), and O
+// passes through a small wave-private LDS area between the lanes' tile layout
+// and row-wise global stores.  Operands are fetched two chunks ahead, in three
+// groups issued as soon as the registers they refill are free.  All loads go
 // through buffer resources (reads past the end of a resource return 0, writes
 // past it are dropped), and no load, store or use of a loaded value sits
 // behind a branch, so the compiler's memory-counter waits stay exact.
@@ -378,19 +502,19 @@ template <> struct Buf<float> {
     }
 };
 
-// A/B fragment of a row-major LDS matrix in natural K order: k0 + 8 gq + (0..7).
-template <typename T>
-__device__ __forceinline__ typename Op<T>::frag frag_nat(const T* M, int ld, int row, int k0) {
-    using frag = typename Op<T>::frag;
-    return *reinterpret_cast<const frag*>(M + (size_t)row * ld + k0 + 8 * (lane_id() >> 4));
-}
-
-// XOR swizzle of the V/O staging tiles (16 rows of four 4-element quads): the
+// XOR swizzle of the O staging tiles (16 rows of four 4-element quads): the
 // quad index is XORed with a function of the row so that both the row-wise
 // side (four lanes per row) and the tile side (one row per lane) spread over
 // the LDS banks.
 __device__ __forceinline__ int swz_vo(int row, int elem) {
     return elem == 2 ? ((row >> 2) & 3) : (((row >> 1) ^ (row >> 3)) & 3);
+}
+
+// Keeps a group of loads where it stands: no memory operation moves across
+// this point, in either direction, at any stage of compilation.
+__device__ __forceinline__ void pin() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Orders this wave's LDS writes before its later LDS reads of the same area.
@@ -403,23 +527,19 @@ struct ScanGeom {
     static constexpr int NWS = DK / 32;                 // waves per workgroup (d_k split)
     static constexpr int TPW = 4 / NWS;                 // token tiles per wave
     static constexpr int E = (int)sizeof(OP);
-    static constexpr int FU = 8 * E / 16;               // 16-byte units per operand fragment
-    static constexpr int QE = 4 * E;                    // bytes per V/O quad
-    static constexpr int VROWB = 16 * E;                // bytes per V/O tile row
-    static constexpr int VB = 16 * VROWB;               // bytes per V/O tile
+    static constexpr int FU = Frag<OP>::FU;             // 16-byte units per operand fragment
+    static constexpr int QE = 4 * E;                    // bytes per 4-element quad
+    static constexpr int VROWB = 16 * E;                // bytes per O tile row
+    static constexpr int VB = 16 * VROWB;               // bytes per O tile
     static constexpr int RLD = kChunk + (E == 2 ? 8 : 4);   // 16-byte rows, staggered banks
 };
 
 template <typename OP, int DK>
 struct ScanSmem {
     using G = ScanGeom<OP, DK>;
-    f32x4 part[G::NWS][8][kWave];        // X^T partials (0..3) and Y^T partials (4..7)
-    alignas(16) OP Rt[16 * G::RLD];      // R as [column][token]
+    f32x4 part[G::NWS][8][kWave];        // Z partials (0..3) and Y^T partials (4..7)
     alignas(16) OP Ut[16 * G::RLD];      // U as [column][token]
-    alignas(16) OP Dt[16 * G::RLD];      // D o U as [column][token]
-    alignas(16) float gam[2][kChunk];    // by chunk parity: e^{G_t}
-    alignas(16) float dec[2][kChunk];    //                  e^{G_last - G_t}
-    alignas(16) char vst[G::NWS][G::TPW][G::VB];   // wave-private V / O tiles
+    alignas(16) char ost[G::NWS][G::TPW][G::VB];   // wave-private O tiles
 };
 
 template <typename OP, int DK>
@@ -429,101 +549,89 @@ struct ScanCtx {
     using frag = typename Op<OP>::frag;
     using quad = typename Op<OP>::quad;
     static constexpr int NWS = G::NWS, TPW = G::TPW, E = G::E, FU = G::FU;
-    // One chunk's operands for one wave, in the order the chunk uses them.
+    // One chunk's operands for one wave.
     struct Stage {
-        f32x2 gate;          // (G2_l, G2_last - G2_l) of token `lane`
-        frag kf[4];          // K[16 tm + r][32 w + 8 gq + (0..7)]
-        frag qf[4];          // Q, same positions
-        quad v[TPW];         // V[16 tw + (l >> 2)][16 blk + 4 (l & 3) + (0..3)]
-        frag t[TPW][2];      // T~[16 tw + r][32 kk + 8 gq + (0..7)]
-        frag p[TPW][2];      // P, same positions
+        frag wf[4];          // W[16 tm + r][paired d_k of slice w]
+        frag qf[4];          // Q~, same positions
+        quad u[TPW];         // u[16 tw + 4 gq + i][16 blk + r]
+        frag kt[2][2];       // K~^T[32 w + 16 sub + r][paired tokens from 32 kk]
+        float gl;            // G2_last
+        frag p[TPW][2];      // P[16 tw + r][32 kk + 8 gq + (0..7)]
     };
 
-    // per-sequence: byte address of the sequence's first chunk in each tensor
-    const char* kb; const char* qb; const char* gb;
-    const char* tb; const char* pb;
-    const char* vb; int64_t vn;                 // V: and the bytes to its end
-    int64_t kq_step, g_step, w_step, v_step;    // bytes per chunk step
-    int v_row;                                  // bytes per token row of V and O
+    // per-sequence: byte address of the sequence's first chunk in each part
+    const char* wb; const char* qb; const char* kb; const char* ub; const char* pb; const char* gb;
+    int64_t m_step, u_step, p_step, g_step;    // bytes per chunk step
+    int u_bytes;                               // bytes of one u block
+    int v_row;                                 // bytes per token row of O
     int w;
     // Loop-invariant per-lane byte offsets.  Row offsets that a bounds check
     // must see stay in the per-lane offset; the scalar offset only carries
     // fragment offsets inside a fully valid block.
-    unsigned v_voff[TPW];   // row-wise V/O of tile tw: row 16 tw + (l >> 2), quad l & 3
+    unsigned o_voff[TPW];   // row-wise O of tile tw: row 16 tw + (l >> 2), quad l & 3
+    unsigned u_voff[TPW];   // u record of (tw, blk) for this lane
     unsigned f_voff;        // fragment-major blocks: unit `lane`
-    unsigned g_voff;        // gate pair of token `lane`
 
-    __device__ __forceinline__ void init(const PrefillArgs& a, int64_t s0, int64_t base, int h, int blk,
-                                         int wave) {
+    __device__ __forceinline__ void init(const PrefillArgs& a, int64_t base, int h, int blk, int wave) {
         const int l = lane_id();
-        const int hq = (h * a.hqk) / a.hv;
         w = wave;
-        const size_t kq0 = ((size_t)base * a.hqk + hq) * (kChunk * DK);
-        kb = reinterpret_cast<const char*>(static_cast<const OP*>(a.ws_k) + kq0);
-        qb = reinterpret_cast<const char*>(static_cast<const OP*>(a.ws_q) + kq0);
-        const size_t w0 = ((size_t)base * a.hv + h) * (kChunk * kChunk);
-        tb = reinterpret_cast<const char*>(static_cast<const OP*>(a.ws_t) + w0);
-        pb = reinterpret_cast<const char*>(static_cast<const OP*>(a.ws_p) + w0);
-        gb = reinterpret_cast<const char*>(a.ws_g + ((size_t)base * a.hv + h) * kGateFloats);
-        const size_t v0 = ((size_t)s0 * a.hv + h) * a.dv + blk * 16;
-        vb = reinterpret_cast<const char*>(static_cast<const OP*>(a.v) + v0);
-        vn = ((int64_t)a.num_tokens * a.hv * a.dv - (int64_t)v0) * E;
+        const size_t b0 = (size_t)base * a.hv + h;
+        wb = reinterpret_cast<const char*>(static_cast<const OP*>(a.ws_w) + b0 * (kChunk * DK));
+        qb = reinterpret_cast<const char*>(static_cast<const OP*>(a.ws_q) + b0 * (kChunk * DK));
+        kb = reinterpret_cast<const char*>(static_cast<const OP*>(a.ws_k) + b0 * (kChunk * DK));
+        ub = reinterpret_cast<const char*>(static_cast<const OP*>(a.ws_u) + b0 * ((size_t)kChunk * a.dv));
+        pb = reinterpret_cast<const char*>(static_cast<const OP*>(a.ws_p) + b0 * (kChunk * kChunk));
+        gb = reinterpret_cast<const char*>(a.ws_g + b0);
+        m_step = (int64_t)a.hv * kChunk * DK * E;
+        u_step = (int64_t)a.hv * kChunk * a.dv * E;
+        p_step = (int64_t)a.hv * kChunk * kChunk * E;
+        g_step = (int64_t)a.hv * 4;
+        u_bytes = kChunk * a.dv * E;
         v_row = a.hv * a.dv * E;
-        kq_step = (int64_t)a.hqk * kChunk * DK * E;
-        g_step = (int64_t)a.hv * kGateFloats * 4;
-        w_step = (int64_t)a.hv * kChunk * kChunk * E;
-        v_step = (int64_t)kChunk * v_row;
+        const int ncb = a.dv / 16;
 #pragma unroll
-        for (int jt = 0; jt < TPW; ++jt)
-            v_voff[jt] = (unsigned)((16 * (w + NWS * jt) + (l >> 2)) * v_row + (l & 3) * G::QE);
+        for (int jt = 0; jt < TPW; ++jt) {
+            const int tw = w + NWS * jt;
+            o_voff[jt] = (unsigned)((16 * tw + (l >> 2)) * v_row + (l & 3) * G::QE);
+            u_voff[jt] = (unsigned)(((tw * ncb + blk) * 64 + l) * G::QE);
+        }
         f_voff = (unsigned)(l * 16);
-        g_voff = (unsigned)(l * 8);
     }
 
+    __device__ __forceinline__ static int64_t cj(int64_t j, bool valid) { return valid ? j : 0; }
     // Fetch the operands of the sequence's chunk j (zeros when !valid), in
-    // four groups issued at different points of a chunk, each as soon as the
-    // registers it refills are free: Q and V, then K and the gates, then T~,
-    // then P.
-    __device__ __forceinline__ int64_t cj(int64_t j, bool valid) const { return valid ? j : 0; }
-    __device__ __forceinline__ void load_qv(Stage& s, int64_t j, bool valid) const {
+    // three groups: W, Q~ and u; K~^T and G2_last; P.
+    __device__ __forceinline__ void load_a(Stage& s, int64_t j, bool valid) const {
         const int64_t jc = cj(j, valid);
-        const auto rq = make_rsrc(qb + jc * kq_step, valid ? (int64_t)kChunk * DK * E : 0);
+        const int64_t mb = valid ? (int64_t)kChunk * DK * E : 0;
+        const auto rw = make_rsrc(wb + jc * m_step, mb);
+        const auto rq = make_rsrc(qb + jc * m_step, mb);
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) s.wf[tm] = B::frag(rw, f_voff, (unsigned)((w * 4 + tm) * FU * 1024));
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm) s.qf[tm] = B::frag(rq, f_voff, (unsigned)((w * 4 + tm) * FU * 1024));
-        const int64_t vo = jc * v_step;
-        const auto rv = make_rsrc(vb + vo, valid ? vn - vo : 0);
+        const auto ru = make_rsrc(ub + jc * u_step, valid ? u_bytes : 0);
 #pragma unroll
-        for (int jt = 0; jt < TPW; ++jt) s.v[jt] = B::quad(rv, v_voff[jt]);
+        for (int jt = 0; jt < TPW; ++jt) s.u[jt] = B::quad(ru, u_voff[jt]);
     }
-    __device__ __forceinline__ void load_kg(Stage& s, int64_t j, bool valid) const {
+    __device__ __forceinline__ void load_b(Stage& s, int64_t j, bool valid) const {
         const int64_t jc = cj(j, valid);
-        const auto rk = make_rsrc(kb + jc * kq_step, valid ? (int64_t)kChunk * DK * E : 0);
+        const auto rk = make_rsrc(kb + jc * m_step, valid ? (int64_t)kChunk * DK * E : 0);
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) s.kf[tm] = B::frag(rk, f_voff, (unsigned)((w * 4 + tm) * FU * 1024));
-        const auto rg = make_rsrc(gb + jc * g_step, valid ? kGateFloats * 4 : 0);
-        s.gate = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, g_voff, 0, 0));
-    }
-    __device__ __forceinline__ void load_t(Stage& s, int64_t j, bool valid) const {
-        const auto rt = make_rsrc(tb + cj(j, valid) * w_step, valid ? kChunk * kChunk * E : 0);
-#pragma unroll
-        for (int jt = 0; jt < TPW; ++jt)
+        for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-                s.t[jt][kk] = B::frag(rt, f_voff, (unsigned)(((w + NWS * jt) * 2 + kk) * FU * 1024));
+                s.kt[sub][kk] = B::frag(rk, f_voff, (unsigned)(((w * 2 + sub) * 2 + kk) * FU * 1024));
+        const auto rg = make_rsrc(gb + jc * g_step, valid ? 4 : 0);
+        s.gl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, 0, 0, 0));
     }
-    __device__ __forceinline__ void load_p(Stage& s, int64_t j, bool valid) const {
-        const auto rp = make_rsrc(pb + cj(j, valid) * w_step, valid ? kChunk * kChunk * E : 0);
+    __device__ __forceinline__ void load_c(Stage& s, int64_t j, bool valid) const {
+        const auto rp = make_rsrc(pb + cj(j, valid) * p_step, valid ? kChunk * kChunk * E : 0);
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt)
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
                 s.p[jt][kk] = B::frag(rp, f_voff, (unsigned)(((w + NWS * jt) * 2 + kk) * FU * 1024));
-    }
-    __device__ __forceinline__ void load(Stage& s, int64_t j, bool valid) const {
-        load_qv(s, j, valid);
-        load_kg(s, j, valid);
-        load_t(s, j, valid);
-        load_p(s, j, valid);
     }
 };
 
@@ -549,172 +657,121 @@ __device__ __forceinline__ void scan_wave(const PrefillArgs& a, ScanSmem<OP, DK>
     const int64_t s0 = si.start(n), s1 = si.start(n + 1);
     const int64_t base = slot_base(s0, n);
     Ctx ctx;
-    ctx.init(a, s0, base, h, blk, w);
+    ctx.init(a, base, h, blk, w);
 
-    // identity fragments: K slot (gq, i) <-> d_k 8 gq + i, state tile `sub`
-    // row n <-> d_k 8 (n/4) + 4 sub + n%4
-    frag Iden[2];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            Iden[sub][i] = from_f32<OP>((gq == (r >> 2) && i == 4 * sub + (r & 3)) ? 1.f : 0.f);
-
-    // S[sub][i] = S[c][32 w + 8 gq + 4 sub + i]
+    // S[sub][i] = S[c][32 w + 16 sub + 4 gq + i]
     f32x4 S[2];
-    const size_t srow = ((size_t)chain * a.dv + c) * DK + 32 * w + 8 * gq;
+    const size_t srow = ((size_t)chain * a.dv + c) * DK + 32 * w + 4 * gq;
     if (a.init_state) {
         S[0] = *reinterpret_cast<const f32x4*>(a.init_state + srow);
-        S[1] = *reinterpret_cast<const f32x4*>(a.init_state + srow + 4);
+        S[1] = *reinterpret_cast<const f32x4*>(a.init_state + srow + 16);
     } else {
         S[0] = zero4();
         S[1] = zero4();
     }
 
-    // V/O staging: row-wise side (row l >> 2, quad l & 3) and tile side
+    // O staging: row-wise side (row l >> 2, quad l & 3) and tile side
     // (row r, quad gq), byte offsets inside a tile
-    const unsigned v_wr = (unsigned)((l >> 2) * G::VROWB + G::QE * ((l & 3) ^ swz_vo(l >> 2, E)));
-    const unsigned v_rd = (unsigned)(r * G::VROWB + G::QE * (gq ^ swz_vo(r, E)));
-    auto gates = [&](const St& s, int par) {
-        sm.gam[par][l] = fast_exp2(s.gate[0]);
-        sm.dec[par][l] = fast_exp2(s.gate[1]);
-    };
+    const unsigned o_rw = (unsigned)((l >> 2) * G::VROWB + G::QE * ((l & 3) ^ swz_vo(l >> 2, E)));
+    const unsigned o_tl = (unsigned)(r * G::VROWB + G::QE * (gq ^ swz_vo(r, E)));
 
     const int64_t nchunks = (s1 - s0 + kChunk - 1) / kChunk;
-    // One chunk j: `cur` holds its operands, `nxt` those of chunk j+1, whose
-    // gates are moved into LDS here (read after the next chunk's first barrier).
-    auto chunk = [&](St& cur, const St& nxt, int64_t j, int par) {
+    auto chunk = [&](St& cur, int64_t j) {
         const int64_t t0 = s0 + j * kChunk;
-        // V tiles into lane layout (read back after E1)
-#pragma unroll
-        for (int jt = 0; jt < TPW; ++jt) *reinterpret_cast<quad*>(sm.vst[w][jt] + v_wr) = cur.v[jt];
-        // ---- partial products over the d_k slice; other waves' X tiles to LDS
+        const bool pre = j + 2 < nchunks;
+        // ---- partial products over the d_k slice; other waves' Z tiles to LDS
         const frag Sb = Ops::pack(S[0], S[1]);
-        f32x4 Xp[4], Yp[4];
+        f32x4 Zp[4], Yp[4];
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) Xp[tm] = Ops::mma(Sb, cur.kf[tm], zero4());
+        for (int tm = 0; tm < 4; ++tm) Zp[tm] = Ops::mma(cur.wf[tm], Sb, zero4());
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm)
-            if (tm % NWS != w) sm.part[w][tm][l] = Xp[tm];
+            if (tm % NWS != w) sm.part[w][tm][l] = Zp[tm];
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm) Yp[tm] = Ops::mma(Sb, cur.qf[tm], zero4());
         __syncthreads();                                                        // E1
-        gates(nxt, par ^ 1);
-        // Q and V of this chunk are consumed: fetch those of chunk j+2
-        const bool pre = j + 2 < nchunks;
-        __builtin_amdgcn_sched_barrier(0);
-        ctx.load_qv(cur, j + 2, pre);
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm)
             if (tm % NWS != w) sm.part[w][4 + tm][l] = Yp[tm];
-        // owner: R^T = V^T - X^T diag(gamma)
-        float gt[TPW];
+        // owner: U = u - Z for tokens 16 tw + 4 gq + i, column 16 blk + r
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt) {
             const int tw = w + NWS * jt;
-            f32x4 X = Xp[tw];
+            f32x4 Z = Zp[tw];
 #pragma unroll
             for (int v2 = 0; v2 < NWS; ++v2)
-                if (v2 != w) X += sm.part[v2][tw][l];
-            gt[jt] = sm.gam[par][16 * tw + r];
-            const quad vq = *reinterpret_cast<const quad*>(sm.vst[w][jt] + v_rd);
+                if (v2 != w) Z += sm.part[v2][tw][l];
+            quad uq;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                sm.Rt[(4 * gq + i) * RLD + 16 * tw + r] = from_f32<OP>(to_f32(vq[i]) - gt[jt] * X[i]);
-        }
-        const float gn = sm.gam[par][kChunk - 1];
-        // K^T in operand layout (exact identity product)
-        frag Ktf[2][2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int sub = 0; sub < 2; ++sub)
-                Ktf[sub][kk] = Ops::pack(Ops::mma(cur.kf[2 * kk], Iden[sub], zero4()),
-                                         Ops::mma(cur.kf[2 * kk + 1], Iden[sub], zero4()));
-        __builtin_amdgcn_sched_barrier(0);
-        ctx.load_kg(cur, j + 2, pre);
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();                                                        // E2
-        const frag Rb0 = frag_nat(sm.Rt, RLD, r, 0), Rb1 = frag_nat(sm.Rt, RLD, r, 32);
-#pragma unroll
-        for (int jt = 0; jt < TPW; ++jt) {
-            const int tw = w + NWS * jt;
-            const f32x4 U = Ops::mma(cur.t[jt][1], Rb1, Ops::mma(cur.t[jt][0], Rb0, zero4()));
-            const f32x4 dc = *reinterpret_cast<const f32x4*>(&sm.dec[par][16 * tw + 4 * gq]);
-            quad uq, dq;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uq[i] = from_f32<OP>(U[i]);
-                dq[i] = from_f32<OP>(U[i] * dc[i]);
-            }
+            for (int i = 0; i < 4; ++i) uq[i] = from_f32<OP>(to_f32(cur.u[jt][i]) - Z[i]);
             *reinterpret_cast<quad*>(&sm.Ut[r * RLD + 16 * tw + 4 * gq]) = uq;
-            *reinterpret_cast<quad*>(&sm.Dt[r * RLD + 16 * tw + 4 * gq]) = dq;
         }
-        __builtin_amdgcn_sched_barrier(0);
-        ctx.load_t(cur, j + 2, pre);
-        __builtin_amdgcn_sched_barrier(0);
-        f32x4 Y[TPW];
-#pragma unroll
-        for (int jt = 0; jt < TPW; ++jt) {
-            const int tw = w + NWS * jt;
-            Y[jt] = Yp[tw];
-#pragma unroll
-            for (int v2 = 0; v2 < NWS; ++v2)
-                if (v2 != w) Y[jt] += sm.part[v2][4 + tw][l];
-        }
-        __syncthreads();                                                        // E3
-        // ---- S_w^T <- gamma_n S_w^T + K_w^T (D o U)   (the serial chain first)
-        const frag Db0 = frag_rows(sm.Dt, RLD, r, 0), Db1 = frag_rows(sm.Dt, RLD, r, 32);
+        // W, Q~ and u of this chunk are consumed: fetch those of chunk j+2
+        pin();
+        ctx.load_a(cur, j + 2, pre);
+        pin();
+        __syncthreads();                                                        // E2
+        // ---- S_w^T <- gamma_last S_w^T + K~_w^T U   (the serial chain first)
+        const float gn = fast_exp2(cur.gl);
+        const frag Db0 = frag_rows(sm.Ut, RLD, r, 0), Db1 = frag_rows(sm.Ut, RLD, r, 32);
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
-            S[sub] = Ops::mma(Ktf[sub][1], Db1, Ops::mma(Ktf[sub][0], Db0, gn * S[sub]));
+            S[sub] = Ops::mma(cur.kt[sub][1], Db1, Ops::mma(cur.kt[sub][0], Db0, gn * S[sub]));
+        pin();
+        ctx.load_b(cur, j + 2, pre);
+        pin();
         // ---- O^T tiles: rows = columns 16 blk + 4 gq + i, column = token 16 tw + r
         const frag Ub0 = frag_nat(sm.Ut, RLD, r, 0), Ub1 = frag_nat(sm.Ut, RLD, r, 32);
         f32x4 Ot[TPW];
 #pragma unroll
-        for (int jt = 0; jt < TPW; ++jt)
-            Ot[jt] = Ops::mma(Ub1, cur.p[jt][1], Ops::mma(Ub0, cur.p[jt][0], gt[jt] * Y[jt]));
-        __builtin_amdgcn_sched_barrier(0);
-        ctx.load_p(cur, j + 2, pre);
-        __builtin_amdgcn_sched_barrier(0);
-        // O through the wave's V/O area to row-wise stores; rows past the end
-        // of the sequence fall outside the resource
+        for (int jt = 0; jt < TPW; ++jt) {
+            const int tw = w + NWS * jt;
+            f32x4 Y = Yp[tw];
+#pragma unroll
+            for (int v2 = 0; v2 < NWS; ++v2)
+                if (v2 != w) Y += sm.part[v2][4 + tw][l];
+            Ot[jt] = Ops::mma(Ub1, cur.p[jt][1], Ops::mma(Ub0, cur.p[jt][0], Y));
+        }
+        pin();
+        ctx.load_c(cur, j + 2, pre);
+        pin();
+        // O through the wave's staging area to row-wise stores; rows past the
+        // end of the sequence fall outside the resource
         {
-            const int64_t ntl = s1 - t0;
-            const auto ro = make_rsrc(static_cast<OP*>(a.out) + ((size_t)t0 * a.hv + h) * a.dv + blk * 16,
+            const int64_t ntl = j < 0 ? 0 : s1 - t0;
+            const auto ro = make_rsrc(static_cast<OP*>(a.out) + ((size_t)(j < 0 ? s0 : t0) * a.hv + h) * a.dv + blk * 16,
                                       ntl > 0 ? (ntl - 1) * ctx.v_row + 16 * E : 0);
 #pragma unroll
             for (int jt = 0; jt < TPW; ++jt) {
                 quad oq;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) oq[i] = from_f32<OP>(Ot[jt][i]);
-                *reinterpret_cast<quad*>(sm.vst[w][jt] + v_rd) = oq;
+                *reinterpret_cast<quad*>(sm.ost[w][jt] + o_tl) = oq;
             }
             wave_lds_fence();
 #pragma unroll
             for (int jt = 0; jt < TPW; ++jt)
-                B::store4(*reinterpret_cast<const quad*>(sm.vst[w][jt] + v_wr), ro, ctx.v_voff[jt]);
+                B::store4(*reinterpret_cast<const quad*>(sm.ost[w][jt] + o_rw), ro, ctx.o_voff[jt]);
         }
     };
 
-    // Chunks are processed in pairs (stages A, B).  An odd count gets one
-    // trailing empty chunk, which is an exact no-op: its loads read zeros
-    // (gates 0, so gamma_n = 1 and S is unchanged) and its stores are dropped.
-    // Keeping the loop free of an early exit keeps the load order identical on
-    // every path into the loop, so the memory-counter waits stay exact.
-    St A, Bs;
-    ctx.load(A, 0, nchunks > 0);
-    ctx.load(Bs, 1, nchunks > 1);
-    gates(A, 0);
-    __syncthreads();   // gates of chunk 0
-    for (int64_t j = 0; j < nchunks; j += 2) {
-        chunk(A, Bs, j, 0);
-        chunk(Bs, A, j + 1, 1);
+    // Chunks are processed in pairs (stages A, B), starting two chunks early
+    // on zeroed stages, so that every load is issued inside the loop body and
+    // the memory-counter waits see the same load order on every path.  An
+    // empty chunk -- the two leading ones, and one trailing one for an odd
+    // count -- is an exact no-op: its operands are zeros (G2_last = 0, so
+    // gamma_last = 1, and U = 0 leaves S unchanged) and its stores are dropped.
+    St A{}, Bs{};
+    // Let the initial-state load land here, outside the loop: otherwise the
+    // loop head would have to wait for every load in flight on each pass.
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int64_t j = -2; j < nchunks; j += 2) {
+        chunk(A, j);
+        chunk(Bs, j + 1);
     }
     if (a.final_state) {
         *reinterpret_cast<f32x4*>(a.final_state + srow) = S[0];
-        *reinterpret_cast<f32x4*>(a.final_state + srow + 4) = S[1];
+        *reinterpret_cast<f32x4*>(a.final_state + srow + 16) = S[1];
     }
 }
 
@@ -723,7 +780,7 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_kernel(PrefillArgs a
     __shared__ ScanSmem<OP, DK> sm;
     // Work item (chain, 16-column block).  With xcd_map, the 8 column blocks of
     // a chain get workgroup ids that the dispatcher sends to one XCD, so they
-    // share that XCD's L2 for K, Q, T~ and P.
+    // share that XCD's L2 for the chunk operands.
     int chain, blk;
     {
         const int L = blockIdx.x, nblk = a.dv / 16;
@@ -743,11 +800,11 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_kernel(PrefillArgs a
     }
 }
 
-template <typename OP, int DK>
+template <typename OP, int DK, int DV>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
     {
         dim3 grid((unsigned)a.num_slots, (unsigned)a.hv), block(kPrepThreads);
-        hipLaunchKernelGGL((gdn_prep_kernel<OP, DK>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((gdn_prep_kernel<OP, DK, DV>), grid, block, 0, st, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -759,12 +816,17 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <typename OP>
+hipError_t launch_prefill_dt(const PrefillArgs& a, int dk, int dv, hipStream_t st) {
+    if (dk == 128) return dv == 128 ? launch_prefill_t<OP, 128, 128>(a, st) : launch_prefill_t<OP, 128, 64>(a, st);
+    return dv == 128 ? launch_prefill_t<OP, 64, 128>(a, st) : launch_prefill_t<OP, 64, 64>(a, st);
+}
+
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int dk, hipStream_t st) {
+hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int dk, int dv, hipStream_t st) {
     if (a.num_seqs == 0) return hipSuccess;
-    if (bf16) return dk == 128 ? launch_prefill_t<__bf16, 128>(a, st) : launch_prefill_t<__bf16, 64>(a, st);
-    return dk == 128 ? launch_prefill_t<float, 128>(a, st) : launch_prefill_t<float, 64>(a, st);
+    return bf16 ? launch_prefill_dt<__bf16>(a, dk, dv, st) : launch_prefill_dt<float>(a, dk, dv, st);
 }
 
 }  // namespace gdn

@@ -94,8 +94,8 @@ typedef struct gdn_shape {
  * final_state [N, Hv, dv, dk] fp32 or NULL.
  *
  * Memory: a stream-ordered workspace of about
- * (num_tokens / 64 + N) * (Hv * (2 * 64 * 64 * sizeof(element) + 512)
- * + Hqk * 2 * 64 * dk * sizeof(element)) bytes is taken
+ * (num_tokens / 64 + N) * Hv * (64 * (3 dk + dv + 64) * sizeof(element) + 4)
+ * bytes is taken
  * from HIP's default memory pool on `stream` and returned to it before the
  * call's work completes (GDN_ERROR_OUT_OF_MEMORY if that fails).
  */

@@ -439,20 +439,22 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
 // ===========================================================================
 // scan: sequential over the chunks of one sequence
 // ===========================================================================
-// One workgroup per (sequence, value head, 16-column block of d_v).  Its
-// NWS = DK / 32 waves split d_k: wave w owns state rows S[:, 32w .. 32w+32)
-// as two fp32 accumulator tiles S^T (16 d_k rows x 16 columns each, tile `sub`
-// holding d_k 32 w + 16 sub + (0..15)); packed together they are the state's
-// operand fragment in paired d_k order.  Wave w also owns token tiles
-// tw = w + NWS jt (jt < TPW = 4 / NWS).  Per chunk:
-//   wave w:  Z_w = W_w S_w^T,  Y_w^T = S_w Q~_w^T        (partial over d_k)
-//   E1 (LDS): Z partials -> the owner of token tile tw sums Z there
-//   owner:   U = u - Z for its tokens, to LDS
-//   E2 (LDS): U for all tokens to every wave, Y partials to the owners
-//   wave w:  S_w^T <- gamma_last S_w^T + K~_w^T U
-//   owner:   O^T = Y^T + U^T P_tw^T
-// A wave keeps its own partial tiles in registers and writes only the tiles
-// other waves own.
+// One workgroup per (sequence, value head, 16-column block of d_v), with
+// NWS = DK / 32 waves.  The state block S (16 columns x d_k) is split by d_k:
+// wave w owns S[:, 32w .. 32w+32) as two fp32 accumulator tiles S^T (tile
+// `sub` holding d_k 32 w + 16 sub + (0..15)); packed to the operand type they
+// are the state's operand fragment for slice w in paired d_k order.  Token
+// tiles are split too: wave w owns tiles tw = w + NWS jt (jt < TPW = 4 / NWS).
+// Per chunk:
+//   B1 (LDS): every wave publishes its state slice (operand fragment), so
+//             each wave sees the whole start state S
+//   wave w:  Z = W_tw S^T, Y^T = S Q~_tw^T for its token tiles (full d_k)
+//            U = u - Z for its tokens, to LDS
+//   B2 (LDS): U for all tokens to every wave
+//   wave w:  S_w^T <- gamma_last S_w^T + K~_w^T U        (its d_k slice)
+//            O^T = Y^T + U^T P_tw^T                       (its token tiles)
+// Nothing is reduced across waves; the only exchanges are the state slices
+// (in the operand type the products use anyway) and U.
 //
 // Global memory.  The vector memory path serves a wave request four lanes at
 // a time, and four lanes on four different rows cost four times as much as
@@ -460,11 +462,13 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
 // consecutive bytes: all operands come fragment-major from the prep kernel's
 // workspace (one 1 KB block per fragment; u as 8-byte lane records), and O
 // passes through a small wave-private LDS area between the lanes' tile layout
-// and row-wise global stores.  Operands are fetched two chunks ahead, in three
-// groups issued as soon as the registers they refill are free.  All loads go
-// through buffer resources (reads past the end of a resource return 0, writes
-// past it are dropped), and no load, store or use of a loaded value sits
-// behind a branch, so the compiler's memory-counter waits stay exact.
+// and row-wise global stores.  Operands are fetched two chunks ahead, each
+// group issued right after the product that consumes the registers it
+// refills, so that the vector memory queue is fed evenly through the chunk.
+// All loads go through buffer resources (reads past the end of a resource
+// return 0, writes past it are dropped), and no load, store or use of a
+// loaded value sits behind a branch, so the compiler's memory-counter waits
+// stay exact.
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -524,7 +528,7 @@ __device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOM
 
 template <typename OP, int DK>
 struct ScanGeom {
-    static constexpr int NWS = DK / 32;                 // waves per workgroup (d_k split)
+    static constexpr int NWS = DK / 32;                 // waves per workgroup (d_k slices)
     static constexpr int TPW = 4 / NWS;                 // token tiles per wave
     static constexpr int E = (int)sizeof(OP);
     static constexpr int FU = Frag<OP>::FU;             // 16-byte units per operand fragment
@@ -537,8 +541,8 @@ struct ScanGeom {
 template <typename OP, int DK>
 struct ScanSmem {
     using G = ScanGeom<OP, DK>;
-    f32x4 part[G::NWS][8][kWave];        // Z partials (0..3) and Y^T partials (4..7)
-    alignas(16) OP Ut[16 * G::RLD];      // U as [column][token]
+    typename Op<OP>::frag sfr[G::NWS][kWave];   // state slices as operand fragments
+    alignas(16) OP Ut[16 * G::RLD];             // U as [column][token]
     alignas(16) char ost[G::NWS][G::TPW][G::VB];   // wave-private O tiles
 };
 
@@ -551,8 +555,8 @@ struct ScanCtx {
     static constexpr int NWS = G::NWS, TPW = G::TPW, E = G::E, FU = G::FU;
     // One chunk's operands for one wave.
     struct Stage {
-        frag wf[4];          // W[16 tm + r][paired d_k of slice w]
-        frag qf[4];          // Q~, same positions
+        frag wf[TPW][NWS];   // W[16 tw + r][paired d_k of slice s]
+        frag qf[TPW][NWS];   // Q~, same positions
         quad u[TPW];         // u[16 tw + 4 gq + i][16 blk + r]
         frag kt[2][2];       // K~^T[32 w + 16 sub + r][paired tokens from 32 kk]
         float gl;            // G2_last
@@ -599,22 +603,29 @@ struct ScanCtx {
     }
 
     __device__ __forceinline__ static int64_t cj(int64_t j, bool valid) { return valid ? j : 0; }
-    // Fetch the operands of the sequence's chunk j (zeros when !valid), in
-    // three groups: W, Q~ and u; K~^T and G2_last; P.
-    __device__ __forceinline__ void load_a(Stage& s, int64_t j, bool valid) const {
-        const int64_t jc = cj(j, valid);
-        const int64_t mb = valid ? (int64_t)kChunk * DK * E : 0;
-        const auto rw = make_rsrc(wb + jc * m_step, mb);
-        const auto rq = make_rsrc(qb + jc * m_step, mb);
+    // Fetch parts of the sequence's chunk j (zeros when !valid).
+    __device__ __forceinline__ void load_w(Stage& s, int64_t j, bool valid) const {
+        const auto rw = make_rsrc(wb + cj(j, valid) * m_step, valid ? (int64_t)kChunk * DK * E : 0);
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) s.wf[tm] = B::frag(rw, f_voff, (unsigned)((w * 4 + tm) * FU * 1024));
+        for (int jt = 0; jt < TPW; ++jt)
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) s.qf[tm] = B::frag(rq, f_voff, (unsigned)((w * 4 + tm) * FU * 1024));
-        const auto ru = make_rsrc(ub + jc * u_step, valid ? u_bytes : 0);
+            for (int sl = 0; sl < NWS; ++sl)
+                s.wf[jt][sl] = B::frag(rw, f_voff, (unsigned)((sl * 4 + w + NWS * jt) * FU * 1024));
+    }
+    __device__ __forceinline__ void load_q(Stage& s, int64_t j, bool valid) const {
+        const auto rq = make_rsrc(qb + cj(j, valid) * m_step, valid ? (int64_t)kChunk * DK * E : 0);
+#pragma unroll
+        for (int jt = 0; jt < TPW; ++jt)
+#pragma unroll
+            for (int sl = 0; sl < NWS; ++sl)
+                s.qf[jt][sl] = B::frag(rq, f_voff, (unsigned)((sl * 4 + w + NWS * jt) * FU * 1024));
+    }
+    __device__ __forceinline__ void load_u(Stage& s, int64_t j, bool valid) const {
+        const auto ru = make_rsrc(ub + cj(j, valid) * u_step, valid ? u_bytes : 0);
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt) s.u[jt] = B::quad(ru, u_voff[jt]);
     }
-    __device__ __forceinline__ void load_b(Stage& s, int64_t j, bool valid) const {
+    __device__ __forceinline__ void load_k(Stage& s, int64_t j, bool valid) const {
         const int64_t jc = cj(j, valid);
         const auto rk = make_rsrc(kb + jc * m_step, valid ? (int64_t)kChunk * DK * E : 0);
 #pragma unroll
@@ -625,7 +636,7 @@ struct ScanCtx {
         const auto rg = make_rsrc(gb + jc * g_step, valid ? 4 : 0);
         s.gl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, 0, 0, 0));
     }
-    __device__ __forceinline__ void load_c(Stage& s, int64_t j, bool valid) const {
+    __device__ __forceinline__ void load_p(Stage& s, int64_t j, bool valid) const {
         const auto rp = make_rsrc(pb + cj(j, valid) * p_step, valid ? kChunk * kChunk * E : 0);
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt)
@@ -679,38 +690,56 @@ __device__ __forceinline__ void scan_wave(const PrefillArgs& a, ScanSmem<OP, DK>
     auto chunk = [&](St& cur, int64_t j) {
         const int64_t t0 = s0 + j * kChunk;
         const bool pre = j + 2 < nchunks;
-        // ---- partial products over the d_k slice; other waves' Z tiles to LDS
-        const frag Sb = Ops::pack(S[0], S[1]);
-        f32x4 Zp[4], Yp[4];
+        // ---- the whole start state, slice by slice
+        frag Sf[NWS];
+        Sf[w] = Ops::pack(S[0], S[1]);
+        sm.sfr[w][l] = Sf[w];
+        __syncthreads();                                                        // B1
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) Zp[tm] = Ops::mma(cur.wf[tm], Sb, zero4());
+        for (int sl = 0; sl < NWS; ++sl)
+            if (sl != w) Sf[sl] = sm.sfr[sl][l];
+        // ---- Z = W S^T for the wave's token tiles; U = u - Z to LDS
+        f32x4 Z[TPW];
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm)
-            if (tm % NWS != w) sm.part[w][tm][l] = Zp[tm];
+        for (int jt = 0; jt < TPW; ++jt) {
+            f32x4 z0 = zero4(), z1 = zero4();
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) Yp[tm] = Ops::mma(Sb, cur.qf[tm], zero4());
-        __syncthreads();                                                        // E1
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm)
-            if (tm % NWS != w) sm.part[w][4 + tm][l] = Yp[tm];
-        // owner: U = u - Z for tokens 16 tw + 4 gq + i, column 16 blk + r
+            for (int sl = 0; sl < NWS; sl += 2) {
+                z0 = Ops::mma(cur.wf[jt][sl], Sf[sl], z0);
+                if (sl + 1 < NWS) z1 = Ops::mma(cur.wf[jt][sl + 1], Sf[sl + 1], z1);
+            }
+            Z[jt] = z0 + z1;
+        }
+        pin();
+        ctx.load_w(cur, j + 2, pre);
+        pin();
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt) {
             const int tw = w + NWS * jt;
-            f32x4 Z = Zp[tw];
-#pragma unroll
-            for (int v2 = 0; v2 < NWS; ++v2)
-                if (v2 != w) Z += sm.part[v2][tw][l];
             quad uq;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) uq[i] = from_f32<OP>(to_f32(cur.u[jt][i]) - Z[i]);
+            for (int i = 0; i < 4; ++i) uq[i] = from_f32<OP>(to_f32(cur.u[jt][i]) - Z[jt][i]);
             *reinterpret_cast<quad*>(&sm.Ut[r * RLD + 16 * tw + 4 * gq]) = uq;
         }
-        // W, Q~ and u of this chunk are consumed: fetch those of chunk j+2
         pin();
-        ctx.load_a(cur, j + 2, pre);
+        ctx.load_u(cur, j + 2, pre);
         pin();
-        __syncthreads();                                                        // E2
+        // ---- Y^T = S Q~^T for the wave's token tiles (off the serial chain)
+        f32x4 Y[TPW];
+#pragma unroll
+        for (int jt = 0; jt < TPW; ++jt) {
+            f32x4 y0 = zero4(), y1 = zero4();
+#pragma unroll
+            for (int sl = 0; sl < NWS; sl += 2) {
+                y0 = Ops::mma(Sf[sl], cur.qf[jt][sl], y0);
+                if (sl + 1 < NWS) y1 = Ops::mma(Sf[sl + 1], cur.qf[jt][sl + 1], y1);
+            }
+            Y[jt] = y0 + y1;
+        }
+        pin();
+        ctx.load_q(cur, j + 2, pre);
+        pin();
+        __syncthreads();                                                        // B2
         // ---- S_w^T <- gamma_last S_w^T + K~_w^T U   (the serial chain first)
         const float gn = fast_exp2(cur.gl);
         const frag Db0 = frag_rows(sm.Ut, RLD, r, 0), Db1 = frag_rows(sm.Ut, RLD, r, 32);
@@ -718,22 +747,16 @@ __device__ __forceinline__ void scan_wave(const PrefillArgs& a, ScanSmem<OP, DK>
         for (int sub = 0; sub < 2; ++sub)
             S[sub] = Ops::mma(cur.kt[sub][1], Db1, Ops::mma(cur.kt[sub][0], Db0, gn * S[sub]));
         pin();
-        ctx.load_b(cur, j + 2, pre);
+        ctx.load_k(cur, j + 2, pre);
         pin();
         // ---- O^T tiles: rows = columns 16 blk + 4 gq + i, column = token 16 tw + r
         const frag Ub0 = frag_nat(sm.Ut, RLD, r, 0), Ub1 = frag_nat(sm.Ut, RLD, r, 32);
         f32x4 Ot[TPW];
 #pragma unroll
-        for (int jt = 0; jt < TPW; ++jt) {
-            const int tw = w + NWS * jt;
-            f32x4 Y = Yp[tw];
-#pragma unroll
-            for (int v2 = 0; v2 < NWS; ++v2)
-                if (v2 != w) Y += sm.part[v2][4 + tw][l];
-            Ot[jt] = Ops::mma(Ub1, cur.p[jt][1], Ops::mma(Ub0, cur.p[jt][0], Y));
-        }
+        for (int jt = 0; jt < TPW; ++jt)
+            Ot[jt] = Ops::mma(Ub1, cur.p[jt][1], Ops::mma(Ub0, cur.p[jt][0], Y[jt]));
         pin();
-        ctx.load_c(cur, j + 2, pre);
+        ctx.load_p(cur, j + 2, pre);
         pin();
         // O through the wave's staging area to row-wise stores; rows past the
         // end of the sequence fall outside the resource

@@ -202,7 +202,7 @@ struct PrepSmem {
 };
 
 template <typename OP, int DK, int DV>
-__global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPrepThreads, 2) void gdn_prep_kernel(PrefillArgs a) {
     using Ops = Op<OP>;
     using frag = typename Ops::frag;
     using quad = typename Ops::quad;
@@ -212,22 +212,79 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
     constexpr int FU = Frag<OP>::FU;
     constexpr int NV = DK / VE;                            // vectors per K/Q row
     constexpr int NVV = DV / VE;                           // vectors per V row
+    constexpr int KQREG = kChunk * NV / kPrepThreads;      // K (and Q) vectors per thread
     constexpr int VREG = kChunk * NVV / kPrepThreads;      // V vectors per thread
     constexpr int NS = DK / 32;                            // scan slices of d_k
     constexpr int NCP = DV / 32;                           // pairs of 16-column blocks of d_v
-    static_assert(VREG * kPrepThreads == kChunk * NVV, "V staging");
+    static_assert(VREG * kPrepThreads == kChunk * NVV && KQREG * kPrepThreads == kChunk * NV, "staging");
     static_assert(sizeof(OP) * kChunk * LDP <= sizeof(float) * kChunk * (kChunk + 4), "T~ diag(gamma) in A");
     __shared__ Sm sm;
 
-    const int64_t slot = blockIdx.x;
-    const int h = blockIdx.y;
-    const SeqIndex si{a.cu, a.seqlen};
-    int n;
-    int64_t t0, t1;
-    if (!locate_slot(si, a.num_seqs, slot, n, t0, t1)) return;   // uniform over the workgroup
-    const int nt = (int)((t1 - t0) < kChunk ? (t1 - t0) : kChunk);
-    const int hq = (h * a.hqk) / a.hv;
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), r = l & 15, gq = l >> 4;
+    const SeqIndex si{a.cu, a.seqlen};
+    const OP* kg = static_cast<const OP*>(a.k);
+    const OP* qg = static_cast<const OP*>(a.q);
+    const OP* vg = static_cast<const OP*>(a.v);
+    const int64_t nitems = a.num_slots * a.hv;
+
+    // One work item = one (slot, value head); a workgroup walks the items
+    // blockIdx.x, blockIdx.x + gridDim.x, ..., fetching the next item's
+    // inputs into registers while it computes the current one.
+    struct Item {
+        bool ok;           // a real chunk (not past the end, not a gap slot)
+        int64_t slot, t0;
+        int h, nt, hq;
+    };
+    auto locate = [&](int64_t item) {
+        Item it{};
+        it.ok = false;
+        if (item < nitems) {
+            it.slot = item / a.hv;
+            it.h = (int)(item - it.slot * a.hv);
+            int n;
+            int64_t t1;
+            it.ok = locate_slot(si, a.num_seqs, it.slot, n, it.t0, t1);
+            it.nt = it.ok ? (int)((t1 - it.t0) < kChunk ? (t1 - it.t0) : kChunk) : 0;
+            it.hq = (it.h * a.hqk) / a.hv;
+        }
+        return it;
+    };
+    // rows past the end of the sequence are clamped here and zeroed when staged
+    u32x4 kreg[KQREG], qreg[KQREG], vreg[VREG];
+    float gv = 0.f, bv = 0.f;
+    auto fetch = [&](const Item& it) {
+#pragma unroll
+        for (int i = 0; i < KQREG; ++i) {
+            const int e = tid + i * kPrepThreads;
+            const int row = e / NV, cv = e - row * NV;
+            const int rc = row < it.nt ? row : it.nt - 1;
+            const size_t off = ((size_t)(it.t0 + rc) * a.hqk + it.hq) * DK + (size_t)cv * VE;
+            kreg[i] = ld16(kg + off);
+            qreg[i] = ld16(qg + off);
+        }
+#pragma unroll
+        for (int i = 0; i < VREG; ++i) {
+            const int e = tid + i * kPrepThreads;
+            const int row = e / NVV, cv = e - row * NVV;
+            const int rc = row < it.nt ? row : it.nt - 1;
+            vreg[i] = ld16(vg + ((size_t)(it.t0 + rc) * a.hv + it.h) * DV + (size_t)cv * VE);
+        }
+        const int lc = l < it.nt ? l : it.nt - 1;
+        gv = a.g[(size_t)(it.t0 + lc) * a.hv + it.h];
+        bv = a.beta[(size_t)(it.t0 + lc) * a.hv + it.h];
+    };
+
+    Item cur = locate(blockIdx.x);
+    if (cur.ok) fetch(cur);
+    for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const Item nxt = locate(item + gridDim.x);
+    if (!cur.ok) {
+        if (nxt.ok) fetch(nxt);
+        cur = nxt;
+        continue;
+    }
+    const int64_t slot = cur.slot;
+    const int h = cur.h, nt = cur.nt, hq = cur.hq;
     const size_t blk = (size_t)slot * a.hv + h;
     OP* const Ww = static_cast<OP*>(a.ws_w) + blk * (kChunk * DK);
     OP* const Qw = static_cast<OP*>(a.ws_q) + blk * (kChunk * DK);
@@ -235,37 +292,30 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
     OP* const Uw = static_cast<OP*>(a.ws_u) + blk * (kChunk * DV);
     OP* const Pw = static_cast<OP*>(a.ws_p) + blk * (kChunk * kChunk);
 
-    // ---- stage K, Q (rows past the end are zero), V into registers, gates
-    const OP* kg = static_cast<const OP*>(a.k);
-    const OP* qg = static_cast<const OP*>(a.q);
-    const OP* vg = static_cast<const OP*>(a.v);
-    for (int e = tid; e < kChunk * NV; e += kPrepThreads) {
+    // ---- stage K and Q into LDS (zero past the end); V stays in registers
+    // until Q's space is free
+#pragma unroll
+    for (int i = 0; i < KQREG; ++i) {
+        const int e = tid + i * kPrepThreads;
         const int row = e / NV, cv = e - row * NV;
-        const int rc = row < nt ? row : nt - 1;
-        const size_t off = ((size_t)(t0 + rc) * a.hqk + hq) * DK + (size_t)cv * VE;
-        u32x4 kv = ld16(kg + off), qv = ld16(qg + off);
-        if (row >= nt) { kv = zero_u4(); qv = zero_u4(); }
-        *reinterpret_cast<u32x4*>(&sm.K[row * LD + cv * VE]) = kv;
-        *reinterpret_cast<u32x4*>(&sm.QV[row * LDQV + cv * VE]) = qv;
+        *reinterpret_cast<u32x4*>(&sm.K[row * LD + cv * VE]) = row < nt ? kreg[i] : zero_u4();
+        *reinterpret_cast<u32x4*>(&sm.QV[row * LDQV + cv * VE]) = row < nt ? qreg[i] : zero_u4();
     }
-    u32x4 vreg[VREG];
+    u32x4 vcur[VREG];
 #pragma unroll
     for (int i = 0; i < VREG; ++i) {
-        const int e = tid + i * kPrepThreads;
-        const int row = e / NVV, cv = e - row * NVV;
-        const int rc = row < nt ? row : nt - 1;
-        vreg[i] = ld16(vg + ((size_t)(t0 + rc) * a.hv + h) * DV + (size_t)cv * VE);
-        if (row >= nt) vreg[i] = zero_u4();
+        const int row = (tid + i * kPrepThreads) / NVV;
+        vcur[i] = row < nt ? vreg[i] : zero_u4();
     }
+    float gc = gv, bc = bv;
+    // the next item's inputs are in flight from here on
+    if (nxt.ok) fetch(nxt);
     if (w == 0) {
-        const int lc = l < nt ? l : nt - 1;
-        float gv = a.g[(size_t)(t0 + lc) * a.hv + h];
-        float bv = a.beta[(size_t)(t0 + lc) * a.hv + h];
-        if (l >= nt) { gv = 0.f; bv = 0.f; }
-        const double G = wave_cumsum_f64((double)gv * 1.4426950408889634);
+        if (l >= nt) { gc = 0.f; bc = 0.f; }
+        const double G = wave_cumsum_f64((double)gc * 1.4426950408889634);
         const double Gl = lane63_f64(G);
         sm.G[l] = G;
-        sm.B[l] = bv;
+        sm.B[l] = bc;
         sm.gam[l] = fast_exp2((float)G);
         sm.dec[l] = fast_exp2((float)(Gl - G));
         if (l == 0) a.ws_g[blk] = (float)Gl;
@@ -343,7 +393,7 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
     for (int i = 0; i < VREG; ++i) {
         const int e = tid + i * kPrepThreads;
         const int row = e / NVV, cv = e - row * NVV;
-        *reinterpret_cast<u32x4*>(&sm.QV[row * LDQV + cv * VE]) = vreg[i];
+        *reinterpret_cast<u32x4*>(&sm.QV[row * LDQV + cv * VE]) = vcur[i];
     }
     // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution
     // (lane c of wave b solves column c of block b), fp32.
@@ -386,11 +436,24 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
     // ---- T~ = T diag(beta) (into P's space) and T~ diag(gamma) (into A's)
     OP* const Tb = sm.P;
     OP* const Tg = reinterpret_cast<OP*>(&sm.A[0][0]);
-    for (int e = tid; e < kChunk * kChunk; e += kPrepThreads) {
-        const int t = e >> 6, s = e & 63;
-        const float x = (s <= t) ? sm.T[t][s] * sm.B[s] : 0.f;
-        Tb[t * LDP + s] = from_f32<OP>(x);
-        Tg[t * LDP + s] = from_f32<OP>(x * sm.gam[s]);
+    for (int e = tid; e < kChunk * kChunk / 8; e += kPrepThreads) {
+        const int t = e >> 3, c0 = (e & 7) * 8;     // row t, columns c0 .. c0 + 7
+        const f32x4 t0v = *reinterpret_cast<const f32x4*>(&sm.T[t][c0]);
+        const f32x4 t1v = *reinterpret_cast<const f32x4*>(&sm.T[t][c0 + 4]);
+        const f32x4 b0v = *reinterpret_cast<const f32x4*>(&sm.B[c0]);
+        const f32x4 b1v = *reinterpret_cast<const f32x4*>(&sm.B[c0 + 4]);
+        const f32x4 g0v = *reinterpret_cast<const f32x4*>(&sm.gam[c0]);
+        const f32x4 g1v = *reinterpret_cast<const f32x4*>(&sm.gam[c0 + 4]);
+        frag tb, tg;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float tv = i < 4 ? t0v[i] : t1v[i - 4];
+            const float x = (c0 + i <= t) ? tv * (i < 4 ? b0v[i] : b1v[i - 4]) : 0.f;
+            tb[i] = from_f32<OP>(x);
+            tg[i] = from_f32<OP>(x * (i < 4 ? g0v[i] : g1v[i - 4]));
+        }
+        *reinterpret_cast<frag*>(&Tb[t * LDP + c0]) = tb;
+        *reinterpret_cast<frag*>(&Tg[t * LDP + c0]) = tg;
     }
     __syncthreads();
 
@@ -433,6 +496,9 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(PrefillArgs a) {
                 *reinterpret_cast<quad*>(Uw + ((size_t)(tw * NCB + 2 * cp + sub) * 64 + l) * 4) = uq;
             }
         }
+    }
+    __syncthreads();   // LDS is restaged for the next item
+    cur = nxt;
     }
 }
 
@@ -826,9 +892,24 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_kernel(PrefillArgs a
 template <typename OP, int DK, int DV>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
     {
-        dim3 grid((unsigned)a.num_slots, (unsigned)a.hv), block(kPrepThreads);
-        hipLaunchKernelGGL((gdn_prep_kernel<OP, DK, DV>), grid, block, 0, st, a);
-        hipError_t e = hipGetLastError();
+        // persistent: as many workgroups as fit on the device at once
+        static int resident[64] = {};   // per device, filled on first use
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+        if (resident[dev] == 0) {
+            int cus = 0, per_cu = 0;
+            e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+            if (e != hipSuccess) return e;
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gdn_prep_kernel<OP, DK, DV>, kPrepThreads, 0);
+            if (e != hipSuccess) return e;
+            resident[dev] = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+        }
+        const int64_t items = a.num_slots * a.hv;
+        const unsigned nwg = (unsigned)(items < resident[dev] ? items : resident[dev]);
+        hipLaunchKernelGGL((gdn_prep_kernel<OP, DK, DV>), dim3(nwg), dim3(kPrepThreads), 0, st, a);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int64_t chains = (int64_t)a.num_seqs * a.hv;

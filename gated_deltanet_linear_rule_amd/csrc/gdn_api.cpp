@@ -174,7 +174,9 @@ gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, con
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const gdn::PrefillWorkspace wl(a.num_slots, a.hv, shape->head_dim_k, shape->head_dim_v, bf16 ? 2 : 4);
-    const int64_t wbytes = wl.total;
+    const int64_t seg = gdn::prefill_segment_chunks(a.num_tokens, a.num_seqs, a.hv, a.dv);
+    const int64_t state_bytes = seg > 0 ? (int64_t)a.num_seqs * a.hv * a.dv * shape->head_dim_k * 4 : 0;
+    const int64_t wbytes = wl.total + state_bytes;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(GDN_ERROR_LAUNCH, "hipGetDevice failed");
     keep_pool_memory(dev);
@@ -190,7 +192,8 @@ gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, con
     a.ws_u = wc + wl.u;
     a.ws_p = wc + wl.p;
     a.ws_g = reinterpret_cast<float*>(wc + wl.g);
-    hipError_t e = gdn::launch_prefill(a, bf16, shape->head_dim_k, shape->head_dim_v, st);
+    float* state_ws = seg > 0 ? reinterpret_cast<float*>(wc + wl.total) : nullptr;
+    hipError_t e = gdn::launch_prefill(a, bf16, shape->head_dim_k, shape->head_dim_v, state_ws, st);
     hipError_t ef = hipFreeAsync(ws, st);
     if (e == hipSuccess) e = ef;
     if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(st);

@@ -45,6 +45,14 @@ struct PrefillArgs {
     void* ws_u;                // 64 x dv  u  = T~ V
     void* ws_p;                // 64 x 64  P  = lower_incl(Gamma o Q K^T)
     float* ws_g;               // G2_last: log2 of the chunk's total decay
+    // One launch covers chunk indices [seg_j0, seg_j1) of every sequence.  The
+    // scan starts from state_in (NULL = zeros) and ends in state_out (NULL =
+    // not kept).  seg_len = 0: the prep kernel walks every slot; seg_len > 0:
+    // it walks (sequence, chunk in the range, value head) items.
+    int64_t seg_j0, seg_j1;
+    int32_t seg_len;
+    const float* state_in;
+    float* state_out;
 };
 
 // Workspace layout of one prefill call (byte offsets of each part and total),
@@ -64,9 +72,16 @@ struct PrefillWorkspace {
     }
 };
 
+// Chunks per segment when the prefill is split into segments whose prep and
+// scan overlap (0: one launch of each kernel).  Segmenting pays when the scan
+// alone cannot fill the device (few sequences x heads) and sequences are long.
+int64_t prefill_segment_chunks(int64_t num_tokens, int num_seqs, int hv, int dv);
+
 // Launchers: return hipSuccess or the launch error.  `bf16` selects the
 // element type of q/k/v/out; dk/dv are 64 or 128.
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, int dk, int dv, hipStream_t s);
-hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int dk, int dv, hipStream_t s);
+// `state_ws` (N * hv * dv * dk floats) carries the state between segments;
+// it may be NULL when prefill_segment_chunks() returned 0.
+hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int dk, int dv, float* state_ws, hipStream_t s);
 
 }  // namespace gdn

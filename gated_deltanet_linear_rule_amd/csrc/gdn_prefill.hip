@@ -38,6 +38,9 @@
 // beta = 0 in the prep kernel; padded rows then carry u = 0 and zero rows of
 // W and K~, so they leave S and the real rows untouched, and
 // gamma_last = e^{G2_63} equals the decay up to the last real token.
+#include <mutex>
+#include <vector>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -140,17 +143,23 @@ template <typename OP> struct Frag {
     static constexpr int FU = 8 / VE;                    // units per operand fragment
 };
 
+// Workspace stores are non-temporal: the scan reads them back much later (or
+// on other compute units), and they should not push its working set out of
+// the caches meanwhile.
+template <typename T>
+__device__ __forceinline__ void ws_store(T* p, const T& x) { __builtin_nontemporal_store(x, p); }
+
 template <typename OP>
 __device__ __forceinline__ void store_frag(OP* base, int f, const typename Op<OP>::frag& x) {
     constexpr int VE = Frag<OP>::VE, FU = Frag<OP>::FU;
     const int l = lane_id();
     if constexpr (FU == 1) {
-        *reinterpret_cast<typename Op<OP>::frag*>(base + ((size_t)f * 64 + l) * VE) = x;
+        ws_store(reinterpret_cast<typename Op<OP>::frag*>(base + ((size_t)f * 64 + l) * VE), x);
     } else {
-        *reinterpret_cast<f32x4*>(base + ((size_t)(f * 2) * 64 + l) * VE) =
-            __builtin_shufflevector(x, x, 0, 1, 2, 3);
-        *reinterpret_cast<f32x4*>(base + ((size_t)(f * 2 + 1) * 64 + l) * VE) =
-            __builtin_shufflevector(x, x, 4, 5, 6, 7);
+        ws_store(reinterpret_cast<f32x4*>(base + ((size_t)(f * 2) * 64 + l) * VE),
+                 f32x4(__builtin_shufflevector(x, x, 0, 1, 2, 3)));
+        ws_store(reinterpret_cast<f32x4*>(base + ((size_t)(f * 2 + 1) * 64 + l) * VE),
+                 f32x4(__builtin_shufflevector(x, x, 4, 5, 6, 7)));
     }
 }
 
@@ -225,7 +234,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void gdn_prep_kernel(PrefillArgs a
     const OP* kg = static_cast<const OP*>(a.k);
     const OP* qg = static_cast<const OP*>(a.q);
     const OP* vg = static_cast<const OP*>(a.v);
-    const int64_t nitems = a.num_slots * a.hv;
+    const int64_t nitems = a.seg_len > 0 ? (int64_t)a.num_seqs * a.seg_len * a.hv : a.num_slots * a.hv;
 
     // One work item = one (slot, value head); a workgroup walks the items
     // blockIdx.x, blockIdx.x + gridDim.x, ..., fetching the next item's
@@ -239,11 +248,26 @@ __global__ __launch_bounds__(kPrepThreads, 2) void gdn_prep_kernel(PrefillArgs a
         Item it{};
         it.ok = false;
         if (item < nitems) {
-            it.slot = item / a.hv;
-            it.h = (int)(item - it.slot * a.hv);
-            int n;
             int64_t t1;
-            it.ok = locate_slot(si, a.num_seqs, it.slot, n, it.t0, t1);
+            if (a.seg_len > 0) {
+                // (sequence, chunk j in [seg_j0, seg_j1), value head)
+                const int64_t per_seq = (int64_t)a.seg_len * a.hv;
+                const int n = (int)(item / per_seq);
+                const int64_t rem = item - n * per_seq;
+                const int64_t j = a.seg_j0 + rem / a.hv;
+                it.h = (int)(rem - (rem / a.hv) * a.hv);
+                const int64_t s0 = si.start(n);
+                t1 = si.start(n + 1);
+                it.t0 = s0 + j * kChunk;
+                it.slot = slot_base(s0, n) + j;
+                it.ok = j < a.seg_j1 && it.t0 < t1;
+            } else {
+                // every slot
+                it.slot = item / a.hv;
+                it.h = (int)(item - it.slot * a.hv);
+                int n;
+                it.ok = locate_slot(si, a.num_seqs, it.slot, n, it.t0, t1);
+            }
             it.nt = it.ok ? (int)((t1 - it.t0) < kChunk ? (t1 - it.t0) : kChunk) : 0;
             it.hq = (it.h * a.hqk) / a.hv;
         }
@@ -387,7 +411,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void gdn_prep_kernel(PrefillArgs a
         const int row = 16 * (f >> 1) + (ln & 15);
         const int col = 32 * (f & 1) + 8 * (ln >> 4) + VE * ((e >> 6) % FU);
         const u32x4 x = ((col >> 4) > (row >> 4)) ? zero_u4() : ld16(sm.P + row * LDP + col);
-        *reinterpret_cast<u32x4*>(Pw + (size_t)e * VE) = x;
+        ws_store(reinterpret_cast<u32x4*>(Pw + (size_t)e * VE), x);
     }
 #pragma unroll
     for (int i = 0; i < VREG; ++i) {
@@ -493,7 +517,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void gdn_prep_kernel(PrefillArgs a
                 quad uq;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) uq[i] = from_f32<OP>(acc[i]);
-                *reinterpret_cast<quad*>(Uw + ((size_t)(tw * NCB + 2 * cp + sub) * 64 + l) * 4) = uq;
+                ws_store(reinterpret_cast<quad*>(Uw + ((size_t)(tw * NCB + 2 * cp + sub) * 64 + l) * 4), uq);
             }
         }
     }
@@ -739,9 +763,9 @@ __device__ __forceinline__ void scan_wave(const PrefillArgs& a, ScanSmem<OP, DK>
     // S[sub][i] = S[c][32 w + 16 sub + 4 gq + i]
     f32x4 S[2];
     const size_t srow = ((size_t)chain * a.dv + c) * DK + 32 * w + 4 * gq;
-    if (a.init_state) {
-        S[0] = *reinterpret_cast<const f32x4*>(a.init_state + srow);
-        S[1] = *reinterpret_cast<const f32x4*>(a.init_state + srow + 16);
+    if (a.state_in) {
+        S[0] = *reinterpret_cast<const f32x4*>(a.state_in + srow);
+        S[1] = *reinterpret_cast<const f32x4*>(a.state_in + srow + 16);
     } else {
         S[0] = zero4();
         S[1] = zero4();
@@ -752,10 +776,13 @@ __device__ __forceinline__ void scan_wave(const PrefillArgs& a, ScanSmem<OP, DK>
     const unsigned o_rw = (unsigned)((l >> 2) * G::VROWB + G::QE * ((l & 3) ^ swz_vo(l >> 2, E)));
     const unsigned o_tl = (unsigned)(r * G::VROWB + G::QE * (gq ^ swz_vo(r, E)));
 
+    // this launch's chunks of the sequence: [jb, je)
     const int64_t nchunks = (s1 - s0 + kChunk - 1) / kChunk;
+    const int64_t jb = a.seg_j0 < nchunks ? a.seg_j0 : nchunks;
+    const int64_t je = a.seg_j1 < nchunks ? a.seg_j1 : nchunks;
     auto chunk = [&](St& cur, int64_t j) {
         const int64_t t0 = s0 + j * kChunk;
-        const bool pre = j + 2 < nchunks;
+        const bool pre = j + 2 < je;
         // ---- the whole start state, slice by slice
         frag Sf[NWS];
         Sf[w] = Ops::pack(S[0], S[1]);
@@ -827,8 +854,9 @@ __device__ __forceinline__ void scan_wave(const PrefillArgs& a, ScanSmem<OP, DK>
         // O through the wave's staging area to row-wise stores; rows past the
         // end of the sequence fall outside the resource
         {
-            const int64_t ntl = j < 0 ? 0 : s1 - t0;
-            const auto ro = make_rsrc(static_cast<OP*>(a.out) + ((size_t)(j < 0 ? s0 : t0) * a.hv + h) * a.dv + blk * 16,
+            const bool mine = j >= jb && j < je;
+            const int64_t ntl = mine ? s1 - t0 : 0;
+            const auto ro = make_rsrc(static_cast<OP*>(a.out) + ((size_t)(mine ? t0 : s0) * a.hv + h) * a.dv + blk * 16,
                                       ntl > 0 ? (ntl - 1) * ctx.v_row + 16 * E : 0);
 #pragma unroll
             for (int jt = 0; jt < TPW; ++jt) {
@@ -854,13 +882,13 @@ __device__ __forceinline__ void scan_wave(const PrefillArgs& a, ScanSmem<OP, DK>
     // Let the initial-state load land here, outside the loop: otherwise the
     // loop head would have to wait for every load in flight on each pass.
     __builtin_amdgcn_s_waitcnt(0);
-    for (int64_t j = -2; j < nchunks; j += 2) {
+    for (int64_t j = jb - 2; j < je; j += 2) {
         chunk(A, j);
         chunk(Bs, j + 1);
     }
-    if (a.final_state) {
-        *reinterpret_cast<f32x4*>(a.final_state + srow) = S[0];
-        *reinterpret_cast<f32x4*>(a.final_state + srow + 16) = S[1];
+    if (a.state_out) {
+        *reinterpret_cast<f32x4*>(a.state_out + srow) = S[0];
+        *reinterpret_cast<f32x4*>(a.state_out + srow + 16) = S[1];
     }
 }
 
@@ -889,29 +917,33 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_kernel(PrefillArgs a
     }
 }
 
+// cu_share: the fraction (1 / cu_share) of the device's compute units the
+// stream st may use.
 template <typename OP, int DK, int DV>
-hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
-    {
-        // persistent: as many workgroups as fit on the device at once
-        static int resident[64] = {};   // per device, filled on first use
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
+hipError_t launch_prep(const PrefillArgs& a, hipStream_t st, int cu_share = 1) {
+    // persistent: as many workgroups as fit on the device at once
+    static int resident[64] = {};   // per device, filled on first use
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (resident[dev] == 0) {
+        int cus = 0, per_cu = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
-        if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-        if (resident[dev] == 0) {
-            int cus = 0, per_cu = 0;
-            e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-            if (e != hipSuccess) return e;
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gdn_prep_kernel<OP, DK, DV>, kPrepThreads, 0);
-            if (e != hipSuccess) return e;
-            resident[dev] = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
-        }
-        const int64_t items = a.num_slots * a.hv;
-        const unsigned nwg = (unsigned)(items < resident[dev] ? items : resident[dev]);
-        hipLaunchKernelGGL((gdn_prep_kernel<OP, DK, DV>), dim3(nwg), dim3(kPrepThreads), 0, st, a);
-        e = hipGetLastError();
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gdn_prep_kernel<OP, DK, DV>, kPrepThreads, 0);
         if (e != hipSuccess) return e;
+        resident[dev] = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
     }
+    const int64_t items = a.seg_len > 0 ? (int64_t)a.num_seqs * a.seg_len * a.hv : a.num_slots * a.hv;
+    const int64_t fit = resident[dev] / cu_share > 0 ? resident[dev] / cu_share : 1;
+    const unsigned nwg = (unsigned)(items < fit ? items : fit);
+    hipLaunchKernelGGL((gdn_prep_kernel<OP, DK, DV>), dim3(nwg), dim3(kPrepThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename OP, int DK>
+hipError_t launch_scan(const PrefillArgs& a, hipStream_t st) {
     const int64_t chains = (int64_t)a.num_seqs * a.hv;
     const int nblk = a.dv / 16;
     const int xcd = (nblk == 8 && chains % 8 == 0) ? 1 : 0;
@@ -920,17 +952,118 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Per-device resources of the segmented launch: one stream for the prep
+// kernels and one for the scan kernels, each confined to one half of the
+// compute units (alternate CUs, so each half spans every XCD), so that the
+// two kernels overlap without sharing a CU; plus a pool of events.  Created
+// on first use (default priority; plain streams if CU masks are unavailable)
+// and kept for the life of the process.
+constexpr int kMaxSegments = 64;
+struct SegmentResources {
+    hipStream_t prep = nullptr, scan = nullptr;
+    int cu_share = 1;              // 2 when each stream has half of the CUs
+    hipEvent_t ev[kMaxSegments + 2] = {};
+};
+
+hipError_t segment_resources(int dev, SegmentResources** out) {
+    static SegmentResources res[64];
+    static std::mutex mu;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    SegmentResources& r = res[dev];
+    if (!r.prep) {
+        int cus = 0;
+        hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        std::vector<uint32_t> even((cus + 31) / 32, 0u), odd((cus + 31) / 32, 0u);
+        for (int c = 0; c < cus; ++c) (c % 2 ? odd : even)[c / 32] |= 1u << (c % 32);
+        if (cus < 2 ||
+            hipExtStreamCreateWithCUMask(&r.scan, (uint32_t)even.size(), even.data()) != hipSuccess ||
+            hipExtStreamCreateWithCUMask(&r.prep, (uint32_t)odd.size(), odd.data()) != hipSuccess) {
+            (void)hipGetLastError();
+            if (r.scan) (void)hipStreamDestroy(r.scan);
+            r.scan = nullptr;
+            if ((e = hipStreamCreateWithFlags(&r.scan, hipStreamNonBlocking)) != hipSuccess) { r.scan = nullptr; return e; }
+            if ((e = hipStreamCreateWithFlags(&r.prep, hipStreamNonBlocking)) != hipSuccess) { r.prep = nullptr; return e; }
+        } else {
+            r.cu_share = 2;
+        }
+        for (auto& ev : r.ev) {
+            e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+            if (e != hipSuccess) return e;
+        }
+    }
+    *out = &r;
+    return hipSuccess;
+}
+
+template <typename OP, int DK, int DV>
+hipError_t launch_prefill_t(const PrefillArgs& a0, float* state_ws, hipStream_t st) {
+    PrefillArgs a = a0;
+    const int64_t cs = prefill_segment_chunks(a0.num_tokens, a0.num_seqs, a0.hv, a0.dv);
+    if (cs == 0 || !state_ws) {
+        a.seg_j0 = 0;
+        a.seg_j1 = INT64_MAX / 2;
+        a.seg_len = 0;
+        a.state_in = a0.init_state;
+        a.state_out = a0.final_state;
+        hipError_t e = launch_prep<OP, DK, DV>(a, st);
+        if (e != hipSuccess) return e;
+        return launch_scan<OP, DK>(a, st);
+    }
+    // Segments of cs chunks: the prep of segment k+1 runs while the scan
+    // works through segment k; the state passes from segment to segment
+    // through state_ws.  Both internal streams start after everything already
+    // queued on st, and st resumes after the last scan.
+    const int64_t max_chunks = a0.cu ? (a0.num_tokens + kChunk - 1) / kChunk : (a0.seqlen + kChunk - 1) / kChunk;
+    const int nseg = (int)((max_chunks + cs - 1) / cs);
+    if (nseg > kMaxSegments) return hipErrorInvalidValue;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    SegmentResources* R = nullptr;
+    if ((e = segment_resources(dev, &R)) != hipSuccess) return e;
+    if ((e = hipEventRecord(R->ev[0], st)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(R->prep, R->ev[0], 0)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(R->scan, R->ev[0], 0)) != hipSuccess) return e;
+    for (int k = 0; k < nseg; ++k) {
+        a.seg_j0 = k * cs;
+        a.seg_j1 = (k + 1) * cs;
+        a.seg_len = (int32_t)cs;
+        a.state_in = k == 0 ? a0.init_state : state_ws;
+        a.state_out = k == nseg - 1 ? a0.final_state : state_ws;
+        if ((e = launch_prep<OP, DK, DV>(a, R->prep, R->cu_share)) != hipSuccess) return e;
+        if ((e = hipEventRecord(R->ev[k + 1], R->prep)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(R->scan, R->ev[k + 1], 0)) != hipSuccess) return e;
+        if ((e = launch_scan<OP, DK>(a, R->scan)) != hipSuccess) return e;
+    }
+    if ((e = hipEventRecord(R->ev[nseg + 1], R->scan)) != hipSuccess) return e;
+    return hipStreamWaitEvent(st, R->ev[nseg + 1], 0);
+}
+
 template <typename OP>
-hipError_t launch_prefill_dt(const PrefillArgs& a, int dk, int dv, hipStream_t st) {
-    if (dk == 128) return dv == 128 ? launch_prefill_t<OP, 128, 128>(a, st) : launch_prefill_t<OP, 128, 64>(a, st);
-    return dv == 128 ? launch_prefill_t<OP, 64, 128>(a, st) : launch_prefill_t<OP, 64, 64>(a, st);
+hipError_t launch_prefill_dt(const PrefillArgs& a, int dk, int dv, float* state_ws, hipStream_t st) {
+    if (dk == 128)
+        return dv == 128 ? launch_prefill_t<OP, 128, 128>(a, state_ws, st) : launch_prefill_t<OP, 128, 64>(a, state_ws, st);
+    return dv == 128 ? launch_prefill_t<OP, 64, 128>(a, state_ws, st) : launch_prefill_t<OP, 64, 64>(a, state_ws, st);
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int dk, int dv, hipStream_t st) {
+int64_t prefill_segment_chunks(int64_t num_tokens, int num_seqs, int hv, int dv) {
+    if (num_seqs <= 0 || num_seqs > 8) return 0;
+    const int64_t scan_wgs = (int64_t)num_seqs * hv * (dv / 16);
+    const int64_t avg_chunks = (num_tokens / num_seqs + kChunk - 1) / kChunk;
+    if (scan_wgs > 192 || avg_chunks < 512) return 0;
+    const int64_t max_chunks = (num_tokens + kChunk - 1) / kChunk;
+    int64_t cs = 256;
+    while ((max_chunks + cs - 1) / cs > 32) cs *= 2;
+    return cs;
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int dk, int dv, float* state_ws, hipStream_t st) {
     if (a.num_seqs == 0) return hipSuccess;
-    return bf16 ? launch_prefill_dt<__bf16>(a, dk, dv, st) : launch_prefill_dt<float>(a, dk, dv, st);
+    return bf16 ? launch_prefill_dt<__bf16>(a, dk, dv, state_ws, st) : launch_prefill_dt<float>(a, dk, dv, state_ws, st);
 }
 
 }  // namespace gdn

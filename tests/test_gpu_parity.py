@@ -105,6 +105,39 @@ def test_long_decay_free_stretch_stays_accurate():
     check_prefill(inp, label="g=0, beta/10")
 
 
+# ------------------------------------------------- segmented prep/scan launch
+# Few long sequences run as segments of 256 chunks whose prep overlaps the
+# previous segment's scan, with the state carried between segments.
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_segmented_long_sequence(dtype):
+    """One 40000-token sequence (625 chunks: three segments, the last partial), given initial state."""
+    inp = gi.make_inputs(gi.custom(dtype=dtype, Hqk=2, Hv=2, dk=128, dv=128, seqlens=(40000,),
+                                   init_state="normal"), seed=21)
+    check_prefill(inp, label=f"segmented 40000 {dtype}")
+
+
+def test_segmented_unequal_packed_sequences():
+    """Two packed sequences of 33000 and 40000 tokens: segments past the end of the shorter one
+    carry its state through unchanged."""
+    inp = gi.make_inputs(gi.custom(dtype="bf16", Hqk=1, Hv=2, dk=128, dv=64, seqlens=(33000, 40000),
+                                   init_state="normal"), seed=22)
+    check_prefill(inp, label="segmented 33000+40000")
+
+
+def test_segmented_equal_length_batch_without_offsets_in_place_state():
+    """Two 36864-token sequences without offsets, initial state updated in place."""
+    inp = gi.make_inputs(gi.custom(dtype="bf16", Hqk=2, Hv=2, dk=64, dv=128, seqlens=(36864, 36864),
+                                   init_state="normal"), seed=23)
+    cu = inp.cu_seqlens
+    inp.cu_seqlens = None            # equal lengths: the library derives the offsets
+    out, fin = run_prefill(inp, out_alias=True, num_seqs=2)
+    inp.cu_seqlens = cu
+    ro, rf = c_oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.init_state, cu)
+    eo, ef = rel_err(out, ro), rel_err(fin, rf)
+    say(f"[parity] segmented 2x36864 no offsets, in place: out {eo:.3e} final {ef:.3e}")
+    assert eo <= 1e-2 and ef <= 1e-2
+
+
 # ------------------------------------------------------------- the workloads
 def test_tiny_f32_workload():
     """T=256, H=2, d=64, fp32 throughout, zero initial state, seed 0."""

@@ -11,8 +11,9 @@ tokens) is reported in the same JSON line as state GB/s.
 
 Timing uses HIP events on the stream the library launches on (torch's
 current stream, handed to the C ABI).  `roofline` uses algorithmic bytes and
-flops per call (see the design doc for the formulas); `cpu_baseline` times the
-fp64 oracle on a bounded sample of the same prefill workload on host cores.
+flops per call (prefill_bytes, prefill_flops_per_token below); `cpu_baseline`
+times the fp64 oracle on a bounded sample of the same prefill workload on
+host cores.
 """
 from __future__ import annotations
 

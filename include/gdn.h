@@ -49,7 +49,7 @@ extern "C" {
 typedef enum gdn_status {
     GDN_SUCCESS = 0,
     GDN_ERROR_INVALID_VALUE = 1,  /* malformed argument (NULL, negative size, misaligned ...) */
-    GDN_ERROR_NOT_SUPPORTED = 2,  /* well-formed shape this build has no kernel for */
+    GDN_ERROR_NOT_SUPPORTED = 2,  /* well-formed shape the library has no kernel for */
     GDN_ERROR_LAUNCH = 3,         /* a HIP launch or enqueue failed */
     GDN_ERROR_OUT_OF_MEMORY = 4   /* the stream-ordered workspace could not be allocated */
 } gdn_status;

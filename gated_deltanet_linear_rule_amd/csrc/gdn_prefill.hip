@@ -552,8 +552,8 @@ __global__ __launch_bounds__(kPrepThreads, 2) void gdn_prep_kernel(PrefillArgs a
 // consecutive bytes: all operands come fragment-major from the prep kernel's
 // workspace (one 1 KB block per fragment; u as 8-byte lane records), and O
 // passes through a small wave-private LDS area between the lanes' tile layout
-// and row-wise global stores.  Operands are fetched two chunks ahead, each
-// group issued right after the product that consumes the registers it
+// and row-wise global stores.  Operands are fetched several chunks ahead,
+// each group issued right after the product that consumes the registers it
 // refills, so that the vector memory queue is fed evenly through the chunk.
 // All loads go through buffer resources (reads past the end of a resource
 // return 0, writes past it are dropped), and no load, store or use of a
@@ -618,8 +618,9 @@ __device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOM
 
 template <typename OP, int DK>
 struct ScanGeom {
-    static constexpr int NWS = DK / 32;                 // waves per workgroup (d_k slices)
+    static constexpr int NWS = DK / 32;                 // d_k slices = waves per role
     static constexpr int TPW = 4 / NWS;                 // token tiles per wave
+    static constexpr int NT = 2 * NWS * kWave;          // threads per workgroup
     static constexpr int E = (int)sizeof(OP);
     static constexpr int FU = Frag<OP>::FU;             // 16-byte units per operand fragment
     static constexpr int QE = 4 * E;                    // bytes per 4-element quad
@@ -633,9 +634,10 @@ struct ScanSmem {
     using G = ScanGeom<OP, DK>;
     typename Op<OP>::frag sfr[G::NWS][kWave];   // state slices as operand fragments
     alignas(16) OP Ut[16 * G::RLD];             // U as [column][token]
-    alignas(16) char ost[G::NWS][G::TPW][G::VB];   // wave-private O tiles
+    alignas(16) char ost[G::NWS][G::TPW][G::VB];   // output waves' private O tiles
 };
 
+// Per-wave addressing of one sequence's operands in the workspace.
 template <typename OP, int DK>
 struct ScanCtx {
     using G = ScanGeom<OP, DK>;
@@ -643,13 +645,15 @@ struct ScanCtx {
     using frag = typename Op<OP>::frag;
     using quad = typename Op<OP>::quad;
     static constexpr int NWS = G::NWS, TPW = G::TPW, E = G::E, FU = G::FU;
-    // One chunk's operands for one wave.
-    struct Stage {
+    // operands of one chunk for a state wave and for an output wave
+    struct StateStage {
         frag wf[TPW][NWS];   // W[16 tw + r][paired d_k of slice s]
-        frag qf[TPW][NWS];   // Q~, same positions
         quad u[TPW];         // u[16 tw + 4 gq + i][16 blk + r]
         frag kt[2][2];       // K~^T[32 w + 16 sub + r][paired tokens from 32 kk]
         float gl;            // G2_last
+    };
+    struct OutStage {
+        frag qf[TPW][NWS];   // Q~[16 tw + r][paired d_k of slice s]
         frag p[TPW][2];      // P[16 tw + r][32 kk + 8 gq + (0..7)]
     };
 
@@ -694,28 +698,24 @@ struct ScanCtx {
 
     __device__ __forceinline__ static int64_t cj(int64_t j, bool valid) { return valid ? j : 0; }
     // Fetch parts of the sequence's chunk j (zeros when !valid).
-    __device__ __forceinline__ void load_w(Stage& s, int64_t j, bool valid) const {
-        const auto rw = make_rsrc(wb + cj(j, valid) * m_step, valid ? (int64_t)kChunk * DK * E : 0);
+    template <typename S>
+    __device__ __forceinline__ void load_tiles(frag (&f)[TPW][NWS], const char* base, int64_t j, bool valid) const {
+        const auto rs = make_rsrc(base + cj(j, valid) * m_step, valid ? (int64_t)kChunk * DK * E : 0);
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt)
 #pragma unroll
             for (int sl = 0; sl < NWS; ++sl)
-                s.wf[jt][sl] = B::frag(rw, f_voff, (unsigned)((sl * 4 + w + NWS * jt) * FU * 1024));
+                f[jt][sl] = B::frag(rs, f_voff, (unsigned)((sl * 4 + w + NWS * jt) * FU * 1024));
     }
-    __device__ __forceinline__ void load_q(Stage& s, int64_t j, bool valid) const {
-        const auto rq = make_rsrc(qb + cj(j, valid) * m_step, valid ? (int64_t)kChunk * DK * E : 0);
-#pragma unroll
-        for (int jt = 0; jt < TPW; ++jt)
-#pragma unroll
-            for (int sl = 0; sl < NWS; ++sl)
-                s.qf[jt][sl] = B::frag(rq, f_voff, (unsigned)((sl * 4 + w + NWS * jt) * FU * 1024));
+    __device__ __forceinline__ void load_w(StateStage& s, int64_t j, bool valid) const {
+        load_tiles<StateStage>(s.wf, wb, j, valid);
     }
-    __device__ __forceinline__ void load_u(Stage& s, int64_t j, bool valid) const {
+    __device__ __forceinline__ void load_u(StateStage& s, int64_t j, bool valid) const {
         const auto ru = make_rsrc(ub + cj(j, valid) * u_step, valid ? u_bytes : 0);
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt) s.u[jt] = B::quad(ru, u_voff[jt]);
     }
-    __device__ __forceinline__ void load_k(Stage& s, int64_t j, bool valid) const {
+    __device__ __forceinline__ void load_k(StateStage& s, int64_t j, bool valid) const {
         const int64_t jc = cj(j, valid);
         const auto rk = make_rsrc(kb + jc * m_step, valid ? (int64_t)kChunk * DK * E : 0);
 #pragma unroll
@@ -726,7 +726,10 @@ struct ScanCtx {
         const auto rg = make_rsrc(gb + jc * g_step, valid ? 4 : 0);
         s.gl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, 0, 0, 0));
     }
-    __device__ __forceinline__ void load_p(Stage& s, int64_t j, bool valid) const {
+    __device__ __forceinline__ void load_q(OutStage& s, int64_t j, bool valid) const {
+        load_tiles<OutStage>(s.qf, qb, j, valid);
+    }
+    __device__ __forceinline__ void load_p(OutStage& s, int64_t j, bool valid) const {
         const auto rp = make_rsrc(pb + cj(j, valid) * p_step, valid ? kChunk * kChunk * E : 0);
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt)
@@ -736,33 +739,62 @@ struct ScanCtx {
     }
 };
 
-// The work of wave W of a scan workgroup (W is a compile-time constant, so
-// every tile index below is static).
+// Sequence bookkeeping shared by both roles.
+struct ScanSeq {
+    int n, h;
+    int64_t s0, s1, base, jb, je;
+};
+__device__ __forceinline__ ScanSeq scan_seq(const PrefillArgs& a, int chain) {
+    ScanSeq q;
+    q.n = chain / a.hv;
+    q.h = chain - q.n * a.hv;
+    const SeqIndex si{a.cu, a.seqlen};
+    q.s0 = si.start(q.n);
+    q.s1 = si.start(q.n + 1);
+    q.base = slot_base(q.s0, q.n);
+    // this launch's chunks of the sequence: [jb, je)
+    const int64_t nchunks = (q.s1 - q.s0 + kChunk - 1) / kChunk;
+    q.jb = a.seg_j0 < nchunks ? a.seg_j0 : nchunks;
+    q.je = a.seg_j1 < nchunks ? a.seg_j1 : nchunks;
+    return q;
+}
+
+// Both roles walk the same chunk sequence with the same two barriers per
+// chunk.  Operands are fetched kStages chunks ahead into a ring of kStages
+// register stages (measured on MI355X: 2, 3, 4 and 6 stages stream equally
+// fast; the compute unit's own limit on outstanding misses, not the depth,
+// bounds the rate).  The loop starts kStages chunks
+// early on zeroed stages, so that every load is issued inside the loop body
+// and the memory-counter waits see the same load order on every path.  An
+// empty chunk -- the leading ones, and the trailing ones that round the count
+// up to a multiple of kStages -- is an exact no-op: its operands are zeros
+// (G2_last = 0, so gamma_last = 1, and U = 0 leaves S unchanged) and its
+// stores are dropped.
+#ifndef GDN_SCAN_STAGES
+#define GDN_SCAN_STAGES 2
+#endif
+template <typename OP> constexpr int scan_stages() { return sizeof(OP) == 2 ? GDN_SCAN_STAGES : 2; }
+
+// State wave W: owns d_k slice W of the state and token tiles W + NWS jt.
 template <typename OP, int DK, int W>
-__device__ __forceinline__ void scan_wave(const PrefillArgs& a, ScanSmem<OP, DK>& sm, int chain, int blk) {
+__device__ __forceinline__ void scan_state_wave(const PrefillArgs& a, ScanSmem<OP, DK>& sm, int chain, int blk) {
     using Ops = Op<OP>;
     using frag = typename Ops::frag;
     using quad = typename Ops::quad;
     using G = ScanGeom<OP, DK>;
     using Ctx = ScanCtx<OP, DK>;
-    using St = typename Ctx::Stage;
-    using B = Buf<OP>;
-    constexpr int NWS = G::NWS, TPW = G::TPW, RLD = G::RLD, E = G::E;
+    using St = typename Ctx::StateStage;
+    constexpr int NWS = G::NWS, TPW = G::TPW, RLD = G::RLD;
+    constexpr int kStages = scan_stages<OP>();
     constexpr int w = W;
-    const int n = chain / a.hv;
-    const int h = chain - n * a.hv;
     const int l = lane_id(), r = l & 15, gq = l >> 4;
-    const int c = blk * 16 + r;
-
-    const SeqIndex si{a.cu, a.seqlen};
-    const int64_t s0 = si.start(n), s1 = si.start(n + 1);
-    const int64_t base = slot_base(s0, n);
+    const ScanSeq q = scan_seq(a, chain);
     Ctx ctx;
-    ctx.init(a, base, h, blk, w);
+    ctx.init(a, q.base, q.h, blk, w);
 
-    // S[sub][i] = S[c][32 w + 16 sub + 4 gq + i]
+    // S[sub][i] = S[c][32 w + 16 sub + 4 gq + i], c = 16 blk + r
     f32x4 S[2];
-    const size_t srow = ((size_t)chain * a.dv + c) * DK + 32 * w + 4 * gq;
+    const size_t srow = ((size_t)chain * a.dv + blk * 16 + r) * DK + 32 * w + 4 * gq;
     if (a.state_in) {
         S[0] = *reinterpret_cast<const f32x4*>(a.state_in + srow);
         S[1] = *reinterpret_cast<const f32x4*>(a.state_in + srow + 16);
@@ -771,19 +803,9 @@ __device__ __forceinline__ void scan_wave(const PrefillArgs& a, ScanSmem<OP, DK>
         S[1] = zero4();
     }
 
-    // O staging: row-wise side (row l >> 2, quad l & 3) and tile side
-    // (row r, quad gq), byte offsets inside a tile
-    const unsigned o_rw = (unsigned)((l >> 2) * G::VROWB + G::QE * ((l & 3) ^ swz_vo(l >> 2, E)));
-    const unsigned o_tl = (unsigned)(r * G::VROWB + G::QE * (gq ^ swz_vo(r, E)));
-
-    // this launch's chunks of the sequence: [jb, je)
-    const int64_t nchunks = (s1 - s0 + kChunk - 1) / kChunk;
-    const int64_t jb = a.seg_j0 < nchunks ? a.seg_j0 : nchunks;
-    const int64_t je = a.seg_j1 < nchunks ? a.seg_j1 : nchunks;
     auto chunk = [&](St& cur, int64_t j) {
-        const int64_t t0 = s0 + j * kChunk;
-        const bool pre = j + 2 < je;
-        // ---- the whole start state, slice by slice
+        const bool pre = j + kStages < q.je;
+        // ---- publish this wave's state slice; read the others
         frag Sf[NWS];
         Sf[w] = Ops::pack(S[0], S[1]);
         sm.sfr[w][l] = Sf[w];
@@ -804,7 +826,7 @@ __device__ __forceinline__ void scan_wave(const PrefillArgs& a, ScanSmem<OP, DK>
             Z[jt] = z0 + z1;
         }
         pin();
-        ctx.load_w(cur, j + 2, pre);
+        ctx.load_w(cur, j + kStages, pre);
         pin();
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt) {
@@ -815,9 +837,65 @@ __device__ __forceinline__ void scan_wave(const PrefillArgs& a, ScanSmem<OP, DK>
             *reinterpret_cast<quad*>(&sm.Ut[r * RLD + 16 * tw + 4 * gq]) = uq;
         }
         pin();
-        ctx.load_u(cur, j + 2, pre);
+        ctx.load_u(cur, j + kStages, pre);
         pin();
-        // ---- Y^T = S Q~^T for the wave's token tiles (off the serial chain)
+        __syncthreads();                                                        // B2
+        // ---- S_w^T <- gamma_last S_w^T + K~_w^T U
+        const float gn = fast_exp2(cur.gl);
+        const frag Db0 = frag_rows(sm.Ut, RLD, r, 0), Db1 = frag_rows(sm.Ut, RLD, r, 32);
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+            S[sub] = Ops::mma(cur.kt[sub][1], Db1, Ops::mma(cur.kt[sub][0], Db0, gn * S[sub]));
+        pin();
+        ctx.load_k(cur, j + kStages, pre);
+        pin();
+    };
+
+    St st[kStages] = {};
+    // Let the initial-state load land here, outside the loop: otherwise the
+    // loop head would have to wait for every load in flight on each pass.
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int64_t j = q.jb - kStages; j < q.je; j += kStages) {
+#pragma unroll
+        for (int i = 0; i < kStages; ++i) chunk(st[i], j + i);
+    }
+    if (a.state_out) {
+        *reinterpret_cast<f32x4*>(a.state_out + srow) = S[0];
+        *reinterpret_cast<f32x4*>(a.state_out + srow + 16) = S[1];
+    }
+}
+
+// Output wave W: token tiles W + NWS jt; reads the published state and U.
+template <typename OP, int DK, int W>
+__device__ __forceinline__ void scan_output_wave(const PrefillArgs& a, ScanSmem<OP, DK>& sm, int chain, int blk) {
+    using Ops = Op<OP>;
+    using frag = typename Ops::frag;
+    using quad = typename Ops::quad;
+    using G = ScanGeom<OP, DK>;
+    using Ctx = ScanCtx<OP, DK>;
+    using St = typename Ctx::OutStage;
+    using B = Buf<OP>;
+    constexpr int NWS = G::NWS, TPW = G::TPW, RLD = G::RLD, E = G::E;
+    constexpr int kStages = scan_stages<OP>();
+    constexpr int w = W;
+    const int l = lane_id(), r = l & 15, gq = l >> 4;
+    const ScanSeq q = scan_seq(a, chain);
+    Ctx ctx;
+    ctx.init(a, q.base, q.h, blk, w);
+
+    // O staging: row-wise side (row l >> 2, quad l & 3) and tile side
+    // (row r, quad gq), byte offsets inside a tile
+    const unsigned o_rw = (unsigned)((l >> 2) * G::VROWB + G::QE * ((l & 3) ^ swz_vo(l >> 2, E)));
+    const unsigned o_tl = (unsigned)(r * G::VROWB + G::QE * (gq ^ swz_vo(r, E)));
+
+    auto chunk = [&](St& cur, int64_t j) {
+        const int64_t t0 = q.s0 + j * kChunk;
+        const bool pre = j + kStages < q.je;
+        __syncthreads();                                                        // B1
+        frag Sf[NWS];
+#pragma unroll
+        for (int sl = 0; sl < NWS; ++sl) Sf[sl] = sm.sfr[sl][l];
+        // ---- Y^T = S Q~^T for the wave's token tiles
         f32x4 Y[TPW];
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt) {
@@ -830,18 +908,9 @@ __device__ __forceinline__ void scan_wave(const PrefillArgs& a, ScanSmem<OP, DK>
             Y[jt] = y0 + y1;
         }
         pin();
-        ctx.load_q(cur, j + 2, pre);
+        ctx.load_q(cur, j + kStages, pre);
         pin();
         __syncthreads();                                                        // B2
-        // ---- S_w^T <- gamma_last S_w^T + K~_w^T U   (the serial chain first)
-        const float gn = fast_exp2(cur.gl);
-        const frag Db0 = frag_rows(sm.Ut, RLD, r, 0), Db1 = frag_rows(sm.Ut, RLD, r, 32);
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-            S[sub] = Ops::mma(cur.kt[sub][1], Db1, Ops::mma(cur.kt[sub][0], Db0, gn * S[sub]));
-        pin();
-        ctx.load_k(cur, j + 2, pre);
-        pin();
         // ---- O^T tiles: rows = columns 16 blk + 4 gq + i, column = token 16 tw + r
         const frag Ub0 = frag_nat(sm.Ut, RLD, r, 0), Ub1 = frag_nat(sm.Ut, RLD, r, 32);
         f32x4 Ot[TPW];
@@ -849,51 +918,37 @@ __device__ __forceinline__ void scan_wave(const PrefillArgs& a, ScanSmem<OP, DK>
         for (int jt = 0; jt < TPW; ++jt)
             Ot[jt] = Ops::mma(Ub1, cur.p[jt][1], Ops::mma(Ub0, cur.p[jt][0], Y[jt]));
         pin();
-        ctx.load_p(cur, j + 2, pre);
+        ctx.load_p(cur, j + kStages, pre);
         pin();
         // O through the wave's staging area to row-wise stores; rows past the
         // end of the sequence fall outside the resource
-        {
-            const bool mine = j >= jb && j < je;
-            const int64_t ntl = mine ? s1 - t0 : 0;
-            const auto ro = make_rsrc(static_cast<OP*>(a.out) + ((size_t)(mine ? t0 : s0) * a.hv + h) * a.dv + blk * 16,
-                                      ntl > 0 ? (ntl - 1) * ctx.v_row + 16 * E : 0);
+        const bool mine = j >= q.jb && j < q.je;
+        const int64_t ntl = mine ? q.s1 - t0 : 0;
+        const auto ro = make_rsrc(static_cast<OP*>(a.out) + ((size_t)(mine ? t0 : q.s0) * a.hv + q.h) * a.dv + blk * 16,
+                                  ntl > 0 ? (ntl - 1) * ctx.v_row + 16 * E : 0);
 #pragma unroll
-            for (int jt = 0; jt < TPW; ++jt) {
-                quad oq;
+        for (int jt = 0; jt < TPW; ++jt) {
+            quad oq;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) oq[i] = from_f32<OP>(Ot[jt][i]);
-                *reinterpret_cast<quad*>(sm.ost[w][jt] + o_tl) = oq;
-            }
-            wave_lds_fence();
-#pragma unroll
-            for (int jt = 0; jt < TPW; ++jt)
-                B::store4(*reinterpret_cast<const quad*>(sm.ost[w][jt] + o_rw), ro, ctx.o_voff[jt]);
+            for (int i = 0; i < 4; ++i) oq[i] = from_f32<OP>(Ot[jt][i]);
+            *reinterpret_cast<quad*>(sm.ost[w][jt] + o_tl) = oq;
         }
+        wave_lds_fence();
+#pragma unroll
+        for (int jt = 0; jt < TPW; ++jt)
+            B::store4(*reinterpret_cast<const quad*>(sm.ost[w][jt] + o_rw), ro, ctx.o_voff[jt]);
     };
 
-    // Chunks are processed in pairs (stages A, B), starting two chunks early
-    // on zeroed stages, so that every load is issued inside the loop body and
-    // the memory-counter waits see the same load order on every path.  An
-    // empty chunk -- the two leading ones, and one trailing one for an odd
-    // count -- is an exact no-op: its operands are zeros (G2_last = 0, so
-    // gamma_last = 1, and U = 0 leaves S unchanged) and its stores are dropped.
-    St A{}, Bs{};
-    // Let the initial-state load land here, outside the loop: otherwise the
-    // loop head would have to wait for every load in flight on each pass.
+    St st[kStages] = {};
     __builtin_amdgcn_s_waitcnt(0);
-    for (int64_t j = jb - 2; j < je; j += 2) {
-        chunk(A, j);
-        chunk(Bs, j + 1);
-    }
-    if (a.state_out) {
-        *reinterpret_cast<f32x4*>(a.state_out + srow) = S[0];
-        *reinterpret_cast<f32x4*>(a.state_out + srow + 16) = S[1];
+    for (int64_t j = q.jb - kStages; j < q.je; j += kStages) {
+#pragma unroll
+        for (int i = 0; i < kStages; ++i) chunk(st[i], j + i);
     }
 }
 
 template <typename OP, int DK>
-__global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_kernel(PrefillArgs a, int xcd_map) {
+__global__ __launch_bounds__(2 * (DK / 32) * kWave) void gdn_scan_kernel(PrefillArgs a, int xcd_map) {
     __shared__ ScanSmem<OP, DK> sm;
     // Work item (chain, 16-column block).  With xcd_map, the 8 column blocks of
     // a chain get workgroup ids that the dispatcher sends to one XCD, so they
@@ -909,11 +964,23 @@ __global__ __launch_bounds__(DK / 32 * kWave) void gdn_scan_kernel(PrefillArgs a
             blk = L - chain * nblk;
         }
     }
+    // waves 0 .. NWS-1: state role; NWS .. 2 NWS - 1: output role
+    constexpr int NWS = DK / 32;
     switch (wave_id()) {
-        case 0: scan_wave<OP, DK, 0>(a, sm, chain, blk); break;
-        case 1: scan_wave<OP, DK, 1>(a, sm, chain, blk); break;
-        case 2: if constexpr (DK / 32 > 2) scan_wave<OP, DK, 2>(a, sm, chain, blk); break;
-        default: if constexpr (DK / 32 > 3) scan_wave<OP, DK, 3>(a, sm, chain, blk); break;
+        case 0: scan_state_wave<OP, DK, 0>(a, sm, chain, blk); break;
+        case 1: scan_state_wave<OP, DK, 1>(a, sm, chain, blk); break;
+        case 2:
+            if constexpr (NWS > 2) scan_state_wave<OP, DK, 2>(a, sm, chain, blk);
+            else scan_output_wave<OP, DK, 0>(a, sm, chain, blk);
+            break;
+        case 3:
+            if constexpr (NWS > 2) scan_state_wave<OP, DK, 3>(a, sm, chain, blk);
+            else scan_output_wave<OP, DK, 1>(a, sm, chain, blk);
+            break;
+        case 4: if constexpr (NWS > 2) scan_output_wave<OP, DK, 0>(a, sm, chain, blk); break;
+        case 5: if constexpr (NWS > 2) scan_output_wave<OP, DK, 1>(a, sm, chain, blk); break;
+        case 6: if constexpr (NWS > 2) scan_output_wave<OP, DK, 2>(a, sm, chain, blk); break;
+        default: if constexpr (NWS > 2) scan_output_wave<OP, DK, 3>(a, sm, chain, blk); break;
     }
 }
 
@@ -947,7 +1014,7 @@ hipError_t launch_scan(const PrefillArgs& a, hipStream_t st) {
     const int64_t chains = (int64_t)a.num_seqs * a.hv;
     const int nblk = a.dv / 16;
     const int xcd = (nblk == 8 && chains % 8 == 0) ? 1 : 0;
-    dim3 grid((unsigned)(chains * nblk)), block(DK / 32 * kWave);
+    dim3 grid((unsigned)(chains * nblk)), block(ScanGeom<OP, DK>::NT);
     hipLaunchKernelGGL((gdn_scan_kernel<OP, DK>), grid, block, 0, st, a, xcd);
     return hipGetLastError();
 }

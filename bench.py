@@ -83,7 +83,7 @@ def measured_traffic(name, sources):
 
 
 CALIB_BYTES = 1 << 30      # bytes read and bytes written by the calibration kernel
-KERNELS = {"gdn_prefill": ("gdn_prep_kernel", "gdn_scan_split_kernel"), "gdn_decode": ("gdn_decode_kernel",)}
+KERNELS = {"gdn_prefill": ("gdn_prep_kernel", "gdn_scan_kernel"), "gdn_decode": ("gdn_decode_kernel",)}
 
 
 def _pmc_per_dispatch(path, counter):
@@ -100,15 +100,21 @@ def _pmc_per_dispatch(path, counter):
     return out
 
 
-def write_traffic_summary(fetch_csv, write_csv):
+def write_traffic_summary(fetch_csv, write_csv, prefill_calls):
     """HBM bytes per call from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled
-    by what the same counter reads for the calibration kernel (1 GiB in, 1 GiB out)."""
+    by what the same counter reads for the calibration kernel (1 GiB in, 1 GiB out).
+    A prefill call may launch its kernels several times (segments): its bytes are the
+    counters summed over all dispatches divided by the number of calls profiled."""
     fetch = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE")
     write = _pmc_per_dispatch(write_csv, "WRITE_SIZE")
 
     def mean_of(table, pred):
         v = [val for name, val in table.values() if pred(name)]
         return (sum(v) / len(v) if v else None), len(v)
+
+    def per_call(table, pred, calls):
+        v = [val for name, val in table.values() if pred(name)]
+        return (sum(v) / calls if v else None), len(v)
 
     is_calib = lambda n: "neg_kernel" in n
     cf, _ = mean_of(fetch, is_calib)
@@ -121,9 +127,10 @@ def write_traffic_summary(fetch_csv, write_csv):
     for call, kernels in KERNELS.items():
         per = {}
         total = 0.0
+        agg = (lambda t, p: per_call(t, p, prefill_calls)) if call == "gdn_prefill" else mean_of
         for kn in kernels:
-            f, nf = mean_of(fetch, lambda n, kn=kn: kn in n)
-            w, nw = mean_of(write, lambda n, kn=kn: kn in n)
+            f, nf = agg(fetch, lambda n, kn=kn: kn in n)
+            w, nw = agg(write, lambda n, kn=kn: kn in n)
             if f is None or w is None:
                 break
             rb, wb = f * 1024 * sf, w * 1024 * sw
@@ -153,9 +160,11 @@ def main():
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a --calib-copy run into profiles/hbm_traffic.json")
+    ap.add_argument("--prefill-calls", type=int, default=3,
+                    help="with --traffic-summary: prefill calls in the profiled run (warmup + steps)")
     args = ap.parse_args()
     if args.traffic_summary:
-        write_traffic_summary(*args.traffic_summary)
+        write_traffic_summary(*args.traffic_summary, args.prefill_calls)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the GDN path here is single-GPU); got --gpus {args.gpus}",

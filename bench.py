@@ -83,7 +83,7 @@ def measured_traffic(name, sources):
 
 
 CALIB_BYTES = 1 << 30      # bytes read and bytes written by the calibration kernel
-KERNELS = {"gdn_prefill": ("gdn_prep_kernel", "gdn_scan_kernel"), "gdn_decode": ("gdn_decode_kernel",)}
+KERNELS = {"gdn_prefill": ("gdn_prep_kernel", "gdn_chunk_kernel", "gdn_link_kernel"), "gdn_decode": ("gdn_decode_kernel",)}
 
 
 def _pmc_per_dispatch(path, counter):

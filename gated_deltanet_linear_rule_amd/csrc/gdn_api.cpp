@@ -92,6 +92,23 @@ void keep_pool_memory(int dev) {
     done[dev] = true;
 }
 
+// Compute units of device `dev` (cached; 0 if the query fails).
+int compute_units(int dev) {
+    static std::mutex mu;
+    static int cached[64] = {};
+    if (dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lk(mu);
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return 0;
+        }
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -173,27 +190,32 @@ gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, con
     if (a.num_slots > INT32_MAX) return fail(GDN_ERROR_NOT_SUPPORTED, "too many chunks");
 
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const gdn::PrefillWorkspace wl(a.num_slots, a.hv, shape->head_dim_k, shape->head_dim_v, bf16 ? 2 : 4);
-    const int64_t seg = gdn::prefill_segment_chunks(a.num_tokens, a.num_seqs, a.hv, a.dv);
-    const int64_t state_bytes = seg > 0 ? (int64_t)a.num_seqs * a.hv * a.dv * shape->head_dim_k * 4 : 0;
-    const int64_t wbytes = wl.total + state_bytes;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(GDN_ERROR_LAUNCH, "hipGetDevice failed");
+    const int cus = compute_units(dev);
+    if (cus <= 0) return fail(GDN_ERROR_LAUNCH, "cannot query the device's compute units");
+    a.part_chunks = gdn::prefill_part_chunks(a.num_tokens, a.num_seqs, a.hv, cus);
+    const int64_t span = a.part_chunks * 64;
+    a.num_part_slots = (a.num_tokens + span - 1) / span + a.num_seqs;
+    const int64_t longest = cu_seqlens ? (a.num_tokens + 63) / 64 : (a.seqlen + 63) / 64;
+    const bool split = a.part_chunks < longest;
+    if (a.num_part_slots * a.hv > INT32_MAX || a.num_seqs * (int64_t)a.hv * (a.dv / 16) > INT32_MAX)
+        return fail(GDN_ERROR_NOT_SUPPORTED, "too many (part, head) pairs");
+    const gdn::PrefillWorkspace wl(a.num_slots, a.num_part_slots, split, a.hv, shape->head_dim_k, shape->head_dim_v,
+                                   bf16 ? 2 : 4);
     keep_pool_memory(dev);
     void* ws = nullptr;
-    if (hipMallocAsync(&ws, (size_t)wbytes, st) != hipSuccess || !ws) {
+    if (hipMallocAsync(&ws, (size_t)wl.total, st) != hipSuccess || !ws) {
         (void)hipGetLastError();
-        return fail(GDN_ERROR_OUT_OF_MEMORY, "prefill workspace of %lld bytes", (long long)wbytes);
+        return fail(GDN_ERROR_OUT_OF_MEMORY, "prefill workspace of %lld bytes", (long long)wl.total);
     }
     char* wc = static_cast<char*>(ws);
-    a.ws_w = wc + wl.w;
-    a.ws_q = wc + wl.q;
-    a.ws_k = wc + wl.k;
-    a.ws_u = wc + wl.u;
-    a.ws_p = wc + wl.p;
-    a.ws_g = reinterpret_cast<float*>(wc + wl.g);
-    float* state_ws = seg > 0 ? reinterpret_cast<float*>(wc + wl.total) : nullptr;
-    hipError_t e = gdn::launch_prefill(a, bf16, shape->head_dim_k, shape->head_dim_v, state_ws, st);
+    a.ws_t = wc + wl.t;
+    a.ws_g = reinterpret_cast<double*>(wc + wl.g);
+    a.ws_m = split ? reinterpret_cast<float*>(wc + wl.m) : nullptr;
+    a.ws_b = split ? reinterpret_cast<float*>(wc + wl.b) : nullptr;
+    a.ws_s = split ? reinterpret_cast<float*>(wc + wl.s) : nullptr;
+    hipError_t e = gdn::launch_prefill(a, bf16, shape->head_dim_k, shape->head_dim_v, st);
     hipError_t ef = hipFreeAsync(ws, st);
     if (e == hipSuccess) e = ef;
     if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(st);

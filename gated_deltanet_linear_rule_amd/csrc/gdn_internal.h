@@ -41,7 +41,8 @@ struct PrefillArgs {
     int64_t num_part_slots;    // part slots: ceil(num_tokens / (64 L)) + num_seqs
     // Workspace.  Per (chunk slot, value head), written by the prep kernel:
     void* ws_t;                // T~ = (I + A)^{-1} diag(beta) as 6 operand fragments
-    double* ws_g;              // 64 log2-scaled cumulative gates (fp64)
+    double* ws_g;              // 1 KB gate record: 64 log2-scaled cumulative gates (fp64),
+                               // then 64 gamma and 64 D (fp32)
     // Per (part slot, value head), fp32 row-major; NULL when no sequence has
     // more than one part:
     float* ws_m;               // d_k x d_k transition M_p of the part
@@ -58,7 +59,7 @@ struct PrefillWorkspace {
         const int64_t blocks = num_slots * hv, pblocks = split ? num_part_slots * hv : 0;
         t = 0;
         g = t + up(blocks * 6 * 64 * 8 * (int64_t)elem_size);
-        m = g + up(blocks * 64 * 8);
+        m = g + up(blocks * 1024);
         b = m + up(pblocks * dk * dk * 4);
         s = b + up(pblocks * dv * dk * 4);
         total = s + up(pblocks * dv * dk * 4);

@@ -54,6 +54,9 @@ namespace {
 constexpr int kPrepThreads = 256;
 constexpr int kTriFrags = 6;       // lower operand fragments of a 64 x 64 matrix
 constexpr int kLinkThreads = 256;
+// Gate record of one (chunk, value head): G2_t = log2-scaled cumulative gate
+// (fp64), then gamma_t = 2^{G2_t} and D_t = 2^{G2_63 - G2_t} (fp32).
+constexpr int kGateRecord = kChunk * 8 + 2 * kChunk * 4;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -235,9 +238,13 @@ __global__ __launch_bounds__(kPrepThreads, 2) void gdn_prep_kernel(PrefillArgs a
     if (w == 0) {
         if (l >= nt) { gc = 0.f; bc = 0.f; }
         const double G = wave_cumsum_f64((double)gc * 1.4426950408889634);
+        const double Gl = lane63_f64(G);
         sm.G[l] = G;
         sm.B[l] = bc;
-        ws_store(a.ws_g + blk * kChunk + l, G);
+        double* rec = a.ws_g + blk * (kGateRecord / 8);
+        ws_store(rec + l, G);
+        ws_store(reinterpret_cast<float*>(rec + kChunk) + l, fast_exp2((float)G));
+        ws_store(reinterpret_cast<float*>(rec + kChunk) + kChunk + l, fast_exp2((float)(Gl - G)));
     }
     __syncthreads();
 
@@ -402,112 +409,76 @@ __device__ __forceinline__ void lds_frag_half(OP* base, int f, int h, const type
     else *reinterpret_cast<quad*>(base + ((size_t)(2 * f + h) * 64 + l) * 4) = x;
 }
 
-template <typename OP, int DK, int DV, bool OUT>
-struct ChunkSmem {
-    static constexpr int QN = OUT ? kChunk * DK : 8;
-    static constexpr int PN = OUT ? kTriFrags * 64 * 8 : 8;
-    static constexpr int ON = OUT ? kChunk * DV : 8;
-    alignas(16) OP K[kChunk * DK];
-    alignas(16) OP V[kChunk * DV];
-    alignas(16) OP Q[QN];
-    alignas(16) OP T[kTriFrags * 64 * 8];   // T~ fragments
-    alignas(16) OP P[PN];                   // P^T tiles as B-operand fragments
-    alignas(16) OP O[ON];                   // output rows (row tile layout)
-    alignas(16) double G2[kChunk];
-    alignas(16) float gam[kChunk];          // e^{G_t}
-    alignas(16) float dec[kChunk];          // e^{G_last - G_t}
-    float gl;                               // e^{G_last}
-};
-
-// One chunk for one 16-row block of the state (rows R0 .. R0 + 15; value rows
-// when HAS_V, else rows of a transition, whose V is zero).  ST[db] holds the
-// block's S^T tile for d_k columns 16 db .. 16 db + 15: lane (n, gq) has
-// S[R0 + n][16 db + 4 gq + i].  Packed pairwise, these tiles are at once the
-// B operand of K S^T and the A operand of S Q^T.
-template <typename OP, int DK, int DV, bool OUT, bool HAS_V>
-__device__ __forceinline__ void chunk_rows(ChunkSmem<OP, DK, DV, OUT>& sm, f32x4 (&ST)[DK / 16], int R0) {
-    using Ops = Op<OP>;
-    using frag = typename Ops::frag;
-    using quad = typename Ops::quad;
-    constexpr int NDB = DK / 16, NKK = DK / 32;
-    const int l = lane_id(), n = l & 15, gq = l >> 4;
-
-    frag Sb[NKK];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) Sb[kk] = Ops::pack(ST[2 * kk], ST[2 * kk + 1]);
-
-    // Y = K S^T (tokens x rows)
-    f32x4 Y[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) acc = Ops::mma(rt_frag<OP, DK>(sm.K, 16 * tb + n, 32 * kk), Sb[kk], acc);
-        Y[tb] = acc;
-    }
-    // Z = S Q^T (rows x tokens), from the start state
-    f32x4 Z[4];
-    if constexpr (OUT) {
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) acc = Ops::mma(Sb[kk], rt_frag<OP, DK>(sm.Q, 16 * tb + n, 32 * kk), acc);
-            Z[tb] = acc;
-        }
-    }
-    // R = V - diag(gamma) Y
-    f32x4 R[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        const f32x4 g4 = *reinterpret_cast<const f32x4*>(&sm.gam[16 * tb + 4 * gq]);
-        f32x4 v = zero4();
-        if constexpr (HAS_V) v = quad_f32<OP>(rt_ctile<OP, DV>(sm.V, 16 * tb, R0));
-        R[tb] = v - g4 * Y[tb];
-    }
-    // U = T~ R (lower triangular T~)
-    const frag Rb0 = Ops::pack(R[0], R[1]), Rb1 = Ops::pack(R[2], R[3]);
-    f32x4 U[4];
-    U[0] = Ops::mma(lds_frag(sm.T, tri_frag(0, 0)), Rb0, zero4());
-    U[1] = Ops::mma(lds_frag(sm.T, tri_frag(1, 0)), Rb0, zero4());
-    U[2] = Ops::mma(lds_frag(sm.T, tri_frag(2, 1)), Rb1, Ops::mma(lds_frag(sm.T, tri_frag(2, 0)), Rb0, zero4()));
-    U[3] = Ops::mma(lds_frag(sm.T, tri_frag(3, 1)), Rb1, Ops::mma(lds_frag(sm.T, tri_frag(3, 0)), Rb0, zero4()));
-    // S^T <- gamma_last S^T + K^T diag(D) U
-    frag Ud[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sm.dec[32 * kk + 4 * gq]);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sm.dec[32 * kk + 16 + 4 * gq]);
-        Ud[kk] = Ops::pack(d0 * U[2 * kk], d1 * U[2 * kk + 1]);
-    }
-    const float gl = sm.gl;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-        f32x4 acc = gl * ST[db];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const frag kt = Ops::join(rt_ctile<OP, DK>(sm.K, 32 * kk, 16 * db), rt_ctile<OP, DK>(sm.K, 32 * kk + 16, 16 * db));
-            acc = Ops::mma(kt, Ud[kk], acc);
-        }
-        ST[db] = acc;
-    }
-    // O^T = diag(gamma) (S Q^T) + U^T P^T, staged as rows of O
-    if constexpr (OUT) {
-        const frag Ua0 = Ops::pack(U[0], U[1]), Ua1 = Ops::pack(U[2], U[3]);
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            f32x4 o = sm.gam[16 * tb + n] * Z[tb];
-            o = Ops::mma(Ua0, lds_frag(sm.P, tri_frag(tb, 0)), o);
-            if (tb >= 2) o = Ops::mma(Ua1, lds_frag(sm.P, tri_frag(tb, 1)), o);
-            quad oq;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) oq[i] = from_f32<OP>(o[i]);
-            *reinterpret_cast<quad*>(sm.O + rt_off<DV>(16 * tb + n, (R0 >> 2) + gq)) = oq;
-        }
-    }
+// Buffer resource over [base, base + bytes): reads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int nb = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nb, 0x00020000);
 }
 
-// Row block R0 .. R0 + 15 of a row-major (rows x DK) fp32 state, as S^T tiles.
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct loads into LDS (gfx950: lane l of the wave writes its 16 bytes to the
+// LDS address given plus 16 l; lanes whose range check fails write zeros).
+// Instruction i of a 64-row tile fills LDS bytes [1024 i, 1024 i + 1024) of the
+// row tile `dst` (rt_off layout): rows past the resource's end read as 0.
+template <typename OP, int D>
+__device__ __forceinline__ void rows_to_lds(OP* dst, __amdgpu_buffer_rsrc_t rs, unsigned rstride, int i) {
+    constexpr int RB = D * (int)sizeof(OP);           // bytes per row
+    constexpr int RPI = 1024 / RB;                    // rows per instruction
+    constexpr int UPR = RB / 16;                      // 16-byte units per row
+    constexpr int QPU = 4 / (int)sizeof(OP);          // 4-element quads per unit
+    const int l = lane_id();
+    const int r = i * RPI + l / UPR, p = l % UPR;
+    const int s = (((r & 7) << 2) | ((r >> 2) & 2)) & (D / 4 - 1);
+    const int u = p ^ (s / QPU);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + i * (1024 / (int)sizeof(OP))), 16,
+                                             (unsigned)r * rstride + (unsigned)u * 16, 0, 0, 0);
+}
+// Plain copy: instruction i fills LDS bytes [1024 i, 1024 i + 1024) from the same
+// bytes of the resource.
+__device__ __forceinline__ void bytes_to_lds(void* dst, __amdgpu_buffer_rsrc_t rs, int i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)((char*)dst + 1024 * i), 16,
+                                             (unsigned)(1024 * i + 16 * lane_id()), 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(0): this wave's loads (and stores) are complete.
+constexpr int kWaitVm0 = 0x0F70;
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses,
+// then s_barrier.  Unlike __syncthreads() it does not wait for direct-to-LDS
+// loads still in flight (those target the other buffer set).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// LDS executes one wave's operations in issue order, so exchanging data between
+// the lanes of one wave needs only that the compiler keeps this wave's LDS
+// accesses in program order across this point (a memory fence would also wait
+// for the direct-to-LDS loads in flight).
+__device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
+
+// One chunk's inputs in LDS.
+template <typename OP, int DK, int DV, bool OUT>
+struct ChunkBuf {
+    alignas(16) OP K[kChunk * DK];
+    alignas(16) OP V[kChunk * DV];
+    alignas(16) OP Q[OUT ? kChunk * DK : 8];
+    alignas(16) OP T[kTriFrags * 64 * 8];   // T~ fragments
+    alignas(16) double G2[kChunk];          // gate record: G2, gamma, D
+    alignas(16) float gam[kChunk];
+    alignas(16) float dec[kChunk];
+};
+
+// Geometry of the chunk kernels: one wave per 16 state rows (two waves per
+// SIMD, so one wave's LDS latency hides behind the other's matrix work).
+// Summary: value block w and transition block w per wave, so every K operand
+// read from LDS feeds two products.
+template <typename OP, int DK, int DV, bool OUT>
+struct ChunkGeom {
+    static constexpr int NR = OUT ? 1 : 2;
+    static constexpr int NW = OUT ? DV / 16 : (DV > DK ? DV : DK) / 16;
+    static constexpr int NT = NW * kWave;
+    static constexpr int NBUF = sizeof(OP) == 2 ? 2 : 1;   // fp32 rows do not fit twice
+};
+
+// Row block R0 .. R0 + 15 of a row-major (rows x DK) fp32 state, as S^T tiles:
+// tile db, lane (n, gq) holds S[R0 + n][16 db + 4 gq + i].
 template <int DK>
 __device__ __forceinline__ void load_state(const float* S, int R0, f32x4 (&ST)[DK / 16]) {
     const int l = lane_id(), n = l & 15, gq = l >> 4;
@@ -522,27 +493,157 @@ __device__ __forceinline__ void store_state(float* S, int R0, const f32x4 (&ST)[
     for (int db = 0; db < DK / 16; ++db) *reinterpret_cast<f32x4*>(S + (size_t)(R0 + n) * DK + 16 * db + 4 * gq) = ST[db];
 }
 
-// Threads of a chunk kernel: one wave per 16-row block (the summary kernel's
-// wave w also carries transition block w).
-template <int DK, int DV, bool OUT>
-constexpr int chunk_waves() { return OUT ? DV / 16 : (DV > DK ? DV : DK) / 16; }
+__device__ __forceinline__ f32x4 exp2_4(f32x4 x) {
+    return f32x4{fast_exp2(x[0]), fast_exp2(x[1]), fast_exp2(x[2]), fast_exp2(x[3])};
+}
+
+// One chunk for the wave's NR state blocks (rows R0[b] .. R0[b] + 15; block b
+// has a V term when bit b of VMASK is set, else it is a transition block whose
+// V is zero).  ST[b][db] holds block b's S^T tile for d_k columns 16 db ..:
+// lane (n, gq) has S[R0 + n][16 db + 4 gq + i].  Packed pairwise, these tiles
+// are at once the B operand of K S^T and the A operand of S Q^T.
+//   Y  = K S^T,  R = V - diag(gamma) Y,  U = T~ R
+//   S^T <- gamma_last S^T + K^T diag(D) U
+//   O^T = diag(gamma) (S Q^T) + U^T P^T     (OUT; after the barrier that
+//                                             publishes P)
+// OUT: the O^T tiles go to the row tile `ost` (rt_off layout, DV columns).
+template <typename OP, int DK, int DV, bool OUT, int NR, int VMASK>
+__device__ __forceinline__ void chunk_rows(const ChunkBuf<OP, DK, DV, OUT>& cb, const OP* P, OP* ost,
+                                           f32x4 (&ST)[NR][DK / 16], const int (&R0)[NR]) {
+    using Ops = Op<OP>;
+    using frag = typename Ops::frag;
+    using quad = typename Ops::quad;
+    constexpr int NDB = DK / 16, NKK = DK / 32;
+    const int l = lane_id(), n = l & 15, gq = l >> 4;
+
+    frag Sb[NR][NKK];
+#pragma unroll
+    for (int b = 0; b < NR; ++b)
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) Sb[b][kk] = Ops::pack(ST[b][2 * kk], ST[b][2 * kk + 1]);
+
+    // Y = K S^T (tokens x rows)
+    f32x4 Y[NR][4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+        for (int b = 0; b < NR; ++b) Y[b][tb] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const frag kf = rt_frag<OP, DK>(cb.K, 16 * tb + n, 32 * kk);
+#pragma unroll
+            for (int b = 0; b < NR; ++b) Y[b][tb] = Ops::mma(kf, Sb[b][kk], Y[b][tb]);
+        }
+    }
+    // R = V - diag(gamma) Y, packed pairwise as the B operand of T~ R
+    frag Rb[NR][2];
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) {
+        f32x4 r2[NR][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int tb = 2 * tp + h;
+            const f32x4 g4 = *reinterpret_cast<const f32x4*>(&cb.gam[16 * tb + 4 * gq]);
+#pragma unroll
+            for (int b = 0; b < NR; ++b) {
+                f32x4 v = zero4();
+                if ((VMASK >> b) & 1) v = quad_f32<OP>(rt_ctile<OP, DV>(cb.V, 16 * tb, R0[b]));
+                r2[b][h] = v - g4 * Y[b][tb];
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < NR; ++b) Rb[b][tp] = Ops::pack(r2[b][0], r2[b][1]);
+    }
+    // U = T~ R (T~ lower triangular: token tile tb needs K steps kk <= tb / 2)
+    f32x4 U[NR][4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        const frag t0 = lds_frag(cb.T, tri_frag(tb, 0));
+#pragma unroll
+        for (int b = 0; b < NR; ++b) U[b][tb] = Ops::mma(t0, Rb[b][0], zero4());
+        if (tb >= 2) {
+            const frag t1 = lds_frag(cb.T, tri_frag(tb, 1));
+#pragma unroll
+            for (int b = 0; b < NR; ++b) U[b][tb] = Ops::mma(t1, Rb[b][1], U[b][tb]);
+        }
+    }
+    // S^T <- gamma_last S^T + K^T diag(D) U
+    frag Ud[NR][2], Ua[NR][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&cb.dec[32 * kk + 4 * gq]);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(&cb.dec[32 * kk + 16 + 4 * gq]);
+#pragma unroll
+        for (int b = 0; b < NR; ++b) {
+            Ud[b][kk] = Ops::pack(d0 * U[b][2 * kk], d1 * U[b][2 * kk + 1]);
+            if constexpr (OUT) Ua[b][kk] = Ops::pack(U[b][2 * kk], U[b][2 * kk + 1]);
+        }
+    }
+    const float gl = cb.gam[kChunk - 1];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int b = 0; b < NR; ++b) ST[b][db] = gl * ST[b][db];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const frag kt = Ops::join(rt_ctile<OP, DK>(cb.K, 32 * kk, 16 * db), rt_ctile<OP, DK>(cb.K, 32 * kk + 16, 16 * db));
+#pragma unroll
+            for (int b = 0; b < NR; ++b) ST[b][db] = Ops::mma(kt, Ud[b][kk], ST[b][db]);
+        }
+    }
+    if constexpr (OUT) {
+        lds_barrier();   // P of this chunk is complete; the previous chunk's O rows are stored
+        // O^T tiles (rows x tokens): lane (n, gq) has O[16 tb + n][R0 + 4 gq + i]
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            f32x4 z[NR];
+#pragma unroll
+            for (int b = 0; b < NR; ++b) z[b] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const frag qf = rt_frag<OP, DK>(cb.Q, 16 * tb + n, 32 * kk);
+#pragma unroll
+                for (int b = 0; b < NR; ++b) z[b] = Ops::mma(Sb[b][kk], qf, z[b]);
+            }
+            const float gt = cb.gam[16 * tb + n];
+            const frag p0 = lds_frag(P, tri_frag(tb, 0));
+#pragma unroll
+            for (int b = 0; b < NR; ++b) z[b] = Ops::mma(Ua[b][0], p0, gt * z[b]);
+            if (tb >= 2) {
+                const frag p1 = lds_frag(P, tri_frag(tb, 1));
+#pragma unroll
+                for (int b = 0; b < NR; ++b) z[b] = Ops::mma(Ua[b][1], p1, z[b]);
+            }
+#pragma unroll
+            for (int b = 0; b < NR; ++b) {
+                quad oq;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) oq[i] = from_f32<OP>(z[b][i]);
+                *reinterpret_cast<quad*>(ost + rt_off<DV>(16 * tb + n, (R0[b] >> 2) + gq)) = oq;
+            }
+        }
+    }
+}
 
 // OUT = false: summary of parts p < np - 1 (B_p into ws_b, M_p into ws_m).
 // OUT = true: outputs of every part, from ws_s (np > 1) or init_state (np = 1);
 // the last part writes final_state.
 template <typename OP, int DK, int DV, bool OUT>
 __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) void gdn_chunk_kernel(PrefillArgs a) {
-    constexpr int NW = chunk_waves<DK, DV, OUT>();
-    constexpr int NT = NW * kWave;
-    constexpr int NVB = DV / 16, NMB = DK / 16;
-    constexpr int VE = Units<OP>::VE, FU = Units<OP>::FU;
-    constexpr int KU = kChunk * DK / VE, VU = kChunk * DV / VE, TU = kTriFrags * 64 * FU;
-    constexpr int KR = (KU + NT - 1) / NT, VR = (VU + NT - 1) / NT, TR = (TU + NT - 1) / NT;
-    constexpr int KPR = DK / VE, VPR = DV / VE;                 // 16-byte units per row
+    using G = ChunkGeom<OP, DK, DV, OUT>;
+    static_assert(G::NT == 64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16), "launch bound must equal the launch size");
+    using Buf = ChunkBuf<OP, DK, DV, OUT>;
     using quad = typename Op<OP>::quad;
-    __shared__ ChunkSmem<OP, DK, DV, OUT> sm;
+    constexpr int NR = G::NR, NW = G::NW, NBUF = G::NBUF;
+    constexpr int NVB = DV / 16, NMB = DK / 16, NDB = DK / 16;
+    constexpr int E = (int)sizeof(OP), FU = Units<OP>::FU;
+    constexpr int UK = kChunk * DK * E / 1024, UV = kChunk * DV * E / 1024, UT = kTriFrags * FU;
+    __shared__ Buf buf0;
+    __shared__ Buf buf1;
+    __shared__ OP Pf[OUT ? kTriFrags * 64 * 8 : 8];
+    __shared__ OP Ost[OUT ? kChunk * DV : 8];   // O rows of the previous chunk (rt_off layout)
 
-    const int tid = threadIdx.x, l = lane_id(), w = wave_id(), n = l & 15, gq = l >> 4;
+    const int l = lane_id(), w = wave_id(), n = l & 15, gq = l >> 4;
     const int64_t pslot = blockIdx.x / a.hv;
     const int h = (int)(blockIdx.x - pslot * a.hv);
     const SeqIndex si{a.cu, a.seqlen};
@@ -555,118 +656,96 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
     if (p < 0 || p >= (np > 1 ? np : 1)) return;               // gap slot
     const int64_t chain = (int64_t)seq * a.hv + h;
     const size_t sblk = (size_t)pslot * a.hv + h;
-    const int R0 = 16 * w;
+
+    // the wave's state blocks
+    int R0[NR];
+    if constexpr (OUT) {
+        R0[0] = 16 * w;
+    } else {
+        R0[0] = w < NVB ? 16 * w : 0;   // value block (discarded when w >= NVB)
+        R0[1] = w < NMB ? 16 * w : 0;   // transition block (discarded when w >= NMB)
+    }
+    f32x4 ST[NR][NDB];
 
     if constexpr (OUT) {
         if (nc == 0) {   // empty sequence: the state passes through
             if (a.final_state) {
-                f32x4 ST[DK / 16];
-                load_state<DK>(a.init_state ? a.init_state + chain * DV * DK : nullptr, R0, ST);
-                store_state<DK>(a.final_state + chain * DV * DK, R0, ST);
+#pragma unroll
+                for (int b = 0; b < NR; ++b) {
+                    load_state<DK>(a.init_state ? a.init_state + chain * DV * DK : nullptr, R0[b], ST[b]);
+                    store_state<DK>(a.final_state + chain * DV * DK, R0[b], ST[b]);
+                }
             }
             return;
         }
+        const float* Sin = np > 1 ? a.ws_s + sblk * DV * DK : (a.init_state ? a.init_state + chain * DV * DK : nullptr);
+#pragma unroll
+        for (int b = 0; b < NR; ++b) load_state<DK>(Sin, R0[b], ST[b]);
     } else {
         if (p >= np - 1) return;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            ST[0][db] = zero4();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ST[1][db][i] = (16 * db + 4 * gq + i == R0[1] + n) ? 1.f : 0.f;
+        }
     }
     const int64_t jb = p * L, je = (jb + L < nc) ? jb + L : nc;
     const int hq = (h * a.hqk) / a.hv;
     const int64_t cbase = span_base(s0, seq, kChunk);
+    const unsigned kstride = (unsigned)(a.hqk * DK * E), vstride = (unsigned)(a.hv * DV * E);
 
-    f32x4 ST0[DK / 16], ST1[DK / 16];
-    if constexpr (OUT) {
-        const float* Sin = np > 1 ? a.ws_s + sblk * DV * DK : (a.init_state ? a.init_state + chain * DV * DK : nullptr);
-        load_state<DK>(Sin, R0, ST0);
-    } else {
-#pragma unroll
-        for (int db = 0; db < DK / 16; ++db) {
-            ST0[db] = zero4();
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ST1[db][i] = (16 * db + 4 * gq + i == R0 + n) ? 1.f : 0.f;
-        }
-    }
-
-    const OP* kg = static_cast<const OP*>(a.k);
-    const OP* qg = static_cast<const OP*>(a.q);
-    const OP* vg = static_cast<const OP*>(a.v);
-    const OP* tg = static_cast<const OP*>(a.ws_t);
-    u32x4 kr[KR], qr[OUT ? KR : 1], vr[VR], tr[TR];
-    double g2r = 0.0;
-    // Global inputs of chunk j into registers (rows past the end clamped; they
-    // are zeroed when staged).
-    auto fetch = [&](int64_t j) {
+    // Direct loads of chunk j's rows, T~ and gates into `B` (spread over the waves).
+    auto issue = [&](int64_t j, Buf& B) {
         const int64_t t0 = s0 + j * kChunk;
-        const int nt = (int)((len - j * kChunk) < kChunk ? (len - j * kChunk) : kChunk);
+        const int64_t nt = (len - j * kChunk) < kChunk ? (len - j * kChunk) : kChunk;
         const size_t cblk = (size_t)(cbase + j) * a.hv + h;
+        const size_t krow = ((size_t)t0 * a.hqk + hq) * DK;
+        const auto rk = make_rsrc(static_cast<const OP*>(a.k) + krow, (nt - 1) * kstride + DK * E);
+        const auto rv = make_rsrc(static_cast<const OP*>(a.v) + ((size_t)t0 * a.hv + h) * DV, (nt - 1) * vstride + DV * E);
+        const auto rt = make_rsrc(static_cast<const OP*>(a.ws_t) + cblk * (kTriFrags * 64 * 8), UT * 1024);
+        const auto rg = make_rsrc(a.ws_g + cblk * (kGateRecord / 8), kGateRecord);
 #pragma unroll
-        for (int i = 0; i < KR; ++i) {
-            const int e = tid + i * NT;
-            if (KR * NT == KU || e < KU) {
-                const int row = e / KPR, u = e - row * KPR;
-                const int rc = row < nt ? row : nt - 1;
-                const size_t off = ((size_t)(t0 + rc) * a.hqk + hq) * DK + (size_t)u * VE;
-                kr[i] = ld16(kg + off);
-                if constexpr (OUT) qr[i] = ld16(qg + off);
-            }
-        }
+        for (int k = 0; k < (UK + NW - 1) / NW; ++k)
+            if (UK % NW == 0 || w + NW * k < UK) rows_to_lds<OP, DK>(B.K, rk, kstride, w + NW * k);
+        if constexpr (OUT) {
+            const auto rq = make_rsrc(static_cast<const OP*>(a.q) + krow, (nt - 1) * kstride + DK * E);
 #pragma unroll
-        for (int i = 0; i < VR; ++i) {
-            const int e = tid + i * NT;
-            if (VR * NT == VU || e < VU) {
-                const int row = e / VPR, u = e - row * VPR;
-                const int rc = row < nt ? row : nt - 1;
-                vr[i] = ld16(vg + ((size_t)(t0 + rc) * a.hv + h) * DV + (size_t)u * VE);
-            }
+            for (int k = 0; k < (UK + NW - 1) / NW; ++k)
+                if (UK % NW == 0 || w + NW * k < UK) rows_to_lds<OP, DK>(B.Q, rq, kstride, w + NW * k);
         }
 #pragma unroll
-        for (int i = 0; i < TR; ++i) {
-            const int e = tid + i * NT;
-            if (TR * NT == TU || e < TU) tr[i] = ld16(tg + cblk * (kTriFrags * 64 * 8) + (size_t)e * VE);
-        }
-        if (w == 0) g2r = a.ws_g[cblk * kChunk + l];
-    };
-    auto stage = [&](int nt) {
+        for (int k = 0; k < (UV + NW - 1) / NW; ++k)
+            if (UV % NW == 0 || w + NW * k < UV) rows_to_lds<OP, DV>(B.V, rv, vstride, w + NW * k);
 #pragma unroll
-        for (int i = 0; i < KR; ++i) {
-            const int e = tid + i * NT;
-            if (KR * NT == KU || e < KU) {
-                const int row = e / KPR, u = e - row * KPR;
-                const int o = rt_off<DK>(row, u * VE / 4);
-                *reinterpret_cast<u32x4*>(sm.K + o) = row < nt ? kr[i] : zero_u4();
-                if constexpr (OUT) *reinterpret_cast<u32x4*>(sm.Q + o) = row < nt ? qr[i] : zero_u4();
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < VR; ++i) {
-            const int e = tid + i * NT;
-            if (VR * NT == VU || e < VU) {
-                const int row = e / VPR, u = e - row * VPR;
-                *reinterpret_cast<u32x4*>(sm.V + rt_off<DV>(row, u * VE / 4)) = row < nt ? vr[i] : zero_u4();
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < TR; ++i) {
-            const int e = tid + i * NT;
-            if (TR * NT == TU || e < TU) *reinterpret_cast<u32x4*>(sm.T + (size_t)e * VE) = tr[i];
-        }
-        if (w == 0) {
-            const double last = lane63_f64(g2r);
-            sm.G2[l] = g2r;
-            sm.gam[l] = fast_exp2((float)g2r);
-            sm.dec[l] = fast_exp2((float)(last - g2r));
-            if (l == 0) sm.gl = fast_exp2((float)last);
-        }
+        for (int k = 0; k < (UT + NW - 1) / NW; ++k)
+            if (UT % NW == 0 || w + NW * k < UT) bytes_to_lds(B.T, rt, w + NW * k);
+        if (w == NW - 1) bytes_to_lds(B.G2, rg, 0);   // gate record: exactly 1 KB
     };
 
+    // O rows of chunk j, staged in Ost, to global memory (rows past the end dropped)
     OP* const og = static_cast<OP*>(a.out);
-    fetch(jb);
-    for (int64_t j = jb; j < je; ++j) {
-        const int nt = (int)((len - j * kChunk) < kChunk ? (len - j * kChunk) : kChunk);
-        __syncthreads();   // the previous chunk is done with LDS
-        stage(nt);
-        fetch(j + 1 < je ? j + 1 : j);
-        __syncthreads();
+    auto store_o = [&](int64_t j) {
+        constexpr int VU = kChunk * DV * E / 16, UPR = DV * E / 16, VE = 16 / E;
+        const int64_t nt = (len - j * kChunk) < kChunk ? (len - j * kChunk) : kChunk;
+        const auto ro = make_rsrc(og + ((size_t)(s0 + j * kChunk) * a.hv + h) * DV, (nt - 1) * vstride + DV * E);
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int k = 0; k < (VU + G::NT - 1) / G::NT; ++k) {
+            const int e = tid + k * G::NT;
+            if (VU % G::NT == 0 || e < VU) {
+                const int row = e / UPR, u = e - row * UPR;
+                const u32x4 x = *reinterpret_cast<const u32x4*>(Ost + rt_off<DV>(row, u * VE / 4));
+                __builtin_amdgcn_raw_buffer_store_b128(x, ro, (unsigned)row * vstride + (unsigned)u * 16, 0, 0);
+            }
+        }
+    };
+    auto body = [&](int64_t j, const Buf& cur, Buf& nxt) {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's loads of chunk j have landed
+        lds_barrier();                          // everyone's have; the previous chunk is done everywhere
+        if (NBUF == 2 && j + 1 < je) issue(j + 1, nxt);
         if constexpr (OUT) {
+            if (j > jb) store_o(j - 1);
             // P^T tiles: P[t][s] = Gamma_ts q_t . k_s for s <= t, as B-operand
             // fragments (tile e: fragment e / 2, K slots 4 (e & 1) ..)
             for (int e = w; e < 2 * kTriFrags; e += NW) {
@@ -682,38 +761,44 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
                     f32x4 acc = zero4();
 #pragma unroll
                     for (int kk = 0; kk < DK / 32; ++kk)
-                        acc = Op<OP>::mma(rt_frag<OP, DK>(sm.K, 16 * sb + n, 32 * kk), rt_frag<OP, DK>(sm.Q, 16 * tb + n, 32 * kk), acc);
+                        acc = Op<OP>::mma(rt_frag<OP, DK>(cur.K, 16 * sb + n, 32 * kk), rt_frag<OP, DK>(cur.Q, 16 * tb + n, 32 * kk), acc);
                     const int t = 16 * tb + n;
-                    const double gt = sm.G2[t];
+                    const double gt = cur.G2[t];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int s = 16 * sb + 4 * gq + i;
-                        pq[i] = from_f32<OP>(s <= t ? fast_exp2((float)(gt - sm.G2[s])) * acc[i] : 0.f);
+                        pq[i] = from_f32<OP>(s <= t ? fast_exp2((float)(gt - cur.G2[s])) * acc[i] : 0.f);
                     }
                 }
-                lds_frag_half(sm.P, f, half, pq);
+                lds_frag_half(Pf, f, half, pq);
             }
-            __syncthreads();
-            chunk_rows<OP, DK, DV, OUT, true>(sm, ST0, R0);
-            __syncthreads();
-            const int64_t t0 = s0 + j * kChunk;
-            for (int e = tid; e < VU; e += NT) {
-                const int row = e / VPR, u = e - row * VPR;
-                if (row < nt)
-                    *reinterpret_cast<u32x4*>(og + ((size_t)(t0 + row) * a.hv + h) * DV + (size_t)u * VE) =
-                        *reinterpret_cast<const u32x4*>(sm.O + rt_off<DV>(row, u * VE / 4));
-            }
+            chunk_rows<OP, DK, DV, OUT, NR, 1>(cur, Pf, Ost, ST, R0);
         } else {
-            if (w < NVB) chunk_rows<OP, DK, DV, OUT, true>(sm, ST0, R0);
-            if (w < NMB) chunk_rows<OP, DK, DV, OUT, false>(sm, ST1, R0);
+            chunk_rows<OP, DK, DV, OUT, NR, 1>(cur, nullptr, nullptr, ST, R0);
         }
+        if (NBUF == 1 && j + 1 < je) {
+            lds_barrier();                      // everyone is done with this chunk's rows
+            issue(j + 1, nxt);
+        }
+    };
+
+    issue(jb, buf0);
+    for (int64_t j = jb; j < je; j += NBUF) {
+        body(j, buf0, NBUF == 2 ? buf1 : buf0);
+        if (NBUF == 2 && j + 1 < je) body(j + 1, buf1, buf0);
+    }
+    if constexpr (OUT) {
+        lds_barrier();
+        store_o(je - 1);
     }
 
     if constexpr (OUT) {
-        if (p == np - 1 && a.final_state) store_state<DK>(a.final_state + chain * DV * DK, R0, ST0);
+        if (p == np - 1 && a.final_state)
+#pragma unroll
+            for (int b = 0; b < NR; ++b) store_state<DK>(a.final_state + chain * DV * DK, R0[b], ST[b]);
     } else {
-        if (w < NVB) store_state<DK>(a.ws_b + sblk * DV * DK, R0, ST0);
-        if (w < NMB) store_state<DK>(a.ws_m + sblk * DK * DK, R0, ST1);
+        if (w < NVB) store_state<DK>(a.ws_b + sblk * DV * DK, R0[0], ST[0]);
+        if (w < NMB) store_state<DK>(a.ws_m + sblk * DK * DK, R0[1], ST[1]);
     }
 }
 
@@ -820,14 +905,14 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     const unsigned parts = (unsigned)(a.num_part_slots * a.hv);
     if (a.ws_m) {
-        hipLaunchKernelGGL((gdn_chunk_kernel<OP, DK, DV, false>), dim3(parts), dim3(64 * chunk_waves<DK, DV, false>()),
+        hipLaunchKernelGGL((gdn_chunk_kernel<OP, DK, DV, false>), dim3(parts), dim3(ChunkGeom<OP, DK, DV, false>::NT),
                            0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const unsigned links = (unsigned)((int64_t)a.num_seqs * a.hv * (DV / 16));
         hipLaunchKernelGGL((gdn_link_kernel<DK, DV>), dim3(links), dim3(kLinkThreads), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((gdn_chunk_kernel<OP, DK, DV, true>), dim3(parts), dim3(64 * chunk_waves<DK, DV, true>()), 0,
+    hipLaunchKernelGGL((gdn_chunk_kernel<OP, DK, DV, true>), dim3(parts), dim3(ChunkGeom<OP, DK, DV, true>::NT), 0,
                        st, a);
     return hipGetLastError();
 }

@@ -333,53 +333,81 @@ __global__ __launch_bounds__(kPrepThreads, 2) void gdn_prep_kernel(PrefillArgs a
 // ===========================================================================
 // chunk kernels: one workgroup per (part, value head)
 // ===========================================================================
-// LDS row tiles: 64 rows x D elements, row-major, with the 4-element quads of
-// row r permuted by XOR with swz(r) (even, so the two quads of a 16-byte unit
-// of bf16 stay adjacent).  With it, the three access patterns used here are
-// free of bank conflicts for D = 128:
-//   * 16-byte row stores (one row per 16 lanes),
-//   * operand fragments (lane (r, gq): quads k0/4 + gq and k0/4 + 4 + gq of row r),
-//   * the LDS transpose read of a 16 x 16 tile (lane L: quad L & 3 of row L / 4).
-template <int D>
-__device__ __forceinline__ int rt_off(int row, int quad) {
-    constexpr int NQ = D / 4;
-    const int s = (((row & 7) << 2) | ((row >> 2) & 2)) & (NQ - 1);
-    return row * D + ((quad ^ s) << 2);
-}
+// LDS row tiles: 64 rows x D elements, row-major, with the 16-byte units of row
+// r permuted by XOR with swz(r).  With it the access patterns used here are
+// free of bank conflicts for D = 128 bf16 (measured on gfx950):
+//   * 16-byte row stores (the direct loads: one row per 16 lanes),
+//   * operand fragments: lane (r, gq) reads unit k0 / 8 + gq of row r, one
+//     16-byte read (16-byte reads move twice the bytes per clock of 8-byte ones),
+//   * the LDS transpose read of a 16 x 16 tile (lane L: row L / 4).
+template <typename OP, int D>
+struct RowTile {
+    static constexpr int VE = 16 / (int)sizeof(OP);    // elements per unit
+    static constexpr int UPR = D / VE;                  // units per row
+    __device__ __forceinline__ static int swz(int r) { return (((r << 1) | ((r >> 3) & 1)) & 15) & (UPR - 1); }
+    __device__ __forceinline__ static int unit(int r, int u) { return r * D + (u ^ swz(r)) * VE; }
+    __device__ __forceinline__ static int elem(int r, int c) { return unit(r, c / VE) + c % VE; }
+};
 
-// Operand fragment of row `row`, 32-wide K step from column k0, paired order.
+// Operand fragment of row `row`, 32-wide K step from column k0, natural order:
+// lane (r, gq) holds columns k0 + 8 gq .. k0 + 8 gq + 7.
 template <typename OP, int D>
 __device__ __forceinline__ typename Op<OP>::frag rt_frag(const OP* t, int row, int k0) {
-    using quad = typename Op<OP>::quad;
+    using RT = RowTile<OP, D>;
     const int gq = lane_id() >> 4;
-    const quad lo = *reinterpret_cast<const quad*>(t + rt_off<D>(row, (k0 >> 2) + gq));
-    const quad hi = *reinterpret_cast<const quad*>(t + rt_off<D>(row, (k0 >> 2) + 4 + gq));
-    return Op<OP>::join(lo, hi);
+    if constexpr (sizeof(OP) == 2) {
+        return *reinterpret_cast<const bf16x8*>(t + RT::unit(row, (k0 >> 3) + gq));
+    } else {
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(t + RT::unit(row, (k0 >> 2) + 2 * gq));
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(t + RT::unit(row, (k0 >> 2) + 2 * gq + 1));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) __bf16 lds_bf16;
 
-// The 16 x 16 tile at (row0, col0) in accumulator layout: lane (n, gq) gets
-// M[row0 + 4 gq + i][col0 + n], i = 0..3.  bf16: one LDS transpose read, for
-// which lane L supplies the 8 bytes at row row0 + L / 4, columns
-// col0 + 4 (L & 3) .. + 3 (gfx950 delivers element b of lane 16 G + 4 j + a's
-// read to lane 16 G + 4 a + b as its element j).  fp32: four scalar reads.
+// A 16 x 16 tile in accumulator layout: rows row0 .. row0 + 15, and the 16
+// columns col0 + cs a + c (a, c = 0..3; cs = 4 for a contiguous tile); lane
+// (n, gq) gets M[row0 + 4 gq + i][col0 + cs (n / 4) + n % 4], i = 0..3.
+// bf16: one LDS transpose read, for which lane L supplies the 8 bytes at row
+// row0 + L / 4, columns col0 + cs (L & 3) .. + 3 (gfx950 delivers element b of
+// lane 16 G + 4 j + a's read to lane 16 G + 4 a + b as its element j).
+// fp32: four scalar reads.
 template <typename OP, int D>
-__device__ __forceinline__ typename Op<OP>::quad rt_ctile(const OP* t, int row0, int col0) {
+__device__ __forceinline__ typename Op<OP>::quad rt_ctile(const OP* t, int row0, int col0, int cs = 4) {
+    using RT = RowTile<OP, D>;
     const int l = lane_id();
     if constexpr (sizeof(OP) == 2) {
-        const OP* p = t + rt_off<D>(row0 + (l >> 2), (col0 >> 2) + (l & 3));
+        const OP* p = t + RT::elem(row0 + (l >> 2), col0 + cs * (l & 3));
         lds_s16x4* lp = (lds_s16x4*)((lds_bf16*)const_cast<OP*>(p));
         return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp));
     } else {
-        const int n = l & 15, gq = l >> 4, c = col0 + n;
+        const int n = l & 15, gq = l >> 4, c = col0 + cs * (n >> 2) + (n & 3);
         f32x4 x;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = t[rt_off<D>(row0 + 4 * gq + i, c >> 2) + (c & 3)];
+        for (int i = 0; i < 4; ++i) x[i] = t[RT::elem(row0 + 4 * gq + i, c)];
         return x;
     }
+}
+
+// The state's d_k columns are kept in a permuted order, so that a pair of
+// state tiles is an operand fragment of eight consecutive d_k columns (one
+// 16-byte LDS read of K or Q for the other operand).  Row rho of state tile
+// db is d_k column pi_dk(db, rho); tiles 2 kk and 2 kk + 1 together cover the
+// columns 32 kk .. 32 kk + 31.
+__device__ __forceinline__ int pi_dk(int db, int rho) {
+    return 32 * (db >> 1) + 8 * (rho >> 2) + 4 * (db & 1) + (rho & 3);
+}
+
+// K^T operand of the state update for state tile db and token half kk: lane
+// (r, gq) holds K[32 kk + 4 gq + i][pi_dk(db, r)] and
+// K[32 kk + 16 + 4 gq + i][pi_dk(db, r)], i = 0..3.
+template <typename OP, int DK>
+__device__ __forceinline__ typename Op<OP>::frag kt_frag(const OP* K, int db, int kk) {
+    const int c0 = 32 * (db >> 1) + 4 * (db & 1);
+    return Op<OP>::join(rt_ctile<OP, DK>(K, 32 * kk, c0, 8), rt_ctile<OP, DK>(K, 32 * kk + 16, c0, 8));
 }
 
 template <typename OP>
@@ -420,17 +448,15 @@ typedef __attribute__((address_space(3))) void lds_void;
 // Direct loads into LDS (gfx950: lane l of the wave writes its 16 bytes to the
 // LDS address given plus 16 l; lanes whose range check fails write zeros).
 // Instruction i of a 64-row tile fills LDS bytes [1024 i, 1024 i + 1024) of the
-// row tile `dst` (rt_off layout): rows past the resource's end read as 0.
+// row tile `dst` (RowTile layout): rows past the resource's end read as 0.
 template <typename OP, int D>
 __device__ __forceinline__ void rows_to_lds(OP* dst, __amdgpu_buffer_rsrc_t rs, unsigned rstride, int i) {
     constexpr int RB = D * (int)sizeof(OP);           // bytes per row
     constexpr int RPI = 1024 / RB;                    // rows per instruction
     constexpr int UPR = RB / 16;                      // 16-byte units per row
-    constexpr int QPU = 4 / (int)sizeof(OP);          // 4-element quads per unit
     const int l = lane_id();
     const int r = i * RPI + l / UPR, p = l % UPR;
-    const int s = (((r & 7) << 2) | ((r >> 2) & 2)) & (D / 4 - 1);
-    const int u = p ^ (s / QPU);
+    const int u = p ^ RowTile<OP, D>::swz(r);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + i * (1024 / (int)sizeof(OP))), 16,
                                              (unsigned)r * rstride + (unsigned)u * 16, 0, 0, 0);
 }
@@ -447,11 +473,6 @@ constexpr int kWaitVm0 = 0x0F70;
 // then s_barrier.  Unlike __syncthreads() it does not wait for direct-to-LDS
 // loads still in flight (those target the other buffer set).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// LDS executes one wave's operations in issue order, so exchanging data between
-// the lanes of one wave needs only that the compiler keeps this wave's LDS
-// accesses in program order across this point (a memory fence would also wait
-// for the direct-to-LDS loads in flight).
-__device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
 
 // One chunk's inputs in LDS.
 template <typename OP, int DK, int DV, bool OUT>
@@ -471,155 +492,270 @@ struct ChunkBuf {
 // read from LDS feeds two products.
 template <typename OP, int DK, int DV, bool OUT>
 struct ChunkGeom {
-    static constexpr int NR = OUT ? 1 : 2;
-    static constexpr int NW = OUT ? DV / 16 : (DV > DK ? DV : DK) / 16;
+    static constexpr int NR = 2;
+    static constexpr int NW = OUT ? DV / 32 : (DV > DK ? DV : DK) / 16;
     static constexpr int NT = NW * kWave;
     static constexpr int NBUF = sizeof(OP) == 2 ? 2 : 1;   // fp32 rows do not fit twice
 };
 
 // Row block R0 .. R0 + 15 of a row-major (rows x DK) fp32 state, as S^T tiles:
-// tile db, lane (n, gq) holds S[R0 + n][16 db + 4 gq + i].
+// tile db, lane (n, gq) holds S[R0 + n][pi_dk(db, 4 gq + i)] (four consecutive
+// columns).
 template <int DK>
 __device__ __forceinline__ void load_state(const float* S, int R0, f32x4 (&ST)[DK / 16]) {
     const int l = lane_id(), n = l & 15, gq = l >> 4;
 #pragma unroll
     for (int db = 0; db < DK / 16; ++db)
-        ST[db] = S ? *reinterpret_cast<const f32x4*>(S + (size_t)(R0 + n) * DK + 16 * db + 4 * gq) : zero4();
+        ST[db] = S ? *reinterpret_cast<const f32x4*>(S + (size_t)(R0 + n) * DK + pi_dk(db, 4 * gq)) : zero4();
 }
 template <int DK>
 __device__ __forceinline__ void store_state(float* S, int R0, const f32x4 (&ST)[DK / 16]) {
     const int l = lane_id(), n = l & 15, gq = l >> 4;
 #pragma unroll
-    for (int db = 0; db < DK / 16; ++db) *reinterpret_cast<f32x4*>(S + (size_t)(R0 + n) * DK + 16 * db + 4 * gq) = ST[db];
+    for (int db = 0; db < DK / 16; ++db) *reinterpret_cast<f32x4*>(S + (size_t)(R0 + n) * DK + pi_dk(db, 4 * gq)) = ST[db];
 }
 
-__device__ __forceinline__ f32x4 exp2_4(f32x4 x) {
-    return f32x4{fast_exp2(x[0]), fast_exp2(x[1]), fast_exp2(x[2]), fast_exp2(x[3])};
-}
+
+// Keeps the compiler's scheduler from moving instructions across this point,
+// so that each group of LDS reads is issued ahead of the products that use the
+// previous group (the reads are then in flight while the matrix cores work).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // One chunk for the wave's NR state blocks (rows R0[b] .. R0[b] + 15; block b
 // has a V term when bit b of VMASK is set, else it is a transition block whose
-// V is zero).  ST[b][db] holds block b's S^T tile for d_k columns 16 db ..:
-// lane (n, gq) has S[R0 + n][16 db + 4 gq + i].  Packed pairwise, these tiles
-// are at once the B operand of K S^T and the A operand of S Q^T.
+// V is zero).  ST[b][db] holds block b's S^T tile for d_k columns
+// pi_dk(db, .): lane (n, gq) has S[R0 + n][pi_dk(db, 4 gq + i)].  Packed
+// pairwise, these tiles are at once the B operand of K S^T and the A operand
+// of S Q^T.
 //   Y  = K S^T,  R = V - diag(gamma) Y,  U = T~ R
 //   S^T <- gamma_last S^T + K^T diag(D) U
-//   O^T = diag(gamma) (S Q^T) + U^T P^T     (OUT; after the barrier that
-//                                             publishes P)
-// OUT: the O^T tiles go to the row tile `ost` (rt_off layout, DV columns).
-template <typename OP, int DK, int DV, bool OUT, int NR, int VMASK>
-__device__ __forceinline__ void chunk_rows(const ChunkBuf<OP, DK, DV, OUT>& cb, const OP* P, OP* ost,
-                                           f32x4 (&ST)[NR][DK / 16], const int (&R0)[NR]) {
+//   O^T = diag(gamma) (S Q^T) + U^T P^T                          (OUT)
+// Before the barrier in the middle, the wave also writes its share of the
+// chunk's K^T operand fragments (bf16) and P^T tiles (OUT); after it, it reads
+// all of them.  OUT: the O^T tiles go to the row tile `ost` (RowTile layout).
+template <typename OP, int DK, int DV, bool OUT, int NR, int VMASK, int NW>
+__device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, OP* P, OP* kt, OP* ost,
+                                           f32x4 (&ST)[NR][DK / 16], const int (&R0)[NR], int w) {
     using Ops = Op<OP>;
     using frag = typename Ops::frag;
     using quad = typename Ops::quad;
     constexpr int NDB = DK / 16, NKK = DK / 32;
+    constexpr bool KT = sizeof(OP) == 2;
+    constexpr int KTF = 2 * NDB;                                // K^T fragments of the chunk
+    constexpr int PT = OUT ? (2 * kTriFrags + NW - 1) / NW : 0;  // P^T tiles per wave
     const int l = lane_id(), n = l & 15, gq = l >> 4;
 
+    // ---- state-free work of the chunk: P^T tiles and K^T fragments.  P[t][s] =
+    // Gamma_ts q_t . k_s for s <= t, as B-operand fragments (tile e: fragment
+    // e / 2, K slots 4 (e & 1) ..); every wave does PT tiles without branches,
+    // tiles past the last repeat tile 0 into a scratch fragment.
+    if constexpr (OUT) {
+        frag pk[PT > 0 ? PT : 1][NKK], pq[PT > 0 ? PT : 1][NKK];
+        int pf[PT > 0 ? PT : 1], ph[PT > 0 ? PT : 1], ptb[PT > 0 ? PT : 1], psb[PT > 0 ? PT : 1];
+#pragma unroll
+        for (int r = 0; r < PT; ++r) {
+            const int e = w + NW * r;
+            const bool real = e < 2 * kTriFrags;
+            const int ee = real ? e : 0;
+            int kk2;
+            tri_frag_pos(ee >> 1, ptb[r], kk2);
+            ph[r] = ee & 1;
+            psb[r] = 2 * kk2 + ph[r];
+            pf[r] = real ? (ee >> 1) : kTriFrags;
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                pk[r][kk] = rt_frag<OP, DK>(cb.K, 16 * psb[r] + n, 32 * kk);
+                pq[r][kk] = rt_frag<OP, DK>(cb.Q, 16 * ptb[r] + n, 32 * kk);
+            }
+        }
+        sched_fence();
+#pragma unroll
+        for (int r = 0; r < PT; ++r) {
+            const int t = 16 * ptb[r] + n;
+            const double gt = cb.G2[t];
+            double gs[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gs[i] = cb.G2[16 * psb[r] + 4 * gq + i];
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) acc = Ops::mma(pk[r][kk], pq[r][kk], acc);
+            quad pv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x = fast_exp2((float)(gt - gs[i])) * acc[i];
+                pv[i] = from_f32<OP>(16 * psb[r] + 4 * gq + i <= t ? x : 0.f);
+            }
+            lds_frag_half(P, pf[r], ph[r], pv);
+        }
+        sched_fence();
+    }
+    if constexpr (KT) {
+#pragma unroll
+        for (int r = 0; r < (KTF + NW - 1) / NW; ++r) {
+            const int f = w + NW * r;
+            if (KTF % NW == 0 || f < KTF)
+                *reinterpret_cast<bf16x8*>(kt + ((size_t)f * 64 + l) * 8) = kt_frag<OP, DK>(cb.K, f >> 1, f & 1);
+        }
+        sched_fence();
+    }
+
+    // ---- Y = K S^T and Z = S Q^T; operands stream in groups of two token tiles
     frag Sb[NR][NKK];
 #pragma unroll
     for (int b = 0; b < NR; ++b)
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) Sb[b][kk] = Ops::pack(ST[b][2 * kk], ST[b][2 * kk + 1]);
-
-    // Y = K S^T (tokens x rows)
-    f32x4 Y[NR][4];
+    f32x4 Y[NR][4], Z[NR][4];
+    frag g0[2][NKK], g1[2][NKK];
+    auto load2 = [&](frag (&g)[2][NKK], const OP* M, int tb0) {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int b = 0; b < NR; ++b) Y[b][tb] = zero4();
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const frag kf = rt_frag<OP, DK>(cb.K, 16 * tb + n, 32 * kk);
-#pragma unroll
-            for (int b = 0; b < NR; ++b) Y[b][tb] = Ops::mma(kf, Sb[b][kk], Y[b][tb]);
-        }
-    }
-    // R = V - diag(gamma) Y, packed pairwise as the B operand of T~ R
-    frag Rb[NR][2];
-#pragma unroll
-    for (int tp = 0; tp < 2; ++tp) {
-        f32x4 r2[NR][2];
+            for (int kk = 0; kk < NKK; ++kk) g[h][kk] = rt_frag<OP, DK>(M, 16 * (tb0 + h) + n, 32 * kk);
+    };
+    auto mmY = [&](const frag (&g)[2][NKK], int tb0) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int tb = 2 * tp + h;
-            const f32x4 g4 = *reinterpret_cast<const f32x4*>(&cb.gam[16 * tb + 4 * gq]);
 #pragma unroll
-            for (int b = 0; b < NR; ++b) {
-                f32x4 v = zero4();
-                if ((VMASK >> b) & 1) v = quad_f32<OP>(rt_ctile<OP, DV>(cb.V, 16 * tb, R0[b]));
-                r2[b][h] = v - g4 * Y[b][tb];
-            }
+            for (int b = 0; b < NR; ++b) Y[b][tb0 + h] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+                for (int b = 0; b < NR; ++b) Y[b][tb0 + h] = Ops::mma(g[h][kk], Sb[b][kk], Y[b][tb0 + h]);
         }
+    };
+    auto mmZ = [&](const frag (&g)[2][NKK], int tb0) {
 #pragma unroll
-        for (int b = 0; b < NR; ++b) Rb[b][tp] = Ops::pack(r2[b][0], r2[b][1]);
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int b = 0; b < NR; ++b) Z[b][tb0 + h] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+                for (int b = 0; b < NR; ++b) Z[b][tb0 + h] = Ops::mma(Sb[b][kk], g[h][kk], Z[b][tb0 + h]);
+        }
+    };
+    load2(g0, cb.K, 0);
+    sched_fence();
+    load2(g1, cb.K, 2);
+    sched_fence();
+    mmY(g0, 0);
+    sched_fence();
+    if constexpr (OUT) load2(g0, cb.Q, 0);
+    sched_fence();
+    mmY(g1, 2);
+    sched_fence();
+    if constexpr (OUT) {
+        load2(g1, cb.Q, 2);
+        sched_fence();
+        mmZ(g0, 0);
+        sched_fence();
     }
-    // U = T~ R (T~ lower triangular: token tile tb needs K steps kk <= tb / 2)
+    // operands of R and U
+    f32x4 g4[4], vt[NR][4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        g4[tb] = *reinterpret_cast<const f32x4*>(&cb.gam[16 * tb + 4 * gq]);
+#pragma unroll
+        for (int b = 0; b < NR; ++b)
+            vt[b][tb] = ((VMASK >> b) & 1) ? quad_f32<OP>(rt_ctile<OP, DV>(cb.V, 16 * tb, R0[b])) : zero4();
+    }
+    frag tf[kTriFrags];
+#pragma unroll
+    for (int f = 0; f < kTriFrags; ++f) tf[f] = lds_frag(cb.T, f);
+    f32x4 dd[2][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        dd[kk][0] = *reinterpret_cast<const f32x4*>(&cb.dec[32 * kk + 4 * gq]);
+        dd[kk][1] = *reinterpret_cast<const f32x4*>(&cb.dec[32 * kk + 16 + 4 * gq]);
+    }
+    const float gl = cb.gam[kChunk - 1];
+    sched_fence();
+    if constexpr (OUT) {
+        mmZ(g1, 2);
+        sched_fence();
+    }
+    // R = V - diag(gamma) Y, packed pairwise as the B operand of T~ R; U = T~ R
+    frag Rb[NR][2];
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+        for (int b = 0; b < NR; ++b)
+            Rb[b][tp] = Ops::pack(vt[b][2 * tp] - g4[2 * tp] * Y[b][2 * tp], vt[b][2 * tp + 1] - g4[2 * tp + 1] * Y[b][2 * tp + 1]);
     f32x4 U[NR][4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-        const frag t0 = lds_frag(cb.T, tri_frag(tb, 0));
 #pragma unroll
-        for (int b = 0; b < NR; ++b) U[b][tb] = Ops::mma(t0, Rb[b][0], zero4());
-        if (tb >= 2) {
-            const frag t1 = lds_frag(cb.T, tri_frag(tb, 1));
+        for (int b = 0; b < NR; ++b) U[b][tb] = Ops::mma(tf[tri_frag(tb, 0)], Rb[b][0], zero4());
+        if (tb >= 2)
 #pragma unroll
-            for (int b = 0; b < NR; ++b) U[b][tb] = Ops::mma(t1, Rb[b][1], U[b][tb]);
-        }
+            for (int b = 0; b < NR; ++b) U[b][tb] = Ops::mma(tf[tri_frag(tb, 1)], Rb[b][1], U[b][tb]);
     }
-    // S^T <- gamma_last S^T + K^T diag(D) U
     frag Ud[NR][2], Ua[NR][2];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&cb.dec[32 * kk + 4 * gq]);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(&cb.dec[32 * kk + 16 + 4 * gq]);
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int b = 0; b < NR; ++b) {
-            Ud[b][kk] = Ops::pack(d0 * U[b][2 * kk], d1 * U[b][2 * kk + 1]);
+            Ud[b][kk] = Ops::pack(dd[kk][0] * U[b][2 * kk], dd[kk][1] * U[b][2 * kk + 1]);
             if constexpr (OUT) Ua[b][kk] = Ops::pack(U[b][2 * kk], U[b][2 * kk + 1]);
         }
-    }
-    const float gl = cb.gam[kChunk - 1];
+
+    // K^T fragments (bf16) and P are complete after this barrier; so is every
+    // wave's read of the previous chunk's O rows.
+    if constexpr (OUT || KT) lds_barrier();
+
+    // ---- S^T <- gamma_last S^T + K^T diag(D) U, operands in two groups
+    constexpr int HD = NDB / 2;
+    frag k0[HD][2], k1[HD][2];
+    auto loadK = [&](frag (&g)[HD][2], int db0) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+        for (int d = 0; d < HD; ++d)
 #pragma unroll
-        for (int b = 0; b < NR; ++b) ST[b][db] = gl * ST[b][db];
+            for (int kk = 0; kk < 2; ++kk) {
+                if constexpr (KT) g[d][kk] = lds_frag(kt, 2 * (db0 + d) + kk);
+                else g[d][kk] = kt_frag<OP, DK>(cb.K, db0 + d, kk);
+            }
+    };
+    auto mmS = [&](const frag (&g)[HD][2], int db0) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const frag kt = Ops::join(rt_ctile<OP, DK>(cb.K, 32 * kk, 16 * db), rt_ctile<OP, DK>(cb.K, 32 * kk + 16, 16 * db));
+        for (int d = 0; d < HD; ++d)
 #pragma unroll
-            for (int b = 0; b < NR; ++b) ST[b][db] = Ops::mma(kt, Ud[b][kk], ST[b][db]);
-        }
-    }
+            for (int b = 0; b < NR; ++b) {
+                f32x4 acc = gl * ST[b][db0 + d];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) acc = Ops::mma(g[d][kk], Ud[b][kk], acc);
+                ST[b][db0 + d] = acc;
+            }
+    };
+    loadK(k0, 0);
+    sched_fence();
+    loadK(k1, HD);
+    sched_fence();
+    mmS(k0, 0);
+    sched_fence();
+    frag pf[kTriFrags];
+    float gt[4];
     if constexpr (OUT) {
-        lds_barrier();   // P of this chunk is complete; the previous chunk's O rows are stored
+#pragma unroll
+        for (int f = 0; f < kTriFrags; ++f) pf[f] = lds_frag(P, f);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) gt[tb] = cb.gam[16 * tb + n];
+    }
+    sched_fence();
+    mmS(k1, HD);
+    if constexpr (OUT) {
+        sched_fence();
         // O^T tiles (rows x tokens): lane (n, gq) has O[16 tb + n][R0 + 4 gq + i]
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
-            f32x4 z[NR];
-#pragma unroll
-            for (int b = 0; b < NR; ++b) z[b] = zero4();
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const frag qf = rt_frag<OP, DK>(cb.Q, 16 * tb + n, 32 * kk);
-#pragma unroll
-                for (int b = 0; b < NR; ++b) z[b] = Ops::mma(Sb[b][kk], qf, z[b]);
-            }
-            const float gt = cb.gam[16 * tb + n];
-            const frag p0 = lds_frag(P, tri_frag(tb, 0));
-#pragma unroll
-            for (int b = 0; b < NR; ++b) z[b] = Ops::mma(Ua[b][0], p0, gt * z[b]);
-            if (tb >= 2) {
-                const frag p1 = lds_frag(P, tri_frag(tb, 1));
-#pragma unroll
-                for (int b = 0; b < NR; ++b) z[b] = Ops::mma(Ua[b][1], p1, z[b]);
-            }
 #pragma unroll
             for (int b = 0; b < NR; ++b) {
+                f32x4 z = Ops::mma(Ua[b][0], pf[tri_frag(tb, 0)], gt[tb] * Z[b][tb]);
+                if (tb >= 2) z = Ops::mma(Ua[b][1], pf[tri_frag(tb, 1)], z);
                 quad oq;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) oq[i] = from_f32<OP>(z[b][i]);
-                *reinterpret_cast<quad*>(ost + rt_off<DV>(16 * tb + n, (R0[b] >> 2) + gq)) = oq;
+                for (int i = 0; i < 4; ++i) oq[i] = from_f32<OP>(z[i]);
+                *reinterpret_cast<quad*>(ost + RowTile<OP, DV>::elem(16 * tb + n, R0[b] + 4 * gq)) = oq;
             }
         }
     }
@@ -629,19 +765,23 @@ __device__ __forceinline__ void chunk_rows(const ChunkBuf<OP, DK, DV, OUT>& cb, 
 // OUT = true: outputs of every part, from ws_s (np > 1) or init_state (np = 1);
 // the last part writes final_state.
 template <typename OP, int DK, int DV, bool OUT>
-__global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) void gdn_chunk_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * (OUT ? DV / 32 : (DV > DK ? DV : DK) / 16)) void gdn_chunk_kernel(PrefillArgs a) {
     using G = ChunkGeom<OP, DK, DV, OUT>;
-    static_assert(G::NT == 64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16), "launch bound must equal the launch size");
+    static_assert(G::NT == 64 * (OUT ? DV / 32 : (DV > DK ? DV : DK) / 16), "launch bound must equal the launch size");
     using Buf = ChunkBuf<OP, DK, DV, OUT>;
-    using quad = typename Op<OP>::quad;
     constexpr int NR = G::NR, NW = G::NW, NBUF = G::NBUF;
     constexpr int NVB = DV / 16, NMB = DK / 16, NDB = DK / 16;
     constexpr int E = (int)sizeof(OP), FU = Units<OP>::FU;
     constexpr int UK = kChunk * DK * E / 1024, UV = kChunk * DV * E / 1024, UT = kTriFrags * FU;
     __shared__ Buf buf0;
     __shared__ Buf buf1;
-    __shared__ OP Pf[OUT ? kTriFrags * 64 * 8 : 8];
-    __shared__ OP Ost[OUT ? kChunk * DV : 8];   // O rows of the previous chunk (rt_off layout)
+    __shared__ OP Pf[OUT ? (kTriFrags + 1) * 64 * 8 : 8];   // + one scratch fragment
+    __shared__ OP Ost[OUT ? kChunk * DV : 8];   // O rows of the previous chunk (RowTile layout)
+    // bf16: the chunk's K^T operand fragments (2 per state tile), transposed once
+    // per chunk instead of once per wave
+    constexpr bool KT = sizeof(OP) == 2;
+    constexpr int KTF = 2 * (DK / 16);
+    __shared__ OP Kt[KT ? KTF * 64 * 8 : 8];
 
     const int l = lane_id(), w = wave_id(), n = l & 15, gq = l >> 4;
     const int64_t pslot = blockIdx.x / a.hv;
@@ -660,7 +800,8 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
     // the wave's state blocks
     int R0[NR];
     if constexpr (OUT) {
-        R0[0] = 16 * w;
+        R0[0] = 32 * w;
+        R0[1] = 32 * w + 16;
     } else {
         R0[0] = w < NVB ? 16 * w : 0;   // value block (discarded when w >= NVB)
         R0[1] = w < NMB ? 16 * w : 0;   // transition block (discarded when w >= NMB)
@@ -687,7 +828,7 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
         for (int db = 0; db < NDB; ++db) {
             ST[0][db] = zero4();
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ST[1][db][i] = (16 * db + 4 * gq + i == R0[1] + n) ? 1.f : 0.f;
+            for (int i = 0; i < 4; ++i) ST[1][db][i] = (pi_dk(db, 4 * gq + i) == R0[1] + n) ? 1.f : 0.f;
         }
     }
     const int64_t jb = p * L, je = (jb + L < nc) ? jb + L : nc;
@@ -726,7 +867,7 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
     // O rows of chunk j, staged in Ost, to global memory (rows past the end dropped)
     OP* const og = static_cast<OP*>(a.out);
     auto store_o = [&](int64_t j) {
-        constexpr int VU = kChunk * DV * E / 16, UPR = DV * E / 16, VE = 16 / E;
+        constexpr int VU = kChunk * DV * E / 16, UPR = DV * E / 16;
         const int64_t nt = (len - j * kChunk) < kChunk ? (len - j * kChunk) : kChunk;
         const auto ro = make_rsrc(og + ((size_t)(s0 + j * kChunk) * a.hv + h) * DV, (nt - 1) * vstride + DV * E);
         const int tid = threadIdx.x;
@@ -735,7 +876,7 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
             const int e = tid + k * G::NT;
             if (VU % G::NT == 0 || e < VU) {
                 const int row = e / UPR, u = e - row * UPR;
-                const u32x4 x = *reinterpret_cast<const u32x4*>(Ost + rt_off<DV>(row, u * VE / 4));
+                const u32x4 x = *reinterpret_cast<const u32x4*>(Ost + RowTile<OP, DV>::unit(row, u));
                 __builtin_amdgcn_raw_buffer_store_b128(x, ro, (unsigned)row * vstride + (unsigned)u * 16, 0, 0);
             }
         }
@@ -746,35 +887,9 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
         if (NBUF == 2 && j + 1 < je) issue(j + 1, nxt);
         if constexpr (OUT) {
             if (j > jb) store_o(j - 1);
-            // P^T tiles: P[t][s] = Gamma_ts q_t . k_s for s <= t, as B-operand
-            // fragments (tile e: fragment e / 2, K slots 4 (e & 1) ..)
-            for (int e = w; e < 2 * kTriFrags; e += NW) {
-                const int f = e >> 1, half = e & 1;
-                int tb, kk2;
-                tri_frag_pos(f, tb, kk2);
-                const int sb = 2 * kk2 + half;
-                quad pq;
-                if (sb > tb) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) pq[i] = from_f32<OP>(0.f);
-                } else {
-                    f32x4 acc = zero4();
-#pragma unroll
-                    for (int kk = 0; kk < DK / 32; ++kk)
-                        acc = Op<OP>::mma(rt_frag<OP, DK>(cur.K, 16 * sb + n, 32 * kk), rt_frag<OP, DK>(cur.Q, 16 * tb + n, 32 * kk), acc);
-                    const int t = 16 * tb + n;
-                    const double gt = cur.G2[t];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int s = 16 * sb + 4 * gq + i;
-                        pq[i] = from_f32<OP>(s <= t ? fast_exp2((float)(gt - cur.G2[s])) * acc[i] : 0.f);
-                    }
-                }
-                lds_frag_half(Pf, f, half, pq);
-            }
-            chunk_rows<OP, DK, DV, OUT, NR, 1>(cur, Pf, Ost, ST, R0);
+            chunk_step<OP, DK, DV, OUT, NR, 3, NW>(cur, Pf, Kt, Ost, ST, R0, w);
         } else {
-            chunk_rows<OP, DK, DV, OUT, NR, 1>(cur, nullptr, nullptr, ST, R0);
+            chunk_step<OP, DK, DV, OUT, NR, 1, NW>(cur, nullptr, Kt, nullptr, ST, R0, w);
         }
         if (NBUF == 1 && j + 1 < je) {
             lds_barrier();                      // everyone is done with this chunk's rows

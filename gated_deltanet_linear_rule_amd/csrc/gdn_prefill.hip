@@ -159,6 +159,7 @@ struct PrepSmem {
 template <typename OP, int DK>
 __global__ __launch_bounds__(kPrepThreads, 2) void gdn_prep_kernel(PrefillArgs a) {
     using Ops = Op<OP>;
+    using frag = typename Ops::frag;
     using Sm = PrepSmem<OP, DK>;
     constexpr int LD = Sm::LD;
     constexpr int VE = Units<OP>::VE, FU = Units<OP>::FU;
@@ -248,36 +249,70 @@ __global__ __launch_bounds__(kPrepThreads, 2) void gdn_prep_kernel(PrefillArgs a
     }
     __syncthreads();
 
-    // ---- A = strict_lower(diag(beta) (Gamma o K K^T)), fp32
-    for (int job = w; job < 10; job += kPrepThreads / kWave) {
-        const int tm = kLowerTiles[job][0], tn = kLowerTiles[job][1];
-        f32x4 acc = zero4();
+    // ---- A = strict_lower(diag(beta) (Gamma o K K^T)), fp32.  Wave w takes the
+    // lower tiles w, w + 4, w + 8; operands are natural-order 16-byte rows of K.
+    // Loads are unconditional and the mask is a select, so no lane branches.
+    auto kfrag = [&](int row, int k0) -> frag {
+        if constexpr (sizeof(OP) == 2) {
+            return *reinterpret_cast<const bf16x8*>(&sm.K[row * LD + k0 + 8 * gq]);
+        } else {
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(&sm.K[row * LD + k0 + 8 * gq]);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(&sm.K[row * LD + k0 + 8 * gq + 4]);
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk)
-            acc = Ops::mma(frag_rows(sm.K, LD, 16 * tm + r, 32 * kk), frag_rows(sm.K, LD, 16 * tn + r, 32 * kk), acc);
-        const int s = 16 * tn + r;
+    for (int jr = 0; jr < 3; ++jr) {
+        const int job = w + 4 * jr;
+        if (job < 10) {
+            const int tm = kLowerTiles[job][0], tn = kLowerTiles[job][1];
+            frag fa[DK / 32], fb[DK / 32];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 16 * tm + 4 * gq + i;
-            sm.A[t][s] = (s < t) ? sm.B[t] * fast_exp2((float)(sm.G[t] - sm.G[s])) * acc[i] : 0.f;
+            for (int kk = 0; kk < DK / 32; ++kk) {
+                fa[kk] = kfrag(16 * tm + r, 32 * kk);
+                fb[kk] = kfrag(16 * tn + r, 32 * kk);
+            }
+            const int s = 16 * tn + r;
+            const double gs = sm.G[s];
+            double gt[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gt[i] = sm.G[16 * tm + 4 * gq + i];
+            const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.B[16 * tm + 4 * gq]);
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) acc = Ops::mma(fa[kk], fb[kk], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * tm + 4 * gq + i;
+                const float x = bt[i] * fast_exp2((float)(gt[i] - gs)) * acc[i];
+                sm.A[t][s] = s < t ? x : 0.f;
+            }
         }
     }
     __syncthreads();
 
-    // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution
-    // (lane c of wave b solves column c of block b), fp32.
-    if (l < 16) {
-        const int b = w, c = l;
+    // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution,
+    // fp32.  Wave b solves block b; lane j holds column j of the block's rows
+    // (a[i] = A[16 b + i][16 b + j]), and lane c (< 16) solves column c, taking
+    // the coefficients A_ij from lane j with readlane.
+    {
+        const int b = w, c = l & 15;
+        float av[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) av[i] = sm.A[16 * b + i][16 * b + c];
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             float acc = (i == c) ? 1.f : 0.f;
 #pragma unroll
-            for (int j = 0; j < i; ++j) acc -= sm.A[16 * b + i][16 * b + j] * x[j];
+            for (int j = 0; j < i; ++j)
+                acc -= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, av[i]), j)) * x[j];
             x[i] = acc;
         }
+        if (l < 16) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sm.T[16 * b + i][16 * b + c] = x[i];
+            for (int i = 0; i < 16; ++i) sm.T[16 * b + i][16 * b + c] = x[i];
+        }
     }
     __syncthreads();
     // Off-diagonal blocks, by distance from the diagonal:
@@ -304,16 +339,24 @@ __global__ __launch_bounds__(kPrepThreads, 2) void gdn_prep_kernel(PrefillArgs a
 
     // ---- T~ = T diag(beta), written as the chunk kernels' A-operand fragments
     OP* const Tw = static_cast<OP*>(a.ws_t) + blk * (kTriFrags * 64 * 8);
-    for (int e = tid; e < kTriFrags * 64; e += kPrepThreads) {
+#pragma unroll
+    for (int it = 0; it < (kTriFrags * 64 + kPrepThreads - 1) / kPrepThreads; ++it) {
+        const int e = tid + it * kPrepThreads;
+        if (e >= kTriFrags * 64) break;   // uniform per wave
         const int f = e >> 6, ln = e & 63, rr = ln & 15, g4 = ln >> 4;
         int tb, kk;
         tri_frag_pos(f, tb, kk);
         const int t = 16 * tb + rr;
+        const f32x4 t0 = *reinterpret_cast<const f32x4*>(&sm.T[t][32 * kk + 4 * g4]);
+        const f32x4 t1 = *reinterpret_cast<const f32x4*>(&sm.T[t][32 * kk + 16 + 4 * g4]);
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(&sm.B[32 * kk + 4 * g4]);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(&sm.B[32 * kk + 16 + 4 * g4]);
         float x[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int s = 32 * kk + (i < 4 ? 4 * g4 + i : 16 + 4 * g4 + i - 4);
-            x[i] = (s <= t) ? sm.T[t][s] * sm.B[s] : 0.f;
+            const float v = i < 4 ? t0[i] * b0[i] : t1[i - 4] * b1[i - 4];
+            x[i] = s <= t ? v : 0.f;   // entries above the diagonal may hold stale values
         }
         if constexpr (FU == 1) {
             bf16x8 v;

@@ -153,7 +153,7 @@ def main():
     ap.add_argument("--decode-runs", type=int, default=3, help="timed 64-step decode runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=131072)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=262144)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB -> 1 GiB elementwise kernel (torch.neg, fp32), the "
                          "known-size reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -283,8 +283,9 @@ def main():
         cw = time.perf_counter() - t1
         cpu = {"value": round(Ts / cw, 1), "unit": "tokens/s", "cores": c_oracle.threads(threads),
                "kind": "oracle",
-               "sample": f"first {Ts} tokens of the T=262144, H=16, d=128 prefill (all 16 heads), "
-                         f"fp64 sequential oracle, {cw:.1f}s wall"}
+               "sample": (f"the whole T=262144, H=16, d=128 prefill (all 16 heads)" if Ts == T else
+                          f"first {Ts} tokens of the T=262144, H=16, d=128 prefill (all 16 heads)")
+                         + f", fp64 sequential oracle, {cw:.1f}s wall"}
         log(f"cpu oracle: {Ts} tokens in {cw:.1f}s on {cpu['cores']} threads")
 
     if args.calib_copy:
@@ -313,7 +314,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic / (ms * 1e-3) / 1e9, 1),
-                     "kernel": "gdn_prefill call (prep + scan kernels)",
+                     "kernel": "gdn_prefill call (prep, summary, link and output kernels)",
                      "bytes_per_call": bytes_call,
                      "mfma_tflops": round(tflops, 1),
                      "mfma_frac_of_bf16_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)},

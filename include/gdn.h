@@ -93,11 +93,14 @@ typedef struct gdn_shape {
  * out         [num_tokens, Hv, dv] in `dtype`.
  * final_state [N, Hv, dv, dk] fp32 or NULL.
  *
- * Memory: a stream-ordered workspace of about
- * (num_tokens / 64 + N) * Hv * (64 * (3 dk + dv + 64) * sizeof(element) + 4)
- * bytes is taken
- * from HIP's default memory pool on `stream` and returned to it before the
- * call's work completes (GDN_ERROR_OUT_OF_MEMORY if that fails).
+ * Memory: a stream-ordered workspace is taken from HIP's default memory pool
+ * on `stream` and returned to it before the call's work completes
+ * (GDN_ERROR_OUT_OF_MEMORY if that fails).  Its size is about
+ * (num_tokens / 64 + N) * Hv * (3072 * sizeof(element) + 1024) bytes (the
+ * chunks' triangular factors and gates), plus, when a sequence is cut into
+ * parts of L chunks because there are fewer (sequence, head) pairs than
+ * compute units, (num_tokens / (64 L) + N) * Hv * (dk + 2 dv) * dk * 4 bytes
+ * (each part's transition, offset and start state).
  */
 gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, const void* v,
                        const float* g, const float* beta, const float* init_state,

@@ -105,26 +105,39 @@ def test_long_decay_free_stretch_stays_accurate():
     check_prefill(inp, label="g=0, beta/10")
 
 
-# ------------------------------------------------- segmented prep/scan launch
-# Few long sequences run as segments of 256 chunks whose prep overlaps the
-# previous segment's scan, with the state carried between segments.
+# ------------------------------------------------------- sequences cut into parts
+# With fewer (sequence, head) chains than compute units, long sequences are cut
+# into parts of L chunks (at least 8): every part but the last is summarised
+# (transition and offset), the link composes the start states, and every part
+# reruns from its true start state.
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_segmented_long_sequence(dtype):
-    """One 40000-token sequence (625 chunks: three segments, the last partial), given initial state."""
+def test_parts_long_sequence(dtype):
+    """One 40000-token sequence (625 chunks: 79 parts of 8, the last partial), given initial state."""
     inp = gi.make_inputs(gi.custom(dtype=dtype, Hqk=2, Hv=2, dk=128, dv=128, seqlens=(40000,),
                                    init_state="normal"), seed=21)
-    check_prefill(inp, label=f"segmented 40000 {dtype}")
+    check_prefill(inp, label=f"parts 40000 {dtype}")
 
 
-def test_segmented_unequal_packed_sequences():
-    """Two packed sequences of 33000 and 40000 tokens: segments past the end of the shorter one
-    carry its state through unchanged."""
+def test_parts_unequal_packed_sequences():
+    """Two packed sequences of 33000 and 40000 tokens (516 and 625 chunks): different part counts
+    per sequence, a partial last part and a partial last chunk in each."""
     inp = gi.make_inputs(gi.custom(dtype="bf16", Hqk=1, Hv=2, dk=128, dv=64, seqlens=(33000, 40000),
                                    init_state="normal"), seed=22)
-    check_prefill(inp, label="segmented 33000+40000")
+    check_prefill(inp, label="parts 33000+40000")
 
 
-def test_segmented_equal_length_batch_without_offsets_in_place_state():
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64)])
+def test_parts_decay_free_f32(dk, dv):
+    """g = 0 over 64 chunks cut into 8 parts: no decay hides an error in the composed transitions
+    (fp32 path, 1e-5)."""
+    inp = gi.make_inputs(gi.custom(dtype="f32", Hqk=1, Hv=1, dk=dk, dv=dv, seqlens=(4096,),
+                                   init_state="normal"), seed=24)
+    inp.g = np.zeros_like(inp.g)
+    inp.beta = (inp.beta * 0.25).astype(np.float32)
+    check_prefill(inp, label=f"parts g=0 f32 dk={dk} dv={dv}")
+
+
+def test_parts_equal_length_batch_without_offsets_in_place_state():
     """Two 36864-token sequences without offsets, initial state updated in place."""
     inp = gi.make_inputs(gi.custom(dtype="bf16", Hqk=2, Hv=2, dk=64, dv=128, seqlens=(36864, 36864),
                                    init_state="normal"), seed=23)
@@ -134,7 +147,7 @@ def test_segmented_equal_length_batch_without_offsets_in_place_state():
     inp.cu_seqlens = cu
     ro, rf = c_oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.init_state, cu)
     eo, ef = rel_err(out, ro), rel_err(fin, rf)
-    say(f"[parity] segmented 2x36864 no offsets, in place: out {eo:.3e} final {ef:.3e}")
+    say(f"[parity] parts 2x36864 no offsets, in place: out {eo:.3e} final {ef:.3e}")
     assert eo <= 1e-2 and ef <= 1e-2
 
 

@@ -535,8 +535,8 @@ struct ChunkBuf {
 // read from LDS feeds two products.
 template <typename OP, int DK, int DV, bool OUT>
 struct ChunkGeom {
-    static constexpr int NR = 2;
-    static constexpr int NW = OUT ? DV / 32 : (DV > DK ? DV : DK) / 16;
+    static constexpr int NR = OUT ? 1 : 2;
+    static constexpr int NW = OUT ? DV / 16 : (DV > DK ? DV : DK) / 16;
     static constexpr int NT = NW * kWave;
     static constexpr int NBUF = sizeof(OP) == 2 ? 2 : 1;   // fp32 rows do not fit twice
 };
@@ -562,7 +562,13 @@ __device__ __forceinline__ void store_state(float* S, int R0, const f32x4 (&ST)[
 // Keeps the compiler's scheduler from moving instructions across this point,
 // so that each group of LDS reads is issued ahead of the products that use the
 // previous group (the reads are then in flight while the matrix cores work).
-__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+// Measured: this helps the summary kernel (two state blocks per wave) and hurts
+// the output kernel (one block per wave, two waves per SIMD), which is left to
+// the compiler's own schedule.
+template <bool ON>
+__device__ __forceinline__ void sched_fence() {
+    if constexpr (ON) __builtin_amdgcn_sched_barrier(0);
+}
 
 // One chunk for the wave's NR state blocks (rows R0[b] .. R0[b] + 15; block b
 // has a V term when bit b of VMASK is set, else it is a transition block whose
@@ -576,9 +582,13 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // Before the barrier in the middle, the wave also writes its share of the
 // chunk's K^T operand fragments (bf16) and P^T tiles (OUT); after it, it reads
 // all of them.  OUT: the O^T tiles go to the row tile `ost` (RowTile layout).
-template <typename OP, int DK, int DV, bool OUT, int NR, int VMASK, int NW>
+//
+// `after_writes` runs once the wave's LDS writes of the state-free part are
+// issued: the next chunk's direct loads are issued there, since the compiler
+// orders any LDS write it cannot tell apart from their target after them.
+template <typename OP, int DK, int DV, bool OUT, int NR, int VMASK, int NW, typename F>
 __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, OP* P, OP* kt, OP* ost,
-                                           f32x4 (&ST)[NR][DK / 16], const int (&R0)[NR], int w) {
+                                           f32x4 (&ST)[NR][DK / 16], const int (&R0)[NR], int w, F&& after_writes) {
     using Ops = Op<OP>;
     using frag = typename Ops::frag;
     using quad = typename Ops::quad;
@@ -611,7 +621,7 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, 
                 pq[r][kk] = rt_frag<OP, DK>(cb.Q, 16 * ptb[r] + n, 32 * kk);
             }
         }
-        sched_fence();
+        sched_fence<!OUT>();
 #pragma unroll
         for (int r = 0; r < PT; ++r) {
             const int t = 16 * ptb[r] + n;
@@ -630,7 +640,7 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, 
             }
             lds_frag_half(P, pf[r], ph[r], pv);
         }
-        sched_fence();
+        sched_fence<!OUT>();
     }
     if constexpr (KT) {
 #pragma unroll
@@ -639,8 +649,10 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, 
             if (KTF % NW == 0 || f < KTF)
                 *reinterpret_cast<bf16x8*>(kt + ((size_t)f * 64 + l) * 8) = kt_frag<OP, DK>(cb.K, f >> 1, f & 1);
         }
-        sched_fence();
+        sched_fence<!OUT>();
     }
+    after_writes();
+    sched_fence<!OUT>();
 
     // ---- Y = K S^T and Z = S Q^T; operands stream in groups of two token tiles
     frag Sb[NR][NKK];
@@ -679,20 +691,20 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, 
         }
     };
     load2(g0, cb.K, 0);
-    sched_fence();
+    sched_fence<!OUT>();
     load2(g1, cb.K, 2);
-    sched_fence();
+    sched_fence<!OUT>();
     mmY(g0, 0);
-    sched_fence();
+    sched_fence<!OUT>();
     if constexpr (OUT) load2(g0, cb.Q, 0);
-    sched_fence();
+    sched_fence<!OUT>();
     mmY(g1, 2);
-    sched_fence();
+    sched_fence<!OUT>();
     if constexpr (OUT) {
         load2(g1, cb.Q, 2);
-        sched_fence();
+        sched_fence<!OUT>();
         mmZ(g0, 0);
-        sched_fence();
+        sched_fence<!OUT>();
     }
     // operands of R and U
     f32x4 g4[4], vt[NR][4];
@@ -713,10 +725,10 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, 
         dd[kk][1] = *reinterpret_cast<const f32x4*>(&cb.dec[32 * kk + 16 + 4 * gq]);
     }
     const float gl = cb.gam[kChunk - 1];
-    sched_fence();
+    sched_fence<!OUT>();
     if constexpr (OUT) {
         mmZ(g1, 2);
-        sched_fence();
+        sched_fence<!OUT>();
     }
     // R = V - diag(gamma) Y, packed pairwise as the B operand of T~ R; U = T~ R
     frag Rb[NR][2];
@@ -771,11 +783,11 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, 
             }
     };
     loadK(k0, 0);
-    sched_fence();
+    sched_fence<!OUT>();
     loadK(k1, HD);
-    sched_fence();
+    sched_fence<!OUT>();
     mmS(k0, 0);
-    sched_fence();
+    sched_fence<!OUT>();
     frag pf[kTriFrags];
     float gt[4];
     if constexpr (OUT) {
@@ -784,10 +796,10 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, 
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) gt[tb] = cb.gam[16 * tb + n];
     }
-    sched_fence();
+    sched_fence<!OUT>();
     mmS(k1, HD);
     if constexpr (OUT) {
-        sched_fence();
+        sched_fence<!OUT>();
         // O^T tiles (rows x tokens): lane (n, gq) has O[16 tb + n][R0 + 4 gq + i]
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
@@ -808,9 +820,9 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, 
 // OUT = true: outputs of every part, from ws_s (np > 1) or init_state (np = 1);
 // the last part writes final_state.
 template <typename OP, int DK, int DV, bool OUT>
-__global__ __launch_bounds__(64 * (OUT ? DV / 32 : (DV > DK ? DV : DK) / 16)) void gdn_chunk_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) void gdn_chunk_kernel(PrefillArgs a) {
     using G = ChunkGeom<OP, DK, DV, OUT>;
-    static_assert(G::NT == 64 * (OUT ? DV / 32 : (DV > DK ? DV : DK) / 16), "launch bound must equal the launch size");
+    static_assert(G::NT == 64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16), "launch bound must equal the launch size");
     using Buf = ChunkBuf<OP, DK, DV, OUT>;
     constexpr int NR = G::NR, NW = G::NW, NBUF = G::NBUF;
     constexpr int NVB = DV / 16, NMB = DK / 16, NDB = DK / 16;
@@ -843,8 +855,7 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 32 : (DV > DK ? DV : DK) / 16)) vo
     // the wave's state blocks
     int R0[NR];
     if constexpr (OUT) {
-        R0[0] = 32 * w;
-        R0[1] = 32 * w + 16;
+        R0[0] = 16 * w;
     } else {
         R0[0] = w < NVB ? 16 * w : 0;   // value block (discarded when w >= NVB)
         R0[1] = w < NMB ? 16 * w : 0;   // transition block (discarded when w >= NMB)
@@ -924,15 +935,69 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 32 : (DV > DK ? DV : DK) / 16)) vo
             }
         }
     };
-    auto body = [&](int64_t j, const Buf& cur, Buf& nxt) {
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's loads of chunk j have landed
+    // L2 prefetch (bf16): while chunk j + 1 loads into LDS, one 4-byte load per
+    // 128-byte line of chunk j + 2 pulls that chunk into L2, so its own LDS
+    // loads, issued a chunk later, hit L2.  The loaded words are consumed two
+    // chunks later, after the wait that covers them, so these loads never hold
+    // up a chunk.  Lines: K, Q (output), V rows, T~, gate record; one 64-lane
+    // load per 64 lines of one array; every wave issues TPW loads (spare ones
+    // read out of range: no traffic).
+    constexpr int LK = kChunk * DK * E / 128, LV = kChunk * DV * E / 128, LT = UT * 8;
+    constexpr int IK = (LK + 63) / 64, IV = (LV + 63) / 64, IT = (LT + 63) / 64;
+    constexpr int NI = (OUT ? 2 * IK : IK) + IV + IT + 1;
+    constexpr int TPW = NBUF == 2 ? (NI + NW - 1) / NW : 0;
+    uint32_t tvA[TPW > 0 ? TPW : 1] = {}, tvB[TPW > 0 ? TPW : 1] = {}, sink = 0;
+    auto touch = [&](int64_t j, uint32_t (&tv)[TPW > 0 ? TPW : 1]) {
+        const int64_t t0 = s0 + j * kChunk;
+        const int64_t nt = (len - j * kChunk) < kChunk ? (len - j * kChunk) : kChunk;
+        const size_t cblk = (size_t)(cbase + j) * a.hv + h;
+        const size_t krow = ((size_t)t0 * a.hqk + hq) * DK;
+        const auto rk = make_rsrc(static_cast<const OP*>(a.k) + krow, (nt - 1) * kstride + DK * E);
+        const auto rq = make_rsrc(static_cast<const OP*>(a.q) + krow, (nt - 1) * kstride + DK * E);
+        const auto rv = make_rsrc(static_cast<const OP*>(a.v) + ((size_t)t0 * a.hv + h) * DV, (nt - 1) * vstride + DV * E);
+        const auto rt = make_rsrc(static_cast<const OP*>(a.ws_t) + cblk * (kTriFrags * 64 * 8), UT * 1024);
+        const auto rg = make_rsrc(a.ws_g + cblk * (kGateRecord / 8), kGateRecord);
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+            int slot = w + NW * k;
+            __amdgpu_buffer_rsrc_t rs = rg;
+            unsigned off = 0xFFFFF000u;   // spare: out of range
+            auto rows = [&](int sub, int lines_per_row, unsigned stride) {
+                const int li = 64 * sub + l;
+                off = (unsigned)(li / lines_per_row) * stride + (unsigned)(li % lines_per_row) * 128;
+            };
+            if (slot < IK) { rs = rk; rows(slot, DK * E / 128, kstride); }
+            else if (OUT && slot < 2 * IK) { rs = rq; rows(slot - IK, DK * E / 128, kstride); }
+            else if (slot < (OUT ? 2 * IK : IK) + IV) { rs = rv; rows(slot - (OUT ? 2 * IK : IK), DV * E / 128, vstride); }
+            else if (slot < NI - 1) { rs = rt; off = (unsigned)(64 * (slot - (NI - 1 - IT)) + l) * 128; }
+            else if (slot == NI - 1) { rs = rg; off = (unsigned)l * 128; }
+            tv[k] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+        }
+    };
+    auto consume = [&](uint32_t (&tv)[TPW > 0 ? TPW : 1]) {
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) sink ^= tv[k];
+    };
+    auto body = [&](int64_t j, const Buf& cur, Buf& nxt, uint32_t (&tv)[TPW > 0 ? TPW : 1]) {
+        // this wave's loads of chunk j have landed (the TPW newest loads are the
+        // L2 prefetch of chunk j + 1)
+        if constexpr (TPW == 0) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        else __builtin_amdgcn_s_waitcnt(kWaitVm0 | (TPW & 15) | ((TPW >> 4) << 14));
         lds_barrier();                          // everyone's have; the previous chunk is done everywhere
-        if (NBUF == 2 && j + 1 < je) issue(j + 1, nxt);
         if constexpr (OUT) {
             if (j > jb) store_o(j - 1);
-            chunk_step<OP, DK, DV, OUT, NR, 3, NW>(cur, Pf, Kt, Ost, ST, R0, w);
+        }
+        auto next_loads = [&]() {
+            if (NBUF == 2 && j + 1 < je) issue(j + 1, nxt);
+            if constexpr (TPW > 0) {
+                consume(tv);
+                touch(j + 2 < je ? j + 2 : je - 1, tv);
+            }
+        };
+        if constexpr (OUT) {
+            chunk_step<OP, DK, DV, OUT, NR, 1, NW>(cur, Pf, Kt, Ost, ST, R0, w, next_loads);
         } else {
-            chunk_step<OP, DK, DV, OUT, NR, 1, NW>(cur, nullptr, Kt, nullptr, ST, R0, w);
+            chunk_step<OP, DK, DV, OUT, NR, 1, NW>(cur, nullptr, Kt, nullptr, ST, R0, w, next_loads);
         }
         if (NBUF == 1 && j + 1 < je) {
             lds_barrier();                      // everyone is done with this chunk's rows
@@ -941,9 +1006,15 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 32 : (DV > DK ? DV : DK) / 16)) vo
     };
 
     issue(jb, buf0);
+    if constexpr (TPW > 0) touch(jb + 1 < je ? jb + 1 : je - 1, tvB);
     for (int64_t j = jb; j < je; j += NBUF) {
-        body(j, buf0, NBUF == 2 ? buf1 : buf0);
-        if (NBUF == 2 && j + 1 < je) body(j + 1, buf1, buf0);
+        body(j, buf0, NBUF == 2 ? buf1 : buf0, tvA);
+        if (NBUF == 2 && j + 1 < je) body(j + 1, buf1, buf0, tvB);
+    }
+    if constexpr (TPW > 0) {
+        consume(tvA);
+        consume(tvB);
+        asm volatile("" ::"v"(sink));
     }
     if constexpr (OUT) {
         lds_barrier();

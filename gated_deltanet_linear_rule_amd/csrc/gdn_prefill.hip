@@ -51,7 +51,6 @@
 namespace gdn {
 namespace {
 
-constexpr int kPrepThreads = 256;
 constexpr int kTriFrags = 6;       // lower operand fragments of a 64 x 64 matrix
 constexpr int kLinkThreads = 256;
 // Gate record of one (chunk, value head): G2_t = log2-scaled cumulative gate
@@ -64,10 +63,6 @@ __device__ __forceinline__ u32x4 zero_u4() { return u32x4{0u, 0u, 0u, 0u}; }
 
 template <typename T>
 __device__ __forceinline__ u32x4 ld16(const T* p) { return *reinterpret_cast<const u32x4*>(p); }
-
-// Lower 16x16 tiles (tm >= tn) of a 64x64 matrix, in a fixed order.
-__constant__ int kLowerTiles[10][2] = {{0, 0}, {1, 0}, {1, 1}, {2, 0}, {2, 1},
-                                       {2, 2}, {3, 0}, {3, 1}, {3, 2}, {3, 3}};
 
 // Operand fragments of a lower-triangular 64 x 64 matrix X (T~ or P): for token
 // tile tb and 32-wide K step kk <= tb / 2, fragment f = tri_frag(tb, kk).  Lane
@@ -144,233 +139,193 @@ template <typename T>
 __device__ __forceinline__ void ws_store(T* p, const T& x) { __builtin_nontemporal_store(x, p); }
 
 // ===========================================================================
-// prep: T~ fragments and G2 for one (chunk, value head)
+// prep: T~ fragments and the gate record of one (chunk, value head) per wave
 // ===========================================================================
-template <typename OP, int DK>
-struct PrepSmem {
-    static constexpr int LD = DK + 16 / (int)sizeof(OP);    // K rows (padded)
-    alignas(16) OP K[kChunk * LD];
-    alignas(16) float A[kChunk][kChunk + 4];
-    alignas(16) float T[kChunk][kChunk + 4];
-    alignas(16) double G[kChunk];                           // log2-scaled cumulative gates (fp64)
-    alignas(16) float B[kChunk];                            // beta
+// The four waves of a workgroup take four consecutive items and share nothing,
+// so the kernel has no workgroup barrier.  A wave keeps its chunk's K as
+// matrix-core operand fragments in registers (loaded straight from memory),
+// forms the ten lower 16x16 tiles of the gated A, solves the diagonal blocks
+// by forward substitution and the off-diagonal blocks on the fp32 matrix
+// cores, and writes T~ = T diag(beta) directly in the chunk kernels' operand
+// order.  Only the gates and the diagonal 16 x 16 blocks pass through LDS.
+constexpr int kPrepWaves = 4;
+constexpr int kDiagLd = 16 * 16 + 8;   // floats per stored 16 x 16 block (padded)
+
+struct PrepWaveSmem {
+    alignas(16) float D[4 * kDiagLd];  // diagonal blocks of A, then of T; column-major
+    alignas(16) double G[kChunk];      // log2-scaled cumulative gates (fp64)
+    alignas(16) float B[kChunk];       // beta
 };
 
+// Orders a wave's LDS accesses: its earlier LDS writes complete before any
+// later LDS read by another lane of the same wave, and the compiler moves no
+// memory access across.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Eight consecutive elements p[0..7] as an operand fragment in natural K order.
+template <typename OP>
+__device__ __forceinline__ typename Op<OP>::frag load_frag8(const OP* p) {
+    if constexpr (sizeof(OP) == 2) {
+        return *reinterpret_cast<const bf16x8*>(p);
+    } else {
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+}
+
+// Index of lower tile (tm, tn), tn <= tm, in row order.
+__host__ __device__ constexpr int lower_tile(int tm, int tn) { return tm * (tm + 1) / 2 + tn; }
+
 template <typename OP, int DK>
-__global__ __launch_bounds__(kPrepThreads, 2) void gdn_prep_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kWave * kPrepWaves) void gdn_prep_kernel(PrefillArgs a) {
     using Ops = Op<OP>;
     using frag = typename Ops::frag;
-    using Sm = PrepSmem<OP, DK>;
-    constexpr int LD = Sm::LD;
     constexpr int VE = Units<OP>::VE, FU = Units<OP>::FU;
-    constexpr int NV = DK / VE;                             // 16-byte vectors per K row
-    constexpr int KREG = kChunk * NV / kPrepThreads;        // K vectors per thread
-    static_assert(KREG * kPrepThreads == kChunk * NV, "staging");
-    __shared__ Sm sm;
+    constexpr int NK = DK / 32;
+    __shared__ PrepWaveSmem smem[kPrepWaves];
 
-    const int tid = threadIdx.x, l = lane_id(), w = wave_id(), r = l & 15, gq = l >> 4;
+    const int l = lane_id(), w = wave_id(), r = l & 15, gq = l >> 4;
+    PrepWaveSmem& sm = smem[w];
+    const int64_t item = (int64_t)blockIdx.x * kPrepWaves + w;
+    if (item >= a.num_slots * a.hv) return;
+    const int64_t slot = item / a.hv;
+    const int h = (int)(item - slot * a.hv);
     const SeqIndex si{a.cu, a.seqlen};
+    int n;
+    int64_t j;
+    locate_span(si, a.num_seqs, kChunk, slot, n, j);
+    const int64_t s1 = si.start(n + 1), t0 = si.start(n) + j * kChunk;
+    if (j < 0 || t0 >= s1) return;   // a gap slot (the whole wave leaves)
+    const int nt = (int)((s1 - t0) < kChunk ? (s1 - t0) : kChunk);
+    const int hq = (h * a.hqk) / a.hv;
+    const size_t blk = (size_t)slot * a.hv + h;
+
+    // ---- loads.  Lane (r, gq) takes K[16 tb + r][32 kk + 8 gq .. + 7]: the A
+    // and B operand fragments of K K^T at once.  Rows past the end repeat the
+    // last row: their beta is 0, so they never reach A, T~ or the gates.
+    frag kf[4][NK];
     const OP* kg = static_cast<const OP*>(a.k);
-    const int64_t nitems = a.num_slots * a.hv;
-
-    // One work item = one (chunk slot, value head); a workgroup walks the items
-    // blockIdx.x, blockIdx.x + gridDim.x, ..., fetching the next item's inputs
-    // into registers while it computes the current one.
-    struct Item {
-        bool ok;           // a real chunk (not past the end, not a gap slot)
-        int64_t slot, t0;
-        int h, nt, hq;
-    };
-    auto locate = [&](int64_t item) {
-        Item it{};
-        it.ok = false;
-        if (item < nitems) {
-            it.slot = item / a.hv;
-            it.h = (int)(item - it.slot * a.hv);
-            int n;
-            int64_t j;
-            locate_span(si, a.num_seqs, kChunk, it.slot, n, j);
-            const int64_t s0 = si.start(n), s1 = si.start(n + 1);
-            it.t0 = s0 + j * kChunk;
-            it.ok = j >= 0 && it.t0 < s1;
-            it.nt = it.ok ? (int)((s1 - it.t0) < kChunk ? (s1 - it.t0) : kChunk) : 0;
-            it.hq = (it.h * a.hqk) / a.hv;
-        }
-        return it;
-    };
-    // rows past the end of the sequence are clamped here and zeroed when staged
-    u32x4 kreg[KREG];
-    float gv = 0.f, bv = 0.f;
-    auto fetch = [&](const Item& it) {
 #pragma unroll
-        for (int i = 0; i < KREG; ++i) {
-            const int e = tid + i * kPrepThreads;
-            const int row = e / NV, cv = e - row * NV;
-            const int rc = row < it.nt ? row : it.nt - 1;
-            kreg[i] = ld16(kg + ((size_t)(it.t0 + rc) * a.hqk + it.hq) * DK + (size_t)cv * VE);
-        }
-        const int lc = l < it.nt ? l : it.nt - 1;
-        gv = a.g[(size_t)(it.t0 + lc) * a.hv + it.h];
-        bv = a.beta[(size_t)(it.t0 + lc) * a.hv + it.h];
-    };
-
-    Item cur = locate(blockIdx.x);
-    if (cur.ok) fetch(cur);
-    for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const Item nxt = locate(item + gridDim.x);
-    if (!cur.ok) {
-        if (nxt.ok) fetch(nxt);
-        cur = nxt;
-        continue;
+    for (int tb = 0; tb < 4; ++tb) {
+        const int row = 16 * tb + r;
+        const OP* src = kg + ((size_t)(t0 + (row < nt ? row : nt - 1)) * a.hqk + hq) * DK + 8 * gq;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) kf[tb][kk] = load_frag8<OP>(src + 32 * kk);
     }
-    const int nt = cur.nt;
-    const size_t blk = (size_t)cur.slot * a.hv + cur.h;
+    const size_t gi = (size_t)(t0 + (l < nt ? l : nt - 1)) * a.hv + h;
+    const float gl = l < nt ? a.g[gi] : 0.f;
+    const float bl = l < nt ? a.beta[gi] : 0.f;
 
-    // ---- stage K into LDS (zero past the end)
-#pragma unroll
-    for (int i = 0; i < KREG; ++i) {
-        const int e = tid + i * kPrepThreads;
-        const int row = e / NV, cv = e - row * NV;
-        *reinterpret_cast<u32x4*>(&sm.K[row * LD + cv * VE]) = row < nt ? kreg[i] : zero_u4();
-    }
-    float gc = gv, bc = bv;
-    // the next item's inputs are in flight from here on
-    if (nxt.ok) fetch(nxt);
-    if (w == 0) {
-        if (l >= nt) { gc = 0.f; bc = 0.f; }
-        const double G = wave_cumsum_f64((double)gc * 1.4426950408889634);
-        const double Gl = lane63_f64(G);
-        sm.G[l] = G;
-        sm.B[l] = bc;
-        double* rec = a.ws_g + blk * (kGateRecord / 8);
-        ws_store(rec + l, G);
-        ws_store(reinterpret_cast<float*>(rec + kChunk) + l, fast_exp2((float)G));
-        ws_store(reinterpret_cast<float*>(rec + kChunk) + kChunk + l, fast_exp2((float)(Gl - G)));
-    }
-    __syncthreads();
+    const double G = wave_cumsum_f64((double)gl * 1.4426950408889634);
+    const double Gl = lane63_f64(G);
+    sm.G[l] = G;
+    sm.B[l] = bl;
+    wave_lds_sync();
 
-    // ---- A = strict_lower(diag(beta) (Gamma o K K^T)), fp32.  Wave w takes the
-    // lower tiles w, w + 4, w + 8; operands are natural-order 16-byte rows of K.
-    // Loads are unconditional and the mask is a select, so no lane branches.
-    auto kfrag = [&](int row, int k0) -> frag {
-        if constexpr (sizeof(OP) == 2) {
-            return *reinterpret_cast<const bf16x8*>(&sm.K[row * LD + k0 + 8 * gq]);
-        } else {
-            const f32x4 lo = *reinterpret_cast<const f32x4*>(&sm.K[row * LD + k0 + 8 * gq]);
-            const f32x4 hi = *reinterpret_cast<const f32x4*>(&sm.K[row * LD + k0 + 8 * gq + 4]);
-            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-    };
+    // ---- A = strict_lower(diag(beta) (Gamma o K K^T)): the ten lower tiles in
+    // accumulator layout (lane (n, gq) holds A[16 tm + 4 gq + i][16 tn + n]).
+    f32x4 at[10];
 #pragma unroll
-    for (int jr = 0; jr < 3; ++jr) {
-        const int job = w + 4 * jr;
-        if (job < 10) {
-            const int tm = kLowerTiles[job][0], tn = kLowerTiles[job][1];
-            frag fa[DK / 32], fb[DK / 32];
+    for (int tm = 0; tm < 4; ++tm) {
+        double gt[4];
 #pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) {
-                fa[kk] = kfrag(16 * tm + r, 32 * kk);
-                fb[kk] = kfrag(16 * tn + r, 32 * kk);
-            }
-            const int s = 16 * tn + r;
-            const double gs = sm.G[s];
-            double gt[4];
+        for (int i = 0; i < 4; ++i) gt[i] = sm.G[16 * tm + 4 * gq + i];
+        const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.B[16 * tm + 4 * gq]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) gt[i] = sm.G[16 * tm + 4 * gq + i];
-            const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.B[16 * tm + 4 * gq]);
+        for (int tn = 0; tn <= tm; ++tn) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) acc = Ops::mma(fa[kk], fb[kk], acc);
+            for (int kk = 0; kk < NK; ++kk) acc = Ops::mma(kf[tm][kk], kf[tn][kk], acc);
+            const double gs = sm.G[16 * tn + r];
+            f32x4 x;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = 16 * tm + 4 * gq + i;
-                const float x = bt[i] * fast_exp2((float)(gt[i] - gs)) * acc[i];
-                sm.A[t][s] = s < t ? x : 0.f;
+                x[i] = bt[i] * fast_exp2((float)(gt[i] - gs)) * acc[i];
+                if (tn == tm) x[i] = r < 4 * gq + i ? x[i] : 0.f;
             }
+            at[lower_tile(tm, tn)] = x;
         }
     }
-    __syncthreads();
 
-    // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution,
-    // fp32.  Wave b solves block b; lane j holds column j of the block's rows
-    // (a[i] = A[16 b + i][16 b + j]), and lane c (< 16) solves column c, taking
-    // the coefficients A_ij from lane j with readlane.
-    {
-        const int b = w, c = l & 15;
-        float av[16];
+    // ---- diagonal blocks of T = (I + A)^{-1}, fp32 forward substitution.
+    // The A blocks go to LDS column-major; lane (c, q) then solves column c of
+    // block q, x_i = delta_ic - sum_{j < i} A_ij x_j, taking column j of the
+    // block (a broadcast read within the lane group) once x_j is final.
 #pragma unroll
-        for (int i = 0; i < 16; ++i) av[i] = sm.A[16 * b + i][16 * b + c];
+    for (int b = 0; b < 4; ++b)
+        *reinterpret_cast<f32x4*>(&sm.D[b * kDiagLd + 16 * r + 4 * gq]) = at[lower_tile(b, b)];
+    wave_lds_sync();
+    {
+        const float* Dq = sm.D + gq * kDiagLd;
         float x[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float acc = (i == c) ? 1.f : 0.f;
+        for (int i = 0; i < 16; ++i) x[i] = i == r ? 1.f : 0.f;
 #pragma unroll
-            for (int j = 0; j < i; ++j)
-                acc -= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, av[i]), j)) * x[j];
-            x[i] = acc;
-        }
-        if (l < 16) {
+        for (int jc = 0; jc < 15; ++jc) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sm.T[16 * b + i][16 * b + c] = x[i];
-        }
-    }
-    __syncthreads();
-    // Off-diagonal blocks, by distance from the diagonal:
-    //   T_mb = -T_mm * sum_{b <= k < m} A_mk T_kb     (fp32 matrix cores)
+            for (int u = (jc + 1) >> 2; u < 4; ++u) {
+                const f32x4 col = *reinterpret_cast<const f32x4*>(Dq + 16 * jc + 4 * u);
 #pragma unroll
-    for (int dist = 1; dist <= 3; ++dist) {
-        if (w < 4 - dist) {
-            const int b = w, m = w + dist;
-            f32x4 z = zero4();
-            for (int kb = b; kb < m; ++kb) {
-                const f32x4 arow = *reinterpret_cast<const f32x4*>(&sm.A[16 * m + r][16 * kb + 4 * gq]);
-                f32x4 tcol;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) tcol[i] = sm.T[16 * kb + 4 * gq + i][16 * b + r];
-                z = mm16_f32(arow, tcol, z);
+                for (int e = 0; e < 4; ++e)
+                    if (4 * u + e > jc) x[4 * u + e] -= col[e] * x[jc];
             }
-            const f32x4 trow = *reinterpret_cast<const f32x4*>(&sm.T[16 * m + r][16 * m + 4 * gq]);
-            const f32x4 res = mm16_f32(trow, z, zero4());
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm.T[16 * m + 4 * gq + i][16 * b + r] = -res[i];
         }
-        __syncthreads();
+        wave_lds_sync();
+        float* Tq = sm.D + gq * kDiagLd + 16 * r;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            *reinterpret_cast<f32x4*>(Tq + 4 * u) = f32x4{x[4 * u], x[4 * u + 1], x[4 * u + 2], x[4 * u + 3]};
+    }
+    wave_lds_sync();
+    // T_bb in accumulator layout (tc) and in A-operand layout (ta: lane (r, gq)
+    // holds T_bb[r][4 gq + i]); the latter is exactly zero above the diagonal.
+    f32x4 tc[4], ta[4][4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        tc[b] = *reinterpret_cast<const f32x4*>(&sm.D[b * kDiagLd + 16 * r + 4 * gq]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ta[b][b][i] = sm.D[b * kDiagLd + 16 * (4 * gq + i) + r];
     }
 
-    // ---- T~ = T diag(beta), written as the chunk kernels' A-operand fragments
+    // ---- off-diagonal blocks, by distance from the diagonal.  Block row m of
+    // T (I + A) = I gives T_mb = -(sum_{b < k <= m} T_mk A_kb) T_bb; it is formed
+    // transposed, y^T = sum_k A_kb^T T_mk^T, then T_mb^T = -T_bb^T y^T, so that
+    // every operand is at hand in the layout the matrix core wants and the
+    // result comes out in A-operand layout.
+#pragma unroll
+    for (int d = 1; d < 4; ++d) {
+#pragma unroll
+        for (int b = 0; b + d < 4; ++b) {
+            const int m = b + d;
+            f32x4 yT = zero4();
+#pragma unroll
+            for (int k = b + 1; k <= m; ++k) yT = mm16_f32(at[lower_tile(k, b)], ta[m][k], yT);
+            ta[m][b] = -mm16_f32(tc[b], yT, zero4());
+        }
+    }
+
+    // ---- T~ = T diag(beta) as operand fragments, and the gate record
+    f32x4 bc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bc[c] = *reinterpret_cast<const f32x4*>(&sm.B[16 * c + 4 * gq]);
     OP* const Tw = static_cast<OP*>(a.ws_t) + blk * (kTriFrags * 64 * 8);
 #pragma unroll
-    for (int it = 0; it < (kTriFrags * 64 + kPrepThreads - 1) / kPrepThreads; ++it) {
-        const int e = tid + it * kPrepThreads;
-        if (e >= kTriFrags * 64) break;   // uniform per wave
-        const int f = e >> 6, ln = e & 63, rr = ln & 15, g4 = ln >> 4;
-        int tb, kk;
-        tri_frag_pos(f, tb, kk);
-        const int t = 16 * tb + rr;
-        const f32x4 t0 = *reinterpret_cast<const f32x4*>(&sm.T[t][32 * kk + 4 * g4]);
-        const f32x4 t1 = *reinterpret_cast<const f32x4*>(&sm.T[t][32 * kk + 16 + 4 * g4]);
-        const f32x4 b0 = *reinterpret_cast<const f32x4*>(&sm.B[32 * kk + 4 * g4]);
-        const f32x4 b1 = *reinterpret_cast<const f32x4*>(&sm.B[32 * kk + 16 + 4 * g4]);
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int s = 32 * kk + (i < 4 ? 4 * g4 + i : 16 + 4 * g4 + i - 4);
-            const float v = i < 4 ? t0[i] * b0[i] : t1[i - 4] * b1[i - 4];
-            x[i] = s <= t ? v : 0.f;   // entries above the diagonal may hold stale values
-        }
+    for (int f = 0; f < kTriFrags; ++f) {
+        const int tb = f < 2 ? f : 2 + ((f - 2) >> 1), kk = f < 2 ? 0 : ((f - 2) & 1);
+        const f32x4 lo = ta[tb][2 * kk] * bc[2 * kk];
+        const f32x4 hi = 2 * kk + 1 <= tb ? ta[tb][2 * kk + 1] * bc[2 * kk + 1] : zero4();
         if constexpr (FU == 1) {
-            bf16x8 v;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = (__bf16)x[i];
-            ws_store(reinterpret_cast<bf16x8*>(Tw + ((size_t)f * 64 + ln) * VE), v);
+            ws_store(reinterpret_cast<frag*>(Tw + ((size_t)f * 64 + l) * VE), Ops::pack(lo, hi));
         } else {
-            ws_store(reinterpret_cast<f32x4*>(Tw + ((size_t)(f * 2) * 64 + ln) * VE), f32x4{x[0], x[1], x[2], x[3]});
-            ws_store(reinterpret_cast<f32x4*>(Tw + ((size_t)(f * 2 + 1) * 64 + ln) * VE), f32x4{x[4], x[5], x[6], x[7]});
+            ws_store(reinterpret_cast<f32x4*>(Tw + ((size_t)(f * 2) * 64 + l) * VE), lo);
+            ws_store(reinterpret_cast<f32x4*>(Tw + ((size_t)(f * 2 + 1) * 64 + l) * VE), hi);
         }
     }
-    __syncthreads();   // LDS is restaged for the next item
-    cur = nxt;
-    }
+    double* rec = a.ws_g + blk * (kGateRecord / 8);
+    ws_store(rec + l, G);
+    ws_store(reinterpret_cast<float*>(rec + kChunk) + l, fast_exp2((float)G));
+    ws_store(reinterpret_cast<float*>(rec + kChunk) + kChunk + l, fast_exp2((float)(Gl - G)));
 }
 
 // ===========================================================================
@@ -1107,24 +1062,10 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
 // ===========================================================================
 template <typename OP, int DK>
 hipError_t launch_prep(const PrefillArgs& a, hipStream_t st) {
-    // persistent: as many workgroups as fit on the device at once
-    static int resident[64] = {};   // per device, filled on first use
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (resident[dev] == 0) {
-        int cus = 0, per_cu = 0;
-        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gdn_prep_kernel<OP, DK>, kPrepThreads, 0);
-        if (e != hipSuccess) return e;
-        resident[dev] = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
-    }
     const int64_t items = a.num_slots * a.hv;
-    const unsigned nwg = (unsigned)(items < resident[dev] ? items : resident[dev]);
+    const unsigned nwg = (unsigned)((items + kPrepWaves - 1) / kPrepWaves);
     if (nwg == 0) return hipSuccess;
-    hipLaunchKernelGGL((gdn_prep_kernel<OP, DK>), dim3(nwg), dim3(kPrepThreads), 0, st, a);
+    hipLaunchKernelGGL((gdn_prep_kernel<OP, DK>), dim3(nwg), dim3(kWave * kPrepWaves), 0, st, a);
     return hipGetLastError();
 }
 

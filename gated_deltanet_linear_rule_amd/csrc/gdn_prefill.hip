@@ -332,17 +332,23 @@ __global__ __launch_bounds__(kWave * kPrepWaves) void gdn_prep_kernel(PrefillArg
 // chunk kernels: one workgroup per (part, value head)
 // ===========================================================================
 // LDS row tiles: 64 rows x D elements, row-major, with the 16-byte units of row
-// r permuted by XOR with swz(r).  With it the access patterns used here are
-// free of bank conflicts for D = 128 bf16 (measured on gfx950):
-//   * 16-byte row stores (the direct loads: one row per 16 lanes),
+// r permuted by XOR with swz(r).  The pattern was chosen by measuring the LDS
+// bank-conflict counters on gfx950 for the accesses used here; with it these
+// are free of bank conflicts for D = 128 bf16:
+//   * 16-byte row stores (the direct loads: consecutive bytes of LDS),
 //   * operand fragments: lane (r, gq) reads unit k0 / 8 + gq of row r, one
-//     16-byte read (16-byte reads move twice the bytes per clock of 8-byte ones),
-//   * the LDS transpose read of a 16 x 16 tile (lane L: row L / 4).
+//     16-byte read,
+//   * the LDS transpose read of a contiguous 16 x 16 tile (lane L: row L / 4).
+// The transpose read of the K^T fragments (eight bytes from each of four
+// units of a row, all in the same half of their unit) meets each bank twice,
+// the least any layout allows for it.  (Rows 8..15 of the pattern differ from
+// rows 0..7 by XOR 8, not XOR 1: the latter makes the fragment reads of rows r
+// and r + 8 collide.)
 template <typename OP, int D>
 struct RowTile {
     static constexpr int VE = 16 / (int)sizeof(OP);    // elements per unit
     static constexpr int UPR = D / VE;                  // units per row
-    __device__ __forceinline__ static int swz(int r) { return (((r << 1) | ((r >> 3) & 1)) & 15) & (UPR - 1); }
+    __device__ __forceinline__ static int swz(int r) { return ((((r << 1) | ((r >> 3) & 1)) ^ (r & 8)) & 15) & (UPR - 1); }
     __device__ __forceinline__ static int unit(int r, int u) { return r * D + (u ^ swz(r)) * VE; }
     __device__ __forceinline__ static int elem(int r, int c) { return unit(r, c / VE) + c % VE; }
 };

@@ -59,8 +59,6 @@ constexpr int kGateRecord = kChunk * 8 + 2 * kChunk * 4;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ u32x4 zero_u4() { return u32x4{0u, 0u, 0u, 0u}; }
-
 template <typename T>
 __device__ __forceinline__ u32x4 ld16(const T* p) { return *reinterpret_cast<const u32x4*>(p); }
 
@@ -439,12 +437,6 @@ __device__ __forceinline__ void lds_frag_half(OP* base, int f, int h, const type
     const int l = lane_id();
     if constexpr (sizeof(OP) == 2) *reinterpret_cast<quad*>(base + ((size_t)f * 64 + l) * 8 + 4 * h) = x;
     else *reinterpret_cast<quad*>(base + ((size_t)(2 * f + h) * 64 + l) * 4) = x;
-}
-
-// Buffer resource over [base, base + bytes): reads past the end return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-    const int nb = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nb, 0x00020000);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -851,40 +843,64 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
     const int64_t cbase = span_base(s0, seq, kChunk);
     const unsigned kstride = (unsigned)(a.hqk * DK * E), vstride = (unsigned)(a.hv * DV * E);
 
+    // Buffer resources of chunk j (jb <= j < je).  Bases are taken once per part:
+    // chunk j's rows start (j - jb) * 64 rows after chunk jb's, its T~ fragments
+    // and gate record (j - jb) * Hv records after; only the sequence's last
+    // chunk may be partial, and its resources end at its last row, so rows past
+    // the end read as 0 and stores to them are dropped.  (Per chunk this is a
+    // few scalar adds: all eight waves compute these resources at the same
+    // point of every chunk, on scalar issue slots they share.)
+    const size_t row0 = (size_t)(s0 + jb * kChunk);
+    const char* const kB0 = static_cast<const char*>(a.k) + ((row0 * a.hqk + hq) * DK) * E;
+    const char* const qB0 = static_cast<const char*>(a.q) + ((row0 * a.hqk + hq) * DK) * E;
+    const char* const vB0 = static_cast<const char*>(a.v) + ((row0 * a.hv + h) * DV) * E;
+    char* const oB0 = static_cast<char*>(a.out) + ((row0 * a.hv + h) * DV) * E;
+    const char* const tB0 = static_cast<const char*>(a.ws_t) + ((size_t)(cbase + jb) * a.hv + h) * (kTriFrags * 64 * 8 * E);
+    const char* const gB0 = reinterpret_cast<const char*>(a.ws_g) + ((size_t)(cbase + jb) * a.hv + h) * kGateRecord;
+    const uint32_t kstep = kChunk * kstride, vstep = kChunk * vstride;
+    const uint32_t tstep = (uint32_t)a.hv * (kTriFrags * 64 * 8 * E), gstep = (uint32_t)a.hv * kGateRecord;
+    const int64_t jl = nc - 1;                                  // the sequence's last chunk
+    const int lrows = (int)(len - jl * kChunk);                  // its rows, 1 .. 64
+    const int kfull = (kChunk - 1) * (int)kstride + DK * E, klast = (lrows - 1) * (int)kstride + DK * E;
+    const int vfull = (kChunk - 1) * (int)vstride + DV * E, vlast = (lrows - 1) * (int)vstride + DV * E;
+    auto rsrc = [](const void* ptr, int bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(ptr), 0, bytes, 0x00020000);
+    };
+    auto at = [&](const char* base, uint32_t step, int64_t j) { return base + (uint64_t)(uint32_t)(j - jb) * step; };
+    auto res_k = [&](int64_t j) { return rsrc(at(kB0, kstep, j), j == jl ? klast : kfull); };
+    auto res_q = [&](int64_t j) { return rsrc(at(qB0, kstep, j), j == jl ? klast : kfull); };
+    auto res_v = [&](int64_t j) { return rsrc(at(vB0, vstep, j), j == jl ? vlast : vfull); };
+    auto res_o = [&](int64_t j) { return rsrc(at(oB0, vstep, j), j == jl ? vlast : vfull); };
+    auto res_t = [&](int64_t j) { return rsrc(at(tB0, tstep, j), UT * 1024); };
+    auto res_g = [&](int64_t j) { return rsrc(at(gB0, gstep, j), kGateRecord); };
+
     // Direct loads of chunk j's rows, T~ and gates into `B` (spread over the waves).
     auto issue = [&](int64_t j, Buf& B) {
-        const int64_t t0 = s0 + j * kChunk;
-        const int64_t nt = (len - j * kChunk) < kChunk ? (len - j * kChunk) : kChunk;
-        const size_t cblk = (size_t)(cbase + j) * a.hv + h;
-        const size_t krow = ((size_t)t0 * a.hqk + hq) * DK;
-        const auto rk = make_rsrc(static_cast<const OP*>(a.k) + krow, (nt - 1) * kstride + DK * E);
-        const auto rv = make_rsrc(static_cast<const OP*>(a.v) + ((size_t)t0 * a.hv + h) * DV, (nt - 1) * vstride + DV * E);
-        const auto rt = make_rsrc(static_cast<const OP*>(a.ws_t) + cblk * (kTriFrags * 64 * 8), UT * 1024);
-        const auto rg = make_rsrc(a.ws_g + cblk * (kGateRecord / 8), kGateRecord);
+        const auto rk = res_k(j);
 #pragma unroll
         for (int k = 0; k < (UK + NW - 1) / NW; ++k)
             if (UK % NW == 0 || w + NW * k < UK) rows_to_lds<OP, DK>(B.K, rk, kstride, w + NW * k);
         if constexpr (OUT) {
-            const auto rq = make_rsrc(static_cast<const OP*>(a.q) + krow, (nt - 1) * kstride + DK * E);
+            const auto rq = res_q(j);
 #pragma unroll
             for (int k = 0; k < (UK + NW - 1) / NW; ++k)
                 if (UK % NW == 0 || w + NW * k < UK) rows_to_lds<OP, DK>(B.Q, rq, kstride, w + NW * k);
         }
+        const auto rv = res_v(j);
 #pragma unroll
         for (int k = 0; k < (UV + NW - 1) / NW; ++k)
             if (UV % NW == 0 || w + NW * k < UV) rows_to_lds<OP, DV>(B.V, rv, vstride, w + NW * k);
+        const auto rt = res_t(j);
 #pragma unroll
         for (int k = 0; k < (UT + NW - 1) / NW; ++k)
             if (UT % NW == 0 || w + NW * k < UT) bytes_to_lds(B.T, rt, w + NW * k);
-        if (w == NW - 1) bytes_to_lds(B.G2, rg, 0);   // gate record: exactly 1 KB
+        if (w == NW - 1) bytes_to_lds(B.G2, res_g(j), 0);   // gate record: exactly 1 KB
     };
 
     // O rows of chunk j, staged in Ost, to global memory (rows past the end dropped)
-    OP* const og = static_cast<OP*>(a.out);
     auto store_o = [&](int64_t j) {
         constexpr int VU = kChunk * DV * E / 16, UPR = DV * E / 16;
-        const int64_t nt = (len - j * kChunk) < kChunk ? (len - j * kChunk) : kChunk;
-        const auto ro = make_rsrc(og + ((size_t)(s0 + j * kChunk) * a.hv + h) * DV, (nt - 1) * vstride + DV * E);
+        const auto ro = res_o(j);
         const int tid = threadIdx.x;
 #pragma unroll
         for (int k = 0; k < (VU + G::NT - 1) / G::NT; ++k) {
@@ -896,43 +912,36 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
             }
         }
     };
-    // L2 prefetch (bf16): while chunk j + 1 loads into LDS, one 4-byte load per
-    // 128-byte line of chunk j + 2 pulls that chunk into L2, so its own LDS
-    // loads, issued a chunk later, hit L2.  The loaded words are consumed two
-    // chunks later, after the wait that covers them, so these loads never hold
-    // up a chunk.  Lines: K, Q (output), V rows, T~, gate record; one 64-lane
-    // load per 64 lines of one array; every wave issues TPW loads (spare ones
-    // read out of range: no traffic).
+    // L2 prefetch (bf16 summary): while chunk j + 1 loads into LDS, one 4-byte
+    // load per 128-byte line of chunk j + 2 pulls that chunk into L2, so its
+    // own LDS loads, issued a chunk later, hit L2.  The loaded words are
+    // consumed two chunks later, after the wait that covers them, so these
+    // loads never hold up a chunk.  Lines: K, V rows, T~, gate record; one
+    // 64-lane load per 64 lines of one array; every wave issues TPW loads
+    // (spare ones read out of range: no traffic).  The output kernel does
+    // without: there the registers and scalar work cost more than it saves
+    // (measured).
     constexpr int LK = kChunk * DK * E / 128, LV = kChunk * DV * E / 128, LT = UT * 8;
     constexpr int IK = (LK + 63) / 64, IV = (LV + 63) / 64, IT = (LT + 63) / 64;
     constexpr int NI = (OUT ? 2 * IK : IK) + IV + IT + 1;
-    constexpr int TPW = NBUF == 2 ? (NI + NW - 1) / NW : 0;
+    constexpr int TPW = (NBUF == 2 && !OUT) ? (NI + NW - 1) / NW : 0;
     uint32_t tvA[TPW > 0 ? TPW : 1] = {}, tvB[TPW > 0 ? TPW : 1] = {}, sink = 0;
     auto touch = [&](int64_t j, uint32_t (&tv)[TPW > 0 ? TPW : 1]) {
-        const int64_t t0 = s0 + j * kChunk;
-        const int64_t nt = (len - j * kChunk) < kChunk ? (len - j * kChunk) : kChunk;
-        const size_t cblk = (size_t)(cbase + j) * a.hv + h;
-        const size_t krow = ((size_t)t0 * a.hqk + hq) * DK;
-        const auto rk = make_rsrc(static_cast<const OP*>(a.k) + krow, (nt - 1) * kstride + DK * E);
-        const auto rq = make_rsrc(static_cast<const OP*>(a.q) + krow, (nt - 1) * kstride + DK * E);
-        const auto rv = make_rsrc(static_cast<const OP*>(a.v) + ((size_t)t0 * a.hv + h) * DV, (nt - 1) * vstride + DV * E);
-        const auto rt = make_rsrc(static_cast<const OP*>(a.ws_t) + cblk * (kTriFrags * 64 * 8), UT * 1024);
-        const auto rg = make_rsrc(a.ws_g + cblk * (kGateRecord / 8), kGateRecord);
 #pragma unroll
         for (int k = 0; k < TPW; ++k) {
-            int slot = w + NW * k;
-            __amdgpu_buffer_rsrc_t rs = rg;
-            unsigned off = 0xFFFFF000u;   // spare: out of range
+            const int slot = w + NW * k;   // wave-uniform: one resource per load
             auto rows = [&](int sub, int lines_per_row, unsigned stride) {
                 const int li = 64 * sub + l;
-                off = (unsigned)(li / lines_per_row) * stride + (unsigned)(li % lines_per_row) * 128;
+                return (unsigned)(li / lines_per_row) * stride + (unsigned)(li % lines_per_row) * 128;
             };
-            if (slot < IK) { rs = rk; rows(slot, DK * E / 128, kstride); }
-            else if (OUT && slot < 2 * IK) { rs = rq; rows(slot - IK, DK * E / 128, kstride); }
-            else if (slot < (OUT ? 2 * IK : IK) + IV) { rs = rv; rows(slot - (OUT ? 2 * IK : IK), DV * E / 128, vstride); }
-            else if (slot < NI - 1) { rs = rt; off = (unsigned)(64 * (slot - (NI - 1 - IT)) + l) * 128; }
-            else if (slot == NI - 1) { rs = rg; off = (unsigned)l * 128; }
-            tv[k] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+            uint32_t x;
+            if (slot < IK) x = __builtin_amdgcn_raw_buffer_load_b32(res_k(j), rows(slot, DK * E / 128, kstride), 0, 0);
+            else if (OUT && slot < 2 * IK) x = __builtin_amdgcn_raw_buffer_load_b32(res_q(j), rows(slot - IK, DK * E / 128, kstride), 0, 0);
+            else if (slot < (OUT ? 2 * IK : IK) + IV)
+                x = __builtin_amdgcn_raw_buffer_load_b32(res_v(j), rows(slot - (OUT ? 2 * IK : IK), DV * E / 128, vstride), 0, 0);
+            else if (slot < NI - 1) x = __builtin_amdgcn_raw_buffer_load_b32(res_t(j), (unsigned)(64 * (slot - (NI - 1 - IT)) + l) * 128, 0, 0);
+            else x = __builtin_amdgcn_raw_buffer_load_b32(res_g(j), slot == NI - 1 ? (unsigned)l * 128 : 0xFFFFF000u, 0, 0);
+            tv[k] = x;
         }
     };
     auto consume = [&](uint32_t (&tv)[TPW > 0 ? TPW : 1]) {

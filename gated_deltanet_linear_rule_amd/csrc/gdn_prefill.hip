@@ -491,7 +491,10 @@ struct ChunkGeom {
     static constexpr int NR = OUT ? 1 : 2;
     static constexpr int NW = OUT ? DV / 16 : (DV > DK ? DV : DK) / 16;
     static constexpr int NT = NW * kWave;
-    static constexpr int NBUF = sizeof(OP) == 2 ? 2 : 1;   // fp32 rows do not fit twice
+    // input buffer sets: bf16 output 2, bf16 summary 3 (its K^T fragments are
+    // formed a chunk ahead, see gdn_chunk_kernel), fp32 1 (rows do not fit twice)
+    static constexpr int NBUF = sizeof(OP) == 2 ? (OUT ? 2 : 3) : 1;
+    static constexpr bool KTA = !OUT && sizeof(OP) == 2;   // K^T fragments one chunk ahead
 };
 
 // Row block R0 .. R0 + 15 of a row-major (rows x DK) fp32 state, as S^T tiles:
@@ -511,6 +514,20 @@ __device__ __forceinline__ void store_state(float* S, int R0, const f32x4 (&ST)[
     for (int db = 0; db < DK / 16; ++db) *reinterpret_cast<f32x4*>(S + (size_t)(R0 + n) * DK + pi_dk(db, 4 * gq)) = ST[db];
 }
 
+
+// The chunk's K^T operand fragments (2 per state tile), transposed once per
+// chunk and shared by all waves: wave w writes fragments w, w + NW, ...
+template <typename OP, int DK, int NW>
+__device__ __forceinline__ void transpose_kt(const OP* K, OP* kt, int w) {
+    constexpr int KTF = 2 * (DK / 16);
+    const int l = lane_id();
+#pragma unroll
+    for (int r = 0; r < (KTF + NW - 1) / NW; ++r) {
+        const int f = w + NW * r;
+        if (KTF % NW == 0 || f < KTF)
+            *reinterpret_cast<bf16x8*>(kt + ((size_t)f * 64 + l) * 8) = kt_frag<OP, DK>(K, f >> 1, f & 1);
+    }
+}
 
 // Keeps the compiler's scheduler from moving instructions across this point,
 // so that each group of LDS reads is issued ahead of the products that use the
@@ -532,13 +549,17 @@ __device__ __forceinline__ void sched_fence() {
 //   Y  = K S^T,  R = V - diag(gamma) Y,  U = T~ R
 //   S^T <- gamma_last S^T + K^T diag(D) U
 //   O^T = diag(gamma) (S Q^T) + U^T P^T                          (OUT)
-// Before the barrier in the middle, the wave also writes its share of the
-// chunk's K^T operand fragments (bf16) and P^T tiles (OUT); after it, it reads
-// all of them.  OUT: the O^T tiles go to the row tile `ost` (RowTile layout).
-//
-// `after_writes` runs once the wave's LDS writes of the state-free part are
-// issued: the next chunk's direct loads are issued there, since the compiler
-// orders any LDS write it cannot tell apart from their target after them.
+// Output (and fp32): before the barrier in the middle, the wave also writes
+// its share of the chunk's K^T operand fragments (bf16) and P^T tiles (OUT);
+// after it, it reads all of them.  OUT: the O^T tiles go to the row tile `ost`
+// (RowTile layout).  `after_writes` runs once the wave's LDS writes of the
+// state-free part are issued: the next chunk's direct loads are issued there,
+// since the compiler orders any LDS write it cannot tell apart from their
+// target after them.
+// bf16 summary: `kt` already holds this chunk's K^T fragments (formed during
+// the previous chunk), there is no barrier, and `after_writes` runs between U
+// and the state update (it forms the next chunk's K^T fragments and issues
+// later loads).
 template <typename OP, int DK, int DV, bool OUT, int NR, int VMASK, int NW, typename F>
 __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, OP* P, OP* kt, OP* ost,
                                            f32x4 (&ST)[NR][DK / 16], const int (&R0)[NR], int w, F&& after_writes) {
@@ -547,7 +568,7 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, 
     using quad = typename Ops::quad;
     constexpr int NDB = DK / 16, NKK = DK / 32;
     constexpr bool KT = sizeof(OP) == 2;
-    constexpr int KTF = 2 * NDB;                                // K^T fragments of the chunk
+    constexpr bool KTA = KT && !OUT;                            // kt was formed a chunk ahead
     constexpr int PT = OUT ? (2 * kTriFrags + NW - 1) / NW : 0;  // P^T tiles per wave
     const int l = lane_id(), n = l & 15, gq = l >> 4;
 
@@ -595,17 +616,14 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, 
         }
         sched_fence<!OUT>();
     }
-    if constexpr (KT) {
-#pragma unroll
-        for (int r = 0; r < (KTF + NW - 1) / NW; ++r) {
-            const int f = w + NW * r;
-            if (KTF % NW == 0 || f < KTF)
-                *reinterpret_cast<bf16x8*>(kt + ((size_t)f * 64 + l) * 8) = kt_frag<OP, DK>(cb.K, f >> 1, f & 1);
-        }
+    if constexpr (KT && !KTA) {
+        transpose_kt<OP, DK, NW>(cb.K, kt, w);
         sched_fence<!OUT>();
     }
-    after_writes();
-    sched_fence<!OUT>();
+    if constexpr (!KTA) {
+        after_writes();
+        sched_fence<!OUT>();
+    }
 
     // ---- Y = K S^T and Z = S Q^T; operands stream in groups of two token tiles
     frag Sb[NR][NKK];
@@ -710,7 +728,11 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, 
 
     // K^T fragments (bf16) and P are complete after this barrier; so is every
     // wave's read of the previous chunk's O rows.
-    if constexpr (OUT || KT) lds_barrier();
+    if constexpr (OUT || (KT && !KTA)) lds_barrier();
+    if constexpr (KTA) {   // measured best here: between U and the state update
+        after_writes();
+        sched_fence<!OUT>();
+    }
 
     // ---- S^T <- gamma_last S^T + K^T diag(D) U, operands in two groups
     constexpr int HD = NDB / 2;
@@ -781,15 +803,15 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
     constexpr int NVB = DV / 16, NMB = DK / 16, NDB = DK / 16;
     constexpr int E = (int)sizeof(OP), FU = Units<OP>::FU;
     constexpr int UK = kChunk * DK * E / 1024, UV = kChunk * DV * E / 1024, UT = kTriFrags * FU;
-    __shared__ Buf buf0;
-    __shared__ Buf buf1;
+    __shared__ Buf bufs[NBUF];
     __shared__ OP Pf[OUT ? (kTriFrags + 1) * 64 * 8 : 8];   // + one scratch fragment
     __shared__ OP Ost[OUT ? kChunk * DV : 8];   // O rows of the previous chunk (RowTile layout)
     // bf16: the chunk's K^T operand fragments (2 per state tile), transposed once
     // per chunk instead of once per wave
     constexpr bool KT = sizeof(OP) == 2;
     constexpr int KTF = 2 * (DK / 16);
-    __shared__ OP Kt[KT ? KTF * 64 * 8 : 8];
+    constexpr int KTS = KT ? KTF * 64 * 8 : 8;
+    __shared__ OP Kt[(G::KTA ? 2 : 1) * KTS];
 
     const int l = lane_id(), w = wave_id(), n = l & 15, gq = l >> 4;
     const int64_t pslot = blockIdx.x / a.hv;
@@ -975,11 +997,50 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
         }
     };
 
-    issue(jb, buf0);
-    if constexpr (TPW > 0) touch(jb + 1 < je ? jb + 1 : je - 1, tvB);
-    for (int64_t j = jb; j < je; j += NBUF) {
-        body(j, buf0, NBUF == 2 ? buf1 : buf0, tvA);
-        if (NBUF == 2 && j + 1 < je) body(j + 1, buf1, buf0, tvB);
+    if constexpr (G::KTA) {
+        // Summary, bf16: chunk j's inputs sit in buffer set (j - jb) mod 3 and
+        // its K^T fragments in Kt half j mod 2.  During chunk j the waves form chunk
+        // j + 1's K^T fragments (its rows landed before the barrier that opens
+        // chunk j) and load chunk j + 2 into the set chunk j - 1 used, so a
+        // chunk needs one barrier.
+        issue(jb, bufs[0]);
+        if (jb + 1 < je) issue(jb + 1, bufs[1]);
+        if constexpr (TPW > 0) touch(jb + 2 < je ? jb + 2 : je - 1, tvB);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        lds_barrier();
+        transpose_kt<OP, DK, NW>(bufs[0].K, Kt + (jb & 1) * KTS, w);
+        int bc = 0;                                   // buffer set of chunk j
+        auto body3 = [&](int64_t j, uint32_t (&tv)[TPW > 0 ? TPW : 1]) {
+            // chunk j + 1's rows have landed (the TPW newest loads are the L2
+            // prefetch of chunk j + 2); everyone's K^T fragments of chunk j are
+            // written and chunk j - 1 is done everywhere
+            __builtin_amdgcn_s_waitcnt(kWaitVm0 | (TPW & 15) | ((TPW >> 4) << 14));
+            lds_barrier();
+            const int b1 = bc == 2 ? 0 : bc + 1, b2 = b1 == 2 ? 0 : b1 + 1;
+            OP* const ktc = Kt + (j & 1) * KTS;
+            OP* const ktn = Kt + ((j + 1) & 1) * KTS;
+            auto ahead = [&]() {
+                if (j + 1 < je) transpose_kt<OP, DK, NW>(bufs[b1].K, ktn, w);
+                if (j + 2 < je) issue(j + 2, bufs[b2]);
+                if constexpr (TPW > 0) {
+                    consume(tv);
+                    touch(j + 3 < je ? j + 3 : je - 1, tv);
+                }
+            };
+            chunk_step<OP, DK, DV, OUT, NR, 1, NW>(bufs[bc], nullptr, ktc, nullptr, ST, R0, w, ahead);
+            bc = b1;
+        };
+        for (int64_t j = jb; j < je; j += 2) {
+            body3(j, tvA);
+            if (j + 1 < je) body3(j + 1, tvB);
+        }
+    } else {
+        issue(jb, bufs[0]);
+        if constexpr (TPW > 0) touch(jb + 1 < je ? jb + 1 : je - 1, tvB);
+        for (int64_t j = jb; j < je; j += NBUF) {
+            body(j, bufs[0], bufs[NBUF == 2 ? 1 : 0], tvA);
+            if (NBUF == 2 && j + 1 < je) body(j + 1, bufs[NBUF == 2 ? 1 : 0], bufs[0], tvB);
+        }
     }
     if constexpr (TPW > 0) {
         consume(tvA);

@@ -552,67 +552,67 @@ __device__ __forceinline__ void sched_fence() {
 // Output (and fp32): before the barrier in the middle, the wave also writes
 // its share of the chunk's K^T operand fragments (bf16) and P^T tiles (OUT);
 // after it, it reads all of them.  OUT: the O^T tiles go to the row tile `ost`
-// (RowTile layout).  `after_writes` runs once the wave's LDS writes of the
-// state-free part are issued: the next chunk's direct loads are issued there,
-// since the compiler orders any LDS write it cannot tell apart from their
-// target after them.
+// (RowTile layout).
 // bf16 summary: `kt` already holds this chunk's K^T fragments (formed during
-// the previous chunk), there is no barrier, and `after_writes` runs between U
-// and the state update (it forms the next chunk's K^T fragments and issues
-// later loads).
+// the previous chunk) and there is no barrier.
+// hook(stage) lets the caller place its other work: stage 0 once the wave's
+// LDS writes of the state-free part are issued (the next chunk's direct loads
+// go there, since the compiler orders any LDS write it cannot tell apart from
+// their target after them), stage 1 once the products of Y are issued, stage
+// 2 between U and the state update.
 template <typename OP, int DK, int DV, bool OUT, int NR, int VMASK, int NW, typename F>
 __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, OP* P, OP* kt, OP* ost,
-                                           f32x4 (&ST)[NR][DK / 16], const int (&R0)[NR], int w, F&& after_writes) {
+                                           f32x4 (&ST)[NR][DK / 16], const int (&R0)[NR], int w, F&& hook) {
     using Ops = Op<OP>;
     using frag = typename Ops::frag;
     using quad = typename Ops::quad;
     constexpr int NDB = DK / 16, NKK = DK / 32;
     constexpr bool KT = sizeof(OP) == 2;
     constexpr bool KTA = KT && !OUT;                            // kt was formed a chunk ahead
-    constexpr int PT = OUT ? (2 * kTriFrags + NW - 1) / NW : 0;  // P^T tiles per wave
     const int l = lane_id(), n = l & 15, gq = l >> 4;
 
-    // ---- state-free work of the chunk: P^T tiles and K^T fragments.  P[t][s] =
-    // Gamma_ts q_t . k_s for s <= t, as B-operand fragments (tile e: fragment
-    // e / 2, K slots 4 (e & 1) ..); every wave does PT tiles without branches,
-    // tiles past the last repeat tile 0 into a scratch fragment.
+    // ---- state-free work of the chunk: P^T fragments and K^T fragments.
+    // P[t][s] = Gamma_ts q_t . k_s for s <= t.  Wave w forms P fragments
+    // w, w + NW, ... (< 6): fragment (tb, kk) is the token tiles 2 kk and
+    // 2 kk + 1 of row tile tb, as B operand of U^T P^T (tile 2 kk + 1 lies above
+    // the diagonal, all zero, when 2 kk + 1 > tb: not computed).
     if constexpr (OUT) {
-        frag pk[PT > 0 ? PT : 1][NKK], pq[PT > 0 ? PT : 1][NKK];
-        int pf[PT > 0 ? PT : 1], ph[PT > 0 ? PT : 1], ptb[PT > 0 ? PT : 1], psb[PT > 0 ? PT : 1];
 #pragma unroll
-        for (int r = 0; r < PT; ++r) {
-            const int e = w + NW * r;
-            const bool real = e < 2 * kTriFrags;
-            const int ee = real ? e : 0;
-            int kk2;
-            tri_frag_pos(ee >> 1, ptb[r], kk2);
-            ph[r] = ee & 1;
-            psb[r] = 2 * kk2 + ph[r];
-            pf[r] = real ? (ee >> 1) : kTriFrags;
+        for (int f = w; f < kTriFrags; f += NW) {
+            int tb, kk;
+            tri_frag_pos(f, tb, kk);
+            const bool two = 2 * kk + 1 <= tb;   // wave-uniform
+            frag pq[NKK], p0[NKK], p1[NKK];
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                pk[r][kk] = rt_frag<OP, DK>(cb.K, 16 * psb[r] + n, 32 * kk);
-                pq[r][kk] = rt_frag<OP, DK>(cb.Q, 16 * ptb[r] + n, 32 * kk);
+            for (int k2 = 0; k2 < NKK; ++k2) {
+                pq[k2] = rt_frag<OP, DK>(cb.Q, 16 * tb + n, 32 * k2);
+                p0[k2] = rt_frag<OP, DK>(cb.K, 32 * kk + n, 32 * k2);
+                if (two) p1[k2] = rt_frag<OP, DK>(cb.K, 32 * kk + 16 + n, 32 * k2);
             }
-        }
-        sched_fence<!OUT>();
-#pragma unroll
-        for (int r = 0; r < PT; ++r) {
-            const int t = 16 * ptb[r] + n;
+            const int t = 16 * tb + n;
             const double gt = cb.G2[t];
-            double gs[4];
+            f32x4 a0 = zero4(), a1 = zero4();
 #pragma unroll
-            for (int i = 0; i < 4; ++i) gs[i] = cb.G2[16 * psb[r] + 4 * gq + i];
-            f32x4 acc = zero4();
+            for (int k2 = 0; k2 < NKK; ++k2) a0 = Ops::mma(p0[k2], pq[k2], a0);
+            if (two) {
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) acc = Ops::mma(pk[r][kk], pq[r][kk], acc);
-            quad pv;
+                for (int k2 = 0; k2 < NKK; ++k2) a1 = Ops::mma(p1[k2], pq[k2], a1);
+            }
+            quad v0, v1;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float x = fast_exp2((float)(gt - gs[i])) * acc[i];
-                pv[i] = from_f32<OP>(16 * psb[r] + 4 * gq + i <= t ? x : 0.f);
+                const int s0 = 32 * kk + 4 * gq + i, s1 = s0 + 16;
+                const float x0 = fast_exp2((float)(gt - cb.G2[s0])) * a0[i];
+                const float x1 = two ? fast_exp2((float)(gt - cb.G2[s1])) * a1[i] : 0.f;
+                v0[i] = from_f32<OP>(s0 <= t ? x0 : 0.f);
+                v1[i] = from_f32<OP>(s1 <= t ? x1 : 0.f);
             }
-            lds_frag_half(P, pf[r], ph[r], pv);
+            if constexpr (sizeof(OP) == 2) {
+                *reinterpret_cast<frag*>(P + ((size_t)f * 64 + l) * 8) = Ops::join(v0, v1);
+            } else {
+                lds_frag_half(P, f, 0, v0);
+                lds_frag_half(P, f, 1, v1);
+            }
         }
         sched_fence<!OUT>();
     }
@@ -620,10 +620,8 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, 
         transpose_kt<OP, DK, NW>(cb.K, kt, w);
         sched_fence<!OUT>();
     }
-    if constexpr (!KTA) {
-        after_writes();
-        sched_fence<!OUT>();
-    }
+    hook(0);
+    sched_fence<!OUT>();
 
     // ---- Y = K S^T and Z = S Q^T; operands stream in groups of two token tiles
     frag Sb[NR][NKK];
@@ -670,6 +668,8 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, 
     if constexpr (OUT) load2(g0, cb.Q, 0);
     sched_fence<!OUT>();
     mmY(g1, 2);
+    sched_fence<!OUT>();
+    hook(1);
     sched_fence<!OUT>();
     if constexpr (OUT) {
         load2(g1, cb.Q, 2);
@@ -729,10 +729,8 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, 
     // K^T fragments (bf16) and P are complete after this barrier; so is every
     // wave's read of the previous chunk's O rows.
     if constexpr (OUT || (KT && !KTA)) lds_barrier();
-    if constexpr (KTA) {   // measured best here: between U and the state update
-        after_writes();
-        sched_fence<!OUT>();
-    }
+    hook(2);
+    sched_fence<!OUT>();
 
     // ---- S^T <- gamma_last S^T + K^T diag(D) U, operands in two groups
     constexpr int HD = NDB / 2;
@@ -804,7 +802,7 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
     constexpr int E = (int)sizeof(OP), FU = Units<OP>::FU;
     constexpr int UK = kChunk * DK * E / 1024, UV = kChunk * DV * E / 1024, UT = kTriFrags * FU;
     __shared__ Buf bufs[NBUF];
-    __shared__ OP Pf[OUT ? (kTriFrags + 1) * 64 * 8 : 8];   // + one scratch fragment
+    __shared__ OP Pf[OUT ? kTriFrags * 64 * 8 : 8];
     __shared__ OP Ost[OUT ? kChunk * DV : 8];   // O rows of the previous chunk (RowTile layout)
     // bf16: the chunk's K^T operand fragments (2 per state tile), transposed once
     // per chunk instead of once per wave
@@ -979,7 +977,8 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
         if constexpr (OUT) {
             if (j > jb) store_o(j - 1);
         }
-        auto next_loads = [&]() {
+        auto next_loads = [&](int stage) {
+            if (stage != 0) return;
             if (NBUF == 2 && j + 1 < je) issue(j + 1, nxt);
             if constexpr (TPW > 0) {
                 consume(tv);
@@ -1019,7 +1018,8 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
             const int b1 = bc == 2 ? 0 : bc + 1, b2 = b1 == 2 ? 0 : b1 + 1;
             OP* const ktc = Kt + (j & 1) * KTS;
             OP* const ktn = Kt + ((j + 1) & 1) * KTS;
-            auto ahead = [&]() {
+            auto ahead = [&](int stage) {   // placed between U and the state update (measured best)
+                if (stage != 2) return;
                 if (j + 1 < je) transpose_kt<OP, DK, NW>(bufs[b1].K, ktn, w);
                 if (j + 2 < je) issue(j + 2, bufs[b2]);
                 if constexpr (TPW > 0) {

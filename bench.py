@@ -54,6 +54,12 @@ def decode_bytes(N, hqk, hv, dk, dv, elem=2):
     return 2 * N * hv * dv * dk * 4 + N * (2 * hqk * dk + 2 * hv * dv) * elem + N * hv * 8
 
 
+def decode_tokens_bytes(N, T, hqk, hv, dk, dv, elem=2, token_states=True):
+    """State read and written once, T per-token states written, T tokens of inputs and outputs."""
+    st = N * hv * dv * dk * 4
+    return 2 * st + (T * st if token_states else 0) + N * T * (2 * hqk * dk + 2 * hv * dv) * elem + N * T * hv * 8
+
+
 def _sha(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -268,6 +274,42 @@ def main():
         }
         log(f"decode: {dms * 1e3:.1f} us/step, {dgbs:.0f} GB/s")
         del state, steps, d
+        torch.cuda.empty_cache()
+
+        # multi-token decode: 256 sequences advance 4 tokens per call, with per-token states
+        m = gi.make_inputs("draft_256x4", seed=0)
+        MT = m.wl.seqlens[0]
+        mN = m.wl.num_seqs
+        mst = dev(m.init_state)
+        margs = tuple(dev(x) for x in (m.q, m.k, m.v, m.g, m.beta))
+        mout = torch.empty((mN * MT, dhv, ddv), dtype=torch.bfloat16, device="cuda")
+        mts = torch.empty((mN, MT, dhv, ddv, ddk), dtype=torch.float32, device="cuda")
+
+        def run_mt(n):
+            for _ in range(n):
+                B.gdn_decode_tokens(*margs, mst, MT, out=mout, token_states=mts)
+
+        run_mt(3)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        run_mt(20)
+        b.record(stream)
+        torch.cuda.synchronize()
+        mms = a.elapsed_time(b) / 20
+        mbytes = decode_tokens_bytes(mN, MT, dhqk, dhv, ddk, ddv)
+        mgbs = mbytes / (mms * 1e-3) / 1e9
+        assert torch.isfinite(mst).all().item()
+        decode["multi_token"] = {
+            "workload": "draft_256x4: 256 seqs x 4 tokens x 16 heads, d=128, bf16, fp32 state in place, "
+                        "per-token states written (gdn_decode_tokens)",
+            "value": round(mgbs, 1), "unit": "GB/s", "ms_per_call": round(mms, 5),
+            "tokens_per_s": round(mN * MT / (mms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(mgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(mgbs / HBM_PEAK_GBS, 4), "bytes_per_call": mbytes},
+        }
+        log(f"multi-token decode: {mms * 1e3:.1f} us/call ({MT} tokens), {mgbs:.0f} GB/s")
+        del mst, margs, mout, mts, m
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ CPU baseline

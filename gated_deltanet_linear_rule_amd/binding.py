@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_prefill.restype = ctypes.c_int
         L.gdn_decode_step.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P]
         L.gdn_decode_step.restype = ctypes.c_int
+        L.gdn_decode_tokens.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_int32, P, P, P, P, P, P, P, P, P]
+        L.gdn_decode_tokens.restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_last_error.argtypes = []
@@ -171,3 +173,35 @@ def gdn_decode_step(q, k, v, g, beta, state, out=None, stream=None):
                                _ptr(state), _ptr(out), _stream(stream))
     _raise(rc, "gdn_decode_step")
     return out
+
+
+def gdn_decode_tokens(q, k, v, g, beta, state, tokens_per_seq, out=None, token_states=None, stream=None):
+    """T = ``tokens_per_seq`` tokens per sequence in one pass; ``state`` [N, Hv, dv, dk] is updated in place.
+
+    q, k [N*T, Hqk, dk]; v [N*T, Hv, dv]; g, beta [N*T, Hv] (token t of sequence n at row n*T + t).
+    ``token_states``: None, True (allocate) or a float32 tensor [N, T, Hv, dv, dk] that receives the
+    state after every token.  Returns (out [N*T, Hv, dv], token_states or None).
+    """
+    NT, hqk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    T = int(tokens_per_seq)
+    N = state.shape[0]
+    io = _io_dtype(q)
+    _check(q, "q", q.dtype, (NT, hqk, dk))
+    _check(k, "k", q.dtype, (NT, hqk, dk))
+    _check(v, "v", q.dtype, (NT, hv, dv))
+    _check(g, "g", torch.float32, (NT, hv))
+    _check(beta, "beta", torch.float32, (NT, hv))
+    _check(state, "state", torch.float32, (N, hv, dv, dk))
+    if out is None:
+        out = torch.empty((NT, hv, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", q.dtype, (NT, hv, dv))
+    if token_states is True:
+        token_states = torch.empty((N, T, hv, dv, dk), dtype=torch.float32, device=q.device)
+    if token_states is not None:
+        _check(token_states, "token_states", torch.float32, (N, T, hv, dv, dk))
+    shape = GdnShape(N, NT, hqk, hv, dk, dv, io)
+    rc = lib().gdn_decode_tokens(ctypes.byref(shape), T, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(state), _ptr(out), _ptr(token_states), _stream(stream))
+    _raise(rc, "gdn_decode_tokens")
+    return out, token_states

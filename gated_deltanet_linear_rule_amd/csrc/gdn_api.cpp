@@ -141,11 +141,48 @@ gdn_status gdn_decode_step(const gdn_shape* shape, const void* q, const void* k,
     GDN_TRY(check_ptr(state, "state", 16, any));
     GDN_TRY(check_ptr(out, "out", 16, any));
     if (!any) return GDN_SUCCESS;
-    gdn::DecodeArgs a{q, k, v, g, beta, state, out, shape->num_seqs, shape->num_qk_heads, shape->num_v_heads};
+    gdn::DecodeArgs a{q, k, v, g, beta, state, out, shape->num_seqs, shape->num_qk_heads, shape->num_v_heads, 1,
+                      nullptr};
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = gdn::launch_decode(a, shape->dtype == GDN_DTYPE_BF16, shape->head_dim_k, shape->head_dim_v, st);
     if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return fail(GDN_ERROR_LAUNCH, "decode: %s", hipGetErrorString(e));
+    return GDN_SUCCESS;
+}
+
+gdn_status gdn_decode_tokens(const gdn_shape* shape, int32_t tokens_per_seq, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta, float* state, void* out,
+                             float* token_states, void* stream) {
+    g_last_error[0] = '\0';
+    GDN_TRY(check_shape(shape, false));
+    if (tokens_per_seq <= 0) return fail(GDN_ERROR_INVALID_VALUE, "tokens_per_seq must be positive (got %d)", tokens_per_seq);
+    if (shape->num_tokens != (int64_t)shape->num_seqs * tokens_per_seq)
+        return fail(GDN_ERROR_INVALID_VALUE, "num_tokens (%lld) must equal num_seqs * tokens_per_seq (%d * %d)",
+                    (long long)shape->num_tokens, shape->num_seqs, tokens_per_seq);
+    const bool any = shape->num_seqs > 0;
+    GDN_TRY(check_ptr(q, "q", 16, any));
+    GDN_TRY(check_ptr(k, "k", 16, any));
+    GDN_TRY(check_ptr(v, "v", 16, any));
+    GDN_TRY(check_ptr(g, "g", 4, any));
+    GDN_TRY(check_ptr(beta, "beta", 4, any));
+    GDN_TRY(check_ptr(state, "state", 16, any));
+    GDN_TRY(check_ptr(out, "out", 16, any));
+    GDN_TRY(check_ptr(token_states, "token_states", 16, false));
+    if (token_states && any) {
+        const size_t sb = (size_t)shape->num_seqs * shape->num_v_heads * shape->head_dim_v * shape->head_dim_k * 4;
+        const char* a0 = reinterpret_cast<const char*>(state);
+        const char* b0 = reinterpret_cast<const char*>(token_states);
+        if (a0 < b0 + sb * (size_t)tokens_per_seq && b0 < a0 + sb)
+            return fail(GDN_ERROR_INVALID_VALUE, "token_states overlaps state");
+    }
+    if (!any) return GDN_SUCCESS;
+    gdn::DecodeArgs a{q, k, v, g, beta, state, out, shape->num_seqs, shape->num_qk_heads, shape->num_v_heads,
+                      tokens_per_seq, token_states};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = gdn::launch_decode_tokens(a, shape->dtype == GDN_DTYPE_BF16, shape->head_dim_k,
+                                             shape->head_dim_v, st);
+    if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(GDN_ERROR_LAUNCH, "decode_tokens: %s", hipGetErrorString(e));
     return GDN_SUCCESS;
 }
 

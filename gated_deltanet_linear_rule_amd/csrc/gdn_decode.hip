@@ -1,5 +1,6 @@
-// gdn_decode.hip -- one-token GDN state update, fused into a single pass over
-// the fp32 state (HBM-bound).
+// gdn_decode.hip -- GDN state updates for decoding, fused into a single pass
+// over the fp32 state (HBM-bound): one token per sequence, or several tokens
+// per sequence with the state held in registers between them.
 //
 // Per (sequence n, value head h) with state S (d_v x d_k, fp32, row-major),
 // alpha = exp(g), and the gated delta rule expanded into its rank-1 form:
@@ -124,6 +125,100 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(DecodeArgs a) {
     }
 }
 
+// Several tokens per sequence in one pass over the state (draft verification
+// and multi-token decode): the state rows stay in the lanes' registers while
+// the T tokens of the sequence are applied in order, exactly as T single
+// steps would (same rank-1 form, same per-row order of operations).  The
+// next token's inputs are fetched while the current one is applied.  If
+// token_states is given, the state after every token is written there
+// ([N, T, Hv, dv, dk]), so that a caller can roll back to any accepted
+// prefix; the final state always goes back to `state`.  HBM traffic per
+// (n, h): the state read and written once (plus T states when requested) and
+// the T tokens' q, k, v, out, gates.
+template <typename IO, int DK, int DV>
+__global__ __launch_bounds__(256) void gdn_decode_tokens_kernel(DecodeArgs a) {
+    constexpr int LPR = 8, NJ = DK / (4 * LPR), RPP = 256 / LPR, NM = DV / RPP;
+    static_assert(NJ >= 1 && NM >= 1, "unsupported head dims");
+    const int unit = blockIdx.x;           // n * hv + h
+    const int n = unit / a.hv;
+    const int h = unit - n * a.hv;
+    const int hq = (h * a.hqk) / a.hv;
+    const int tid = threadIdx.x, sub = tid & (LPR - 1), rg = tid / LPR;
+    const int T = a.tokens;
+    float* S = a.state + (size_t)unit * DV * DK;
+
+    f32x4 s[NM][NJ];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            s[m][j] = __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4*>(S + (size_t)(rg + RPP * m) * DK + 4 * sub + 32 * j));
+
+    struct Tok {
+        float kr[4 * NJ], qr[4 * NJ], vr[NM], alpha, beta;
+    };
+    auto fetch = [&](int t, Tok& x) {
+        const size_t tok = (size_t)n * T + t;
+        const IO* qp = static_cast<const IO*>(a.q) + (tok * a.hqk + hq) * DK;
+        const IO* kp = static_cast<const IO*>(a.k) + (tok * a.hqk + hq) * DK;
+        const IO* vp = static_cast<const IO*>(a.v) + (tok * a.hv + h) * DV;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            load4<IO>(kp + 4 * sub + 32 * j, x.kr + 4 * j);
+            load4<IO>(qp + 4 * sub + 32 * j, x.qr + 4 * j);
+        }
+#pragma unroll
+        for (int m = 0; m < NM; ++m) x.vr[m] = to_f32(vp[rg + RPP * m]);
+        x.alpha = expf(a.g[tok * a.hv + h]);
+        x.beta = a.beta[tok * a.hv + h];
+    };
+
+    Tok cur, nxt;
+    fetch(0, cur);
+    for (int t = 0; t < T; ++t) {
+        if (t + 1 < T) fetch(t + 1, nxt);
+        float kq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4 * NJ; ++e) kq += cur.kr[e] * cur.qr[e];
+        kq = sum8(kq);
+        IO* op = static_cast<IO*>(a.out) + ((size_t)n * T + t) * a.hv * DV + (size_t)h * DV;
+        float* ts = a.token_states ? a.token_states + (((size_t)n * T + t) * a.hv + h) * DV * DK : nullptr;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sk += s[m][j][e] * cur.kr[4 * j + e];
+                    sq += s[m][j][e] * cur.qr[4 * j + e];
+                }
+            sk = sum8(sk);
+            sq = sum8(sq);
+            const float u = cur.beta * (cur.vr[m] - cur.alpha * sk);
+            const float o = cur.alpha * sq + kq * u;
+            const int row = rg + RPP * m;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[m][j][e] = cur.alpha * s[m][j][e] + u * cur.kr[4 * j + e];
+            if (ts) {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    __builtin_nontemporal_store(s[m][j], reinterpret_cast<f32x4*>(ts + (size_t)row * DK + 4 * sub + 32 * j));
+            }
+            if (sub == 0) op[row] = from_f32<IO>(o);
+        }
+        cur = nxt;
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            __builtin_nontemporal_store(s[m][j], reinterpret_cast<f32x4*>(S + (size_t)(rg + RPP * m) * DK + 4 * sub + 32 * j));
+}
+
 template <typename IO>
 hipError_t launch_decode_t(const DecodeArgs& a, int dk, int dv, hipStream_t st) {
     dim3 grid((unsigned)((int64_t)a.num_seqs * a.hv)), block(256);
@@ -134,7 +229,22 @@ hipError_t launch_decode_t(const DecodeArgs& a, int dk, int dv, hipStream_t st) 
     return hipGetLastError();
 }
 
+template <typename IO>
+hipError_t launch_decode_tokens_t(const DecodeArgs& a, int dk, int dv, hipStream_t st) {
+    dim3 grid((unsigned)((int64_t)a.num_seqs * a.hv)), block(256);
+    if (dk == 128 && dv == 128) hipLaunchKernelGGL((gdn_decode_tokens_kernel<IO, 128, 128>), grid, block, 0, st, a);
+    else if (dk == 128 && dv == 64) hipLaunchKernelGGL((gdn_decode_tokens_kernel<IO, 128, 64>), grid, block, 0, st, a);
+    else if (dk == 64 && dv == 128) hipLaunchKernelGGL((gdn_decode_tokens_kernel<IO, 64, 128>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((gdn_decode_tokens_kernel<IO, 64, 64>), grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_decode_tokens(const DecodeArgs& a, bool bf16, int dk, int dv, hipStream_t st) {
+    if (a.num_seqs == 0) return hipSuccess;
+    return bf16 ? launch_decode_tokens_t<__bf16>(a, dk, dv, st) : launch_decode_tokens_t<float>(a, dk, dv, st);
+}
 
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, int dk, int dv, hipStream_t st) {
     if (a.num_seqs == 0) return hipSuccess;

@@ -18,6 +18,8 @@ struct DecodeArgs {
     int32_t num_seqs;
     int32_t hqk;
     int32_t hv;
+    int32_t tokens;          // tokens per sequence (multi-token decode; 1 for a step)
+    float* token_states;     // [N, tokens, Hv, dv, dk] or nullptr (multi-token decode)
 };
 
 struct PrefillArgs {
@@ -74,6 +76,7 @@ int64_t prefill_part_chunks(int64_t num_tokens, int num_seqs, int hv, int num_cu
 // Launchers: return hipSuccess or the launch error.  `bf16` selects the
 // element type of q/k/v/out; dk/dv are 64 or 128.
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, int dk, int dv, hipStream_t s);
+hipError_t launch_decode_tokens(const DecodeArgs& a, bool bf16, int dk, int dv, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int dk, int dv, hipStream_t s);
 
 }  // namespace gdn

@@ -95,6 +95,9 @@ def _workload(cfg: str) -> Workload:
         return Workload("varlen_8x", "bf16", 16, 32, 128, 128, [], init_state="normal", packed=True)
     if cfg == "prefill_256k":
         return Workload("prefill_256k", "bf16", 16, 16, 128, 128, [262144])
+    if cfg == "draft_256x4":
+        # multi-token decode: 256 sequences advance 4 tokens each in one call
+        return Workload("draft_256x4", "bf16", 16, 16, 128, 128, [4] * 256, init_state="normal")
     if cfg == "decode_256x64":
         return Workload("decode_256x64", "bf16", 16, 16, 128, 128, [1] * 256,
                         init_state="normal", decode_steps=64)

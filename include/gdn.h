@@ -118,6 +118,33 @@ gdn_status gdn_decode_step(const gdn_shape* shape, const void* q, const void* k,
                            const float* g, const float* beta, float* state, void* out,
                            void* stream);
 
+/*
+ * gdn_decode_tokens -- advance N sequences by T tokens each in one pass over
+ * the state (multi-token decode, e.g. verifying T draft tokens).  Drafting
+ * several tokens at a time is what the model's multi-token-prediction module
+ * is for (flozi.net, "Qwen3.8-Flash-Next architecture", the stack table, draft
+ * module row); verifying them advances every GDN layer by T tokens.
+ *
+ * The result equals T successive gdn_decode_step calls on the sequences'
+ * tokens in order (the same recurrence as gdn_prefill over N sequences of T
+ * tokens), but the state is read and written once instead of T times.
+ *
+ * tokens_per_seq  T >= 1; shape->num_tokens must equal num_seqs * T.
+ * q, k            [N * T, Hqk, dk], token t of sequence n at row n * T + t.
+ * v, out          [N * T, Hv, dv];   g, beta [N * T, Hv] fp32.
+ * state           [N, Hv, dv, dk] fp32, read, then overwritten with the state
+ *                 after each sequence's last token.
+ * token_states    [N, T, Hv, dv, dk] fp32 or NULL.  If given, receives the
+ *                 state after every token (token_states[n][t] is the state
+ *                 after token t of sequence n), so that a caller that accepts
+ *                 only the first m tokens can copy token_states[n][m - 1] back
+ *                 into state.  It must not overlap state.
+ * Needs no workspace and allocates nothing.
+ */
+gdn_status gdn_decode_tokens(const gdn_shape* shape, int32_t tokens_per_seq, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta, float* state, void* out,
+                             float* token_states, void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* gdn_status_string(gdn_status status);
 

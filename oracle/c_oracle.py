@@ -104,3 +104,23 @@ def decode_step(q, k, v, g, beta, state, nthreads=0):
     if rc != 0:
         raise RuntimeError(f"gdn_oracle_decode_step failed ({rc})")
     return out
+
+
+def decode_tokens(q, k, v, g, beta, state, tokens_per_seq, nthreads=0):
+    """T tokens per sequence as T successive C decode steps (fp64).
+
+    Stored inputs as for ``decode_step`` but with N*T token rows (token t of
+    sequence n at row n*T + t); ``state`` fp32 or fp64 [N, Hv, dv, dk] (not
+    modified).  Returns (out [N*T, Hv, dv], token_states [N, T, Hv, dv, dk],
+    final [N, Hv, dv, dk]), all fp64.
+    """
+    T = int(tokens_per_seq)
+    N = state.shape[0]
+    hv, dv, dk = state.shape[1], state.shape[2], state.shape[3]
+    st = np.array(state, dtype=np.float64, copy=True, order="C")
+    out = np.empty((N * T, hv, dv), dtype=np.float64)
+    states = np.empty((N, T, hv, dv, dk), dtype=np.float64)
+    for t in range(T):
+        out[t::T] = decode_step(q[t::T], k[t::T], v[t::T], g[t::T], beta[t::T], st, nthreads=nthreads)
+        states[:, t] = st
+    return out, states, st

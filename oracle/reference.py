@@ -156,3 +156,27 @@ def decode_step(q, k, v, g, beta, state):
             new[n, h] = S
             out[n, h] = S @ qt
     return out, new
+
+
+def decode_tokens(q, k, v, g, beta, state, tokens_per_seq):
+    """T tokens per sequence, applied as T successive decode steps.
+
+    q, k [N*T, Hqk, dk]; v [N*T, Hv, dv]; g, beta [N*T, Hv], token t of
+    sequence n at row n*T + t; state [N, Hv, dv, dk].  Returns
+    (out [N*T, Hv, dv], token_states [N, T, Hv, dv, dk], final [N, Hv, dv, dk]),
+    token_states[n, t] being the state after token t.  (Several tokens per
+    sequence per call: the verification step of multi-token-prediction
+    drafting, flozi.net, "Qwen3.8-Flash-Next architecture", stack table,
+    draft-module row.)
+    """
+    T = int(tokens_per_seq)
+    N = state.shape[0]
+    hv, dv, dk = state.shape[1], state.shape[2], state.shape[3]
+    out = np.zeros((N * T, hv, dv))
+    states = np.zeros((N, T, hv, dv, dk))
+    st = np.array(state, dtype=np.float64, copy=True)
+    for t in range(T):
+        o, st = decode_step(q[t::T], k[t::T], v[t::T], g[t::T], beta[t::T], st)
+        out[t::T] = o
+        states[:, t] = st
+    return out, states, st

@@ -26,8 +26,8 @@ def _declared_functions():
 
 
 def test_header_declares_the_abi():
-    assert _declared_functions() == ["gdn_abi_version", "gdn_decode_step", "gdn_last_error",
-                                     "gdn_prefill", "gdn_status_string"]
+    assert _declared_functions() == ["gdn_abi_version", "gdn_decode_step", "gdn_decode_tokens",
+                                     "gdn_last_error", "gdn_prefill", "gdn_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -124,6 +124,39 @@ def test_prefill_with_nothing_to_do_succeeds_without_a_device():
 def test_decode_rejects_bad_arguments(shape_kw, ptrs, status, msg):
     rc, err = _decode(_shape(**shape_kw), **ptrs)
     assert rc == status and msg in err, (rc, err)
+
+
+def _decode_tokens(shape, T, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state=FAKE, out=FAKE, ts=None)
+    p.update(ptrs)
+    c = ctypes.c_void_p
+    L = _lib()
+    rc = L.gdn_decode_tokens(ctypes.byref(shape), T, c(p["q"]), c(p["k"]), c(p["v"]), c(p["g"]), c(p["beta"]),
+                             c(p["state"]), c(p["out"]), c(p["ts"]), None)
+    return rc, L.gdn_last_error().decode()
+
+
+# state of 4 sequences x 2 heads x 64 x 64 fp32 = 128 KiB
+@pytest.mark.parametrize("shape_kw,T,ptrs,status,msg", [
+    (dict(num_seqs=4, num_tokens=12), 0, {}, B.GDN_ERROR_INVALID_VALUE, "tokens_per_seq must be positive"),
+    (dict(num_seqs=4, num_tokens=12), -3, {}, B.GDN_ERROR_INVALID_VALUE, "tokens_per_seq must be positive"),
+    (dict(num_seqs=4, num_tokens=13), 3, {}, B.GDN_ERROR_INVALID_VALUE, "num_seqs * tokens_per_seq"),
+    (dict(num_seqs=4, num_tokens=12), 3, dict(state=None), B.GDN_ERROR_INVALID_VALUE, "state is NULL"),
+    (dict(num_seqs=4, num_tokens=12), 3, dict(v=None), B.GDN_ERROR_INVALID_VALUE, "v is NULL"),
+    (dict(num_seqs=4, num_tokens=12), 3, dict(ts=FAKE + 8), B.GDN_ERROR_INVALID_VALUE, "aligned"),
+    (dict(num_seqs=4, num_tokens=12), 3, dict(ts=FAKE + 65536), B.GDN_ERROR_INVALID_VALUE, "overlaps"),
+    (dict(num_seqs=4, num_tokens=12), 3, dict(ts=FAKE - 3 * 131072 + 16), B.GDN_ERROR_INVALID_VALUE, "overlaps"),
+    (dict(num_seqs=4, num_tokens=12, head_dim_v=96), 3, {}, B.GDN_ERROR_NOT_SUPPORTED, "head dims"),
+])
+def test_decode_tokens_rejects_bad_arguments(shape_kw, T, ptrs, status, msg):
+    rc, err = _decode_tokens(_shape(**shape_kw), T, **ptrs)
+    assert rc == status and msg in err, (rc, err)
+
+
+def test_decode_tokens_with_nothing_to_do_succeeds_without_a_device():
+    rc, err = _decode_tokens(_shape(num_seqs=0, num_tokens=0), 4, q=None, k=None, v=None, g=None, beta=None,
+                             state=None, out=None)
+    assert rc == B.GDN_SUCCESS and err == ""
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch):

@@ -229,3 +229,66 @@ def test_decode_256x64_workload():
     es = rel_err(host64(state), ref)
     say(f"[parity] decode_256x64: out {eo:.3e} state {es:.3e}")
     assert eo <= 1e-2 and es <= 1e-2
+
+
+# ------------------------------------------------------- multi-token decode
+def _decode_tokens_check(inp, T, tol, label, with_states=True):
+    N = inp.wl.num_seqs
+    state = dev(inp.init_state)
+    out, ts = B.gdn_decode_tokens(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), state, T,
+                                  token_states=True if with_states else None)
+    torch.cuda.synchronize()
+    ro, rs, rf = c_oracle.decode_tokens(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.init_state, T)
+    eo, ef = rel_err(host64(out), ro), rel_err(host64(state), rf)
+    et = rel_err(host64(ts), rs) if with_states else 0.0
+    say(f"[parity] {label}: out {eo:.3e} final {ef:.3e} token states {et:.3e}")
+    assert np.all(np.isfinite(host64(out)))
+    assert eo <= tol and ef <= tol and et <= tol
+    return out, ts, state
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (128, 64), (64, 128)])
+@pytest.mark.parametrize("T", [1, 2, 5, 8])
+def test_decode_tokens_small(dtype, dk, dv, T):
+    """N = 5 sequences x T tokens, grouped value heads, per-token states checked."""
+    inp = gi.make_inputs(gi.custom(dtype=dtype, Hqk=2, Hv=4, dk=dk, dv=dv, seqlens=(T,) * 5,
+                                   init_state="normal"), seed=30 + T)
+    _decode_tokens_check(inp, T, TOL[dtype], f"decode_tokens {dtype} dk={dk} dv={dv} T={T}")
+
+
+def test_decode_tokens_without_token_states_matches_with():
+    inp = gi.make_inputs(gi.custom(dtype="bf16", Hqk=2, Hv=2, dk=128, dv=128, seqlens=(6,) * 3,
+                                   init_state="normal"), seed=37)
+    o1, _, s1 = _decode_tokens_check(inp, 6, TOL["bf16"], "decode_tokens with states")
+    o2, _, s2 = _decode_tokens_check(inp, 6, TOL["bf16"], "decode_tokens without states", with_states=False)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_decode_tokens_rollback_to_accepted_prefix():
+    """Accept the first m of T drafted tokens: restoring token_states[:, m - 1] and decoding the
+    corrected token equals the oracle run over the accepted prefix plus that token."""
+    T, m = 4, 2
+    inp = gi.make_inputs(gi.custom(dtype="f32", Hqk=1, Hv=2, dk=64, dv=64, seqlens=(T,) * 3,
+                                   init_state="normal"), seed=38)
+    state = dev(inp.init_state)
+    _, ts = B.gdn_decode_tokens(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), state, T,
+                                token_states=True)
+    state = ts[:, m - 1].contiguous()
+    fix = gi.make_inputs(gi.custom(dtype="f32", Hqk=1, Hv=2, dk=64, dv=64, seqlens=(1,) * 3), seed=39)
+    out = B.gdn_decode_step(dev(fix.q), dev(fix.k), dev(fix.v), dev(fix.g), dev(fix.beta), state)
+    torch.cuda.synchronize()
+    keep = np.concatenate([np.arange(n * T, n * T + m) for n in range(3)])
+    ro, _, rf = c_oracle.decode_tokens(inp.q[keep], inp.k[keep], inp.v[keep], inp.g[keep], inp.beta[keep],
+                                       inp.init_state, m)
+    r2 = rf.copy()
+    ro2 = c_oracle.decode_step(fix.q, fix.k, fix.v, fix.g, fix.beta, r2)
+    eo, es = rel_err(host64(out), ro2), rel_err(host64(state), r2)
+    say(f"[parity] rollback to {m} of {T}: out {eo:.3e} state {es:.3e}")
+    assert eo <= TOL["f32"] and es <= TOL["f32"]
+
+
+def test_decode_tokens_draft_256x4_workload():
+    """256 sequences x 16 heads x 4 tokens, d=128, bf16, fp32 state in place, per-token states."""
+    inp = gi.make_inputs("draft_256x4", seed=0)
+    _decode_tokens_check(inp, 4, 1e-2, "draft_256x4")

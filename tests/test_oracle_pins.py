@@ -346,3 +346,35 @@ def test_state_size_is_independent_of_length():
         q, k, v, g, beta, _ = _rand(rng, T, 1, 1, 8, 4)
         shapes.add(_c_prefill(q, k, v, g, beta)[1].shape)
     assert shapes == {(1, 1, 4, 8)}
+
+
+# --------------------------------------------------------------------------
+# Multi-token decode: T decode steps per sequence.  Pinned against two other
+# routes: the literal matrix-form recurrence over packed sequences of T
+# tokens, and (per-token states) that recurrence cut after t + 1 tokens.
+def test_decode_tokens_equals_packed_sequential_and_truncations():
+    rng = np.random.default_rng(41)
+    N, T, hqk, hv, dk, dv = 3, 5, 1, 2, 4, 3
+    q, k, v, g, beta, s0 = _rand(rng, N * T, hqk, hv, dk, dv, nseq_init=N)
+    out, states, fin = ref.decode_tokens(q, k, v, g, beta, s0, T)
+    cu = np.arange(0, N * T + 1, T)
+    so, sf = ref.sequential(q, k, v, g, beta, s0, cu)
+    assert _rel(out, so) <= RTOL and _rel(fin, sf) <= RTOL
+    assert _rel(states[:, -1], sf) <= RTOL
+    for t in range(T):
+        rows = np.concatenate([np.arange(n * T, n * T + t + 1) for n in range(N)])
+        cut = np.arange(0, N * (t + 1) + 1, t + 1)
+        _, ft = ref.sequential(q[rows], k[rows], v[rows], g[rows], beta[rows], s0, cut)
+        assert _rel(states[:, t], ft) <= RTOL, t
+
+
+def test_c_decode_tokens_equals_c_prefill_and_numpy():
+    rng = np.random.default_rng(42)
+    N, T, hqk, hv, dk, dv = 4, 3, 2, 4, 8, 6
+    q, k, v, g, beta, s0 = _rand(rng, N * T, hqk, hv, dk, dv, nseq_init=N)
+    q, k, v, g, beta, s0 = _f32(q, k, v, g, beta, s0)
+    out, states, fin = c_oracle.decode_tokens(q, k, v, g, beta, s0, T)
+    po, pf = c_oracle.prefill(q, k, v, g, beta, s0, np.arange(0, N * T + 1, T))
+    assert _rel(out, po) <= RTOL and _rel(fin, pf) <= RTOL
+    ro, rs, rf = ref.decode_tokens(*(x.astype(np.float64) for x in (q, k, v, g, beta, s0)), T)
+    assert _rel(out, ro) <= RTOL and _rel(states, rs) <= RTOL and _rel(fin, rf) <= RTOL

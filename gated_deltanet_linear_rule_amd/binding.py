@@ -57,6 +57,9 @@ def lib() -> ctypes.CDLL:
         L.gdn_decode_step.restype = ctypes.c_int
         L.gdn_decode_tokens.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_int32, P, P, P, P, P, P, P, P, P]
         L.gdn_decode_tokens.restype = ctypes.c_int
+        L.gdn_decode_slots.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_int32, P, P, P, P, P, P, ctypes.c_int64,
+                                       P, P, P, P]
+        L.gdn_decode_slots.restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_last_error.argtypes = []
@@ -204,4 +207,38 @@ def gdn_decode_tokens(q, k, v, g, beta, state, tokens_per_seq, out=None, token_s
     rc = lib().gdn_decode_tokens(ctypes.byref(shape), T, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                  _ptr(state), _ptr(out), _ptr(token_states), _stream(stream))
     _raise(rc, "gdn_decode_tokens")
+    return out, token_states
+
+
+def gdn_decode_slots(q, k, v, g, beta, state_pool, slot_idx, tokens_per_seq=1, out=None, token_states=None,
+                     stream=None):
+    """``gdn_decode_tokens`` over a state pool: sequence n uses ``state_pool[slot_idx[n]]``.
+
+    state_pool float32 [P, Hv, dv, dk]; slot_idx int32 [N] on the GPU (negative = padding, skipped).
+    Returns (out [N*T, Hv, dv], token_states or None).
+    """
+    NT, hqk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    T = int(tokens_per_seq)
+    N = slot_idx.shape[0]
+    io = _io_dtype(q)
+    _check(q, "q", q.dtype, (NT, hqk, dk))
+    _check(k, "k", q.dtype, (NT, hqk, dk))
+    _check(v, "v", q.dtype, (NT, hv, dv))
+    _check(g, "g", torch.float32, (NT, hv))
+    _check(beta, "beta", torch.float32, (NT, hv))
+    _check(state_pool, "state_pool", torch.float32, (state_pool.shape[0], hv, dv, dk))
+    _check(slot_idx, "slot_idx", torch.int32, (N,))
+    if out is None:
+        out = torch.empty((NT, hv, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", q.dtype, (NT, hv, dv))
+    if token_states is True:
+        token_states = torch.empty((N, T, hv, dv, dk), dtype=torch.float32, device=q.device)
+    if token_states is not None:
+        _check(token_states, "token_states", torch.float32, (N, T, hv, dv, dk))
+    shape = GdnShape(N, NT, hqk, hv, dk, dv, io)
+    rc = lib().gdn_decode_slots(ctypes.byref(shape), T, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                _ptr(state_pool), int(state_pool.shape[0]), _ptr(slot_idx), _ptr(out),
+                                _ptr(token_states), _stream(stream))
+    _raise(rc, "gdn_decode_slots")
     return out, token_states

@@ -142,7 +142,7 @@ gdn_status gdn_decode_step(const gdn_shape* shape, const void* q, const void* k,
     GDN_TRY(check_ptr(out, "out", 16, any));
     if (!any) return GDN_SUCCESS;
     gdn::DecodeArgs a{q, k, v, g, beta, state, out, shape->num_seqs, shape->num_qk_heads, shape->num_v_heads, 1,
-                      nullptr};
+                      nullptr, nullptr, 0};
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = gdn::launch_decode(a, shape->dtype == GDN_DTYPE_BF16, shape->head_dim_k, shape->head_dim_v, st);
     if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(st);
@@ -150,9 +150,14 @@ gdn_status gdn_decode_step(const gdn_shape* shape, const void* q, const void* k,
     return GDN_SUCCESS;
 }
 
-gdn_status gdn_decode_tokens(const gdn_shape* shape, int32_t tokens_per_seq, const void* q, const void* k,
-                             const void* v, const float* g, const float* beta, float* state, void* out,
-                             float* token_states, void* stream) {
+}  // extern "C"
+
+namespace {
+
+gdn_status decode_tokens_impl(const char* who, const gdn_shape* shape, int32_t tokens_per_seq, const void* q,
+                              const void* k, const void* v, const float* g, const float* beta, float* state,
+                              int64_t pool_slots, const int32_t* slot_idx, void* out, float* token_states,
+                              void* stream) {
     g_last_error[0] = '\0';
     GDN_TRY(check_shape(shape, false));
     if (tokens_per_seq <= 0) return fail(GDN_ERROR_INVALID_VALUE, "tokens_per_seq must be positive (got %d)", tokens_per_seq);
@@ -160,30 +165,56 @@ gdn_status gdn_decode_tokens(const gdn_shape* shape, int32_t tokens_per_seq, con
         return fail(GDN_ERROR_INVALID_VALUE, "num_tokens (%lld) must equal num_seqs * tokens_per_seq (%d * %d)",
                     (long long)shape->num_tokens, shape->num_seqs, tokens_per_seq);
     const bool any = shape->num_seqs > 0;
+    const int64_t slots = slot_idx ? pool_slots : shape->num_seqs;
+    if (slot_idx && pool_slots < 0) return fail(GDN_ERROR_INVALID_VALUE, "negative pool_slots (%lld)", (long long)pool_slots);
     GDN_TRY(check_ptr(q, "q", 16, any));
     GDN_TRY(check_ptr(k, "k", 16, any));
     GDN_TRY(check_ptr(v, "v", 16, any));
     GDN_TRY(check_ptr(g, "g", 4, any));
     GDN_TRY(check_ptr(beta, "beta", 4, any));
-    GDN_TRY(check_ptr(state, "state", 16, any));
+    GDN_TRY(check_ptr(state, "state", 16, any && slots > 0));
     GDN_TRY(check_ptr(out, "out", 16, any));
+    GDN_TRY(check_ptr(slot_idx, "slot_idx", 4, false));
     GDN_TRY(check_ptr(token_states, "token_states", 16, false));
-    if (token_states && any) {
-        const size_t sb = (size_t)shape->num_seqs * shape->num_v_heads * shape->head_dim_v * shape->head_dim_k * 4;
+    if (token_states && state && any && slots > 0) {
+        const size_t sb = (size_t)shape->num_v_heads * shape->head_dim_v * shape->head_dim_k * 4;
         const char* a0 = reinterpret_cast<const char*>(state);
         const char* b0 = reinterpret_cast<const char*>(token_states);
-        if (a0 < b0 + sb * (size_t)tokens_per_seq && b0 < a0 + sb)
+        if (a0 < b0 + sb * (size_t)shape->num_seqs * tokens_per_seq && b0 < a0 + sb * (size_t)slots)
             return fail(GDN_ERROR_INVALID_VALUE, "token_states overlaps state");
     }
-    if (!any) return GDN_SUCCESS;
+    if (!any || slots == 0) return GDN_SUCCESS;
     gdn::DecodeArgs a{q, k, v, g, beta, state, out, shape->num_seqs, shape->num_qk_heads, shape->num_v_heads,
-                      tokens_per_seq, token_states};
+                      tokens_per_seq, token_states, slot_idx, pool_slots};
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = gdn::launch_decode_tokens(a, shape->dtype == GDN_DTYPE_BF16, shape->head_dim_k,
                                              shape->head_dim_v, st);
     if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(st);
-    if (e != hipSuccess) return fail(GDN_ERROR_LAUNCH, "decode_tokens: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(GDN_ERROR_LAUNCH, "%s: %s", who, hipGetErrorString(e));
     return GDN_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_decode_tokens(const gdn_shape* shape, int32_t tokens_per_seq, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta, float* state, void* out,
+                             float* token_states, void* stream) {
+    return decode_tokens_impl("decode_tokens", shape, tokens_per_seq, q, k, v, g, beta, state, 0, nullptr, out,
+                              token_states, stream);
+}
+
+gdn_status gdn_decode_slots(const gdn_shape* shape, int32_t tokens_per_seq, const void* q, const void* k,
+                            const void* v, const float* g, const float* beta, float* state_pool,
+                            int64_t pool_slots, const int32_t* slot_idx, void* out, float* token_states,
+                            void* stream) {
+    if (!slot_idx) {
+        g_last_error[0] = '\0';
+        return fail(GDN_ERROR_INVALID_VALUE, "slot_idx is NULL");
+    }
+    return decode_tokens_impl("decode_slots", shape, tokens_per_seq, q, k, v, g, beta, state_pool, pool_slots,
+                              slot_idx, out, token_states, stream);
 }
 
 gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, const void* v, const float* g,

@@ -132,7 +132,10 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(DecodeArgs a) {
 // next token's inputs are fetched while the current one is applied.  If
 // token_states is given, the state after every token is written there
 // ([N, T, Hv, dv, dk]), so that a caller can roll back to any accepted
-// prefix; the final state always goes back to `state`.  HBM traffic per
+// prefix; the final state always goes back to `state`.  With slot_idx, the
+// state of sequence n is slot slot_idx[n] of a state pool (serving engines
+// keep the states of all live requests in one pool and pass each batch's
+// slots); negative slots mark padding rows and are skipped.  HBM traffic per
 // (n, h): the state read and written once (plus T states when requested) and
 // the T tokens' q, k, v, out, gates.
 template <typename IO, int DK, int DV>
@@ -145,7 +148,12 @@ __global__ __launch_bounds__(256) void gdn_decode_tokens_kernel(DecodeArgs a) {
     const int hq = (h * a.hqk) / a.hv;
     const int tid = threadIdx.x, sub = tid & (LPR - 1), rg = tid / LPR;
     const int T = a.tokens;
-    float* S = a.state + (size_t)unit * DV * DK;
+    int64_t slot = n;
+    if (a.slot_idx) {
+        slot = a.slot_idx[n];
+        if (slot < 0 || slot >= a.pool_slots) return;   // padding entry (or out of the pool): skipped
+    }
+    float* S = a.state + ((size_t)slot * a.hv + h) * DV * DK;
 
     f32x4 s[NM][NJ];
 #pragma unroll

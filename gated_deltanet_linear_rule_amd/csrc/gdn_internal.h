@@ -20,6 +20,8 @@ struct DecodeArgs {
     int32_t hv;
     int32_t tokens;          // tokens per sequence (multi-token decode; 1 for a step)
     float* token_states;     // [N, tokens, Hv, dv, dk] or nullptr (multi-token decode)
+    const int32_t* slot_idx; // state of sequence n at state[slot_idx[n]] (nullptr: slot n)
+    int64_t pool_slots;      // slots in `state` when slot_idx is given; others are skipped
 };
 
 struct PrefillArgs {

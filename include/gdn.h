@@ -145,6 +145,28 @@ gdn_status gdn_decode_tokens(const gdn_shape* shape, int32_t tokens_per_seq, con
                              const void* v, const float* g, const float* beta, float* state, void* out,
                              float* token_states, void* stream);
 
+/*
+ * gdn_decode_slots -- gdn_decode_tokens over a pool of states.
+ *
+ * Serving engines keep the states of all live requests in one pool and pass,
+ * for every batch, which pool entry each sequence uses.  Sequence n reads and
+ * updates state_pool[slot_idx[n]] instead of state[n].
+ *
+ * state_pool   [pool_slots, Hv, dv, dk] fp32.
+ * slot_idx     DEVICE int32 [N].  Entries must be distinct, except that a
+ *              negative entry marks a padding row: that sequence is skipped
+ *              (no state touched, its out rows and token_states left as they
+ *              were).  Entries >= pool_slots are skipped the same way.
+ * token_states [N, T, Hv, dv, dk] fp32 or NULL, indexed by sequence (not by
+ *              slot).  It must not overlap the pool.
+ * The other arguments and the result are as for gdn_decode_tokens; T = 1
+ * gives a single decode step over the pool.
+ */
+gdn_status gdn_decode_slots(const gdn_shape* shape, int32_t tokens_per_seq, const void* q, const void* k,
+                            const void* v, const float* g, const float* beta, float* state_pool,
+                            int64_t pool_slots, const int32_t* slot_idx, void* out, float* token_states,
+                            void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* gdn_status_string(gdn_status status);
 

@@ -26,7 +26,7 @@ def _declared_functions():
 
 
 def test_header_declares_the_abi():
-    assert _declared_functions() == ["gdn_abi_version", "gdn_decode_step", "gdn_decode_tokens",
+    assert _declared_functions() == ["gdn_abi_version", "gdn_decode_slots", "gdn_decode_step", "gdn_decode_tokens",
                                      "gdn_last_error", "gdn_prefill", "gdn_status_string"]
 
 
@@ -156,6 +156,34 @@ def test_decode_tokens_rejects_bad_arguments(shape_kw, T, ptrs, status, msg):
 def test_decode_tokens_with_nothing_to_do_succeeds_without_a_device():
     rc, err = _decode_tokens(_shape(num_seqs=0, num_tokens=0), 4, q=None, k=None, v=None, g=None, beta=None,
                              state=None, out=None)
+    assert rc == B.GDN_SUCCESS and err == ""
+
+
+def _decode_slots(shape, T, pool_slots, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, pool=FAKE, idx=FAKE, out=FAKE, ts=None)
+    p.update(ptrs)
+    c = ctypes.c_void_p
+    L = _lib()
+    rc = L.gdn_decode_slots(ctypes.byref(shape), T, c(p["q"]), c(p["k"]), c(p["v"]), c(p["g"]), c(p["beta"]),
+                            c(p["pool"]), pool_slots, c(p["idx"]), c(p["out"]), c(p["ts"]), None)
+    return rc, L.gdn_last_error().decode()
+
+
+@pytest.mark.parametrize("T,pool,ptrs,status,msg", [
+    (1, 8, dict(idx=None), B.GDN_ERROR_INVALID_VALUE, "slot_idx is NULL"),
+    (1, 8, dict(idx=FAKE + 2), B.GDN_ERROR_INVALID_VALUE, "aligned"),
+    (1, -1, {}, B.GDN_ERROR_INVALID_VALUE, "negative pool_slots"),
+    (1, 8, dict(pool=None), B.GDN_ERROR_INVALID_VALUE, "state is NULL"),
+    (2, 8, {}, B.GDN_ERROR_INVALID_VALUE, "num_seqs * tokens_per_seq"),
+    (1, 8, dict(ts=FAKE + 7 * 32768), B.GDN_ERROR_INVALID_VALUE, "overlaps"),
+])
+def test_decode_slots_rejects_bad_arguments(T, pool, ptrs, status, msg):
+    rc, err = _decode_slots(_shape(num_seqs=4, num_tokens=4), T, pool, **ptrs)
+    assert rc == status and msg in err, (rc, err)
+
+
+def test_decode_slots_with_an_empty_pool_succeeds_without_a_device():
+    rc, err = _decode_slots(_shape(num_seqs=4, num_tokens=4), 1, 0, pool=None)
     assert rc == B.GDN_SUCCESS and err == ""
 
 

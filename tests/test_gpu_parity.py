@@ -292,3 +292,34 @@ def test_decode_tokens_draft_256x4_workload():
     """256 sequences x 16 heads x 4 tokens, d=128, bf16, fp32 state in place, per-token states."""
     inp = gi.make_inputs("draft_256x4", seed=0)
     _decode_tokens_check(inp, 4, 1e-2, "draft_256x4")
+
+
+@pytest.mark.parametrize("dtype,T", [("f32", 1), ("bf16", 3)])
+def test_decode_slots_over_a_state_pool(dtype, T):
+    """5 sequences over a pool of 7 states, one padding row (-1): used slots match the oracle run on
+    their own states, other slots and the padding row's outputs and token states stay untouched."""
+    N, P = 5, 7
+    slots = np.array([4, -1, 0, 6, 2], dtype=np.int32)
+    inp = gi.make_inputs(gi.custom(dtype=dtype, Hqk=2, Hv=4, dk=128, dv=64, seqlens=(T,) * N,
+                                   init_state="normal"), seed=40 + T)
+    pool0 = (0.1 * np.random.default_rng(5).standard_normal((P, 4, 64, 128))).astype(np.float32)
+    pool = dev(pool0)
+    out = torch.full((N * T, 4, 64), 7.0, dtype=torch.float32 if dtype == "f32" else torch.bfloat16, device="cuda")
+    ts = torch.full((N, T, 4, 64, 128), 5.0, dtype=torch.float32, device="cuda")
+    B.gdn_decode_slots(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), pool,
+                       torch.from_numpy(slots).cuda(), T, out=out, token_states=ts)
+    torch.cuda.synchronize()
+    po, o, t = host64(pool), host64(out), host64(ts)
+    live = [n for n in range(N) if slots[n] >= 0]
+    rows = np.concatenate([np.arange(n * T, n * T + T) for n in live])
+    sub = lambda a: a[rows]
+    ro, rs, rf = c_oracle.decode_tokens(sub(inp.q), sub(inp.k), sub(inp.v), sub(inp.g), sub(inp.beta),
+                                        pool0[slots[live]], T)
+    eo = rel_err(o[rows], ro)
+    es = rel_err(po[slots[live]], rf)
+    et = rel_err(t[live], rs)
+    say(f"[parity] decode_slots {dtype} T={T}: out {eo:.3e} states {es:.3e} token states {et:.3e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype] and et <= TOL[dtype]
+    for s in set(range(P)) - set(int(x) for x in slots if x >= 0):
+        assert np.array_equal(po[s], pool0[s].astype(np.float64)), s
+    assert np.all(o[T:2 * T] == 7.0) and np.all(t[1] == 5.0)

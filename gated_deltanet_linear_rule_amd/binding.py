@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_decode_slots.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_int32, P, P, P, P, P, P, ctypes.c_int64,
                                        P, P, P, P]
         L.gdn_decode_slots.restype = ctypes.c_int
+        L.gdn_prefill_snapshots.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, P]
+        L.gdn_prefill_snapshots.restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_last_error.argtypes = []
@@ -242,3 +244,45 @@ def gdn_decode_slots(q, k, v, g, beta, state_pool, slot_idx, tokens_per_seq=1, o
                                 _ptr(token_states), _stream(stream))
     _raise(rc, "gdn_decode_slots")
     return out, token_states
+
+
+def snapshot_slots(num_tokens, num_seqs, snapshot_chunks):
+    """Slots a snapshot buffer needs: floor(num_tokens / P) + num_seqs, P = 64 * snapshot_chunks."""
+    return num_tokens // (64 * snapshot_chunks) + num_seqs
+
+
+def gdn_prefill_snapshots(q, k, v, g, beta, snapshot_chunks, init_state=None, cu_seqlens=None, snapshots=None,
+                          out=None, final_state=None, stream=None, num_seqs=None):
+    """``gdn_prefill`` that also writes the state after every 64 * ``snapshot_chunks`` tokens of each
+    sequence into ``snapshots`` [slots, Hv, dv, dk] (allocated if None; see ``snapshot_slots``).
+    Returns (out, final_state, snapshots)."""
+    T, hqk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    if num_seqs is None:
+        num_seqs = (cu_seqlens.shape[0] - 1) if cu_seqlens is not None else 1
+    N = int(num_seqs)
+    io = _io_dtype(q)
+    for t, n, dt, shp in ((q, "q", q.dtype, (T, hqk, dk)), (k, "k", q.dtype, (T, hqk, dk)),
+                          (v, "v", q.dtype, (T, hv, dv)), (g, "g", torch.float32, (T, hv)),
+                          (beta, "beta", torch.float32, (T, hv))):
+        _check(t, n, dt, shp)
+    if init_state is not None:
+        _check(init_state, "init_state", torch.float32, (N, hv, dv, dk))
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
+    if out is None:
+        out = torch.empty((T, hv, dv), dtype=q.dtype, device=q.device)
+    if final_state is None:
+        final_state = torch.empty((N, hv, dv, dk), dtype=torch.float32, device=q.device)
+    if snapshots is None:
+        snapshots = torch.zeros((snapshot_slots(T, N, snapshot_chunks), hv, dv, dk), dtype=torch.float32,
+                                device=q.device)
+    _check(out, "out", q.dtype, (T, hv, dv))
+    _check(final_state, "final_state", torch.float32, (N, hv, dv, dk))
+    _check(snapshots, "snapshots", torch.float32, (snapshots.shape[0], hv, dv, dk))
+    shape = GdnShape(N, T, hqk, hv, dk, dv, io)
+    rc = lib().gdn_prefill_snapshots(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(init_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state),
+                                     int(snapshot_chunks), _ptr(snapshots), _stream(stream))
+    _raise(rc, "gdn_prefill_snapshots")
+    return out, final_state, snapshots

@@ -217,9 +217,13 @@ gdn_status gdn_decode_slots(const gdn_shape* shape, int32_t tokens_per_seq, cons
                               slot_idx, out, token_states, stream);
 }
 
-gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, const void* v, const float* g,
-                       const float* beta, const float* init_state, const int32_t* cu_seqlens, void* out,
-                       float* final_state, void* stream) {
+}  // extern "C"
+
+namespace {
+
+gdn_status prefill_impl(const char* who, const gdn_shape* shape, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, const float* init_state, const int32_t* cu_seqlens,
+                        void* out, float* final_state, int32_t snapshot_chunks, float* snapshots, void* stream) {
     g_last_error[0] = '\0';
     GDN_TRY(check_shape(shape, false));
     const bool tok = shape->num_tokens > 0;
@@ -242,10 +246,15 @@ gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, con
         if (a0 < b0 + bytes && b0 < a0 + bytes)
             return fail(GDN_ERROR_INVALID_VALUE, "init_state and final_state overlap partially");
     }
+    GDN_TRY(check_ptr(snapshots, "snapshots", 16, false));
+    if (snapshots && snapshot_chunks <= 0)
+        return fail(GDN_ERROR_INVALID_VALUE, "snapshot_chunks must be positive (got %d)", snapshot_chunks);
     if (shape->num_seqs == 0) return GDN_SUCCESS;
 
     const bool bf16 = shape->dtype == GDN_DTYPE_BF16;
     gdn::PrefillArgs a{};
+    a.snapshots = snapshots;
+    a.snap_chunks = snapshots ? snapshot_chunks : 0;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.init_state = init_state; a.cu = cu_seqlens; a.out = out; a.final_state = final_state;
     a.num_tokens = shape->num_tokens;
@@ -287,8 +296,31 @@ gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, con
     hipError_t ef = hipFreeAsync(ws, st);
     if (e == hipSuccess) e = ef;
     if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(st);
-    if (e != hipSuccess) return fail(GDN_ERROR_LAUNCH, "prefill: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(GDN_ERROR_LAUNCH, "%s: %s", who, hipGetErrorString(e));
     return GDN_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, const float* init_state, const int32_t* cu_seqlens, void* out,
+                       float* final_state, void* stream) {
+    return prefill_impl("prefill", shape, q, k, v, g, beta, init_state, cu_seqlens, out, final_state, 0, nullptr,
+                        stream);
+}
+
+gdn_status gdn_prefill_snapshots(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const float* init_state,
+                                 const int32_t* cu_seqlens, void* out, float* final_state, int32_t snapshot_chunks,
+                                 float* snapshots, void* stream) {
+    if (!snapshots) {
+        g_last_error[0] = '\0';
+        return fail(GDN_ERROR_INVALID_VALUE, "snapshots is NULL");
+    }
+    return prefill_impl("prefill_snapshots", shape, q, k, v, g, beta, init_state, cu_seqlens, out, final_state,
+                        snapshot_chunks, snapshots, stream);
 }
 
 }  // extern "C"

@@ -52,6 +52,11 @@ struct PrefillArgs {
     float* ws_m;               // d_k x d_k transition M_p of the part
     float* ws_b;               // d_v x d_k offset B_p of the part (state from zero)
     float* ws_s;               // d_v x d_k start state S_p of the part
+    // Optional state snapshots every snap_chunks chunks of each sequence:
+    // snapshot s (state after the first 64 s snap_chunks tokens) of sequence n
+    // at slot floor(start(n) / (64 snap_chunks)) + n + s - 1.
+    float* snapshots;          // [slots, Hv, dv, dk] or nullptr
+    int32_t snap_chunks;
 };
 
 // Workspace layout of one prefill call (byte offsets of each part and total),

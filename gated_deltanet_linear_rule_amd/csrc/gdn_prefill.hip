@@ -968,6 +968,8 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
 #pragma unroll
         for (int k = 0; k < TPW; ++k) sink ^= tv[k];
     };
+    // output: the next count of finished chunks at which a snapshot is due
+    int64_t next_snap = a.snapshots ? (jb / a.snap_chunks + 1) * a.snap_chunks : -1;
     auto body = [&](int64_t j, const Buf& cur, Buf& nxt, uint32_t (&tv)[TPW > 0 ? TPW : 1]) {
         // this wave's loads of chunk j have landed (the TPW newest loads are the
         // L2 prefetch of chunk j + 1)
@@ -987,6 +989,15 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
         };
         if constexpr (OUT) {
             chunk_step<OP, DK, DV, OUT, NR, 1, NW>(cur, Pf, Kt, Ost, ST, R0, w, next_loads);
+            if (a.snapshots && j + 1 == next_snap) {   // state after a full snapshot interval
+                if ((j + 1) * kChunk <= len) {
+                    const int64_t slot = span_base(s0, seq, (int64_t)a.snap_chunks * kChunk) + (j + 1) / a.snap_chunks - 1;
+#pragma unroll
+                    for (int b = 0; b < NR; ++b)
+                        store_state<DK>(a.snapshots + ((size_t)slot * a.hv + h) * DV * DK, R0[b], ST[b]);
+                }
+                next_snap += a.snap_chunks;
+            }
         } else {
             chunk_step<OP, DK, DV, OUT, NR, 1, NW>(cur, nullptr, Kt, nullptr, ST, R0, w, next_loads);
         }

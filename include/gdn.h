@@ -108,6 +108,26 @@ gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, con
                        void* stream);
 
 /*
+ * gdn_prefill_snapshots -- gdn_prefill that also writes the state at every
+ * snapshot_chunks * 64 tokens of each sequence (chunk-boundary snapshots for
+ * prefix reuse: a later request that shares the first s * P tokens of a
+ * prompt can start from snapshot s instead of recomputing them).
+ *
+ * snapshot_chunks  P / 64 >= 1, where P is the snapshot interval in tokens.
+ * snapshots        [slots, Hv, dv, dk] fp32, not NULL.  Snapshot s (s = 1 ..
+ *                  floor(len_n / P)), the state after the first s * P tokens of
+ *                  sequence n, goes to slot floor(cu[n] / P) + n + s - 1
+ *                  (cu[n] = n * len without cu_seqlens).  floor(num_tokens / P)
+ *                  + N slots always suffice; slots that hold no snapshot are
+ *                  left as they were.  It must not overlap any other argument.
+ * Everything else is as for gdn_prefill.
+ */
+gdn_status gdn_prefill_snapshots(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const float* init_state,
+                                 const int32_t* cu_seqlens, void* out, float* final_state, int32_t snapshot_chunks,
+                                 float* snapshots, void* stream);
+
+/*
  * gdn_decode_step -- advance N sequences by one token each.
  *
  * Tokens = sequences: q, k [N, Hqk, dk]; v, out [N, Hv, dv]; g, beta [N, Hv].

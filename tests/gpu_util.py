@@ -74,3 +74,20 @@ def check_prefill(inp, tol=None, label="", **kw):
     assert eo <= tol, f"out rel err {eo}"
     assert ef <= tol, f"final-state rel err {ef}"
     return eo, ef
+
+
+def oracle_snapshots(inp, P):
+    """fp64 states after every P tokens of each sequence, keyed by snapshot slot
+    floor(cu[n] / P) + n + s - 1: the oracle run on each prefix of s * P tokens
+    from the sequence's own initial state (no hand-over between runs)."""
+    T = inp.q.shape[0]
+    cu = inp.cu_seqlens if inp.cu_seqlens is not None else np.array([0, T])
+    snaps = {}
+    for n in range(len(cu) - 1):
+        a, b = int(cu[n]), int(cu[n + 1])
+        st = None if inp.init_state is None else inp.init_state[n:n + 1]
+        for s in range(1, (b - a) // P + 1):
+            t1 = a + s * P
+            _, fin = c_oracle.prefill(inp.q[a:t1], inp.k[a:t1], inp.v[a:t1], inp.g[a:t1], inp.beta[a:t1], st, None)
+            snaps[a // P + n + s - 1] = fin[0]
+    return snaps

@@ -27,7 +27,7 @@ def _declared_functions():
 
 def test_header_declares_the_abi():
     assert _declared_functions() == ["gdn_abi_version", "gdn_decode_slots", "gdn_decode_step", "gdn_decode_tokens",
-                                     "gdn_last_error", "gdn_prefill", "gdn_status_string"]
+                                     "gdn_last_error", "gdn_prefill", "gdn_prefill_snapshots", "gdn_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -185,6 +185,25 @@ def test_decode_slots_rejects_bad_arguments(T, pool, ptrs, status, msg):
 def test_decode_slots_with_an_empty_pool_succeeds_without_a_device():
     rc, err = _decode_slots(_shape(num_seqs=4, num_tokens=4), 1, 0, pool=None)
     assert rc == B.GDN_SUCCESS and err == ""
+
+
+def _prefill_snapshots(shape, chunks, snaps):
+    c = ctypes.c_void_p
+    L = _lib()
+    rc = L.gdn_prefill_snapshots(ctypes.byref(shape), c(FAKE), c(FAKE), c(FAKE), c(FAKE), c(FAKE), None, None,
+                                 c(FAKE), None, chunks, c(snaps) if snaps else None, None)
+    return rc, L.gdn_last_error().decode()
+
+
+@pytest.mark.parametrize("chunks,snaps,status,msg", [
+    (2, None, B.GDN_ERROR_INVALID_VALUE, "snapshots is NULL"),
+    (0, FAKE, B.GDN_ERROR_INVALID_VALUE, "snapshot_chunks must be positive"),
+    (-4, FAKE, B.GDN_ERROR_INVALID_VALUE, "snapshot_chunks must be positive"),
+    (2, FAKE + 4, B.GDN_ERROR_INVALID_VALUE, "aligned"),
+])
+def test_prefill_snapshots_rejects_bad_arguments(chunks, snaps, status, msg):
+    rc, err = _prefill_snapshots(_shape(), chunks, snaps)
+    assert rc == status and msg in err, (rc, err)
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch):

@@ -12,7 +12,8 @@ import torch
 from gated_deltanet_linear_rule_amd import binding as B
 from gated_deltanet_linear_rule_amd import inputs as gi
 from oracle import c_oracle
-from tests.gpu_util import TOL, check_prefill, dev, host64, rel_err, run_prefill, say
+from tests.gpu_util import (TOL, check_prefill, dev, host64, oracle_prefill, oracle_snapshots, rel_err,
+                            run_prefill, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -323,3 +324,49 @@ def test_decode_slots_over_a_state_pool(dtype, T):
     for s in set(range(P)) - set(int(x) for x in slots if x >= 0):
         assert np.array_equal(po[s], pool0[s].astype(np.float64)), s
     assert np.all(o[T:2 * T] == 7.0) and np.all(t[1] == 5.0)
+
+
+# ------------------------------------------------------- prefill snapshots
+def _check_snapshots(inp, chunks, tol, label, num_seqs=None):
+    P = 64 * chunks
+    T = inp.q.shape[0]
+    N = num_seqs or (len(inp.cu_seqlens) - 1 if inp.cu_seqlens is not None else 1)
+    slots = B.snapshot_slots(T, N, chunks)
+    snaps = torch.full((slots, inp.v.shape[1], inp.v.shape[2], inp.q.shape[2]), 3.0, dtype=torch.float32,
+                       device="cuda")
+    cu = None if inp.cu_seqlens is None or num_seqs else dev(inp.cu_seqlens)
+    out, fin, snaps = B.gdn_prefill_snapshots(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), chunks,
+                                              None if inp.init_state is None else dev(inp.init_state), cu,
+                                              snapshots=snaps, num_seqs=num_seqs)
+    torch.cuda.synchronize()
+    ro, rf = oracle_prefill(inp)
+    ref = oracle_snapshots(inp, P)
+    got = host64(snaps)
+    es = max((rel_err(got[i], r) for i, r in ref.items()), default=0.0)
+    eo, ef = rel_err(host64(out), ro), rel_err(host64(fin), rf)
+    say(f"[parity] {label}: {len(ref)} snapshots {es:.3e} out {eo:.3e} final {ef:.3e}")
+    assert len(ref) > 0 and es <= tol and eo <= tol and ef <= tol
+    for i in set(range(slots)) - set(ref):
+        assert np.all(got[i] == 3.0), i
+
+
+def test_prefill_snapshots_packed_varlen():
+    """Lengths 300, 64, 1000, 129 with a snapshot every 128 tokens (one sequence shorter than the
+    interval, one ending exactly on it), grouped value heads, bf16."""
+    inp = gi.make_inputs(gi.custom(dtype="bf16", Hqk=1, Hv=2, dk=128, dv=128, seqlens=(300, 64, 1000, 128),
+                                   init_state="normal"), seed=50)
+    _check_snapshots(inp, 2, TOL["bf16"], "snapshots varlen P=128")
+
+
+def test_prefill_snapshots_across_parts_f32():
+    """One 8192-token sequence cut into parts; a snapshot every 192 tokens, so snapshots fall on
+    both sides of part boundaries (fp32, 1e-5)."""
+    inp = gi.make_inputs(gi.custom(dtype="f32", Hqk=1, Hv=1, dk=64, dv=64, seqlens=(8192,),
+                                   init_state="normal"), seed=51)
+    _check_snapshots(inp, 3, TOL["f32"], "snapshots parts P=192")
+
+
+def test_prefill_snapshots_equal_lengths_without_offsets():
+    inp = gi.make_inputs(gi.custom(dtype="bf16", Hqk=2, Hv=2, dk=64, dv=128, seqlens=(640, 640, 640),
+                                   init_state="zero"), seed=52)
+    _check_snapshots(inp, 1, TOL["bf16"], "snapshots 3x640 P=64 no offsets", num_seqs=3)

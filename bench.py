@@ -230,6 +230,24 @@ def main():
     tflops = flops_call / (ms * 1e-3) / 1e12
     tok_s = T / (ms * 1e-3)
     traffic = measured_traffic("gdn_prefill", PREFILL_SOURCES)
+
+    # the same call with a state snapshot every 4096 tokens (prefix reuse)
+    snap_chunks = 64
+    snaps = torch.empty((B.snapshot_slots(T, 1, snap_chunks), hv, dv, dk), dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        B.gdn_prefill_snapshots(q, k, v, g, beta, snap_chunks, snapshots=snaps, out=out, final_state=fin)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(5):
+        B.gdn_prefill_snapshots(q, k, v, g, beta, snap_chunks, snapshots=snaps, out=out, final_state=fin)
+    b.record(stream)
+    torch.cuda.synchronize()
+    snap_ms = a.elapsed_time(b) / 5
+    log(f"prefill with a snapshot every {64 * snap_chunks} tokens: {snap_ms:.3f} ms/call")
+    snapshot_rec = {"workload": f"prefill_256k with a state snapshot every {64 * snap_chunks} tokens "
+                                f"({T // (64 * snap_chunks)} snapshots x 16 heads, gdn_prefill_snapshots)",
+                    "ms_per_call": round(snap_ms, 4), "tokens_per_s": round(T / (snap_ms * 1e-3), 1)}
+    del snaps
     del q, k, v, g, beta, out
     torch.cuda.empty_cache()
 
@@ -309,6 +327,28 @@ def main():
                          "frac": round(mgbs / HBM_PEAK_GBS, 4), "bytes_per_call": mbytes},
         }
         log(f"multi-token decode: {mms * 1e3:.1f} us/call ({MT} tokens), {mgbs:.0f} GB/s")
+
+        # one decode step over a pool of 512 states, the batch's 256 sequences on permuted slots
+        pool = torch.zeros((2 * mN, dhv, ddv, ddk), dtype=torch.float32, device="cuda")
+        sidx = torch.randperm(2 * mN, generator=torch.Generator().manual_seed(0))[:mN].to(torch.int32).cuda()
+        sargs = tuple(x[::MT].contiguous() for x in margs)
+        sout = torch.empty((mN, dhv, ddv), dtype=torch.bfloat16, device="cuda")
+        for _ in range(3):
+            B.gdn_decode_slots(*sargs, pool, sidx, 1, out=sout)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(20):
+            B.gdn_decode_slots(*sargs, pool, sidx, 1, out=sout)
+        b.record(stream)
+        torch.cuda.synchronize()
+        pms = a.elapsed_time(b) / 20
+        pbytes = decode_bytes(mN, dhqk, dhv, ddk, ddv)
+        decode["state_pool"] = {
+            "workload": "one decode step of 256 seqs x 16 heads over a pool of 512 states (permuted slots, "
+                        "gdn_decode_slots)",
+            "value": round(pbytes / (pms * 1e-3) / 1e9, 1), "unit": "GB/s", "ms_per_step": round(pms, 5)}
+        log(f"decode over a state pool: {pms * 1e3:.1f} us/step, {pbytes / (pms * 1e-3) / 1e9:.0f} GB/s")
+        del pool, sidx, sargs, sout
         del mst, margs, mout, mts, m
         torch.cuda.empty_cache()
 
@@ -362,6 +402,7 @@ def main():
                      "mfma_frac_of_bf16_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
         "cpu_baseline": cpu,
         "decode": decode,
+        "prefill_snapshots": snapshot_rec,
     }
     print(json.dumps(rec), flush=True)
 

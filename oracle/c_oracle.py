@@ -42,6 +42,10 @@ def _load():
                                                ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                P, P, P, P, P, P, P, ctypes.c_int]
         lib.gdn_oracle_decode_step.restype = ctypes.c_int
+        lib.gdn_oracle_prefill_raw.argtypes = lib.gdn_oracle_prefill.argtypes
+        lib.gdn_oracle_prefill_raw.restype = ctypes.c_int
+        lib.gdn_oracle_decode_step_raw.argtypes = lib.gdn_oracle_decode_step.argtypes
+        lib.gdn_oracle_decode_step_raw.restype = ctypes.c_int
         lib.gdn_oracle_threads.argtypes = [ctypes.c_int]
         lib.gdn_oracle_threads.restype = ctypes.c_int
         _lib = lib
@@ -65,9 +69,12 @@ def threads(nthreads: int = 0) -> int:
     return _load().gdn_oracle_threads(nthreads)
 
 
-def prefill(q, k, v, g, beta, init_state=None, cu=None, nthreads=0, final=True):
+def prefill(q, k, v, g, beta, init_state=None, cu=None, nthreads=0, final=True, raw=False):
     """fp64 outputs [T, Hv, dv] and final states [N, Hv, dv, dk].
 
+    raw=True: q, k are unnormalised and g, beta hold the gate and write-strength
+    logits a, b; the prologue (q, k L2-normalised, g = -softplus(a),
+    beta = sigmoid(b)) is applied per token in fp64.
     q, k, v are stored inputs (uint16 bf16 bits or float32); g, beta float32;
     init_state float32 [N, Hv, dv, dk] or None; cu int [N+1] or None.
     """
@@ -81,7 +88,8 @@ def prefill(q, k, v, g, beta, init_state=None, cu=None, nthreads=0, final=True):
     s0 = None if init_state is None else np.ascontiguousarray(init_state, dtype=np.float32)
     out = np.empty((T, hv, dv), dtype=np.float64)
     fin = np.empty((nseq, hv, dv, dk), dtype=np.float64) if final else None
-    rc = _load().gdn_oracle_prefill(nseq, _ptr(cu64), hqk, hv, dk, dv, _elem(arrs[0]),
+    fn = _load().gdn_oracle_prefill_raw if raw else _load().gdn_oracle_prefill
+    rc = fn(nseq, _ptr(cu64), hqk, hv, dk, dv, _elem(arrs[0]),
                                     _ptr(arrs[0]), _ptr(arrs[1]), _ptr(arrs[2]), _ptr(g),
                                     _ptr(beta), _ptr(s0), _ptr(out), _ptr(fin), nthreads)
     if rc != 0:
@@ -89,7 +97,7 @@ def prefill(q, k, v, g, beta, init_state=None, cu=None, nthreads=0, final=True):
     return out, fin
 
 
-def decode_step(q, k, v, g, beta, state, nthreads=0):
+def decode_step(q, k, v, g, beta, state, nthreads=0, raw=False):
     """Advance the fp64 ``state`` [N, Hv, dv, dk] in place; returns out [N, Hv, dv]."""
     N, hqk, dk = q.shape
     hv, dv = v.shape[1], v.shape[2]
@@ -98,7 +106,8 @@ def decode_step(q, k, v, g, beta, state, nthreads=0):
     g = np.ascontiguousarray(g, dtype=np.float32)
     beta = np.ascontiguousarray(beta, dtype=np.float32)
     out = np.empty((N, hv, dv), dtype=np.float64)
-    rc = _load().gdn_oracle_decode_step(N, hqk, hv, dk, dv, _elem(arrs[0]), _ptr(arrs[0]),
+    fn = _load().gdn_oracle_decode_step_raw if raw else _load().gdn_oracle_decode_step
+    rc = fn(N, hqk, hv, dk, dv, _elem(arrs[0]), _ptr(arrs[0]),
                                         _ptr(arrs[1]), _ptr(arrs[2]), _ptr(g), _ptr(beta),
                                         _ptr(state), _ptr(out), nthreads)
     if rc != 0:
@@ -106,7 +115,7 @@ def decode_step(q, k, v, g, beta, state, nthreads=0):
     return out
 
 
-def decode_tokens(q, k, v, g, beta, state, tokens_per_seq, nthreads=0):
+def decode_tokens(q, k, v, g, beta, state, tokens_per_seq, nthreads=0, raw=False):
     """T tokens per sequence as T successive C decode steps (fp64).
 
     Stored inputs as for ``decode_step`` but with N*T token rows (token t of
@@ -121,6 +130,6 @@ def decode_tokens(q, k, v, g, beta, state, tokens_per_seq, nthreads=0):
     out = np.empty((N * T, hv, dv), dtype=np.float64)
     states = np.empty((N, T, hv, dv, dk), dtype=np.float64)
     for t in range(T):
-        out[t::T] = decode_step(q[t::T], k[t::T], v[t::T], g[t::T], beta[t::T], st, nthreads=nthreads)
+        out[t::T] = decode_step(q[t::T], k[t::T], v[t::T], g[t::T], beta[t::T], st, nthreads=nthreads, raw=raw)
         states[:, t] = st
     return out, states, st

@@ -38,6 +38,16 @@
  *
  * Parallelism: independent chains (sequence, value head) only; the token loop
  * of a chain is strictly sequential.
+ *
+ * Raw-projection variants (..._raw): the steps just before the recurrence are
+ * applied per token, in fp64, before the same token step:
+ *     q <- q / sqrt(|q|^2 + 1e-6),   k <- k / sqrt(|k|^2 + 1e-6),
+ *     g  = -softplus(a) = -(max(a, 0) + log1p(exp(-|a|))),
+ *     beta = 1 / (1 + exp(-b)),
+ * where a and b are the per-(token, value head) gate and write-strength
+ * logits passed in place of g and beta.  (The pages give the model's layer
+ * layout but none of these formulas; these are the usual forms, matching the
+ * value distributions of the synthetic inputs.)
  */
 #include <math.h>
 #include <stdint.h>
@@ -77,6 +87,18 @@ static void gdn_token(double* S, int dk, int dv, const double* kt, const double*
     }
 }
 
+static const double kNormEps = 1e-6;
+
+/* The prologue of the raw-projection variants, in place. */
+static void normalise(double* x, int d) {
+    double s2 = 0.0;
+    for (int j = 0; j < d; ++j) s2 += x[j] * x[j];
+    const double inv = 1.0 / sqrt(s2 + kNormEps);
+    for (int j = 0; j < d; ++j) x[j] *= inv;
+}
+static double gate_from_logit(double a) { return -((a > 0.0 ? a : 0.0) + log1p(exp(-fabs(a)))); }
+static double beta_from_logit(double b) { return 1.0 / (1.0 + exp(-b)); }
+
 static int max_threads(int nthreads) {
 #ifdef _OPENMP
     return nthreads > 0 ? nthreads : omp_get_max_threads();
@@ -89,10 +111,10 @@ static int max_threads(int nthreads) {
 int gdn_oracle_threads(int nthreads) { return max_threads(nthreads); }
 
 /* Prefill: every sequence from its initial state, outputs for every token. */
-int gdn_oracle_prefill(int64_t nseq, const int64_t* cu, int hqk, int hv, int dk, int dv,
-                       int elem, const void* q, const void* k, const void* v, const float* g,
-                       const float* beta, const float* init_state, double* out,
-                       double* final_state, int nthreads) {
+static int prefill(int raw, int64_t nseq, const int64_t* cu, int hqk, int hv, int dk, int dv,
+                   int elem, const void* q, const void* k, const void* v, const float* g,
+                   const float* beta, const float* init_state, double* out,
+                   double* final_state, int nthreads) {
     if (nseq < 0 || hqk <= 0 || hv <= 0 || dk <= 0 || dv <= 0 || hv % hqk != 0) return 1;
     int64_t nchain = nseq * hv;
     int err = 0;
@@ -122,8 +144,14 @@ int gdn_oracle_prefill(int64_t nseq, const int64_t* cu, int hqk, int hv, int dk,
                 qt[j] = widen(q, (t * hqk + hq) * dk + j, elem);
             }
             for (int i = 0; i < dv; ++i) vt[i] = widen(v, (t * hv + h) * dv + i, elem);
-            double alpha = exp((double)g[t * hv + h]);
-            gdn_token(S, dk, dv, kt, qt, vt, alpha, (double)beta[t * hv + h], s, u, ot);
+            double gt = (double)g[t * hv + h], bt = (double)beta[t * hv + h];
+            if (raw) {
+                normalise(kt, dk);
+                normalise(qt, dk);
+                gt = gate_from_logit(gt);
+                bt = beta_from_logit(bt);
+            }
+            gdn_token(S, dk, dv, kt, qt, vt, exp(gt), bt, s, u, ot);
             memcpy(out + (t * hv + h) * dv, ot, sizeof(double) * dv);
         }
         if (final_state) memcpy(final_state + sbase, S, sizeof(double) * (size_t)dv * dk);
@@ -134,9 +162,9 @@ int gdn_oracle_prefill(int64_t nseq, const int64_t* cu, int hqk, int hv, int dk,
 }
 
 /* Decode: one token per sequence, fp64 state [N, Hv, dv, dk] updated in place. */
-int gdn_oracle_decode_step(int64_t nseq, int hqk, int hv, int dk, int dv, int elem,
-                           const void* q, const void* k, const void* v, const float* g,
-                           const float* beta, double* state, double* out, int nthreads) {
+static int decode_step(int raw, int64_t nseq, int hqk, int hv, int dk, int dv, int elem,
+                       const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, double* state, double* out, int nthreads) {
     if (nseq < 0 || hqk <= 0 || hv <= 0 || dk <= 0 || dv <= 0 || hv % hqk != 0) return 1;
     int64_t nchain = nseq * hv;
     int err = 0;
@@ -159,11 +187,45 @@ int gdn_oracle_decode_step(int64_t nseq, int hqk, int hv, int dk, int dv, int el
             qt[j] = widen(q, (n * hqk + hq) * dk + j, elem);
         }
         for (int i = 0; i < dv; ++i) vt[i] = widen(v, (n * hv + h) * dv + i, elem);
-        double alpha = exp((double)g[n * hv + h]);
-        gdn_token(state + c * (int64_t)dv * dk, dk, dv, kt, qt, vt, alpha,
-                  (double)beta[n * hv + h], s, u, ot);
+        double gt = (double)g[n * hv + h], bt = (double)beta[n * hv + h];
+        if (raw) {
+            normalise(kt, dk);
+            normalise(qt, dk);
+            gt = gate_from_logit(gt);
+            bt = beta_from_logit(bt);
+        }
+        gdn_token(state + c * (int64_t)dv * dk, dk, dv, kt, qt, vt, exp(gt), bt, s, u, ot);
         memcpy(out + c * dv, ot, sizeof(double) * dv);
         free(buf);
     }
     return err;
+}
+
+int gdn_oracle_prefill(int64_t nseq, const int64_t* cu, int hqk, int hv, int dk, int dv,
+                       int elem, const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, const float* init_state, double* out,
+                       double* final_state, int nthreads) {
+    return prefill(0, nseq, cu, hqk, hv, dk, dv, elem, q, k, v, g, beta, init_state, out,
+                   final_state, nthreads);
+}
+
+/* a, b: gate and write-strength logits in place of g, beta; q, k unnormalised. */
+int gdn_oracle_prefill_raw(int64_t nseq, const int64_t* cu, int hqk, int hv, int dk, int dv,
+                           int elem, const void* q, const void* k, const void* v, const float* a,
+                           const float* b, const float* init_state, double* out,
+                           double* final_state, int nthreads) {
+    return prefill(1, nseq, cu, hqk, hv, dk, dv, elem, q, k, v, a, b, init_state, out,
+                   final_state, nthreads);
+}
+
+int gdn_oracle_decode_step(int64_t nseq, int hqk, int hv, int dk, int dv, int elem,
+                           const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, double* state, double* out, int nthreads) {
+    return decode_step(0, nseq, hqk, hv, dk, dv, elem, q, k, v, g, beta, state, out, nthreads);
+}
+
+int gdn_oracle_decode_step_raw(int64_t nseq, int hqk, int hv, int dk, int dv, int elem,
+                               const void* q, const void* k, const void* v, const float* a,
+                               const float* b, double* state, double* out, int nthreads) {
+    return decode_step(1, nseq, hqk, hv, dk, dv, elem, q, k, v, a, b, state, out, nthreads);
 }

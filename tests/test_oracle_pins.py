@@ -378,3 +378,58 @@ def test_c_decode_tokens_equals_c_prefill_and_numpy():
     assert _rel(out, po) <= RTOL and _rel(fin, pf) <= RTOL
     ro, rs, rf = ref.decode_tokens(*(x.astype(np.float64) for x in (q, k, v, g, beta, s0)), T)
     assert _rel(out, ro) <= RTOL and _rel(states, rs) <= RTOL and _rel(fin, rf) <= RTOL
+
+
+# --------------------------------------------------------------------------
+# Raw-projection prologue (q, k L2-normalised, g = -softplus(a), beta = sigmoid(b)).
+def _raw_inputs(rng, T, hqk, hv, dk, dv):
+    q = 3.0 * rng.standard_normal((T, hqk, dk))
+    k = 0.7 * rng.standard_normal((T, hqk, dk))
+    v = rng.standard_normal((T, hv, dv))
+    a = rng.standard_normal((T, hv))
+    b = rng.standard_normal((T, hv))
+    return _f32(q, k, v, a, b)
+
+
+def test_raw_prologue_is_invariant_to_the_scale_of_q_and_k():
+    rng = np.random.default_rng(60)
+    q, k, v, a, b = _raw_inputs(rng, 40, 1, 2, 8, 4)
+    o1, f1 = c_oracle.prefill(q, k, v, a, b, raw=True)
+    o2, f2 = c_oracle.prefill((q * 0.25).astype(np.float32), (k * 4.0).astype(np.float32), v, a, b, raw=True)
+    assert _rel(o2, o1) <= 1e-6 and _rel(f2, f1) <= 1e-6
+
+
+def test_raw_prologue_at_zero_logits_is_half_decay_and_half_write():
+    """a = b = 0: alpha = exp(-ln 2) = 1/2 and beta = 1/2 exactly; unit-norm q, k stay unit up to the
+    1e-6 guard, so the result is the plain recurrence with g = -ln 2, beta = 1/2."""
+    rng = np.random.default_rng(61)
+    q, k, v, g, beta, _ = _rand(rng, 30, 1, 2, 8, 4)
+    q, k, v = _f32(q, k, v)
+    z = np.zeros((30, 2), dtype=np.float32)
+    o1, f1 = c_oracle.prefill(q, k, v, z, z, raw=True)
+    o2, f2 = ref.sequential(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                            np.full((30, 2), -math.log(2.0)), np.full((30, 2), 0.5))
+    assert _rel(o1, o2) <= 1e-5 and _rel(f1, f2) <= 1e-5
+
+
+def test_raw_prologue_saturated_logits_give_no_decay_and_full_write():
+    """a -> -inf gives alpha -> 1, b -> +inf gives beta -> 1."""
+    rng = np.random.default_rng(62)
+    q, k, v, _, _, _ = _rand(rng, 20, 1, 1, 8, 3)
+    q, k, v = _f32(q, k, v)
+    a = np.full((20, 1), -60.0, dtype=np.float32)
+    b = np.full((20, 1), 60.0, dtype=np.float32)
+    o1, f1 = c_oracle.prefill(q, k, v, a, b, raw=True)
+    o2, f2 = ref.sequential(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                            np.zeros((20, 1)), np.ones((20, 1)))
+    assert _rel(o1, o2) <= 1e-5 and _rel(f1, f2) <= 1e-5
+
+
+def test_raw_decode_tokens_equals_raw_prefill():
+    rng = np.random.default_rng(63)
+    N, T = 3, 4
+    q, k, v, a, b = _raw_inputs(rng, N * T, 2, 4, 8, 6)
+    s0 = (0.1 * rng.standard_normal((N, 4, 6, 8))).astype(np.float32)
+    o1, _, f1 = c_oracle.decode_tokens(q, k, v, a, b, s0, T, raw=True)
+    o2, f2 = c_oracle.prefill(q, k, v, a, b, s0, np.arange(0, N * T + 1, T), raw=True)
+    assert _rel(o1, o2) <= RTOL and _rel(f1, f2) <= RTOL

@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
         L.gdn_decode_slots.restype = ctypes.c_int
         L.gdn_prefill_snapshots.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, P]
         L.gdn_prefill_snapshots.restype = ctypes.c_int
+        L.gdn_prefill_raw.argtypes = L.gdn_prefill.argtypes
+        L.gdn_prefill_raw.restype = ctypes.c_int
+        L.gdn_decode_tokens_raw.argtypes = L.gdn_decode_tokens.argtypes
+        L.gdn_decode_tokens_raw.restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_last_error.argtypes = []
@@ -120,13 +124,14 @@ def _raise(rc, where):
 
 
 def gdn_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, out=None, final_state=None,
-                stream=None, num_seqs=None, return_final_state=True):
+                stream=None, num_seqs=None, return_final_state=True, raw=False):
     """Chunked GDN prefill over packed sequences.
 
     q, k [T, Hqk, dk]; v [T, Hv, dv] (bf16 or fp32, same dtype); g, beta [T, Hv]
     fp32; init_state [N, Hv, dv, dk] fp32 or None; cu_seqlens int32 [N+1] on
     the GPU or None (then ``num_seqs`` equal-length sequences, default 1).
     Returns (out, final_state); final_state is None if not requested.
+    raw=True calls gdn_prefill_raw: q, k unnormalised, g and beta are the logits a, b.
     """
     T, hqk, dk = q.shape
     hv, dv = v.shape[1], v.shape[2]
@@ -149,10 +154,10 @@ def gdn_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, out=None, fi
         final_state = torch.empty((N, hv, dv, dk), dtype=torch.float32, device=q.device)
     _check(final_state, "final_state", torch.float32, (N, hv, dv, dk))
     shape = GdnShape(N, T, hqk, hv, dk, dv, io)
-    rc = lib().gdn_prefill(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                           _ptr(init_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state),
-                           _stream(stream))
-    _raise(rc, "gdn_prefill")
+    fn = lib().gdn_prefill_raw if raw else lib().gdn_prefill
+    rc = fn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+            _ptr(init_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state), _stream(stream))
+    _raise(rc, "gdn_prefill_raw" if raw else "gdn_prefill")
     return out, final_state
 
 
@@ -180,12 +185,14 @@ def gdn_decode_step(q, k, v, g, beta, state, out=None, stream=None):
     return out
 
 
-def gdn_decode_tokens(q, k, v, g, beta, state, tokens_per_seq, out=None, token_states=None, stream=None):
+def gdn_decode_tokens(q, k, v, g, beta, state, tokens_per_seq, out=None, token_states=None, stream=None,
+                      raw=False):
     """T = ``tokens_per_seq`` tokens per sequence in one pass; ``state`` [N, Hv, dv, dk] is updated in place.
 
     q, k [N*T, Hqk, dk]; v [N*T, Hv, dv]; g, beta [N*T, Hv] (token t of sequence n at row n*T + t).
     ``token_states``: None, True (allocate) or a float32 tensor [N, T, Hv, dv, dk] that receives the
     state after every token.  Returns (out [N*T, Hv, dv], token_states or None).
+    raw=True calls gdn_decode_tokens_raw: q, k unnormalised, g and beta are the logits a, b.
     """
     NT, hqk, dk = q.shape
     hv, dv = v.shape[1], v.shape[2]
@@ -206,9 +213,10 @@ def gdn_decode_tokens(q, k, v, g, beta, state, tokens_per_seq, out=None, token_s
     if token_states is not None:
         _check(token_states, "token_states", torch.float32, (N, T, hv, dv, dk))
     shape = GdnShape(N, NT, hqk, hv, dk, dv, io)
-    rc = lib().gdn_decode_tokens(ctypes.byref(shape), T, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                 _ptr(state), _ptr(out), _ptr(token_states), _stream(stream))
-    _raise(rc, "gdn_decode_tokens")
+    fn = lib().gdn_decode_tokens_raw if raw else lib().gdn_decode_tokens
+    rc = fn(ctypes.byref(shape), T, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+            _ptr(state), _ptr(out), _ptr(token_states), _stream(stream))
+    _raise(rc, "gdn_decode_tokens_raw" if raw else "gdn_decode_tokens")
     return out, token_states
 
 

@@ -157,7 +157,7 @@ namespace {
 gdn_status decode_tokens_impl(const char* who, const gdn_shape* shape, int32_t tokens_per_seq, const void* q,
                               const void* k, const void* v, const float* g, const float* beta, float* state,
                               int64_t pool_slots, const int32_t* slot_idx, void* out, float* token_states,
-                              void* stream) {
+                              void* stream, bool raw = false) {
     g_last_error[0] = '\0';
     GDN_TRY(check_shape(shape, false));
     if (tokens_per_seq <= 0) return fail(GDN_ERROR_INVALID_VALUE, "tokens_per_seq must be positive (got %d)", tokens_per_seq);
@@ -188,7 +188,7 @@ gdn_status decode_tokens_impl(const char* who, const gdn_shape* shape, int32_t t
                       tokens_per_seq, token_states, slot_idx, pool_slots};
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = gdn::launch_decode_tokens(a, shape->dtype == GDN_DTYPE_BF16, shape->head_dim_k,
-                                             shape->head_dim_v, st);
+                                             shape->head_dim_v, st, raw);
     if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return fail(GDN_ERROR_LAUNCH, "%s: %s", who, hipGetErrorString(e));
     return GDN_SUCCESS;
@@ -217,13 +217,21 @@ gdn_status gdn_decode_slots(const gdn_shape* shape, int32_t tokens_per_seq, cons
                               slot_idx, out, token_states, stream);
 }
 
+gdn_status gdn_decode_tokens_raw(const gdn_shape* shape, int32_t tokens_per_seq, const void* q, const void* k,
+                                 const void* v, const float* a_gate, const float* b_beta, float* state, void* out,
+                                 float* token_states, void* stream) {
+    return decode_tokens_impl("decode_tokens_raw", shape, tokens_per_seq, q, k, v, a_gate, b_beta, state, 0,
+                              nullptr, out, token_states, stream, true);
+}
+
 }  // extern "C"
 
 namespace {
 
 gdn_status prefill_impl(const char* who, const gdn_shape* shape, const void* q, const void* k, const void* v,
                         const float* g, const float* beta, const float* init_state, const int32_t* cu_seqlens,
-                        void* out, float* final_state, int32_t snapshot_chunks, float* snapshots, void* stream) {
+                        void* out, float* final_state, int32_t snapshot_chunks, float* snapshots, void* stream,
+                        bool raw = false) {
     g_last_error[0] = '\0';
     GDN_TRY(check_shape(shape, false));
     const bool tok = shape->num_tokens > 0;
@@ -292,7 +300,7 @@ gdn_status prefill_impl(const char* who, const gdn_shape* shape, const void* q, 
     a.ws_m = split ? reinterpret_cast<float*>(wc + wl.m) : nullptr;
     a.ws_b = split ? reinterpret_cast<float*>(wc + wl.b) : nullptr;
     a.ws_s = split ? reinterpret_cast<float*>(wc + wl.s) : nullptr;
-    hipError_t e = gdn::launch_prefill(a, bf16, shape->head_dim_k, shape->head_dim_v, st);
+    hipError_t e = gdn::launch_prefill(a, bf16, shape->head_dim_k, shape->head_dim_v, st, raw);
     hipError_t ef = hipFreeAsync(ws, st);
     if (e == hipSuccess) e = ef;
     if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(st);
@@ -321,6 +329,13 @@ gdn_status gdn_prefill_snapshots(const gdn_shape* shape, const void* q, const vo
     }
     return prefill_impl("prefill_snapshots", shape, q, k, v, g, beta, init_state, cu_seqlens, out, final_state,
                         snapshot_chunks, snapshots, stream);
+}
+
+gdn_status gdn_prefill_raw(const gdn_shape* shape, const void* q, const void* k, const void* v, const float* a_gate,
+                           const float* b_beta, const float* init_state, const int32_t* cu_seqlens, void* out,
+                           float* final_state, void* stream) {
+    return prefill_impl("prefill_raw", shape, q, k, v, a_gate, b_beta, init_state, cu_seqlens, out, final_state, 0,
+                        nullptr, stream, true);
 }
 
 }  // extern "C"

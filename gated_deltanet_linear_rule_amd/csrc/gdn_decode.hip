@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(DecodeArgs a) {
 // slots); negative slots mark padding rows and are skipped.  HBM traffic per
 // (n, h): the state read and written once (plus T states when requested) and
 // the T tokens' q, k, v, out, gates.
-template <typename IO, int DK, int DV>
+template <typename IO, int DK, int DV, bool RAW>
 __global__ __launch_bounds__(256) void gdn_decode_tokens_kernel(DecodeArgs a) {
     constexpr int LPR = 8, NJ = DK / (4 * LPR), RPP = 256 / LPR, NM = DV / RPP;
     static_assert(NJ >= 1 && NM >= 1, "unsupported head dims");
@@ -178,8 +178,25 @@ __global__ __launch_bounds__(256) void gdn_decode_tokens_kernel(DecodeArgs a) {
         }
 #pragma unroll
         for (int m = 0; m < NM; ++m) x.vr[m] = to_f32(vp[rg + RPP * m]);
-        x.alpha = expf(a.g[tok * a.hv + h]);
-        x.beta = a.beta[tok * a.hv + h];
+        if constexpr (RAW) {   // the eight lanes of a row group hold all of k and q
+            float kk2 = 0.f, qq2 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4 * NJ; ++e) {
+                kk2 += x.kr[e] * x.kr[e];
+                qq2 += x.qr[e] * x.qr[e];
+            }
+            const float ik = 1.f / sqrtf(sum8(kk2) + kNormEps), iq = 1.f / sqrtf(sum8(qq2) + kNormEps);
+#pragma unroll
+            for (int e = 0; e < 4 * NJ; ++e) {
+                x.kr[e] *= ik;
+                x.qr[e] *= iq;
+            }
+            x.alpha = expf(gate_from_logit(a.g[tok * a.hv + h]));
+            x.beta = beta_from_logit(a.beta[tok * a.hv + h]);
+        } else {
+            x.alpha = expf(a.g[tok * a.hv + h]);
+            x.beta = a.beta[tok * a.hv + h];
+        }
     };
 
     Tok cur, nxt;
@@ -237,21 +254,23 @@ hipError_t launch_decode_t(const DecodeArgs& a, int dk, int dv, hipStream_t st) 
     return hipGetLastError();
 }
 
-template <typename IO>
+template <typename IO, bool RAW>
 hipError_t launch_decode_tokens_t(const DecodeArgs& a, int dk, int dv, hipStream_t st) {
     dim3 grid((unsigned)((int64_t)a.num_seqs * a.hv)), block(256);
-    if (dk == 128 && dv == 128) hipLaunchKernelGGL((gdn_decode_tokens_kernel<IO, 128, 128>), grid, block, 0, st, a);
-    else if (dk == 128 && dv == 64) hipLaunchKernelGGL((gdn_decode_tokens_kernel<IO, 128, 64>), grid, block, 0, st, a);
-    else if (dk == 64 && dv == 128) hipLaunchKernelGGL((gdn_decode_tokens_kernel<IO, 64, 128>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((gdn_decode_tokens_kernel<IO, 64, 64>), grid, block, 0, st, a);
+    if (dk == 128 && dv == 128) hipLaunchKernelGGL((gdn_decode_tokens_kernel<IO, 128, 128, RAW>), grid, block, 0, st, a);
+    else if (dk == 128 && dv == 64) hipLaunchKernelGGL((gdn_decode_tokens_kernel<IO, 128, 64, RAW>), grid, block, 0, st, a);
+    else if (dk == 64 && dv == 128) hipLaunchKernelGGL((gdn_decode_tokens_kernel<IO, 64, 128, RAW>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((gdn_decode_tokens_kernel<IO, 64, 64, RAW>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode_tokens(const DecodeArgs& a, bool bf16, int dk, int dv, hipStream_t st) {
+hipError_t launch_decode_tokens(const DecodeArgs& a, bool bf16, int dk, int dv, hipStream_t st, bool raw) {
     if (a.num_seqs == 0) return hipSuccess;
-    return bf16 ? launch_decode_tokens_t<__bf16>(a, dk, dv, st) : launch_decode_tokens_t<float>(a, dk, dv, st);
+    if (raw)
+        return bf16 ? launch_decode_tokens_t<__bf16, true>(a, dk, dv, st) : launch_decode_tokens_t<float, true>(a, dk, dv, st);
+    return bf16 ? launch_decode_tokens_t<__bf16, false>(a, dk, dv, st) : launch_decode_tokens_t<float, false>(a, dk, dv, st);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, int dk, int dv, hipStream_t st) {

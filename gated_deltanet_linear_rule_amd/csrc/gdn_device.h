@@ -95,6 +95,22 @@ __device__ __forceinline__ f32x4 mm16_f32(f32x4 a, f32x4 b, f32x4 c) {
 }
 
 // ---------------------------------------------------------------------------
+// raw projections
+// ---------------------------------------------------------------------------
+// The *_raw entry points take q and k unnormalised and the gates as logits a
+// (decay) and b (write strength), and apply per (token, head)
+//     q <- q / sqrt(|q|^2 + kNormEps),  k likewise,
+//     g = -softplus(a),  beta = sigmoid(b)
+// -- the steps that precede the recurrence in the layer; the resulting
+// distributions are those of the synthetic inputs (unit q, k; g < 0; beta in
+// (0, 1)).
+constexpr float kNormEps = 1e-6f;
+__device__ __forceinline__ float gate_from_logit(float a) {
+    return -(fmaxf(a, 0.f) + log1pf(expf(-fabsf(a))));
+}
+__device__ __forceinline__ float beta_from_logit(float b) { return 1.f / (1.f + expf(-b)); }
+
+// ---------------------------------------------------------------------------
 // element I/O
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float to_f32(float x) { return x; }

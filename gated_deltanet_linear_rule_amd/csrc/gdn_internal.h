@@ -83,7 +83,8 @@ int64_t prefill_part_chunks(int64_t num_tokens, int num_seqs, int hv, int num_cu
 // Launchers: return hipSuccess or the launch error.  `bf16` selects the
 // element type of q/k/v/out; dk/dv are 64 or 128.
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, int dk, int dv, hipStream_t s);
-hipError_t launch_decode_tokens(const DecodeArgs& a, bool bf16, int dk, int dv, hipStream_t s);
-hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int dk, int dv, hipStream_t s);
+hipError_t launch_decode_tokens(const DecodeArgs& a, bool bf16, int dk, int dv, hipStream_t s, bool raw = false);
+// raw: q, k unnormalised and g, beta given as logits (see gdn_prefill_raw).
+hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int dk, int dv, hipStream_t s, bool raw = false);
 
 }  // namespace gdn

@@ -153,7 +153,30 @@ struct PrepWaveSmem {
     alignas(16) float D[4 * kDiagLd];  // diagonal blocks of A, then of T; column-major
     alignas(16) double G[kChunk];      // log2-scaled cumulative gates (fp64)
     alignas(16) float B[kChunk];       // beta
+    alignas(16) float IK[kChunk];      // raw projections: 1 / |k_t|
 };
+
+// Raw projections (see gdn_device.h): the norms are not applied to the stored
+// rows; 1 / |k_t| and 1 / |q_t| scale the products in which k_t and q_t appear.
+
+// Sum over the four lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48).
+__device__ __forceinline__ float sum_groups(float x) {
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+// Squares of the eight elements of an operand fragment, summed.
+template <typename OP>
+__device__ __forceinline__ float frag_sq(const typename Op<OP>::frag& f) {
+    float s2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x = to_f32(f[e]);
+        s2 += x * x;
+    }
+    return s2;
+}
 
 // Orders a wave's LDS accesses: its earlier LDS writes complete before any
 // later LDS read by another lane of the same wave, and the compiler moves no
@@ -175,7 +198,7 @@ __device__ __forceinline__ typename Op<OP>::frag load_frag8(const OP* p) {
 // Index of lower tile (tm, tn), tn <= tm, in row order.
 __host__ __device__ constexpr int lower_tile(int tm, int tn) { return tm * (tm + 1) / 2 + tn; }
 
-template <typename OP, int DK>
+template <typename OP, int DK, bool RAW>
 __global__ __launch_bounds__(kWave * kPrepWaves) void gdn_prep_kernel(PrefillArgs a) {
     using Ops = Op<OP>;
     using frag = typename Ops::frag;
@@ -212,8 +235,22 @@ __global__ __launch_bounds__(kWave * kPrepWaves) void gdn_prep_kernel(PrefillArg
         for (int kk = 0; kk < NK; ++kk) kf[tb][kk] = load_frag8<OP>(src + 32 * kk);
     }
     const size_t gi = (size_t)(t0 + (l < nt ? l : nt - 1)) * a.hv + h;
-    const float gl = l < nt ? a.g[gi] : 0.f;
-    const float bl = l < nt ? a.beta[gi] : 0.f;
+    float gl = l < nt ? a.g[gi] : 0.f;
+    float bl = l < nt ? a.beta[gi] : 0.f;
+    // raw projections: gates from logits; ikr[tb] = 1 / |k| of row 16 tb + r
+    float ikr[4] = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (RAW) {
+        gl = l < nt ? gate_from_logit(gl) : 0.f;
+        bl = l < nt ? beta_from_logit(bl) : 0.f;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            float s2 = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) s2 += frag_sq<OP>(kf[tb][kk]);
+            ikr[tb] = 1.f / sqrtf(sum_groups(s2) + kNormEps);
+            if (gq == 0) sm.IK[16 * tb + r] = ikr[tb];
+        }
+    }
 
     const double G = wave_cumsum_f64((double)gl * 1.4426950408889634);
     const double Gl = lane63_f64(G);
@@ -229,12 +266,14 @@ __global__ __launch_bounds__(kWave * kPrepWaves) void gdn_prep_kernel(PrefillArg
         double gt[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) gt[i] = sm.G[16 * tm + 4 * gq + i];
-        const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.B[16 * tm + 4 * gq]);
+        f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.B[16 * tm + 4 * gq]);
+        if constexpr (RAW) bt = bt * *reinterpret_cast<const f32x4*>(&sm.IK[16 * tm + 4 * gq]);
 #pragma unroll
         for (int tn = 0; tn <= tm; ++tn) {
             f32x4 acc = zero4();
 #pragma unroll
             for (int kk = 0; kk < NK; ++kk) acc = Ops::mma(kf[tm][kk], kf[tn][kk], acc);
+            if constexpr (RAW) acc = acc * ikr[tn];
             const double gs = sm.G[16 * tn + r];
             f32x4 x;
 #pragma unroll
@@ -320,10 +359,13 @@ __global__ __launch_bounds__(kWave * kPrepWaves) void gdn_prep_kernel(PrefillArg
             ws_store(reinterpret_cast<f32x4*>(Tw + ((size_t)(f * 2 + 1) * 64 + l) * VE), hi);
         }
     }
+    // (raw projections: gamma and D carry 1 / |k_t|, as they only ever scale
+    // products with k_t; the chunk kernels take gamma itself from G2)
     double* rec = a.ws_g + blk * (kGateRecord / 8);
+    const float ikl = RAW ? sm.IK[l] : 1.f;
     ws_store(rec + l, G);
-    ws_store(reinterpret_cast<float*>(rec + kChunk) + l, fast_exp2((float)G));
-    ws_store(reinterpret_cast<float*>(rec + kChunk) + kChunk + l, fast_exp2((float)(Gl - G)));
+    ws_store(reinterpret_cast<float*>(rec + kChunk) + l, fast_exp2((float)G) * ikl);
+    ws_store(reinterpret_cast<float*>(rec + kChunk) + kChunk + l, fast_exp2((float)(Gl - G)) * ikl);
 }
 
 // ===========================================================================
@@ -560,9 +602,10 @@ __device__ __forceinline__ void sched_fence() {
 // go there, since the compiler orders any LDS write it cannot tell apart from
 // their target after them), stage 1 once the products of Y are issued, stage
 // 2 between U and the state update.
-template <typename OP, int DK, int DV, bool OUT, int NR, int VMASK, int NW, typename F>
+template <typename OP, int DK, int DV, bool OUT, int NR, int VMASK, int NW, bool RAW, typename F>
 __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, OP* P, OP* kt, OP* ost,
-                                           f32x4 (&ST)[NR][DK / 16], const int (&R0)[NR], int w, F&& hook) {
+                                           f32x4 (&ST)[NR][DK / 16], const int (&R0)[NR], int w, F&& hook,
+                                           float* nrm) {
     using Ops = Op<OP>;
     using frag = typename Ops::frag;
     using quad = typename Ops::quad;
@@ -597,6 +640,30 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, 
             if (two) {
 #pragma unroll
                 for (int k2 = 0; k2 < NKK; ++k2) a1 = Ops::mma(p1[k2], pq[k2], a1);
+            }
+            if constexpr (RAW) {
+                // 1 / |q_t| for this lane's row t and 1 / |k_s| for the rows of
+                // the two K tiles, from the operand fragments already loaded;
+                // 1 / |q| goes to nrm[0, 64) for the outputs, 1 / |k| through
+                // nrm[64, 128) to the lanes whose columns need it
+                float sq = 0.f, s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                for (int k2 = 0; k2 < NKK; ++k2) {
+                    sq += frag_sq<OP>(pq[k2]);
+                    s0 += frag_sq<OP>(p0[k2]);
+                    if (two) s1 += frag_sq<OP>(p1[k2]);
+                }
+                const float iq = 1.f / sqrtf(sum_groups(sq) + kNormEps);
+                const float ik0 = 1.f / sqrtf(sum_groups(s0) + kNormEps);
+                const float ik1 = 1.f / sqrtf(sum_groups(s1) + kNormEps);
+                if (gq == 0) {
+                    nrm[t] = iq;
+                    nrm[kChunk + 32 * kk + n] = ik0;
+                    if (two) nrm[kChunk + 32 * kk + 16 + n] = ik1;
+                }
+                wave_lds_sync();
+                a0 = a0 * iq * *reinterpret_cast<const f32x4*>(&nrm[kChunk + 32 * kk + 4 * gq]);
+                if (two) a1 = a1 * iq * *reinterpret_cast<const f32x4*>(&nrm[kChunk + 32 * kk + 16 + 4 * gq]);
             }
             quad v0, v1;
 #pragma unroll
@@ -695,7 +762,8 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, 
         dd[kk][0] = *reinterpret_cast<const f32x4*>(&cb.dec[32 * kk + 4 * gq]);
         dd[kk][1] = *reinterpret_cast<const f32x4*>(&cb.dec[32 * kk + 16 + 4 * gq]);
     }
-    const float gl = cb.gam[kChunk - 1];
+    // gamma_last (raw projections: from G2, the gamma slot carries 1 / |k|)
+    const float gl = RAW ? fast_exp2((float)cb.G2[kChunk - 1]) : cb.gam[kChunk - 1];
     sched_fence<!OUT>();
     if constexpr (OUT) {
         mmZ(g1, 2);
@@ -767,7 +835,8 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, 
 #pragma unroll
         for (int f = 0; f < kTriFrags; ++f) pf[f] = lds_frag(P, f);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) gt[tb] = cb.gam[16 * tb + n];
+        for (int tb = 0; tb < 4; ++tb)
+            gt[tb] = RAW ? fast_exp2((float)cb.G2[16 * tb + n]) * nrm[16 * tb + n] : cb.gam[16 * tb + n];
     }
     sched_fence<!OUT>();
     mmS(k1, HD);
@@ -792,7 +861,7 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, 
 // OUT = false: summary of parts p < np - 1 (B_p into ws_b, M_p into ws_m).
 // OUT = true: outputs of every part, from ws_s (np > 1) or init_state (np = 1);
 // the last part writes final_state.
-template <typename OP, int DK, int DV, bool OUT>
+template <typename OP, int DK, int DV, bool OUT, bool RAW>
 __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) void gdn_chunk_kernel(PrefillArgs a) {
     using G = ChunkGeom<OP, DK, DV, OUT>;
     static_assert(G::NT == 64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16), "launch bound must equal the launch size");
@@ -810,6 +879,7 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
     constexpr int KTF = 2 * (DK / 16);
     constexpr int KTS = KT ? KTF * 64 * 8 : 8;
     __shared__ OP Kt[(G::KTA ? 2 : 1) * KTS];
+    __shared__ float Nrm[OUT && RAW ? 2 * kChunk : 1];   // raw projections: 1 / |q|, 1 / |k| of the chunk
 
     const int l = lane_id(), w = wave_id(), n = l & 15, gq = l >> 4;
     const int64_t pslot = blockIdx.x / a.hv;
@@ -988,7 +1058,7 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
             }
         };
         if constexpr (OUT) {
-            chunk_step<OP, DK, DV, OUT, NR, 1, NW>(cur, Pf, Kt, Ost, ST, R0, w, next_loads);
+            chunk_step<OP, DK, DV, OUT, NR, 1, NW, RAW>(cur, Pf, Kt, Ost, ST, R0, w, next_loads, Nrm);
             if (a.snapshots && j + 1 == next_snap) {   // state after a full snapshot interval
                 if ((j + 1) * kChunk <= len) {
                     const int64_t slot = span_base(s0, seq, (int64_t)a.snap_chunks * kChunk) + (j + 1) / a.snap_chunks - 1;
@@ -999,7 +1069,7 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
                 next_snap += a.snap_chunks;
             }
         } else {
-            chunk_step<OP, DK, DV, OUT, NR, 1, NW>(cur, nullptr, Kt, nullptr, ST, R0, w, next_loads);
+            chunk_step<OP, DK, DV, OUT, NR, 1, NW, RAW>(cur, nullptr, Kt, nullptr, ST, R0, w, next_loads, Nrm);
         }
         if (NBUF == 1 && j + 1 < je) {
             lds_barrier();                      // everyone is done with this chunk's rows
@@ -1038,7 +1108,7 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
                     touch(j + 3 < je ? j + 3 : je - 1, tv);
                 }
             };
-            chunk_step<OP, DK, DV, OUT, NR, 1, NW>(bufs[bc], nullptr, ktc, nullptr, ST, R0, w, ahead);
+            chunk_step<OP, DK, DV, OUT, NR, 1, NW, RAW>(bufs[bc], nullptr, ktc, nullptr, ST, R0, w, ahead, Nrm);
             bc = b1;
         };
         for (int64_t j = jb; j < je; j += 2) {
@@ -1147,38 +1217,38 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
 // ===========================================================================
 // host side
 // ===========================================================================
-template <typename OP, int DK>
+template <typename OP, int DK, bool RAW>
 hipError_t launch_prep(const PrefillArgs& a, hipStream_t st) {
     const int64_t items = a.num_slots * a.hv;
     const unsigned nwg = (unsigned)((items + kPrepWaves - 1) / kPrepWaves);
     if (nwg == 0) return hipSuccess;
-    hipLaunchKernelGGL((gdn_prep_kernel<OP, DK>), dim3(nwg), dim3(kWave * kPrepWaves), 0, st, a);
+    hipLaunchKernelGGL((gdn_prep_kernel<OP, DK, RAW>), dim3(nwg), dim3(kWave * kPrepWaves), 0, st, a);
     return hipGetLastError();
 }
 
-template <typename OP, int DK, int DV>
+template <typename OP, int DK, int DV, bool RAW>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
-    hipError_t e = launch_prep<OP, DK>(a, st);
+    hipError_t e = launch_prep<OP, DK, RAW>(a, st);
     if (e != hipSuccess) return e;
     const unsigned parts = (unsigned)(a.num_part_slots * a.hv);
     if (a.ws_m) {
-        hipLaunchKernelGGL((gdn_chunk_kernel<OP, DK, DV, false>), dim3(parts), dim3(ChunkGeom<OP, DK, DV, false>::NT),
-                           0, st, a);
+        hipLaunchKernelGGL((gdn_chunk_kernel<OP, DK, DV, false, RAW>), dim3(parts),
+                           dim3(ChunkGeom<OP, DK, DV, false>::NT), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const unsigned links = (unsigned)((int64_t)a.num_seqs * a.hv * (DV / 16));
         hipLaunchKernelGGL((gdn_link_kernel<DK, DV>), dim3(links), dim3(kLinkThreads), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((gdn_chunk_kernel<OP, DK, DV, true>), dim3(parts), dim3(ChunkGeom<OP, DK, DV, true>::NT), 0,
-                       st, a);
+    hipLaunchKernelGGL((gdn_chunk_kernel<OP, DK, DV, true, RAW>), dim3(parts), dim3(ChunkGeom<OP, DK, DV, true>::NT),
+                       0, st, a);
     return hipGetLastError();
 }
 
-template <typename OP>
+template <typename OP, bool RAW>
 hipError_t launch_prefill_dt(const PrefillArgs& a, int dk, int dv, hipStream_t st) {
     if (dk == 128)
-        return dv == 128 ? launch_prefill_t<OP, 128, 128>(a, st) : launch_prefill_t<OP, 128, 64>(a, st);
-    return dv == 128 ? launch_prefill_t<OP, 64, 128>(a, st) : launch_prefill_t<OP, 64, 64>(a, st);
+        return dv == 128 ? launch_prefill_t<OP, 128, 128, RAW>(a, st) : launch_prefill_t<OP, 128, 64, RAW>(a, st);
+    return dv == 128 ? launch_prefill_t<OP, 64, 128, RAW>(a, st) : launch_prefill_t<OP, 64, 64, RAW>(a, st);
 }
 
 }  // namespace
@@ -1195,9 +1265,10 @@ int64_t prefill_part_chunks(int64_t num_tokens, int num_seqs, int hv, int num_cu
     return L < whole ? L : whole;
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int dk, int dv, hipStream_t st) {
+hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int dk, int dv, hipStream_t st, bool raw) {
     if (a.num_seqs == 0) return hipSuccess;
-    return bf16 ? launch_prefill_dt<__bf16>(a, dk, dv, st) : launch_prefill_dt<float>(a, dk, dv, st);
+    if (raw) return bf16 ? launch_prefill_dt<__bf16, true>(a, dk, dv, st) : launch_prefill_dt<float, true>(a, dk, dv, st);
+    return bf16 ? launch_prefill_dt<__bf16, false>(a, dk, dv, st) : launch_prefill_dt<float, false>(a, dk, dv, st);
 }
 
 }  // namespace gdn

@@ -75,6 +75,7 @@ class Workload:
     decode_steps: int = 0      # >0: decode workload (each sequence advances 1 token per step)
     seed: int = 0
     packed: bool = False       # True: pass cu_seqlens (varlen packing)
+    raw: bool = False          # True: q, k unnormalised (per-token scales), g and beta hold logits
 
     @property
     def num_seqs(self) -> int:
@@ -186,6 +187,21 @@ def make_inputs(cfg, seed: int = 0, seqlens=None) -> Inputs:
             inp.steps.append(dict(q=q, k=k, v=v, g=g, beta=beta))
         return inp
     T = wl.total_tokens
+    if wl.raw:
+        # raw projections: N(0,1) rows times a per-(token, head) scale in [0.1, 10), logits N(0,1)
+        def raw_rows(H, d):
+            x = _normal(rng, (T, H, d)) * np.exp(rng.uniform(np.log(0.1), np.log(10.0), (T, H, 1))).astype(np.float32)
+            return _store(x.astype(np.float32), dt)
+        inp.q = raw_rows(Hqk, dk)
+        inp.k = raw_rows(Hqk, dk)
+        inp.v = _draw_v(rng, T, Hv, dv, dt)
+        inp.beta = _normal(rng, (T, Hv))
+        inp.g = _normal(rng, (T, Hv))
+        if wl.init_state == "normal":
+            inp.init_state = (0.1 * _normal(rng, (wl.num_seqs, Hv, dv, dk))).astype(np.float32)
+        if wl.packed or wl.num_seqs > 1:
+            inp.cu_seqlens = np.concatenate([[0], np.cumsum(wl.seqlens)]).astype(np.int32)
+        return inp
     inp.q = _draw_qk(rng, T, Hqk, dk, dt)
     inp.k = _draw_qk(rng, T, Hqk, dk, dt)
     inp.v = _draw_v(rng, T, Hv, dv, dt)
@@ -199,7 +215,8 @@ def make_inputs(cfg, seed: int = 0, seqlens=None) -> Inputs:
 
 
 def custom(dtype="bf16", Hqk=2, Hv=2, dk=64, dv=64, seqlens=(100,), init_state="zero",
-           decode_steps=0, name="custom") -> Workload:
-    """A workload of arbitrary (small) shape with the standard distributions."""
+           decode_steps=0, name="custom", raw=False) -> Workload:
+    """A workload of arbitrary (small) shape with the standard distributions
+    (raw=True: the raw projections the *_raw entry points take)."""
     return Workload(name, dtype, Hqk, Hv, dk, dv, list(seqlens), init_state=init_state,
-                    decode_steps=decode_steps, packed=len(seqlens) > 1)
+                    decode_steps=decode_steps, packed=len(seqlens) > 1, raw=raw)

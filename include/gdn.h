@@ -187,6 +187,28 @@ gdn_status gdn_decode_slots(const gdn_shape* shape, int32_t tokens_per_seq, cons
                             int64_t pool_slots, const int32_t* slot_idx, void* out, float* token_states,
                             void* stream);
 
+/*
+ * gdn_prefill_raw, gdn_decode_tokens_raw -- the same calls from the layer's
+ * raw projections, with the steps that precede the recurrence fused into the
+ * kernels (no extra pass over HBM).  q and k are taken unnormalised and g,
+ * beta are replaced by logits a_gate, b_beta [tokens, Hv] fp32; per (token,
+ * head) the library uses
+ *     q / sqrt(|q|^2 + 1e-6),  k / sqrt(|k|^2 + 1e-6),
+ *     g = -softplus(a_gate),   beta = sigmoid(b_beta).
+ * (The pages name the layer -- a fixed-size recurrent state per head,
+ * flozi.net, "Qwen3.8-Flash-Next architecture", "Der Weg eines Tokens durch
+ * das Modell", item 1 -- but print none of these formulas; they are the usual
+ * forms and give the input distributions the rest of this library is
+ * measured on.)  All other arguments, layouts and rules are those of
+ * gdn_prefill and gdn_decode_tokens.
+ */
+gdn_status gdn_prefill_raw(const gdn_shape* shape, const void* q, const void* k, const void* v, const float* a_gate,
+                           const float* b_beta, const float* init_state, const int32_t* cu_seqlens, void* out,
+                           float* final_state, void* stream);
+gdn_status gdn_decode_tokens_raw(const gdn_shape* shape, int32_t tokens_per_seq, const void* q, const void* k,
+                                 const void* v, const float* a_gate, const float* b_beta, float* state, void* out,
+                                 float* token_states, void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* gdn_status_string(gdn_status status);
 

@@ -27,7 +27,8 @@ def _declared_functions():
 
 def test_header_declares_the_abi():
     assert _declared_functions() == ["gdn_abi_version", "gdn_decode_slots", "gdn_decode_step", "gdn_decode_tokens",
-                                     "gdn_last_error", "gdn_prefill", "gdn_prefill_snapshots", "gdn_status_string"]
+                                     "gdn_decode_tokens_raw", "gdn_last_error", "gdn_prefill", "gdn_prefill_raw",
+                                     "gdn_prefill_snapshots", "gdn_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -204,6 +205,17 @@ def _prefill_snapshots(shape, chunks, snaps):
 def test_prefill_snapshots_rejects_bad_arguments(chunks, snaps, status, msg):
     rc, err = _prefill_snapshots(_shape(), chunks, snaps)
     assert rc == status and msg in err, (rc, err)
+
+
+def test_raw_entry_points_apply_the_same_argument_checks():
+    c = ctypes.c_void_p
+    L = _lib()
+    rc = L.gdn_prefill_raw(ctypes.byref(_shape(num_qk_heads=3, num_v_heads=4)), c(FAKE), c(FAKE), c(FAKE), c(FAKE),
+                           c(FAKE), None, None, c(FAKE), None, None)
+    assert rc == B.GDN_ERROR_INVALID_VALUE and "multiple" in L.gdn_last_error().decode()
+    rc = L.gdn_decode_tokens_raw(ctypes.byref(_shape(num_seqs=4, num_tokens=12)), 3, c(FAKE), c(FAKE), c(FAKE),
+                                 None, c(FAKE), c(FAKE), c(FAKE), None, None)
+    assert rc == B.GDN_ERROR_INVALID_VALUE and "g is NULL" in L.gdn_last_error().decode()
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch):

@@ -370,3 +370,46 @@ def test_prefill_snapshots_equal_lengths_without_offsets():
     inp = gi.make_inputs(gi.custom(dtype="bf16", Hqk=2, Hv=2, dk=64, dv=128, seqlens=(640, 640, 640),
                                    init_state="zero"), seed=52)
     _check_snapshots(inp, 1, TOL["bf16"], "snapshots 3x640 P=64 no offsets", num_seqs=3)
+
+
+# ---------------------------------------------- raw projections (fused prologue)
+def _check_raw_prefill(inp, tol, label):
+    cu = None if inp.cu_seqlens is None else dev(inp.cu_seqlens)
+    out, fin = B.gdn_prefill(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta),
+                             None if inp.init_state is None else dev(inp.init_state), cu, raw=True)
+    torch.cuda.synchronize()
+    ro, rf = c_oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.init_state, inp.cu_seqlens, raw=True)
+    eo, ef = rel_err(host64(out), ro), rel_err(host64(fin), rf)
+    say(f"[parity] {label}: out {eo:.3e} final {ef:.3e}")
+    assert np.all(np.isfinite(host64(out)))
+    assert eo <= tol and ef <= tol
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (128, 64)])
+def test_prefill_raw_packed(dtype, dk, dv):
+    """Unnormalised q, k (per-token scales 0.1 .. 10) and gate logits; packed ragged sequences."""
+    inp = gi.make_inputs(gi.custom(dtype=dtype, Hqk=2, Hv=4, dk=dk, dv=dv, seqlens=(200, 7, 130),
+                                   init_state="normal", raw=True), seed=70)
+    _check_raw_prefill(inp, TOL[dtype], f"prefill_raw {dtype} dk={dk} dv={dv}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_raw_long_sequence_in_parts(dtype):
+    inp = gi.make_inputs(gi.custom(dtype=dtype, Hqk=1, Hv=1, dk=128, dv=128, seqlens=(4096,),
+                                   init_state="normal", raw=True), seed=71)
+    _check_raw_prefill(inp, TOL[dtype], f"prefill_raw parts {dtype}")
+
+
+@pytest.mark.parametrize("dtype,T", [("f32", 1), ("f32", 4), ("bf16", 3)])
+def test_decode_tokens_raw(dtype, T):
+    inp = gi.make_inputs(gi.custom(dtype=dtype, Hqk=2, Hv=4, dk=128, dv=64, seqlens=(T,) * 5,
+                                   init_state="normal", raw=True), seed=72 + T)
+    state = dev(inp.init_state)
+    out, ts = B.gdn_decode_tokens(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), state, T,
+                                  token_states=True, raw=True)
+    torch.cuda.synchronize()
+    ro, rs, rf = c_oracle.decode_tokens(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.init_state, T, raw=True)
+    eo, es, et = rel_err(host64(out), ro), rel_err(host64(state), rf), rel_err(host64(ts), rs)
+    say(f"[parity] decode_tokens_raw {dtype} T={T}: out {eo:.3e} state {es:.3e} token states {et:.3e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype] and et <= TOL[dtype]

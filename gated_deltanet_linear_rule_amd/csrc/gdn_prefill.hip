@@ -1149,12 +1149,17 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
 // One workgroup per (sequence, value head, 16-row block of the state); rows of
 // S never mix, so the blocks are independent.  S_0 (init_state or zeros) and
 // every later S_p go to ws_s at the part's slot.  Wave w computes the d_k
-// column blocks w, w + 4, ... of S_{p+1} on the fp32 matrix cores.
+// column blocks w, w + 4, ... of S_{p+1} on the fp32 matrix cores.  M_p does
+// not depend on S, so M_{p+1} streams into the second LDS buffer (direct
+// loads) while step p computes: a step waits for one load, not a chain of them.
 template <int DK, int DV>
 __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
     constexpr int NVB = DV / 16, NDB = DK / 16, NKK = DK / 32, LD = DK + 4;
     constexpr int NWV = kLinkThreads / kWave, PER = (NDB + NWV - 1) / NWV;
+    constexpr int MI = DK * DK * 4 / 1024;               // 1 KB direct loads per M
+    static_assert(MI % NWV == 0, "M loads per wave");
     __shared__ float S[16][LD];
+    __shared__ float Mb[2][DK * DK];                      // M_p, row-major
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), n = l & 15, gq = l >> 4;
     const int vb = (int)(blockIdx.x % NVB);
     const int64_t chain = blockIdx.x / NVB;
@@ -1167,25 +1172,51 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
     const int64_t pbase = span_base(s0, seq, L * kChunk);
     const int R0 = 16 * vb;
 
+    auto load_m = [&](int64_t p, int buf) {
+        const float* M = a.ws_m + ((size_t)(pbase + p) * a.hv + h) * DK * DK;
+        const auto rm = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(M), 0, DK * DK * 4, 0x00020000);
+#pragma unroll
+        for (int k = 0; k < MI / NWV; ++k) bytes_to_lds(&Mb[buf][0], rm, w + NWV * k);
+    };
+    load_m(0, 0);
     for (int e = tid; e < 16 * DK / 4; e += kLinkThreads) {
         const int row = e / (DK / 4), c = 4 * (e - row * (DK / 4));
         const f32x4 x = a.init_state ? *reinterpret_cast<const f32x4*>(a.init_state + (chain * DV + R0 + row) * DK + c) : zero4();
         *reinterpret_cast<f32x4*>(&S[row][c]) = x;
         *reinterpret_cast<f32x4*>(a.ws_s + (((size_t)pbase * a.hv + h) * DV + R0 + row) * DK + c) = x;
     }
+    // this lane's share of B_p (accumulator layout), fetched a step ahead
+    auto load_b = [&](int64_t p, f32x4 (&c)[PER]) {
+        const float* B = a.ws_b + ((size_t)(pbase + p) * a.hv + h) * DV * DK + (size_t)R0 * DK;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int db = w + NWV * k;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) c[k][i] = db < NDB ? B[(size_t)(4 * gq + i) * DK + 16 * db + n] : 0.f;
+        }
+    };
+    f32x4 bnext[PER];
+    load_b(0, bnext);
     for (int64_t p = 0; p + 1 < np; ++p) {
-        __syncthreads();
-        const size_t blk = (size_t)(pbase + p) * a.hv + h;
-        const float* M = a.ws_m + blk * DK * DK;
-        const float* B = a.ws_b + blk * DV * DK + (size_t)R0 * DK;
+        const int cb = (int)(p & 1);
+        f32x4 bcur[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) bcur[k] = bnext[k];
+        // this wave's share of M_p (and B_p) is in; the PER * 4 newest memory
+        // operations, the stores of S_p, may still be in flight
+        __builtin_amdgcn_s_waitcnt(kWaitVm0 | ((PER * 4) & 15) | (((PER * 4) >> 4) << 14));
+        __syncthreads();                                 // everyone's is; S_p is written
+        if (p + 2 < np) {
+            load_m(p + 1, cb ^ 1);                       // the other buffer was read in step p - 1
+            load_b(p + 1, bnext);
+        }
+        const float* M = Mb[cb];
         f32x4 res[PER];
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int db = w + NWV * k;
             if (db >= NDB) break;
-            f32x4 c;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) c[i] = B[(size_t)(4 * gq + i) * DK + 16 * db + n];
+            f32x4 c = bcur[k];
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
                 f32x8 av, bv;
@@ -1193,13 +1224,13 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
                 for (int i = 0; i < 8; ++i) {
                     const int rr = 32 * kk + (i < 4 ? 4 * gq + i : 16 + 4 * gq + i - 4);
                     av[i] = S[n][rr];
-                    bv[i] = M[(size_t)rr * DK + 16 * db + n];
+                    bv[i] = M[rr * DK + 16 * db + n];
                 }
                 c = Op<float>::mma(av, bv, c);
             }
             res[k] = c;
         }
-        __syncthreads();
+        lds_barrier();                                   // S_p read by everyone (M_{p+1} may be in flight)
         float* Sn = a.ws_s + ((size_t)(pbase + p + 1) * a.hv + h) * DV * DK + (size_t)R0 * DK;
 #pragma unroll
         for (int k = 0; k < PER; ++k) {

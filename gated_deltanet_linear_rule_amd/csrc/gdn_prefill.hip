@@ -166,14 +166,22 @@ __device__ __forceinline__ float sum_groups(float x) {
     return x;
 }
 
-// Squares of the eight elements of an operand fragment, summed.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Squares of the eight elements of an operand fragment, summed (bf16: four
+// two-term dot products with fp32 accumulation).
 template <typename OP>
 __device__ __forceinline__ float frag_sq(const typename Op<OP>::frag& f) {
     float s2 = 0.f;
+    if constexpr (sizeof(OP) == 2) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float x = to_f32(f[e]);
-        s2 += x * x;
+        for (int e = 0; e < 4; ++e) {
+            const bf16x2 x = {f[2 * e], f[2 * e + 1]};
+            s2 = __builtin_amdgcn_fdot2_f32_bf16(x, x, s2, false);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s2 += f[e] * f[e];
     }
     return s2;
 }

@@ -159,6 +159,9 @@ def main():
     ap.add_argument("--decode-runs", type=int, default=3, help="timed 64-step decode runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="headline prefill and single-step decode only (no raw-projection, snapshot, "
+                         "multi-token or state-pool legs): the run the counter summaries are taken on")
     ap.add_argument("--cpu-sample-tokens", type=int, default=262144)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB -> 1 GiB elementwise kernel (torch.neg, fp32), the "
@@ -231,39 +234,41 @@ def main():
     tok_s = T / (ms * 1e-3)
     traffic = measured_traffic("gdn_prefill", PREFILL_SOURCES)
 
-    # the same call from raw projections (fused q/k normalisation and gate
-    # activations; the normalised inputs and their gates stand in as values)
-    for _ in range(2):
-        B.gdn_prefill(q, k, v, g, beta, None, None, out=out, final_state=fin, raw=True)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(5):
-        B.gdn_prefill(q, k, v, g, beta, None, None, out=out, final_state=fin, raw=True)
-    b.record(stream)
-    torch.cuda.synchronize()
-    raw_ms = a.elapsed_time(b) / 5
-    log(f"prefill from raw projections (fused prologue): {raw_ms:.3f} ms/call")
-    raw_rec = {"workload": "prefill_256k from raw projections (q, k normalised and gates activated inside the "
-                           "kernels, gdn_prefill_raw)",
-               "ms_per_call": round(raw_ms, 4), "tokens_per_s": round(T / (raw_ms * 1e-3), 1)}
+    raw_rec = snapshot_rec = None
+    if not args.no_variants:
+        # the same call from raw projections (fused q/k normalisation and gate
+        # activations; the normalised inputs and their gates stand in as values)
+        for _ in range(2):
+            B.gdn_prefill(q, k, v, g, beta, None, None, out=out, final_state=fin, raw=True)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(5):
+            B.gdn_prefill(q, k, v, g, beta, None, None, out=out, final_state=fin, raw=True)
+        b.record(stream)
+        torch.cuda.synchronize()
+        raw_ms = a.elapsed_time(b) / 5
+        log(f"prefill from raw projections (fused prologue): {raw_ms:.3f} ms/call")
+        raw_rec = {"workload": "prefill_256k from raw projections (q, k normalised and gates activated inside the "
+                               "kernels, gdn_prefill_raw)",
+                   "ms_per_call": round(raw_ms, 4), "tokens_per_s": round(T / (raw_ms * 1e-3), 1)}
 
-    # the same call with a state snapshot every 4096 tokens (prefix reuse)
-    snap_chunks = 64
-    snaps = torch.empty((B.snapshot_slots(T, 1, snap_chunks), hv, dv, dk), dtype=torch.float32, device="cuda")
-    for _ in range(2):
-        B.gdn_prefill_snapshots(q, k, v, g, beta, snap_chunks, snapshots=snaps, out=out, final_state=fin)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(5):
-        B.gdn_prefill_snapshots(q, k, v, g, beta, snap_chunks, snapshots=snaps, out=out, final_state=fin)
-    b.record(stream)
-    torch.cuda.synchronize()
-    snap_ms = a.elapsed_time(b) / 5
-    log(f"prefill with a snapshot every {64 * snap_chunks} tokens: {snap_ms:.3f} ms/call")
-    snapshot_rec = {"workload": f"prefill_256k with a state snapshot every {64 * snap_chunks} tokens "
-                                f"({T // (64 * snap_chunks)} snapshots x 16 heads, gdn_prefill_snapshots)",
-                    "ms_per_call": round(snap_ms, 4), "tokens_per_s": round(T / (snap_ms * 1e-3), 1)}
-    del snaps
+        # the same call with a state snapshot every 4096 tokens (prefix reuse)
+        snap_chunks = 64
+        snaps = torch.empty((B.snapshot_slots(T, 1, snap_chunks), hv, dv, dk), dtype=torch.float32, device="cuda")
+        for _ in range(2):
+            B.gdn_prefill_snapshots(q, k, v, g, beta, snap_chunks, snapshots=snaps, out=out, final_state=fin)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(5):
+            B.gdn_prefill_snapshots(q, k, v, g, beta, snap_chunks, snapshots=snaps, out=out, final_state=fin)
+        b.record(stream)
+        torch.cuda.synchronize()
+        snap_ms = a.elapsed_time(b) / 5
+        log(f"prefill with a snapshot every {64 * snap_chunks} tokens: {snap_ms:.3f} ms/call")
+        snapshot_rec = {"workload": f"prefill_256k with a state snapshot every {64 * snap_chunks} tokens "
+                                    f"({T // (64 * snap_chunks)} snapshots x 16 heads, gdn_prefill_snapshots)",
+                        "ms_per_call": round(snap_ms, 4), "tokens_per_s": round(T / (snap_ms * 1e-3), 1)}
+        del snaps
     del q, k, v, g, beta, out
     torch.cuda.empty_cache()
 
@@ -310,62 +315,63 @@ def main():
         del state, steps, d
         torch.cuda.empty_cache()
 
-        # multi-token decode: 256 sequences advance 4 tokens per call, with per-token states
-        m = gi.make_inputs("draft_256x4", seed=0)
-        MT = m.wl.seqlens[0]
-        mN = m.wl.num_seqs
-        mst = dev(m.init_state)
-        margs = tuple(dev(x) for x in (m.q, m.k, m.v, m.g, m.beta))
-        mout = torch.empty((mN * MT, dhv, ddv), dtype=torch.bfloat16, device="cuda")
-        mts = torch.empty((mN, MT, dhv, ddv, ddk), dtype=torch.float32, device="cuda")
+        if not args.no_variants:
+            # multi-token decode: 256 sequences advance 4 tokens per call, with per-token states
+            m = gi.make_inputs("draft_256x4", seed=0)
+            MT = m.wl.seqlens[0]
+            mN = m.wl.num_seqs
+            mst = dev(m.init_state)
+            margs = tuple(dev(x) for x in (m.q, m.k, m.v, m.g, m.beta))
+            mout = torch.empty((mN * MT, dhv, ddv), dtype=torch.bfloat16, device="cuda")
+            mts = torch.empty((mN, MT, dhv, ddv, ddk), dtype=torch.float32, device="cuda")
 
-        def run_mt(n):
-            for _ in range(n):
-                B.gdn_decode_tokens(*margs, mst, MT, out=mout, token_states=mts)
+            def run_mt(n):
+                for _ in range(n):
+                    B.gdn_decode_tokens(*margs, mst, MT, out=mout, token_states=mts)
 
-        run_mt(3)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        run_mt(20)
-        b.record(stream)
-        torch.cuda.synchronize()
-        mms = a.elapsed_time(b) / 20
-        mbytes = decode_tokens_bytes(mN, MT, dhqk, dhv, ddk, ddv)
-        mgbs = mbytes / (mms * 1e-3) / 1e9
-        assert torch.isfinite(mst).all().item()
-        decode["multi_token"] = {
-            "workload": "draft_256x4: 256 seqs x 4 tokens x 16 heads, d=128, bf16, fp32 state in place, "
-                        "per-token states written (gdn_decode_tokens)",
-            "value": round(mgbs, 1), "unit": "GB/s", "ms_per_call": round(mms, 5),
-            "tokens_per_s": round(mN * MT / (mms * 1e-3), 1),
-            "roofline": {"bound": "hbm", "achieved": round(mgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(mgbs / HBM_PEAK_GBS, 4), "bytes_per_call": mbytes},
-        }
-        log(f"multi-token decode: {mms * 1e3:.1f} us/call ({MT} tokens), {mgbs:.0f} GB/s")
+            run_mt(3)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            run_mt(20)
+            b.record(stream)
+            torch.cuda.synchronize()
+            mms = a.elapsed_time(b) / 20
+            mbytes = decode_tokens_bytes(mN, MT, dhqk, dhv, ddk, ddv)
+            mgbs = mbytes / (mms * 1e-3) / 1e9
+            assert torch.isfinite(mst).all().item()
+            decode["multi_token"] = {
+                "workload": "draft_256x4: 256 seqs x 4 tokens x 16 heads, d=128, bf16, fp32 state in place, "
+                            "per-token states written (gdn_decode_tokens)",
+                "value": round(mgbs, 1), "unit": "GB/s", "ms_per_call": round(mms, 5),
+                "tokens_per_s": round(mN * MT / (mms * 1e-3), 1),
+                "roofline": {"bound": "hbm", "achieved": round(mgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(mgbs / HBM_PEAK_GBS, 4), "bytes_per_call": mbytes},
+            }
+            log(f"multi-token decode: {mms * 1e3:.1f} us/call ({MT} tokens), {mgbs:.0f} GB/s")
 
-        # one decode step over a pool of 512 states, the batch's 256 sequences on permuted slots
-        pool = torch.zeros((2 * mN, dhv, ddv, ddk), dtype=torch.float32, device="cuda")
-        sidx = torch.randperm(2 * mN, generator=torch.Generator().manual_seed(0))[:mN].to(torch.int32).cuda()
-        sargs = tuple(x[::MT].contiguous() for x in margs)
-        sout = torch.empty((mN, dhv, ddv), dtype=torch.bfloat16, device="cuda")
-        for _ in range(3):
-            B.gdn_decode_slots(*sargs, pool, sidx, 1, out=sout)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for _ in range(20):
-            B.gdn_decode_slots(*sargs, pool, sidx, 1, out=sout)
-        b.record(stream)
-        torch.cuda.synchronize()
-        pms = a.elapsed_time(b) / 20
-        pbytes = decode_bytes(mN, dhqk, dhv, ddk, ddv)
-        decode["state_pool"] = {
-            "workload": "one decode step of 256 seqs x 16 heads over a pool of 512 states (permuted slots, "
-                        "gdn_decode_slots)",
-            "value": round(pbytes / (pms * 1e-3) / 1e9, 1), "unit": "GB/s", "ms_per_step": round(pms, 5)}
-        log(f"decode over a state pool: {pms * 1e3:.1f} us/step, {pbytes / (pms * 1e-3) / 1e9:.0f} GB/s")
-        del pool, sidx, sargs, sout
-        del mst, margs, mout, mts, m
+            # one decode step over a pool of 512 states, the batch's 256 sequences on permuted slots
+            pool = torch.zeros((2 * mN, dhv, ddv, ddk), dtype=torch.float32, device="cuda")
+            sidx = torch.randperm(2 * mN, generator=torch.Generator().manual_seed(0))[:mN].to(torch.int32).cuda()
+            sargs = tuple(x[::MT].contiguous() for x in margs)
+            sout = torch.empty((mN, dhv, ddv), dtype=torch.bfloat16, device="cuda")
+            for _ in range(3):
+                B.gdn_decode_slots(*sargs, pool, sidx, 1, out=sout)
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(20):
+                B.gdn_decode_slots(*sargs, pool, sidx, 1, out=sout)
+            b.record(stream)
+            torch.cuda.synchronize()
+            pms = a.elapsed_time(b) / 20
+            pbytes = decode_bytes(mN, dhqk, dhv, ddk, ddv)
+            decode["state_pool"] = {
+                "workload": "one decode step of 256 seqs x 16 heads over a pool of 512 states (permuted slots, "
+                            "gdn_decode_slots)",
+                "value": round(pbytes / (pms * 1e-3) / 1e9, 1), "unit": "GB/s", "ms_per_step": round(pms, 5)}
+            log(f"decode over a state pool: {pms * 1e3:.1f} us/step, {pbytes / (pms * 1e-3) / 1e9:.0f} GB/s")
+            del pool, sidx, sargs, sout
+            del mst, margs, mout, mts, m
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ CPU baseline

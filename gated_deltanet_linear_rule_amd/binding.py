@@ -62,6 +62,11 @@ def lib() -> ctypes.CDLL:
         L.gdn_decode_slots.restype = ctypes.c_int
         L.gdn_prefill_snapshots.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, P]
         L.gdn_prefill_snapshots.restype = ctypes.c_int
+        L.gdn_prefill_workspace_size.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_int32,
+                                                 ctypes.POINTER(ctypes.c_size_t)]
+        L.gdn_prefill_workspace_size.restype = ctypes.c_int
+        L.gdn_prefill_ws.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.gdn_prefill_ws.restype = ctypes.c_int
         L.gdn_prefill_raw.argtypes = L.gdn_prefill.argtypes
         L.gdn_prefill_raw.restype = ctypes.c_int
         L.gdn_decode_tokens_raw.argtypes = L.gdn_decode_tokens.argtypes
@@ -123,8 +128,21 @@ def _raise(rc, where):
         raise GdnError(rc, where, lib().gdn_last_error().decode())
 
 
+def gdn_prefill_workspace_size(q, v, cu_seqlens=None, num_seqs=None) -> int:
+    """Bytes of device workspace that ``gdn_prefill(..., workspace=...)`` needs for these
+    shapes on the current device (q [T, Hqk, dk], v [T, Hv, dv]; packed if cu_seqlens is given)."""
+    T, hqk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    N = cu_seqlens.numel() - 1 if cu_seqlens is not None else (1 if num_seqs is None else int(num_seqs))
+    shape = GdnShape(N, T, hqk, hv, dk, dv, _io_dtype(q))
+    n = ctypes.c_size_t(0)
+    _raise(lib().gdn_prefill_workspace_size(ctypes.byref(shape), int(cu_seqlens is not None), ctypes.byref(n)),
+           "gdn_prefill_workspace_size")
+    return int(n.value)
+
+
 def gdn_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, out=None, final_state=None,
-                stream=None, num_seqs=None, return_final_state=True, raw=False):
+                stream=None, num_seqs=None, return_final_state=True, raw=False, workspace=None):
     """Chunked GDN prefill over packed sequences.
 
     q, k [T, Hqk, dk]; v [T, Hv, dv] (bf16 or fp32, same dtype); g, beta [T, Hv]
@@ -132,6 +150,8 @@ def gdn_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, out=None, fi
     the GPU or None (then ``num_seqs`` equal-length sequences, default 1).
     Returns (out, final_state); final_state is None if not requested.
     raw=True calls gdn_prefill_raw: q, k unnormalised, g and beta are the logits a, b.
+    workspace: a contiguous GPU tensor of at least gdn_prefill_workspace_size bytes
+    (calls gdn_prefill_ws, which allocates nothing; not with raw=True).
     """
     T, hqk, dk = q.shape
     hv, dv = v.shape[1], v.shape[2]
@@ -154,6 +174,15 @@ def gdn_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, out=None, fi
         final_state = torch.empty((N, hv, dv, dk), dtype=torch.float32, device=q.device)
     _check(final_state, "final_state", torch.float32, (N, hv, dv, dk))
     shape = GdnShape(N, T, hqk, hv, dk, dv, io)
+    if workspace is not None:
+        if raw:
+            raise ValueError("a caller workspace is taken by gdn_prefill_ws, which has no raw-projection form")
+        _check(workspace, "workspace")
+        rc = lib().gdn_prefill_ws(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                  _ptr(init_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+        _raise(rc, "gdn_prefill_ws")
+        return out, final_state
     fn = lib().gdn_prefill_raw if raw else lib().gdn_prefill
     rc = fn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
             _ptr(init_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state), _stream(stream))

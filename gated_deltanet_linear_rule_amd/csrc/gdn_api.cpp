@@ -2,7 +2,8 @@
 //
 // Validates every host-checkable argument before touching HIP, picks the
 // kernel variant, takes the prefill workspace from HIP's stream-ordered pool
-// and enqueues the kernels on the caller's stream.  No exception or abort
+// (or from the caller, gdn_prefill_ws) and enqueues the kernels on the
+// caller's stream.  No exception or abort
 // crosses the ABI; the text of the last failure is kept per thread.
 #include <hip/hip_runtime.h>
 
@@ -228,10 +229,39 @@ gdn_status gdn_decode_tokens_raw(const gdn_shape* shape, int32_t tokens_per_seq,
 
 namespace {
 
+// The part length, slot counts and workspace layout of one prefill call on
+// the current device; `packed` tells whether cu_seqlens will be given.
+gdn_status plan_prefill(const gdn_shape* shape, bool packed, gdn::PrefillArgs& a, bool& split, int64_t& total) {
+    a.num_tokens = shape->num_tokens;
+    a.seqlen = shape->num_tokens / shape->num_seqs;
+    a.num_seqs = shape->num_seqs;
+    a.hqk = shape->num_qk_heads;
+    a.hv = shape->num_v_heads;
+    a.dv = shape->head_dim_v;
+    a.num_slots = (shape->num_tokens + 63) / 64 + shape->num_seqs;
+    if (a.num_slots > INT32_MAX) return fail(GDN_ERROR_NOT_SUPPORTED, "too many chunks");
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(GDN_ERROR_LAUNCH, "hipGetDevice failed");
+    const int cus = compute_units(dev);
+    if (cus <= 0) return fail(GDN_ERROR_LAUNCH, "cannot query the device's compute units");
+    a.part_chunks = gdn::prefill_part_chunks(a.num_tokens, a.num_seqs, a.hv, cus);
+    const int64_t span = a.part_chunks * 64;
+    a.num_part_slots = (a.num_tokens + span - 1) / span + a.num_seqs;
+    const int64_t longest = packed ? (a.num_tokens + 63) / 64 : (a.seqlen + 63) / 64;
+    split = a.part_chunks < longest;
+    if (a.num_part_slots * a.hv > INT32_MAX || a.num_seqs * (int64_t)a.hv * (a.dv / 16) > INT32_MAX)
+        return fail(GDN_ERROR_NOT_SUPPORTED, "too many (part, head) pairs");
+    const gdn::PrefillWorkspace wl(a.num_slots, a.num_part_slots, split, a.hv, shape->head_dim_k, shape->head_dim_v,
+                                   shape->dtype == GDN_DTYPE_BF16 ? 2 : 4);
+    total = wl.total;
+    return GDN_SUCCESS;
+}
+
+// `workspace` NULL: the workspace comes from HIP's stream-ordered pool.
 gdn_status prefill_impl(const char* who, const gdn_shape* shape, const void* q, const void* k, const void* v,
                         const float* g, const float* beta, const float* init_state, const int32_t* cu_seqlens,
                         void* out, float* final_state, int32_t snapshot_chunks, float* snapshots, void* stream,
-                        bool raw = false) {
+                        bool raw = false, void* workspace = nullptr, size_t workspace_bytes = 0) {
     g_last_error[0] = '\0';
     GDN_TRY(check_shape(shape, false));
     const bool tok = shape->num_tokens > 0;
@@ -244,6 +274,7 @@ gdn_status prefill_impl(const char* who, const gdn_shape* shape, const void* q, 
     GDN_TRY(check_ptr(init_state, "init_state", 16, false));
     GDN_TRY(check_ptr(final_state, "final_state", 16, false));
     GDN_TRY(check_ptr(cu_seqlens, "cu_seqlens", 4, false));
+    GDN_TRY(check_ptr(workspace, "workspace", 256, false));
     if (!cu_seqlens && shape->num_seqs > 0 && shape->num_tokens % shape->num_seqs != 0)
         return fail(GDN_ERROR_INVALID_VALUE, "num_tokens (%lld) is not a multiple of num_seqs (%d) and no cu_seqlens",
                     (long long)shape->num_tokens, shape->num_seqs);
@@ -265,34 +296,25 @@ gdn_status prefill_impl(const char* who, const gdn_shape* shape, const void* q, 
     a.snap_chunks = snapshots ? snapshot_chunks : 0;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.init_state = init_state; a.cu = cu_seqlens; a.out = out; a.final_state = final_state;
-    a.num_tokens = shape->num_tokens;
-    a.seqlen = shape->num_tokens / shape->num_seqs;
-    a.num_seqs = shape->num_seqs;
-    a.hqk = shape->num_qk_heads;
-    a.hv = shape->num_v_heads;
-    a.dv = shape->head_dim_v;
-    a.num_slots = (shape->num_tokens + 63) / 64 + shape->num_seqs;
-    if (a.num_slots > INT32_MAX) return fail(GDN_ERROR_NOT_SUPPORTED, "too many chunks");
-
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return fail(GDN_ERROR_LAUNCH, "hipGetDevice failed");
-    const int cus = compute_units(dev);
-    if (cus <= 0) return fail(GDN_ERROR_LAUNCH, "cannot query the device's compute units");
-    a.part_chunks = gdn::prefill_part_chunks(a.num_tokens, a.num_seqs, a.hv, cus);
-    const int64_t span = a.part_chunks * 64;
-    a.num_part_slots = (a.num_tokens + span - 1) / span + a.num_seqs;
-    const int64_t longest = cu_seqlens ? (a.num_tokens + 63) / 64 : (a.seqlen + 63) / 64;
-    const bool split = a.part_chunks < longest;
-    if (a.num_part_slots * a.hv > INT32_MAX || a.num_seqs * (int64_t)a.hv * (a.dv / 16) > INT32_MAX)
-        return fail(GDN_ERROR_NOT_SUPPORTED, "too many (part, head) pairs");
+    bool split = false;
+    int64_t total = 0;
+    GDN_TRY(plan_prefill(shape, cu_seqlens != nullptr, a, split, total));
     const gdn::PrefillWorkspace wl(a.num_slots, a.num_part_slots, split, a.hv, shape->head_dim_k, shape->head_dim_v,
                                    bf16 ? 2 : 4);
-    keep_pool_memory(dev);
-    void* ws = nullptr;
-    if (hipMallocAsync(&ws, (size_t)wl.total, st) != hipSuccess || !ws) {
-        (void)hipGetLastError();
-        return fail(GDN_ERROR_OUT_OF_MEMORY, "prefill workspace of %lld bytes", (long long)wl.total);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    void* ws = workspace;
+    if (workspace) {
+        if (workspace_bytes < (size_t)total)
+            return fail(GDN_ERROR_INVALID_VALUE, "workspace of %zu bytes, this call needs %lld", workspace_bytes,
+                        (long long)total);
+    } else {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return fail(GDN_ERROR_LAUNCH, "hipGetDevice failed");
+        keep_pool_memory(dev);
+        if (hipMallocAsync(&ws, (size_t)total, st) != hipSuccess || !ws) {
+            (void)hipGetLastError();
+            return fail(GDN_ERROR_OUT_OF_MEMORY, "prefill workspace of %lld bytes", (long long)total);
+        }
     }
     char* wc = static_cast<char*>(ws);
     a.ws_t = wc + wl.t;
@@ -301,8 +323,10 @@ gdn_status prefill_impl(const char* who, const gdn_shape* shape, const void* q, 
     a.ws_b = split ? reinterpret_cast<float*>(wc + wl.b) : nullptr;
     a.ws_s = split ? reinterpret_cast<float*>(wc + wl.s) : nullptr;
     hipError_t e = gdn::launch_prefill(a, bf16, shape->head_dim_k, shape->head_dim_v, st, raw);
-    hipError_t ef = hipFreeAsync(ws, st);
-    if (e == hipSuccess) e = ef;
+    if (!workspace) {
+        const hipError_t ef = hipFreeAsync(ws, st);
+        if (e == hipSuccess) e = ef;
+    }
     if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return fail(GDN_ERROR_LAUNCH, "%s: %s", who, hipGetErrorString(e));
     return GDN_SUCCESS;
@@ -317,6 +341,34 @@ gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, con
                        float* final_state, void* stream) {
     return prefill_impl("prefill", shape, q, k, v, g, beta, init_state, cu_seqlens, out, final_state, 0, nullptr,
                         stream);
+}
+
+gdn_status gdn_prefill_workspace_size(const gdn_shape* shape, int32_t packed, size_t* bytes) {
+    g_last_error[0] = '\0';
+    if (!bytes) return fail(GDN_ERROR_INVALID_VALUE, "bytes is NULL");
+    *bytes = 0;
+    GDN_TRY(check_shape(shape, false));
+    if (!packed && shape->num_seqs > 0 && shape->num_tokens % shape->num_seqs != 0)
+        return fail(GDN_ERROR_INVALID_VALUE, "num_tokens (%lld) is not a multiple of num_seqs (%d) and not packed",
+                    (long long)shape->num_tokens, shape->num_seqs);
+    if (shape->num_seqs == 0) return GDN_SUCCESS;
+    gdn::PrefillArgs a{};
+    bool split = false;
+    int64_t total = 0;
+    GDN_TRY(plan_prefill(shape, packed != 0, a, split, total));
+    *bytes = (size_t)total;
+    return GDN_SUCCESS;
+}
+
+gdn_status gdn_prefill_ws(const gdn_shape* shape, const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const float* init_state, const int32_t* cu_seqlens, void* out,
+                          float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!workspace) {
+        g_last_error[0] = '\0';
+        return fail(GDN_ERROR_INVALID_VALUE, "workspace is NULL");
+    }
+    return prefill_impl("prefill_ws", shape, q, k, v, g, beta, init_state, cu_seqlens, out, final_state, 0, nullptr,
+                        stream, false, workspace, workspace_bytes);
 }
 
 gdn_status gdn_prefill_snapshots(const gdn_shape* shape, const void* q, const void* k, const void* v,

@@ -38,6 +38,7 @@
 #ifndef GDN_H_
 #define GDN_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -106,6 +107,33 @@ gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, con
                        const float* g, const float* beta, const float* init_state,
                        const int32_t* cu_seqlens, void* out, float* final_state,
                        void* stream);
+
+/*
+ * gdn_prefill_workspace_size -- the device workspace, in bytes, that
+ * gdn_prefill_ws needs for `shape` on the current device (the part length L
+ * above depends on the device's compute-unit count).  `packed` is nonzero
+ * when the call will pass cu_seqlens.  Writes 0 when num_seqs is 0.
+ * Host-only: launches nothing and allocates nothing.
+ */
+gdn_status gdn_prefill_workspace_size(const gdn_shape* shape, int32_t packed, size_t* bytes);
+
+/*
+ * gdn_prefill_ws -- gdn_prefill with a caller-owned workspace; allocates
+ * nothing (for callers that manage device memory themselves).  Same
+ * recurrence and outputs as gdn_prefill.
+ *
+ * workspace        DEVICE memory, 256-byte aligned, not NULL, overlapping no
+ *                  other argument.  It needs no initialisation; its contents
+ *                  are undefined afterwards.  It is in use until the call's
+ *                  work on `stream` completes, so calls that share one must
+ *                  be ordered (for instance, on one stream).
+ * workspace_bytes  at least gdn_prefill_workspace_size(shape, cu_seqlens !=
+ *                  NULL) on this device, else GDN_ERROR_INVALID_VALUE.
+ */
+gdn_status gdn_prefill_ws(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                          const float* g, const float* beta, const float* init_state,
+                          const int32_t* cu_seqlens, void* out, float* final_state,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * gdn_prefill_snapshots -- gdn_prefill that also writes the state at every

@@ -28,7 +28,8 @@ def _declared_functions():
 def test_header_declares_the_abi():
     assert _declared_functions() == ["gdn_abi_version", "gdn_decode_slots", "gdn_decode_step", "gdn_decode_tokens",
                                      "gdn_decode_tokens_raw", "gdn_last_error", "gdn_prefill", "gdn_prefill_raw",
-                                     "gdn_prefill_snapshots", "gdn_status_string"]
+                                     "gdn_prefill_snapshots", "gdn_prefill_workspace_size", "gdn_prefill_ws",
+                                     "gdn_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -216,6 +217,40 @@ def test_raw_entry_points_apply_the_same_argument_checks():
     rc = L.gdn_decode_tokens_raw(ctypes.byref(_shape(num_seqs=4, num_tokens=12)), 3, c(FAKE), c(FAKE), c(FAKE),
                                  None, c(FAKE), c(FAKE), c(FAKE), None, None)
     assert rc == B.GDN_ERROR_INVALID_VALUE and "g is NULL" in L.gdn_last_error().decode()
+
+
+def _prefill_ws(shape, ws, nbytes):
+    c = ctypes.c_void_p
+    L = _lib()
+    rc = L.gdn_prefill_ws(ctypes.byref(shape), c(FAKE), c(FAKE), c(FAKE), c(FAKE), c(FAKE), None, None, c(FAKE),
+                          None, c(ws) if ws else None, nbytes, None)
+    return rc, L.gdn_last_error().decode()
+
+
+@pytest.mark.parametrize("ws,status,msg", [
+    (None, B.GDN_ERROR_INVALID_VALUE, "workspace is NULL"),
+    (FAKE + 16, B.GDN_ERROR_INVALID_VALUE, "aligned"),
+])
+def test_prefill_ws_rejects_bad_workspace(ws, status, msg):
+    rc, err = _prefill_ws(_shape(), ws, 1 << 20)
+    assert rc == status and msg in err, (rc, err)
+
+
+def test_prefill_ws_applies_the_prefill_checks():
+    rc, err = _prefill_ws(_shape(num_qk_heads=3, num_v_heads=4), FAKE, 1 << 20)
+    assert rc == B.GDN_ERROR_INVALID_VALUE and "multiple" in err
+
+
+def test_prefill_workspace_size_host_paths():
+    L = _lib()
+    n = ctypes.c_size_t(123)
+    assert L.gdn_prefill_workspace_size(ctypes.byref(_shape()), 0, None) == B.GDN_ERROR_INVALID_VALUE
+    assert L.gdn_prefill_workspace_size(None, 0, ctypes.byref(n)) == B.GDN_ERROR_INVALID_VALUE and n.value == 0
+    rc = L.gdn_prefill_workspace_size(ctypes.byref(_shape(num_seqs=3, num_tokens=64)), 0, ctypes.byref(n))
+    assert rc == B.GDN_ERROR_INVALID_VALUE and "not packed" in L.gdn_last_error().decode()
+    n.value = 123
+    rc = L.gdn_prefill_workspace_size(ctypes.byref(_shape(num_seqs=0, num_tokens=0)), 1, ctypes.byref(n))
+    assert rc == B.GDN_SUCCESS and n.value == 0
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch):

@@ -413,3 +413,40 @@ def test_decode_tokens_raw(dtype, T):
     eo, es, et = rel_err(host64(out), ro), rel_err(host64(state), rf), rel_err(host64(ts), rs)
     say(f"[parity] decode_tokens_raw {dtype} T={T}: out {eo:.3e} state {es:.3e} token states {et:.3e}")
     assert eo <= TOL[dtype] and es <= TOL[dtype] and et <= TOL[dtype]
+
+
+# ------------------------------------------------- caller-owned workspace
+@pytest.mark.parametrize("dtype,lens,packed", [("bf16", (4096,), False), ("f32", (300, 0, 1000, 65), True),
+                                               ("bf16", (128, 128, 128), False)])
+def test_prefill_with_caller_workspace_matches_pool_workspace(dtype, lens, packed):
+    """gdn_prefill_ws on a caller buffer gives gdn_prefill's bits, on parts (one long sequence) and on
+    packed ragged sequences; the buffer's prior contents do not matter; and the oracle agrees."""
+    inp = gi.make_inputs(gi.custom(dtype=dtype, Hqk=2, Hv=4, dk=128, dv=128, seqlens=lens,
+                                   init_state="normal"), seed=80)
+    q, k, v, g, beta = (dev(x) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
+    init = dev(inp.init_state)
+    cu = dev(inp.cu_seqlens) if packed else None
+    N = len(lens)
+    kw = dict(cu_seqlens=cu) if packed else dict(num_seqs=N)
+    need = B.gdn_prefill_workspace_size(q, v, **kw)
+    assert need > 0
+    ref_o, ref_f = B.gdn_prefill(q, k, v, g, beta, init, **kw)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+    for _ in range(2):   # the second call finds the first call's leftovers in the workspace
+        o, f = B.gdn_prefill(q, k, v, g, beta, init, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(f, ref_f)
+    if packed:
+        ro, rf = c_oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.init_state, inp.cu_seqlens)
+        assert rel_err(host64(o), ro) <= TOL[dtype] and rel_err(host64(f), rf) <= TOL[dtype]
+
+
+def test_prefill_with_too_small_workspace_is_rejected():
+    inp = gi.make_inputs(gi.custom(dtype="bf16", Hqk=1, Hv=1, dk=128, dv=128, seqlens=(4096,)), seed=81)
+    q, k, v, g, beta = (dev(x) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
+    need = B.gdn_prefill_workspace_size(q, v)
+    ws = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.GdnError, match="workspace of"):
+        B.gdn_prefill(q, k, v, g, beta, workspace=ws)
+    with pytest.raises(ValueError):
+        B.gdn_prefill(q, k, v, g, beta, workspace=ws, raw=True)

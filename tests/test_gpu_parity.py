@@ -401,6 +401,40 @@ def test_prefill_raw_long_sequence_in_parts(dtype):
     _check_raw_prefill(inp, TOL[dtype], f"prefill_raw parts {dtype}")
 
 
+def _guard_rows(inp, dtype):
+    """Tokens t = 0 mod 5 get q, k rows of squared norm 1e-6 (the guard's own size), tokens t = 0 mod 7
+    get zero q, k rows (normalised to zero by the guard instead of dividing by zero)."""
+    for name in ("q", "k"):
+        x = gi.to_f64(getattr(inp, name), dtype)
+        x[::5] *= 1e-3 / np.linalg.norm(x[::5], axis=-1, keepdims=True)
+        x[::7] = 0.0
+        x = x.astype(np.float32)
+        setattr(inp, name, gi.f32_to_bf16_bits(x) if dtype == "bf16" else x)
+    return inp
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_raw_guard_sized_and_zero_rows(dtype):
+    inp = gi.make_inputs(gi.custom(dtype=dtype, Hqk=2, Hv=4, dk=128, dv=64, seqlens=(150, 64, 33),
+                                   init_state="normal", raw=True), seed=74)
+    _check_raw_prefill(_guard_rows(inp, dtype), TOL[dtype], f"prefill_raw guard rows {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_tokens_raw_guard_sized_and_zero_rows(dtype):
+    T = 5
+    inp = _guard_rows(gi.make_inputs(gi.custom(dtype=dtype, Hqk=2, Hv=4, dk=128, dv=128, seqlens=(T,) * 7,
+                                                init_state="normal", raw=True), seed=75), dtype)
+    state = dev(inp.init_state)
+    out, _ = B.gdn_decode_tokens(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), state, T,
+                                 raw=True)
+    torch.cuda.synchronize()
+    ro, _, rf = c_oracle.decode_tokens(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.init_state, T, raw=True)
+    eo, ef = rel_err(host64(out), ro), rel_err(host64(state), rf)
+    say(f"[parity] decode_tokens_raw guard rows {dtype}: out {eo:.3e} state {ef:.3e}")
+    assert eo <= TOL[dtype] and ef <= TOL[dtype]
+
+
 @pytest.mark.parametrize("dtype,T", [("f32", 1), ("f32", 4), ("bf16", 3)])
 def test_decode_tokens_raw(dtype, T):
     inp = gi.make_inputs(gi.custom(dtype=dtype, Hqk=2, Hv=4, dk=128, dv=64, seqlens=(T,) * 5,

@@ -425,6 +425,31 @@ def test_raw_prologue_saturated_logits_give_no_decay_and_full_write():
     assert _rel(o1, o2) <= 1e-5 and _rel(f1, f2) <= 1e-5
 
 
+def test_raw_prologue_guard_halves_rows_of_squared_norm_1e6():
+    """Rows with |x|^2 = 1e-6 meet the 1e-6 guard: x / sqrt(|x|^2 + 1e-6) = x_hat / sqrt(2).  With zero
+    logits (alpha = beta = 1/2) the raw path must equal the plain recurrence on q_hat / sqrt(2) and
+    k_hat / sqrt(2); a guard of any other size (or none) gives a different row scale."""
+    rng = np.random.default_rng(64)
+    T, H, dk, dv = 24, 2, 8, 5
+    qh = rng.standard_normal((T, 1, dk))
+    kh = rng.standard_normal((T, 1, dk))
+    qh /= np.linalg.norm(qh, axis=-1, keepdims=True)
+    kh /= np.linalg.norm(kh, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, H, dv)).astype(np.float32)
+    q32, k32 = (1e-3 * qh).astype(np.float32), (1e-3 * kh).astype(np.float32)
+    z = np.zeros((T, H), dtype=np.float32)
+    o1, f1 = c_oracle.prefill(q32, k32, v, z, z, raw=True)
+    q64, k64 = q32.astype(np.float64), k32.astype(np.float64)
+    qs = q64 / np.linalg.norm(q64, axis=-1, keepdims=True) / math.sqrt(2.0)
+    ks = k64 / np.linalg.norm(k64, axis=-1, keepdims=True) / math.sqrt(2.0)
+    o2, f2 = ref.sequential(qs, ks, v.astype(np.float64), np.full((T, H), -math.log(2.0)), np.full((T, H), 0.5))
+    assert _rel(o1, o2) <= 1e-6 and _rel(f1, f2) <= 1e-6
+    # and the guard is what makes the difference: unit rows would give sqrt(2) larger outputs
+    o3, _ = ref.sequential(qs * math.sqrt(2.0), ks * math.sqrt(2.0), v.astype(np.float64),
+                           np.full((T, H), -math.log(2.0)), np.full((T, H), 0.5))
+    assert _rel(o1, o3) > 0.1
+
+
 def test_raw_decode_tokens_equals_raw_prefill():
     rng = np.random.default_rng(63)
     N, T = 3, 4

@@ -484,3 +484,42 @@ def test_prefill_with_too_small_workspace_is_rejected():
         B.gdn_prefill(q, k, v, g, beta, workspace=ws)
     with pytest.raises(ValueError):
         B.gdn_prefill(q, k, v, g, beta, workspace=ws, raw=True)
+
+
+# ------------------------------------------------------ seeded shape sweep
+def _sweep_case(i):
+    r = np.random.default_rng(1000 + i)
+    dtype = ["f32", "bf16"][int(r.integers(2))]
+    dk, dv = (int(x) for x in r.choice([64, 128], size=2))
+    hqk = int(r.choice([1, 2, 4]))
+    hv = hqk * int(r.choice([1, 2])) if hqk == 4 else hqk * int(r.choice([1, 2, 4]))
+    n = int(r.integers(1, 6))
+    edge = [0, 1, 63, 64, 65, 127, 128, 129]
+    lens = [int(r.choice(edge)) if r.random() < 0.5 else int(r.integers(1, 600)) for _ in range(n)]
+    if i % 4 == 1:
+        lens[0] = int(r.integers(1500, 3000))   # few chains, long sequence: cut into parts
+    init = "normal" if r.random() < 0.6 else "zero"
+    raw = i % 4 == 3
+    return dict(dtype=dtype, Hqk=hqk, Hv=hv, dk=dk, dv=dv, seqlens=tuple(lens), init_state=init, raw=raw)
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_seeded_shape_sweep(i):
+    """Random shapes (dtype, head dims, grouped value heads, ragged and edge lengths, parts, initial
+    state, raw projections) against the oracle; the caller-workspace path must give the same bits."""
+    c = _sweep_case(i)
+    say(f"[sweep {i}] {c}")
+    inp = gi.make_inputs(gi.custom(**c), seed=2000 + i)
+    if c["raw"]:
+        _check_raw_prefill(inp, TOL[c["dtype"]], f"sweep {i} raw")
+        return
+    check_prefill(inp, label=f"sweep {i}")
+    q, k, v, g, beta = (dev(x) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
+    cu = dev(inp.cu_seqlens) if inp.cu_seqlens is not None else None
+    kw = dict(cu_seqlens=cu) if cu is not None else dict(num_seqs=len(c["seqlens"]))
+    s0 = dev(inp.init_state)
+    ref_o, ref_f = B.gdn_prefill(q, k, v, g, beta, s0, **kw)
+    ws = torch.empty(max(B.gdn_prefill_workspace_size(q, v, **kw), 256), dtype=torch.uint8, device="cuda")
+    o, f = B.gdn_prefill(q, k, v, g, beta, s0, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(f, ref_f)

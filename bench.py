@@ -272,6 +272,39 @@ def main():
     del q, k, v, g, beta, out
     torch.cuda.empty_cache()
 
+    # the two smaller prefill workloads, reported beside the headline: 4,096 tokens x 16 heads, and 8
+    # packed sequences of U[1024, 16384] tokens with 32 value heads on 16 q/k heads and initial states
+    other = None
+    if not args.no_variants:
+        other = {}
+        for name, reps in (("prefill_4k", 50), ("varlen_8x", 10)):
+            o_inp = gi.make_inputs(name, seed=0)
+            ow = o_inp.wl
+            oq, ok, ov, og, ob = (dev(x) for x in (o_inp.q, o_inp.k, o_inp.v, o_inp.g, o_inp.beta))
+            ocu = dev(o_inp.cu_seqlens) if o_inp.cu_seqlens is not None else None
+            os0 = dev(o_inp.init_state) if o_inp.init_state is not None else None
+            kw = dict(cu_seqlens=ocu) if ocu is not None else dict(num_seqs=ow.num_seqs)
+            oo = torch.empty((ow.total_tokens, ow.num_v_heads, ow.head_dim_v), dtype=torch.bfloat16, device="cuda")
+            of = torch.empty((ow.num_seqs, ow.num_v_heads, ow.head_dim_v, ow.head_dim_k), dtype=torch.float32,
+                             device="cuda")
+            for _ in range(3):
+                B.gdn_prefill(oq, ok, ov, og, ob, os0, out=oo, final_state=of, **kw)
+            torch.cuda.synchronize()
+            oev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for a, b in oev:
+                a.record(stream)
+                B.gdn_prefill(oq, ok, ov, og, ob, os0, out=oo, final_state=of, **kw)
+                b.record(stream)
+            torch.cuda.synchronize()
+            t = np.array([a.elapsed_time(b) for a, b in oev])
+            other[name] = {"workload": f"{name}: {ow.num_seqs} seq(s), {ow.total_tokens} tokens, H_qk={ow.num_qk_heads}, "
+                                       f"H_v={ow.num_v_heads}, d={ow.head_dim_k}, bf16",
+                           "ms_median": round(float(np.median(t)), 4),
+                           "tokens_per_s": round(ow.total_tokens / (float(np.median(t)) * 1e-3), 1)}
+            log(f"{name}: median {np.median(t):.4f} ms/call, {other[name]['tokens_per_s'] / 1e6:.1f} M tokens/s")
+            del oq, ok, ov, og, ob, ocu, os0, oo, of, o_inp
+        torch.cuda.empty_cache()
+
     # ------------------------------------------------------------- decode leg
     decode = None
     if not args.no_decode:
@@ -408,6 +441,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_p10_median_p90": [round(float(np.percentile(per_call_ms, x)), 4) for x in (10, 50, 90)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -426,6 +460,7 @@ def main():
         "decode": decode,
         "prefill_snapshots": snapshot_rec,
         "prefill_raw": raw_rec,
+        "prefill_other_workloads": other,
     }
     print(json.dumps(rec), flush=True)
 

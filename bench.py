@@ -60,11 +60,25 @@ def decode_tokens_bytes(N, T, hqk, hv, dk, dv, elem=2, token_states=True):
     return 2 * st + (T * st if token_states else 0) + N * T * (2 * hqk * dk + 2 * hv * dv) * elem + N * T * hv * 8
 
 
-def _sha(paths):
+def _code_text(text):
+    """Source text without comments and blank lines (so that a comment edit does not
+    count as a change of the kernels; string literals in these files hold no comment marks)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
+def _sha(paths, read=None):
+    """Hash of the kernel sources' code (comments and blank lines dropped)."""
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        if read is None:
+            with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+                text = f.read()
+        else:
+            text = read(p)
+        h.update(_code_text(text).encode())
     return h.hexdigest()[:16]
 
 

@@ -1210,8 +1210,9 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
         f32x4 bcur[PER];
 #pragma unroll
         for (int k = 0; k < PER; ++k) bcur[k] = bnext[k];
-        // this wave's share of M_p (and B_p) is in; the PER * 4 newest memory
-        // operations, the stores of S_p, may still be in flight
+        // this wave's share of M_p is in; the PER * 4 newest memory operations
+        // may still be in flight: the stores of S_p, or at p = 0 the loads of
+        // B_0, whose registers the compiler waits for where they are read
         __builtin_amdgcn_s_waitcnt(kWaitVm0 | ((PER * 4) & 15) | (((PER * 4) >> 4) << 14));
         __syncthreads();                                 // everyone's is; S_p is written
         if (p + 2 < np) {

@@ -231,7 +231,8 @@ namespace {
 
 // The part length, slot counts and workspace layout of one prefill call on
 // the current device; `packed` tells whether cu_seqlens will be given.
-gdn_status plan_prefill(const gdn_shape* shape, bool packed, gdn::PrefillArgs& a, bool& split, int64_t& total) {
+gdn_status plan_prefill(const gdn_shape* shape, bool packed, bool raw, gdn::PrefillArgs& a, bool& split,
+                        int64_t& total) {
     a.num_tokens = shape->num_tokens;
     a.seqlen = shape->num_tokens / shape->num_seqs;
     a.num_seqs = shape->num_seqs;
@@ -252,7 +253,7 @@ gdn_status plan_prefill(const gdn_shape* shape, bool packed, gdn::PrefillArgs& a
     if (a.num_part_slots * a.hv > INT32_MAX || a.num_seqs * (int64_t)a.hv * (a.dv / 16) > INT32_MAX)
         return fail(GDN_ERROR_NOT_SUPPORTED, "too many (part, head) pairs");
     const gdn::PrefillWorkspace wl(a.num_slots, a.num_part_slots, split, a.hv, shape->head_dim_k, shape->head_dim_v,
-                                   shape->dtype == GDN_DTYPE_BF16 ? 2 : 4);
+                                   shape->dtype == GDN_DTYPE_BF16 ? 2 : 4, raw);
     total = wl.total;
     return GDN_SUCCESS;
 }
@@ -298,9 +299,9 @@ gdn_status prefill_impl(const char* who, const gdn_shape* shape, const void* q, 
     a.init_state = init_state; a.cu = cu_seqlens; a.out = out; a.final_state = final_state;
     bool split = false;
     int64_t total = 0;
-    GDN_TRY(plan_prefill(shape, cu_seqlens != nullptr, a, split, total));
+    GDN_TRY(plan_prefill(shape, cu_seqlens != nullptr, raw, a, split, total));
     const gdn::PrefillWorkspace wl(a.num_slots, a.num_part_slots, split, a.hv, shape->head_dim_k, shape->head_dim_v,
-                                   bf16 ? 2 : 4);
+                                   bf16 ? 2 : 4, raw);
     hipStream_t st = static_cast<hipStream_t>(stream);
     void* ws = workspace;
     if (workspace) {
@@ -319,6 +320,7 @@ gdn_status prefill_impl(const char* who, const gdn_shape* shape, const void* q, 
     char* wc = static_cast<char*>(ws);
     a.ws_t = wc + wl.t;
     a.ws_g = reinterpret_cast<double*>(wc + wl.g);
+    a.ws_ik = raw ? reinterpret_cast<float*>(wc + wl.ik) : nullptr;
     a.ws_m = split ? reinterpret_cast<float*>(wc + wl.m) : nullptr;
     a.ws_b = split ? reinterpret_cast<float*>(wc + wl.b) : nullptr;
     a.ws_s = split ? reinterpret_cast<float*>(wc + wl.s) : nullptr;
@@ -355,7 +357,7 @@ gdn_status gdn_prefill_workspace_size(const gdn_shape* shape, int32_t packed, si
     gdn::PrefillArgs a{};
     bool split = false;
     int64_t total = 0;
-    GDN_TRY(plan_prefill(shape, packed != 0, a, split, total));
+    GDN_TRY(plan_prefill(shape, packed != 0, false, a, split, total));
     *bytes = (size_t)total;
     return GDN_SUCCESS;
 }

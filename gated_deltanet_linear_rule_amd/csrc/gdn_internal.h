@@ -47,6 +47,7 @@ struct PrefillArgs {
     void* ws_t;                // T~ = (I + A)^{-1} diag(beta) as 6 operand fragments
     double* ws_g;              // 1 KB gate record: 64 log2-scaled cumulative gates (fp64),
                                // then 64 gamma and 64 D (fp32)
+    float* ws_ik;              // raw projections only: 64 values 1 / |k_t| (256 B)
     // Per (part slot, value head), fp32 row-major; NULL when no sequence has
     // more than one part:
     float* ws_m;               // d_k x d_k transition M_p of the part
@@ -62,13 +63,15 @@ struct PrefillArgs {
 // Workspace layout of one prefill call (byte offsets of each part and total),
 // element size 2 for bf16, 4 for fp32.
 struct PrefillWorkspace {
-    int64_t t, g, m, b, s, total;
-    PrefillWorkspace(int64_t num_slots, int64_t num_part_slots, bool split, int hv, int dk, int dv, int elem_size) {
+    int64_t t, g, ik, m, b, s, total;
+    PrefillWorkspace(int64_t num_slots, int64_t num_part_slots, bool split, int hv, int dk, int dv, int elem_size,
+                     bool raw = false) {
         auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
         const int64_t blocks = num_slots * hv, pblocks = split ? num_part_slots * hv : 0;
         t = 0;
         g = t + up(blocks * 6 * 64 * 8 * (int64_t)elem_size);
-        m = g + up(blocks * 1024);
+        ik = g + up(blocks * 1024);
+        m = ik + (raw ? up(blocks * 256) : 0);
         b = m + up(pblocks * dk * dk * 4);
         s = b + up(pblocks * dv * dk * 4);
         total = s + up(pblocks * dv * dk * 4);

@@ -374,6 +374,8 @@ __global__ __launch_bounds__(kWave * kPrepWaves) void gdn_prep_kernel(PrefillArg
     ws_store(rec + l, G);
     ws_store(reinterpret_cast<float*>(rec + kChunk) + l, fast_exp2((float)G) * ikl);
     ws_store(reinterpret_cast<float*>(rec + kChunk) + kChunk + l, fast_exp2((float)(Gl - G)) * ikl);
+    // and 1 / |k_t| itself, for the output kernel's intra-chunk products
+    if constexpr (RAW) ws_store(a.ws_ik + blk * kChunk + l, ikl);
 }
 
 // ===========================================================================
@@ -520,8 +522,9 @@ constexpr int kWaitVm0 = 0x0F70;
 // loads still in flight (those target the other buffer set).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// One chunk's inputs in LDS.
-template <typename OP, int DK, int DV, bool OUT>
+// One chunk's inputs in LDS.  IKB: also 1 / |k_t| of the raw-projection
+// prefill (64 values; the 1 KB region is what one direct load writes).
+template <typename OP, int DK, int DV, bool OUT, bool IKB = false>
 struct ChunkBuf {
     alignas(16) OP K[kChunk * DK];
     alignas(16) OP V[kChunk * DV];
@@ -530,6 +533,7 @@ struct ChunkBuf {
     alignas(16) double G2[kChunk];          // gate record: G2, gamma, D
     alignas(16) float gam[kChunk];
     alignas(16) float dec[kChunk];
+    alignas(16) float IK[IKB ? 256 : 4];
 };
 
 // Geometry of the chunk kernels: one wave per 16 state rows (two waves per
@@ -611,7 +615,7 @@ __device__ __forceinline__ void sched_fence() {
 // their target after them), stage 1 once the products of Y are issued, stage
 // 2 between U and the state update.
 template <typename OP, int DK, int DV, bool OUT, int NR, int VMASK, int NW, bool RAW, typename F>
-__device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, OP* P, OP* kt, OP* ost,
+__device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT, OUT && RAW>& cb, OP* P, OP* kt, OP* ost,
                                            f32x4 (&ST)[NR][DK / 16], const int (&R0)[NR], int w, F&& hook,
                                            float* nrm) {
     using Ops = Op<OP>;
@@ -650,28 +654,17 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT>& cb, 
                 for (int k2 = 0; k2 < NKK; ++k2) a1 = Ops::mma(p1[k2], pq[k2], a1);
             }
             if constexpr (RAW) {
-                // 1 / |q_t| for this lane's row t and 1 / |k_s| for the rows of
-                // the two K tiles, from the operand fragments already loaded;
-                // 1 / |q| goes to nrm[0, 64) for the outputs, 1 / |k| through
-                // nrm[64, 128) to the lanes whose columns need it
-                float sq = 0.f, s0 = 0.f, s1 = 0.f;
+                // 1 / |q_t| for this lane's row t from the Q fragments already
+                // loaded (kept in nrm for the outputs' gamma after the barrier in
+                // the middle, written once per row tile); 1 / |k_s| from the prep
+                // kernel, loaded with the chunk
+                float sq = 0.f;
 #pragma unroll
-                for (int k2 = 0; k2 < NKK; ++k2) {
-                    sq += frag_sq<OP>(pq[k2]);
-                    s0 += frag_sq<OP>(p0[k2]);
-                    if (two) s1 += frag_sq<OP>(p1[k2]);
-                }
+                for (int k2 = 0; k2 < NKK; ++k2) sq += frag_sq<OP>(pq[k2]);
                 const float iq = 1.f / sqrtf(sum_groups(sq) + kNormEps);
-                const float ik0 = 1.f / sqrtf(sum_groups(s0) + kNormEps);
-                const float ik1 = 1.f / sqrtf(sum_groups(s1) + kNormEps);
-                if (gq == 0) {
-                    nrm[t] = iq;
-                    nrm[kChunk + 32 * kk + n] = ik0;
-                    if (two) nrm[kChunk + 32 * kk + 16 + n] = ik1;
-                }
-                wave_lds_sync();
-                a0 = a0 * iq * *reinterpret_cast<const f32x4*>(&nrm[kChunk + 32 * kk + 4 * gq]);
-                if (two) a1 = a1 * iq * *reinterpret_cast<const f32x4*>(&nrm[kChunk + 32 * kk + 16 + 4 * gq]);
+                if (kk == 0 && gq == 0) nrm[t] = iq;
+                a0 = a0 * iq * *reinterpret_cast<const f32x4*>(&cb.IK[32 * kk + 4 * gq]);
+                if (two) a1 = a1 * iq * *reinterpret_cast<const f32x4*>(&cb.IK[32 * kk + 16 + 4 * gq]);
             }
             quad v0, v1;
 #pragma unroll
@@ -873,7 +866,7 @@ template <typename OP, int DK, int DV, bool OUT, bool RAW>
 __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) void gdn_chunk_kernel(PrefillArgs a) {
     using G = ChunkGeom<OP, DK, DV, OUT>;
     static_assert(G::NT == 64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16), "launch bound must equal the launch size");
-    using Buf = ChunkBuf<OP, DK, DV, OUT>;
+    using Buf = ChunkBuf<OP, DK, DV, OUT, OUT && RAW>;
     constexpr int NR = G::NR, NW = G::NW, NBUF = G::NBUF;
     constexpr int NVB = DV / 16, NMB = DK / 16, NDB = DK / 16;
     constexpr int E = (int)sizeof(OP), FU = Units<OP>::FU;
@@ -887,7 +880,7 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
     constexpr int KTF = 2 * (DK / 16);
     constexpr int KTS = KT ? KTF * 64 * 8 : 8;
     __shared__ OP Kt[(G::KTA ? 2 : 1) * KTS];
-    __shared__ float Nrm[OUT && RAW ? 2 * kChunk : 1];   // raw projections: 1 / |q|, 1 / |k| of the chunk
+    __shared__ float Nrm[OUT && RAW ? kChunk : 1];   // raw projections: 1 / |q| of the chunk's tokens
 
     const int l = lane_id(), w = wave_id(), n = l & 15, gq = l >> 4;
     const int64_t pslot = blockIdx.x / a.hv;
@@ -971,6 +964,9 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
     auto res_o = [&](int64_t j) { return rsrc(at(oB0, vstep, j), j == jl ? vlast : vfull); };
     auto res_t = [&](int64_t j) { return rsrc(at(tB0, tstep, j), UT * 1024); };
     auto res_g = [&](int64_t j) { return rsrc(at(gB0, gstep, j), kGateRecord); };
+    const char* const ikB0 = OUT && RAW ? reinterpret_cast<const char*>(a.ws_ik) + ((size_t)(cbase + jb) * a.hv + h) * (kChunk * 4)
+                                        : nullptr;
+    auto res_ik = [&](int64_t j) { return rsrc(at(ikB0, (uint32_t)a.hv * (kChunk * 4), j), kChunk * 4); };
 
     // Direct loads of chunk j's rows, T~ and gates into `B` (spread over the waves).
     auto issue = [&](int64_t j, Buf& B) {
@@ -993,6 +989,9 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
         for (int k = 0; k < (UT + NW - 1) / NW; ++k)
             if (UT % NW == 0 || w + NW * k < UT) bytes_to_lds(B.T, rt, w + NW * k);
         if (w == NW - 1) bytes_to_lds(B.G2, res_g(j), 0);   // gate record: exactly 1 KB
+        if constexpr (OUT && RAW) {
+            if (w == NW - 2) bytes_to_lds(B.IK, res_ik(j), 0);   // 256 B; the rest reads as zero
+        }
     };
 
     // O rows of chunk j, staged in Ost, to global memory (rows past the end dropped)

@@ -228,7 +228,8 @@ gdn_status gdn_decode_slots(const gdn_shape* shape, int32_t tokens_per_seq, cons
  * das Modell", item 1 -- but print none of these formulas; they are the usual
  * forms and give the input distributions the rest of this library is
  * measured on.)  All other arguments, layouts and rules are those of
- * gdn_prefill and gdn_decode_tokens.
+ * gdn_prefill and gdn_decode_tokens; gdn_prefill_raw's pool workspace is
+ * larger by (num_tokens / 64 + N) * Hv * 256 bytes (1 / |k| per token).
  */
 gdn_status gdn_prefill_raw(const gdn_shape* shape, const void* q, const void* k, const void* v, const float* a_gate,
                            const float* b_beta, const float* init_state, const int32_t* cu_seqlens, void* out,

@@ -655,14 +655,14 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT, OUT &
             }
             if constexpr (RAW) {
                 // 1 / |q_t| for this lane's row t from the Q fragments already
-                // loaded (kept in nrm for the outputs' gamma after the barrier in
-                // the middle, written once per row tile); 1 / |k_s| from the prep
-                // kernel, loaded with the chunk
+                // loaded (gamma_t / |q_t| is kept in nrm for the outputs after the
+                // barrier in the middle, written once per row tile); 1 / |k_s|
+                // from the prep kernel, loaded with the chunk
                 float sq = 0.f;
 #pragma unroll
                 for (int k2 = 0; k2 < NKK; ++k2) sq += frag_sq<OP>(pq[k2]);
                 const float iq = 1.f / sqrtf(sum_groups(sq) + kNormEps);
-                if (kk == 0 && gq == 0) nrm[t] = iq;
+                if (kk == 0 && gq == 0) nrm[t] = fast_exp2((float)gt) * iq;
                 a0 = a0 * iq * *reinterpret_cast<const f32x4*>(&cb.IK[32 * kk + 4 * gq]);
                 if (two) a1 = a1 * iq * *reinterpret_cast<const f32x4*>(&cb.IK[32 * kk + 16 + 4 * gq]);
             }
@@ -837,7 +837,7 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT, OUT &
         for (int f = 0; f < kTriFrags; ++f) pf[f] = lds_frag(P, f);
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
-            gt[tb] = RAW ? fast_exp2((float)cb.G2[16 * tb + n]) * nrm[16 * tb + n] : cb.gam[16 * tb + n];
+            gt[tb] = RAW ? nrm[16 * tb + n] : cb.gam[16 * tb + n];
     }
     sched_fence<!OUT>();
     mmS(k1, HD);
@@ -880,7 +880,7 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
     constexpr int KTF = 2 * (DK / 16);
     constexpr int KTS = KT ? KTF * 64 * 8 : 8;
     __shared__ OP Kt[(G::KTA ? 2 : 1) * KTS];
-    __shared__ float Nrm[OUT && RAW ? kChunk : 1];   // raw projections: 1 / |q| of the chunk's tokens
+    __shared__ float Nrm[OUT && RAW ? kChunk : 1];   // raw projections: gamma_t / |q_t| of the chunk
 
     const int l = lane_id(), w = wave_id(), n = l & 15, gq = l >> 4;
     const int64_t pslot = blockIdx.x / a.hv;

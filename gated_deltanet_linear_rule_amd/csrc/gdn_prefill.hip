@@ -1009,49 +1009,10 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
             }
         }
     };
-    // L2 prefetch (bf16 summary): while chunk j + 1 loads into LDS, one 4-byte
-    // load per 128-byte line of chunk j + 2 pulls that chunk into L2, so its
-    // own LDS loads, issued a chunk later, hit L2.  The loaded words are
-    // consumed two chunks later, after the wait that covers them, so these
-    // loads never hold up a chunk.  Lines: K, V rows, T~, gate record; one
-    // 64-lane load per 64 lines of one array; every wave issues TPW loads
-    // (spare ones read out of range: no traffic).  The output kernel does
-    // without: there the registers and scalar work cost more than it saves
-    // (measured).
-    constexpr int LK = kChunk * DK * E / 128, LV = kChunk * DV * E / 128, LT = UT * 8;
-    constexpr int IK = (LK + 63) / 64, IV = (LV + 63) / 64, IT = (LT + 63) / 64;
-    constexpr int NI = (OUT ? 2 * IK : IK) + IV + IT + 1;
-    constexpr int TPW = (NBUF == 2 && !OUT) ? (NI + NW - 1) / NW : 0;
-    uint32_t tvA[TPW > 0 ? TPW : 1] = {}, tvB[TPW > 0 ? TPW : 1] = {}, sink = 0;
-    auto touch = [&](int64_t j, uint32_t (&tv)[TPW > 0 ? TPW : 1]) {
-#pragma unroll
-        for (int k = 0; k < TPW; ++k) {
-            const int slot = w + NW * k;   // wave-uniform: one resource per load
-            auto rows = [&](int sub, int lines_per_row, unsigned stride) {
-                const int li = 64 * sub + l;
-                return (unsigned)(li / lines_per_row) * stride + (unsigned)(li % lines_per_row) * 128;
-            };
-            uint32_t x;
-            if (slot < IK) x = __builtin_amdgcn_raw_buffer_load_b32(res_k(j), rows(slot, DK * E / 128, kstride), 0, 0);
-            else if (OUT && slot < 2 * IK) x = __builtin_amdgcn_raw_buffer_load_b32(res_q(j), rows(slot - IK, DK * E / 128, kstride), 0, 0);
-            else if (slot < (OUT ? 2 * IK : IK) + IV)
-                x = __builtin_amdgcn_raw_buffer_load_b32(res_v(j), rows(slot - (OUT ? 2 * IK : IK), DV * E / 128, vstride), 0, 0);
-            else if (slot < NI - 1) x = __builtin_amdgcn_raw_buffer_load_b32(res_t(j), (unsigned)(64 * (slot - (NI - 1 - IT)) + l) * 128, 0, 0);
-            else x = __builtin_amdgcn_raw_buffer_load_b32(res_g(j), slot == NI - 1 ? (unsigned)l * 128 : 0xFFFFF000u, 0, 0);
-            tv[k] = x;
-        }
-    };
-    auto consume = [&](uint32_t (&tv)[TPW > 0 ? TPW : 1]) {
-#pragma unroll
-        for (int k = 0; k < TPW; ++k) sink ^= tv[k];
-    };
     // output: the next count of finished chunks at which a snapshot is due
     int64_t next_snap = a.snapshots ? (jb / a.snap_chunks + 1) * a.snap_chunks : -1;
-    auto body = [&](int64_t j, const Buf& cur, Buf& nxt, uint32_t (&tv)[TPW > 0 ? TPW : 1]) {
-        // this wave's loads of chunk j have landed (the TPW newest loads are the
-        // L2 prefetch of chunk j + 1)
-        if constexpr (TPW == 0) __builtin_amdgcn_s_waitcnt(kWaitVm0);
-        else __builtin_amdgcn_s_waitcnt(kWaitVm0 | (TPW & 15) | ((TPW >> 4) << 14));
+    auto body = [&](int64_t j, const Buf& cur, Buf& nxt) {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's loads of chunk j have landed
         lds_barrier();                          // everyone's have; the previous chunk is done everywhere
         if constexpr (OUT) {
             if (j > jb) store_o(j - 1);
@@ -1059,10 +1020,6 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
         auto next_loads = [&](int stage) {
             if (stage != 0) return;
             if (NBUF == 2 && j + 1 < je) issue(j + 1, nxt);
-            if constexpr (TPW > 0) {
-                consume(tv);
-                touch(j + 2 < je ? j + 2 : je - 1, tv);
-            }
         };
         if constexpr (OUT) {
             chunk_step<OP, DK, DV, OUT, NR, 1, NW, RAW>(cur, Pf, Kt, Ost, ST, R0, w, next_loads, Nrm);
@@ -1092,16 +1049,14 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
         // chunk needs one barrier.
         issue(jb, bufs[0]);
         if (jb + 1 < je) issue(jb + 1, bufs[1]);
-        if constexpr (TPW > 0) touch(jb + 2 < je ? jb + 2 : je - 1, tvB);
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
         lds_barrier();
         transpose_kt<OP, DK, NW>(bufs[0].K, Kt + (jb & 1) * KTS, w);
         int bc = 0;                                   // buffer set of chunk j
-        auto body3 = [&](int64_t j, uint32_t (&tv)[TPW > 0 ? TPW : 1]) {
-            // chunk j + 1's rows have landed (the TPW newest loads are the L2
-            // prefetch of chunk j + 2); everyone's K^T fragments of chunk j are
-            // written and chunk j - 1 is done everywhere
-            __builtin_amdgcn_s_waitcnt(kWaitVm0 | (TPW & 15) | ((TPW >> 4) << 14));
+        auto body3 = [&](int64_t j) {
+            // chunk j + 1's rows have landed; everyone's K^T fragments of chunk
+            // j are written and chunk j - 1 is done everywhere
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);
             lds_barrier();
             const int b1 = bc == 2 ? 0 : bc + 1, b2 = b1 == 2 ? 0 : b1 + 1;
             OP* const ktc = Kt + (j & 1) * KTS;
@@ -1110,30 +1065,17 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
                 if (stage != 2) return;
                 if (j + 1 < je) transpose_kt<OP, DK, NW>(bufs[b1].K, ktn, w);
                 if (j + 2 < je) issue(j + 2, bufs[b2]);
-                if constexpr (TPW > 0) {
-                    consume(tv);
-                    touch(j + 3 < je ? j + 3 : je - 1, tv);
-                }
             };
             chunk_step<OP, DK, DV, OUT, NR, 1, NW, RAW>(bufs[bc], nullptr, ktc, nullptr, ST, R0, w, ahead, Nrm);
             bc = b1;
         };
-        for (int64_t j = jb; j < je; j += 2) {
-            body3(j, tvA);
-            if (j + 1 < je) body3(j + 1, tvB);
-        }
+        for (int64_t j = jb; j < je; ++j) body3(j);
     } else {
         issue(jb, bufs[0]);
-        if constexpr (TPW > 0) touch(jb + 1 < je ? jb + 1 : je - 1, tvB);
         for (int64_t j = jb; j < je; j += NBUF) {
-            body(j, bufs[0], bufs[NBUF == 2 ? 1 : 0], tvA);
-            if (NBUF == 2 && j + 1 < je) body(j + 1, bufs[NBUF == 2 ? 1 : 0], bufs[0], tvB);
+            body(j, bufs[0], bufs[NBUF == 2 ? 1 : 0]);
+            if (NBUF == 2 && j + 1 < je) body(j + 1, bufs[NBUF == 2 ? 1 : 0], bufs[0]);
         }
-    }
-    if constexpr (TPW > 0) {
-        consume(tvA);
-        consume(tvB);
-        asm volatile("" ::"v"(sink));
     }
     if constexpr (OUT) {
         lds_barrier();

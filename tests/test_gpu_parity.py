@@ -523,3 +523,31 @@ def test_seeded_shape_sweep(i):
     o, f = B.gdn_prefill(q, k, v, g, beta, s0, workspace=ws, **kw)
     torch.cuda.synchronize()
     assert torch.equal(o, ref_o) and torch.equal(f, ref_f)
+
+
+# -------------------------------------------------- degenerate gate values
+def _gates(kind, T, hv, rng):
+    if kind == "no_write":            # beta = 0: the state only decays
+        return rng.uniform(-1.0, 0.0, (T, hv)), np.zeros((T, hv))
+    if kind == "total_decay":         # alpha = e^-60: every step forgets (gamma underflows in fp32)
+        return np.full((T, hv), -60.0), rng.uniform(0.0, 1.0, (T, hv))
+    if kind == "no_decay_full_write": # alpha = 1, beta = 1
+        return np.zeros((T, hv)), np.ones((T, hv))
+    # alternating extremes token by token
+    t = np.arange(T)[:, None] % 4
+    g = np.where(t == 0, -30.0, 0.0) + np.zeros((T, hv))
+    b = np.where(t % 2 == 0, 1.0, 0.0) + np.zeros((T, hv))
+    return g, b
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind", ["no_write", "total_decay", "no_decay_full_write", "alternating"])
+@pytest.mark.parametrize("lens", [(700, 5, 129), (3000,)])
+def test_degenerate_gates(dtype, kind, lens):
+    """Gate values at the ends of their ranges, on ragged sequences and on one sequence cut into parts."""
+    inp = gi.make_inputs(gi.custom(dtype=dtype, Hqk=1, Hv=2, dk=128, dv=64, seqlens=lens,
+                                   init_state="normal"), seed=90)
+    rng = np.random.default_rng(91)
+    g, b = _gates(kind, inp.q.shape[0], 2, rng)
+    inp.g, inp.beta = g.astype(np.float32), b.astype(np.float32)
+    check_prefill(inp, label=f"degenerate {kind} {dtype} {lens}")

@@ -551,3 +551,21 @@ def test_degenerate_gates(dtype, kind, lens):
     g, b = _gates(kind, inp.q.shape[0], 2, rng)
     inp.g, inp.beta = g.astype(np.float32), b.astype(np.float32)
     check_prefill(inp, label=f"degenerate {kind} {dtype} {lens}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind", ["no_write", "total_decay", "no_decay_full_write", "alternating"])
+def test_decode_tokens_degenerate_gates(dtype, kind):
+    T = 4
+    inp = gi.make_inputs(gi.custom(dtype=dtype, Hqk=2, Hv=4, dk=128, dv=128, seqlens=(T,) * 6,
+                                   init_state="normal"), seed=92)
+    g, b = _gates(kind, inp.q.shape[0], 4, np.random.default_rng(93))
+    inp.g, inp.beta = g.astype(np.float32), b.astype(np.float32)
+    state = dev(inp.init_state)
+    out, ts = B.gdn_decode_tokens(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), state, T,
+                                  token_states=True)
+    torch.cuda.synchronize()
+    ro, rs, rf = c_oracle.decode_tokens(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.init_state, T)
+    eo, es, et = rel_err(host64(out), ro), rel_err(host64(state), rf), rel_err(host64(ts), rs)
+    say(f"[parity] decode_tokens degenerate {kind} {dtype}: out {eo:.3e} state {es:.3e} token states {et:.3e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype] and et <= TOL[dtype]

@@ -248,7 +248,7 @@ def main():
     tok_s = T / (ms * 1e-3)
     traffic = measured_traffic("gdn_prefill", PREFILL_SOURCES)
 
-    raw_rec = snapshot_rec = None
+    raw_rec = snapshot_rec = affine_rec = None
     if not args.no_variants:
         # the same call from raw projections (fused q/k normalisation and gate
         # activations; the normalised inputs and their gates stand in as values)
@@ -283,6 +283,21 @@ def main():
                                     f"({T // (64 * snap_chunks)} snapshots x 16 heads, gdn_prefill_snapshots)",
                         "ms_per_call": round(snap_ms, 4), "tokens_per_s": round(T / (snap_ms * 1e-3), 1)}
         del snaps
+
+        # the affine state map of the whole sequence (per-device half of a sequence-sharded prefill)
+        for _ in range(2):
+            B.gdn_prefill_affine(k, v, g, beta)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(5):
+            B.gdn_prefill_affine(k, v, g, beta)
+        b.record(stream)
+        torch.cuda.synchronize()
+        aff_ms = a.elapsed_time(b) / 5
+        log(f"affine state map of the sequence: {aff_ms:.3f} ms/call")
+        affine_rec = {"workload": "prefill_256k summarised to its state map S -> S M + B (every part's map, "
+                                  "composed; gdn_prefill_affine)",
+                      "ms_per_call": round(aff_ms, 4), "tokens_per_s": round(T / (aff_ms * 1e-3), 1)}
     del q, k, v, g, beta, out
     torch.cuda.empty_cache()
 
@@ -474,6 +489,7 @@ def main():
         "decode": decode,
         "prefill_snapshots": snapshot_rec,
         "prefill_raw": raw_rec,
+        "prefill_affine": affine_rec,
         "prefill_other_workloads": other,
     }
     print(json.dumps(rec), flush=True)

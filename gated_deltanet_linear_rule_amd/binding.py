@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_prefill_workspace_size.restype = ctypes.c_int
         L.gdn_prefill_ws.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.gdn_prefill_ws.restype = ctypes.c_int
+        L.gdn_prefill_affine.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P]
+        L.gdn_prefill_affine.restype = ctypes.c_int
         L.gdn_prefill_raw.argtypes = L.gdn_prefill.argtypes
         L.gdn_prefill_raw.restype = ctypes.c_int
         L.gdn_decode_tokens_raw.argtypes = L.gdn_decode_tokens.argtypes
@@ -188,6 +190,36 @@ def gdn_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, out=None, fi
             _ptr(init_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state), _stream(stream))
     _raise(rc, "gdn_prefill_raw" if raw else "gdn_prefill")
     return out, final_state
+
+
+def gdn_prefill_affine(k, v, g, beta, cu_seqlens=None, transition=None, offset=None, stream=None, num_seqs=None):
+    """State map of each whole sequence: S -> S @ transition + offset.
+
+    k [T, Hqk, dk]; v [T, Hv, dv] (bf16 or fp32); g, beta [T, Hv] fp32; cu_seqlens as for gdn_prefill.
+    Returns (transition [N, Hv, dk, dk], offset [N, Hv, dv, dk]), fp32 (allocated if None)."""
+    T, hqk, dk = k.shape
+    hv, dv = v.shape[1], v.shape[2]
+    io = _io_dtype(k)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", torch.int32)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = 1 if num_seqs is None else int(num_seqs)
+    _check(k, "k", k.dtype, (T, hqk, dk))
+    _check(v, "v", k.dtype, (T, hv, dv))
+    _check(g, "g", torch.float32, (T, hv))
+    _check(beta, "beta", torch.float32, (T, hv))
+    if transition is None:
+        transition = torch.empty((N, hv, dk, dk), dtype=torch.float32, device=k.device)
+    if offset is None:
+        offset = torch.empty((N, hv, dv, dk), dtype=torch.float32, device=k.device)
+    _check(transition, "transition", torch.float32, (N, hv, dk, dk))
+    _check(offset, "offset", torch.float32, (N, hv, dv, dk))
+    shape = GdnShape(N, T, hqk, hv, dk, dv, io)
+    rc = lib().gdn_prefill_affine(ctypes.byref(shape), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                  _ptr(transition), _ptr(offset), _stream(stream))
+    _raise(rc, "gdn_prefill_affine")
+    return transition, offset
 
 
 def gdn_decode_step(q, k, v, g, beta, state, out=None, stream=None):

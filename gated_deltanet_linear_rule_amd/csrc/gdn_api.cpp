@@ -373,6 +373,66 @@ gdn_status gdn_prefill_ws(const gdn_shape* shape, const void* q, const void* k, 
                         stream, false, workspace, workspace_bytes);
 }
 
+gdn_status gdn_prefill_affine(const gdn_shape* shape, const void* k, const void* v, const float* g,
+                              const float* beta, const int32_t* cu_seqlens, float* transition, float* offset,
+                              void* stream) {
+    g_last_error[0] = '\0';
+    GDN_TRY(check_shape(shape, false));
+    const bool tok = shape->num_tokens > 0;
+    GDN_TRY(check_ptr(k, "k", 16, tok));
+    GDN_TRY(check_ptr(v, "v", 16, tok));
+    GDN_TRY(check_ptr(g, "g", 4, tok));
+    GDN_TRY(check_ptr(beta, "beta", 4, tok));
+    GDN_TRY(check_ptr(cu_seqlens, "cu_seqlens", 4, false));
+    const bool any = shape->num_seqs > 0;
+    GDN_TRY(check_ptr(transition, "transition", 16, any));
+    GDN_TRY(check_ptr(offset, "offset", 16, any));
+    if (!cu_seqlens && shape->num_seqs > 0 && shape->num_tokens % shape->num_seqs != 0)
+        return fail(GDN_ERROR_INVALID_VALUE, "num_tokens (%lld) is not a multiple of num_seqs (%d) and no cu_seqlens",
+                    (long long)shape->num_tokens, shape->num_seqs);
+    if (!any) return GDN_SUCCESS;
+    {
+        const size_t mb = (size_t)shape->num_seqs * shape->num_v_heads * shape->head_dim_k * shape->head_dim_k * 4;
+        const size_t bb = (size_t)shape->num_seqs * shape->num_v_heads * shape->head_dim_v * shape->head_dim_k * 4;
+        const char* m0 = reinterpret_cast<const char*>(transition);
+        const char* b0 = reinterpret_cast<const char*>(offset);
+        if (m0 < b0 + bb && b0 < m0 + mb) return fail(GDN_ERROR_INVALID_VALUE, "transition and offset overlap");
+    }
+    const bool bf16 = shape->dtype == GDN_DTYPE_BF16;
+    gdn::PrefillArgs a{};
+    a.q = k; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.cu = cu_seqlens;
+    a.aff_m = transition;
+    a.aff_b = offset;
+    bool split = false;
+    int64_t total = 0;
+    GDN_TRY(plan_prefill(shape, cu_seqlens != nullptr, false, a, split, total));
+    // every sequence gets its part maps, split or not
+    const gdn::PrefillWorkspace wl(a.num_slots, a.num_part_slots, true, a.hv, shape->head_dim_k, shape->head_dim_v,
+                                   bf16 ? 2 : 4);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(GDN_ERROR_LAUNCH, "hipGetDevice failed");
+    keep_pool_memory(dev);
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, (size_t)wl.total, st) != hipSuccess || !ws) {
+        (void)hipGetLastError();
+        return fail(GDN_ERROR_OUT_OF_MEMORY, "prefill_affine workspace of %lld bytes", (long long)wl.total);
+    }
+    char* wc = static_cast<char*>(ws);
+    a.ws_t = wc + wl.t;
+    a.ws_g = reinterpret_cast<double*>(wc + wl.g);
+    a.ws_m = reinterpret_cast<float*>(wc + wl.m);
+    a.ws_b = reinterpret_cast<float*>(wc + wl.b);
+    a.ws_s = reinterpret_cast<float*>(wc + wl.s);
+    hipError_t e = gdn::launch_prefill_affine(a, bf16, shape->head_dim_k, shape->head_dim_v, st);
+    const hipError_t ef = hipFreeAsync(ws, st);
+    if (e == hipSuccess) e = ef;
+    if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(GDN_ERROR_LAUNCH, "prefill_affine: %s", hipGetErrorString(e));
+    return GDN_SUCCESS;
+}
+
 gdn_status gdn_prefill_snapshots(const gdn_shape* shape, const void* q, const void* k, const void* v,
                                  const float* g, const float* beta, const float* init_state,
                                  const int32_t* cu_seqlens, void* out, float* final_state, int32_t snapshot_chunks,

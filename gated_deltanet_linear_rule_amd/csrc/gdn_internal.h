@@ -58,6 +58,11 @@ struct PrefillArgs {
     // at slot floor(start(n) / (64 snap_chunks)) + n + s - 1.
     float* snapshots;          // [slots, Hv, dv, dk] or nullptr
     int32_t snap_chunks;
+    // Affine map of each sequence (gdn_prefill_affine): the summary covers
+    // every part and the link composes them, from zero (offset rows) and from
+    // the identity (transition rows), into these instead of start states:
+    float* aff_m;              // [N, Hv, dk, dk] transition, or nullptr (ordinary prefill)
+    float* aff_b;              // [N, Hv, dv, dk] offset
 };
 
 // Workspace layout of one prefill call (byte offsets of each part and total),
@@ -89,5 +94,7 @@ hipError_t launch_decode(const DecodeArgs& a, bool bf16, int dk, int dv, hipStre
 hipError_t launch_decode_tokens(const DecodeArgs& a, bool bf16, int dk, int dv, hipStream_t s, bool raw = false);
 // raw: q, k unnormalised and g, beta given as logits (see gdn_prefill_raw).
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int dk, int dv, hipStream_t s, bool raw = false);
+// The affine map of each sequence (a.aff_m, a.aff_b set; q and out unused).
+hipError_t launch_prefill_affine(const PrefillArgs& a, bool bf16, int dk, int dv, hipStream_t s);
 
 }  // namespace gdn

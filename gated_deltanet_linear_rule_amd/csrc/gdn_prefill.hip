@@ -921,7 +921,9 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
 #pragma unroll
         for (int b = 0; b < NR; ++b) load_state<DK>(Sin, R0[b], ST[b]);
     } else {
-        if (p >= np - 1) return;
+        // every part but the last (its map is not needed to link), or every
+        // part for the affine map of whole sequences
+        if (a.aff_m ? p >= np : p >= np - 1) return;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             ST[0][db] = zero4();
@@ -1097,7 +1099,10 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
 // ===========================================================================
 // One workgroup per (sequence, value head, 16-row block of the state); rows of
 // S never mix, so the blocks are independent.  S_0 (init_state or zeros) and
-// every later S_p go to ws_s at the part's slot.  Wave w computes the d_k
+// every later S_p go to ws_s at the part's slot.  For the affine map of whole
+// sequences (aff_m set) the chain runs over every part from zero (offset
+// rows) and from the identity (transition rows, without B_p) and ends in
+// aff_b and aff_m.  Wave w computes the d_k
 // column blocks w, w + 4, ... of S_{p+1} on the fp32 matrix cores.  M_p does
 // not depend on S, so M_{p+1} streams into the second LDS buffer (direct
 // loads) while step p computes: a step waits for one load, not a chain of them.
@@ -1110,16 +1115,31 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
     __shared__ float S[16][LD];
     __shared__ float Mb[2][DK * DK];                      // M_p, row-major
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), n = l & 15, gq = l >> 4;
-    const int vb = (int)(blockIdx.x % NVB);
-    const int64_t chain = blockIdx.x / NVB;
+    // affine map: row blocks 0 .. NVB - 1 are offset rows (from zero, + B_p),
+    // NVB .. NVB + NDB - 1 transition rows (from the identity, no B_p)
+    const bool aff = a.aff_m != nullptr;
+    const int NBK = aff ? NVB + NDB : NVB;
+    const int vb = (int)(blockIdx.x % NBK);
+    const int64_t chain = blockIdx.x / NBK;
+    const bool trans = vb >= NVB;
     const int seq = (int)(chain / a.hv), h = (int)(chain - (int64_t)seq * a.hv);
     const SeqIndex si{a.cu, a.seqlen};
     const int64_t L = a.part_chunks;
     const int64_t s0 = si.start(seq), len = si.start(seq + 1) - s0;
     const int64_t nc = (len + kChunk - 1) / kChunk, np = (nc + L - 1) / L;
-    if (np <= 1) return;
+    const int64_t steps = aff ? np : np - 1;             // S_{p+1} = S_p M_p + B_p for p < steps
+    const int R0 = trans ? 16 * (vb - NVB) : 16 * vb;
+    float* const outp = !aff ? nullptr
+                             : trans ? a.aff_m + (chain * DK + R0) * DK : a.aff_b + (chain * DV + R0) * DK;
+    if (aff && steps == 0) {                             // empty sequence: M = I, B = 0
+        for (int e = tid; e < 16 * DK; e += kLinkThreads) {
+            const int row = e / DK, c = e - row * DK;
+            outp[(size_t)row * DK + c] = trans && R0 + row == c ? 1.f : 0.f;
+        }
+        return;
+    }
+    if (steps <= 0) return;
     const int64_t pbase = span_base(s0, seq, L * kChunk);
-    const int R0 = 16 * vb;
 
     auto load_m = [&](int64_t p, int buf) {
         const float* M = a.ws_m + ((size_t)(pbase + p) * a.hv + h) * DK * DK;
@@ -1130,9 +1150,17 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
     load_m(0, 0);
     for (int e = tid; e < 16 * DK / 4; e += kLinkThreads) {
         const int row = e / (DK / 4), c = 4 * (e - row * (DK / 4));
-        const f32x4 x = a.init_state ? *reinterpret_cast<const f32x4*>(a.init_state + (chain * DV + R0 + row) * DK + c) : zero4();
-        *reinterpret_cast<f32x4*>(&S[row][c]) = x;
-        *reinterpret_cast<f32x4*>(a.ws_s + (((size_t)pbase * a.hv + h) * DV + R0 + row) * DK + c) = x;
+        if (aff) {
+            f32x4 x = zero4();
+            if (trans)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[i] = R0 + row == c + i ? 1.f : 0.f;
+            *reinterpret_cast<f32x4*>(&S[row][c]) = x;
+        } else {
+            const f32x4 x = a.init_state ? *reinterpret_cast<const f32x4*>(a.init_state + (chain * DV + R0 + row) * DK + c) : zero4();
+            *reinterpret_cast<f32x4*>(&S[row][c]) = x;
+            *reinterpret_cast<f32x4*>(a.ws_s + (((size_t)pbase * a.hv + h) * DV + R0 + row) * DK + c) = x;
+        }
     }
     // this lane's share of B_p (accumulator layout), fetched a step ahead
     auto load_b = [&](int64_t p, f32x4 (&c)[PER]) {
@@ -1141,22 +1169,23 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
         for (int k = 0; k < PER; ++k) {
             const int db = w + NWV * k;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) c[k][i] = db < NDB ? B[(size_t)(4 * gq + i) * DK + 16 * db + n] : 0.f;
+            for (int i = 0; i < 4; ++i) c[k][i] = db < NDB && !trans ? B[(size_t)(4 * gq + i) * DK + 16 * db + n] : 0.f;
         }
     };
     f32x4 bnext[PER];
     load_b(0, bnext);
-    for (int64_t p = 0; p + 1 < np; ++p) {
+    for (int64_t p = 0; p < steps; ++p) {
         const int cb = (int)(p & 1);
         f32x4 bcur[PER];
 #pragma unroll
         for (int k = 0; k < PER; ++k) bcur[k] = bnext[k];
-        // this wave's share of M_p is in; the PER * 4 newest memory operations
-        // may still be in flight: the stores of S_p, or at p = 0 the loads of
-        // B_0, whose registers the compiler waits for where they are read
-        __builtin_amdgcn_s_waitcnt(kWaitVm0 | ((PER * 4) & 15) | (((PER * 4) >> 4) << 14));
+        // this wave's share of M_p is in: at the first step everything is
+        // waited for; later the PER * 4 newest memory operations, the stores
+        // of S_p, may still be in flight
+        if (p == 0) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        else __builtin_amdgcn_s_waitcnt(kWaitVm0 | ((PER * 4) & 15) | (((PER * 4) >> 4) << 14));
         __syncthreads();                                 // everyone's is; S_p is written
-        if (p + 2 < np) {
+        if (p + 1 < steps) {
             load_m(p + 1, cb ^ 1);                       // the other buffer was read in step p - 1
             load_b(p + 1, bnext);
         }
@@ -1181,7 +1210,7 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
             res[k] = c;
         }
         lds_barrier();                                   // S_p read by everyone (M_{p+1} may be in flight)
-        float* Sn = a.ws_s + ((size_t)(pbase + p + 1) * a.hv + h) * DV * DK + (size_t)R0 * DK;
+        float* Sn = aff ? outp : a.ws_s + ((size_t)(pbase + p + 1) * a.hv + h) * DV * DK + (size_t)R0 * DK;
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int db = w + NWV * k;
@@ -1225,6 +1254,18 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <typename OP, int DK, int DV>
+hipError_t launch_prefill_affine_t(const PrefillArgs& a, hipStream_t st) {
+    hipError_t e = launch_prep<OP, DK, false>(a, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gdn_chunk_kernel<OP, DK, DV, false, false>), dim3((unsigned)(a.num_part_slots * a.hv)),
+                       dim3(ChunkGeom<OP, DK, DV, false>::NT), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const unsigned links = (unsigned)((int64_t)a.num_seqs * a.hv * (DV / 16 + DK / 16));
+    hipLaunchKernelGGL((gdn_link_kernel<DK, DV>), dim3(links), dim3(kLinkThreads), 0, st, a);
+    return hipGetLastError();
+}
+
 template <typename OP, bool RAW>
 hipError_t launch_prefill_dt(const PrefillArgs& a, int dk, int dv, hipStream_t st) {
     if (dk == 128)
@@ -1244,6 +1285,17 @@ int64_t prefill_part_chunks(int64_t num_tokens, int num_seqs, int hv, int num_cu
     int64_t L = (chunks * hv + num_cus - 1) / (num_cus > 0 ? num_cus : 1);
     L = L > kMinPartChunks ? L : kMinPartChunks;
     return L < whole ? L : whole;
+}
+
+hipError_t launch_prefill_affine(const PrefillArgs& a, bool bf16, int dk, int dv, hipStream_t st) {
+    if (a.num_seqs == 0) return hipSuccess;
+    auto go = [&](auto op) {
+        using OP = decltype(op);
+        if (dk == 128)
+            return dv == 128 ? launch_prefill_affine_t<OP, 128, 128>(a, st) : launch_prefill_affine_t<OP, 128, 64>(a, st);
+        return dv == 128 ? launch_prefill_affine_t<OP, 64, 128>(a, st) : launch_prefill_affine_t<OP, 64, 64>(a, st);
+    };
+    return bf16 ? go(__bf16{}) : go(0.f);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int dk, int dv, hipStream_t st, bool raw) {

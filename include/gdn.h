@@ -136,6 +136,26 @@ gdn_status gdn_prefill_ws(const gdn_shape* shape, const void* q, const void* k, 
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_prefill_affine -- the state map of each whole sequence.  Over its tokens
+ * the recurrence maps any start state S to S M + B: the product of the
+ * per-token maps (flozi.net, "Qwen3.8-Flash-Next architecture", "Der Weg eines
+ * Tokens durch das Modell", item 1: the layer's state is a fixed-size
+ * recurrent state, so a token range acts on it as one affine map).  This is
+ * the per-device half of a sequence-sharded prefill: each device summarises
+ * its range of tokens, the maps are gathered and composed, and each device
+ * reruns gdn_prefill on its range from the composed start state.
+ *
+ * k, v, g, beta, cu_seqlens as for gdn_prefill (q is not needed).
+ * transition  [N, Hv, dk, dk] fp32, M (the identity for an empty sequence).
+ * offset      [N, Hv, dv, dk] fp32, B (the state reached from zero).
+ * The two must not overlap.  Memory: a stream-ordered workspace from HIP's
+ * default pool, as for gdn_prefill (with the part maps for every sequence).
+ */
+gdn_status gdn_prefill_affine(const gdn_shape* shape, const void* k, const void* v, const float* g,
+                              const float* beta, const int32_t* cu_seqlens, float* transition, float* offset,
+                              void* stream);
+
+/*
  * gdn_prefill_snapshots -- gdn_prefill that also writes the state at every
  * snapshot_chunks * 64 tokens of each sequence (chunk-boundary snapshots for
  * prefix reuse: a later request that shares the first s * P tokens of a

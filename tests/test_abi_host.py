@@ -27,7 +27,8 @@ def _declared_functions():
 
 def test_header_declares_the_abi():
     assert _declared_functions() == ["gdn_abi_version", "gdn_decode_slots", "gdn_decode_step", "gdn_decode_tokens",
-                                     "gdn_decode_tokens_raw", "gdn_last_error", "gdn_prefill", "gdn_prefill_raw",
+                                     "gdn_decode_tokens_raw", "gdn_last_error", "gdn_prefill", "gdn_prefill_affine",
+                                     "gdn_prefill_raw",
                                      "gdn_prefill_snapshots", "gdn_prefill_workspace_size", "gdn_prefill_ws",
                                      "gdn_status_string"]
 
@@ -251,6 +252,30 @@ def test_prefill_workspace_size_host_paths():
     n.value = 123
     rc = L.gdn_prefill_workspace_size(ctypes.byref(_shape(num_seqs=0, num_tokens=0)), 1, ctypes.byref(n))
     assert rc == B.GDN_SUCCESS and n.value == 0
+
+
+def _affine(shape, m, b):
+    c = ctypes.c_void_p
+    L = _lib()
+    rc = L.gdn_prefill_affine(ctypes.byref(shape), c(FAKE), c(FAKE), c(FAKE), c(FAKE), None,
+                              c(m) if m else None, c(b) if b else None, None)
+    return rc, L.gdn_last_error().decode()
+
+
+@pytest.mark.parametrize("m,b,status,msg", [
+    (None, FAKE, B.GDN_ERROR_INVALID_VALUE, "transition is NULL"),
+    (FAKE, None, B.GDN_ERROR_INVALID_VALUE, "offset is NULL"),
+    (FAKE, FAKE + 1024, B.GDN_ERROR_INVALID_VALUE, "overlap"),
+    (FAKE + 8, FAKE + (1 << 22), B.GDN_ERROR_INVALID_VALUE, "aligned"),
+])
+def test_prefill_affine_rejects_bad_arguments(m, b, status, msg):
+    rc, err = _affine(_shape(), m, b)
+    assert rc == status and msg in err, (rc, err)
+
+
+def test_prefill_affine_applies_the_shape_checks():
+    rc, err = _affine(_shape(num_qk_heads=3, num_v_heads=4), FAKE, FAKE + (1 << 22))
+    assert rc == B.GDN_ERROR_INVALID_VALUE and "multiple" in err
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch):

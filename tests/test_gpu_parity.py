@@ -569,3 +569,71 @@ def test_decode_tokens_degenerate_gates(dtype, kind):
     eo, es, et = rel_err(host64(out), ro), rel_err(host64(state), rf), rel_err(host64(ts), rs)
     say(f"[parity] decode_tokens degenerate {kind} {dtype}: out {eo:.3e} state {es:.3e} token states {et:.3e}")
     assert eo <= TOL[dtype] and es <= TOL[dtype] and et <= TOL[dtype]
+
+
+# ------------------------------------- affine state map of a token range
+def _oracle_affine(inp):
+    """(M, B) of every sequence from the oracle: B is the state reached from zero; M is the state
+    reached from the identity with v = 0 (so that its rows carry the transition alone)."""
+    dt, dk = inp.wl.dtype, inp.wl.head_dim_k
+    N, hv = inp.wl.num_seqs, inp.wl.num_v_heads
+    _, rb = c_oracle.prefill(inp.k, inp.k, inp.v, inp.g, inp.beta, None, inp.cu_seqlens)
+    zv = np.zeros((inp.k.shape[0], hv, dk), dtype=inp.v.dtype)
+    eye = np.broadcast_to(np.eye(dk, dtype=np.float32), (N, hv, dk, dk)).copy()
+    _, rm = c_oracle.prefill(inp.k, inp.k, zv, inp.g, inp.beta, eye, inp.cu_seqlens)
+    return rm, rb
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("decay", [True, False])
+@pytest.mark.parametrize("dk,dv,lens", [(128, 128, (300, 0, 65, 1)), (64, 128, (200, 7)), (128, 64, (2500,)),
+                                        (64, 64, (130,))])
+def test_prefill_affine_matches_oracle(dtype, decay, dk, dv, lens):
+    """decay=False: g = 0, so the transition is a product of the (I - beta k k^T) and does not fade."""
+    inp = gi.make_inputs(gi.custom(dtype=dtype, Hqk=1, Hv=2, dk=dk, dv=dv, seqlens=lens), seed=100)
+    if not decay:
+        inp.g = np.zeros_like(inp.g)
+    cu = dev(inp.cu_seqlens) if inp.cu_seqlens is not None else None
+    kw = dict(cu_seqlens=cu) if cu is not None else dict(num_seqs=len(lens))
+    m, b = B.gdn_prefill_affine(dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), **kw)
+    torch.cuda.synchronize()
+    rm, rb = _oracle_affine(inp)
+    # The transition starts as the identity and every token's factor alpha (I - beta k k^T) has spectral
+    # norm <= 1 (alpha <= 1, beta in [0, 1], |k| = 1), so its natural scale is 1: its error is measured
+    # against max(max|M|, 1) (a long decay-free product can shrink M far below 1, where its own maximum
+    # says nothing about the states it acts on).  The offset is a state and keeps the usual measure.
+    em = float(np.max(np.abs(host64(m) - rm))) / max(float(np.max(np.abs(rm))), 1.0)
+    eb = rel_err(host64(b), rb)
+    say(f"[parity] affine {dtype} decay={decay} dk={dk} dv={dv} {lens}: transition {em:.3e} offset {eb:.3e} "
+        f"(max|M| {np.abs(rm).max():.2f})")
+    assert em <= TOL[dtype] and eb <= TOL[dtype]
+    if 0 in lens:   # an empty sequence maps S to S
+        z = lens.index(0)
+        assert torch.equal(m[z], torch.eye(dk, device="cuda").expand(2, dk, dk)) and not b[z].any()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sequence_sharded_prefill_on_one_gpu(dtype):
+    """Four ranges of one sequence as four ranks would run them: each range's affine map, the maps
+    composed in order from the initial state, then each range rerun from its composed start state;
+    the concatenated outputs and the last final state against the oracle's single run."""
+    T, cuts = 4096, (0, 1000, 2100, 3333, 4096)
+    inp = gi.make_inputs(gi.custom(dtype=dtype, Hqk=1, Hv=2, dk=128, dv=128, seqlens=(T,), init_state="normal"),
+                         seed=101)
+    q, k, v, g, beta = (dev(x) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
+    maps = [B.gdn_prefill_affine(k[a:e], v[a:e], g[a:e], beta[a:e]) for a, e in zip(cuts, cuts[1:])]
+    torch.cuda.synchronize()
+    s = inp.init_state.astype(np.float64)                      # composed on the host in fp64
+    starts = []
+    for m, b in maps:
+        starts.append(s.astype(np.float32))
+        s = s @ host64(m) + host64(b)
+    outs, fin = [], None
+    for (a, e), s0 in zip(zip(cuts, cuts[1:]), starts):
+        o, fin = B.gdn_prefill(q[a:e], k[a:e], v[a:e], g[a:e], beta[a:e], torch.from_numpy(s0).cuda())
+        outs.append(o)
+    torch.cuda.synchronize()
+    ro, rf = c_oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.init_state, None)
+    eo, ef = rel_err(host64(torch.cat(outs)), ro), rel_err(host64(fin), rf)
+    say(f"[parity] sharded over 4 ranges {dtype}: out {eo:.3e} final {ef:.3e}")
+    assert eo <= TOL[dtype] and ef <= TOL[dtype]

@@ -12,7 +12,8 @@
  *     o_t = S_t q_t,                 alpha_t = exp(g_t),
  *
  * with the output read after the token's own write, no query scaling and no
- * normalisation of q or k inside the library.
+ * normalisation of q or k inside the library (except in the *_raw entry
+ * points, which take the raw projections; see below).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -63,7 +64,8 @@ typedef enum gdn_dtype {
 /* Problem shape.
  * num_seqs   N >= 0 sequences.
  * num_tokens total tokens in q/k/v/out (prefill: sum of the lengths;
- *            decode: must equal num_seqs, one token per sequence).
+ *            gdn_decode_step: num_seqs, one token per sequence;
+ *            gdn_decode_tokens / _slots: num_seqs * tokens_per_seq).
  * Without cu_seqlens the N sequences have equal length num_tokens / N
  * (num_tokens must be a multiple of N), stored one after another. */
 typedef struct gdn_shape {

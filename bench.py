@@ -103,7 +103,18 @@ def measured_traffic(name, sources):
 
 
 CALIB_BYTES = 1 << 30      # bytes read and bytes written by the calibration kernel
-KERNELS = {"gdn_prefill": ("gdn_prep_kernel", "gdn_chunk_kernel", "gdn_link_kernel"), "gdn_decode": ("gdn_decode_kernel",)}
+KERNELS = {"gdn_prefill": ("gdn_prep_kernel", "gdn_chunk_kernel<summary>", "gdn_link_kernel", "gdn_chunk_kernel<output>"),
+           "gdn_decode": ("gdn_decode_kernel",)}
+
+
+def _kernel_matches(label, name):
+    """Does a dispatch's (mangled) kernel name belong to `label`?  The two chunk kernels are one
+    template; its fourth argument (OUT) tells them apart."""
+    import re
+    if label.startswith("gdn_chunk_kernel<"):
+        m = re.search(r"gdn_chunk_kernelI\w+?Li\d+ELi\d+ELb([01])E", name)
+        return bool(m) and m.group(1) == ("1" if label.endswith("<output>") else "0")
+    return label in name
 
 
 def _pmc_per_dispatch(path, counter):
@@ -149,8 +160,8 @@ def write_traffic_summary(fetch_csv, write_csv, prefill_calls):
         total = 0.0
         agg = (lambda t, p: per_call(t, p, prefill_calls)) if call == "gdn_prefill" else mean_of
         for kn in kernels:
-            f, nf = agg(fetch, lambda n, kn=kn: kn in n)
-            w, nw = agg(write, lambda n, kn=kn: kn in n)
+            f, nf = agg(fetch, lambda n, kn=kn: _kernel_matches(kn, n))
+            w, nw = agg(write, lambda n, kn=kn: _kernel_matches(kn, n))
             if f is None or w is None:
                 break
             rb, wb = f * 1024 * sf, w * 1024 * sw

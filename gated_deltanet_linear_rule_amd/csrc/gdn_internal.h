@@ -44,7 +44,7 @@ struct PrefillArgs {
     int64_t part_chunks;       // L: chunks per part
     int64_t num_part_slots;    // part slots: ceil(num_tokens / (64 L)) + num_seqs
     // Workspace.  Per (chunk slot, value head), written by the prep kernel:
-    void* ws_t;                // T~ = (I + A)^{-1} diag(beta) as 6 operand fragments
+    void* ws_t;                // T~ = (I + A)^{-1} diag(beta) as operand fragments (5 KB bf16, 12 KB fp32)
     double* ws_g;              // 1 KB gate record: 64 log2-scaled cumulative gates (fp64),
                                // then 64 gamma and 64 D (fp32)
     float* ws_ik;              // raw projections only: 64 values 1 / |k_t| (256 B)
@@ -74,7 +74,7 @@ struct PrefillWorkspace {
         auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
         const int64_t blocks = num_slots * hv, pblocks = split ? num_part_slots * hv : 0;
         t = 0;
-        g = t + up(blocks * 6 * 64 * 8 * (int64_t)elem_size);
+        g = t + up(blocks * (elem_size == 2 ? 5 : 12) * 1024);   // T~: 5 KB bf16, 12 KB fp32
         ik = g + up(blocks * 1024);
         m = ik + (raw ? up(blocks * 256) : 0);
         b = m + up(pblocks * dk * dk * 4);

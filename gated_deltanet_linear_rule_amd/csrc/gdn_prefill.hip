@@ -77,7 +77,17 @@ __device__ __forceinline__ void tri_frag_pos(int f, int& tb, int& kk) {
 template <typename OP> struct Units {
     static constexpr int VE = 16 / (int)sizeof(OP);   // elements per 16-byte unit
     static constexpr int FU = 8 / VE;                 // units per operand fragment
+    // T~ per (chunk, value head), in 1 KB units (64 lanes x 16 bytes).  bf16:
+    // the four full lower fragments (1, 2, 4, 5), then the lower halves of
+    // fragments 0 and 3, whose upper halves (tiles above the diagonal) are
+    // zero: 5 units.  fp32: all six fragments, two units each.
+    static constexpr int TU = sizeof(OP) == 2 ? 5 : 12;
 };
+
+// bf16 T~ storage: unit of full fragment f (1, 2, 4, 5), and element offset
+// of the lane's lower half of fragment f (0, 3) in the fifth unit.
+__host__ __device__ constexpr int tri_full_unit(int f) { return f - 1 - (f > 3 ? 1 : 0); }
+__host__ __device__ constexpr int tri_half_elem(int f, int lane) { return 4 * 512 + (f == 3 ? 256 : 0) + 4 * lane; }
 
 // Slots of width `span` tokens: part j of sequence n (first token
 // start(n) + span j) gets slot floor(start(n) / span) + n + j.  Slots are
@@ -354,14 +364,21 @@ __global__ __launch_bounds__(kWave * kPrepWaves) void gdn_prep_kernel(PrefillArg
     f32x4 bc[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) bc[c] = *reinterpret_cast<const f32x4*>(&sm.B[16 * c + 4 * gq]);
-    OP* const Tw = static_cast<OP*>(a.ws_t) + blk * (kTriFrags * 64 * 8);
+    OP* const Tw = static_cast<OP*>(a.ws_t) + blk * (Units<OP>::TU * 1024 / sizeof(OP));
 #pragma unroll
     for (int f = 0; f < kTriFrags; ++f) {
         const int tb = f < 2 ? f : 2 + ((f - 2) >> 1), kk = f < 2 ? 0 : ((f - 2) & 1);
         const f32x4 lo = ta[tb][2 * kk] * bc[2 * kk];
         const f32x4 hi = 2 * kk + 1 <= tb ? ta[tb][2 * kk + 1] * bc[2 * kk + 1] : zero4();
         if constexpr (FU == 1) {
-            ws_store(reinterpret_cast<frag*>(Tw + ((size_t)f * 64 + l) * VE), Ops::pack(lo, hi));
+            if (f == 0 || f == 3) {   // the upper half is zero: only the lower is stored
+                typename Ops::quad q;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) q[i] = from_f32<OP>(lo[i]);
+                ws_store(reinterpret_cast<typename Ops::quad*>(Tw + tri_half_elem(f, l)), q);
+            } else {
+                ws_store(reinterpret_cast<frag*>(Tw + ((size_t)tri_full_unit(f) * 64 + l) * VE), Ops::pack(lo, hi));
+            }
         } else {
             ws_store(reinterpret_cast<f32x4*>(Tw + ((size_t)(f * 2) * 64 + l) * VE), lo);
             ws_store(reinterpret_cast<f32x4*>(Tw + ((size_t)(f * 2 + 1) * 64 + l) * VE), hi);
@@ -479,6 +496,21 @@ __device__ __forceinline__ typename Op<OP>::frag lds_frag(const OP* base, int f)
         const f32x4 lo = *reinterpret_cast<const f32x4*>(base + ((size_t)(2 * f) * 64 + l) * 4);
         const f32x4 hi = *reinterpret_cast<const f32x4*>(base + ((size_t)(2 * f + 1) * 64 + l) * 4);
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+}
+
+// Fragment f of T~ as stored by the prep kernel (see Units::TU).
+template <typename OP>
+__device__ __forceinline__ typename Op<OP>::frag t_frag(const OP* base, int f) {
+    if constexpr (sizeof(OP) == 2) {
+        const int l = lane_id();
+        if (f == 0 || f == 3) {
+            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(base + tri_half_elem(f, l));
+            return Op<OP>::join(lo, bf16x4{});
+        }
+        return *reinterpret_cast<const bf16x8*>(base + ((size_t)tri_full_unit(f) * 64 + l) * 8);
+    } else {
+        return lds_frag(base, f);
     }
 }
 
@@ -756,7 +788,7 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT, OUT &
     }
     frag tf[kTriFrags];
 #pragma unroll
-    for (int f = 0; f < kTriFrags; ++f) tf[f] = lds_frag(cb.T, f);
+    for (int f = 0; f < kTriFrags; ++f) tf[f] = t_frag(cb.T, f);
     f32x4 dd[2][2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -869,8 +901,8 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
     using Buf = ChunkBuf<OP, DK, DV, OUT, OUT && RAW>;
     constexpr int NR = G::NR, NW = G::NW, NBUF = G::NBUF;
     constexpr int NVB = DV / 16, NMB = DK / 16, NDB = DK / 16;
-    constexpr int E = (int)sizeof(OP), FU = Units<OP>::FU;
-    constexpr int UK = kChunk * DK * E / 1024, UV = kChunk * DV * E / 1024, UT = kTriFrags * FU;
+    constexpr int E = (int)sizeof(OP);
+    constexpr int UK = kChunk * DK * E / 1024, UV = kChunk * DV * E / 1024, UT = Units<OP>::TU;
     __shared__ Buf bufs[NBUF];
     __shared__ OP Pf[OUT ? kTriFrags * 64 * 8 : 8];
     __shared__ OP Ost[OUT ? kChunk * DV : 8];   // O rows of the previous chunk (RowTile layout)
@@ -948,10 +980,10 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
     const char* const qB0 = static_cast<const char*>(a.q) + ((row0 * a.hqk + hq) * DK) * E;
     const char* const vB0 = static_cast<const char*>(a.v) + ((row0 * a.hv + h) * DV) * E;
     char* const oB0 = static_cast<char*>(a.out) + ((row0 * a.hv + h) * DV) * E;
-    const char* const tB0 = static_cast<const char*>(a.ws_t) + ((size_t)(cbase + jb) * a.hv + h) * (kTriFrags * 64 * 8 * E);
+    const char* const tB0 = static_cast<const char*>(a.ws_t) + ((size_t)(cbase + jb) * a.hv + h) * (UT * 1024);
     const char* const gB0 = reinterpret_cast<const char*>(a.ws_g) + ((size_t)(cbase + jb) * a.hv + h) * kGateRecord;
     const uint32_t kstep = kChunk * kstride, vstep = kChunk * vstride;
-    const uint32_t tstep = (uint32_t)a.hv * (kTriFrags * 64 * 8 * E), gstep = (uint32_t)a.hv * kGateRecord;
+    const uint32_t tstep = (uint32_t)a.hv * (UT * 1024), gstep = (uint32_t)a.hv * kGateRecord;
     const int64_t jl = nc - 1;                                  // the sequence's last chunk
     const int lrows = (int)(len - jl * kChunk);                  // its rows, 1 .. 64
     const int kfull = (kChunk - 1) * (int)kstride + DK * E, klast = (lrows - 1) * (int)kstride + DK * E;

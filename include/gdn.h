@@ -99,8 +99,8 @@ typedef struct gdn_shape {
  * Memory: a stream-ordered workspace is taken from HIP's default memory pool
  * on `stream` and returned to it before the call's work completes
  * (GDN_ERROR_OUT_OF_MEMORY if that fails).  Its size is about
- * (num_tokens / 64 + N) * Hv * (3072 * sizeof(element) + 1024) bytes (the
- * chunks' triangular factors and gates), plus, when a sequence is cut into
+ * (num_tokens / 64 + N) * Hv * (6 KB for bf16, 13 KB for fp32) (the chunks'
+ * triangular factors and gates), plus, when a sequence is cut into
  * parts of L chunks because there are fewer (sequence, head) pairs than
  * compute units, (num_tokens / (64 L) + N) * Hv * (dk + 2 dv) * dk * 4 bytes
  * (each part's transition, offset and start state).

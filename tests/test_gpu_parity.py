@@ -637,3 +637,56 @@ def test_sequence_sharded_prefill_on_one_gpu(dtype):
     eo, ef = rel_err(host64(torch.cat(outs)), ro), rel_err(host64(fin), rf)
     say(f"[parity] sharded over 4 ranges {dtype}: out {eo:.3e} final {ef:.3e}")
     assert eo <= TOL[dtype] and ef <= TOL[dtype]
+
+
+# ------------------------------- seeded sweep over the other entry points
+def _sweep2_case(i):
+    r = np.random.default_rng(3000 + i)
+    dtype = ["f32", "bf16"][int(r.integers(2))]
+    dk, dv = (int(x) for x in r.choice([64, 128], size=2))
+    hqk = int(r.choice([1, 2, 4]))
+    hv = hqk * int(r.choice([1, 2]))
+    n = int(r.integers(1, 5))
+    lens = [int(r.choice([0, 1, 63, 64, 65, int(r.integers(1, 900)), int(r.integers(900, 3000))])) for _ in range(n)]
+    kind = ["decode_tokens", "decode_tokens_raw", "snapshots", "affine"][i % 4]
+    return dict(dtype=dtype, dk=dk, dv=dv, hqk=hqk, hv=hv, lens=lens, kind=kind,
+                init="normal" if r.random() < 0.6 else "zero", T=int(r.integers(1, 6)), P=int(r.choice([1, 2, 5])))
+
+
+@pytest.mark.parametrize("i", range(48))
+def test_seeded_entry_point_sweep(i):
+    """Random shapes for multi-token decode (plain and raw), prefill with snapshots and the affine
+    state map, against the oracle."""
+    c = _sweep2_case(i)
+    say(f"[sweep2 {i}] {c}")
+    dt, kind = c["dtype"], c["kind"]
+    if kind.startswith("decode_tokens"):
+        T, raw = c["T"], kind.endswith("raw")
+        inp = gi.make_inputs(gi.custom(dtype=dt, Hqk=c["hqk"], Hv=c["hv"], dk=c["dk"], dv=c["dv"],
+                                       seqlens=(T,) * len(c["lens"]), init_state="normal", raw=raw), seed=4000 + i)
+        st = dev(inp.init_state)
+        o, ts = B.gdn_decode_tokens(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), st, T,
+                                    token_states=True, raw=raw)
+        torch.cuda.synchronize()
+        ro, rs, rf = c_oracle.decode_tokens(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.init_state, T, raw=raw)
+        errs = [rel_err(host64(o), ro), rel_err(host64(st), rf), rel_err(host64(ts), rs)]
+    else:
+        inp = gi.make_inputs(gi.custom(dtype=dt, Hqk=c["hqk"], Hv=c["hv"], dk=c["dk"], dv=c["dv"],
+                                       seqlens=tuple(c["lens"]), init_state=c["init"]), seed=4000 + i)
+        q, k, v, g, b = (dev(x) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
+        cu = dev(inp.cu_seqlens) if inp.cu_seqlens is not None else None
+        kw = dict(cu_seqlens=cu) if cu is not None else dict(num_seqs=len(c["lens"]))
+        if kind == "affine":
+            m, bb = B.gdn_prefill_affine(k, v, g, b, **kw)
+            torch.cuda.synchronize()
+            rm, rb = _oracle_affine(inp)
+            errs = [float(np.max(np.abs(host64(m) - rm))) / max(float(np.max(np.abs(rm))), 1.0), rel_err(host64(bb), rb)]
+        else:
+            P = c["P"]
+            o, f, sn = B.gdn_prefill_snapshots(q, k, v, g, b, P, init_state=dev(inp.init_state), **kw)
+            torch.cuda.synchronize()
+            ro, rf = oracle_prefill(inp)
+            errs = [rel_err(host64(o), ro), rel_err(host64(f), rf)]
+            errs += [rel_err(host64(sn[slot]), ref) for slot, ref in oracle_snapshots(inp, 64 * P).items()]
+    say(f"[parity] sweep2 {i} {kind} {dt}: worst {max(errs):.3e}")
+    assert max(errs) <= TOL[dt]

@@ -176,6 +176,17 @@ def write_traffic_summary(fetch_csv, write_csv, prefill_calls):
     print(json.dumps(rec, indent=1))
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -463,7 +474,17 @@ def main():
                "sample": (f"the whole T=262144, H=16, d=128 prefill (all 16 heads)" if Ts == T else
                           f"first {Ts} tokens of the T=262144, H=16, d=128 prefill (all 16 heads)")
                          + f", fp64 sequential oracle, {cw:.1f}s wall"}
-        log(f"cpu oracle: {Ts} tokens in {cw:.1f}s on {cpu['cores']} threads")
+        # One thread on a shorter prefix of the same workload, for the per-core rate.
+        T1 = min(8192, Ts)
+        t1 = time.perf_counter()
+        c_oracle.prefill(sub.q[:T1], sub.k[:T1], sub.v[:T1], sub.g[:T1], sub.beta[:T1], None, None,
+                         nthreads=1)
+        cw1 = time.perf_counter() - t1
+        cpu["single_thread"] = {"value": round(T1 / cw1, 1), "unit": "tokens/s",
+                                "sample": f"first {T1} tokens, all 16 heads, {cw1:.1f}s wall"}
+        cpu["host"] = {"cpus": os.cpu_count(), "model": _cpu_model()}
+        log(f"cpu oracle: {Ts} tokens in {cw:.1f}s on {cpu['cores']} threads; "
+            f"{T1} tokens in {cw1:.1f}s on 1 thread")
 
     if args.calib_copy:
         src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")

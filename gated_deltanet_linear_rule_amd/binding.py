@@ -23,6 +23,9 @@ GDN_ERROR_LAUNCH = 3
 GDN_ERROR_OUT_OF_MEMORY = 4
 GDN_DTYPE_F32 = 0
 GDN_DTYPE_BF16 = 1
+GDN_WS_PACKED = 1
+GDN_WS_RAW = 2
+GDN_WS_AFFINE = 4
 
 
 class GdnShape(ctypes.Structure):
@@ -62,15 +65,22 @@ def lib() -> ctypes.CDLL:
         L.gdn_decode_slots.restype = ctypes.c_int
         L.gdn_prefill_snapshots.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, P]
         L.gdn_prefill_snapshots.restype = ctypes.c_int
-        L.gdn_prefill_workspace_size.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_int32,
+        L.gdn_prefill_snapshots_ws.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, ctypes.c_int32,
+                                               P, P, ctypes.c_size_t, P]
+        L.gdn_prefill_snapshots_ws.restype = ctypes.c_int
+        L.gdn_prefill_workspace_size.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_uint32,
                                                  ctypes.POINTER(ctypes.c_size_t)]
         L.gdn_prefill_workspace_size.restype = ctypes.c_int
         L.gdn_prefill_ws.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.gdn_prefill_ws.restype = ctypes.c_int
         L.gdn_prefill_affine.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P]
         L.gdn_prefill_affine.restype = ctypes.c_int
+        L.gdn_prefill_affine_ws.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.gdn_prefill_affine_ws.restype = ctypes.c_int
         L.gdn_prefill_raw.argtypes = L.gdn_prefill.argtypes
         L.gdn_prefill_raw.restype = ctypes.c_int
+        L.gdn_prefill_raw_ws.argtypes = L.gdn_prefill_ws.argtypes
+        L.gdn_prefill_raw_ws.restype = ctypes.c_int
         L.gdn_decode_tokens_raw.argtypes = L.gdn_decode_tokens.argtypes
         L.gdn_decode_tokens_raw.restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
@@ -130,30 +140,48 @@ def _raise(rc, where):
         raise GdnError(rc, where, lib().gdn_last_error().decode())
 
 
-def gdn_prefill_workspace_size(q, v, cu_seqlens=None, num_seqs=None) -> int:
-    """Bytes of device workspace that ``gdn_prefill(..., workspace=...)`` needs for these
-    shapes on the current device (q [T, Hqk, dk], v [T, Hv, dv]; packed if cu_seqlens is given)."""
+def gdn_prefill_workspace_size(q, v, cu_seqlens=None, num_seqs=None, raw=False, affine=False) -> int:
+    """Bytes of device workspace a prefill call with these shapes needs on the current device
+    (q [T, Hqk, dk] -- for the affine map pass k --, v [T, Hv, dv]; packed if cu_seqlens is given;
+    raw / affine for gdn_prefill_raw / gdn_prefill_affine)."""
     T, hqk, dk = q.shape
     hv, dv = v.shape[1], v.shape[2]
     N = cu_seqlens.numel() - 1 if cu_seqlens is not None else (1 if num_seqs is None else int(num_seqs))
     shape = GdnShape(N, T, hqk, hv, dk, dv, _io_dtype(q))
+    flags = (GDN_WS_PACKED if cu_seqlens is not None else 0) | (GDN_WS_RAW if raw else 0) | \
+        (GDN_WS_AFFINE if affine else 0)
     n = ctypes.c_size_t(0)
-    _raise(lib().gdn_prefill_workspace_size(ctypes.byref(shape), int(cu_seqlens is not None), ctypes.byref(n)),
+    _raise(lib().gdn_prefill_workspace_size(ctypes.byref(shape), flags, ctypes.byref(n)),
            "gdn_prefill_workspace_size")
     return int(n.value)
 
 
+def _workspace(workspace, use_pool, q, v, cu_seqlens, N, raw=False, affine=False):
+    """(pointer, bytes) of the workspace for a *_ws call, or None for the pool form.
+    workspace=None allocates one from torch's allocator for this call."""
+    if use_pool:
+        if workspace is not None:
+            raise ValueError("use_pool=True takes no workspace")
+        return None
+    if workspace is None:
+        n = gdn_prefill_workspace_size(q, v, cu_seqlens, N, raw=raw, affine=affine)
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+    _check(workspace, "workspace")
+    return workspace, ctypes.c_size_t(workspace.numel() * workspace.element_size())
+
+
 def gdn_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, out=None, final_state=None,
-                stream=None, num_seqs=None, return_final_state=True, raw=False, workspace=None):
+                stream=None, num_seqs=None, return_final_state=True, raw=False, workspace=None, use_pool=False):
     """Chunked GDN prefill over packed sequences.
 
     q, k [T, Hqk, dk]; v [T, Hv, dv] (bf16 or fp32, same dtype); g, beta [T, Hv]
     fp32; init_state [N, Hv, dv, dk] fp32 or None; cu_seqlens int32 [N+1] on
     the GPU or None (then ``num_seqs`` equal-length sequences, default 1).
     Returns (out, final_state); final_state is None if not requested.
-    raw=True calls gdn_prefill_raw: q, k unnormalised, g and beta are the logits a, b.
-    workspace: a contiguous GPU tensor of at least gdn_prefill_workspace_size bytes
-    (calls gdn_prefill_ws, which allocates nothing; not with raw=True).
+    raw=True calls the raw-projection form: q, k unnormalised, g and beta are the logits a, b.
+    workspace: a contiguous GPU tensor of at least gdn_prefill_workspace_size bytes (allocated from
+    torch for this call if None); the library's *_ws entry point runs on it.  use_pool=True calls the
+    form that takes its workspace from HIP's default stream-ordered pool instead.
     """
     T, hqk, dk = q.shape
     hv, dv = v.shape[1], v.shape[2]
@@ -176,27 +204,23 @@ def gdn_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, out=None, fi
         final_state = torch.empty((N, hv, dv, dk), dtype=torch.float32, device=q.device)
     _check(final_state, "final_state", torch.float32, (N, hv, dv, dk))
     shape = GdnShape(N, T, hqk, hv, dk, dv, io)
-    if workspace is not None:
-        if raw:
-            raise ValueError("a caller workspace is taken by gdn_prefill_ws, which has no raw-projection form")
-        _check(workspace, "workspace")
-        rc = lib().gdn_prefill_ws(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                  _ptr(init_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state),
-                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
-        _raise(rc, "gdn_prefill_ws")
-        return out, final_state
-    fn = lib().gdn_prefill_raw if raw else lib().gdn_prefill
-    rc = fn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-            _ptr(init_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state), _stream(stream))
-    _raise(rc, "gdn_prefill_raw" if raw else "gdn_prefill")
+    args = (ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(init_state), _ptr(cu_seqlens),
+            _ptr(out), _ptr(final_state))
+    ws = _workspace(workspace, use_pool, q, v, cu_seqlens, N, raw=raw)
+    name = "gdn_prefill" + ("_raw" if raw else "") + ("" if ws is None else "_ws")
+    fn = getattr(lib(), name)
+    rc = fn(*args, _stream(stream)) if ws is None else fn(*args, _ptr(ws[0]), ws[1], _stream(stream))
+    _raise(rc, name)
     return out, final_state
 
 
-def gdn_prefill_affine(k, v, g, beta, cu_seqlens=None, transition=None, offset=None, stream=None, num_seqs=None):
+def gdn_prefill_affine(k, v, g, beta, cu_seqlens=None, transition=None, offset=None, stream=None, num_seqs=None,
+                       workspace=None, use_pool=False):
     """State map of each whole sequence: S -> S @ transition + offset.
 
     k [T, Hqk, dk]; v [T, Hv, dv] (bf16 or fp32); g, beta [T, Hv] fp32; cu_seqlens as for gdn_prefill.
-    Returns (transition [N, Hv, dk, dk], offset [N, Hv, dv, dk]), fp32 (allocated if None)."""
+    Returns (transition [N, Hv, dk, dk], offset [N, Hv, dv, dk]), fp32 (allocated if None).
+    workspace / use_pool as for gdn_prefill."""
     T, hqk, dk = k.shape
     hv, dv = v.shape[1], v.shape[2]
     io = _io_dtype(k)
@@ -216,9 +240,13 @@ def gdn_prefill_affine(k, v, g, beta, cu_seqlens=None, transition=None, offset=N
     _check(transition, "transition", torch.float32, (N, hv, dk, dk))
     _check(offset, "offset", torch.float32, (N, hv, dv, dk))
     shape = GdnShape(N, T, hqk, hv, dk, dv, io)
-    rc = lib().gdn_prefill_affine(ctypes.byref(shape), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
-                                  _ptr(transition), _ptr(offset), _stream(stream))
-    _raise(rc, "gdn_prefill_affine")
+    args = (ctypes.byref(shape), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), _ptr(transition),
+            _ptr(offset))
+    ws = _workspace(workspace, use_pool, k, v, cu_seqlens, N, affine=True)
+    if ws is None:
+        _raise(lib().gdn_prefill_affine(*args, _stream(stream)), "gdn_prefill_affine")
+    else:
+        _raise(lib().gdn_prefill_affine_ws(*args, _ptr(ws[0]), ws[1], _stream(stream)), "gdn_prefill_affine_ws")
     return transition, offset
 
 
@@ -321,10 +349,10 @@ def snapshot_slots(num_tokens, num_seqs, snapshot_chunks):
 
 
 def gdn_prefill_snapshots(q, k, v, g, beta, snapshot_chunks, init_state=None, cu_seqlens=None, snapshots=None,
-                          out=None, final_state=None, stream=None, num_seqs=None):
+                          out=None, final_state=None, stream=None, num_seqs=None, workspace=None, use_pool=False):
     """``gdn_prefill`` that also writes the state after every 64 * ``snapshot_chunks`` tokens of each
     sequence into ``snapshots`` [slots, Hv, dv, dk] (allocated if None; see ``snapshot_slots``).
-    Returns (out, final_state, snapshots)."""
+    workspace / use_pool as for gdn_prefill.  Returns (out, final_state, snapshots)."""
     T, hqk, dk = q.shape
     hv, dv = v.shape[1], v.shape[2]
     if num_seqs is None:
@@ -350,8 +378,11 @@ def gdn_prefill_snapshots(q, k, v, g, beta, snapshot_chunks, init_state=None, cu
     _check(final_state, "final_state", torch.float32, (N, hv, dv, dk))
     _check(snapshots, "snapshots", torch.float32, (snapshots.shape[0], hv, dv, dk))
     shape = GdnShape(N, T, hqk, hv, dk, dv, io)
-    rc = lib().gdn_prefill_snapshots(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                     _ptr(init_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state),
-                                     int(snapshot_chunks), _ptr(snapshots), _stream(stream))
-    _raise(rc, "gdn_prefill_snapshots")
+    args = (ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(init_state), _ptr(cu_seqlens),
+            _ptr(out), _ptr(final_state), int(snapshot_chunks), _ptr(snapshots))
+    ws = _workspace(workspace, use_pool, q, v, cu_seqlens, N)
+    if ws is None:
+        _raise(lib().gdn_prefill_snapshots(*args, _stream(stream)), "gdn_prefill_snapshots")
+    else:
+        _raise(lib().gdn_prefill_snapshots_ws(*args, _ptr(ws[0]), ws[1], _stream(stream)), "gdn_prefill_snapshots_ws")
     return out, final_state, snapshots

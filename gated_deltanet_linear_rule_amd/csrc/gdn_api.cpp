@@ -1,17 +1,17 @@
 // gdn_api.cpp -- the C ABI of libgdn.so (declared in include/gdn.h).
 //
 // Validates every host-checkable argument before touching HIP, picks the
-// kernel variant, takes the prefill workspace from HIP's stream-ordered pool
-// (or from the caller, gdn_prefill_ws) and enqueues the kernels on the
-// caller's stream.  No exception or abort
-// crosses the ABI; the text of the last failure is kept per thread.
+// kernel variant, takes the prefill workspace from the caller (the *_ws entry
+// points) or from the device's default stream-ordered pool, and enqueues the
+// kernels on the caller's stream.  No exception or abort crosses the ABI; the
+// text of the last failure is kept per thread.  The library keeps no state
+// between calls and changes no process-wide setting.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
-#include <mutex>
 
 #include "gdn.h"
 #include "gdn_internal.h"
@@ -33,11 +33,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // Optional debugging aid: GDN_DEBUG_SYNC=1 synchronises the stream after each
 // call and reports asynchronous kernel errors as GDN_ERROR_LAUNCH.
 bool debug_sync() {
-    static const bool on = [] {
-        const char* s = std::getenv("GDN_DEBUG_SYNC");
-        return s && s[0] && s[0] != '0';
-    }();
-    return on;
+    const char* s = std::getenv("GDN_DEBUG_SYNC");
+    return s && s[0] && s[0] != '0';
 }
 
 gdn_status check_shape(const gdn_shape* s, bool decode) {
@@ -77,37 +74,15 @@ gdn_status check_ptr(const void* p, const char* name, uintptr_t align, bool requ
         if (st_ != GDN_SUCCESS) return st_;   \
     } while (0)
 
-// Keep freed workspace in HIP's default pool instead of returning it to the
-// driver at every synchronisation (set once per device).
-void keep_pool_memory(int dev) {
-    static std::mutex mu;
-    static bool done[64] = {};
-    if (dev < 0 || dev >= 64) return;
-    std::lock_guard<std::mutex> lk(mu);
-    if (done[dev]) return;
-    hipMemPool_t pool;
-    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
-        uint64_t thr = UINT64_MAX;
-        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+// Compute units of the current device (0 if the query fails); queried on every
+// call, so the library keeps no per-device state.
+int current_compute_units() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
     }
-    done[dev] = true;
-}
-
-// Compute units of device `dev` (cached; 0 if the query fails).
-int compute_units(int dev) {
-    static std::mutex mu;
-    static int cached[64] = {};
-    if (dev < 0 || dev >= 64) return 0;
-    std::lock_guard<std::mutex> lk(mu);
-    if (cached[dev] == 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
-            (void)hipGetLastError();
-            return 0;
-        }
-        cached[dev] = cus;
-    }
-    return cached[dev];
+    return cus;
 }
 
 }  // namespace
@@ -229,9 +204,13 @@ gdn_status gdn_decode_tokens_raw(const gdn_shape* shape, int32_t tokens_per_seq,
 
 namespace {
 
+// Which prefill entry point a call comes from (selects the kernels and the
+// workspace layout).
+enum PrefillKind { kPlain, kRaw, kSnapshots, kAffine };
+
 // The part length, slot counts and workspace layout of one prefill call on
 // the current device; `packed` tells whether cu_seqlens will be given.
-gdn_status plan_prefill(const gdn_shape* shape, bool packed, bool raw, gdn::PrefillArgs& a, bool& split,
+gdn_status plan_prefill(const gdn_shape* shape, bool packed, PrefillKind kind, gdn::PrefillArgs& a, bool& split,
                         int64_t& total) {
     a.num_tokens = shape->num_tokens;
     a.seqlen = shape->num_tokens / shape->num_seqs;
@@ -241,91 +220,123 @@ gdn_status plan_prefill(const gdn_shape* shape, bool packed, bool raw, gdn::Pref
     a.dv = shape->head_dim_v;
     a.num_slots = (shape->num_tokens + 63) / 64 + shape->num_seqs;
     if (a.num_slots > INT32_MAX) return fail(GDN_ERROR_NOT_SUPPORTED, "too many chunks");
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return fail(GDN_ERROR_LAUNCH, "hipGetDevice failed");
-    const int cus = compute_units(dev);
+    const int cus = current_compute_units();
     if (cus <= 0) return fail(GDN_ERROR_LAUNCH, "cannot query the device's compute units");
     a.part_chunks = gdn::prefill_part_chunks(a.num_tokens, a.num_seqs, a.hv, cus);
     const int64_t span = a.part_chunks * 64;
     a.num_part_slots = (a.num_tokens + span - 1) / span + a.num_seqs;
     const int64_t longest = packed ? (a.num_tokens + 63) / 64 : (a.seqlen + 63) / 64;
-    split = a.part_chunks < longest;
-    if (a.num_part_slots * a.hv > INT32_MAX || a.num_seqs * (int64_t)a.hv * (a.dv / 16) > INT32_MAX)
+    // the affine map needs every sequence's part maps, split or not
+    split = kind == kAffine || a.part_chunks < longest;
+    if (a.num_part_slots * a.hv > INT32_MAX ||
+        a.num_seqs * (int64_t)a.hv * (a.dv / 16 + shape->head_dim_k / 16) > INT32_MAX)
         return fail(GDN_ERROR_NOT_SUPPORTED, "too many (part, head) pairs");
     const gdn::PrefillWorkspace wl(a.num_slots, a.num_part_slots, split, a.hv, shape->head_dim_k, shape->head_dim_v,
-                                   shape->dtype == GDN_DTYPE_BF16 ? 2 : 4, raw);
+                                   shape->dtype == GDN_DTYPE_BF16 ? 2 : 4, kind == kRaw);
     total = wl.total;
     return GDN_SUCCESS;
 }
 
-// `workspace` NULL: the workspace comes from HIP's stream-ordered pool.
-gdn_status prefill_impl(const char* who, const gdn_shape* shape, const void* q, const void* k, const void* v,
-                        const float* g, const float* beta, const float* init_state, const int32_t* cu_seqlens,
-                        void* out, float* final_state, int32_t snapshot_chunks, float* snapshots, void* stream,
-                        bool raw = false, void* workspace = nullptr, size_t workspace_bytes = 0) {
+// The arguments of every prefill entry point (unused ones NULL / 0).
+struct PrefillCall {
+    const void *q, *k, *v;
+    const float *g, *beta, *init_state;
+    const int32_t* cu;
+    void* out;
+    float* final_state;
+    int32_t snapshot_chunks;
+    float* snapshots;
+    float *transition, *offset;   // affine map
+};
+
+// Where a prefill call's workspace comes from: the current device's default
+// stream-ordered pool (hipMallocAsync / hipFreeAsync on the call's stream; the
+// pool's settings are left as the caller set them) or the caller.
+enum WsSource { kPoolWs, kCallerWs };
+
+// Validates a prefill call, lays out its workspace and enqueues its kernels.
+gdn_status prefill_impl(const char* who, PrefillKind kind, const gdn_shape* shape, const PrefillCall& c, void* stream,
+                        WsSource src, void* workspace = nullptr, size_t workspace_bytes = 0) {
     g_last_error[0] = '\0';
+    const bool caller_ws = src == kCallerWs;
+    if (caller_ws && !workspace) return fail(GDN_ERROR_INVALID_VALUE, "workspace is NULL");
+    if (kind == kSnapshots && !c.snapshots) return fail(GDN_ERROR_INVALID_VALUE, "snapshots is NULL");
     GDN_TRY(check_shape(shape, false));
-    const bool tok = shape->num_tokens > 0;
-    GDN_TRY(check_ptr(q, "q", 16, tok));
-    GDN_TRY(check_ptr(k, "k", 16, tok));
-    GDN_TRY(check_ptr(v, "v", 16, tok));
-    GDN_TRY(check_ptr(g, "g", 4, tok));
-    GDN_TRY(check_ptr(beta, "beta", 4, tok));
-    GDN_TRY(check_ptr(out, "out", 16, tok));
-    GDN_TRY(check_ptr(init_state, "init_state", 16, false));
-    GDN_TRY(check_ptr(final_state, "final_state", 16, false));
-    GDN_TRY(check_ptr(cu_seqlens, "cu_seqlens", 4, false));
+    const bool tok = shape->num_tokens > 0, any = shape->num_seqs > 0;
+    const bool affine = kind == kAffine;
+    if (!affine) GDN_TRY(check_ptr(c.q, "q", 16, tok));
+    GDN_TRY(check_ptr(c.k, "k", 16, tok));
+    GDN_TRY(check_ptr(c.v, "v", 16, tok));
+    GDN_TRY(check_ptr(c.g, "g", 4, tok));
+    GDN_TRY(check_ptr(c.beta, "beta", 4, tok));
+    if (affine) {
+        GDN_TRY(check_ptr(c.transition, "transition", 16, any));
+        GDN_TRY(check_ptr(c.offset, "offset", 16, any));
+    } else {
+        GDN_TRY(check_ptr(c.out, "out", 16, tok));
+        GDN_TRY(check_ptr(c.init_state, "init_state", 16, false));
+        GDN_TRY(check_ptr(c.final_state, "final_state", 16, false));
+    }
+    GDN_TRY(check_ptr(c.cu, "cu_seqlens", 4, false));
     GDN_TRY(check_ptr(workspace, "workspace", 256, false));
-    if (!cu_seqlens && shape->num_seqs > 0 && shape->num_tokens % shape->num_seqs != 0)
+    if (!c.cu && any && shape->num_tokens % shape->num_seqs != 0)
         return fail(GDN_ERROR_INVALID_VALUE, "num_tokens (%lld) is not a multiple of num_seqs (%d) and no cu_seqlens",
                     (long long)shape->num_tokens, shape->num_seqs);
-    if (init_state && final_state && init_state != final_state) {
-        const size_t bytes = (size_t)shape->num_seqs * shape->num_v_heads * shape->head_dim_v * shape->head_dim_k * 4;
-        const char* a0 = reinterpret_cast<const char*>(init_state);
-        const char* b0 = reinterpret_cast<const char*>(final_state);
-        if (a0 < b0 + bytes && b0 < a0 + bytes)
+    const size_t sbytes = (size_t)shape->num_seqs * shape->num_v_heads * shape->head_dim_v * shape->head_dim_k * 4;
+    if (c.init_state && c.final_state && c.init_state != c.final_state) {
+        const char* a0 = reinterpret_cast<const char*>(c.init_state);
+        const char* b0 = reinterpret_cast<const char*>(c.final_state);
+        if (a0 < b0 + sbytes && b0 < a0 + sbytes)
             return fail(GDN_ERROR_INVALID_VALUE, "init_state and final_state overlap partially");
     }
-    GDN_TRY(check_ptr(snapshots, "snapshots", 16, false));
-    if (snapshots && snapshot_chunks <= 0)
-        return fail(GDN_ERROR_INVALID_VALUE, "snapshot_chunks must be positive (got %d)", snapshot_chunks);
-    if (shape->num_seqs == 0) return GDN_SUCCESS;
+    if (affine && any) {
+        const size_t mb = (size_t)shape->num_seqs * shape->num_v_heads * shape->head_dim_k * shape->head_dim_k * 4;
+        const char* m0 = reinterpret_cast<const char*>(c.transition);
+        const char* b0 = reinterpret_cast<const char*>(c.offset);
+        if (m0 < b0 + sbytes && b0 < m0 + mb) return fail(GDN_ERROR_INVALID_VALUE, "transition and offset overlap");
+    }
+    if (kind == kSnapshots) {
+        GDN_TRY(check_ptr(c.snapshots, "snapshots", 16, true));
+        if (c.snapshot_chunks <= 0)
+            return fail(GDN_ERROR_INVALID_VALUE, "snapshot_chunks must be positive (got %d)", c.snapshot_chunks);
+    }
+    if (!any) return GDN_SUCCESS;
 
     const bool bf16 = shape->dtype == GDN_DTYPE_BF16;
     gdn::PrefillArgs a{};
-    a.snapshots = snapshots;
-    a.snap_chunks = snapshots ? snapshot_chunks : 0;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
-    a.init_state = init_state; a.cu = cu_seqlens; a.out = out; a.final_state = final_state;
+    a.q = affine ? c.k : c.q;
+    a.k = c.k; a.v = c.v; a.g = c.g; a.beta = c.beta;
+    a.init_state = c.init_state; a.cu = c.cu; a.out = c.out; a.final_state = c.final_state;
+    a.snapshots = kind == kSnapshots ? c.snapshots : nullptr;
+    a.snap_chunks = kind == kSnapshots ? c.snapshot_chunks : 0;
+    a.aff_m = affine ? c.transition : nullptr;
+    a.aff_b = affine ? c.offset : nullptr;
     bool split = false;
     int64_t total = 0;
-    GDN_TRY(plan_prefill(shape, cu_seqlens != nullptr, raw, a, split, total));
+    GDN_TRY(plan_prefill(shape, c.cu != nullptr, kind, a, split, total));
     const gdn::PrefillWorkspace wl(a.num_slots, a.num_part_slots, split, a.hv, shape->head_dim_k, shape->head_dim_v,
-                                   bf16 ? 2 : 4, raw);
+                                   bf16 ? 2 : 4, kind == kRaw);
     hipStream_t st = static_cast<hipStream_t>(stream);
     void* ws = workspace;
-    if (workspace) {
+    if (caller_ws) {
         if (workspace_bytes < (size_t)total)
             return fail(GDN_ERROR_INVALID_VALUE, "workspace of %zu bytes, this call needs %lld", workspace_bytes,
                         (long long)total);
-    } else {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return fail(GDN_ERROR_LAUNCH, "hipGetDevice failed");
-        keep_pool_memory(dev);
-        if (hipMallocAsync(&ws, (size_t)total, st) != hipSuccess || !ws) {
-            (void)hipGetLastError();
-            return fail(GDN_ERROR_OUT_OF_MEMORY, "prefill workspace of %lld bytes", (long long)total);
-        }
+    } else if (hipMallocAsync(&ws, (size_t)total, st) != hipSuccess || !ws) {
+        (void)hipGetLastError();
+        return fail(GDN_ERROR_OUT_OF_MEMORY, "%s workspace of %lld bytes", who, (long long)total);
     }
     char* wc = static_cast<char*>(ws);
     a.ws_t = wc + wl.t;
     a.ws_g = reinterpret_cast<double*>(wc + wl.g);
-    a.ws_ik = raw ? reinterpret_cast<float*>(wc + wl.ik) : nullptr;
+    a.ws_ik = kind == kRaw ? reinterpret_cast<float*>(wc + wl.ik) : nullptr;
     a.ws_m = split ? reinterpret_cast<float*>(wc + wl.m) : nullptr;
     a.ws_b = split ? reinterpret_cast<float*>(wc + wl.b) : nullptr;
     a.ws_s = split ? reinterpret_cast<float*>(wc + wl.s) : nullptr;
-    hipError_t e = gdn::launch_prefill(a, bf16, shape->head_dim_k, shape->head_dim_v, st, raw);
-    if (!workspace) {
+    const int dk = shape->head_dim_k, dv = shape->head_dim_v;
+    hipError_t e = affine ? gdn::launch_prefill_affine(a, bf16, dk, dv, st)
+                          : gdn::launch_prefill(a, bf16, dk, dv, st, kind == kRaw);
+    if (src == kPoolWs) {
         const hipError_t ef = hipFreeAsync(ws, st);
         if (e == hipSuccess) e = ef;
     }
@@ -334,22 +345,36 @@ gdn_status prefill_impl(const char* who, const gdn_shape* shape, const void* q, 
     return GDN_SUCCESS;
 }
 
+PrefillCall call_of(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                    const float* init_state, const int32_t* cu, void* out, float* final_state) {
+    PrefillCall c{};
+    c.q = q; c.k = k; c.v = v; c.g = g; c.beta = beta;
+    c.init_state = init_state; c.cu = cu; c.out = out; c.final_state = final_state;
+    return c;
+}
+
+PrefillCall affine_call(const void* k, const void* v, const float* g, const float* beta, const int32_t* cu,
+                        float* transition, float* offset) {
+    PrefillCall c{};
+    c.k = k; c.v = v; c.g = g; c.beta = beta; c.cu = cu;
+    c.transition = transition; c.offset = offset;
+    return c;
+}
+
 }  // namespace
 
 extern "C" {
 
-gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, const void* v, const float* g,
-                       const float* beta, const float* init_state, const int32_t* cu_seqlens, void* out,
-                       float* final_state, void* stream) {
-    return prefill_impl("prefill", shape, q, k, v, g, beta, init_state, cu_seqlens, out, final_state, 0, nullptr,
-                        stream);
-}
-
-gdn_status gdn_prefill_workspace_size(const gdn_shape* shape, int32_t packed, size_t* bytes) {
+gdn_status gdn_prefill_workspace_size(const gdn_shape* shape, uint32_t flags, size_t* bytes) {
     g_last_error[0] = '\0';
     if (!bytes) return fail(GDN_ERROR_INVALID_VALUE, "bytes is NULL");
     *bytes = 0;
+    if (flags & ~(uint32_t)(GDN_WS_PACKED | GDN_WS_RAW | GDN_WS_AFFINE))
+        return fail(GDN_ERROR_INVALID_VALUE, "unknown workspace flags 0x%x", (unsigned)flags);
+    if ((flags & GDN_WS_RAW) && (flags & GDN_WS_AFFINE))
+        return fail(GDN_ERROR_INVALID_VALUE, "GDN_WS_RAW and GDN_WS_AFFINE exclude each other");
     GDN_TRY(check_shape(shape, false));
+    const bool packed = (flags & GDN_WS_PACKED) != 0;
     if (!packed && shape->num_seqs > 0 && shape->num_tokens % shape->num_seqs != 0)
         return fail(GDN_ERROR_INVALID_VALUE, "num_tokens (%lld) is not a multiple of num_seqs (%d) and not packed",
                     (long long)shape->num_tokens, shape->num_seqs);
@@ -357,99 +382,77 @@ gdn_status gdn_prefill_workspace_size(const gdn_shape* shape, int32_t packed, si
     gdn::PrefillArgs a{};
     bool split = false;
     int64_t total = 0;
-    GDN_TRY(plan_prefill(shape, packed != 0, false, a, split, total));
+    const PrefillKind kind = (flags & GDN_WS_RAW) ? kRaw : (flags & GDN_WS_AFFINE) ? kAffine : kPlain;
+    GDN_TRY(plan_prefill(shape, packed, kind, a, split, total));
     *bytes = (size_t)total;
     return GDN_SUCCESS;
+}
+
+gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, const float* init_state, const int32_t* cu_seqlens, void* out,
+                       float* final_state, void* stream) {
+    return prefill_impl("prefill", kPlain, shape, call_of(q, k, v, g, beta, init_state, cu_seqlens, out, final_state),
+                        stream, kPoolWs);
 }
 
 gdn_status gdn_prefill_ws(const gdn_shape* shape, const void* q, const void* k, const void* v, const float* g,
                           const float* beta, const float* init_state, const int32_t* cu_seqlens, void* out,
                           float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
-    if (!workspace) {
-        g_last_error[0] = '\0';
-        return fail(GDN_ERROR_INVALID_VALUE, "workspace is NULL");
-    }
-    return prefill_impl("prefill_ws", shape, q, k, v, g, beta, init_state, cu_seqlens, out, final_state, 0, nullptr,
-                        stream, false, workspace, workspace_bytes);
+    return prefill_impl("prefill_ws", kPlain, shape,
+                        call_of(q, k, v, g, beta, init_state, cu_seqlens, out, final_state), stream, kCallerWs, workspace,
+                        workspace_bytes);
 }
 
-gdn_status gdn_prefill_affine(const gdn_shape* shape, const void* k, const void* v, const float* g,
-                              const float* beta, const int32_t* cu_seqlens, float* transition, float* offset,
-                              void* stream) {
-    g_last_error[0] = '\0';
-    GDN_TRY(check_shape(shape, false));
-    const bool tok = shape->num_tokens > 0;
-    GDN_TRY(check_ptr(k, "k", 16, tok));
-    GDN_TRY(check_ptr(v, "v", 16, tok));
-    GDN_TRY(check_ptr(g, "g", 4, tok));
-    GDN_TRY(check_ptr(beta, "beta", 4, tok));
-    GDN_TRY(check_ptr(cu_seqlens, "cu_seqlens", 4, false));
-    const bool any = shape->num_seqs > 0;
-    GDN_TRY(check_ptr(transition, "transition", 16, any));
-    GDN_TRY(check_ptr(offset, "offset", 16, any));
-    if (!cu_seqlens && shape->num_seqs > 0 && shape->num_tokens % shape->num_seqs != 0)
-        return fail(GDN_ERROR_INVALID_VALUE, "num_tokens (%lld) is not a multiple of num_seqs (%d) and no cu_seqlens",
-                    (long long)shape->num_tokens, shape->num_seqs);
-    if (!any) return GDN_SUCCESS;
-    {
-        const size_t mb = (size_t)shape->num_seqs * shape->num_v_heads * shape->head_dim_k * shape->head_dim_k * 4;
-        const size_t bb = (size_t)shape->num_seqs * shape->num_v_heads * shape->head_dim_v * shape->head_dim_k * 4;
-        const char* m0 = reinterpret_cast<const char*>(transition);
-        const char* b0 = reinterpret_cast<const char*>(offset);
-        if (m0 < b0 + bb && b0 < m0 + mb) return fail(GDN_ERROR_INVALID_VALUE, "transition and offset overlap");
-    }
-    const bool bf16 = shape->dtype == GDN_DTYPE_BF16;
-    gdn::PrefillArgs a{};
-    a.q = k; a.k = k; a.v = v; a.g = g; a.beta = beta;
-    a.cu = cu_seqlens;
-    a.aff_m = transition;
-    a.aff_b = offset;
-    bool split = false;
-    int64_t total = 0;
-    GDN_TRY(plan_prefill(shape, cu_seqlens != nullptr, false, a, split, total));
-    // every sequence gets its part maps, split or not
-    const gdn::PrefillWorkspace wl(a.num_slots, a.num_part_slots, true, a.hv, shape->head_dim_k, shape->head_dim_v,
-                                   bf16 ? 2 : 4);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return fail(GDN_ERROR_LAUNCH, "hipGetDevice failed");
-    keep_pool_memory(dev);
-    void* ws = nullptr;
-    if (hipMallocAsync(&ws, (size_t)wl.total, st) != hipSuccess || !ws) {
-        (void)hipGetLastError();
-        return fail(GDN_ERROR_OUT_OF_MEMORY, "prefill_affine workspace of %lld bytes", (long long)wl.total);
-    }
-    char* wc = static_cast<char*>(ws);
-    a.ws_t = wc + wl.t;
-    a.ws_g = reinterpret_cast<double*>(wc + wl.g);
-    a.ws_m = reinterpret_cast<float*>(wc + wl.m);
-    a.ws_b = reinterpret_cast<float*>(wc + wl.b);
-    a.ws_s = reinterpret_cast<float*>(wc + wl.s);
-    hipError_t e = gdn::launch_prefill_affine(a, bf16, shape->head_dim_k, shape->head_dim_v, st);
-    const hipError_t ef = hipFreeAsync(ws, st);
-    if (e == hipSuccess) e = ef;
-    if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(st);
-    if (e != hipSuccess) return fail(GDN_ERROR_LAUNCH, "prefill_affine: %s", hipGetErrorString(e));
-    return GDN_SUCCESS;
+gdn_status gdn_prefill_raw(const gdn_shape* shape, const void* q, const void* k, const void* v, const float* a_gate,
+                           const float* b_beta, const float* init_state, const int32_t* cu_seqlens, void* out,
+                           float* final_state, void* stream) {
+    return prefill_impl("prefill_raw", kRaw, shape,
+                        call_of(q, k, v, a_gate, b_beta, init_state, cu_seqlens, out, final_state), stream, kPoolWs);
+}
+
+gdn_status gdn_prefill_raw_ws(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                              const float* a_gate, const float* b_beta, const float* init_state,
+                              const int32_t* cu_seqlens, void* out, float* final_state, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    return prefill_impl("prefill_raw_ws", kRaw, shape,
+                        call_of(q, k, v, a_gate, b_beta, init_state, cu_seqlens, out, final_state), stream, kCallerWs,
+                        workspace, workspace_bytes);
 }
 
 gdn_status gdn_prefill_snapshots(const gdn_shape* shape, const void* q, const void* k, const void* v,
                                  const float* g, const float* beta, const float* init_state,
                                  const int32_t* cu_seqlens, void* out, float* final_state, int32_t snapshot_chunks,
                                  float* snapshots, void* stream) {
-    if (!snapshots) {
-        g_last_error[0] = '\0';
-        return fail(GDN_ERROR_INVALID_VALUE, "snapshots is NULL");
-    }
-    return prefill_impl("prefill_snapshots", shape, q, k, v, g, beta, init_state, cu_seqlens, out, final_state,
-                        snapshot_chunks, snapshots, stream);
+    PrefillCall c = call_of(q, k, v, g, beta, init_state, cu_seqlens, out, final_state);
+    c.snapshot_chunks = snapshot_chunks;
+    c.snapshots = snapshots;
+    return prefill_impl("prefill_snapshots", kSnapshots, shape, c, stream, kPoolWs);
 }
 
-gdn_status gdn_prefill_raw(const gdn_shape* shape, const void* q, const void* k, const void* v, const float* a_gate,
-                           const float* b_beta, const float* init_state, const int32_t* cu_seqlens, void* out,
-                           float* final_state, void* stream) {
-    return prefill_impl("prefill_raw", shape, q, k, v, a_gate, b_beta, init_state, cu_seqlens, out, final_state, 0,
-                        nullptr, stream, true);
+gdn_status gdn_prefill_snapshots_ws(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                                    const float* g, const float* beta, const float* init_state,
+                                    const int32_t* cu_seqlens, void* out, float* final_state,
+                                    int32_t snapshot_chunks, float* snapshots, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    PrefillCall c = call_of(q, k, v, g, beta, init_state, cu_seqlens, out, final_state);
+    c.snapshot_chunks = snapshot_chunks;
+    c.snapshots = snapshots;
+    return prefill_impl("prefill_snapshots_ws", kSnapshots, shape, c, stream, kCallerWs, workspace, workspace_bytes);
+}
+
+gdn_status gdn_prefill_affine(const gdn_shape* shape, const void* k, const void* v, const float* g,
+                              const float* beta, const int32_t* cu_seqlens, float* transition, float* offset,
+                              void* stream) {
+    return prefill_impl("prefill_affine", kAffine, shape, affine_call(k, v, g, beta, cu_seqlens, transition, offset),
+                        stream, kPoolWs);
+}
+
+gdn_status gdn_prefill_affine_ws(const gdn_shape* shape, const void* k, const void* v, const float* g,
+                                 const float* beta, const int32_t* cu_seqlens, float* transition, float* offset,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_impl("prefill_affine_ws", kAffine, shape,
+                        affine_call(k, v, g, beta, cu_seqlens, transition, offset), stream, kCallerWs, workspace,
+                        workspace_bytes);
 }
 
 }  // extern "C"

@@ -46,14 +46,14 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_status {
     GDN_SUCCESS = 0,
     GDN_ERROR_INVALID_VALUE = 1,  /* malformed argument (NULL, negative size, misaligned ...) */
     GDN_ERROR_NOT_SUPPORTED = 2,  /* well-formed shape the library has no kernel for */
     GDN_ERROR_LAUNCH = 3,         /* a HIP launch or enqueue failed */
-    GDN_ERROR_OUT_OF_MEMORY = 4   /* the stream-ordered workspace could not be allocated */
+    GDN_ERROR_OUT_OF_MEMORY = 4   /* the pool workspace could not be allocated (non-_ws forms) */
 } gdn_status;
 
 typedef enum gdn_dtype {
@@ -79,6 +79,43 @@ typedef struct gdn_shape {
 } gdn_shape;
 
 /*
+ * Workspace.  Every prefill entry point needs device scratch memory: per
+ * 64-token chunk and value head the chunk's triangular factor and gates
+ * (about 6 KB for bf16, 13 KB for fp32), and, when a sequence is cut into
+ * parts of L chunks because there are fewer (sequence, head) pairs than
+ * compute units, per part and value head its transition, offset and start
+ * state ((dk + 2 dv) * dk * 4 bytes).  Each entry point comes in two forms:
+ *   gdn_prefill*_ws  take a caller-owned workspace and allocate nothing;
+ *   gdn_prefill*     take it from the current device's default stream-ordered
+ *                    memory pool (hipMallocAsync / hipFreeAsync on `stream`,
+ *                    GDN_ERROR_OUT_OF_MEMORY if that fails).  The pool's
+ *                    settings are the caller's: the library changes none.
+ * Both forms run the same kernels and give bit-identical results.  The
+ * library keeps no state between calls.
+ *
+ * A caller workspace is DEVICE memory, 256-byte aligned, not NULL and
+ * overlapping no other argument.  It needs no initialisation; its contents are
+ * undefined afterwards.  It is in use until the call's work on `stream`
+ * completes, so calls that share one must be ordered (for instance, on one
+ * stream).  workspace_bytes must be at least what gdn_prefill_workspace_size
+ * returns for the same shape, flags and device, else GDN_ERROR_INVALID_VALUE
+ * (nothing enqueued).
+ */
+#define GDN_WS_PACKED 1u   /* the call passes cu_seqlens                        */
+#define GDN_WS_RAW 2u      /* for gdn_prefill_raw_ws                             */
+#define GDN_WS_AFFINE 4u   /* for gdn_prefill_affine_ws (excludes GDN_WS_RAW)    */
+
+/*
+ * gdn_prefill_workspace_size -- bytes of workspace a prefill call with this
+ * shape needs on the current device (the part length L depends on the
+ * device's compute-unit count).  flags: GDN_WS_PACKED if the call passes
+ * cu_seqlens, plus GDN_WS_RAW or GDN_WS_AFFINE for those entry points
+ * (gdn_prefill_ws and gdn_prefill_snapshots_ws need neither).  Writes 0 when
+ * num_seqs is 0.  Host-only: launches nothing and allocates nothing.
+ */
+gdn_status gdn_prefill_workspace_size(const gdn_shape* shape, uint32_t flags, size_t* bytes);
+
+/*
  * gdn_prefill -- run the recurrence over whole sequences (packed varlen).
  *
  * Computes o_t for every token of every sequence and, if final_state is not
@@ -95,43 +132,15 @@ typedef struct gdn_shape {
  *             are allowed: their final state equals their initial state.
  * out         [num_tokens, Hv, dv] in `dtype`.
  * final_state [N, Hv, dv, dk] fp32 or NULL.
- *
- * Memory: a stream-ordered workspace is taken from HIP's default memory pool
- * on `stream` and returned to it before the call's work completes
- * (GDN_ERROR_OUT_OF_MEMORY if that fails).  Its size is about
- * (num_tokens / 64 + N) * Hv * (6 KB for bf16, 13 KB for fp32) (the chunks'
- * triangular factors and gates), plus, when a sequence is cut into
- * parts of L chunks because there are fewer (sequence, head) pairs than
- * compute units, (num_tokens / (64 L) + N) * Hv * (dk + 2 dv) * dk * 4 bytes
- * (each part's transition, offset and start state).
+ * Workspace from the default pool (see above).
  */
 gdn_status gdn_prefill(const gdn_shape* shape, const void* q, const void* k, const void* v,
                        const float* g, const float* beta, const float* init_state,
                        const int32_t* cu_seqlens, void* out, float* final_state,
                        void* stream);
 
-/*
- * gdn_prefill_workspace_size -- the device workspace, in bytes, that
- * gdn_prefill_ws needs for `shape` on the current device (the part length L
- * above depends on the device's compute-unit count).  `packed` is nonzero
- * when the call will pass cu_seqlens.  Writes 0 when num_seqs is 0.
- * Host-only: launches nothing and allocates nothing.
- */
-gdn_status gdn_prefill_workspace_size(const gdn_shape* shape, int32_t packed, size_t* bytes);
-
-/*
- * gdn_prefill_ws -- gdn_prefill with a caller-owned workspace; allocates
- * nothing (for callers that manage device memory themselves).  Same
- * recurrence and outputs as gdn_prefill.
- *
- * workspace        DEVICE memory, 256-byte aligned, not NULL, overlapping no
- *                  other argument.  It needs no initialisation; its contents
- *                  are undefined afterwards.  It is in use until the call's
- *                  work on `stream` completes, so calls that share one must
- *                  be ordered (for instance, on one stream).
- * workspace_bytes  at least gdn_prefill_workspace_size(shape, cu_seqlens !=
- *                  NULL) on this device, else GDN_ERROR_INVALID_VALUE.
- */
+/* gdn_prefill_ws -- gdn_prefill on a caller-owned workspace (flags
+ * GDN_WS_PACKED if cu_seqlens is given); allocates nothing. */
 gdn_status gdn_prefill_ws(const gdn_shape* shape, const void* q, const void* k, const void* v,
                           const float* g, const float* beta, const float* init_state,
                           const int32_t* cu_seqlens, void* out, float* final_state,
@@ -139,23 +148,29 @@ gdn_status gdn_prefill_ws(const gdn_shape* shape, const void* q, const void* k, 
 
 /*
  * gdn_prefill_affine -- the state map of each whole sequence.  Over its tokens
- * the recurrence maps any start state S to S M + B: the product of the
- * per-token maps (flozi.net, "Qwen3.8-Flash-Next architecture", "Der Weg eines
- * Tokens durch das Modell", item 1: the layer's state is a fixed-size
- * recurrent state, so a token range acts on it as one affine map).  This is
- * the per-device half of a sequence-sharded prefill: each device summarises
- * its range of tokens, the maps are gathered and composed, and each device
- * reruns gdn_prefill on its range from the composed start state.
+ * the recurrence maps any start state S to S M + B: every token's update is
+ * affine in the state, so their composition is too (a property of the
+ * recurrence itself, which keeps one fixed-size state per head: flozi.net,
+ * "Qwen3.8-Flash-Next architecture", "Der Weg eines Tokens durch das
+ * Modell", item 1).  This is the per-device half of a sequence-sharded
+ * prefill: each device summarises its range of tokens, the maps are gathered
+ * and composed, and each device reruns gdn_prefill on its range from the
+ * composed start state.
  *
  * k, v, g, beta, cu_seqlens as for gdn_prefill (q is not needed).
  * transition  [N, Hv, dk, dk] fp32, M (the identity for an empty sequence).
  * offset      [N, Hv, dv, dk] fp32, B (the state reached from zero).
- * The two must not overlap.  Memory: a stream-ordered workspace from HIP's
- * default pool, as for gdn_prefill (with the part maps for every sequence).
+ * The two must not overlap.  Workspace from the default pool (see above).
  */
 gdn_status gdn_prefill_affine(const gdn_shape* shape, const void* k, const void* v, const float* g,
                               const float* beta, const int32_t* cu_seqlens, float* transition, float* offset,
                               void* stream);
+
+/* gdn_prefill_affine_ws -- gdn_prefill_affine on a caller-owned workspace
+ * (flags GDN_WS_AFFINE, plus GDN_WS_PACKED if cu_seqlens is given). */
+gdn_status gdn_prefill_affine_ws(const gdn_shape* shape, const void* k, const void* v, const float* g,
+                                 const float* beta, const int32_t* cu_seqlens, float* transition, float* offset,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * gdn_prefill_snapshots -- gdn_prefill that also writes the state at every
@@ -170,12 +185,20 @@ gdn_status gdn_prefill_affine(const gdn_shape* shape, const void* k, const void*
  *                  (cu[n] = n * len without cu_seqlens).  floor(num_tokens / P)
  *                  + N slots always suffice; slots that hold no snapshot are
  *                  left as they were.  It must not overlap any other argument.
- * Everything else is as for gdn_prefill.
+ * Everything else is as for gdn_prefill (workspace from the default pool).
  */
 gdn_status gdn_prefill_snapshots(const gdn_shape* shape, const void* q, const void* k, const void* v,
                                  const float* g, const float* beta, const float* init_state,
                                  const int32_t* cu_seqlens, void* out, float* final_state, int32_t snapshot_chunks,
                                  float* snapshots, void* stream);
+
+/* gdn_prefill_snapshots_ws -- gdn_prefill_snapshots on a caller-owned
+ * workspace (flags as for gdn_prefill_ws); allocates nothing. */
+gdn_status gdn_prefill_snapshots_ws(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                                    const float* g, const float* beta, const float* init_state,
+                                    const int32_t* cu_seqlens, void* out, float* final_state,
+                                    int32_t snapshot_chunks, float* snapshots, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /*
  * gdn_decode_step -- advance N sequences by one token each.
@@ -250,8 +273,9 @@ gdn_status gdn_decode_slots(const gdn_shape* shape, int32_t tokens_per_seq, cons
  * das Modell", item 1 -- but print none of these formulas; they are the usual
  * forms and give the input distributions the rest of this library is
  * measured on.)  All other arguments, layouts and rules are those of
- * gdn_prefill and gdn_decode_tokens; gdn_prefill_raw's pool workspace is
- * larger by (num_tokens / 64 + N) * Hv * 256 bytes (1 / |k| per token).
+ * gdn_prefill and gdn_decode_tokens; gdn_prefill_raw's workspace is larger by
+ * (num_tokens / 64 + N) * Hv * 256 bytes (1 / |k| per token): size it with
+ * GDN_WS_RAW.
  */
 gdn_status gdn_prefill_raw(const gdn_shape* shape, const void* q, const void* k, const void* v, const float* a_gate,
                            const float* b_beta, const float* init_state, const int32_t* cu_seqlens, void* out,
@@ -259,6 +283,12 @@ gdn_status gdn_prefill_raw(const gdn_shape* shape, const void* q, const void* k,
 gdn_status gdn_decode_tokens_raw(const gdn_shape* shape, int32_t tokens_per_seq, const void* q, const void* k,
                                  const void* v, const float* a_gate, const float* b_beta, float* state, void* out,
                                  float* token_states, void* stream);
+/* gdn_prefill_raw_ws -- gdn_prefill_raw on a caller-owned workspace (flags
+ * GDN_WS_RAW, plus GDN_WS_PACKED if cu_seqlens is given); allocates nothing. */
+gdn_status gdn_prefill_raw_ws(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                              const float* a_gate, const float* b_beta, const float* init_state,
+                              const int32_t* cu_seqlens, void* out, float* final_state, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /* Static English text for a status code (never NULL). */
 const char* gdn_status_string(gdn_status status);

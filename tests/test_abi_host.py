@@ -28,9 +28,9 @@ def _declared_functions():
 def test_header_declares_the_abi():
     assert _declared_functions() == ["gdn_abi_version", "gdn_decode_slots", "gdn_decode_step", "gdn_decode_tokens",
                                      "gdn_decode_tokens_raw", "gdn_last_error", "gdn_prefill", "gdn_prefill_affine",
-                                     "gdn_prefill_raw",
-                                     "gdn_prefill_snapshots", "gdn_prefill_workspace_size", "gdn_prefill_ws",
-                                     "gdn_status_string"]
+                                     "gdn_prefill_affine_ws", "gdn_prefill_raw", "gdn_prefill_raw_ws",
+                                     "gdn_prefill_snapshots", "gdn_prefill_snapshots_ws",
+                                     "gdn_prefill_workspace_size", "gdn_prefill_ws", "gdn_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -48,7 +48,7 @@ def test_library_exports_only_the_abi():
 
 
 def test_abi_version_and_status_strings():
-    assert B.gdn_abi_version() == 1
+    assert B.gdn_abi_version() == 2
     seen = set()
     for st in range(5):
         s = B.status_string(st)
@@ -220,28 +220,6 @@ def test_raw_entry_points_apply_the_same_argument_checks():
     assert rc == B.GDN_ERROR_INVALID_VALUE and "g is NULL" in L.gdn_last_error().decode()
 
 
-def _prefill_ws(shape, ws, nbytes):
-    c = ctypes.c_void_p
-    L = _lib()
-    rc = L.gdn_prefill_ws(ctypes.byref(shape), c(FAKE), c(FAKE), c(FAKE), c(FAKE), c(FAKE), None, None, c(FAKE),
-                          None, c(ws) if ws else None, nbytes, None)
-    return rc, L.gdn_last_error().decode()
-
-
-@pytest.mark.parametrize("ws,status,msg", [
-    (None, B.GDN_ERROR_INVALID_VALUE, "workspace is NULL"),
-    (FAKE + 16, B.GDN_ERROR_INVALID_VALUE, "aligned"),
-])
-def test_prefill_ws_rejects_bad_workspace(ws, status, msg):
-    rc, err = _prefill_ws(_shape(), ws, 1 << 20)
-    assert rc == status and msg in err, (rc, err)
-
-
-def test_prefill_ws_applies_the_prefill_checks():
-    rc, err = _prefill_ws(_shape(num_qk_heads=3, num_v_heads=4), FAKE, 1 << 20)
-    assert rc == B.GDN_ERROR_INVALID_VALUE and "multiple" in err
-
-
 def test_prefill_workspace_size_host_paths():
     L = _lib()
     n = ctypes.c_size_t(123)
@@ -250,8 +228,73 @@ def test_prefill_workspace_size_host_paths():
     rc = L.gdn_prefill_workspace_size(ctypes.byref(_shape(num_seqs=3, num_tokens=64)), 0, ctypes.byref(n))
     assert rc == B.GDN_ERROR_INVALID_VALUE and "not packed" in L.gdn_last_error().decode()
     n.value = 123
-    rc = L.gdn_prefill_workspace_size(ctypes.byref(_shape(num_seqs=0, num_tokens=0)), 1, ctypes.byref(n))
+    rc = L.gdn_prefill_workspace_size(ctypes.byref(_shape(num_seqs=0, num_tokens=0)), B.GDN_WS_PACKED,
+                                      ctypes.byref(n))
     assert rc == B.GDN_SUCCESS and n.value == 0
+
+
+@pytest.mark.parametrize("flags,msg", [(8, "unknown workspace flags"), (1 << 31, "unknown workspace flags"),
+                                       (B.GDN_WS_RAW | B.GDN_WS_AFFINE, "exclude each other")])
+def test_prefill_workspace_size_rejects_bad_flags(flags, msg):
+    L = _lib()
+    n = ctypes.c_size_t(123)
+    assert L.gdn_prefill_workspace_size(ctypes.byref(_shape()), flags, ctypes.byref(n)) == B.GDN_ERROR_INVALID_VALUE
+    assert msg in L.gdn_last_error().decode() and n.value == 0
+
+
+def _ws_call(name, shape, ws, nbytes, **kw):
+    """One of the caller-workspace prefill forms with host-side stand-in pointers."""
+    c = ctypes.c_void_p
+    L = _lib()
+    w = (c(ws) if ws else None, nbytes, None)
+    if name == "gdn_prefill_affine_ws":
+        rc = L.gdn_prefill_affine_ws(ctypes.byref(shape), c(FAKE), c(FAKE), c(FAKE), c(FAKE), None,
+                                     c(kw.get("m", FAKE)), c(kw.get("b", FAKE + (1 << 22))), *w)
+    elif name == "gdn_prefill_snapshots_ws":
+        rc = L.gdn_prefill_snapshots_ws(ctypes.byref(shape), c(FAKE), c(FAKE), c(FAKE), c(FAKE), c(FAKE), None, None,
+                                        c(FAKE), None, kw.get("chunks", 2), c(kw.get("snaps", FAKE)), *w)
+    else:
+        rc = getattr(L, name)(ctypes.byref(shape), c(FAKE), c(FAKE), c(FAKE), c(FAKE), c(FAKE), None, None, c(FAKE),
+                              None, *w)
+    return rc, L.gdn_last_error().decode()
+
+
+WS_FORMS = ["gdn_prefill_ws", "gdn_prefill_raw_ws", "gdn_prefill_snapshots_ws", "gdn_prefill_affine_ws"]
+
+
+@pytest.mark.parametrize("name", WS_FORMS)
+@pytest.mark.parametrize("ws,status,msg", [
+    (None, B.GDN_ERROR_INVALID_VALUE, "workspace is NULL"),
+    (FAKE + 16, B.GDN_ERROR_INVALID_VALUE, "aligned"),
+])
+def test_prefill_ws_forms_reject_bad_workspace(name, ws, status, msg):
+    rc, err = _ws_call(name, _shape(), ws, 1 << 20)
+    assert rc == status and msg in err, (name, rc, err)
+
+
+@pytest.mark.parametrize("name", WS_FORMS)
+def test_prefill_ws_forms_apply_the_prefill_checks(name):
+    rc, err = _ws_call(name, _shape(num_qk_heads=3, num_v_heads=4), FAKE, 1 << 20)
+    assert rc == B.GDN_ERROR_INVALID_VALUE and "multiple" in err
+    rc, err = _ws_call(name, _shape(num_seqs=0, num_tokens=0), FAKE, 0)
+    assert rc == B.GDN_SUCCESS and err == ""
+
+
+def test_prefill_ws_forms_check_their_own_arguments():
+    rc, err = _ws_call("gdn_prefill_snapshots_ws", _shape(), FAKE, 1 << 20, snaps=0)
+    assert rc == B.GDN_ERROR_INVALID_VALUE and "snapshots is NULL" in err
+    rc, err = _ws_call("gdn_prefill_snapshots_ws", _shape(), FAKE, 1 << 20, chunks=0)
+    assert rc == B.GDN_ERROR_INVALID_VALUE and "snapshot_chunks must be positive" in err
+    rc, err = _ws_call("gdn_prefill_affine_ws", _shape(), FAKE, 1 << 20, b=FAKE + 1024)
+    assert rc == B.GDN_ERROR_INVALID_VALUE and "overlap" in err
+    rc, err = _ws_call("gdn_prefill_affine_ws", _shape(), FAKE, 1 << 20, m=0)
+    assert rc == B.GDN_ERROR_INVALID_VALUE and "transition is NULL" in err
+
+
+def test_library_changes_no_pool_setting():
+    """The library never sets an attribute of a memory pool (a process-wide setting)."""
+    src = open(os.path.join(ROOT, "gated_deltanet_linear_rule_amd", "csrc", "gdn_api.cpp")).read()
+    assert "hipMemPoolSetAttribute" not in src and "hipDeviceSetMemPool" not in src
 
 
 def _affine(shape, m, b):

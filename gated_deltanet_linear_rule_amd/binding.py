@@ -26,6 +26,7 @@ GDN_DTYPE_BF16 = 1
 GDN_WS_PACKED = 1
 GDN_WS_RAW = 2
 GDN_WS_AFFINE = 4
+GDN_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class GdnShape(ctypes.Structure):
@@ -73,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_prefill_workspace_size.restype = ctypes.c_int
         L.gdn_prefill_ws.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.gdn_prefill_ws.restype = ctypes.c_int
+        L.gdn_prefill_static.argtypes = L.gdn_prefill.argtypes
+        L.gdn_prefill_static.restype = ctypes.c_int
         L.gdn_prefill_affine.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P]
         L.gdn_prefill_affine.restype = ctypes.c_int
         L.gdn_prefill_affine_ws.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
@@ -171,7 +174,8 @@ def _workspace(workspace, use_pool, q, v, cu_seqlens, N, raw=False, affine=False
 
 
 def gdn_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, out=None, final_state=None,
-                stream=None, num_seqs=None, return_final_state=True, raw=False, workspace=None, use_pool=False):
+                stream=None, num_seqs=None, return_final_state=True, raw=False, workspace=None, use_pool=False,
+                use_static=False):
     """Chunked GDN prefill over packed sequences.
 
     q, k [T, Hqk, dk]; v [T, Hv, dv] (bf16 or fp32, same dtype); g, beta [T, Hv]
@@ -181,7 +185,8 @@ def gdn_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, out=None, fi
     raw=True calls the raw-projection form: q, k unnormalised, g and beta are the logits a, b.
     workspace: a contiguous GPU tensor of at least gdn_prefill_workspace_size bytes (allocated from
     torch for this call if None); the library's *_ws entry point runs on it.  use_pool=True calls the
-    form that takes its workspace from HIP's default stream-ordered pool instead.
+    form that takes its workspace from HIP's default stream-ordered pool instead, use_static=True the
+    one that runs on the library's static scratch (gdn_prefill_static; not with raw).
     """
     T, hqk, dk = q.shape
     hv, dv = v.shape[1], v.shape[2]
@@ -206,6 +211,11 @@ def gdn_prefill(q, k, v, g, beta, init_state=None, cu_seqlens=None, out=None, fi
     shape = GdnShape(N, T, hqk, hv, dk, dv, io)
     args = (ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(init_state), _ptr(cu_seqlens),
             _ptr(out), _ptr(final_state))
+    if use_static:
+        if raw or use_pool or workspace is not None:
+            raise ValueError("use_static=True takes no workspace and has no raw-projection form")
+        _raise(lib().gdn_prefill_static(*args, _stream(stream)), "gdn_prefill_static")
+        return out, final_state
     ws = _workspace(workspace, use_pool, q, v, cu_seqlens, N, raw=raw)
     name = "gdn_prefill" + ("_raw" if raw else "") + ("" if ws is None else "_ws")
     fn = getattr(lib(), name)

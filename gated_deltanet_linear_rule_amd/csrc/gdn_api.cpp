@@ -12,6 +12,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 
 #include "gdn.h"
 #include "gdn_internal.h"
@@ -249,10 +250,46 @@ struct PrefillCall {
     float *transition, *offset;   // affine map
 };
 
+// Static scratch for gdn_prefill_static: one array per device, allocated when
+// the library's code object is loaded onto that device and held until the
+// process ends.  In host code `scratch` is only a host-side stand-in for the
+// symbol; its device address comes from hipGetSymbolAddress, looked up once
+// per device (with that device current) and kept in scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[GDN_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the first
+// call on that device), or NULL with the error recorded.
+void* scratch_address(gdn_status& st) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        st = fail(GDN_ERROR_LAUNCH, "prefill_static: no usable current device (%d)", dev);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            st = fail(GDN_ERROR_LAUNCH, "prefill_static: scratch address lookup on device %d: %s", dev,
+                      hipGetErrorString(e));
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
 // Where a prefill call's workspace comes from: the current device's default
 // stream-ordered pool (hipMallocAsync / hipFreeAsync on the call's stream; the
-// pool's settings are left as the caller set them) or the caller.
-enum WsSource { kPoolWs, kCallerWs };
+// pool's settings are left as the caller set them), the caller, or the static
+// scratch array.
+enum WsSource { kPoolWs, kCallerWs, kStaticWs };
 
 // Validates a prefill call, lays out its workspace and enqueues its kernels.
 gdn_status prefill_impl(const char* who, PrefillKind kind, const gdn_shape* shape, const PrefillCall& c, void* stream,
@@ -322,6 +359,15 @@ gdn_status prefill_impl(const char* who, PrefillKind kind, const gdn_shape* shap
         if (workspace_bytes < (size_t)total)
             return fail(GDN_ERROR_INVALID_VALUE, "workspace of %zu bytes, this call needs %lld", workspace_bytes,
                         (long long)total);
+    } else if (src == kStaticWs) {
+        if ((size_t)total > (size_t)GDN_STATIC_SCRATCH_BYTES)
+            return fail(GDN_ERROR_NOT_SUPPORTED,
+                        "%s: this call needs %lld bytes of scratch, the static scratch holds %zu (use "
+                        "gdn_prefill_ws with a caller workspace)", who, (long long)total,
+                        (size_t)GDN_STATIC_SCRATCH_BYTES);
+        gdn_status sst = GDN_SUCCESS;
+        ws = scratch_address(sst);
+        if (!ws) return sst;
     } else if (hipMallocAsync(&ws, (size_t)total, st) != hipSuccess || !ws) {
         (void)hipGetLastError();
         return fail(GDN_ERROR_OUT_OF_MEMORY, "%s workspace of %lld bytes", who, (long long)total);
@@ -401,6 +447,13 @@ gdn_status gdn_prefill_ws(const gdn_shape* shape, const void* q, const void* k, 
     return prefill_impl("prefill_ws", kPlain, shape,
                         call_of(q, k, v, g, beta, init_state, cu_seqlens, out, final_state), stream, kCallerWs, workspace,
                         workspace_bytes);
+}
+
+gdn_status gdn_prefill_static(const gdn_shape* shape, const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, const float* init_state, const int32_t* cu_seqlens, void* out,
+                              float* final_state, void* stream) {
+    return prefill_impl("prefill_static", kPlain, shape,
+                        call_of(q, k, v, g, beta, init_state, cu_seqlens, out, final_state), stream, kStaticWs);
 }
 
 gdn_status gdn_prefill_raw(const gdn_shape* shape, const void* q, const void* k, const void* v, const float* a_gate,

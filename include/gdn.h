@@ -90,8 +90,9 @@ typedef struct gdn_shape {
  *                    memory pool (hipMallocAsync / hipFreeAsync on `stream`,
  *                    GDN_ERROR_OUT_OF_MEMORY if that fails).  The pool's
  *                    settings are the caller's: the library changes none.
- * Both forms run the same kernels and give bit-identical results.  The
- * library keeps no state between calls.
+ * Both forms run the same kernels and give bit-identical results.  Apart from
+ * the device address of gdn_prefill_static's scratch array, which it looks up
+ * once per device, the library keeps no state between calls.
  *
  * A caller workspace is DEVICE memory, 256-byte aligned, not NULL and
  * overlapping no other argument.  It needs no initialisation; its contents are
@@ -145,6 +146,29 @@ gdn_status gdn_prefill_ws(const gdn_shape* shape, const void* q, const void* k, 
                           const float* g, const float* beta, const float* init_state,
                           const int32_t* cu_seqlens, void* out, float* final_state,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_prefill_static -- gdn_prefill for callers that cannot allocate device
+ * memory at all (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc) and have no workspace to pass: it runs on a static
+ * scratch array of GDN_STATIC_SCRATCH_BYTES that the library holds on every
+ * device it runs on, from the load of its code onto that device until the
+ * process ends.  It calls no allocator.  Same arguments, kernels and results
+ * as gdn_prefill_ws.
+ *
+ * A shape whose workspace (gdn_prefill_workspace_size) exceeds
+ * GDN_STATIC_SCRATCH_BYTES is rejected with GDN_ERROR_NOT_SUPPORTED before
+ * anything is enqueued; on a 256-CU device, at 16 value heads and d = 128 in
+ * bf16, that admits one sequence of up to 8,192 tokens.
+ * Every call on one device shares that device's array and leaves its contents
+ * behind (the kernels need none of them): calls whose work may overlap on one
+ * device, on different streams or from different threads, race on the array
+ * and must be ordered by the caller.
+ */
+#define GDN_STATIC_SCRATCH_BYTES (64u << 20)
+gdn_status gdn_prefill_static(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, const float* init_state,
+                              const int32_t* cu_seqlens, void* out, float* final_state, void* stream);
 
 /*
  * gdn_prefill_affine -- the state map of each whole sequence.  Over its tokens

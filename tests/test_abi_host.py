@@ -29,7 +29,7 @@ def test_header_declares_the_abi():
     assert _declared_functions() == ["gdn_abi_version", "gdn_decode_slots", "gdn_decode_step", "gdn_decode_tokens",
                                      "gdn_decode_tokens_raw", "gdn_last_error", "gdn_prefill", "gdn_prefill_affine",
                                      "gdn_prefill_affine_ws", "gdn_prefill_raw", "gdn_prefill_raw_ws",
-                                     "gdn_prefill_snapshots", "gdn_prefill_snapshots_ws",
+                                     "gdn_prefill_snapshots", "gdn_prefill_snapshots_ws", "gdn_prefill_static",
                                      "gdn_prefill_workspace_size", "gdn_prefill_ws", "gdn_status_string"]
 
 
@@ -289,6 +289,20 @@ def test_prefill_ws_forms_check_their_own_arguments():
     assert rc == B.GDN_ERROR_INVALID_VALUE and "overlap" in err
     rc, err = _ws_call("gdn_prefill_affine_ws", _shape(), FAKE, 1 << 20, m=0)
     assert rc == B.GDN_ERROR_INVALID_VALUE and "transition is NULL" in err
+
+
+def test_prefill_static_applies_the_prefill_checks_before_any_hip_call():
+    c = ctypes.c_void_p
+    L = _lib()
+    rc = L.gdn_prefill_static(ctypes.byref(_shape(num_qk_heads=3, num_v_heads=4)), c(FAKE), c(FAKE), c(FAKE),
+                              c(FAKE), c(FAKE), None, None, c(FAKE), None, None)
+    assert rc == B.GDN_ERROR_INVALID_VALUE and "multiple" in L.gdn_last_error().decode()
+    rc = L.gdn_prefill_static(ctypes.byref(_shape()), c(FAKE), c(FAKE + 2), c(FAKE), c(FAKE), c(FAKE), None, None,
+                              c(FAKE), None, None)
+    assert rc == B.GDN_ERROR_INVALID_VALUE and "aligned" in L.gdn_last_error().decode()
+    rc = L.gdn_prefill_static(ctypes.byref(_shape(num_seqs=0, num_tokens=0)), None, None, None, None, None, None,
+                              None, None, None, None)
+    assert rc == B.GDN_SUCCESS
 
 
 def test_library_changes_no_pool_setting():

@@ -44,9 +44,10 @@ struct PrefillArgs {
     int64_t part_chunks;       // L: chunks per part
     int64_t num_part_slots;    // part slots: ceil(num_tokens / (64 L)) + num_seqs
     // Workspace.  Per (chunk slot, value head), written by the prep kernel:
-    void* ws_t;                // T~ = (I + A)^{-1} diag(beta) as operand fragments (5 KB bf16, 12 KB fp32)
-    double* ws_g;              // 1 KB gate record: 64 log2-scaled cumulative gates (fp64),
-                               // then 64 gamma and 64 D (fp32)
+    void* ws_t;                // T~ = (I + A)^{-1} diag(beta) without its diagonal, as operand
+                               // fragments (5 KB bf16, 12 KB fp32)
+    double* ws_g;              // 1.25 KB gate record: 64 log2-scaled cumulative gates (fp64),
+                               // then 64 gamma, 64 D and 64 beta (fp32)
     float* ws_ik;              // raw projections only: 64 values 1 / |k_t| (256 B)
     // Per (part slot, value head), fp32 row-major; NULL when no sequence has
     // more than one part:
@@ -75,7 +76,7 @@ struct PrefillWorkspace {
         const int64_t blocks = num_slots * hv, pblocks = split ? num_part_slots * hv : 0;
         t = 0;
         g = t + up(blocks * (elem_size == 2 ? 5 : 12) * 1024);   // T~: 5 KB bf16, 12 KB fp32
-        ik = g + up(blocks * 1024);
+        ik = g + up(blocks * 1280);                               // gate record: 1.25 KB
         m = ik + (raw ? up(blocks * 256) : 0);
         b = m + up(pblocks * dk * dk * 4);
         s = b + up(pblocks * dv * dk * 4);

@@ -54,8 +54,8 @@ namespace {
 constexpr int kTriFrags = 6;       // lower operand fragments of a 64 x 64 matrix
 constexpr int kLinkThreads = 256;
 // Gate record of one (chunk, value head): G2_t = log2-scaled cumulative gate
-// (fp64), then gamma_t = 2^{G2_t} and D_t = 2^{G2_63 - G2_t} (fp32).
-constexpr int kGateRecord = kChunk * 8 + 2 * kChunk * 4;
+// (fp64), then gamma_t = 2^{G2_t}, D_t = 2^{G2_63 - G2_t} and beta_t (fp32).
+constexpr int kGateRecord = kChunk * 8 + 3 * kChunk * 4;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -360,16 +360,26 @@ __global__ __launch_bounds__(kWave * kPrepWaves) void gdn_prep_kernel(PrefillArg
         }
     }
 
-    // ---- T~ = T diag(beta) as operand fragments, and the gate record
+    // ---- T~ = T diag(beta) as operand fragments, with its diagonal (beta_t:
+    // T is unit lower triangular) left out: the chunk kernels add beta_t r_t
+    // to u_t in fp32, so the largest entries are never rounded to the operand
+    // type.  Then the gate record.
     f32x4 bc[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) bc[c] = *reinterpret_cast<const f32x4*>(&sm.B[16 * c + 4 * gq]);
     OP* const Tw = static_cast<OP*>(a.ws_t) + blk * (Units<OP>::TU * 1024 / sizeof(OP));
+    auto off_diag = [&](f32x4 x) {   // lane (r, gq) holds entries (r, 4 gq + i) of a diagonal tile
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = r == 4 * gq + i ? 0.f : x[i];
+        return x;
+    };
 #pragma unroll
     for (int f = 0; f < kTriFrags; ++f) {
         const int tb = f < 2 ? f : 2 + ((f - 2) >> 1), kk = f < 2 ? 0 : ((f - 2) & 1);
-        const f32x4 lo = ta[tb][2 * kk] * bc[2 * kk];
-        const f32x4 hi = 2 * kk + 1 <= tb ? ta[tb][2 * kk + 1] * bc[2 * kk + 1] : zero4();
+        f32x4 lo = ta[tb][2 * kk] * bc[2 * kk];
+        f32x4 hi = 2 * kk + 1 <= tb ? ta[tb][2 * kk + 1] * bc[2 * kk + 1] : zero4();
+        if (2 * kk == tb) lo = off_diag(lo);
+        if (2 * kk + 1 == tb) hi = off_diag(hi);
         if constexpr (FU == 1) {
             if (f == 0 || f == 3) {   // the upper half is zero: only the lower is stored
                 typename Ops::quad q;
@@ -391,6 +401,7 @@ __global__ __launch_bounds__(kWave * kPrepWaves) void gdn_prep_kernel(PrefillArg
     ws_store(rec + l, G);
     ws_store(reinterpret_cast<float*>(rec + kChunk) + l, fast_exp2((float)G) * ikl);
     ws_store(reinterpret_cast<float*>(rec + kChunk) + kChunk + l, fast_exp2((float)(Gl - G)) * ikl);
+    ws_store(reinterpret_cast<float*>(rec + kChunk) + 2 * kChunk + l, bl);
     // and 1 / |k_t| itself, for the output kernel's intra-chunk products
     if constexpr (RAW) ws_store(a.ws_ik + blk * kChunk + l, ikl);
 }
@@ -562,9 +573,11 @@ struct ChunkBuf {
     alignas(16) OP V[kChunk * DV];
     alignas(16) OP Q[OUT ? kChunk * DK : 8];
     alignas(16) OP T[kTriFrags * 64 * 8];   // T~ fragments
-    alignas(16) double G2[kChunk];          // gate record: G2, gamma, D
+    alignas(16) double G2[kChunk];          // gate record: G2, gamma, D, beta
     alignas(16) float gam[kChunk];
     alignas(16) float dec[kChunk];
+    alignas(16) float bet[kChunk];
+    float gpad[(2048 - kGateRecord) / 4];   // the gate record's second 1 KB load writes up to here
     alignas(16) float IK[IKB ? 256 : 4];
 };
 
@@ -626,19 +639,65 @@ __device__ __forceinline__ void sched_fence() {
     if constexpr (ON) __builtin_amdgcn_sched_barrier(0);
 }
 
+// Lane move inside groups of four lanes (DPP quad permutation CTRL).
+template <int CTRL>
+__device__ __forceinline__ float quad_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// 4 x 4 transpose across the four lanes of a group: lane a's element i becomes
+// lane i's element a.  Two exchange steps, with lanes a ^ 1 (elements whose
+// index differs from a in bit 0) and a ^ 2 (bit 1).
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 x) {
+    const int a = lane_id() & 3;
+    f32x4 p, m;
+    p[0] = quad_mov<0xB1>(x[1]); p[1] = quad_mov<0xB1>(x[0]); p[2] = quad_mov<0xB1>(x[3]); p[3] = quad_mov<0xB1>(x[2]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m[i] = ((i ^ a) & 1) ? p[i] : x[i];
+    p[0] = quad_mov<0x4E>(m[2]); p[1] = quad_mov<0x4E>(m[3]); p[2] = quad_mov<0x4E>(m[0]); p[3] = quad_mov<0x4E>(m[1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = ((i ^ a) & 2) ? p[i] : m[i];
+    return x;
+}
+
+template <int CTRL>
+__device__ __forceinline__ unsigned quad_mov_u(unsigned x) {
+    return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+// The same transpose after rounding to bf16: lane a packs its four values as
+// (x0, x1), (x2, x3) and ends with the four lanes' element a, as bf16x4.
+// Step 1 swaps 16-bit halves with lane a ^ 1 (v_perm with the lane-parity
+// selector sel: even lanes keep their low halves, odd lanes their high
+// halves), step 2 swaps whole dwords with lane a ^ 2.
+__device__ __forceinline__ bf16x4 quad_transpose_bf16(f32x4 x, unsigned sel) {
+    const int a = lane_id() & 3;
+    const bf16x2 p0 = {(__bf16)x[0], (__bf16)x[1]}, p1 = {(__bf16)x[2], (__bf16)x[3]};
+    const unsigned d0 = __builtin_bit_cast(unsigned, p0), d1 = __builtin_bit_cast(unsigned, p1);
+    const unsigned e0 = __builtin_amdgcn_perm(d0, quad_mov_u<0xB1>(d0), sel);
+    const unsigned e1 = __builtin_amdgcn_perm(d1, quad_mov_u<0xB1>(d1), sel);
+    const unsigned q0 = quad_mov_u<0x4E>(e0), q1 = quad_mov_u<0x4E>(e1);
+    const unsigned f0 = (a & 2) ? q1 : e0, f1 = (a & 2) ? e1 : q0;
+    const bf16x2 r0 = __builtin_bit_cast(bf16x2, f0), r1 = __builtin_bit_cast(bf16x2, f1);
+    return bf16x4{r0[0], r0[1], r1[0], r1[1]};
+}
+
 // One chunk for the wave's NR state blocks (rows R0[b] .. R0[b] + 15; block b
 // has a V term when bit b of VMASK is set, else it is a transition block whose
 // V is zero).  ST[b][db] holds block b's S^T tile for d_k columns
 // pi_dk(db, .): lane (n, gq) has S[R0 + n][pi_dk(db, 4 gq + i)].  Packed
-// pairwise, these tiles are at once the B operand of K S^T and the A operand
-// of S Q^T.
-//   Y  = K S^T,  R = V - diag(gamma) Y,  U = T~ R
+// pairwise, these tiles are the B operand of K S^T and of Q S^T.
+//   Y  = K S^T,  R = V - diag(gamma) Y,  U = T~_off R + diag(beta) R
 //   S^T <- gamma_last S^T + K^T diag(D) U
-//   O^T = diag(gamma) (S Q^T) + U^T P^T                          (OUT)
+//   O  = diag(gamma) (Q S^T) + P_off U + diag(P) U                 (OUT)
+// T~_off and P_off are T~ and P without their diagonals; the diagonal terms
+// (beta_t and q_t . k_t, the largest entries) multiply u_t and r_t in fp32,
+// lane by lane, since Y, R, U, Z and O share one tile layout (tokens x state
+// rows).  Only the off-diagonal entries are rounded to the operand type.
 // Output (and fp32): before the barrier in the middle, the wave also writes
-// its share of the chunk's K^T operand fragments (bf16) and P^T tiles (OUT);
-// after it, it reads all of them.  OUT: the O^T tiles go to the row tile `ost`
-// (RowTile layout).
+// its share of the chunk's K^T operand fragments (bf16), P fragments and P
+// diagonal (OUT); after it, it reads all of them.  OUT: the O tiles go to the
+// row tile `ost` (RowTile layout).
 // bf16 summary: `kt` already holds this chunk's K^T fragments (formed during
 // the previous chunk) and there is no barrier.
 // hook(stage) lets the caller place its other work: stage 0 once the wave's
@@ -649,7 +708,7 @@ __device__ __forceinline__ void sched_fence() {
 template <typename OP, int DK, int DV, bool OUT, int NR, int VMASK, int NW, bool RAW, typename F>
 __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT, OUT && RAW>& cb, OP* P, OP* kt, OP* ost,
                                            f32x4 (&ST)[NR][DK / 16], const int (&R0)[NR], int w, F&& hook,
-                                           float* nrm) {
+                                           float* nrm, float* pdg) {
     using Ops = Op<OP>;
     using frag = typename Ops::frag;
     using quad = typename Ops::quad;
@@ -698,14 +757,26 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT, OUT &
                 a0 = a0 * iq * *reinterpret_cast<const f32x4*>(&cb.IK[32 * kk + 4 * gq]);
                 if (two) a1 = a1 * iq * *reinterpret_cast<const f32x4*>(&cb.IK[32 * kk + 16 + 4 * gq]);
             }
+            // the diagonal P_tt goes to pdg in fp32 (applied to u_t in fp32), the
+            // strictly lower entries to the operand fragment
             quad v0, v1;
+            f32x4 x0, x1;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int s0 = 32 * kk + 4 * gq + i, s1 = s0 + 16;
-                const float x0 = fast_exp2((float)(gt - cb.G2[s0])) * a0[i];
-                const float x1 = two ? fast_exp2((float)(gt - cb.G2[s1])) * a1[i] : 0.f;
-                v0[i] = from_f32<OP>(s0 <= t ? x0 : 0.f);
-                v1[i] = from_f32<OP>(s1 <= t ? x1 : 0.f);
+                x0[i] = fast_exp2((float)(gt - cb.G2[s0])) * a0[i];
+                x1[i] = two ? fast_exp2((float)(gt - cb.G2[s1])) * a1[i] : 0.f;
+                v0[i] = from_f32<OP>(s0 < t ? x0[i] : 0.f);
+                v1[i] = from_f32<OP>(s1 < t ? x1[i] : 0.f);
+            }
+            // the diagonal tile of this row tile is token tile 2 kk (x0) or 2 kk + 1
+            // (x1); lane (n, gq) holds its entry (n, n) iff gq = n / 4, as element n % 4.
+            // Every lane stores (no branch): the others into a spare slot.
+            if (2 * kk == tb || 2 * kk + 1 == tb) {   // wave-uniform
+                const f32x4 xd = 2 * kk == tb ? x0 : x1;
+                const int e = n & 3;
+                const float d = e == 0 ? xd[0] : e == 1 ? xd[1] : e == 2 ? xd[2] : xd[3];
+                pdg[gq == (n >> 2) ? t : kChunk + l] = d;
             }
             if constexpr (sizeof(OP) == 2) {
                 *reinterpret_cast<frag*>(P + ((size_t)f * 64 + l) * 8) = Ops::join(v0, v1);
@@ -756,7 +827,7 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT, OUT &
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-                for (int b = 0; b < NR; ++b) Z[b][tb0 + h] = Ops::mma(Sb[b][kk], g[h][kk], Z[b][tb0 + h]);
+                for (int b = 0; b < NR; ++b) Z[b][tb0 + h] = Ops::mma(g[h][kk], Sb[b][kk], Z[b][tb0 + h]);
         }
     };
     load2(g0, cb.K, 0);
@@ -802,18 +873,24 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT, OUT &
         mmZ(g1, 2);
         sched_fence<!OUT>();
     }
-    // R = V - diag(gamma) Y, packed pairwise as the B operand of T~ R; U = T~ R
+    // R = V - diag(gamma) Y (fp32, in Y's registers), packed pairwise as the B
+    // operand of T~_off R; U = T~_off R + diag(beta) R, the product accumulating
+    // onto the fp32 diagonal term
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int b = 0; b < NR; ++b) Y[b][tb] = vt[b][tb] - g4[tb] * Y[b][tb];
     frag Rb[NR][2];
 #pragma unroll
     for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
-        for (int b = 0; b < NR; ++b)
-            Rb[b][tp] = Ops::pack(vt[b][2 * tp] - g4[2 * tp] * Y[b][2 * tp], vt[b][2 * tp + 1] - g4[2 * tp + 1] * Y[b][2 * tp + 1]);
+        for (int b = 0; b < NR; ++b) Rb[b][tp] = Ops::pack(Y[b][2 * tp], Y[b][2 * tp + 1]);
     f32x4 U[NR][4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
+        const f32x4 bt = *reinterpret_cast<const f32x4*>(&cb.bet[16 * tb + 4 * gq]);
 #pragma unroll
-        for (int b = 0; b < NR; ++b) U[b][tb] = Ops::mma(tf[tri_frag(tb, 0)], Rb[b][0], zero4());
+        for (int b = 0; b < NR; ++b) U[b][tb] = Ops::mma(tf[tri_frag(tb, 0)], Rb[b][0], bt * Y[b][tb]);
         if (tb >= 2)
 #pragma unroll
             for (int b = 0; b < NR; ++b) U[b][tb] = Ops::mma(tf[tri_frag(tb, 1)], Rb[b][1], U[b][tb]);
@@ -863,29 +940,40 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT, OUT &
     mmS(k0, 0);
     sched_fence<!OUT>();
     frag pf[kTriFrags];
-    float gt[4];
+    f32x4 gt[4], pd[4];
+    // byte selector of the first exchange step of quad_transpose_bf16 (by lane parity)
+    const unsigned psel = (l & 1) ? 0x07060302u : 0x01000504u;
     if constexpr (OUT) {
 #pragma unroll
         for (int f = 0; f < kTriFrags; ++f) pf[f] = lds_frag(P, f);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-            gt[tb] = RAW ? nrm[16 * tb + n] : cb.gam[16 * tb + n];
+        for (int tb = 0; tb < 4; ++tb) {
+            gt[tb] = *reinterpret_cast<const f32x4*>(RAW ? &nrm[16 * tb + 4 * gq] : &cb.gam[16 * tb + 4 * gq]);
+            pd[tb] = *reinterpret_cast<const f32x4*>(&pdg[16 * tb + 4 * gq]);
+        }
     }
     sched_fence<!OUT>();
     mmS(k1, HD);
     if constexpr (OUT) {
         sched_fence<!OUT>();
-        // O^T tiles (rows x tokens): lane (n, gq) has O[16 tb + n][R0 + 4 gq + i]
+        // O tiles (tokens x rows): lane (n, gq) has O[16 tb + 4 gq + i][R0 + n]; after
+        // the transpose inside each group of four lanes, O[16 tb + 4 gq + (n & 3)][R0 +
+        // 4 (n >> 2) + i], four consecutive columns of one row for the LDS row tile
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
             for (int b = 0; b < NR; ++b) {
-                f32x4 z = Ops::mma(Ua[b][0], pf[tri_frag(tb, 0)], gt[tb] * Z[b][tb]);
-                if (tb >= 2) z = Ops::mma(Ua[b][1], pf[tri_frag(tb, 1)], z);
+                f32x4 o = Ops::mma(pf[tri_frag(tb, 0)], Ua[b][0], gt[tb] * Z[b][tb] + pd[tb] * U[b][tb]);
+                if (tb >= 2) o = Ops::mma(pf[tri_frag(tb, 1)], Ua[b][1], o);
                 quad oq;
+                if constexpr (sizeof(OP) == 2) {
+                    oq = quad_transpose_bf16(o, psel);
+                } else {
+                    o = quad_transpose(o);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) oq[i] = from_f32<OP>(z[i]);
-                *reinterpret_cast<quad*>(ost + RowTile<OP, DV>::elem(16 * tb + n, R0[b] + 4 * gq)) = oq;
+                    for (int i = 0; i < 4; ++i) oq[i] = from_f32<OP>(o[i]);
+                }
+                *reinterpret_cast<quad*>(ost + RowTile<OP, DV>::elem(16 * tb + 4 * gq + (n & 3), R0[b] + 4 * (n >> 2))) = oq;
             }
         }
     }
@@ -893,8 +981,8 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT, OUT &
 
 // OUT = false: summary of parts p < np - 1 (B_p into ws_b, M_p into ws_m).
 // OUT = true: outputs of every part, from ws_s (np > 1) or init_state (np = 1);
-// the last part writes final_state.
-template <typename OP, int DK, int DV, bool OUT, bool RAW>
+// the last part writes final_state; SNAP: also the state snapshots.
+template <typename OP, int DK, int DV, bool OUT, bool RAW, bool SNAP = false>
 __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) void gdn_chunk_kernel(PrefillArgs a) {
     using G = ChunkGeom<OP, DK, DV, OUT>;
     static_assert(G::NT == 64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16), "launch bound must equal the launch size");
@@ -913,6 +1001,7 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
     constexpr int KTS = KT ? KTF * 64 * 8 : 8;
     __shared__ OP Kt[(G::KTA ? 2 : 1) * KTS];
     __shared__ float Nrm[OUT && RAW ? kChunk : 1];   // raw projections: gamma_t / |q_t| of the chunk
+    __shared__ float Pdg[OUT ? kChunk + kWave : 1];  // diagonal of the chunk's P, fp32 (then spare slots)
 
     const int l = lane_id(), w = wave_id(), n = l & 15, gq = l >> 4;
     const int64_t pslot = blockIdx.x / a.hv;
@@ -1022,7 +1111,10 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
 #pragma unroll
         for (int k = 0; k < (UT + NW - 1) / NW; ++k)
             if (UT % NW == 0 || w + NW * k < UT) bytes_to_lds(B.T, rt, w + NW * k);
-        if (w == NW - 1) bytes_to_lds(B.G2, res_g(j), 0);   // gate record: exactly 1 KB
+        if (w == NW - 1) {   // gate record: 1.25 KB in two loads (the second fills the pad with zeros)
+            bytes_to_lds(B.G2, res_g(j), 0);
+            bytes_to_lds(B.G2, res_g(j), 1);
+        }
         if constexpr (OUT && RAW) {
             if (w == NW - 2) bytes_to_lds(B.IK, res_ik(j), 0);   // 256 B; the rest reads as zero
         }
@@ -1044,7 +1136,7 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
         }
     };
     // output: the next count of finished chunks at which a snapshot is due
-    int64_t next_snap = a.snapshots ? (jb / a.snap_chunks + 1) * a.snap_chunks : -1;
+    int64_t next_snap = SNAP ? (jb / a.snap_chunks + 1) * a.snap_chunks : -1;
     auto body = [&](int64_t j, const Buf& cur, Buf& nxt) {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's loads of chunk j have landed
         lds_barrier();                          // everyone's have; the previous chunk is done everywhere
@@ -1056,8 +1148,8 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
             if (NBUF == 2 && j + 1 < je) issue(j + 1, nxt);
         };
         if constexpr (OUT) {
-            chunk_step<OP, DK, DV, OUT, NR, 1, NW, RAW>(cur, Pf, Kt, Ost, ST, R0, w, next_loads, Nrm);
-            if (a.snapshots && j + 1 == next_snap) {   // state after a full snapshot interval
+            chunk_step<OP, DK, DV, OUT, NR, 1, NW, RAW>(cur, Pf, Kt, Ost, ST, R0, w, next_loads, Nrm, Pdg);
+            if (SNAP && j + 1 == next_snap) {   // state after a full snapshot interval
                 if ((j + 1) * kChunk <= len) {
                     const int64_t slot = span_base(s0, seq, (int64_t)a.snap_chunks * kChunk) + (j + 1) / a.snap_chunks - 1;
 #pragma unroll
@@ -1067,7 +1159,7 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
                 next_snap += a.snap_chunks;
             }
         } else {
-            chunk_step<OP, DK, DV, OUT, NR, 1, NW, RAW>(cur, nullptr, Kt, nullptr, ST, R0, w, next_loads, Nrm);
+            chunk_step<OP, DK, DV, OUT, NR, 1, NW, RAW>(cur, nullptr, Kt, nullptr, ST, R0, w, next_loads, Nrm, Pdg);
         }
         if (NBUF == 1 && j + 1 < je) {
             lds_barrier();                      // everyone is done with this chunk's rows
@@ -1100,7 +1192,7 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
                 if (j + 1 < je) transpose_kt<OP, DK, NW>(bufs[b1].K, ktn, w);
                 if (j + 2 < je) issue(j + 2, bufs[b2]);
             };
-            chunk_step<OP, DK, DV, OUT, NR, 1, NW, RAW>(bufs[bc], nullptr, ktc, nullptr, ST, R0, w, ahead, Nrm);
+            chunk_step<OP, DK, DV, OUT, NR, 1, NW, RAW>(bufs[bc], nullptr, ktc, nullptr, ST, R0, w, ahead, Nrm, Pdg);
             bc = b1;
         };
         for (int64_t j = jb; j < je; ++j) body3(j);
@@ -1280,6 +1372,13 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
         const unsigned links = (unsigned)((int64_t)a.num_seqs * a.hv * (DV / 16));
         hipLaunchKernelGGL((gdn_link_kernel<DK, DV>), dim3(links), dim3(kLinkThreads), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if constexpr (!RAW) {   // snapshots come with the plain prefill only
+        if (a.snapshots) {
+            hipLaunchKernelGGL((gdn_chunk_kernel<OP, DK, DV, true, false, true>), dim3(parts),
+                               dim3(ChunkGeom<OP, DK, DV, true>::NT), 0, st, a);
+            return hipGetLastError();
+        }
     }
     hipLaunchKernelGGL((gdn_chunk_kernel<OP, DK, DV, true, RAW>), dim3(parts), dim3(ChunkGeom<OP, DK, DV, true>::NT),
                        0, st, a);

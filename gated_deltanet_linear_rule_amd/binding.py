@@ -14,6 +14,7 @@ import os
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+POISON_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn_poison.so")
 _lib = None
 
 GDN_SUCCESS = 0
@@ -50,50 +51,55 @@ def lib() -> ctypes.CDLL:
     """The loaded libgdn.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
-                               "`python -m gated_deltanet_linear_rule_amd.build`")
-        L = ctypes.CDLL(_LIB_PATH)
-        P = ctypes.c_void_p
-        L.gdn_prefill.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, P]
-        L.gdn_prefill.restype = ctypes.c_int
-        L.gdn_decode_step.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P]
-        L.gdn_decode_step.restype = ctypes.c_int
-        L.gdn_decode_tokens.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_int32, P, P, P, P, P, P, P, P, P]
-        L.gdn_decode_tokens.restype = ctypes.c_int
-        L.gdn_decode_slots.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_int32, P, P, P, P, P, P, ctypes.c_int64,
-                                       P, P, P, P]
-        L.gdn_decode_slots.restype = ctypes.c_int
-        L.gdn_prefill_snapshots.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, P]
-        L.gdn_prefill_snapshots.restype = ctypes.c_int
-        L.gdn_prefill_snapshots_ws.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, ctypes.c_int32,
-                                               P, P, ctypes.c_size_t, P]
-        L.gdn_prefill_snapshots_ws.restype = ctypes.c_int
-        L.gdn_prefill_workspace_size.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_uint32,
-                                                 ctypes.POINTER(ctypes.c_size_t)]
-        L.gdn_prefill_workspace_size.restype = ctypes.c_int
-        L.gdn_prefill_ws.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-        L.gdn_prefill_ws.restype = ctypes.c_int
-        L.gdn_prefill_static.argtypes = L.gdn_prefill.argtypes
-        L.gdn_prefill_static.restype = ctypes.c_int
-        L.gdn_prefill_affine.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P]
-        L.gdn_prefill_affine.restype = ctypes.c_int
-        L.gdn_prefill_affine_ws.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-        L.gdn_prefill_affine_ws.restype = ctypes.c_int
-        L.gdn_prefill_raw.argtypes = L.gdn_prefill.argtypes
-        L.gdn_prefill_raw.restype = ctypes.c_int
-        L.gdn_prefill_raw_ws.argtypes = L.gdn_prefill_ws.argtypes
-        L.gdn_prefill_raw_ws.restype = ctypes.c_int
-        L.gdn_decode_tokens_raw.argtypes = L.gdn_decode_tokens.argtypes
-        L.gdn_decode_tokens_raw.restype = ctypes.c_int
-        L.gdn_status_string.argtypes = [ctypes.c_int]
-        L.gdn_status_string.restype = ctypes.c_char_p
-        L.gdn_last_error.argtypes = []
-        L.gdn_last_error.restype = ctypes.c_char_p
-        L.gdn_abi_version.argtypes = []
-        L.gdn_abi_version.restype = ctypes.c_int
-        _lib = L
+        _lib = open_library(_LIB_PATH)
     return _lib
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """Load a build of the library (libgdn.so, or its race-check build libgdn_poison.so)
+    and declare the C ABI's argument types on it."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m gated_deltanet_linear_rule_amd.build`")
+    L = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    L.gdn_prefill.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, P]
+    L.gdn_prefill.restype = ctypes.c_int
+    L.gdn_decode_step.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P]
+    L.gdn_decode_step.restype = ctypes.c_int
+    L.gdn_decode_tokens.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_int32, P, P, P, P, P, P, P, P, P]
+    L.gdn_decode_tokens.restype = ctypes.c_int
+    L.gdn_decode_slots.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_int32, P, P, P, P, P, P, ctypes.c_int64,
+                                   P, P, P, P]
+    L.gdn_decode_slots.restype = ctypes.c_int
+    L.gdn_prefill_snapshots.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, P]
+    L.gdn_prefill_snapshots.restype = ctypes.c_int
+    L.gdn_prefill_snapshots_ws.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, ctypes.c_int32,
+                                           P, P, ctypes.c_size_t, P]
+    L.gdn_prefill_snapshots_ws.restype = ctypes.c_int
+    L.gdn_prefill_workspace_size.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_uint32,
+                                             ctypes.POINTER(ctypes.c_size_t)]
+    L.gdn_prefill_workspace_size.restype = ctypes.c_int
+    L.gdn_prefill_ws.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.gdn_prefill_ws.restype = ctypes.c_int
+    L.gdn_prefill_static.argtypes = L.gdn_prefill.argtypes
+    L.gdn_prefill_static.restype = ctypes.c_int
+    L.gdn_prefill_affine.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P]
+    L.gdn_prefill_affine.restype = ctypes.c_int
+    L.gdn_prefill_affine_ws.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.gdn_prefill_affine_ws.restype = ctypes.c_int
+    L.gdn_prefill_raw.argtypes = L.gdn_prefill.argtypes
+    L.gdn_prefill_raw.restype = ctypes.c_int
+    L.gdn_prefill_raw_ws.argtypes = L.gdn_prefill_ws.argtypes
+    L.gdn_prefill_raw_ws.restype = ctypes.c_int
+    L.gdn_decode_tokens_raw.argtypes = L.gdn_decode_tokens.argtypes
+    L.gdn_decode_tokens_raw.restype = ctypes.c_int
+    L.gdn_status_string.argtypes = [ctypes.c_int]
+    L.gdn_status_string.restype = ctypes.c_char_p
+    L.gdn_last_error.argtypes = []
+    L.gdn_last_error.restype = ctypes.c_char_p
+    L.gdn_abi_version.argtypes = []
+    L.gdn_abi_version.restype = ctypes.c_int
+    return L
 
 
 def gdn_abi_version() -> int:

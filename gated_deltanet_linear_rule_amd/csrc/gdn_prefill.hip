@@ -146,6 +146,21 @@ __device__ __forceinline__ double lane63_f64(double x) {
 template <typename T>
 __device__ __forceinline__ void ws_store(T* p, const T& x) { __builtin_nontemporal_store(x, p); }
 
+// Race-check builds (GDN_POISON_LDS): every kernel fills its shared memory with
+// all-ones words (NaN in fp64, fp32 and bf16) at entry, and the chunk kernels
+// refill each input slice with them just before its next direct load.  A read
+// of LDS that the protocol has not (re)written since then returns NaN and
+// shows up in the results; the arithmetic is unchanged otherwise.
+#ifdef GDN_POISON_LDS
+constexpr bool kPoisonLds = true;
+#else
+constexpr bool kPoisonLds = false;
+#endif
+__device__ __forceinline__ void poison_lds(void* p, int bytes, int tid, int nthreads) {
+    u32x4* q = reinterpret_cast<u32x4*>(p);
+    for (int i = tid; i < bytes / 16; i += nthreads) q[i] = u32x4{~0u, ~0u, ~0u, ~0u};
+}
+
 // ===========================================================================
 // prep: T~ fragments and the gate record of one (chunk, value head) per wave
 // ===========================================================================
@@ -236,6 +251,10 @@ __global__ __launch_bounds__(kWave * kPrepWaves) void gdn_prep_kernel(PrefillArg
     locate_span(si, a.num_seqs, kChunk, slot, n, j);
     const int64_t s1 = si.start(n + 1), t0 = si.start(n) + j * kChunk;
     if (j < 0 || t0 >= s1) return;   // a gap slot (the whole wave leaves)
+    if constexpr (kPoisonLds) {
+        poison_lds(&sm, (int)sizeof(PrepWaveSmem), l, kWave);
+        wave_lds_sync();
+    }
     const int nt = (int)((s1 - t0) < kChunk ? (s1 - t0) : kChunk);
     const int hq = (h * a.hqk) / a.hv;
     const size_t blk = (size_t)slot * a.hv + h;
@@ -1093,6 +1112,19 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
 
     // Direct loads of chunk j's rows, T~ and gates into `B` (spread over the waves).
     auto issue = [&](int64_t j, Buf& B) {
+        if constexpr (kPoisonLds) {   // this wave's target slices, then the loads
+            constexpr int EK = 1024 / (int)sizeof(OP);
+            for (int k = w; k < UK; k += NW) poison_lds(B.K + k * EK, 1024, l, kWave);
+            if constexpr (OUT)
+                for (int k = w; k < UK; k += NW) poison_lds(B.Q + k * EK, 1024, l, kWave);
+            for (int k = w; k < UV; k += NW) poison_lds(B.V + k * EK, 1024, l, kWave);
+            for (int k = w; k < UT; k += NW) poison_lds(B.T + k * EK, 1024, l, kWave);
+            if (w == NW - 1) poison_lds(B.G2, 2048, l, kWave);
+            if constexpr (OUT && RAW) {
+                if (w == NW - 2) poison_lds(B.IK, 1024, l, kWave);
+            }
+            wave_lds_sync();
+        }
         const auto rk = res_k(j);
 #pragma unroll
         for (int k = 0; k < (UK + NW - 1) / NW; ++k)
@@ -1167,6 +1199,15 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
         }
     };
 
+    if constexpr (kPoisonLds) {
+        poison_lds(bufs, (int)sizeof(bufs), threadIdx.x, G::NT);
+        poison_lds(Pf, (int)sizeof(Pf), threadIdx.x, G::NT);
+        poison_lds(Ost, (int)sizeof(Ost), threadIdx.x, G::NT);
+        poison_lds(Kt, (int)sizeof(Kt), threadIdx.x, G::NT);
+        poison_lds(Pdg, (int)sizeof(Pdg), threadIdx.x, G::NT);
+        if constexpr (OUT && RAW) poison_lds(Nrm, (int)sizeof(Nrm), threadIdx.x, G::NT);
+        __syncthreads();
+    }
     if constexpr (G::KTA) {
         // Summary, bf16: chunk j's inputs sit in buffer set (j - jb) mod 3 and
         // its K^T fragments in Kt half j mod 2.  During chunk j the waves form chunk
@@ -1263,6 +1304,11 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
         return;
     }
     if (steps <= 0) return;
+    if constexpr (kPoisonLds) {
+        poison_lds(S, (int)sizeof(S), tid, kLinkThreads);
+        poison_lds(Mb, (int)sizeof(Mb), tid, kLinkThreads);
+        __syncthreads();
+    }
     const int64_t pbase = span_base(s0, seq, L * kChunk);
 
     auto load_m = [&](int64_t p, int buf) {

@@ -27,9 +27,11 @@
 namespace gdn {
 namespace {
 
+// DPP lane move; the patterns used here give every lane a source, so no "old"
+// value is needed.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
 // Sum over the 8 consecutive lanes (a half DPP row) that share a state row.

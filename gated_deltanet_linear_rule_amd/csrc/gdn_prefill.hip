@@ -658,10 +658,11 @@ __device__ __forceinline__ void sched_fence() {
     if constexpr (ON) __builtin_amdgcn_sched_barrier(0);
 }
 
-// Lane move inside groups of four lanes (DPP quad permutation CTRL).
+// Lane move inside groups of four lanes (DPP quad permutation CTRL; every lane
+// is written, so no "old" value is needed).
 template <int CTRL>
 __device__ __forceinline__ float quad_mov(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
 // 4 x 4 transpose across the four lanes of a group: lane a's element i becomes
@@ -681,7 +682,7 @@ __device__ __forceinline__ f32x4 quad_transpose(f32x4 x) {
 
 template <int CTRL>
 __device__ __forceinline__ unsigned quad_mov_u(unsigned x) {
-    return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+    return (unsigned)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false);
 }
 
 // The same transpose after rounding to bf16: lane a packs its four values as

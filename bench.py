@@ -186,6 +186,91 @@ def write_traffic_summary(fetch_csv, write_csv, prefill_calls):
     print(json.dumps(rec, indent=1))
 
 
+SQ_PASSES = (
+    ("GRBM_GUI_ACTIVE", "SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_MFMA",
+     "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR"),
+    ("GRBM_GUI_ACTIVE", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+     "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU"),
+    ("GRBM_GUI_ACTIVE", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS",
+     "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_ACTIVE_INST_SCA", "SQ_INSTS_SMEM"),
+)
+XCDS, CUS, SIMDS = 8, 256, 1024
+
+
+def write_sq_summary(csvs, workload, calls, wave_chunks):
+    """Per-kernel shader-sequencer metrics from rocprofv3 --pmc counter files (the passes of
+    SQ_PASSES, each a separate run of the same command).  Counters are summed over the
+    dispatches of each prefill kernel and divided by the number of calls; `wave_chunks` maps a
+    kernel label to its chunk steps summed over its working waves (for per-chunk figures).
+    Cycles = GRBM_GUI_ACTIVE / 8 XCDs; SQ_*_CYCLES and SQ_ACTIVE_/WAIT_ counters are in
+    units of 4 cycles per wave."""
+    tot = {}
+    for path in csvs:
+        for name, vals in _pmc_all(path).items():
+            lab = next((k for k in KERNELS["gdn_prefill"] if _kernel_matches(k, name)), None)
+            if lab is None:
+                continue
+            agg = tot.setdefault(lab, {})
+            for c, v in vals.items():
+                agg.setdefault(c, []).append(v)
+    out = {}
+    for lab, agg in tot.items():
+        m = {c: sum(v) / calls for c, v in agg.items() if c != "GRBM_GUI_ACTIVE"}
+        # every pass holds GRBM_GUI_ACTIVE summed over its `calls` dispatches of the kernel
+        cyc = sum(agg["GRBM_GUI_ACTIVE"]) / len(agg["GRBM_GUI_ACTIVE"]) / calls / XCDS
+        waves = m.get("SQ_WAVES", 0.0)
+        wc = wave_chunks.get(lab)
+        rec = {"cycles": round(cyc), "waves": round(waves)}
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            rec["mfma_busy"] = round(m["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * SIMDS), 4)
+        if "SQ_LDS_IDX_ACTIVE" in m:
+            rec["lds_active"] = round(m["SQ_LDS_IDX_ACTIVE"] / (cyc * CUS), 4)
+            rec["lds_bank_conflict_share"] = round(m["SQ_LDS_BANK_CONFLICT"] / max(m["SQ_LDS_IDX_ACTIVE"], 1), 4)
+        if "SQ_WAVE_CYCLES" in m:
+            wcyc = m["SQ_WAVE_CYCLES"]
+            rec["issuing"] = round(m["SQ_ACTIVE_INST_ANY"] / wcyc, 4)
+            rec["waiting_on_counters"] = round(m["SQ_WAIT_ANY"] / wcyc, 4)
+            rec["waiting_to_issue"] = round(m["SQ_WAIT_INST_ANY"] / wcyc, 4)
+        if wc:
+            n = wc
+            for c, key in (("SQ_INSTS_VALU", "valu"), ("SQ_INSTS_MFMA", "mfma"), ("SQ_INSTS_SALU", "salu"),
+                           ("SQ_INSTS_LDS", "lds"), ("SQ_INSTS_VMEM_RD", "vmem_rd"), ("SQ_INSTS_VMEM_WR", "vmem_wr")):
+                if c in m:
+                    rec.setdefault("per_wave_chunk", {})[key] = round(m[c] / n, 1)
+        out[lab] = rec
+    path = os.path.join(ROOT, "profiles", "sq_counters.json")
+    try:
+        with open(path) as f:
+            allrec = json.load(f)
+    except (OSError, ValueError):
+        allrec = {}
+    allrec[workload] = {"kernels": out, "source_sha": _sha(PREFILL_SOURCES), "calls": calls}
+    with open(path, "w") as f:
+        json.dump(allrec, f, indent=1)
+    print(json.dumps(allrec[workload], indent=1))
+
+
+def _pmc_all(path):
+    """{kernel name: {counter: value summed over that kernel's dispatches}} of a rocprofv3 csv."""
+    import csv
+    out = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            d = out.setdefault(row["Kernel_Name"], {})
+            d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    return out
+
+
+def counters_current(workload):
+    """Whether profiles/sq_counters.json holds counters of `workload` taken on the current kernel code."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "sq_counters.json")) as f:
+            rec = json.load(f)[workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec.get("source_sha") == _sha(PREFILL_SOURCES)
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -216,10 +301,37 @@ def main():
                     help="no GPU: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a --calib-copy run into profiles/hbm_traffic.json")
     ap.add_argument("--prefill-calls", type=int, default=3,
-                    help="with --traffic-summary: prefill calls in the profiled run (warmup + steps)")
+                    help="with --traffic-summary / --sq-summary: prefill calls in the profiled run (warmup + steps)")
+    ap.add_argument("--sq-summary", nargs="+", metavar="CSV",
+                    help="no GPU: reduce rocprofv3 --pmc counter files of the SQ_PASSES passes of one run into "
+                         "profiles/sq_counters.json (with --prefill-workload naming the workload)")
+    ap.add_argument("--prefill-workload", default="prefill_256k",
+                    help="workload of the prefill leg (profiling runs of the smaller workloads); the headline "
+                         "metric is the default, prefill_256k")
     args = ap.parse_args()
     if args.traffic_summary:
         write_traffic_summary(*args.traffic_summary, args.prefill_calls)
+        return
+    if args.sq_summary:
+        from gated_deltanet_linear_rule_amd import inputs as gi
+        wl = gi.make_inputs(args.prefill_workload, seed=0).wl
+        # chunk steps per wave: every wave of a part's workgroup runs the part's chunks; parts are
+        # 64 L tokens, L as the library chooses on a 256-CU device (one part per sequence when the
+        # (sequence, head) chains alone fill it)
+        total_chunks = sum((n + 63) // 64 for n in wl.seqlens)
+        chains = wl.num_seqs * wl.num_v_heads
+        per_seq = [(n + 63) // 64 for n in wl.seqlens]
+        if chains >= CUS:
+            L = max(per_seq)
+        else:
+            L = min(max(8, -(-total_chunks * wl.num_v_heads // CUS)), max(per_seq))
+        parts = [max(1, -(-c // L)) for c in per_seq]
+        out_chunks = sum(per_seq) * wl.num_v_heads
+        sum_chunks = sum(c - min(c, c - (p - 1) * L) for c, p in zip(per_seq, parts)) * wl.num_v_heads
+        wcs = {"gdn_chunk_kernel<output>": out_chunks * (wl.head_dim_v // 16)}
+        if sum_chunks:
+            wcs["gdn_chunk_kernel<summary>"] = sum_chunks * (max(wl.head_dim_v, wl.head_dim_k) // 16)
+        write_sq_summary(args.sq_summary, args.prefill_workload, args.prefill_calls, wcs)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the GDN path here is single-GPU); got --gpus {args.gpus}",
@@ -244,21 +356,25 @@ def main():
 
     # ------------------------------------------------------------ prefill leg
     t_gen = time.time()
-    inp = gi.make_inputs("prefill_256k", seed=0)
+    inp = gi.make_inputs(args.prefill_workload, seed=0)
     wl = inp.wl
     T, hqk, hv, dk, dv = wl.total_tokens, wl.num_qk_heads, wl.num_v_heads, wl.head_dim_k, wl.head_dim_v
+    NS = wl.num_seqs
     q, k, v, g, beta = dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta)
+    pcu = dev(inp.cu_seqlens) if NS > 1 else None
+    ps0 = dev(inp.init_state) if inp.init_state is not None else None
+    pkw = dict(cu_seqlens=pcu) if pcu is not None else {}
     out = torch.empty((T, hv, dv), dtype=torch.bfloat16, device="cuda")
-    fin = torch.empty((1, hv, dv, dk), dtype=torch.float32, device="cuda")
+    fin = torch.empty((NS, hv, dv, dk), dtype=torch.float32, device="cuda")
     log(f"prefill inputs generated and uploaded in {time.time() - t_gen:.1f}s")
 
     # every prefill leg runs on a workspace allocated here, outside the timed region
-    ws_bytes = max(B.gdn_prefill_workspace_size(q, v), B.gdn_prefill_workspace_size(q, v, raw=True),
-                   B.gdn_prefill_workspace_size(k, v, affine=True))
+    ws_bytes = max(B.gdn_prefill_workspace_size(q, v, **pkw), B.gdn_prefill_workspace_size(q, v, raw=True, **pkw),
+                   B.gdn_prefill_workspace_size(k, v, affine=True, **pkw))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
 
     def step():
-        B.gdn_prefill(q, k, v, g, beta, None, None, out=out, final_state=fin, workspace=ws)
+        B.gdn_prefill(q, k, v, g, beta, ps0, out=out, final_state=fin, workspace=ws, **pkw)
 
     for _ in range(args.warmup):
         step()
@@ -278,15 +394,24 @@ def main():
     assert torch.isfinite(out.float()).all().item(), "non-finite prefill output"
     log(f"prefill: mean {ms:.3f} ms/call, median {np.median(per_call_ms):.3f}, wall {1e3 * wall / args.steps:.3f} ms/step")
 
-    bytes_call = prefill_bytes(T, 1, hqk, hv, dk, dv)
+    bytes_call = prefill_bytes(T, NS, hqk, hv, dk, dv, init=ps0 is not None)
     flops_call = prefill_flops_per_token(hqk, hv, dk, dv) * T
     gbs = bytes_call / (ms * 1e-3) / 1e9
     tflops = flops_call / (ms * 1e-3) / 1e12
     tok_s = T / (ms * 1e-3)
     traffic = measured_traffic("gdn_prefill", PREFILL_SOURCES)
+    # shader counters of this workload's kernels (profiles/sq_counters.json), while taken on this code
+    counters = None
+    if counters_current(args.prefill_workload):
+        with open(os.path.join(ROOT, "profiles", "sq_counters.json")) as f:
+            crec = json.load(f)[args.prefill_workload]
+        counters = {"source_sha": crec["source_sha"],
+                    "kernels": {k: {m: v.get(m) for m in ("mfma_busy", "lds_active", "issuing", "waiting_on_counters")}
+                                for k, v in crec["kernels"].items()}}
 
     raw_rec = snapshot_rec = affine_rec = None
-    if not args.no_variants:
+    headline = args.prefill_workload == "prefill_256k"
+    if not args.no_variants and headline:
         # the same call from raw projections (fused q/k normalisation and gate
         # activations; the normalised inputs and their gates stand in as values)
         for _ in range(2):
@@ -345,7 +470,7 @@ def main():
     # the two smaller prefill workloads, reported beside the headline: 4,096 tokens x 16 heads, and 8
     # packed sequences of U[1024, 16384] tokens with 32 value heads on 16 q/k heads and initial states
     other = None
-    if not args.no_variants:
+    if not args.no_variants and headline:
         other = {}
         for name, reps in (("prefill_4k", 50), ("varlen_8x", 10)):
             o_inp = gi.make_inputs(name, seed=0)
@@ -540,8 +665,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded: q,k ~ N(0,1) L2-normalised, v ~ N(0,1), beta = sigmoid(N(0,1)), g = -softplus(N(0,1)))",
-        "config": {"workload": "prefill_256k: B=1, T=262144, H_qk=H_v=16, d_k=d_v=128, bf16 I/O, fp32 gates and state, zero initial state, chunk 64",
+        "config": {"workload": "prefill_256k: B=1, T=262144, H_qk=H_v=16, d_k=d_v=128, bf16 I/O, fp32 gates and state, zero initial state, chunk 64"
+                   if headline else args.prefill_workload,
                    "global_batch": 1, "seq_len": T, "parallelism": "single GPU"},
+        "counters": counters,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic / (ms * 1e-3) / 1e9, 1),

@@ -122,3 +122,41 @@ def test_traffic_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     dec = rec["gdn_decode"]
     assert dec["bytes_per_call"] == pytest.approx((50 * 2 + 60) * 1024)
     assert dec["source_sha"] == "sha-gdn_decode.hip"
+
+
+def _write_pmc_multi(path, rows):
+    """rows: (dispatch, kernel, {counter: value})."""
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for d, name, vals in rows:
+            for c, v in vals.items():
+                w.writerow([d, name, c, v])
+
+
+def test_sq_summary_per_call_rates(tmp_path, monkeypatch):
+    """Two passes over two calls of one kernel: cycles from GRBM_GUI_ACTIVE / 8 XCDs per call,
+    matrix-core busy over 1024 SIMDs, LDS over 256 CUs, per-wave-chunk instruction counts."""
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "_sha", lambda paths, read=None: "sha")
+    cyc = 1000
+    p1 = [(d, OUTPUT, {"GRBM_GUI_ACTIVE": 8 * cyc, "SQ_WAVES": 16, "SQ_INSTS_VALU": 3200, "SQ_INSTS_MFMA": 640})
+          for d in (1, 2)]
+    p2 = [(d, OUTPUT, {"GRBM_GUI_ACTIVE": 8 * cyc, "SQ_VALU_MFMA_BUSY_CYCLES": 1024 * cyc / 4,
+                       "SQ_LDS_IDX_ACTIVE": 256 * cyc / 2, "SQ_LDS_BANK_CONFLICT": 256 * cyc / 20,
+                       "SQ_WAVE_CYCLES": 400, "SQ_ACTIVE_INST_ANY": 100, "SQ_WAIT_ANY": 200, "SQ_WAIT_INST_ANY": 50})
+          for d in (1, 2)]
+    _write_pmc_multi(tmp_path / "p1.csv", p1)
+    _write_pmc_multi(tmp_path / "p2.csv", p2)
+    bench.write_sq_summary([str(tmp_path / "p1.csv"), str(tmp_path / "p2.csv")], "w", calls=2,
+                           wave_chunks={"gdn_chunk_kernel<output>": 16 * 10})
+    rec = json.loads((tmp_path / "profiles" / "sq_counters.json").read_text())["w"]
+    k = rec["kernels"]["gdn_chunk_kernel<output>"]
+    assert rec["source_sha"] == "sha" and k["cycles"] == cyc
+    assert k["mfma_busy"] == pytest.approx(0.25) and k["lds_active"] == pytest.approx(0.5)
+    assert k["lds_bank_conflict_share"] == pytest.approx(0.1)
+    assert (k["issuing"], k["waiting_on_counters"], k["waiting_to_issue"]) == (0.25, 0.5, 0.125)
+    # per call 3200 VALU and 640 MFMA instructions over 16 waves x 10 chunks
+    assert k["per_wave_chunk"] == {"valu": 20.0, "mfma": 4.0}
+    assert bench.counters_current("w") and not bench.counters_current("other")

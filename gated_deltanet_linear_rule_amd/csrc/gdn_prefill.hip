@@ -174,6 +174,21 @@ __device__ __forceinline__ void poison_lds(void* p, int bytes, int tid, int nthr
 constexpr int kPrepWaves = 4;
 constexpr int kDiagLd = 16 * 16 + 8;   // floats per stored 16 x 16 block (padded)
 
+// Workgroups are dispatched to the eight XCDs in turn (workgroup b to XCD
+// b mod 8), and each XCD has its own L2.  The value heads of one chunk read
+// the same 128-byte lines of g and beta ([tokens, Hv] fp32), so the prep
+// kernel hands kPrepGroup consecutive runs of items (kPrepGroup * 4 items: all
+// 16 heads of a chunk at Hv = 16) to workgroups of one XCD: in every full
+// block of 8 * kPrepGroup workgroups, workgroup 8 i + x takes run
+// kPrepGroup x + (i mod kPrepGroup) of that block; the rest keep their order.
+constexpr int kXcds = 8, kPrepGroup = 4;
+__device__ __forceinline__ int64_t prep_run(int64_t b, int64_t nwg) {
+    constexpr int64_t B = kXcds * kPrepGroup;
+    if (b >= nwg - nwg % B) return b;
+    const int64_t base = b - b % B, i = (b % B) / kXcds, x = b % kXcds;
+    return base + kPrepGroup * x + i;
+}
+
 struct PrepWaveSmem {
     alignas(16) float D[4 * kDiagLd];  // diagonal blocks of A, then of T; column-major
     alignas(16) double G[kChunk];      // log2-scaled cumulative gates (fp64)
@@ -241,7 +256,7 @@ __global__ __launch_bounds__(kWave * kPrepWaves) void gdn_prep_kernel(PrefillArg
 
     const int l = lane_id(), w = wave_id(), r = l & 15, gq = l >> 4;
     PrepWaveSmem& sm = smem[w];
-    const int64_t item = (int64_t)blockIdx.x * kPrepWaves + w;
+    const int64_t item = prep_run(blockIdx.x, gridDim.x) * kPrepWaves + w;
     if (item >= a.num_slots * a.hv) return;
     const int64_t slot = item / a.hv;
     const int h = (int)(item - slot * a.hv);
@@ -603,7 +618,8 @@ struct ChunkBuf {
 // Geometry of the chunk kernels: one wave per 16 state rows (two waves per
 // SIMD, so one wave's LDS latency hides behind the other's matrix work).
 // Summary: value block w and transition block w per wave, so every K operand
-// read from LDS feeds two products.
+// read from LDS feeds two products (with d_v != d_k, the waves past the
+// smaller block count hold one block).
 template <typename OP, int DK, int DV, bool OUT>
 struct ChunkGeom {
     static constexpr int NR = OUT ? 1 : 2;
@@ -630,6 +646,18 @@ __device__ __forceinline__ void store_state(float* S, int R0, const f32x4 (&ST)[
     const int l = lane_id(), n = l & 15, gq = l >> 4;
 #pragma unroll
     for (int db = 0; db < DK / 16; ++db) *reinterpret_cast<f32x4*>(S + (size_t)(R0 + n) * DK + pi_dk(db, 4 * gq)) = ST[db];
+}
+// The transition M_p in the workspace: row r keeps its 16-column blocks in the
+// order c / 16 XOR ((r / 4) mod 4), so that the link kernel's operand reads
+// (rows 4 g + i for the four lane groups g, one 16-column block) meet four
+// different bank groups instead of one.
+__host__ __device__ constexpr int m_col(int r, int c) { return c ^ (((r >> 2) & 3) << 4); }
+template <int DK>
+__device__ __forceinline__ void store_transition(float* M, int R0, const f32x4 (&ST)[DK / 16]) {
+    const int l = lane_id(), n = l & 15, gq = l >> 4;
+#pragma unroll
+    for (int db = 0; db < DK / 16; ++db)
+        *reinterpret_cast<f32x4*>(M + (size_t)(R0 + n) * DK + m_col(R0 + n, pi_dk(db, 4 * gq))) = ST[db];
 }
 
 
@@ -1042,8 +1070,8 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
     if constexpr (OUT) {
         R0[0] = 16 * w;
     } else {
-        R0[0] = w < NVB ? 16 * w : 0;   // value block (discarded when w >= NVB)
-        R0[1] = w < NMB ? 16 * w : 0;   // transition block (discarded when w >= NMB)
+        R0[0] = w < NVB ? 16 * w : 0;   // value block (none when w >= NVB)
+        R0[1] = w < NMB ? 16 * w : 0;   // transition block (none when w >= NMB)
     }
     f32x4 ST[NR][NDB];
 
@@ -1168,6 +1196,23 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
             }
         }
     };
+    // Summary chunk step over the wave's blocks.  With d_v != d_k the waves
+    // past the smaller block count have one block only and run a one-block step
+    // (a wave-uniform branch; every wave still meets the same barriers).
+    auto summary_blocks = [&](const Buf& cb, OP* ktc, auto&& hook) {
+        if constexpr (!OUT) {
+            using One = f32x4(&)[1][NDB];
+            using OneR = const int(&)[1];
+            if (NVB == NMB || (w < NVB && w < NMB))
+                chunk_step<OP, DK, DV, OUT, NR, 1, NW, RAW>(cb, nullptr, ktc, nullptr, ST, R0, w, hook, Nrm, Pdg);
+            else if (w < NMB)   // d_v < d_k: a transition block only
+                chunk_step<OP, DK, DV, OUT, 1, 0, NW, RAW>(cb, nullptr, ktc, nullptr, reinterpret_cast<One>(ST[1]),
+                                                           reinterpret_cast<OneR>(R0[1]), w, hook, Nrm, Pdg);
+            else                // d_k < d_v: a value block only
+                chunk_step<OP, DK, DV, OUT, 1, 1, NW, RAW>(cb, nullptr, ktc, nullptr, reinterpret_cast<One>(ST[0]),
+                                                           reinterpret_cast<OneR>(R0[0]), w, hook, Nrm, Pdg);
+        }
+    };
     // output: the next count of finished chunks at which a snapshot is due
     int64_t next_snap = SNAP ? (jb / a.snap_chunks + 1) * a.snap_chunks : -1;
     auto body = [&](int64_t j, const Buf& cur, Buf& nxt) {
@@ -1192,7 +1237,7 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
                 next_snap += a.snap_chunks;
             }
         } else {
-            chunk_step<OP, DK, DV, OUT, NR, 1, NW, RAW>(cur, nullptr, Kt, nullptr, ST, R0, w, next_loads, Nrm, Pdg);
+            summary_blocks(cur, Kt, next_loads);
         }
         if (NBUF == 1 && j + 1 < je) {
             lds_barrier();                      // everyone is done with this chunk's rows
@@ -1234,7 +1279,7 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
                 if (j + 1 < je) transpose_kt<OP, DK, NW>(bufs[b1].K, ktn, w);
                 if (j + 2 < je) issue(j + 2, bufs[b2]);
             };
-            chunk_step<OP, DK, DV, OUT, NR, 1, NW, RAW>(bufs[bc], nullptr, ktc, nullptr, ST, R0, w, ahead, Nrm, Pdg);
+            summary_blocks(bufs[bc], ktc, ahead);
             bc = b1;
         };
         for (int64_t j = jb; j < je; ++j) body3(j);
@@ -1256,7 +1301,7 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
             for (int b = 0; b < NR; ++b) store_state<DK>(a.final_state + chain * DV * DK, R0[b], ST[b]);
     } else {
         if (w < NVB) store_state<DK>(a.ws_b + sblk * DV * DK, R0[0], ST[0]);
-        if (w < NMB) store_state<DK>(a.ws_m + sblk * DK * DK, R0[1], ST[1]);
+        if (w < NMB) store_transition<DK>(a.ws_m + sblk * DK * DK, R0[1], ST[1]);
     }
 }
 
@@ -1279,7 +1324,7 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
     constexpr int MI = DK * DK * 4 / 1024;               // 1 KB direct loads per M
     static_assert(MI % NWV == 0, "M loads per wave");
     __shared__ float S[16][LD];
-    __shared__ float Mb[2][DK * DK];                      // M_p, row-major
+    __shared__ float Mb[2][DK * DK];                      // M_p, row-major (column blocks as m_col)
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), n = l & 15, gq = l >> 4;
     // affine map: row blocks 0 .. NVB - 1 are offset rows (from zero, + B_p),
     // NVB .. NVB + NDB - 1 transition rows (from the identity, no B_p)
@@ -1374,7 +1419,7 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
                 for (int i = 0; i < 8; ++i) {
                     const int rr = 32 * kk + (i < 4 ? 4 * gq + i : 16 + 4 * gq + i - 4);
                     av[i] = S[n][rr];
-                    bv[i] = M[rr * DK + 16 * db + n];
+                    bv[i] = M[rr * DK + m_col(rr, 16 * db + n)];
                 }
                 c = Op<float>::mma(av, bv, c);
             }

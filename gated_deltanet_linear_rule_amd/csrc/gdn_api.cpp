@@ -230,7 +230,7 @@ gdn_status plan_prefill(const gdn_shape* shape, bool packed, PrefillKind kind, g
     // the affine map needs every sequence's part maps, split or not
     split = kind == kAffine || a.part_chunks < longest;
     if (a.num_part_slots * a.hv > INT32_MAX ||
-        a.num_seqs * (int64_t)a.hv * (a.dv / 16 + shape->head_dim_k / 16) > INT32_MAX)
+        (a.num_seqs * (int64_t)a.hv + 7) * (a.dv / 16 + shape->head_dim_k / 16) > INT32_MAX)
         return fail(GDN_ERROR_NOT_SUPPORTED, "too many (part, head) pairs");
     const gdn::PrefillWorkspace wl(a.num_slots, a.num_part_slots, split, a.hv, shape->head_dim_k, shape->head_dim_v,
                                    shape->dtype == GDN_DTYPE_BF16 ? 2 : 4, kind == kRaw);

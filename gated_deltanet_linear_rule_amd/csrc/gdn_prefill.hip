@@ -1330,8 +1330,13 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
     // NVB .. NVB + NDB - 1 transition rows (from the identity, no B_p)
     const bool aff = a.aff_m != nullptr;
     const int NBK = aff ? NVB + NDB : NVB;
-    const int vb = (int)(blockIdx.x % NBK);
-    const int64_t chain = blockIdx.x / NBK;
+    // Workgroup b takes row block b / C of chain b mod C (C = chains rounded up
+    // to a multiple of the 8 XCDs): all row blocks of a chain then run on one
+    // XCD, and every M_p they all load comes from that XCD's L2 after the first.
+    const int64_t nchain = (int64_t)a.num_seqs * a.hv, C = (nchain + kXcds - 1) / kXcds * kXcds;
+    const int vb = (int)(blockIdx.x / C);
+    const int64_t chain = blockIdx.x - (int64_t)vb * C;
+    if (chain >= nchain) return;
     const bool trans = vb >= NVB;
     const int seq = (int)(chain / a.hv), h = (int)(chain - (int64_t)seq * a.hv);
     const SeqIndex si{a.cu, a.seqlen};
@@ -1406,6 +1411,25 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
             load_b(p + 1, bnext);
         }
         const float* M = Mb[cb];
+        // every operand of the step's products is read from LDS first, then the
+        // products run (one wait for LDS instead of one per K step)
+        f32x8 av[NKK], bv[PER][NKK];
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) av[kk][i] = S[n][32 * kk + (i < 4 ? 4 * gq + i : 16 + 4 * gq + i - 4)];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int db = w + NWV * k < NDB ? w + NWV * k : w;   // (an unused block reads a valid one)
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int rr = 32 * kk + (i < 4 ? 4 * gq + i : 16 + 4 * gq + i - 4);
+                    bv[k][kk][i] = M[rr * DK + m_col(rr, 16 * db + n)];
+                }
+        }
+        __builtin_amdgcn_sched_barrier(0);
         f32x4 res[PER];
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
@@ -1413,16 +1437,7 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
             if (db >= NDB) break;
             f32x4 c = bcur[k];
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                f32x8 av, bv;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int rr = 32 * kk + (i < 4 ? 4 * gq + i : 16 + 4 * gq + i - 4);
-                    av[i] = S[n][rr];
-                    bv[i] = M[rr * DK + m_col(rr, 16 * db + n)];
-                }
-                c = Op<float>::mma(av, bv, c);
-            }
+            for (int kk = 0; kk < NKK; ++kk) c = Op<float>::mma(av[kk], bv[k][kk], c);
             res[k] = c;
         }
         lds_barrier();                                   // S_p read by everyone (M_{p+1} may be in flight)
@@ -1461,7 +1476,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
         hipLaunchKernelGGL((gdn_chunk_kernel<OP, DK, DV, false, RAW>), dim3(parts),
                            dim3(ChunkGeom<OP, DK, DV, false>::NT), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        const unsigned links = (unsigned)((int64_t)a.num_seqs * a.hv * (DV / 16));
+        const unsigned links = (unsigned)(((int64_t)a.num_seqs * a.hv + kXcds - 1) / kXcds * kXcds * (DV / 16));
         hipLaunchKernelGGL((gdn_link_kernel<DK, DV>), dim3(links), dim3(kLinkThreads), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -1484,7 +1499,7 @@ hipError_t launch_prefill_affine_t(const PrefillArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((gdn_chunk_kernel<OP, DK, DV, false, false>), dim3((unsigned)(a.num_part_slots * a.hv)),
                        dim3(ChunkGeom<OP, DK, DV, false>::NT), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const unsigned links = (unsigned)((int64_t)a.num_seqs * a.hv * (DV / 16 + DK / 16));
+    const unsigned links = (unsigned)(((int64_t)a.num_seqs * a.hv + kXcds - 1) / kXcds * kXcds * (DV / 16 + DK / 16));
     hipLaunchKernelGGL((gdn_link_kernel<DK, DV>), dim3(links), dim3(kLinkThreads), 0, st, a);
     return hipGetLastError();
 }

@@ -647,17 +647,18 @@ __device__ __forceinline__ void store_state(float* S, int R0, const f32x4 (&ST)[
 #pragma unroll
     for (int db = 0; db < DK / 16; ++db) *reinterpret_cast<f32x4*>(S + (size_t)(R0 + n) * DK + pi_dk(db, 4 * gq)) = ST[db];
 }
-// The transition M_p in the workspace: row r keeps its 16-column blocks in the
-// order c / 16 XOR ((r / 4) mod 4), so that the link kernel's operand reads
-// (rows 4 g + i for the four lane groups g, one 16-column block) meet four
-// different bank groups instead of one.
-__host__ __device__ constexpr int m_col(int r, int c) { return c ^ (((r >> 2) & 3) << 4); }
+// The transition M_p in the workspace, transposed: entry M[r][c] at c DK + tr(c, r)
+// with tr(c, r) = r XOR 4 (c mod 16).  The link kernel's B operand for
+// column c is M[r .. r + 3][c] for aligned r: 16 contiguous bytes, and the XOR
+// spreads the 16 columns of a read over all 64 banks.
+__host__ __device__ constexpr int m_pos(int c, int r, int dk) { return c * dk + (r ^ ((c & 15) << 2)); }
 template <int DK>
 __device__ __forceinline__ void store_transition(float* M, int R0, const f32x4 (&ST)[DK / 16]) {
     const int l = lane_id(), n = l & 15, gq = l >> 4;
 #pragma unroll
     for (int db = 0; db < DK / 16; ++db)
-        *reinterpret_cast<f32x4*>(M + (size_t)(R0 + n) * DK + m_col(R0 + n, pi_dk(db, 4 * gq))) = ST[db];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) M[m_pos(pi_dk(db, 4 * gq + i), R0 + n, DK)] = ST[db][i];
 }
 
 
@@ -1324,7 +1325,7 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
     constexpr int MI = DK * DK * 4 / 1024;               // 1 KB direct loads per M
     static_assert(MI % NWV == 0, "M loads per wave");
     __shared__ float S[16][LD];
-    __shared__ float Mb[2][DK * DK];                      // M_p, row-major (column blocks as m_col)
+    __shared__ float Mb[2][DK * DK];                      // M_p, transposed (m_pos)
     const int tid = threadIdx.x, l = lane_id(), w = wave_id(), n = l & 15, gq = l >> 4;
     // affine map: row blocks 0 .. NVB - 1 are offset rows (from zero, + B_p),
     // NVB .. NVB + NDB - 1 transition rows (from the identity, no B_p)
@@ -1422,12 +1423,12 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
         for (int k = 0; k < PER; ++k) {
             const int db = w + NWV * k < NDB ? w + NWV * k : w;   // (an unused block reads a valid one)
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int rr = 32 * kk + (i < 4 ? 4 * gq + i : 16 + 4 * gq + i - 4);
-                    bv[k][kk][i] = M[rr * DK + m_col(rr, 16 * db + n)];
-                }
+            for (int kk = 0; kk < NKK; ++kk) {
+                const int c = 16 * db + n;
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(&M[m_pos(c, 32 * kk + 4 * gq, DK)]);
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(&M[m_pos(c, 32 * kk + 16 + 4 * gq, DK)]);
+                bv[k][kk] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         f32x4 res[PER];
@@ -1519,7 +1520,7 @@ int64_t prefill_part_chunks(int64_t num_tokens, int num_seqs, int hv, int num_cu
     const int64_t chains = (int64_t)num_seqs * hv;
     if (num_seqs <= 0 || chains >= num_cus) return whole;
     // about one part per compute unit, at least kMinPartChunks chunks each
-    constexpr int64_t kMinPartChunks = 8;
+    constexpr int64_t kMinPartChunks = 6;
     int64_t L = (chunks * hv + num_cus - 1) / (num_cus > 0 ? num_cus : 1);
     L = L > kMinPartChunks ? L : kMinPartChunks;
     return L < whole ? L : whole;

@@ -121,12 +121,13 @@ def test_long_decay_free_stretch_stays_accurate():
 
 # ------------------------------------------------------- sequences cut into parts
 # With fewer (sequence, head) chains than compute units, long sequences are cut
-# into parts of L chunks (at least 8): every part but the last is summarised
+# into parts of L chunks (at least 6): every part but the last is summarised
 # (transition and offset), the link composes the start states, and every part
 # reruns from its true start state.
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_parts_long_sequence(dtype):
-    """One 40000-token sequence (625 chunks: 79 parts of 8, the last partial), given initial state."""
+    """One 40000-token sequence (625 chunks: 105 parts of 6 on 256 compute units, the last partial), given
+    initial state."""
     inp = gi.make_inputs(gi.custom(dtype=dtype, Hqk=2, Hv=2, dk=128, dv=128, seqlens=(40000,),
                                    init_state="normal"), seed=21)
     check_prefill(inp, label=f"parts 40000 {dtype}")

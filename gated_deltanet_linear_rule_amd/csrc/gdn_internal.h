@@ -51,7 +51,7 @@ struct PrefillArgs {
     float* ws_ik;              // raw projections only: 64 values 1 / |k_t| (256 B)
     // Per (part slot, value head), fp32 row-major; NULL when no sequence has
     // more than one part:
-    float* ws_m;               // d_k x d_k transition M_p of the part
+    float* ws_m;               // d_k x d_k transition M_p of the part, transposed (see m_pos)
     float* ws_b;               // d_v x d_k offset B_p of the part (state from zero)
     float* ws_s;               // d_v x d_k start state S_p of the part
     // Optional state snapshots every snap_chunks chunks of each sequence:

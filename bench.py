@@ -195,7 +195,6 @@ SQ_PASSES = (
      "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_ACTIVE_INST_SCA", "SQ_INSTS_SMEM"),
 )
 XCDS, CUS, SIMDS = 8, 256, 1024
-LEG_PAUSE_S = 0.5   # idle time before each secondary timing leg
 
 
 def write_sq_summary(csvs, workload, calls, wave_chunks):
@@ -414,11 +413,7 @@ def main():
     headline = args.prefill_workload == "prefill_256k"
     if not args.no_variants and headline:
         # the same call from raw projections (fused q/k normalisation and gate
-        # activations; the normalised inputs and their gates stand in as values).
-        # Each secondary leg starts after a short idle pause: the GPU lowers its
-        # clock under sustained load, and the pause keeps one leg's power state
-        # from biasing the next leg's timing.
-        time.sleep(LEG_PAUSE_S)
+        # activations; the normalised inputs and their gates stand in as values)
         for _ in range(2):
             B.gdn_prefill(q, k, v, g, beta, None, None, out=out, final_state=fin, raw=True, workspace=ws)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -434,7 +429,6 @@ def main():
                    "ms_per_call": round(raw_ms, 4), "tokens_per_s": round(T / (raw_ms * 1e-3), 1)}
 
         # the same call with a state snapshot every 4096 tokens (prefix reuse)
-        time.sleep(LEG_PAUSE_S)
         snap_chunks = 64
         snaps = torch.empty((B.snapshot_slots(T, 1, snap_chunks), hv, dv, dk), dtype=torch.float32, device="cuda")
         for _ in range(2):
@@ -455,7 +449,6 @@ def main():
         del snaps
 
         # the affine state map of the whole sequence (per-device half of a sequence-sharded prefill)
-        time.sleep(LEG_PAUSE_S)
         aff_m = torch.empty((1, hv, dk, dk), dtype=torch.float32, device="cuda")
         aff_b = torch.empty((1, hv, dv, dk), dtype=torch.float32, device="cuda")
         for _ in range(2):

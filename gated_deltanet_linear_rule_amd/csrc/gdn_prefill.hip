@@ -1028,41 +1028,89 @@ __device__ __forceinline__ void chunk_step(const ChunkBuf<OP, DK, DV, OUT, OUT &
     }
 }
 
+// Shared memory of a chunk-kernel workgroup.
+template <typename OP, int DK, int DV, bool OUT, bool RAW>
+struct ChunkSmem {
+    using G = ChunkGeom<OP, DK, DV, OUT>;
+    // bf16: the chunk's K^T operand fragments (2 per state tile), transposed once
+    // per chunk instead of once per wave
+    static constexpr int KTS = sizeof(OP) == 2 ? 2 * (DK / 16) * 64 * 8 : 8;
+    ChunkBuf<OP, DK, DV, OUT, OUT && RAW> bufs[G::NBUF];
+    alignas(16) OP Pf[OUT ? kTriFrags * 64 * 8 : 8];
+    alignas(16) OP Ost[OUT ? kChunk * DV : 8];        // O rows of the previous chunk (RowTile layout)
+    alignas(16) OP Kt[(G::KTA ? 2 : 1) * KTS];
+    alignas(16) float Nrm[OUT && RAW ? kChunk : 1];   // raw projections: gamma_t / |q_t| of the chunk
+    alignas(16) float Pdg[OUT ? kChunk + kWave : 1];  // diagonal of the chunk's P, fp32 (then spare slots)
+};
+
+// Where a workgroup's chunk-kernel arrays are (ChunkSmem's members, wherever
+// they are placed).
+template <typename OP, int DK, int DV, bool OUT, bool RAW>
+struct ChunkLds {
+    ChunkBuf<OP, DK, DV, OUT, OUT && RAW>* bufs;
+    OP *Pf, *Ost, *Kt;
+    float *Nrm, *Pdg;
+    __device__ static ChunkLds of(ChunkSmem<OP, DK, DV, OUT, RAW>& m) { return {m.bufs, m.Pf, m.Ost, m.Kt, m.Nrm, m.Pdg}; }
+};
+
+// The parts of a sequence of nc chunks on its ns = ceil(nc / L) slots of L
+// chunks (one slot when it is empty).  The first part takes slots [0, kk)
+// (chunks [0, min(kk L, nc))) and every later slot j is a part of its own
+// (chunks [j L, min(j L + L, nc))); slots 1 .. kk - 1 are gaps.  A sequence of
+// more than `cut` chunks has kk = min(first_slots, ns), any other is one part
+// (kk = ns).  One pass over every part: cut = 0, first_slots = 1.
+struct SeqParts {
+    int64_t nc, L, ns, kk;
+    __device__ SeqParts(int64_t nc_, int64_t L_, int64_t cut, int64_t first_slots) : nc(nc_), L(L_) {
+        ns = nc > 0 ? (nc + L - 1) / L : 1;
+        kk = nc > cut ? (first_slots < ns ? first_slots : ns) : ns;
+    }
+    __device__ bool is_part(int64_t j) const { return j == 0 || (j >= kk && j < ns); }
+    __device__ int64_t last() const { return ns > kk ? ns - 1 : 0; }
+    __device__ int64_t begin(int64_t j) const { return j * L; }
+    __device__ int64_t end(int64_t j) const {
+        const int64_t e = j == 0 ? kk * L : j * L + L;
+        return e < nc ? e : nc;
+    }
+};
+
+// One (part slot, value head) of a chunk kernel.
 // OUT = false: summary of parts p < np - 1 (B_p into ws_b, M_p into ws_m).
 // OUT = true: outputs of every part, from ws_s (np > 1) or init_state (np = 1);
-// the last part writes final_state; SNAP: also the state snapshots.
-template <typename OP, int DK, int DV, bool OUT, bool RAW, bool SNAP = false>
-__global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) void gdn_chunk_kernel(PrefillArgs a) {
+// the last part writes final_state; SNAP: also the state snapshots.  In the
+// balanced schedule (a.phase 1 and 2, see launch_prefill_t) the first part of
+// every sequence runs in phase 1 from init_state, the later parts in phase 2.
+template <typename OP, int DK, int DV, bool OUT, bool RAW, bool SNAP>
+__device__ __forceinline__ void chunk_part(const PrefillArgs& a, int64_t item, const ChunkLds<OP, DK, DV, OUT, RAW>& sm) {
     using G = ChunkGeom<OP, DK, DV, OUT>;
-    static_assert(G::NT == 64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16), "launch bound must equal the launch size");
     using Buf = ChunkBuf<OP, DK, DV, OUT, OUT && RAW>;
     constexpr int NR = G::NR, NW = G::NW, NBUF = G::NBUF;
     constexpr int NVB = DV / 16, NMB = DK / 16, NDB = DK / 16;
     constexpr int E = (int)sizeof(OP);
     constexpr int UK = kChunk * DK * E / 1024, UV = kChunk * DV * E / 1024, UT = Units<OP>::TU;
-    __shared__ Buf bufs[NBUF];
-    __shared__ OP Pf[OUT ? kTriFrags * 64 * 8 : 8];
-    __shared__ OP Ost[OUT ? kChunk * DV : 8];   // O rows of the previous chunk (RowTile layout)
-    // bf16: the chunk's K^T operand fragments (2 per state tile), transposed once
-    // per chunk instead of once per wave
+    Buf* const bufs = sm.bufs;
+    OP* const Pf = sm.Pf;
+    OP* const Ost = sm.Ost;
     constexpr bool KT = sizeof(OP) == 2;
-    constexpr int KTF = 2 * (DK / 16);
-    constexpr int KTS = KT ? KTF * 64 * 8 : 8;
-    __shared__ OP Kt[(G::KTA ? 2 : 1) * KTS];
-    __shared__ float Nrm[OUT && RAW ? kChunk : 1];   // raw projections: gamma_t / |q_t| of the chunk
-    __shared__ float Pdg[OUT ? kChunk + kWave : 1];  // diagonal of the chunk's P, fp32 (then spare slots)
+    constexpr int KTS = ChunkSmem<OP, DK, DV, OUT, RAW>::KTS;
+    OP* const Kt = sm.Kt;
+    float* const Nrm = sm.Nrm;
+    float* const Pdg = sm.Pdg;
 
     const int l = lane_id(), w = wave_id(), n = l & 15, gq = l >> 4;
-    const int64_t pslot = blockIdx.x / a.hv;
-    const int h = (int)(blockIdx.x - pslot * a.hv);
+    const int64_t pslot = item / a.hv;
+    const int h = (int)(item - pslot * a.hv);
     const SeqIndex si{a.cu, a.seqlen};
     const int64_t L = a.part_chunks;
     int seq;
     int64_t p;
     locate_span(si, a.num_seqs, L * kChunk, pslot, seq, p);
     const int64_t s0 = si.start(seq), len = si.start(seq + 1) - s0;
-    const int64_t nc = (len + kChunk - 1) / kChunk, np = (nc + L - 1) / L;
-    if (p < 0 || p >= (np > 1 ? np : 1)) return;               // gap slot
+    const int64_t nc = (len + kChunk - 1) / kChunk;
+    const SeqParts sp(nc, L, a.cut_chunks, a.first_slots);
+    if (p < 0 || !sp.is_part(p)) return;                        // gap slot
+    const bool last = p == sp.last();
+    if (OUT && (a.phase == 1 ? p != 0 : a.phase == 2 && p == 0)) return;   // the other phase's part
     const int64_t chain = (int64_t)seq * a.hv + h;
     const size_t sblk = (size_t)pslot * a.hv + h;
 
@@ -1075,6 +1123,7 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
         R0[1] = w < NMB ? 16 * w : 0;   // transition block (none when w >= NMB)
     }
     f32x4 ST[NR][NDB];
+    float* Send = nullptr;
 
     if constexpr (OUT) {
         if (nc == 0) {   // empty sequence: the state passes through
@@ -1087,13 +1136,22 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
             }
             return;
         }
-        const float* Sin = np > 1 ? a.ws_s + sblk * DV * DK : (a.init_state ? a.init_state + chain * DV * DK : nullptr);
+        // the part's start state: written by the link (one pass over more than
+        // one part, and the later parts of the balanced schedule), else init_state
+        const float* Sin = a.phase == 2 || (a.phase == 0 && sp.ns > 1)
+                               ? a.ws_s + sblk * DV * DK
+                               : (a.init_state ? a.init_state + chain * DV * DK : nullptr);
+        // where the part's end state goes: final_state after the last part; in
+        // the balanced schedule's first launch, the start of the first later part
+        Send = last ? (a.final_state ? a.final_state + chain * DV * DK : nullptr)
+                    : a.phase == 1 ? a.ws_s + ((size_t)(pslot + sp.kk) * a.hv + h) * DV * DK : nullptr;
 #pragma unroll
         for (int b = 0; b < NR; ++b) load_state<DK>(Sin, R0[b], ST[b]);
     } else {
         // every part but the last (its map is not needed to link), or every
-        // part for the affine map of whole sequences
-        if (a.aff_m ? p >= np : p >= np - 1) return;
+        // part for the affine map of whole sequences; in the balanced schedule
+        // not the first part either (its outputs give the next start state)
+        if (a.aff_m ? nc == 0 : last || (a.phase == 1 && p == 0)) return;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             ST[0][db] = zero4();
@@ -1101,7 +1159,7 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
             for (int i = 0; i < 4; ++i) ST[1][db][i] = (pi_dk(db, 4 * gq + i) == R0[1] + n) ? 1.f : 0.f;
         }
     }
-    const int64_t jb = p * L, je = (jb + L < nc) ? jb + L : nc;
+    const int64_t jb = sp.begin(p), je = sp.end(p);
     const int hq = (h * a.hqk) / a.hv;
     const int64_t cbase = span_base(s0, seq, kChunk);
     const unsigned kstride = (unsigned)(a.hqk * DK * E), vstride = (unsigned)(a.hv * DV * E);
@@ -1247,12 +1305,13 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
     };
 
     if constexpr (kPoisonLds) {
-        poison_lds(bufs, (int)sizeof(bufs), threadIdx.x, G::NT);
-        poison_lds(Pf, (int)sizeof(Pf), threadIdx.x, G::NT);
-        poison_lds(Ost, (int)sizeof(Ost), threadIdx.x, G::NT);
-        poison_lds(Kt, (int)sizeof(Kt), threadIdx.x, G::NT);
-        poison_lds(Pdg, (int)sizeof(Pdg), threadIdx.x, G::NT);
-        if constexpr (OUT && RAW) poison_lds(Nrm, (int)sizeof(Nrm), threadIdx.x, G::NT);
+        using SM = ChunkSmem<OP, DK, DV, OUT, RAW>;
+        poison_lds(bufs, (int)sizeof(SM::bufs), threadIdx.x, G::NT);
+        poison_lds(Pf, (int)sizeof(SM::Pf), threadIdx.x, G::NT);
+        poison_lds(Ost, (int)sizeof(SM::Ost), threadIdx.x, G::NT);
+        poison_lds(Kt, (int)sizeof(SM::Kt), threadIdx.x, G::NT);
+        poison_lds(Pdg, (int)sizeof(SM::Pdg), threadIdx.x, G::NT);
+        if constexpr (OUT && RAW) poison_lds(Nrm, (int)sizeof(SM::Nrm), threadIdx.x, G::NT);
         __syncthreads();
     }
     if constexpr (G::KTA) {
@@ -1297,13 +1356,49 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
     }
 
     if constexpr (OUT) {
-        if (p == np - 1 && a.final_state)
+        if (Send)
 #pragma unroll
-            for (int b = 0; b < NR; ++b) store_state<DK>(a.final_state + chain * DV * DK, R0[b], ST[b]);
+            for (int b = 0; b < NR; ++b) store_state<DK>(Send, R0[b], ST[b]);
     } else {
         if (w < NVB) store_state<DK>(a.ws_b + sblk * DV * DK, R0[0], ST[0]);
         if (w < NMB) store_transition<DK>(a.ws_m + sblk * DK * DK, R0[1], ST[1]);
     }
+}
+
+// Workgroup b: (part slot, value head) b of chunk_part.
+template <typename OP, int DK, int DV, bool OUT, bool RAW, bool SNAP = false>
+__global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) void gdn_chunk_kernel(PrefillArgs a) {
+    static_assert(ChunkGeom<OP, DK, DV, OUT>::NT == 64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16),
+                  "launch bound must equal the launch size");
+    // separate arrays (the compiler's own placement needs fewer registers than
+    // one ChunkSmem here)
+    using SM = ChunkSmem<OP, DK, DV, OUT, RAW>;
+    __shared__ decltype(SM::bufs) bufs;
+    __shared__ decltype(SM::Pf) Pf;
+    __shared__ decltype(SM::Ost) Ost;
+    __shared__ decltype(SM::Kt) Kt;
+    __shared__ decltype(SM::Nrm) Nrm;
+    __shared__ decltype(SM::Pdg) Pdg;
+    chunk_part<OP, DK, DV, OUT, RAW, SNAP>(a, blockIdx.x, ChunkLds<OP, DK, DV, OUT, RAW>{bufs, Pf, Ost, Kt, Nrm, Pdg});
+}
+
+// Phase 1 of the balanced schedule (d_k = d_v): workgroups [0, n) run the first
+// part of every sequence from init_state (outputs), workgroups [n, 2n) the
+// summaries, n = part slots x value heads.  The two kinds share the shared
+// memory, one at a time.
+template <typename OP, int D, bool RAW>
+__global__ __launch_bounds__(64 * D / 16) void gdn_chunk_first_kernel(PrefillArgs a) {
+    using SO = ChunkSmem<OP, D, D, true, RAW>;
+    using SS = ChunkSmem<OP, D, D, false, RAW>;
+    static_assert(ChunkGeom<OP, D, D, true>::NT == 64 * D / 16 && ChunkGeom<OP, D, D, false>::NT == 64 * D / 16,
+                  "both kinds use the launch size");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[sizeof(SO) > sizeof(SS) ? sizeof(SO) : sizeof(SS)];
+    const int64_t n = a.num_part_slots * a.hv;
+    if ((int64_t)blockIdx.x < n)
+        chunk_part<OP, D, D, true, RAW, false>(a, blockIdx.x, ChunkLds<OP, D, D, true, RAW>::of(*reinterpret_cast<SO*>(smem)));
+    else
+        chunk_part<OP, D, D, false, RAW, false>(a, (int64_t)blockIdx.x - n,
+                                                ChunkLds<OP, D, D, false, RAW>::of(*reinterpret_cast<SS*>(smem)));
 }
 
 // ===========================================================================
@@ -1343,8 +1438,16 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
     const SeqIndex si{a.cu, a.seqlen};
     const int64_t L = a.part_chunks;
     const int64_t s0 = si.start(seq), len = si.start(seq + 1) - s0;
-    const int64_t nc = (len + kChunk - 1) / kChunk, np = (nc + L - 1) / L;
-    const int64_t steps = aff ? np : np - 1;             // S_{p+1} = S_p M_p + B_p for p < steps
+    const int64_t nc = (len + kChunk - 1) / kChunk;
+    const SeqParts sp(nc, L, a.cut_chunks, a.first_slots);
+    // S_{j+1} = S_j M_j + B_j for slots j0 <= j < j0 + steps.  One pass over
+    // every part: from S_0 (init_state) over every part but the last (the
+    // affine map: from zero / the identity over every part).  Balanced
+    // schedule: from the start state of the first later part (slot kk, written
+    // by the first part's outputs) over the later parts but the last.
+    const bool bal = a.phase != 0;
+    const int64_t j0 = bal ? sp.kk : 0;
+    const int64_t steps = bal ? sp.ns - 1 - sp.kk : aff ? (nc > 0 ? sp.ns : 0) : (nc > 0 ? sp.ns - 1 : 0);
     const int R0 = trans ? 16 * (vb - NVB) : 16 * vb;
     float* const outp = !aff ? nullptr
                              : trans ? a.aff_m + (chain * DK + R0) * DK : a.aff_b + (chain * DV + R0) * DK;
@@ -1361,7 +1464,7 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
         poison_lds(Mb, (int)sizeof(Mb), tid, kLinkThreads);
         __syncthreads();
     }
-    const int64_t pbase = span_base(s0, seq, L * kChunk);
+    const int64_t pbase = span_base(s0, seq, L * kChunk) + j0;   // slot of step 0
 
     auto load_m = [&](int64_t p, int buf) {
         const float* M = a.ws_m + ((size_t)(pbase + p) * a.hv + h) * DK * DK;
@@ -1378,6 +1481,9 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) x[i] = R0 + row == c + i ? 1.f : 0.f;
             *reinterpret_cast<f32x4*>(&S[row][c]) = x;
+        } else if (bal) {
+            *reinterpret_cast<f32x4*>(&S[row][c]) =
+                *reinterpret_cast<const f32x4*>(a.ws_s + (((size_t)pbase * a.hv + h) * DV + R0 + row) * DK + c);
         } else {
             const f32x4 x = a.init_state ? *reinterpret_cast<const f32x4*>(a.init_state + (chain * DV + R0 + row) * DK + c) : zero4();
             *reinterpret_cast<f32x4*>(&S[row][c]) = x;
@@ -1473,23 +1579,48 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
     hipError_t e = launch_prep<OP, DK, RAW>(a, st);
     if (e != hipSuccess) return e;
     const unsigned parts = (unsigned)(a.num_part_slots * a.hv);
-    if (a.ws_m) {
+    if constexpr (DK == DV && sizeof(OP) == 2) {
+        if (a.phase != 0 && a.ws_m && !a.snapshots) {
+            // Balanced schedule: phase 1 runs the first part of every sequence
+            // (outputs; the whole sequence when it is not cut) in the same
+            // launch as the summaries of the cut sequences' other parts, the
+            // link gives the later parts' start states, and phase 2 runs the
+            // later parts.  The first parts, which need no start state, fill
+            // the compute units that a single pass leaves idle while the
+            // longest sequences finish.
+            PrefillArgs b = a;
+            b.phase = 1;
+            hipLaunchKernelGGL((gdn_chunk_first_kernel<OP, DK, RAW>), dim3(2 * parts),
+                               dim3(ChunkGeom<OP, DK, DV, true>::NT), 0, st, b);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            const unsigned links = (unsigned)(((int64_t)a.num_seqs * a.hv + kXcds - 1) / kXcds * kXcds * (DV / 16));
+            hipLaunchKernelGGL((gdn_link_kernel<DK, DV>), dim3(links), dim3(kLinkThreads), 0, st, a);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            b.phase = 2;
+            hipLaunchKernelGGL((gdn_chunk_kernel<OP, DK, DV, true, RAW>), dim3(parts),
+                               dim3(ChunkGeom<OP, DK, DV, true>::NT), 0, st, b);
+            return hipGetLastError();
+        }
+    }
+    PrefillArgs c = a;   // one output pass over every part
+    c.phase = 0;
+    if (c.ws_m) {
         hipLaunchKernelGGL((gdn_chunk_kernel<OP, DK, DV, false, RAW>), dim3(parts),
-                           dim3(ChunkGeom<OP, DK, DV, false>::NT), 0, st, a);
+                           dim3(ChunkGeom<OP, DK, DV, false>::NT), 0, st, c);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        const unsigned links = (unsigned)(((int64_t)a.num_seqs * a.hv + kXcds - 1) / kXcds * kXcds * (DV / 16));
-        hipLaunchKernelGGL((gdn_link_kernel<DK, DV>), dim3(links), dim3(kLinkThreads), 0, st, a);
+        const unsigned links = (unsigned)(((int64_t)c.num_seqs * c.hv + kXcds - 1) / kXcds * kXcds * (DV / 16));
+        hipLaunchKernelGGL((gdn_link_kernel<DK, DV>), dim3(links), dim3(kLinkThreads), 0, st, c);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if constexpr (!RAW) {   // snapshots come with the plain prefill only
-        if (a.snapshots) {
+        if (c.snapshots) {
             hipLaunchKernelGGL((gdn_chunk_kernel<OP, DK, DV, true, false, true>), dim3(parts),
-                               dim3(ChunkGeom<OP, DK, DV, true>::NT), 0, st, a);
+                               dim3(ChunkGeom<OP, DK, DV, true>::NT), 0, st, c);
             return hipGetLastError();
         }
     }
     hipLaunchKernelGGL((gdn_chunk_kernel<OP, DK, DV, true, RAW>), dim3(parts), dim3(ChunkGeom<OP, DK, DV, true>::NT),
-                       0, st, a);
+                       0, st, c);
     return hipGetLastError();
 }
 
@@ -1514,16 +1645,31 @@ hipError_t launch_prefill_dt(const PrefillArgs& a, int dk, int dv, hipStream_t s
 
 }  // namespace
 
-int64_t prefill_part_chunks(int64_t num_tokens, int num_seqs, int hv, int num_cus) {
+PartPlan prefill_part_plan(int64_t num_tokens, int num_seqs, int hv, int num_cus, bool balanced_ok) {
     const int64_t chunks = (num_tokens + kChunk - 1) / kChunk;
     const int64_t whole = chunks > 1 ? chunks : 1;             // no sequence has more chunks
     const int64_t chains = (int64_t)num_seqs * hv;
-    if (num_seqs <= 0 || chains >= num_cus) return whole;
-    // about one part per compute unit, at least kMinPartChunks chunks each
     constexpr int64_t kMinPartChunks = 6;
-    int64_t L = (chunks * hv + num_cus - 1) / (num_cus > 0 ? num_cus : 1);
-    L = L > kMinPartChunks ? L : kMinPartChunks;
-    return L < whole ? L : whole;
+    if (num_seqs <= 0 || num_cus <= 0) return {whole, 0, 1, 0};
+    if (chains < num_cus) {
+        // about one part per compute unit, at least kMinPartChunks chunks each
+        int64_t L = (chunks * hv + num_cus - 1) / num_cus;
+        L = L > kMinPartChunks ? L : kMinPartChunks;
+        return {L < whole ? L : whole, 0, 1, 0};
+    }
+    if (balanced_ok && num_seqs > 1 && chains <= 2 * (int64_t)num_cus) {
+        // share = chunk steps per compute unit.  A chain of more than one share
+        // keeps a first part of about one share (it needs no start state, so
+        // it runs beside the summaries) and is cut into parts of 0.2 shares
+        // after it, which run after the link.  (Chosen with a list-scheduling
+        // model of the two launches over random length mixes, and measured.)
+        const double share = (double)chunks * hv / num_cus;
+        int64_t L = (int64_t)(0.2 * share), cut = (int64_t)(1.0 * share);
+        L = L > kMinPartChunks ? L : kMinPartChunks;
+        cut = cut > L ? cut : L;
+        if (L < whole && cut < whole) return {L, cut, cut / L, 1};
+    }
+    return {whole, 0, 1, 0};
 }
 
 hipError_t launch_prefill_affine(const PrefillArgs& a, bool bf16, int dk, int dv, hipStream_t st) {

@@ -81,10 +81,14 @@ typedef struct gdn_shape {
 /*
  * Workspace.  Every prefill entry point needs device scratch memory: per
  * 64-token chunk and value head the chunk's triangular factor and gates
- * (about 6 KB for bf16, 13 KB for fp32), and, when a sequence is cut into
- * parts of L chunks because there are fewer (sequence, head) pairs than
- * compute units, per part and value head its transition, offset and start
- * state ((dk + 2 dv) * dk * 4 bytes).  Each entry point comes in two forms:
+ * (about 6 KB for bf16, 13 KB for fp32), and, when sequences are cut into
+ * parts, per part and value head its transition, offset and start state
+ * ((dk + 2 dv) * dk * 4 bytes).  Sequences are cut when there are fewer
+ * (sequence, value head) pairs than compute units (every sequence, into parts
+ * of about one compute unit's share), and on packed bf16 input with
+ * dk = dv and up to twice as many pairs as compute units (only the sequences
+ * longer than one share, so that the long ones do not leave the others' compute
+ * units idle).  Each entry point comes in two forms:
  *   gdn_prefill*_ws  take a caller-owned workspace and allocate nothing;
  *   gdn_prefill*     take it from the current device's default stream-ordered
  *                    memory pool (hipMallocAsync / hipFreeAsync on `stream`,

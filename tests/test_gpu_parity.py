@@ -166,6 +166,58 @@ def test_parts_equal_length_batch_without_offsets_in_place_state():
     assert eo <= 1e-2 and ef <= 1e-2
 
 
+# ------------------------------------------- the balanced schedule (packed bf16)
+# With between one and two (sequence, value head) chains per compute unit on
+# packed bf16 input (d_k = d_v), a sequence of more than one share of chunks
+# (share = chunk steps per compute unit) keeps a first part of about one share
+# and is cut into parts of 0.2 shares (at least 6 chunks) after it.  The first
+# parts run from init_state in the launch that also summarises the later
+# parts; their end states seed the link, and a second launch runs the later
+# parts.
+def _balanced_batch(seed, dk=128, raw=False):
+    """16 value heads and num_seqs x 16 = compute units: one 15000-token sequence and shorter ones,
+    empty and one-token ones among them.  At 256 compute units: share 34.75 chunks, parts of 6, first
+    parts of 30 chunks (5 slots); the long sequence has 35 later parts (34 link steps), the 3000- and
+    2900-token ones three (two steps), the 2600- and 2500-token ones two (one step)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    hv = 16
+    n = max(2, cus // hv)
+    tail = [1700, 3000, 0, 2600, 64, 1, 1700, 900, 2000, 130, 2900, 1200, 65, 1800, 2500]
+    lens = ([15000] + tail * ((n - 1) // len(tail) + 1))[:n]
+    return gi.make_inputs(gi.custom(dtype="bf16", Hqk=hv // 2, Hv=hv, dk=dk, dv=dk, seqlens=lens,
+                                    init_state="normal", raw=raw), seed=seed)
+
+
+@pytest.mark.parametrize("dk", [64, 128])
+@pytest.mark.parametrize("decay", [True, False])
+def test_balanced_schedule_packed_batch(dk, decay):
+    """Decay-free with small beta, the later parts' outputs depend on the linked start states."""
+    inp = _balanced_batch(80 + dk, dk=dk)
+    if not decay:
+        inp.g = np.zeros_like(inp.g)
+        inp.beta = (inp.beta * 0.1).astype(np.float32)
+    check_prefill(inp, label=f"balanced dk={dk} decay={decay}")
+
+
+def test_balanced_schedule_in_place_state():
+    """init_state and final_state are one buffer: the first parts read it in the first launch, the
+    last parts write it in the second."""
+    inp = _balanced_batch(82)
+    check_prefill(inp, label="balanced in place", out_alias=True)
+
+
+def test_balanced_schedule_raw_projections():
+    inp = _balanced_batch(83, raw=True)
+    _check_raw_prefill(inp, TOL["bf16"], "balanced raw")
+
+
+def test_balanced_schedule_bitwise_deterministic():
+    inp = _balanced_batch(84)
+    a = run_prefill(inp)
+    b = run_prefill(inp)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 # ------------------------------------------------------------- the workloads
 def test_tiny_f32_workload():
     """T=256, H=2, d=64, fp32 throughout, zero initial state, seed 0."""

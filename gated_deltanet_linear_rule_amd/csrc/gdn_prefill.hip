@@ -1404,8 +1404,9 @@ __global__ __launch_bounds__(64 * D / 16) void gdn_chunk_first_kernel(PrefillArg
 // ===========================================================================
 // link: start states of the parts, S_{p+1} = S_p M_p + B_p
 // ===========================================================================
-// One workgroup per (sequence, value head, 16-row block of the state); rows of
-// S never mix, so the blocks are independent.  S_0 (init_state or zeros) and
+// One workgroup per (sequence, value head, RB 16-row blocks of the state);
+// rows of S never mix, so the blocks are independent (the RB blocks of a
+// workgroup share the loads of M_p).  S_0 (init_state or zeros) and
 // every later S_p go to ws_s at the part's slot.  For the affine map of whole
 // sequences (aff_m set) the chain runs over every part from zero (offset
 // rows) and from the identity (transition rows, without B_p) and ends in
@@ -1413,25 +1414,30 @@ __global__ __launch_bounds__(64 * D / 16) void gdn_chunk_first_kernel(PrefillArg
 // column blocks w, w + 4, ... of S_{p+1} on the fp32 matrix cores.  M_p does
 // not depend on S, so M_{p+1} streams into the second LDS buffer (direct
 // loads) while step p computes: a step waits for one load, not a chain of them.
-template <int DK, int DV>
-__global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
+template <int DK, int DV, int RB = 1>
+__global__ __launch_bounds__(kLinkThreads * RB) void gdn_link_kernel(PrefillArgs a) {
     constexpr int NVB = DV / 16, NDB = DK / 16, NKK = DK / 32, LD = DK + 4;
     constexpr int NWV = kLinkThreads / kWave, PER = (NDB + NWV - 1) / NWV;
     constexpr int MI = DK * DK * 4 / 1024;               // 1 KB direct loads per M
-    static_assert(MI % NWV == 0, "M loads per wave");
-    __shared__ float S[16][LD];
+    static_assert(MI % (NWV * RB) == 0, "M loads per wave");
+    static_assert(NVB % RB == 0 && NDB % RB == 0, "row blocks of a workgroup are all offset or all transition rows");
+    __shared__ float Sall[RB][16][LD];
     __shared__ float Mb[2][DK * DK];                      // M_p, transposed (m_pos)
-    const int tid = threadIdx.x, l = lane_id(), w = wave_id(), n = l & 15, gq = l >> 4;
+    // RB row blocks per workgroup (kLinkThreads threads each), sharing M_p
+    const int l = lane_id(), n = l & 15, gq = l >> 4;
+    const int sub = wave_id() / NWV, w = wave_id() - sub * NWV, tid = (int)threadIdx.x - sub * kLinkThreads;
+    float (&S)[16][LD] = Sall[sub];
     // affine map: row blocks 0 .. NVB - 1 are offset rows (from zero, + B_p),
     // NVB .. NVB + NDB - 1 transition rows (from the identity, no B_p)
     const bool aff = a.aff_m != nullptr;
     const int NBK = aff ? NVB + NDB : NVB;
-    // Workgroup b takes row block b / C of chain b mod C (C = chains rounded up
-    // to a multiple of the 8 XCDs): all row blocks of a chain then run on one
-    // XCD, and every M_p they all load comes from that XCD's L2 after the first.
+    // Workgroup b takes row blocks RB (b / C) .. + RB - 1 of chain b mod C (C =
+    // chains rounded up to a multiple of the 8 XCDs): all row blocks of a chain
+    // then run on one XCD, and every M_p they all load comes from that XCD's L2
+    // after the first.
     const int64_t nchain = (int64_t)a.num_seqs * a.hv, C = (nchain + kXcds - 1) / kXcds * kXcds;
-    const int vb = (int)(blockIdx.x / C);
-    const int64_t chain = blockIdx.x - (int64_t)vb * C;
+    const int vg = (int)(blockIdx.x / C), vb = RB * vg + sub;
+    const int64_t chain = blockIdx.x - (int64_t)vg * C;
     if (chain >= nchain) return;
     const bool trans = vb >= NVB;
     const int seq = (int)(chain / a.hv), h = (int)(chain - (int64_t)seq * a.hv);
@@ -1460,8 +1466,8 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
     }
     if (steps <= 0) return;
     if constexpr (kPoisonLds) {
-        poison_lds(S, (int)sizeof(S), tid, kLinkThreads);
-        poison_lds(Mb, (int)sizeof(Mb), tid, kLinkThreads);
+        poison_lds(Sall, (int)sizeof(Sall), (int)threadIdx.x, kLinkThreads * RB);
+        poison_lds(Mb, (int)sizeof(Mb), (int)threadIdx.x, kLinkThreads * RB);
         __syncthreads();
     }
     const int64_t pbase = span_base(s0, seq, L * kChunk) + j0;   // slot of step 0
@@ -1470,7 +1476,7 @@ __global__ __launch_bounds__(kLinkThreads) void gdn_link_kernel(PrefillArgs a) {
         const float* M = a.ws_m + ((size_t)(pbase + p) * a.hv + h) * DK * DK;
         const auto rm = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(M), 0, DK * DK * 4, 0x00020000);
 #pragma unroll
-        for (int k = 0; k < MI / NWV; ++k) bytes_to_lds(&Mb[buf][0], rm, w + NWV * k);
+        for (int k = 0; k < MI / (NWV * RB); ++k) bytes_to_lds(&Mb[buf][0], rm, wave_id() + NWV * RB * k);
     };
     load_m(0, 0);
     for (int e = tid; e < 16 * DK / 4; e += kLinkThreads) {
@@ -1593,8 +1599,11 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
             hipLaunchKernelGGL((gdn_chunk_first_kernel<OP, DK, RAW>), dim3(2 * parts),
                                dim3(ChunkGeom<OP, DK, DV, true>::NT), 0, st, b);
             if ((e = hipGetLastError()) != hipSuccess) return e;
-            const unsigned links = (unsigned)(((int64_t)a.num_seqs * a.hv + kXcds - 1) / kXcds * kXcds * (DV / 16));
-            hipLaunchKernelGGL((gdn_link_kernel<DK, DV>), dim3(links), dim3(kLinkThreads), 0, st, a);
+            // two row blocks per workgroup: the link's workgroups hold 140 KB of
+            // shared memory (one per compute unit), and here many chains link
+            // at once
+            const unsigned links = (unsigned)(((int64_t)a.num_seqs * a.hv + kXcds - 1) / kXcds * kXcds * (DV / 32));
+            hipLaunchKernelGGL((gdn_link_kernel<DK, DV, 2>), dim3(links), dim3(2 * kLinkThreads), 0, st, a);
             if ((e = hipGetLastError()) != hipSuccess) return e;
             b.phase = 2;
             hipLaunchKernelGGL((gdn_chunk_kernel<OP, DK, DV, true, RAW>), dim3(parts),

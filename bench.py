@@ -113,7 +113,8 @@ def measured_traffic(name, sources):
 
 
 CALIB_BYTES = 1 << 30      # bytes read and bytes written by the calibration kernel
-KERNELS = {"gdn_prefill": ("gdn_prep_kernel", "gdn_chunk_kernel<summary>", "gdn_link_kernel", "gdn_chunk_kernel<output>"),
+KERNELS = {"gdn_prefill": ("gdn_prep_kernel", "gdn_chunk_kernel<summary>", "gdn_chunk_first_kernel", "gdn_link_kernel",
+                           "gdn_chunk_kernel<output>"),
            "gdn_decode": ("gdn_decode_kernel",)}
 
 
@@ -169,15 +170,15 @@ def write_traffic_summary(fetch_csv, write_csv, prefill_calls):
         per = {}
         total = 0.0
         agg = (lambda t, p: per_call(t, p, prefill_calls)) if call == "gdn_prefill" else mean_of
-        for kn in kernels:
+        for kn in kernels:   # (a schedule runs some of the call's kernels only)
             f, nf = agg(fetch, lambda n, kn=kn: _kernel_matches(kn, n))
             w, nw = agg(write, lambda n, kn=kn: _kernel_matches(kn, n))
             if f is None or w is None:
-                break
+                continue
             rb, wb = f * 1024 * sf, w * 1024 * sw
             per[kn] = {"read_bytes": rb, "write_bytes": wb, "dispatches": min(nf, nw)}
             total += rb + wb
-        else:
+        if per:
             srcs = PREFILL_SOURCES if call == "gdn_prefill" else DECODE_SOURCES
             rec[call] = {"bytes_per_call": total, "kernels": per, "source_sha": _sha(srcs)}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
@@ -195,6 +196,55 @@ SQ_PASSES = (
      "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_ACTIVE_INST_SCA", "SQ_INSTS_SMEM"),
 )
 XCDS, CUS, SIMDS = 8, 256, 1024
+
+
+def part_plan(wl, cus=CUS):
+    """The library's part plan for a workload on a `cus`-CU device (mirrors prefill_part_plan and
+    SeqParts in gdn_prefill.hip): per sequence, the chunk counts of its first part and of its later
+    parts, and whether the balanced schedule runs."""
+    chunks = -(-wl.total_tokens // 64)
+    whole = max(chunks, 1)
+    chains = wl.num_seqs * wl.num_v_heads
+    L, cut, first, balanced = whole, 0, 1, False
+    if chains < cus:
+        L = min(max(-(-chunks * wl.num_v_heads // cus), 6), whole)
+    elif (wl.dtype == "bf16" and wl.num_seqs > 1 and wl.head_dim_k == wl.head_dim_v and chains <= 2 * cus
+          and (wl.packed or wl.num_seqs > 1)):
+        share = chunks * wl.num_v_heads / cus
+        Lb, cb = max(int(0.2 * share), 6), int(1.0 * share)
+        cb = max(cb, Lb)
+        if Lb < whole and cb < whole:
+            L, cut, first, balanced = Lb, cb, cb // Lb, True
+    seqs = []
+    for n in wl.seqlens:
+        nc = -(-n // 64)
+        ns = max(-(-nc // L), 1)
+        kk = min(first, ns) if nc > cut else ns
+        head = min(kk * L, nc)
+        seqs.append((head, [min((j + 1) * L, nc) - j * L for j in range(kk, ns)]))
+    return seqs, balanced
+
+
+def wave_chunks(wl):
+    """Chunk steps summed over the working waves of each chunk kernel in one prefill call (every wave
+    of a part's workgroup runs the part's chunks; d_k = d_v here or d_v waves for outputs and
+    max(d_k, d_v) for summaries)."""
+    seqs, balanced = part_plan(wl)
+    nwo, nws = wl.head_dim_v // 16, max(wl.head_dim_v, wl.head_dim_k) // 16
+    H = wl.num_v_heads
+    if balanced:
+        # first launch: first parts (outputs) and the later parts' summaries but the last's
+        first = sum(h for h, _ in seqs) * H * nwo + sum(sum(r[:-1]) for _, r in seqs) * H * nws
+        later = sum(sum(r) for _, r in seqs) * H * nwo
+        return {"gdn_chunk_first_kernel": first, "gdn_chunk_kernel<output>": later}
+    # one pass over every part; with no later parts the sequence is one part.  Summaries: every
+    # part but the last (the first part of a cut sequence is the first slot, the rest follow)
+    out = sum(h + sum(r) for h, r in seqs) * H * nwo
+    summ = sum((h + sum(r[:-1])) if r else 0 for h, r in seqs) * H * nws
+    wcs = {"gdn_chunk_kernel<output>": out}
+    if summ:
+        wcs["gdn_chunk_kernel<summary>"] = summ
+    return wcs
 
 
 def write_sq_summary(csvs, workload, calls, wave_chunks):
@@ -318,20 +368,7 @@ def main():
         # chunk steps per wave: every wave of a part's workgroup runs the part's chunks; parts are
         # 64 L tokens, L as the library chooses on a 256-CU device (one part per sequence when the
         # (sequence, head) chains alone fill it)
-        total_chunks = sum((n + 63) // 64 for n in wl.seqlens)
-        chains = wl.num_seqs * wl.num_v_heads
-        per_seq = [(n + 63) // 64 for n in wl.seqlens]
-        if chains >= CUS:
-            L = max(per_seq)
-        else:
-            L = min(max(8, -(-total_chunks * wl.num_v_heads // CUS)), max(per_seq))
-        parts = [max(1, -(-c // L)) for c in per_seq]
-        out_chunks = sum(per_seq) * wl.num_v_heads
-        sum_chunks = sum(c - min(c, c - (p - 1) * L) for c, p in zip(per_seq, parts)) * wl.num_v_heads
-        wcs = {"gdn_chunk_kernel<output>": out_chunks * (wl.head_dim_v // 16)}
-        if sum_chunks:
-            wcs["gdn_chunk_kernel<summary>"] = sum_chunks * (max(wl.head_dim_v, wl.head_dim_k) // 16)
-        write_sq_summary(args.sq_summary, args.prefill_workload, args.prefill_calls, wcs)
+        write_sq_summary(args.sq_summary, args.prefill_workload, args.prefill_calls, wave_chunks(wl))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the GDN path here is single-GPU); got --gpus {args.gpus}",

@@ -510,7 +510,7 @@ def main():
     other = None
     if not args.no_variants and headline:
         other = {}
-        for name, reps in (("prefill_4k", 50), ("varlen_8x", 10)):
+        for name, reps in (("prefill_4k", 50), ("varlen_8x", 50)):
             o_inp = gi.make_inputs(name, seed=0)
             ow = o_inp.wl
             oq, ok, ov, og, ob = (dev(x) for x in (o_inp.q, o_inp.k, o_inp.v, o_inp.g, o_inp.beta))

@@ -223,21 +223,21 @@ gdn_status plan_prefill(const gdn_shape* shape, bool packed, PrefillKind kind, g
     if (a.num_slots > INT32_MAX) return fail(GDN_ERROR_NOT_SUPPORTED, "too many chunks");
     const int cus = current_compute_units();
     if (cus <= 0) return fail(GDN_ERROR_LAUNCH, "cannot query the device's compute units");
-    // the balanced schedule: plain and raw-projection calls on packed bf16
-    // sequences with d_k = d_v
+    // the two-launch schedule of packed batches: plain and raw-projection calls,
+    // bf16, d_k = d_v
     const gdn::PartPlan pp = gdn::prefill_part_plan(
         a.num_tokens, a.num_seqs, a.hv, cus,
-        packed && (kind == kPlain || kind == kRaw) && shape->head_dim_k == shape->head_dim_v &&
-            shape->dtype == GDN_DTYPE_BF16);
+        (kind == kPlain || kind == kRaw) && shape->head_dim_k == shape->head_dim_v && shape->dtype == GDN_DTYPE_BF16,
+        packed);
     a.part_chunks = pp.part_chunks;
+    a.first_chunks = pp.first_chunks;
     a.cut_chunks = pp.cut_chunks;
-    a.first_slots = pp.first_slots;
     a.phase = pp.phase;
     const int64_t span = a.part_chunks * 64;
     a.num_part_slots = (a.num_tokens + span - 1) / span + a.num_seqs;
     const int64_t longest = packed ? (a.num_tokens + 63) / 64 : (a.seqlen + 63) / 64;
     // the affine map needs every sequence's part maps, split or not
-    split = kind == kAffine || a.part_chunks < longest;
+    split = kind == kAffine || longest > (a.first_chunks > a.cut_chunks ? a.first_chunks : a.cut_chunks);
     if (2 * a.num_part_slots * a.hv > INT32_MAX ||
         (a.num_seqs * (int64_t)a.hv + 7) * (a.dv / 16 + shape->head_dim_k / 16) > INT32_MAX)
         return fail(GDN_ERROR_NOT_SUPPORTED, "too many (part, head) pairs");

@@ -42,12 +42,13 @@ struct PrefillArgs {
     int32_t dv;
     int64_t num_slots;         // chunk slots: ceil(num_tokens / 64) + num_seqs
     int64_t part_chunks;       // L: chunks per part
-    int64_t cut_chunks;        // sequences of more chunks than this are cut: their first part
-    int64_t first_slots;       // takes first_slots slots of L chunks, every later slot is a
-                               // part; other sequences are one part (0 and 1: parts of L)
+    int64_t first_chunks;      // F: chunks of a cut sequence's first part (later parts: L)
+    int64_t cut_chunks;        // sequences of at most this many chunks (or of at most F) are
+                               // one part
     int64_t num_part_slots;    // part slots: ceil(num_tokens / (64 L)) + num_seqs
-    int32_t phase;             // 0: one output pass over every part; 1: balanced schedule
-                               // (first parts beside the summaries, later parts after the link)
+    int32_t phase;             // 0: one output pass over every part; 1: two launches (first
+                               // parts beside the later parts' summaries, later parts after
+                               // the link)
     // Workspace.  Per (chunk slot, value head), written by the prep kernel:
     void* ws_t;                // T~ = (I + A)^{-1} diag(beta) without its diagonal, as operand
                                // fragments (5 KB bf16, 12 KB fp32)
@@ -90,17 +91,18 @@ struct PrefillWorkspace {
 };
 
 // How a prefill call cuts its sequences into parts (PrefillArgs::part_chunks,
-// cut_chunks, first_slots, phase).  With fewer (sequence, value head) chains
-// than compute units every sequence is cut into parts of about one compute
-// unit's share.  With up to twice as many chains as compute units (packed bf16,
-// d_k = d_v: balanced_ok) the sequences longer than one share keep a first
-// part of about one share and are cut into short parts after it, and the
-// balanced schedule runs.  Otherwise every sequence is one part.
+// first_chunks, cut_chunks, phase).  two_launch: bf16, d_k = d_v, plain or
+// raw-projection call; packed: cu_seqlens given.  With fewer (sequence, value
+// head) chains than compute units every sequence is cut into parts of about
+// one compute unit's share.  With one to two chains per compute unit on packed
+// two_launch input, the sequences longer than one share keep a first part of
+// about one share and are cut into short parts after it (two launches).
+// Otherwise every sequence is one part.
 struct PartPlan {
-    int64_t part_chunks, cut_chunks, first_slots;
+    int64_t part_chunks, first_chunks, cut_chunks;
     int32_t phase;
 };
-PartPlan prefill_part_plan(int64_t num_tokens, int num_seqs, int hv, int num_cus, bool balanced_ok);
+PartPlan prefill_part_plan(int64_t num_tokens, int num_seqs, int hv, int num_cus, bool two_launch, bool packed);
 
 // Launchers: return hipSuccess or the launch error.  `bf16` selects the
 // element type of q/k/v/out; dk/dv are 64 or 128.

@@ -94,20 +94,22 @@ __host__ __device__ constexpr int tri_half_elem(int f, int lane) { return 4 * 51
 // distinct and increase with (n, j); sequence n owns
 // [base(n), base(n) + max(1, ceil(len / span))), so ceil(tokens / span) + N
 // slots cover every sequence.  An empty sequence owns one slot.
-__device__ __forceinline__ int64_t span_base(int64_t start, int n, int64_t span) { return start / span + n; }
+__device__ __forceinline__ int64_t span_base(int64_t start, int n, int64_t span, int per = 1) {
+    return start / span + (int64_t)per * n;
+}
 
 // Sequence owning slot `slot` and the slot's index within it (may be past the
 // sequence's last part: a gap).
 __device__ __forceinline__ void locate_span(const SeqIndex& si, int nseq, int64_t span, int64_t slot, int& n_out,
-                                            int64_t& idx) {
+                                            int64_t& idx, int per = 1) {
     int lo = 0, hi = nseq - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (span_base(si.start(mid), mid, span) <= slot) lo = mid;
+        if (span_base(si.start(mid), mid, span, per) <= slot) lo = mid;
         else hi = mid - 1;
     }
     n_out = lo;
-    idx = slot - span_base(si.start(lo), lo, span);
+    idx = slot - span_base(si.start(lo), lo, span, per);
 }
 
 // Lane shuffle of a double by a DPP control (two 32-bit halves); lanes whose
@@ -1053,24 +1055,23 @@ struct ChunkLds {
     __device__ static ChunkLds of(ChunkSmem<OP, DK, DV, OUT, RAW>& m) { return {m.bufs, m.Pf, m.Ost, m.Kt, m.Nrm, m.Pdg}; }
 };
 
-// The parts of a sequence of nc chunks on its ns = ceil(nc / L) slots of L
-// chunks (one slot when it is empty).  The first part takes slots [0, kk)
-// (chunks [0, min(kk L, nc))) and every later slot j is a part of its own
-// (chunks [j L, min(j L + L, nc))); slots 1 .. kk - 1 are gaps.  A sequence of
-// more than `cut` chunks has kk = min(first_slots, ns), any other is one part
-// (kk = ns).  One pass over every part: cut = 0, first_slots = 1.
+// The parts of a sequence of nc chunks (one part of no chunks when it is
+// empty).  A sequence of at most `cut` chunks, or of at most F, is one part;
+// any other has a first part of F chunks and later parts of L chunks (the last
+// one shorter): part j >= 1 holds chunks [F + (j - 1) L, min(F + j L, nc)).
+// One pass over every part: F = L, cut = 0.  Part j of sequence n has part
+// slot span_base(start(n), n, 64 L) + j; with F >= L a sequence of len tokens
+// has at most ceil(len / (64 L)) parts, which its slots cover.
+constexpr int kPartSlotsPerSeq = 1;
 struct SeqParts {
-    int64_t nc, L, ns, kk;
-    __device__ SeqParts(int64_t nc_, int64_t L_, int64_t cut, int64_t first_slots) : nc(nc_), L(L_) {
-        ns = nc > 0 ? (nc + L - 1) / L : 1;
-        kk = nc > cut ? (first_slots < ns ? first_slots : ns) : ns;
+    int64_t nc, L, F, np;
+    __device__ SeqParts(int64_t nc_, int64_t L_, int64_t F_, int64_t cut) : nc(nc_), L(L_), F(F_) {
+        np = (nc <= cut || nc <= F) ? 1 : 1 + (nc - F + L - 1) / L;
     }
-    __device__ bool is_part(int64_t j) const { return j == 0 || (j >= kk && j < ns); }
-    __device__ int64_t last() const { return ns > kk ? ns - 1 : 0; }
-    __device__ int64_t begin(int64_t j) const { return j * L; }
+    __device__ int64_t begin(int64_t j) const { return j == 0 ? 0 : F + (j - 1) * L; }
     __device__ int64_t end(int64_t j) const {
-        const int64_t e = j == 0 ? kk * L : j * L + L;
-        return e < nc ? e : nc;
+        const int64_t e = F + j * L;
+        return np == 1 || e > nc ? nc : e;
     }
 };
 
@@ -1104,12 +1105,12 @@ __device__ __forceinline__ void chunk_part(const PrefillArgs& a, int64_t item, c
     const int64_t L = a.part_chunks;
     int seq;
     int64_t p;
-    locate_span(si, a.num_seqs, L * kChunk, pslot, seq, p);
+    locate_span(si, a.num_seqs, L * kChunk, pslot, seq, p, kPartSlotsPerSeq);
     const int64_t s0 = si.start(seq), len = si.start(seq + 1) - s0;
     const int64_t nc = (len + kChunk - 1) / kChunk;
-    const SeqParts sp(nc, L, a.cut_chunks, a.first_slots);
-    if (p < 0 || !sp.is_part(p)) return;                        // gap slot
-    const bool last = p == sp.last();
+    const SeqParts sp(nc, L, a.first_chunks, a.cut_chunks);
+    if (p < 0 || p >= sp.np) return;                            // gap slot
+    const bool last = p == sp.np - 1;
     if (OUT && (a.phase == 1 ? p != 0 : a.phase == 2 && p == 0)) return;   // the other phase's part
     const int64_t chain = (int64_t)seq * a.hv + h;
     const size_t sblk = (size_t)pslot * a.hv + h;
@@ -1138,13 +1139,13 @@ __device__ __forceinline__ void chunk_part(const PrefillArgs& a, int64_t item, c
         }
         // the part's start state: written by the link (one pass over more than
         // one part, and the later parts of the balanced schedule), else init_state
-        const float* Sin = a.phase == 2 || (a.phase == 0 && sp.ns > 1)
+        const float* Sin = a.phase == 2 || (a.phase == 0 && sp.np > 1)
                                ? a.ws_s + sblk * DV * DK
                                : (a.init_state ? a.init_state + chain * DV * DK : nullptr);
         // where the part's end state goes: final_state after the last part; in
         // the balanced schedule's first launch, the start of the first later part
         Send = last ? (a.final_state ? a.final_state + chain * DV * DK : nullptr)
-                    : a.phase == 1 ? a.ws_s + ((size_t)(pslot + sp.kk) * a.hv + h) * DV * DK : nullptr;
+                    : a.phase == 1 ? a.ws_s + ((size_t)(pslot + 1) * a.hv + h) * DV * DK : nullptr;
 #pragma unroll
         for (int b = 0; b < NR; ++b) load_state<DK>(Sin, R0[b], ST[b]);
     } else {
@@ -1445,15 +1446,15 @@ __global__ __launch_bounds__(kLinkThreads * RB) void gdn_link_kernel(PrefillArgs
     const int64_t L = a.part_chunks;
     const int64_t s0 = si.start(seq), len = si.start(seq + 1) - s0;
     const int64_t nc = (len + kChunk - 1) / kChunk;
-    const SeqParts sp(nc, L, a.cut_chunks, a.first_slots);
-    // S_{j+1} = S_j M_j + B_j for slots j0 <= j < j0 + steps.  One pass over
+    const SeqParts sp(nc, L, a.first_chunks, a.cut_chunks);
+    // S_{j+1} = S_j M_j + B_j for parts j0 <= j < j0 + steps.  One pass over
     // every part: from S_0 (init_state) over every part but the last (the
-    // affine map: from zero / the identity over every part).  Balanced
-    // schedule: from the start state of the first later part (slot kk, written
-    // by the first part's outputs) over the later parts but the last.
+    // affine map: from zero / the identity over every part).  Two launches:
+    // from S_1 (written by the first part's outputs) over the later parts but
+    // the last.
     const bool bal = a.phase != 0;
-    const int64_t j0 = bal ? sp.kk : 0;
-    const int64_t steps = bal ? sp.ns - 1 - sp.kk : aff ? (nc > 0 ? sp.ns : 0) : (nc > 0 ? sp.ns - 1 : 0);
+    const int64_t j0 = bal ? 1 : 0;
+    const int64_t steps = bal ? sp.np - 2 : aff ? (nc > 0 ? sp.np : 0) : (nc > 0 ? sp.np - 1 : 0);
     const int R0 = trans ? 16 * (vb - NVB) : 16 * vb;
     float* const outp = !aff ? nullptr
                              : trans ? a.aff_m + (chain * DK + R0) * DK : a.aff_b + (chain * DV + R0) * DK;
@@ -1470,7 +1471,7 @@ __global__ __launch_bounds__(kLinkThreads * RB) void gdn_link_kernel(PrefillArgs
         poison_lds(Mb, (int)sizeof(Mb), (int)threadIdx.x, kLinkThreads * RB);
         __syncthreads();
     }
-    const int64_t pbase = span_base(s0, seq, L * kChunk) + j0;   // slot of step 0
+    const int64_t pbase = span_base(s0, seq, L * kChunk, kPartSlotsPerSeq) + j0;   // slot of step 0
 
     auto load_m = [&](int64_t p, int buf) {
         const float* M = a.ws_m + ((size_t)(pbase + p) * a.hv + h) * DK * DK;
@@ -1654,19 +1655,23 @@ hipError_t launch_prefill_dt(const PrefillArgs& a, int dk, int dv, hipStream_t s
 
 }  // namespace
 
-PartPlan prefill_part_plan(int64_t num_tokens, int num_seqs, int hv, int num_cus, bool balanced_ok) {
+PartPlan prefill_part_plan(int64_t num_tokens, int num_seqs, int hv, int num_cus, bool two_launch, bool packed) {
     const int64_t chunks = (num_tokens + kChunk - 1) / kChunk;
     const int64_t whole = chunks > 1 ? chunks : 1;             // no sequence has more chunks
     const int64_t chains = (int64_t)num_seqs * hv;
     constexpr int64_t kMinPartChunks = 6;
-    if (num_seqs <= 0 || num_cus <= 0) return {whole, 0, 1, 0};
+    if (num_seqs <= 0 || num_cus <= 0) return {whole, whole, 0, 0};
     if (chains < num_cus) {
-        // about one part per compute unit, at least kMinPartChunks chunks each
+        // about one part per compute unit, at least kMinPartChunks chunks each.
+        // (A short first part whose outputs run beside the other parts'
+        // summaries measured slower: among summary workgroups an output
+        // workgroup's chunk step took about twice as long.)
         int64_t L = (chunks * hv + num_cus - 1) / num_cus;
         L = L > kMinPartChunks ? L : kMinPartChunks;
-        return {L < whole ? L : whole, 0, 1, 0};
+        L = L < whole ? L : whole;
+        return {L, L, 0, 0};
     }
-    if (balanced_ok && num_seqs > 1 && chains <= 2 * (int64_t)num_cus) {
+    if (two_launch && packed && num_seqs > 1 && chains <= 2 * (int64_t)num_cus) {
         // share = chunk steps per compute unit.  A chain of more than one share
         // keeps a first part of about one share (it needs no start state, so
         // it runs beside the summaries) and is cut into parts of 0.2 shares
@@ -1676,9 +1681,9 @@ PartPlan prefill_part_plan(int64_t num_tokens, int num_seqs, int hv, int num_cus
         int64_t L = (int64_t)(0.2 * share), cut = (int64_t)(1.0 * share);
         L = L > kMinPartChunks ? L : kMinPartChunks;
         cut = cut > L ? cut : L;
-        if (L < whole && cut < whole) return {L, cut, cut / L, 1};
+        if (L < whole && cut < whole) return {L, cut / L * L, cut, 1};
     }
-    return {whole, 0, 1, 0};
+    return {whole, whole, 0, 0};
 }
 
 hipError_t launch_prefill_affine(const PrefillArgs& a, bool bf16, int dk, int dv, hipStream_t st) {

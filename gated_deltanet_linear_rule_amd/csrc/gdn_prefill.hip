@@ -94,22 +94,20 @@ __host__ __device__ constexpr int tri_half_elem(int f, int lane) { return 4 * 51
 // distinct and increase with (n, j); sequence n owns
 // [base(n), base(n) + max(1, ceil(len / span))), so ceil(tokens / span) + N
 // slots cover every sequence.  An empty sequence owns one slot.
-__device__ __forceinline__ int64_t span_base(int64_t start, int n, int64_t span, int per = 1) {
-    return start / span + (int64_t)per * n;
-}
+__device__ __forceinline__ int64_t span_base(int64_t start, int n, int64_t span) { return start / span + n; }
 
 // Sequence owning slot `slot` and the slot's index within it (may be past the
 // sequence's last part: a gap).
 __device__ __forceinline__ void locate_span(const SeqIndex& si, int nseq, int64_t span, int64_t slot, int& n_out,
-                                            int64_t& idx, int per = 1) {
+                                            int64_t& idx) {
     int lo = 0, hi = nseq - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (span_base(si.start(mid), mid, span, per) <= slot) lo = mid;
+        if (span_base(si.start(mid), mid, span) <= slot) lo = mid;
         else hi = mid - 1;
     }
     n_out = lo;
-    idx = slot - span_base(si.start(lo), lo, span, per);
+    idx = slot - span_base(si.start(lo), lo, span);
 }
 
 // Lane shuffle of a double by a DPP control (two 32-bit halves); lanes whose
@@ -1062,7 +1060,6 @@ struct ChunkLds {
 // One pass over every part: F = L, cut = 0.  Part j of sequence n has part
 // slot span_base(start(n), n, 64 L) + j; with F >= L a sequence of len tokens
 // has at most ceil(len / (64 L)) parts, which its slots cover.
-constexpr int kPartSlotsPerSeq = 1;
 struct SeqParts {
     int64_t nc, L, F, np;
     __device__ SeqParts(int64_t nc_, int64_t L_, int64_t F_, int64_t cut) : nc(nc_), L(L_), F(F_) {
@@ -1080,7 +1077,8 @@ struct SeqParts {
 // OUT = true: outputs of every part, from ws_s (np > 1) or init_state (np = 1);
 // the last part writes final_state; SNAP: also the state snapshots.  In the
 // balanced schedule (a.phase 1 and 2, see launch_prefill_t) the first part of
-// every sequence runs in phase 1 from init_state, the later parts in phase 2.
+// every sequence runs in phase 1 from init_state and leaves its end state as
+// the second part's start state; the later parts run in phase 2.
 template <typename OP, int DK, int DV, bool OUT, bool RAW, bool SNAP>
 __device__ __forceinline__ void chunk_part(const PrefillArgs& a, int64_t item, const ChunkLds<OP, DK, DV, OUT, RAW>& sm) {
     using G = ChunkGeom<OP, DK, DV, OUT>;
@@ -1105,7 +1103,7 @@ __device__ __forceinline__ void chunk_part(const PrefillArgs& a, int64_t item, c
     const int64_t L = a.part_chunks;
     int seq;
     int64_t p;
-    locate_span(si, a.num_seqs, L * kChunk, pslot, seq, p, kPartSlotsPerSeq);
+    locate_span(si, a.num_seqs, L * kChunk, pslot, seq, p);
     const int64_t s0 = si.start(seq), len = si.start(seq + 1) - s0;
     const int64_t nc = (len + kChunk - 1) / kChunk;
     const SeqParts sp(nc, L, a.first_chunks, a.cut_chunks);
@@ -1471,7 +1469,7 @@ __global__ __launch_bounds__(kLinkThreads * RB) void gdn_link_kernel(PrefillArgs
         poison_lds(Mb, (int)sizeof(Mb), (int)threadIdx.x, kLinkThreads * RB);
         __syncthreads();
     }
-    const int64_t pbase = span_base(s0, seq, L * kChunk, kPartSlotsPerSeq) + j0;   // slot of step 0
+    const int64_t pbase = span_base(s0, seq, L * kChunk) + j0;   // slot of step 0
 
     auto load_m = [&](int64_t p, int buf) {
         const float* M = a.ws_m + ((size_t)(pbase + p) * a.hv + h) * DK * DK;

@@ -211,6 +211,26 @@ def test_balanced_schedule_raw_projections():
     _check_raw_prefill(inp, TOL["bf16"], "balanced raw")
 
 
+@pytest.mark.parametrize("i", range(6))
+def test_balanced_schedule_seeded_batches(i):
+    """Seeded packed batches with one to two (sequence, value head) chains per compute unit: mostly
+    short sequences (some empty or one token), one to three long ones, d = 64 or 128, grouped value
+    heads, with initial state; every cut falls where the lengths put it."""
+    rng = np.random.default_rng(900 + i)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    hv = int(rng.choice([16, 32]))
+    hqk = hv // int(rng.choice([1, 2]))
+    dk = int(rng.choice([64, 128]))
+    n = int(rng.integers(cus // hv, 2 * cus // hv + 1))
+    lens = [int(x) for x in rng.integers(0, 1500, size=n)]
+    lens[int(rng.integers(0, n))] = int(rng.integers(0, 2))
+    for j in rng.choice(n, size=int(rng.integers(1, 4)), replace=False):
+        lens[int(j)] = int(rng.integers(4000, 12000))
+    inp = gi.make_inputs(gi.custom(dtype="bf16", Hqk=hqk, Hv=hv, dk=dk, dv=dk, seqlens=lens,
+                                   init_state="normal"), seed=910 + i)
+    check_prefill(inp, label=f"balanced seeded {i}: N={n} Hv={hv} Hqk={hqk} d={dk} longest {max(lens)}")
+
+
 def test_balanced_schedule_bitwise_deterministic():
     inp = _balanced_batch(84)
     a = run_prefill(inp)

@@ -32,6 +32,13 @@
 //  * gdn_chunk_kernel<output> runs every part from its true start state and
 //    writes the outputs (and the final state, from the last part).
 //
+// Packed batches whose chains alone fill the device run in two launches
+// instead: the sequences longer than one compute unit's share keep a first
+// part of about one share and are cut into short parts after it.
+// gdn_chunk_first_kernel runs every first part (outputs, from init_state; its
+// end state starts the second part) beside the summaries of the later parts,
+// the link runs over the later parts, and gdn_chunk_kernel<output> runs them.
+//
 // A workgroup of the chunk kernels holds the whole state of its (part, head)
 // in fp32 accumulator tiles, 16 state rows per wave; the chunk's K, Q, V rows
 // sit in LDS, and every product reads its operands from there (K^T and V

@@ -1416,22 +1416,23 @@ __global__ __launch_bounds__(64 * D / 16) void gdn_chunk_first_kernel(PrefillArg
 // every later S_p go to ws_s at the part's slot.  For the affine map of whole
 // sequences (aff_m set) the chain runs over every part from zero (offset
 // rows) and from the identity (transition rows, without B_p) and ends in
-// aff_b and aff_m.  Wave w computes the d_k
-// column blocks w, w + 4, ... of S_{p+1} on the fp32 matrix cores.  M_p does
+// aff_b and aff_m.  With NWV waves per row block, wave w computes the d_k
+// column blocks w, w + NWV, ... of S_{p+1} on the fp32 matrix cores (NWV =
+// d_k / 16: one block each, so a step's products are one block deep).  M_p does
 // not depend on S, so M_{p+1} streams into the second LDS buffer (direct
 // loads) while step p computes: a step waits for one load, not a chain of them.
-template <int DK, int DV, int RB = 1>
-__global__ __launch_bounds__(kLinkThreads * RB) void gdn_link_kernel(PrefillArgs a) {
+template <int DK, int DV, int RB = 1, int NWV = kLinkThreads / kWave>
+__global__ __launch_bounds__(kWave * NWV * RB) void gdn_link_kernel(PrefillArgs a) {
     constexpr int NVB = DV / 16, NDB = DK / 16, NKK = DK / 32, LD = DK + 4;
-    constexpr int NWV = kLinkThreads / kWave, PER = (NDB + NWV - 1) / NWV;
+    constexpr int NT = kWave * NWV, PER = (NDB + NWV - 1) / NWV;   // threads per row block
     constexpr int MI = DK * DK * 4 / 1024;               // 1 KB direct loads per M
     static_assert(MI % (NWV * RB) == 0, "M loads per wave");
     static_assert(NVB % RB == 0 && NDB % RB == 0, "row blocks of a workgroup are all offset or all transition rows");
     __shared__ float Sall[RB][16][LD];
     __shared__ float Mb[2][DK * DK];                      // M_p, transposed (m_pos)
-    // RB row blocks per workgroup (kLinkThreads threads each), sharing M_p
+    // RB row blocks per workgroup (NWV waves each), sharing M_p
     const int l = lane_id(), n = l & 15, gq = l >> 4;
-    const int sub = wave_id() / NWV, w = wave_id() - sub * NWV, tid = (int)threadIdx.x - sub * kLinkThreads;
+    const int sub = wave_id() / NWV, w = wave_id() - sub * NWV, tid = (int)threadIdx.x - sub * NT;
     float (&S)[16][LD] = Sall[sub];
     // affine map: row blocks 0 .. NVB - 1 are offset rows (from zero, + B_p),
     // NVB .. NVB + NDB - 1 transition rows (from the identity, no B_p)
@@ -1464,7 +1465,7 @@ __global__ __launch_bounds__(kLinkThreads * RB) void gdn_link_kernel(PrefillArgs
     float* const outp = !aff ? nullptr
                              : trans ? a.aff_m + (chain * DK + R0) * DK : a.aff_b + (chain * DV + R0) * DK;
     if (aff && steps == 0) {                             // empty sequence: M = I, B = 0
-        for (int e = tid; e < 16 * DK; e += kLinkThreads) {
+        for (int e = tid; e < 16 * DK; e += NT) {
             const int row = e / DK, c = e - row * DK;
             outp[(size_t)row * DK + c] = trans && R0 + row == c ? 1.f : 0.f;
         }
@@ -1472,8 +1473,8 @@ __global__ __launch_bounds__(kLinkThreads * RB) void gdn_link_kernel(PrefillArgs
     }
     if (steps <= 0) return;
     if constexpr (kPoisonLds) {
-        poison_lds(Sall, (int)sizeof(Sall), (int)threadIdx.x, kLinkThreads * RB);
-        poison_lds(Mb, (int)sizeof(Mb), (int)threadIdx.x, kLinkThreads * RB);
+        poison_lds(Sall, (int)sizeof(Sall), (int)threadIdx.x, NT * RB);
+        poison_lds(Mb, (int)sizeof(Mb), (int)threadIdx.x, NT * RB);
         __syncthreads();
     }
     const int64_t pbase = span_base(s0, seq, L * kChunk) + j0;   // slot of step 0
@@ -1485,7 +1486,7 @@ __global__ __launch_bounds__(kLinkThreads * RB) void gdn_link_kernel(PrefillArgs
         for (int k = 0; k < MI / (NWV * RB); ++k) bytes_to_lds(&Mb[buf][0], rm, wave_id() + NWV * RB * k);
     };
     load_m(0, 0);
-    for (int e = tid; e < 16 * DK / 4; e += kLinkThreads) {
+    for (int e = tid; e < 16 * DK / 4; e += NT) {
         const int row = e / (DK / 4), c = 4 * (e - row * (DK / 4));
         if (aff) {
             f32x4 x = zero4();
@@ -1609,7 +1610,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
             // shared memory (one per compute unit), and here many chains link
             // at once
             const unsigned links = (unsigned)(((int64_t)a.num_seqs * a.hv + kXcds - 1) / kXcds * kXcds * (DV / 32));
-            hipLaunchKernelGGL((gdn_link_kernel<DK, DV, 2>), dim3(links), dim3(2 * kLinkThreads), 0, st, a);
+            hipLaunchKernelGGL((gdn_link_kernel<DK, DV, 2, DK / 16>), dim3(links), dim3(2 * kWave * (DK / 16)), 0, st, a);
             if ((e = hipGetLastError()) != hipSuccess) return e;
             b.phase = 2;
             hipLaunchKernelGGL((gdn_chunk_kernel<OP, DK, DV, true, RAW>), dim3(parts),
@@ -1624,7 +1625,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
                            dim3(ChunkGeom<OP, DK, DV, false>::NT), 0, st, c);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const unsigned links = (unsigned)(((int64_t)c.num_seqs * c.hv + kXcds - 1) / kXcds * kXcds * (DV / 16));
-        hipLaunchKernelGGL((gdn_link_kernel<DK, DV>), dim3(links), dim3(kLinkThreads), 0, st, c);
+        hipLaunchKernelGGL((gdn_link_kernel<DK, DV, 1, DK / 16>), dim3(links), dim3(kWave * (DK / 16)), 0, st, c);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if constexpr (!RAW) {   // snapshots come with the plain prefill only
@@ -1647,7 +1648,7 @@ hipError_t launch_prefill_affine_t(const PrefillArgs& a, hipStream_t st) {
                        dim3(ChunkGeom<OP, DK, DV, false>::NT), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const unsigned links = (unsigned)(((int64_t)a.num_seqs * a.hv + kXcds - 1) / kXcds * kXcds * (DV / 16 + DK / 16));
-    hipLaunchKernelGGL((gdn_link_kernel<DK, DV>), dim3(links), dim3(kLinkThreads), 0, st, a);
+    hipLaunchKernelGGL((gdn_link_kernel<DK, DV, 1, DK / 16>), dim3(links), dim3(kWave * (DK / 16)), 0, st, a);
     return hipGetLastError();
 }
 

@@ -1097,7 +1097,6 @@ __device__ __forceinline__ void chunk_part(const PrefillArgs& a, int64_t item, c
     Buf* const bufs = sm.bufs;
     OP* const Pf = sm.Pf;
     OP* const Ost = sm.Ost;
-    constexpr bool KT = sizeof(OP) == 2;
     constexpr int KTS = ChunkSmem<OP, DK, DV, OUT, RAW>::KTS;
     OP* const Kt = sm.Kt;
     float* const Nrm = sm.Nrm;

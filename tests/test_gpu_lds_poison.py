@@ -75,3 +75,22 @@ def test_poisoned_shared_memory_workloads(libs, monkeypatch, name):
     for a, b in zip(ref, got):
         assert torch.equal(a, b)
     say(f"[poison] {name}: identical to the normal build")
+
+
+@pytest.mark.parametrize("kind", ["plain", "raw"])
+def test_poisoned_shared_memory_two_launch_schedule(libs, monkeypatch, kind):
+    """A packed batch with as many (sequence, value head) chains as compute units and one long sequence:
+    the two-launch schedule (first parts and summaries in one launch, sharing its shared memory between
+    the two kinds of workgroup; the link with two row blocks per workgroup; the later parts)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n = max(2, cus // 16)
+    lens = ([9000] + [700, 0, 1, 1500, 64, 300] * n)[:n]
+    inp = gi.make_inputs(gi.custom(dtype="bf16", Hqk=8, Hv=16, dk=128, dv=128, seqlens=lens, init_state="normal",
+                                   raw=kind == "raw"), seed=501)
+    normal, poisoned = libs
+    ref = _run(monkeypatch, normal, kind, inp)
+    got = _run(monkeypatch, poisoned, kind, inp)
+    for a, b in zip(ref, got):
+        assert torch.isfinite(b.float()).all()
+        assert torch.equal(a, b)
+    say(f"[poison] two-launch {kind} {n} seqs: identical to the normal build")

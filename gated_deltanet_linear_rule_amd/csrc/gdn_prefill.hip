@@ -1595,9 +1595,9 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
         if (a.phase != 0 && a.ws_m && !a.snapshots) {
             // Balanced schedule: phase 1 runs the first part of every sequence
             // (outputs; the whole sequence when it is not cut) in the same
-            // launch as the summaries of the cut sequences' other parts, the
-            // link gives the later parts' start states, and phase 2 runs the
-            // later parts.  The first parts, which need no start state, fill
+            // launch as the summaries of the cut sequences' later parts (all
+            // but the last), the link gives the later parts' start states, and
+            // phase 2 runs the later parts.  The first parts, which need no start state, fill
             // the compute units that a single pass leaves idle while the
             // longest sequences finish.
             PrefillArgs b = a;

@@ -449,7 +449,7 @@ def main():
                     "kernels": {k: {m: v.get(m) for m in ("mfma_busy", "lds_active", "issuing", "waiting_on_counters")}
                                 for k, v in crec["kernels"].items()}}
 
-    raw_rec = snapshot_rec = affine_rec = None
+    raw_rec = snapshot_rec = affine_rec = slow_rec = None
     headline = args.prefill_workload == "prefill_256k"
     if not args.no_variants and headline:
         # the same call from raw projections (fused q/k normalisation and gate
@@ -487,6 +487,26 @@ def main():
                                     f"({T // (64 * snap_chunks)} snapshots x 16 heads, gdn_prefill_snapshots)",
                         "ms_per_call": round(snap_ms, 4), "tokens_per_s": round(T / (snap_ms * 1e-3), 1)}
         del snaps
+
+        # the same call with slowly decaying gates (g / 1000: about 19 bits of decay over a part of
+        # 256 chunks), so that no part summary finds a decay horizon and every summary runs over its
+        # whole part: the time the call takes when the gates keep a long memory
+        g_slow = g * 1e-3
+        for _ in range(2):
+            B.gdn_prefill(q, k, v, g_slow, beta, ps0, out=out, final_state=fin, workspace=ws, **pkw)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(5):
+            B.gdn_prefill(q, k, v, g_slow, beta, ps0, out=out, final_state=fin, workspace=ws, **pkw)
+        b.record(stream)
+        torch.cuda.synchronize()
+        slow_ms = a.elapsed_time(b) / 5
+        log(f"prefill with slowly decaying gates (g / 1000, no decay horizon): {slow_ms:.3f} ms/call")
+        slow_rec = {"workload": "prefill_256k with the gates g scaled by 1/1000 (about 19 bits of decay per part: "
+                                "no part summary starts at a decay horizon)",
+                    "ms_per_call": round(slow_ms, 4), "tokens_per_s": round(T / (slow_ms * 1e-3), 1),
+                    "hbm_frac": round(bytes_call / (slow_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del g_slow
 
         # the affine state map of the whole sequence (per-device half of a sequence-sharded prefill)
         aff_m = torch.empty((1, hv, dk, dk), dtype=torch.float32, device="cuda")
@@ -721,6 +741,7 @@ def main():
         "prefill_snapshots": snapshot_rec,
         "prefill_raw": raw_rec,
         "prefill_affine": affine_rec,
+        "prefill_slow_gates": slow_rec,
         "prefill_other_workloads": other,
         "context": VENDOR_CONTEXT,
     }

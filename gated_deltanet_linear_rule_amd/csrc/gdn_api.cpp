@@ -385,6 +385,7 @@ gdn_status prefill_impl(const char* who, PrefillKind kind, const gdn_shape* shap
     a.ws_t = wc + wl.t;
     a.ws_g = reinterpret_cast<double*>(wc + wl.g);
     a.ws_ik = kind == kRaw ? reinterpret_cast<float*>(wc + wl.ik) : nullptr;
+    a.ws_hz = reinterpret_cast<float*>(wc + wl.hz);
     a.ws_m = split ? reinterpret_cast<float*>(wc + wl.m) : nullptr;
     a.ws_b = split ? reinterpret_cast<float*>(wc + wl.b) : nullptr;
     a.ws_s = split ? reinterpret_cast<float*>(wc + wl.s) : nullptr;

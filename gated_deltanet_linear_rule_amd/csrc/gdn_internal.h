@@ -55,6 +55,9 @@ struct PrefillArgs {
     double* ws_g;              // 1.25 KB gate record: 64 log2-scaled cumulative gates (fp64),
                                // then 64 gamma, 64 D and 64 beta (fp32)
     float* ws_ik;              // raw projections only: 64 values 1 / |k_t| (256 B)
+    float* ws_hz;              // the chunk's log2 decay sum_t g_t / ln 2 when every token of it is
+                               // a contraction (0 <= beta_t |k_t|^2 <= 1.99, g_t <= 0), else +inf
+                               // (4 B; read by the summary's decay horizon)
     // Per (part slot, value head), fp32 row-major; NULL when no sequence has
     // more than one part:
     float* ws_m;               // d_k x d_k transition M_p of the part, transposed (see m_pos)
@@ -75,7 +78,7 @@ struct PrefillArgs {
 // Workspace layout of one prefill call (byte offsets of each part and total),
 // element size 2 for bf16, 4 for fp32.
 struct PrefillWorkspace {
-    int64_t t, g, ik, m, b, s, total;
+    int64_t t, g, ik, hz, m, b, s, total;
     PrefillWorkspace(int64_t num_slots, int64_t num_part_slots, bool split, int hv, int dk, int dv, int elem_size,
                      bool raw = false) {
         auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
@@ -83,7 +86,8 @@ struct PrefillWorkspace {
         t = 0;
         g = t + up(blocks * (elem_size == 2 ? 5 : 12) * 1024);   // T~: 5 KB bf16, 12 KB fp32
         ik = g + up(blocks * 1280);                               // gate record: 1.25 KB
-        m = ik + (raw ? up(blocks * 256) : 0);
+        hz = ik + (raw ? up(blocks * 256) : 0);
+        m = hz + up(blocks * 4);                                  // chunk decay / contraction: 4 B
         b = m + up(pblocks * dk * dk * 4);
         s = b + up(pblocks * dv * dk * 4);
         total = s + up(pblocks * dv * dk * 4);

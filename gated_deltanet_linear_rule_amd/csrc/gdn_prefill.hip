@@ -445,6 +445,26 @@ __global__ __launch_bounds__(kWave * kPrepWaves) void gdn_prep_kernel(PrefillArg
     ws_store(reinterpret_cast<float*>(rec + kChunk) + 2 * kChunk + l, bl);
     // and 1 / |k_t| itself, for the output kernel's intra-chunk products
     if constexpr (RAW) ws_store(a.ws_ik + blk * kChunk + l, ikl);
+
+    // ---- the chunk's entry for the summary's decay horizon: its log2 decay
+    // G2_63 if every token's factor alpha_t (I - beta_t k_t k_t^T) is a
+    // contraction of spectral norm <= alpha_t <= 1 (g_t <= 0, 0 <= beta_t |k_t|^2
+    // <= 2, taken as <= 1.99 against the rounding of |k_t|^2), else +inf.  Lane
+    // (r, gq) checks row 16 tb + r of K (the four lane groups alike) and its own
+    // token's gates; NaN anywhere fails every comparison.
+    if (a.ws_hz) {
+        bool ok = gl <= 0.f && bl >= 0.f;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            float s2 = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) s2 += frag_sq<OP>(kf[tb][kk]);
+            s2 = sum_groups(s2) * ikr[tb] * ikr[tb];
+            ok = ok && sm.B[16 * tb + r] * s2 <= 1.99f;
+        }
+        const bool all_ok = __ballot(!ok) == 0;
+        if (l == 0) a.ws_hz[blk] = all_ok ? (float)Gl : __builtin_inff();
+    }
 }
 
 // ===========================================================================
@@ -1060,6 +1080,41 @@ struct ChunkLds {
     __device__ static ChunkLds of(ChunkSmem<OP, DK, DV, OUT, RAW>& m) { return {m.bufs, m.Pf, m.Ost, m.Kt, m.Nrm, m.Pdg}; }
 };
 
+// Decay horizon of a part summary.  Over chunks [c, je) the state maps as
+// S -> S M' + B'.  If every token of the part is a contraction (each factor
+// alpha_t (I - beta_t k_t k_t^T) of spectral norm <= alpha_t <= 1, checked by the
+// prep kernel) then |M'| <= 2^(sum of the chunks' log2 decays), and the part's
+// map (M_p, B_p) = (M_0 M', B_0 M' + B') differs from (M', B') by at most that
+// factor times |M_0 - I| <= 2 and |B_0| <= sum_t beta_t |v_t| |k_t| (the state the
+// chunks before c leave from zero).  Once the factor is below 2^-160 (under the
+// smallest fp32 magnitude) the summary may start at c, from zero and from the
+// identity, instead of at the part's first chunk.  Returns the latest such c
+// (jb when there is none, or when some chunk of the part is not a contraction).
+// Lane l reads the entries of chunks e - 1 - l, 64 chunks at a time from the end;
+// every wave computes the same value.
+constexpr double kHorizonLog2 = -160.0;
+__device__ int64_t horizon_start(const float* hz, int64_t cbase, int hv, int h, int64_t jb, int64_t je) {
+    if (!hz) return jb;
+    const int l = lane_id();
+    double carry = 0.0;
+    int64_t c = jb;
+    bool found = false, ok = true;
+    for (int64_t e = je; e > jb; e -= kWave) {
+        const int64_t j = e - 1 - l;
+        const float xj = hz[(cbase + (j >= jb ? j : jb)) * hv + h];   // (in bounds on every lane)
+        const float x = j >= jb ? xj : 0.f;
+        ok = ok && __ballot(!(x <= 0.f)) == 0;                  // +inf (not a contraction) or NaN
+        const double sfx = carry + wave_cumsum_f64((double)x);  // sum over chunks [e - 1 - l, je)
+        const unsigned long long m = __ballot(sfx <= kHorizonLog2);
+        if (!found && m != 0) {
+            found = true;
+            c = e - 1 - __builtin_ctzll(m);
+        }
+        carry = lane63_f64(sfx);
+    }
+    return ok && found ? c : jb;
+}
+
 // The parts of a sequence of nc chunks (one part of no chunks when it is
 // empty).  A sequence of at most `cut` chunks, or of at most F, is one part;
 // any other has a first part of F chunks and later parts of L chunks (the last
@@ -1167,6 +1222,8 @@ __device__ __forceinline__ void chunk_part(const PrefillArgs& a, int64_t item, c
     const int64_t jb = sp.begin(p), je = sp.end(p);
     const int hq = (h * a.hqk) / a.hv;
     const int64_t cbase = span_base(s0, seq, kChunk);
+    // first chunk this workgroup runs: the summary starts at its decay horizon
+    const int64_t js = OUT ? jb : horizon_start(a.ws_hz, cbase, a.hv, h, jb, je);
     const unsigned kstride = (unsigned)(a.hqk * DK * E), vstride = (unsigned)(a.hv * DV * E);
 
     // Buffer resources of chunk j (jb <= j < je).  Bases are taken once per part:
@@ -1320,16 +1377,16 @@ __device__ __forceinline__ void chunk_part(const PrefillArgs& a, int64_t item, c
         __syncthreads();
     }
     if constexpr (G::KTA) {
-        // Summary, bf16: chunk j's inputs sit in buffer set (j - jb) mod 3 and
+        // Summary, bf16: chunk j's inputs sit in buffer set (j - js) mod 3 and
         // its K^T fragments in Kt half j mod 2.  During chunk j the waves form chunk
         // j + 1's K^T fragments (its rows landed before the barrier that opens
         // chunk j) and load chunk j + 2 into the set chunk j - 1 used, so a
         // chunk needs one barrier.
-        issue(jb, bufs[0]);
-        if (jb + 1 < je) issue(jb + 1, bufs[1]);
+        issue(js, bufs[0]);
+        if (js + 1 < je) issue(js + 1, bufs[1]);
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
         lds_barrier();
-        transpose_kt<OP, DK, NW>(bufs[0].K, Kt + (jb & 1) * KTS, w);
+        transpose_kt<OP, DK, NW>(bufs[0].K, Kt + (js & 1) * KTS, w);
         int bc = 0;                                   // buffer set of chunk j
         auto body3 = [&](int64_t j) {
             // chunk j + 1's rows have landed; everyone's K^T fragments of chunk
@@ -1347,10 +1404,10 @@ __device__ __forceinline__ void chunk_part(const PrefillArgs& a, int64_t item, c
             summary_blocks(bufs[bc], ktc, ahead);
             bc = b1;
         };
-        for (int64_t j = jb; j < je; ++j) body3(j);
+        for (int64_t j = js; j < je; ++j) body3(j);
     } else {
-        issue(jb, bufs[0]);
-        for (int64_t j = jb; j < je; j += NBUF) {
+        issue(js, bufs[0]);
+        for (int64_t j = js; j < je; j += NBUF) {
             body(j, bufs[0], bufs[NBUF == 2 ? 1 : 0]);
             if (NBUF == 2 && j + 1 < je) body(j + 1, bufs[NBUF == 2 ? 1 : 0], bufs[0]);
         }

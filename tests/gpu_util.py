@@ -76,6 +76,18 @@ def check_prefill(inp, tol=None, label="", **kw):
     return eo, ef
 
 
+def oracle_affine(inp):
+    """(M, B) of every sequence from the oracle: B is the state reached from zero; M is the state
+    reached from the identity with v = 0 (so that its rows carry the transition alone)."""
+    dk = inp.wl.head_dim_k
+    N, hv = inp.wl.num_seqs, inp.wl.num_v_heads
+    _, rb = c_oracle.prefill(inp.k, inp.k, inp.v, inp.g, inp.beta, None, inp.cu_seqlens)
+    zv = np.zeros((inp.k.shape[0], hv, dk), dtype=inp.v.dtype)
+    eye = np.broadcast_to(np.eye(dk, dtype=np.float32), (N, hv, dk, dk)).copy()
+    _, rm = c_oracle.prefill(inp.k, inp.k, zv, inp.g, inp.beta, eye, inp.cu_seqlens)
+    return rm, rb
+
+
 def oracle_snapshots(inp, P):
     """fp64 states after every P tokens of each sequence, keyed by snapshot slot
     floor(cu[n] / P) + n + s - 1: the oracle run on each prefix of s * P tokens

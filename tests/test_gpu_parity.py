@@ -12,8 +12,8 @@ import torch
 from gated_deltanet_linear_rule_amd import binding as B
 from gated_deltanet_linear_rule_amd import inputs as gi
 from oracle import c_oracle
-from tests.gpu_util import (TOL, check_prefill, dev, host64, oracle_prefill, oracle_snapshots, rel_err,
-                            run_prefill, say)
+from tests.gpu_util import (TOL, check_prefill, dev, host64, oracle_affine, oracle_prefill, oracle_snapshots,
+                            rel_err, run_prefill, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -673,18 +673,6 @@ def test_decode_tokens_degenerate_gates(dtype, kind):
 
 
 # ------------------------------------- affine state map of a token range
-def _oracle_affine(inp):
-    """(M, B) of every sequence from the oracle: B is the state reached from zero; M is the state
-    reached from the identity with v = 0 (so that its rows carry the transition alone)."""
-    dt, dk = inp.wl.dtype, inp.wl.head_dim_k
-    N, hv = inp.wl.num_seqs, inp.wl.num_v_heads
-    _, rb = c_oracle.prefill(inp.k, inp.k, inp.v, inp.g, inp.beta, None, inp.cu_seqlens)
-    zv = np.zeros((inp.k.shape[0], hv, dk), dtype=inp.v.dtype)
-    eye = np.broadcast_to(np.eye(dk, dtype=np.float32), (N, hv, dk, dk)).copy()
-    _, rm = c_oracle.prefill(inp.k, inp.k, zv, inp.g, inp.beta, eye, inp.cu_seqlens)
-    return rm, rb
-
-
 def _mild_gates(inp, decay):
     """Gates under which the transition of a few thousand tokens stays of order one: beta scaled by
     0.02, and g scaled by 0.0002 (decay) or zero.  Every token's factor alpha (I - beta k k^T) then
@@ -707,7 +695,7 @@ def test_prefill_affine_matches_oracle(dtype, decay, dk, dv, lens):
     kw = dict(cu_seqlens=cu) if cu is not None else dict(num_seqs=len(lens))
     m, b = B.gdn_prefill_affine(dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), **kw)
     torch.cuda.synchronize()
-    rm, rb = _oracle_affine(inp)
+    rm, rb = oracle_affine(inp)
     em, eb = rel_err(host64(m), rm), rel_err(host64(b), rb)
     # smallest of the sequences' largest transition entries: every M here is of order one
     mmin = min(float(np.abs(rm[n]).max()) for n in range(len(lens)))
@@ -729,7 +717,7 @@ def test_prefill_affine_under_strong_decay(dtype):
     inp = gi.make_inputs(gi.custom(dtype=dtype, Hqk=1, Hv=2, dk=128, dv=128, seqlens=(3000,)), seed=102)
     m, b = B.gdn_prefill_affine(dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta))
     torch.cuda.synchronize()
-    rm, rb = _oracle_affine(inp)
+    rm, rb = oracle_affine(inp)
     bound = float(np.exp(inp.g.astype(np.float64).sum(axis=0)).max())
     eb, mg = rel_err(host64(b), rb), float(host64(m).__abs__().max())
     say(f"[parity] affine strong decay {dtype}: offset {eb:.3e}, max|M| {mg:.3e} (bound {bound:.1e})")
@@ -837,7 +825,7 @@ def test_seeded_entry_point_sweep(i):
             g, b = dev(inp.g), dev(inp.beta)
             m, bb = B.gdn_prefill_affine(k, v, g, b, **kw)
             torch.cuda.synchronize()
-            rm, rb = _oracle_affine(inp)
+            rm, rb = oracle_affine(inp)
             errs = [rel_err(host64(m), rm), rel_err(host64(bb), rb)]
         else:
             P = c["P"]

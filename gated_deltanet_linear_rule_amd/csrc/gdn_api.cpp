@@ -389,6 +389,7 @@ gdn_status prefill_impl(const char* who, PrefillKind kind, const gdn_shape* shap
     a.ws_m = split ? reinterpret_cast<float*>(wc + wl.m) : nullptr;
     a.ws_b = split ? reinterpret_cast<float*>(wc + wl.b) : nullptr;
     a.ws_s = split ? reinterpret_cast<float*>(wc + wl.s) : nullptr;
+    a.ws_hf = split ? reinterpret_cast<int32_t*>(wc + wl.hf) : nullptr;
     const int dk = shape->head_dim_k, dv = shape->head_dim_v;
     hipError_t e = affine ? gdn::launch_prefill_affine(a, bf16, dk, dv, st)
                           : gdn::launch_prefill(a, bf16, dk, dv, st, kind == kRaw);

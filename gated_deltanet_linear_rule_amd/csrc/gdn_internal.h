@@ -63,6 +63,8 @@ struct PrefillArgs {
     float* ws_m;               // d_k x d_k transition M_p of the part, transposed (see m_pos)
     float* ws_b;               // d_v x d_k offset B_p of the part (state from zero)
     float* ws_s;               // d_v x d_k start state S_p of the part
+    int32_t* ws_hf;            // 1 if the part's summary started at its decay horizon (M_p is
+                               // negligible: S_{p+1} = B_p), else 0
     // Optional state snapshots every snap_chunks chunks of each sequence:
     // snapshot s (state after the first 64 s snap_chunks tokens) of sequence n
     // at slot floor(start(n) / (64 snap_chunks)) + n + s - 1.
@@ -78,7 +80,7 @@ struct PrefillArgs {
 // Workspace layout of one prefill call (byte offsets of each part and total),
 // element size 2 for bf16, 4 for fp32.
 struct PrefillWorkspace {
-    int64_t t, g, ik, hz, m, b, s, total;
+    int64_t t, g, ik, hz, m, b, s, hf, total;
     PrefillWorkspace(int64_t num_slots, int64_t num_part_slots, bool split, int hv, int dk, int dv, int elem_size,
                      bool raw = false) {
         auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
@@ -90,7 +92,8 @@ struct PrefillWorkspace {
         m = hz + up(blocks * 4);                                  // chunk decay / contraction: 4 B
         b = m + up(pblocks * dk * dk * 4);
         s = b + up(pblocks * dv * dk * 4);
-        total = s + up(pblocks * dv * dk * 4);
+        hf = s + up(pblocks * dv * dk * 4);
+        total = hf + up(pblocks * 4);                             // horizon flags: 4 B
     }
 };
 

@@ -317,6 +317,26 @@ __global__ __launch_bounds__(kWave * kPrepWaves) void gdn_prep_kernel(PrefillArg
     sm.B[l] = bl;
     wave_lds_sync();
 
+    // ---- whether every token's factor alpha_t (I - beta_t k_t k_t^T) is a
+    // contraction of spectral norm <= alpha_t <= 1: g_t <= 0 and 0 <= beta_t
+    // |k_t|^2 <= 2 (taken as <= 1.99 against the rounding of |k_t|^2).  Lane (r, gq)
+    // checks row 16 tb + r of K (the four lane groups alike) and its own token's
+    // gates; NaN anywhere fails every comparison.  Decided here, while K is in
+    // registers anyway; the summary's decay horizon reads the result.
+    bool contracting;
+    {
+        bool ok = gl <= 0.f && bl >= 0.f;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            float s2 = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) s2 += frag_sq<OP>(kf[tb][kk]);
+            s2 = sum_groups(s2) * ikr[tb] * ikr[tb];
+            ok = ok && sm.B[16 * tb + r] * s2 <= 1.99f;
+        }
+        contracting = __ballot(!ok) == 0;
+    }
+
     // ---- A = strict_lower(diag(beta) (Gamma o K K^T)): the ten lower tiles in
     // accumulator layout (lane (n, gq) holds A[16 tm + 4 gq + i][16 tn + n]).
     f32x4 at[10];
@@ -445,26 +465,9 @@ __global__ __launch_bounds__(kWave * kPrepWaves) void gdn_prep_kernel(PrefillArg
     ws_store(reinterpret_cast<float*>(rec + kChunk) + 2 * kChunk + l, bl);
     // and 1 / |k_t| itself, for the output kernel's intra-chunk products
     if constexpr (RAW) ws_store(a.ws_ik + blk * kChunk + l, ikl);
-
-    // ---- the chunk's entry for the summary's decay horizon: its log2 decay
-    // G2_63 if every token's factor alpha_t (I - beta_t k_t k_t^T) is a
-    // contraction of spectral norm <= alpha_t <= 1 (g_t <= 0, 0 <= beta_t |k_t|^2
-    // <= 2, taken as <= 1.99 against the rounding of |k_t|^2), else +inf.  Lane
-    // (r, gq) checks row 16 tb + r of K (the four lane groups alike) and its own
-    // token's gates; NaN anywhere fails every comparison.
-    if (a.ws_hz) {
-        bool ok = gl <= 0.f && bl >= 0.f;
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            float s2 = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) s2 += frag_sq<OP>(kf[tb][kk]);
-            s2 = sum_groups(s2) * ikr[tb] * ikr[tb];
-            ok = ok && sm.B[16 * tb + r] * s2 <= 1.99f;
-        }
-        const bool all_ok = __ballot(!ok) == 0;
-        if (l == 0) a.ws_hz[blk] = all_ok ? (float)Gl : __builtin_inff();
-    }
+    // the chunk's entry for the summary's decay horizon: its log2 decay G2_63
+    // if every token is a contraction, else +inf
+    if (l == 0 && a.ws_hz) a.ws_hz[blk] = contracting ? (float)Gl : __builtin_inff();
 }
 
 // ===========================================================================
@@ -1089,11 +1092,13 @@ struct ChunkLds {
 // chunks before c leave from zero).  Once the factor is below 2^-160 (under the
 // smallest fp32 magnitude) the summary may start at c, from zero and from the
 // identity, instead of at the part's first chunk.  Returns the latest such c
-// (jb when there is none, or when some chunk of the part is not a contraction).
-// Lane l reads the entries of chunks e - 1 - l, 64 chunks at a time from the end;
-// every wave computes the same value.
+// (jb when there is none, or when some chunk of the part is not a contraction),
+// and in `taken` whether there is one: then M_p is negligible and the link may
+// take S_{p+1} = B_p.  Lane l reads the entries of chunks e - 1 - l, 64 chunks at
+// a time from the end; every wave computes the same values.
 constexpr double kHorizonLog2 = -160.0;
-__device__ int64_t horizon_start(const float* hz, int64_t cbase, int hv, int h, int64_t jb, int64_t je) {
+__device__ int64_t horizon_start(const float* hz, int64_t cbase, int hv, int h, int64_t jb, int64_t je, bool& taken) {
+    taken = false;
     if (!hz) return jb;
     const int l = lane_id();
     double carry = 0.0;
@@ -1112,7 +1117,8 @@ __device__ int64_t horizon_start(const float* hz, int64_t cbase, int hv, int h, 
         }
         carry = lane63_f64(sfx);
     }
-    return ok && found ? c : jb;
+    taken = ok && found;
+    return taken ? c : jb;
 }
 
 // The parts of a sequence of nc chunks (one part of no chunks when it is
@@ -1197,10 +1203,14 @@ __device__ __forceinline__ void chunk_part(const PrefillArgs& a, int64_t item, c
             return;
         }
         // the part's start state: written by the link (one pass over more than
-        // one part, and the later parts of the balanced schedule), else init_state
-        const float* Sin = a.phase == 2 || (a.phase == 0 && sp.np > 1)
-                               ? a.ws_s + sblk * DV * DK
-                               : (a.init_state ? a.init_state + chain * DV * DK : nullptr);
+        // one part, and the later parts of the balanced schedule), else init_state;
+        // B_{p-1} itself when the previous part was summarised from its decay
+        // horizon (the link then writes nothing for this part)
+        const bool linked = a.phase == 2 || (a.phase == 0 && sp.np > 1);
+        const bool from_b = linked && p >= (a.phase == 2 ? 2 : 1) && a.ws_hf[sblk - a.hv] != 0;
+        const float* Sin = from_b ? a.ws_b + (sblk - a.hv) * DV * DK
+                           : linked ? a.ws_s + sblk * DV * DK
+                                    : (a.init_state ? a.init_state + chain * DV * DK : nullptr);
         // where the part's end state goes: final_state after the last part; in
         // the balanced schedule's first launch, the start of the first later part
         Send = last ? (a.final_state ? a.final_state + chain * DV * DK : nullptr)
@@ -1222,8 +1232,11 @@ __device__ __forceinline__ void chunk_part(const PrefillArgs& a, int64_t item, c
     const int64_t jb = sp.begin(p), je = sp.end(p);
     const int hq = (h * a.hqk) / a.hv;
     const int64_t cbase = span_base(s0, seq, kChunk);
-    // first chunk this workgroup runs: the summary starts at its decay horizon
-    const int64_t js = OUT ? jb : horizon_start(a.ws_hz, cbase, a.hv, h, jb, je);
+    // first chunk this workgroup runs: the summary starts at its decay horizon,
+    // and records whether it found one
+    bool taken = false;
+    const int64_t js = OUT ? jb : horizon_start(a.ws_hz, cbase, a.hv, h, jb, je, taken);
+    if (!OUT && w == 0 && l == 0) a.ws_hf[sblk] = taken ? 1 : 0;
     const unsigned kstride = (unsigned)(a.hqk * DK * E), vstride = (unsigned)(a.hv * DV * E);
 
     // Buffer resources of chunk j (jb <= j < je).  Bases are taken once per part:
@@ -1535,13 +1548,47 @@ __global__ __launch_bounds__(kWave * NWV * RB) void gdn_link_kernel(PrefillArgs 
     }
     const int64_t pbase = span_base(s0, seq, L * kChunk) + j0;   // slot of step 0
 
+    // Steps whose part was summarised from its decay horizon: M_p is negligible
+    // and S_{p+1} = B_p (the transition rows of the affine map become 0).  Bit
+    // p mod 64 of `neg` covers step p of the current group of 64 steps.
+    auto neg_group = [&](int64_t p0) {
+        const int64_t p = p0 + l;
+        const int f = a.ws_hf[(pbase + (p < steps ? p : p0)) * a.hv + h];   // (in bounds on every lane)
+        return __ballot(p < steps && f != 0);
+    };
+    bool all_neg = true;
+    for (int64_t p0 = 0; p0 < steps; p0 += kWave) {
+        const unsigned long long m = neg_group(p0);
+        const int64_t left = steps - p0;
+        all_neg = all_neg && m == (left >= kWave ? ~0ull : (1ull << left) - 1);
+    }
+    if (all_neg) {
+        // every step: nothing to chain.  The output kernel starts each later
+        // part from B_{p-1} itself; S_0 still goes to ws_s (one pass), and the
+        // affine map is (0, B of the last part).
+        for (int e = tid; e < 16 * DK / 4; e += NT) {
+            const int row = e / (DK / 4), c = 4 * (e - row * (DK / 4));
+            if (aff) {
+                const f32x4 x = trans ? zero4()
+                                      : *reinterpret_cast<const f32x4*>(
+                                            a.ws_b + (((size_t)(pbase + steps - 1) * a.hv + h) * DV + R0 + row) * DK + c);
+                *reinterpret_cast<f32x4*>(outp + (size_t)row * DK + c) = x;
+            } else if (!bal) {
+                const f32x4 x = a.init_state ? *reinterpret_cast<const f32x4*>(a.init_state + (chain * DV + R0 + row) * DK + c) : zero4();
+                *reinterpret_cast<f32x4*>(a.ws_s + (((size_t)pbase * a.hv + h) * DV + R0 + row) * DK + c) = x;
+            }
+        }
+        return;
+    }
+    unsigned long long neg = neg_group(0);
+
     auto load_m = [&](int64_t p, int buf) {
         const float* M = a.ws_m + ((size_t)(pbase + p) * a.hv + h) * DK * DK;
         const auto rm = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(M), 0, DK * DK * 4, 0x00020000);
 #pragma unroll
         for (int k = 0; k < MI / (NWV * RB); ++k) bytes_to_lds(&Mb[buf][0], rm, wave_id() + NWV * RB * k);
     };
-    load_m(0, 0);
+    if (!(neg & 1)) load_m(0, 0);
     for (int e = tid; e < 16 * DK / 4; e += NT) {
         const int row = e / (DK / 4), c = 4 * (e - row * (DK / 4));
         if (aff) {
@@ -1582,10 +1629,17 @@ __global__ __launch_bounds__(kWave * NWV * RB) void gdn_link_kernel(PrefillArgs 
         if (p == 0) __builtin_amdgcn_s_waitcnt(kWaitVm0);
         else __builtin_amdgcn_s_waitcnt(kWaitVm0 | ((PER * 4) & 15) | (((PER * 4) >> 4) << 14));
         __syncthreads();                                 // everyone's is; S_p is written
+        const bool neg_p = (neg >> (p & 63)) & 1;
+        if (((p + 1) & 63) == 0 && p + 1 < steps) neg = neg_group(p + 1);
         if (p + 1 < steps) {
-            load_m(p + 1, cb ^ 1);                       // the other buffer was read in step p - 1
+            if (!((neg >> ((p + 1) & 63)) & 1)) load_m(p + 1, cb ^ 1);   // the other buffer was read in step p - 1
             load_b(p + 1, bnext);
         }
+        f32x4 res[PER];
+        if (neg_p) {                                     // S_{p+1} = B_p (transition rows: 0)
+#pragma unroll
+            for (int k = 0; k < PER; ++k) res[k] = trans ? zero4() : bcur[k];
+        } else {
         const float* M = Mb[cb];
         // every operand of the step's products is read from LDS first, then the
         // products run (one wait for LDS instead of one per K step)
@@ -1606,7 +1660,6 @@ __global__ __launch_bounds__(kWave * NWV * RB) void gdn_link_kernel(PrefillArgs 
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        f32x4 res[PER];
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int db = w + NWV * k;
@@ -1615,6 +1668,7 @@ __global__ __launch_bounds__(kWave * NWV * RB) void gdn_link_kernel(PrefillArgs 
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) c = Op<float>::mma(av[kk], bv[k][kk], c);
             res[k] = c;
+        }
         }
         lds_barrier();                                   // S_p read by everyone (M_{p+1} may be in flight)
         float* Sn = aff ? outp : a.ws_s + ((size_t)(pbase + p + 1) * a.hv + h) * DV * DK + (size_t)R0 * DK;

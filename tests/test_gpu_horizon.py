@@ -11,7 +11,8 @@ affine map entry point, which runs the summaries alone, that the horizon is
 taken exactly when the part's tokens allow it: a NaN value at the first token
 stays out of the map when the horizon is taken and reaches it when a
 non-contracting token (beta |k|^2 > 2, or g > 0) anywhere in the part forbids
-it.
+it.  Parts of both kinds in one sequence exercise the link, which takes
+S_{p+1} = B_p after a part with a horizon and S_p M_p + B_p after one without.
 """
 import numpy as np
 import pytest
@@ -65,14 +66,16 @@ def test_horizon_packed_varlen_with_raw_projections():
     assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("T", [384, 65536])
 @pytest.mark.parametrize("refuse", [None, "beta", "gate"])
-def test_horizon_is_taken_exactly_on_contracting_parts(refuse):
-    """Affine map of a 65536-token sequence (every part summarised) with v = NaN at token 0.  With
-    the standard gates every part's horizon is a few chunks from its end, so the NaN cannot reach the
-    map: M and B are finite and match the oracle run with v = 0 at token 0.  One token of the first
-    chunk with beta |k|^2 = 2.5, or with g = +0.25, makes the first part non-contracting: its summary
-    then runs from its first chunk and the NaN reaches B in every head."""
-    inp = _long("bf16", 1.0, 201)
+def test_horizon_is_taken_exactly_on_contracting_parts(refuse, T):
+    """Affine map of one sequence (every part summarised) with v = NaN at token 0.  With the standard
+    gates every part's horizon is a few chunks from its end, so the NaN cannot reach the map: M and B
+    are finite and match the oracle run with v = 0 at token 0.  One token of the first chunk with
+    beta |k|^2 = 2.5, or with g = +0.25, makes the first part non-contracting: its summary then runs
+    from its first chunk, and with T = 384 (one part of six chunks) the NaN reaches B in every head.
+    (Over 65536 tokens the later parts' horizons cut the NaN off again: S_{p+1} = B_p.)"""
+    inp = _long("bf16", 1.0, 201, T=T)
     if refuse == "beta":
         inp.beta[5, :] = 2.5
     elif refuse == "gate":
@@ -82,14 +85,54 @@ def test_horizon_is_taken_exactly_on_contracting_parts(refuse):
     m, b = B.gdn_prefill_affine(dev(inp.k), dev(vn), dev(inp.g), dev(inp.beta))
     torch.cuda.synchronize()
     nan_heads = int(torch.isnan(b).flatten(2).any(dim=2).sum().item())
-    say(f"[horizon] refuse={refuse}: heads with NaN in B {nan_heads} of {b.shape[1]}, max|M| "
+    say(f"[horizon] T={T} refuse={refuse}: heads with NaN in B {nan_heads} of {b.shape[1]}, max|M| "
         f"{float(torch.nan_to_num(m, nan=0.0).abs().max()):.3e}")
-    if refuse is None:
+    if refuse is None or T > 384:
         inp.v[0] = 0
         rm, rb = oracle_affine(inp)
         eb = rel_err(host64(b), rb)
-        say(f"[parity] horizon affine: offset {eb:.3e}, oracle max|M| {np.abs(rm).max():.3e}")
+        say(f"[parity] horizon affine T={T}: offset {eb:.3e}, oracle max|M| {np.abs(rm).max():.3e}")
         assert nan_heads == 0 and torch.isfinite(m).all()
         assert eb <= TOL["bf16"] and float(m.abs().max()) <= 1e-6 and np.abs(rm).max() <= 1e-6
     else:
         assert nan_heads == b.shape[1]
+
+
+def _mixed_gates(inp, period=3000):
+    """Alternating stretches of `period` tokens: the standard gates, then g = 0 with beta / 20 (no
+    decay, a transition of order one), so that some parts of a long sequence are summarised from a
+    decay horizon and others in full, and the link chains both kinds."""
+    t = np.arange(inp.g.shape[0])
+    weak = (t // period) % 2 == 1
+    inp.g[weak] = 0
+    inp.beta[weak] *= 0.05
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_link_over_parts_with_and_without_horizon(dtype):
+    inp = _long(dtype, 1.0, 203)
+    _mixed_gates(inp)
+    check_prefill(inp, label=f"mixed horizons {dtype}")
+
+
+def test_affine_map_over_parts_with_and_without_horizon():
+    """The map's offset chains parts of both kinds; its transition passes through a part with a
+    horizon, so it vanishes (as the oracle's does)."""
+    inp = _long("bf16", 1.0, 204, T=40000)
+    _mixed_gates(inp)
+    m, b = B.gdn_prefill_affine(dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta))
+    torch.cuda.synchronize()
+    rm, rb = oracle_affine(inp)
+    eb = rel_err(host64(b), rb)
+    say(f"[parity] affine, mixed horizons: offset {eb:.3e}, max|M| {float(m.abs().max()):.3e} "
+        f"(oracle {np.abs(rm).max():.3e})")
+    assert eb <= TOL["bf16"] and float(m.abs().max()) <= 1e-6 and np.abs(rm).max() <= 1e-6
+
+
+def test_balanced_schedule_with_and_without_horizon():
+    """Packed batch under the two-launch schedule (later parts start from B of the part before when
+    that part had a horizon, else from the link's state)."""
+    from tests.test_gpu_parity import _balanced_batch
+    inp = _balanced_batch(205)
+    _mixed_gates(inp, period=1100)
+    check_prefill(inp, label="balanced, mixed horizons")

@@ -225,22 +225,60 @@ def part_plan(wl, cus=CUS):
     return seqs, balanced
 
 
-def wave_chunks(wl):
+HORIZON_LOG2 = -160.0
+
+
+def summary_steps(inp, seq, a, e):
+    """Chunk steps the summary of chunks [a, e) of sequence `seq` runs, summed over the value heads:
+    from its decay horizon when it has one (every token a contraction, g <= 0 and 0 <= beta |k|^2 <=
+    1.99, and the chunks' log2 decays summing to <= -160 from some chunk to the end; the prep and
+    summary kernels decide this on the device), else all e - a.  For the per-chunk counter figures."""
+    wl = inp.wl
+    cu = np.concatenate([[0], np.cumsum(wl.seqlens)])
+    t0, t1 = int(cu[seq]) + 64 * a, min(int(cu[seq]) + 64 * e, int(cu[seq + 1]))
+    g = inp.g[t0:t1].astype(np.float64)                         # [tokens, Hv]
+    beta = inp.beta[t0:t1].astype(np.float64)
+    k = inp.k[t0:t1]
+    k = (k.astype(np.uint32) << 16).view(np.float32) if k.dtype == np.uint16 else k
+    k2 = (k.astype(np.float64) ** 2).sum(axis=2)                # [tokens, Hqk]
+    k2 = np.repeat(k2, wl.num_v_heads // wl.num_qk_heads, axis=1)
+    ok = np.all((g <= 0) & (beta >= 0) & (beta * k2 <= 1.99), axis=0)
+    pad = (-(t1 - t0)) % 64
+    dec = np.concatenate([g, np.zeros((pad, g.shape[1]))]).reshape(-1, 64, g.shape[1]).sum(axis=1) / np.log(2)
+    suffix = np.cumsum(dec[::-1], axis=0)[::-1]                 # sum over chunks [c, e)
+    steps = 0
+    for h in range(g.shape[1]):
+        hit = np.nonzero(suffix[:, h] <= HORIZON_LOG2)[0]
+        steps += (e - a) - int(hit[-1]) if ok[h] and len(hit) else e - a
+    return steps
+
+
+def wave_chunks(wl, inp=None):
     """Chunk steps summed over the working waves of each chunk kernel in one prefill call (every wave
     of a part's workgroup runs the part's chunks; d_k = d_v here or d_v waves for outputs and
-    max(d_k, d_v) for summaries)."""
+    max(d_k, d_v) for summaries).  A summary runs from its part's decay horizon when it has one
+    (summary_steps, with the inputs `inp`; without them every chunk of the part is counted)."""
     seqs, balanced = part_plan(wl)
     nwo, nws = wl.head_dim_v // 16, max(wl.head_dim_v, wl.head_dim_k) // 16
     H = wl.num_v_heads
+
+    def summ_of(n, head, rest, summarised):
+        # chunk ranges of the summarised parts of sequence n: the first part (unless the balanced
+        # schedule runs it from init_state), then the later parts but the last
+        bounds = [(0, head)] + [(head + sum(rest[:j]), head + sum(rest[:j + 1])) for j in range(len(rest))]
+        parts = bounds[:-1] if summarised else bounds[1:-1]
+        if inp is None:
+            return sum(e - a for a, e in parts) * H
+        return sum(summary_steps(inp, n, a, e) for a, e in parts)
     if balanced:
         # first launch: first parts (outputs) and the later parts' summaries but the last's
-        first = sum(h for h, _ in seqs) * H * nwo + sum(sum(r[:-1]) for _, r in seqs) * H * nws
+        first = sum(h for h, _ in seqs) * H * nwo + sum(summ_of(n, h, r, False) for n, (h, r) in enumerate(seqs)) * nws
         later = sum(sum(r) for _, r in seqs) * H * nwo
         return {"gdn_chunk_first_kernel": first, "gdn_chunk_kernel<output>": later}
     # one pass over every part; with no later parts the sequence is one part.  Summaries: every
     # part but the last (the first part of a cut sequence is the first slot, the rest follow)
     out = sum(h + sum(r) for h, r in seqs) * H * nwo
-    summ = sum((h + sum(r[:-1])) if r else 0 for h, r in seqs) * H * nws
+    summ = sum(summ_of(n, h, r, True) if r else 0 for n, (h, r) in enumerate(seqs)) * nws
     wcs = {"gdn_chunk_kernel<output>": out}
     if summ:
         wcs["gdn_chunk_kernel<summary>"] = summ
@@ -366,11 +404,11 @@ def main():
         return
     if args.sq_summary:
         from gated_deltanet_linear_rule_amd import inputs as gi
-        wl = gi.make_inputs(args.prefill_workload, seed=0).wl
-        # chunk steps per wave: every wave of a part's workgroup runs the part's chunks; parts are
-        # 64 L tokens, L as the library chooses on a 256-CU device (one part per sequence when the
-        # (sequence, head) chains alone fill it)
-        write_sq_summary(args.sq_summary, args.prefill_workload, args.prefill_calls, wave_chunks(wl))
+        winp = gi.make_inputs(args.prefill_workload, seed=0)
+        # chunk steps per wave: every wave of a part's workgroup runs the part's chunks (a summary
+        # from its decay horizon); parts are 64 L tokens, L as the library chooses on a 256-CU device
+        # (one part per sequence when the (sequence, head) chains alone fill it)
+        write_sq_summary(args.sq_summary, args.prefill_workload, args.prefill_calls, wave_chunks(winp.wl, winp))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the GDN path here is single-GPU); got --gpus {args.gpus}",

@@ -160,3 +160,19 @@ def test_sq_summary_per_call_rates(tmp_path, monkeypatch):
     # per call 3200 VALU and 640 MFMA instructions over 16 waves x 10 chunks
     assert k["per_wave_chunk"] == {"valu": 20.0, "mfma": 4.0}
     assert bench.counters_current("w") and not bench.counters_current("other")
+
+
+def test_summary_steps_follow_the_decay_horizon():
+    """Per-chunk counter figures count a summary's chunks from its decay horizon: about three chunks
+    per head with the workload's gates (a chunk decays by about 2^-74), every chunk with g = 0 or when
+    one token of the range has beta |k|^2 > 2 (not a contraction)."""
+    from gated_deltanet_linear_rule_amd import inputs as gi
+    inp = gi.make_inputs(gi.custom(dtype="bf16", Hqk=2, Hv=4, dk=128, dv=128, seqlens=(640,)), seed=1)
+    assert 4 * 2 <= bench.summary_steps(inp, 0, 0, 10) <= 4 * 4
+    beta = inp.beta.copy()
+    inp.beta[100, 1] = 2.5
+    got = bench.summary_steps(inp, 0, 0, 10)
+    assert 3 * 2 + 10 <= got <= 3 * 4 + 10            # head 1 runs every chunk
+    inp.beta = beta
+    inp.g[:] = 0
+    assert bench.summary_steps(inp, 0, 0, 10) == 4 * 10

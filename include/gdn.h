@@ -127,6 +127,14 @@ gdn_status gdn_prefill_workspace_size(const gdn_shape* shape, uint32_t flags, si
  * NULL, the state after each sequence's last token.  The chunk-wise WY / UT
  * form (chunks of 64 tokens, restarting at every sequence start) is used on
  * the GPU; the result equals the token-by-token recurrence up to rounding.
+ * Decay horizon: when a sequence is cut into parts and every token of a part
+ * contracts the state (g_t <= 0 and 0 <= beta_t |k_t|^2 <= 2, so that the
+ * token's factor exp(g_t) (I - beta_t k_t k_t^T) has norm <= exp(g_t)), the
+ * part's summary starts at the latest chunk from which the gates to the
+ * part's end multiply to at most 2^-160, and the next part's start state
+ * drops the earlier state's contribution (scaled by at most that factor,
+ * below fp32 resolution).  Results are unchanged to rounding; a NaN or inf
+ * input stays within its own part there instead of reaching later parts.
  *
  * init_state  [N, Hv, dv, dk] fp32 or NULL (zero initial state).  It may be
  *             the same buffer as final_state (each sequence's slice is read

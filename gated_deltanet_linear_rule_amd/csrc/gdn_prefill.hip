@@ -1332,12 +1332,16 @@ __device__ __forceinline__ void chunk_part(const PrefillArgs& a, int64_t item, c
     };
     // Summary chunk step over the wave's blocks.  With d_v != d_k the waves
     // past the smaller block count have one block only and run a one-block step
-    // (a wave-uniform branch; every wave still meets the same barriers).
+    // (a wave-uniform branch; every wave still meets the same barriers).  From a
+    // decay horizon only the value block runs (M_p is not needed).
     auto summary_blocks = [&](const Buf& cb, OP* ktc, auto&& hook) {
         if constexpr (!OUT) {
             using One = f32x4(&)[1][NDB];
             using OneR = const int(&)[1];
-            if (NVB == NMB || (w < NVB && w < NMB))
+            if (taken && w < NVB)   // from a decay horizon M_p is not needed: the value block only
+                chunk_step<OP, DK, DV, OUT, 1, 1, NW, RAW>(cb, nullptr, ktc, nullptr, reinterpret_cast<One>(ST[0]),
+                                                           reinterpret_cast<OneR>(R0[0]), w, hook, Nrm, Pdg);
+            else if (NVB == NMB || (w < NVB && w < NMB))
                 chunk_step<OP, DK, DV, OUT, NR, 1, NW, RAW>(cb, nullptr, ktc, nullptr, ST, R0, w, hook, Nrm, Pdg);
             else if (w < NMB)   // d_v < d_k: a transition block only
                 chunk_step<OP, DK, DV, OUT, 1, 0, NW, RAW>(cb, nullptr, ktc, nullptr, reinterpret_cast<One>(ST[1]),
@@ -1436,7 +1440,7 @@ __device__ __forceinline__ void chunk_part(const PrefillArgs& a, int64_t item, c
             for (int b = 0; b < NR; ++b) store_state<DK>(Send, R0[b], ST[b]);
     } else {
         if (w < NVB) store_state<DK>(a.ws_b + sblk * DV * DK, R0[0], ST[0]);
-        if (w < NMB) store_transition<DK>(a.ws_m + sblk * DK * DK, R0[1], ST[1]);
+        if (w < NMB && !taken) store_transition<DK>(a.ws_m + sblk * DK * DK, R0[1], ST[1]);   // (no reader after a horizon)
     }
 }
 

@@ -771,6 +771,9 @@ def main():
         "prefill_raw": raw_rec,
         "prefill_affine": affine_rec,
         "prefill_slow_gates": slow_rec,
+        "method_note": "with these gates every part summary starts at its decay horizon (the chunks before it reach "
+                       "the part's end scaled by at most 2^-160, every token a contraction; checked on the device "
+                       "per call): prefill_slow_gates is the same call with g / 1000, where no summary has one",
         "prefill_other_workloads": other,
         "context": VENDOR_CONTEXT,
     }

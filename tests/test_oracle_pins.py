@@ -211,6 +211,27 @@ def test_contraction_spectral_norm_nonincreasing():
     assert all(b <= a * (1 + 1e-12) for a, b in zip(norms, norms[1:]))
 
 
+def test_transition_of_a_contracting_range_is_bounded_by_its_decay():
+    """The bound a part summary's decay horizon rests on: when every token has g_t <= 0 and
+    0 <= beta_t |k_t|^2 <= 2, the map of a token range, M (the state reached from the identity with
+    v = 0), has spectral norm <= prod alpha_t = exp(sum g_t).  beta up to 1.99 / |k|^2 is included.
+    One token with beta |k|^2 = 2.5 (and alpha = 1) breaks it: I - 2.5 k k^T has norm 1.5."""
+    rng = np.random.default_rng(16)
+    dk = 8
+    for trial in range(4):
+        q, k, v, g, beta, _ = _rand(rng, 50, 1, 1, dk, dk)
+        beta = rng.uniform(0.0, 1.99, size=beta.shape)          # |k| = 1: beta |k|^2 in [0, 1.99]
+        g = g * rng.uniform(0.0, 0.2)                           # mild decay: the bound stays far above 0
+        eye = np.eye(dk)[None, None]
+        _, M = ref.sequential(q, k, np.zeros_like(v), g, beta, eye)
+        bound = math.exp(float(g.sum()))
+        assert np.linalg.norm(M[0, 0], 2) <= bound * (1 + 1e-12)
+    k1 = np.zeros((1, 1, dk))
+    k1[0, 0, 0] = 1.0
+    _, M1 = ref.sequential(k1, k1, np.zeros((1, 1, dk)), np.zeros((1, 1)), np.full((1, 1), 2.5), np.eye(dk)[None, None])
+    assert abs(np.linalg.norm(M1[0, 0], 2) - 1.5) < 1e-12
+
+
 # --------------------------------------------------------------------------
 # structure: linearity, row independence, boundaries
 # --------------------------------------------------------------------------

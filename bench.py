@@ -71,12 +71,13 @@ def decode_tokens_bytes(N, T, hqk, hv, dk, dv, elem=2, token_states=True):
 
 
 def _code_text(text):
-    """Source text without comments and blank lines (so that a comment edit does not
-    count as a change of the kernels; string literals in these files hold no comment marks)."""
+    """Source text without comments, blank lines and indentation, runs of spaces as one (so that
+    a comment edit or a re-indent does not count as a change of the kernels; string literals in
+    these files hold no comment marks)."""
     import re
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     text = re.sub(r"//[^\n]*", "", text)
-    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+    return "\n".join(" ".join(ln.split()) for ln in text.splitlines() if ln.strip())
 
 
 def _sha(paths, read=None):

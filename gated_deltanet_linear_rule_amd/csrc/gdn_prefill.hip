@@ -1644,35 +1644,35 @@ __global__ __launch_bounds__(kWave * NWV * RB) void gdn_link_kernel(PrefillArgs 
 #pragma unroll
             for (int k = 0; k < PER; ++k) res[k] = trans ? zero4() : bcur[k];
         } else {
-        const float* M = Mb[cb];
-        // every operand of the step's products is read from LDS first, then the
-        // products run (one wait for LDS instead of one per K step)
-        f32x8 av[NKK], bv[PER][NKK];
+            const float* M = Mb[cb];
+            // every operand of the step's products is read from LDS first, then the
+            // products run (one wait for LDS instead of one per K step)
+            f32x8 av[NKK], bv[PER][NKK];
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
+            for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) av[kk][i] = S[n][32 * kk + (i < 4 ? 4 * gq + i : 16 + 4 * gq + i - 4)];
+                for (int i = 0; i < 8; ++i) av[kk][i] = S[n][32 * kk + (i < 4 ? 4 * gq + i : 16 + 4 * gq + i - 4)];
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int db = w + NWV * k < NDB ? w + NWV * k : w;   // (an unused block reads a valid one)
+            for (int k = 0; k < PER; ++k) {
+                const int db = w + NWV * k < NDB ? w + NWV * k : w;   // (an unused block reads a valid one)
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const int c = 16 * db + n;
-                const f32x4 lo = *reinterpret_cast<const f32x4*>(&M[m_pos(c, 32 * kk + 4 * gq, DK)]);
-                const f32x4 hi = *reinterpret_cast<const f32x4*>(&M[m_pos(c, 32 * kk + 16 + 4 * gq, DK)]);
-                bv[k][kk] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const int c = 16 * db + n;
+                    const f32x4 lo = *reinterpret_cast<const f32x4*>(&M[m_pos(c, 32 * kk + 4 * gq, DK)]);
+                    const f32x4 hi = *reinterpret_cast<const f32x4*>(&M[m_pos(c, 32 * kk + 16 + 4 * gq, DK)]);
+                    bv[k][kk] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
             }
-        }
-        __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int db = w + NWV * k;
-            if (db >= NDB) break;
-            f32x4 c = bcur[k];
+            for (int k = 0; k < PER; ++k) {
+                const int db = w + NWV * k;
+                if (db >= NDB) break;
+                f32x4 c = bcur[k];
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) c = Op<float>::mma(av[kk], bv[k][kk], c);
-            res[k] = c;
-        }
+                for (int kk = 0; kk < NKK; ++kk) c = Op<float>::mma(av[kk], bv[k][kk], c);
+                res[k] = c;
+            }
         }
         lds_barrier();                                   // S_p read by everyone (M_{p+1} may be in flight)
         float* Sn = aff ? outp : a.ws_s + ((size_t)(pbase + p + 1) * a.hv + h) * DV * DK + (size_t)R0 * DK;

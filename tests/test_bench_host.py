@@ -73,10 +73,11 @@ def test_source_hash_ignores_comments_but_not_code():
     texts = {
         "base": base,
         "comment": "/* header\n   block */\nint f(int x) {\n\n  return x + 1;  // add 1\n}\n",
+        "indent": "int f(int x) {\n        return   x + 1;\n}\n",
         "code": base.replace("x + 1", "x + 2"),
     }
     h = {k: bench._sha(["a"], read=lambda p, t=t: t) for k, t in texts.items()}
-    assert h["base"] == h["comment"]
+    assert h["base"] == h["comment"] == h["indent"]
     assert h["base"] != h["code"]
 
 

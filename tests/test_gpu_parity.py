@@ -709,18 +709,19 @@ def test_prefill_affine_matches_oracle(dtype, decay, dk, dv, lens):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_prefill_affine_under_strong_decay(dtype):
+@pytest.mark.parametrize("dk,dv", [(128, 128), (128, 64), (64, 128)])
+def test_prefill_affine_under_strong_decay(dtype, dk, dv):
     """The workload's gates (mean alpha 0.5) over 3000 tokens in parts: B against the oracle (plain
     metric).  Every token's factor alpha (I - beta k k^T) has spectral norm at most alpha (|k| = 1 to
     bf16 rounding, beta in [0, 1]), so |M_ij| <= exp(sum g), which is below 1e-300 here: the computed
     transition must vanish to within fp32 rounding of the identity it starts from."""
-    inp = gi.make_inputs(gi.custom(dtype=dtype, Hqk=1, Hv=2, dk=128, dv=128, seqlens=(3000,)), seed=102)
+    inp = gi.make_inputs(gi.custom(dtype=dtype, Hqk=1, Hv=2, dk=dk, dv=dv, seqlens=(3000,)), seed=102)
     m, b = B.gdn_prefill_affine(dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta))
     torch.cuda.synchronize()
     rm, rb = oracle_affine(inp)
     bound = float(np.exp(inp.g.astype(np.float64).sum(axis=0)).max())
     eb, mg = rel_err(host64(b), rb), float(host64(m).__abs__().max())
-    say(f"[parity] affine strong decay {dtype}: offset {eb:.3e}, max|M| {mg:.3e} (bound {bound:.1e})")
+    say(f"[parity] affine strong decay {dtype} dk={dk} dv={dv}: offset {eb:.3e}, max|M| {mg:.3e} (bound {bound:.1e})")
     assert bound < 1e-300 and np.abs(rm).max() <= bound
     assert eb <= TOL[dtype] and mg <= 1e-6
 

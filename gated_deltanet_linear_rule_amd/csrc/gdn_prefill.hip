@@ -29,6 +29,10 @@
 //    giving the part's offset B_p (d_v x d_k) and transition M_p (d_k x d_k).
 //  * gdn_link_kernel   -- per (sequence, head, 16 state rows), sequentially
 //    over parts: S_{p+1} = S_p M_p + B_p (fp32 matrix cores).
+//  * decay horizon: when every token of a part contracts the state and its
+//    gates multiply to at most 2^-160 over the part's last few chunks, the
+//    summary starts there (value rows only) and S_{p+1} = B_p: see
+//    horizon_start.
 //  * gdn_chunk_kernel<output> runs every part from its true start state and
 //    writes the outputs (and the final state, from the last part).
 //
@@ -1494,6 +1498,9 @@ __global__ __launch_bounds__(64 * D / 16) void gdn_chunk_first_kernel(PrefillArg
 // d_k / 16: one block each, so a step's products are one block deep).  M_p does
 // not depend on S, so M_{p+1} streams into the second LDS buffer (direct
 // loads) while step p computes: a step waits for one load, not a chain of them.
+// A step whose part was summarised from its decay horizon takes S_{p+1} = B_p
+// without M_p; when every step of a chain is such, the workgroup only copies
+// S_0 (the output kernel then starts each later part from the B before it).
 template <int DK, int DV, int RB = 1, int NWV = kLinkThreads / kWave>
 __global__ __launch_bounds__(kWave * NWV * RB) void gdn_link_kernel(PrefillArgs a) {
     constexpr int NVB = DV / 16, NDB = DK / 16, NKK = DK / 32, LD = DK + 4;

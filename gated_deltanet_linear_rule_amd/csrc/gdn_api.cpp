@@ -238,7 +238,7 @@ gdn_status plan_prefill(const gdn_shape* shape, bool packed, PrefillKind kind, g
     const int64_t longest = packed ? (a.num_tokens + 63) / 64 : (a.seqlen + 63) / 64;
     // the affine map needs every sequence's part maps, split or not
     split = kind == kAffine || longest > (a.first_chunks > a.cut_chunks ? a.first_chunks : a.cut_chunks);
-    if (2 * a.num_part_slots * a.hv > INT32_MAX ||
+    if (3 * a.num_part_slots * a.hv > INT32_MAX ||
         (a.num_seqs * (int64_t)a.hv + 7) * (a.dv / 16 + shape->head_dim_k / 16) > INT32_MAX)
         return fail(GDN_ERROR_NOT_SUPPORTED, "too many (part, head) pairs");
     const gdn::PrefillWorkspace wl(a.num_slots, a.num_part_slots, split, a.hv, shape->head_dim_k, shape->head_dim_v,

@@ -1144,15 +1144,25 @@ struct SeqParts {
     }
 };
 
-// One (part slot, value head) of a chunk kernel.
+// Chunks of the part before it that a later part reruns from zero (its decay
+// horizon's depth) to find its own start state, at most.
+constexpr int64_t kWarmChunks = 6;
+
+// One (part slot, value head) of a chunk kernel, in phase ph (the launch's
+// a.phase, or its role in the balanced schedule's first launch).
 // OUT = false: summary of parts p < np - 1 (B_p into ws_b, M_p into ws_m).
 // OUT = true: outputs of every part, from ws_s (np > 1) or init_state (np = 1);
 // the last part writes final_state; SNAP: also the state snapshots.  In the
-// balanced schedule (a.phase 1 and 2, see launch_prefill_t) the first part of
+// balanced schedule (phases 1 to 3, see launch_prefill_t) the first part of
 // every sequence runs in phase 1 from init_state and leaves its end state as
-// the second part's start state; the later parts run in phase 2.
+// the second part's start state.  A later part whose predecessor has a decay
+// horizon at most kWarmChunks from its end runs in phase 3, in the same
+// launch: from zero at that horizon, through the predecessor's last chunks
+// (outputs not stored), then its own.  The other later parts run in phase 2,
+// after the link.
 template <typename OP, int DK, int DV, bool OUT, bool RAW, bool SNAP>
-__device__ __forceinline__ void chunk_part(const PrefillArgs& a, int64_t item, const ChunkLds<OP, DK, DV, OUT, RAW>& sm) {
+__device__ __forceinline__ void chunk_part(const PrefillArgs& a, int64_t item, const ChunkLds<OP, DK, DV, OUT, RAW>& sm,
+                                           int ph) {
     using G = ChunkGeom<OP, DK, DV, OUT>;
     using Buf = ChunkBuf<OP, DK, DV, OUT, OUT && RAW>;
     constexpr int NR = G::NR, NW = G::NW, NBUF = G::NBUF;
@@ -1180,7 +1190,15 @@ __device__ __forceinline__ void chunk_part(const PrefillArgs& a, int64_t item, c
     const SeqParts sp(nc, L, a.first_chunks, a.cut_chunks);
     if (p < 0 || p >= sp.np) return;                            // gap slot
     const bool last = p == sp.np - 1;
-    if (OUT && (a.phase == 1 ? p != 0 : a.phase == 2 && p == 0)) return;   // the other phase's part
+    const int64_t cbase = span_base(s0, seq, kChunk);
+    if (OUT && ph == 1 && p != 0) return;                        // a later part
+    int64_t jw = 0;                                              // phase 3: first chunk of the rerun
+    if (OUT && (ph == 2 || ph == 3)) {
+        if (p == 0) return;                                      // a first part
+        bool t;
+        jw = horizon_start(a.ws_hz, cbase, a.hv, h, sp.begin(p - 1), sp.begin(p), t);
+        if ((t && sp.begin(p) - jw <= kWarmChunks) != (ph == 3)) return;   // the other phase's part
+    }
     const int64_t chain = (int64_t)seq * a.hv + h;
     const size_t sblk = (size_t)pslot * a.hv + h;
 
@@ -1210,22 +1228,24 @@ __device__ __forceinline__ void chunk_part(const PrefillArgs& a, int64_t item, c
         // one part, and the later parts of the balanced schedule), else init_state;
         // B_{p-1} itself when the previous part was summarised from its decay
         // horizon (the link then writes nothing for this part)
-        const bool linked = a.phase == 2 || (a.phase == 0 && sp.np > 1);
-        const bool from_b = linked && p >= (a.phase == 2 ? 2 : 1) && a.ws_hf[sblk - a.hv] != 0;
+        // (phase 3: zero, at the predecessor's horizon)
+        const bool linked = ph == 2 || (ph == 0 && sp.np > 1);
+        const bool from_b = linked && p >= (ph == 2 ? 2 : 1) && a.ws_hf[sblk - a.hv] != 0;
         const float* Sin = from_b ? a.ws_b + (sblk - a.hv) * DV * DK
                            : linked ? a.ws_s + sblk * DV * DK
-                                    : (a.init_state ? a.init_state + chain * DV * DK : nullptr);
+                           : ph == 3 ? nullptr
+                                     : (a.init_state ? a.init_state + chain * DV * DK : nullptr);
         // where the part's end state goes: final_state after the last part; in
         // the balanced schedule's first launch, the start of the first later part
         Send = last ? (a.final_state ? a.final_state + chain * DV * DK : nullptr)
-                    : a.phase == 1 ? a.ws_s + ((size_t)(pslot + 1) * a.hv + h) * DV * DK : nullptr;
+                    : ph == 1 ? a.ws_s + ((size_t)(pslot + 1) * a.hv + h) * DV * DK : nullptr;
 #pragma unroll
         for (int b = 0; b < NR; ++b) load_state<DK>(Sin, R0[b], ST[b]);
     } else {
         // every part but the last (its map is not needed to link), or every
         // part for the affine map of whole sequences; in the balanced schedule
         // not the first part either (its outputs give the next start state)
-        if (a.aff_m ? nc == 0 : last || (a.phase == 1 && p == 0)) return;
+        if (a.aff_m ? nc == 0 : last || (ph == 1 && p == 0)) return;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             ST[0][db] = zero4();
@@ -1235,28 +1255,27 @@ __device__ __forceinline__ void chunk_part(const PrefillArgs& a, int64_t item, c
     }
     const int64_t jb = sp.begin(p), je = sp.end(p);
     const int hq = (h * a.hqk) / a.hv;
-    const int64_t cbase = span_base(s0, seq, kChunk);
     // first chunk this workgroup runs: the summary starts at its decay horizon,
-    // and records whether it found one
+    // and records whether it found one; phase 3 at its predecessor's
     bool taken = false;
-    const int64_t js = OUT ? jb : horizon_start(a.ws_hz, cbase, a.hv, h, jb, je, taken);
+    const int64_t js = OUT ? (ph == 3 ? jw : jb) : horizon_start(a.ws_hz, cbase, a.hv, h, jb, je, taken);
     if (!OUT && w == 0 && l == 0) a.ws_hf[sblk] = taken ? 1 : 0;
     const unsigned kstride = (unsigned)(a.hqk * DK * E), vstride = (unsigned)(a.hv * DV * E);
 
-    // Buffer resources of chunk j (jb <= j < je).  Bases are taken once per part:
-    // chunk j's rows start (j - jb) * 64 rows after chunk jb's, its T~ fragments
-    // and gate record (j - jb) * Hv records after; only the sequence's last
+    // Buffer resources of chunk j (js <= j < je).  Bases are taken once per part:
+    // chunk j's rows start (j - js) * 64 rows after chunk js's, its T~ fragments
+    // and gate record (j - js) * Hv records after; only the sequence's last
     // chunk may be partial, and its resources end at its last row, so rows past
     // the end read as 0 and stores to them are dropped.  (Per chunk this is a
     // few scalar adds: all eight waves compute these resources at the same
     // point of every chunk, on scalar issue slots they share.)
-    const size_t row0 = (size_t)(s0 + jb * kChunk);
+    const size_t row0 = (size_t)(s0 + js * kChunk);
     const char* const kB0 = static_cast<const char*>(a.k) + ((row0 * a.hqk + hq) * DK) * E;
     const char* const qB0 = static_cast<const char*>(a.q) + ((row0 * a.hqk + hq) * DK) * E;
     const char* const vB0 = static_cast<const char*>(a.v) + ((row0 * a.hv + h) * DV) * E;
     char* const oB0 = static_cast<char*>(a.out) + ((row0 * a.hv + h) * DV) * E;
-    const char* const tB0 = static_cast<const char*>(a.ws_t) + ((size_t)(cbase + jb) * a.hv + h) * (UT * 1024);
-    const char* const gB0 = reinterpret_cast<const char*>(a.ws_g) + ((size_t)(cbase + jb) * a.hv + h) * kGateRecord;
+    const char* const tB0 = static_cast<const char*>(a.ws_t) + ((size_t)(cbase + js) * a.hv + h) * (UT * 1024);
+    const char* const gB0 = reinterpret_cast<const char*>(a.ws_g) + ((size_t)(cbase + js) * a.hv + h) * kGateRecord;
     const uint32_t kstep = kChunk * kstride, vstep = kChunk * vstride;
     const uint32_t tstep = (uint32_t)a.hv * (UT * 1024), gstep = (uint32_t)a.hv * kGateRecord;
     const int64_t jl = nc - 1;                                  // the sequence's last chunk
@@ -1266,14 +1285,14 @@ __device__ __forceinline__ void chunk_part(const PrefillArgs& a, int64_t item, c
     auto rsrc = [](const void* ptr, int bytes) {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(ptr), 0, bytes, 0x00020000);
     };
-    auto at = [&](const char* base, uint32_t step, int64_t j) { return base + (uint64_t)(uint32_t)(j - jb) * step; };
+    auto at = [&](const char* base, uint32_t step, int64_t j) { return base + (uint64_t)(uint32_t)(j - js) * step; };
     auto res_k = [&](int64_t j) { return rsrc(at(kB0, kstep, j), j == jl ? klast : kfull); };
     auto res_q = [&](int64_t j) { return rsrc(at(qB0, kstep, j), j == jl ? klast : kfull); };
     auto res_v = [&](int64_t j) { return rsrc(at(vB0, vstep, j), j == jl ? vlast : vfull); };
     auto res_o = [&](int64_t j) { return rsrc(at(oB0, vstep, j), j == jl ? vlast : vfull); };
     auto res_t = [&](int64_t j) { return rsrc(at(tB0, tstep, j), UT * 1024); };
     auto res_g = [&](int64_t j) { return rsrc(at(gB0, gstep, j), kGateRecord); };
-    const char* const ikB0 = OUT && RAW ? reinterpret_cast<const char*>(a.ws_ik) + ((size_t)(cbase + jb) * a.hv + h) * (kChunk * 4)
+    const char* const ikB0 = OUT && RAW ? reinterpret_cast<const char*>(a.ws_ik) + ((size_t)(cbase + js) * a.hv + h) * (kChunk * 4)
                                         : nullptr;
     auto res_ik = [&](int64_t j) { return rsrc(at(ikB0, (uint32_t)a.hv * (kChunk * 4), j), kChunk * 4); };
 
@@ -1462,13 +1481,15 @@ __global__ __launch_bounds__(64 * (OUT ? DV / 16 : (DV > DK ? DV : DK) / 16)) vo
     __shared__ decltype(SM::Kt) Kt;
     __shared__ decltype(SM::Nrm) Nrm;
     __shared__ decltype(SM::Pdg) Pdg;
-    chunk_part<OP, DK, DV, OUT, RAW, SNAP>(a, blockIdx.x, ChunkLds<OP, DK, DV, OUT, RAW>{bufs, Pf, Ost, Kt, Nrm, Pdg});
+    chunk_part<OP, DK, DV, OUT, RAW, SNAP>(a, blockIdx.x, ChunkLds<OP, DK, DV, OUT, RAW>{bufs, Pf, Ost, Kt, Nrm, Pdg},
+                                           a.phase);
 }
 
-// Phase 1 of the balanced schedule (d_k = d_v): workgroups [0, n) run the first
-// part of every sequence from init_state (outputs), workgroups [n, 2n) the
-// summaries, n = part slots x value heads.  The two kinds share the shared
-// memory, one at a time.
+// The first launch of the balanced schedule (d_k = d_v): workgroups [0, n) run
+// the first part of every sequence from init_state (outputs, phase 1),
+// workgroups [n, 2n) the summaries, workgroups [2n, 3n) the later parts whose
+// predecessor has a near decay horizon (outputs, phase 3), n = part slots x
+// value heads.  The kinds share the shared memory, one at a time.
 template <typename OP, int D, bool RAW>
 __global__ __launch_bounds__(64 * D / 16) void gdn_chunk_first_kernel(PrefillArgs a) {
     using SO = ChunkSmem<OP, D, D, true, RAW>;
@@ -1476,12 +1497,14 @@ __global__ __launch_bounds__(64 * D / 16) void gdn_chunk_first_kernel(PrefillArg
     static_assert(ChunkGeom<OP, D, D, true>::NT == 64 * D / 16 && ChunkGeom<OP, D, D, false>::NT == 64 * D / 16,
                   "both kinds use the launch size");
     __shared__ __attribute__((aligned(16))) unsigned char smem[sizeof(SO) > sizeof(SS) ? sizeof(SO) : sizeof(SS)];
-    const int64_t n = a.num_part_slots * a.hv;
-    if ((int64_t)blockIdx.x < n)
-        chunk_part<OP, D, D, true, RAW, false>(a, blockIdx.x, ChunkLds<OP, D, D, true, RAW>::of(*reinterpret_cast<SO*>(smem)));
+    const int64_t n = a.num_part_slots * a.hv, b = blockIdx.x;
+    if (b < n || b >= 2 * n)
+        chunk_part<OP, D, D, true, RAW, false>(a, b < n ? b : b - 2 * n,
+                                               ChunkLds<OP, D, D, true, RAW>::of(*reinterpret_cast<SO*>(smem)),
+                                               b < n ? 1 : 3);
     else
-        chunk_part<OP, D, D, false, RAW, false>(a, (int64_t)blockIdx.x - n,
-                                                ChunkLds<OP, D, D, false, RAW>::of(*reinterpret_cast<SS*>(smem)));
+        chunk_part<OP, D, D, false, RAW, false>(a, b - n, ChunkLds<OP, D, D, false, RAW>::of(*reinterpret_cast<SS*>(smem)),
+                                                1);
 }
 
 // ===========================================================================
@@ -1718,13 +1741,15 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
             // Balanced schedule: phase 1 runs the first part of every sequence
             // (outputs; the whole sequence when it is not cut) in the same
             // launch as the summaries of the cut sequences' later parts (all
-            // but the last), the link gives the later parts' start states, and
-            // phase 2 runs the later parts.  The first parts, which need no start state, fill
-            // the compute units that a single pass leaves idle while the
-            // longest sequences finish.
+            // but the last) and, as phase 3, the later parts whose predecessor
+            // has a near decay horizon (each reruns that predecessor's last
+            // chunks from zero); the link gives the other later parts' start
+            // states, and phase 2 runs them.  The first parts, which need no
+            // start state, fill the compute units that a single pass leaves
+            // idle while the longest sequences finish.
             PrefillArgs b = a;
             b.phase = 1;
-            hipLaunchKernelGGL((gdn_chunk_first_kernel<OP, DK, RAW>), dim3(2 * parts),
+            hipLaunchKernelGGL((gdn_chunk_first_kernel<OP, DK, RAW>), dim3(3 * parts),
                                dim3(ChunkGeom<OP, DK, DV, true>::NT), 0, st, b);
             if ((e = hipGetLastError()) != hipSuccess) return e;
             // two row blocks per workgroup: the link's workgroups hold 140 KB of

@@ -227,13 +227,14 @@ def part_plan(wl, cus=CUS):
 
 
 HORIZON_LOG2 = -160.0
+WARM_CHUNKS = 6            # deepest predecessor horizon a later part reruns in the first launch
 
 
-def summary_steps(inp, seq, a, e):
-    """Chunk steps the summary of chunks [a, e) of sequence `seq` runs, summed over the value heads:
-    from its decay horizon when it has one (every token a contraction, g <= 0 and 0 <= beta |k|^2 <=
+def horizon_depths(inp, seq, a, e):
+    """Per value head, the number of chunks from the decay horizon of chunks [a, e) of sequence
+    `seq` to e, or None where there is none (every token a contraction, g <= 0 and 0 <= beta |k|^2 <=
     1.99, and the chunks' log2 decays summing to <= -160 from some chunk to the end; the prep and
-    summary kernels decide this on the device), else all e - a.  For the per-chunk counter figures."""
+    chunk kernels decide this on the device).  For the per-chunk counter figures."""
     wl = inp.wl
     cu = np.concatenate([[0], np.cumsum(wl.seqlens)])
     t0, t1 = int(cu[seq]) + 64 * a, min(int(cu[seq]) + 64 * e, int(cu[seq + 1]))
@@ -247,11 +248,17 @@ def summary_steps(inp, seq, a, e):
     pad = (-(t1 - t0)) % 64
     dec = np.concatenate([g, np.zeros((pad, g.shape[1]))]).reshape(-1, 64, g.shape[1]).sum(axis=1) / np.log(2)
     suffix = np.cumsum(dec[::-1], axis=0)[::-1]                 # sum over chunks [c, e)
-    steps = 0
+    depths = []
     for h in range(g.shape[1]):
         hit = np.nonzero(suffix[:, h] <= HORIZON_LOG2)[0]
-        steps += (e - a) - int(hit[-1]) if ok[h] and len(hit) else e - a
-    return steps
+        depths.append((e - a) - int(hit[-1]) if ok[h] and len(hit) else None)
+    return depths
+
+
+def summary_steps(inp, seq, a, e):
+    """Chunk steps the summary of chunks [a, e) of sequence `seq` runs, summed over the value heads:
+    from its decay horizon when it has one, else all e - a."""
+    return sum(e - a if d is None else d for d in horizon_depths(inp, seq, a, e))
 
 
 def wave_chunks(wl, inp=None):
@@ -272,9 +279,20 @@ def wave_chunks(wl, inp=None):
             return sum(e - a for a, e in parts) * H
         return sum(summary_steps(inp, n, a, e) for a, e in parts)
     if balanced:
-        # first launch: first parts (outputs) and the later parts' summaries but the last's
+        # first launch: first parts (outputs), the later parts' summaries but the last's, and the later
+        # parts whose predecessor has a horizon at most WARM_CHUNKS from its end (their own chunks and
+        # the rerun ones); second launch: the other later parts
         first = sum(h for h, _ in seqs) * H * nwo + sum(summ_of(n, h, r, False) for n, (h, r) in enumerate(seqs)) * nws
-        later = sum(sum(r) for _, r in seqs) * H * nwo
+        later = 0
+        for n, (h, r) in enumerate(seqs):
+            bounds = [(0, h)] + [(h + sum(r[:j]), h + sum(r[:j + 1])) for j in range(len(r))]
+            for (a0, e0), (a1, e1) in zip(bounds, bounds[1:]):
+                depths = horizon_depths(inp, n, a0, e0) if inp is not None else [None] * H
+                for d in depths:
+                    if d is not None and d <= WARM_CHUNKS:
+                        first += (e1 - a1 + d) * nwo
+                    else:
+                        later += (e1 - a1) * nwo
         return {"gdn_chunk_first_kernel": first, "gdn_chunk_kernel<output>": later}
     # one pass over every part; with no later parts the sequence is one part.  Summaries: every
     # part but the last (the first part of a cut sequence is the first slot, the rest follow)

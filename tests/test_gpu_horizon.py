@@ -130,8 +130,9 @@ def test_affine_map_over_parts_with_and_without_horizon():
 
 
 def test_balanced_schedule_with_and_without_horizon():
-    """Packed batch under the two-launch schedule (later parts start from B of the part before when
-    that part had a horizon, else from the link's state)."""
+    """Packed batch under the two-launch schedule: a later part whose predecessor has a horizon at most
+    six chunks from its end reruns those chunks from zero in the first launch; the others start from B
+    of the part before (a deeper horizon) or from the link's state, in the second launch."""
     from tests.test_gpu_parity import _balanced_batch
     inp = _balanced_batch(205)
     _mixed_gates(inp, period=1100)

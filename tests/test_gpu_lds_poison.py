@@ -77,16 +77,23 @@ def test_poisoned_shared_memory_workloads(libs, monkeypatch, name):
     say(f"[poison] {name}: identical to the normal build")
 
 
-@pytest.mark.parametrize("kind", ["plain", "raw"])
+@pytest.mark.parametrize("kind", ["plain", "raw", "mixed"])
 def test_poisoned_shared_memory_two_launch_schedule(libs, monkeypatch, kind):
     """A packed batch with as many (sequence, value head) chains as compute units and one long sequence:
-    the two-launch schedule (first parts and summaries in one launch, sharing its shared memory between
-    the two kinds of workgroup; the link with two row blocks per workgroup; the later parts)."""
+    the two-launch schedule (first parts, summaries and the later parts after a near decay horizon in
+    one launch, sharing its shared memory between the kinds of workgroup; the link with two row blocks
+    per workgroup; the other later parts).  "mixed": stretches of g = 0 among the standard gates, so
+    that later parts run in both launches."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     n = max(2, cus // 16)
     lens = ([9000] + [700, 0, 1, 1500, 64, 300] * n)[:n]
     inp = gi.make_inputs(gi.custom(dtype="bf16", Hqk=8, Hv=16, dk=128, dv=128, seqlens=lens, init_state="normal",
                                    raw=kind == "raw"), seed=501)
+    if kind == "mixed":
+        weak = (np.arange(inp.g.shape[0]) // 1100) % 2 == 1
+        inp.g[weak] = 0
+        inp.beta[weak] *= 0.05
+        kind = "plain"
     normal, poisoned = libs
     ref = _run(monkeypatch, normal, kind, inp)
     got = _run(monkeypatch, poisoned, kind, inp)

@@ -1197,7 +1197,11 @@ __device__ __forceinline__ void chunk_part(const PrefillArgs& a, int64_t item, c
         if (p == 0) return;                                      // a first part
         bool t;
         jw = horizon_start(a.ws_hz, cbase, a.hv, h, sp.begin(p - 1), sp.begin(p), t);
-        if ((t && sp.begin(p) - jw <= kWarmChunks) != (ph == 3)) return;   // the other phase's part
+        // (a last part that writes final_state in place of init_state stays in
+        // phase 2: in phase 3 it would share a launch with the first part that
+        // reads init_state)
+        const bool in_place = last && a.init_state != nullptr && a.init_state == a.final_state;
+        if ((t && sp.begin(p) - jw <= kWarmChunks && !in_place) != (ph == 3)) return;   // the other phase's part
     }
     const int64_t chain = (int64_t)seq * a.hv + h;
     const size_t sblk = (size_t)pslot * a.hv + h;

@@ -177,3 +177,19 @@ def test_summary_steps_follow_the_decay_horizon():
     inp.beta = beta
     inp.g[:] = 0
     assert bench.summary_steps(inp, 0, 0, 10) == 4 * 10
+
+
+def test_wave_chunks_place_later_parts_by_their_predecessors_horizon():
+    """Per-chunk counter figures of the packed schedule: with the workload's gates every later part of
+    varlen_8x follows a part whose horizon is a few chunks from its end, so its chunks (and the rerun
+    ones) count in the first launch; with g = 0 none does, and they count in the second launch, as
+    without inputs."""
+    from gated_deltanet_linear_rule_amd import inputs as gi
+    inp = gi.make_inputs("varlen_8x", seed=0)
+    plain = bench.wave_chunks(inp.wl)
+    fast = bench.wave_chunks(inp.wl, inp)
+    assert fast["gdn_chunk_kernel<output>"] == 0
+    assert fast["gdn_chunk_first_kernel"] > plain["gdn_chunk_first_kernel"]
+    inp.g[:] = 0
+    slow = bench.wave_chunks(inp.wl, inp)
+    assert slow["gdn_chunk_kernel<output>"] == plain["gdn_chunk_kernel<output>"] > 0
